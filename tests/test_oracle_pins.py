@@ -1,0 +1,372 @@
+"""Pins of the CPU oracle to facts outside itself (run with -m "not gpu").
+
+Each test checks the oracle against something the pages or the mathematics
+fix: values the pages print (golden files), closed forms, invariants, special
+cases that reduce to a library routine, and brute-force enumeration on tiny
+inputs.  Together they are meant to fail on any plausible slip in the oracle
+(a dropped term, a wrong comparator, sign or index, a transposed operand).
+"""
+
+import math
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import synthetic as syn
+from oracle import brute, calibrate, gemv, sparsify, spmm, swiglu
+
+
+# --------------------------------------------------------------------------
+# threshold sparsifier
+# --------------------------------------------------------------------------
+
+def test_threshold_hand_case_keeps_equal_magnitude():
+    x = np.array([0.5, -0.5, 0.25, 0.0, -1.0, -0.0, 0.75], dtype=np.float16)
+    keep, idx, val, nnz = sparsify.threshold_sparsify(x, 0.5)
+    assert keep.tolist() == [True, True, False, False, True, False, True]
+    assert idx.tolist() == [0, 1, 4, 6]
+    assert val.astype(np.float64).tolist() == [0.5, -0.5, -1.0, 0.75]
+    assert nnz == 4
+
+
+def test_threshold_matches_python_loop():
+    for seed in range(5):
+        x = syn.laplace_f16((257,), 1.0, seed)
+        t = float(np.float32(0.3 + 0.1 * seed))
+        keep = sparsify.threshold_sparsify(x, t)[0]
+        assert np.array_equal(keep, brute.threshold_loop(x, t))
+
+
+def test_threshold_zero_is_dense_product():
+    """t = 0 keeps every nonzero, so W x_s equals the dense product W x."""
+    x = syn.gaussian_f16((300,), 1.0, 7)
+    x[::17] = 0
+    wt = syn.weight_t(96, 300, 11)
+    keep, idx, val, nnz = sparsify.threshold_sparsify(x, 0.0)
+    assert nnz == np.count_nonzero(x)
+    y = gemv.sparse_gemv(wt, idx, val)
+    ref = x.astype(np.float64) @ wt.astype(np.float64)  # numpy matmul
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_sparsity_definition_identity():
+    """Q-Sparse replies: sparsity is the fraction of zeros of the activation."""
+    for seed in range(4):
+        x = syn.gaussian_f16((1024,), 1.0, seed)
+        t = float(np.float32(0.6745))
+        keep, idx, val, nnz = sparsify.threshold_sparsify(x, t)
+        xs = sparsify.apply_mask(x, keep)
+        assert sparsify.activation_sparsity(xs) == 1.0 - nnz / 1024
+
+
+def test_threshold_equals_topk_with_distinct_magnitudes():
+    x = (np.random.default_rng(3).permutation(512).astype(np.float32) + 1) / 64
+    x = (x * np.where(np.arange(512) % 3 == 0, -1, 1)).astype(np.float16)
+    assert len(np.unique(np.abs(x))) == 512
+    t = float(np.sort(np.abs(x.astype(np.float64)))[200])
+    keep = sparsify.threshold_sparsify(x, t)[0]
+    keep_k = sparsify.topk_sparsify(x, int(keep.sum()))[0]
+    assert np.array_equal(keep, keep_k)
+
+
+def test_threshold_rows():
+    X = syn.gaussian_f16((3, 64), 1.0, 5)
+    keep, idx, val, nnz = sparsify.threshold_sparsify(X, 0.5)
+    for r in range(3):
+        k1, i1, v1, n1 = sparsify.threshold_sparsify(X[r], 0.5)
+        assert np.array_equal(keep[r], k1) and np.array_equal(idx[r], i1) and nnz[r] == n1
+
+
+# --------------------------------------------------------------------------
+# Top-K
+# --------------------------------------------------------------------------
+
+def test_topk_hand_ties_to_lower_index():
+    x = np.array([1.0, -2.0, 2.0, 1.0, -1.0, 0.0], dtype=np.float16)
+    assert sparsify.topk_sparsify(x, 2)[1].tolist() == [1, 2]
+    assert sparsify.topk_sparsify(x, 3)[1].tolist() == [0, 1, 2]
+    assert sparsify.topk_sparsify(x, 4)[1].tolist() == [0, 1, 2, 3]
+    assert sparsify.topk_sparsify(x, 0)[3] == 0
+    assert sparsify.topk_sparsify(x, 6)[1].tolist() == [0, 1, 2, 3, 4, 5]
+
+
+def test_topk_signed_zero_is_a_tie():
+    x = np.array([-0.0, 0.0, -0.0, 1.0], dtype=np.float16)
+    assert sparsify.topk_sparsify(x, 2)[1].tolist() == [0, 3]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    d = int(rng.integers(1, 13))
+    # few distinct magnitudes so ties are common; includes signed zeros
+    pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0, 0.125], dtype=np.float16)
+    x = pool[rng.integers(0, len(pool), size=d)]
+    for k in range(0, d + 1):
+        keep = sparsify.topk_sparsify(x, k)[0]
+        assert np.array_equal(keep, brute.topk_brute(x, k)), (x, k)
+        assert keep.sum() == k
+
+
+def test_topk_percent_to_sparsity(golden):
+    """TopK = 60/50/40 % keeps 60/50/40 % of entries: sparsity 40/50/60 %."""
+    for topk_pct, sp_pct in golden("topk_sparsity.txt"):
+        for d in (4096, 11008):
+            k = syn.topk_k(int(topk_pct), d)
+            x = syn.laplace_f16((d,), 1.0, 0)
+            keep = sparsify.topk_sparsify(x, k)[0]
+            sp = sparsify.activation_sparsity(sparsify.apply_mask(x, keep))
+            assert abs(sp - int(sp_pct) / 100) < 1.0 / d
+
+
+# --------------------------------------------------------------------------
+# N:M
+# --------------------------------------------------------------------------
+
+def test_nm_layout_counts_match_pages(golden):
+    for n, m, count in golden("nm_layout_counts.txt"):
+        assert len(brute.nm_layouts(int(n), int(m))) == int(count)
+
+
+def test_nm_hand_case():
+    x = np.array([3, -1, 4, 1, -5, 9, 2, -6], dtype=np.float16)
+    keep, vals = sparsify.nm_sparsify(x, 2, 4)
+    assert keep.tolist() == [True, False, True, False, False, True, False, True]
+    assert vals.astype(np.float64).tolist() == [3.0, 4.0, 9.0, -6.0]
+
+
+@pytest.mark.parametrize("n,m", [(1, 4), (2, 4), (3, 4), (2, 8), (4, 8), (7, 8)])
+def test_nm_brute_force(n, m):
+    rng = np.random.default_rng(n * 31 + m)
+    pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 3.0, 0.25], dtype=np.float16)
+    x = pool[rng.integers(0, len(pool), size=4 * m)]
+    keep, vals = sparsify.nm_sparsify(x, n, m)
+    assert np.array_equal(keep, brute.nm_brute(x, n, m))
+    assert np.all(keep.reshape(-1, m).sum(axis=1) == n)
+    assert np.array_equal(vals, x[keep])
+
+
+def test_nm_brute_force_16():
+    rng = np.random.default_rng(5)
+    pool = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0], dtype=np.float16)
+    x = pool[rng.integers(0, len(pool), size=32)]
+    keep = sparsify.nm_sparsify(x, 8, 16)[0]
+    assert np.array_equal(keep, brute.nm_brute(x, 8, 16))
+
+
+def test_nm_whole_row_equals_topk_and_full_is_dense():
+    x = syn.gaussian_f16((2, 64), 1.0, 9)
+    for r in range(2):
+        keep_nm = sparsify.nm_sparsify(x[r], 20, 64)[0]
+        keep_k = sparsify.topk_sparsify(x[r], 20)[0]
+        assert np.array_equal(keep_nm, keep_k)
+    keep, vals = sparsify.nm_sparsify(x, 8, 8)
+    assert keep.all() and np.array_equal(vals, x)
+
+
+# --------------------------------------------------------------------------
+# mask packing
+# --------------------------------------------------------------------------
+
+def test_pack_mask_bit_order():
+    keep = np.zeros(40, dtype=bool)
+    keep[[0, 3, 31, 32, 39]] = True
+    w = sparsify.pack_mask(keep)
+    assert w.tolist() == [(1 << 0) | (1 << 3) | (1 << 31), (1 << 0) | (1 << 7)]
+    assert np.array_equal(sparsify.unpack_mask(w, 40), keep)
+
+
+# --------------------------------------------------------------------------
+# GEMV
+# --------------------------------------------------------------------------
+
+def test_gemv_identity_weight_returns_sparse_activation():
+    d = 64
+    wt = np.eye(d, dtype=np.float16)
+    x = syn.gaussian_f16((d,), 1.0, 2)
+    keep, idx, val, _ = sparsify.threshold_sparsify(x, 0.7)
+    y = gemv.sparse_gemv(wt, idx, val)
+    assert np.array_equal(y, sparsify.apply_mask(x, keep))
+
+
+def test_gemv_rank_one_closed_form():
+    """W = b a^T (W[o][k] = b_o a_k) gives y = b * (a . x_s)."""
+    a = np.array([1, 2, -1, 0.5, 4, -2], dtype=np.float16)
+    b = np.array([1, -3, 0.25, 2], dtype=np.float16)
+    wt = np.outer(a, b).astype(np.float16)  # WT[k][o] = a_k b_o, exact
+    x = np.array([0.5, -1, 2, 0.25, -0.125, 1], dtype=np.float16)
+    keep, idx, val, _ = sparsify.threshold_sparsify(x, 0.5)  # keeps 0,1,2,5
+    y = gemv.sparse_gemv(wt, idx, val)
+    dot = 1 * 0.5 + 2 * -1 + -1 * 2 + -2 * 1
+    assert y.tolist() == [1 * dot, -3 * dot, 0.25 * dot, 2 * dot]
+
+
+def test_gemv_order_free_and_linear():
+    wt = syn.weight_t(128, 200, 3)
+    x = syn.laplace_f16((200,), 1.0, 4)
+    _, idx, val, _ = sparsify.threshold_sparsify(x, 0.69)
+    y = gemv.sparse_gemv(wt, idx, val)
+    perm = np.random.default_rng(0).permutation(len(idx))
+    np.testing.assert_allclose(gemv.sparse_gemv(wt, idx[perm], val[perm]), y, rtol=1e-12, atol=1e-13)
+    y2 = gemv.sparse_gemv(wt, idx, (val.astype(np.float64) * 2))
+    assert np.array_equal(y2, 2 * y)
+
+
+def test_gemv_dense_matches_library_matmul():
+    wt = syn.weight_t(72, 130, 8)
+    x = syn.gaussian_f16((130,), 1.0, 1)
+    ref = x.astype(np.float64) @ wt.astype(np.float64)
+    np.testing.assert_allclose(gemv.dense_gemv(wt, x), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_gemv_flops_formula(golden):
+    for d, flops in golden("gemv_flops.txt"):
+        assert gemv.gemv_flops(int(d), int(d)) == int(flops)
+    assert gemv.gemv_flops(4096, 5504) == 45088768
+
+
+def test_batched_union_and_rows():
+    wt = syn.weight_t(64, 96, 5)
+    X = syn.laplace_f16((4, 96), 1.0, 6)
+    keep = np.stack([sparsify.topk_sparsify(X[b], 40)[0] for b in range(4)])
+    Y = gemv.batched_masked_gemv(wt, X, keep)
+    for b in range(4):
+        ref = sparsify.apply_mask(X[b], keep[b]) @ wt.astype(np.float64)
+        np.testing.assert_allclose(Y[b], ref, rtol=1e-12, atol=1e-13)
+    assert gemv.union_columns(keep) == int(np.count_nonzero(keep.any(axis=0)))
+    assert gemv.union_columns(keep[:1]) == 40
+
+
+# --------------------------------------------------------------------------
+# SiLU / masked SwiGLU down
+# --------------------------------------------------------------------------
+
+def test_silu_closed_forms():
+    assert swiglu.silu(np.array([0.0]))[0] == 0.0
+    # sigmoid(ln 3) = 3/4
+    z = math.log(3.0)
+    assert abs(swiglu.silu(np.array([z]))[0] - 0.75 * z) < 1e-15
+    # SiLU(z) - SiLU(-z) = z (sigmoid(z) + sigmoid(-z) = 1)
+    zs = np.linspace(-12, 12, 97)
+    np.testing.assert_allclose(swiglu.silu(zs) - swiglu.silu(-zs), zs, rtol=1e-13, atol=1e-14)
+    # tails: -> z for large z, -> 0 for very negative z
+    assert abs(swiglu.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(swiglu.silu(np.array([-40.0]))[0]) < 1e-15
+    assert swiglu.silu(np.array([-60000.0]))[0] == 0.0
+
+
+def test_column_norms():
+    wdt = np.array([[3, 4, 0], [1, 0, 0], [0, 0, 0], [1, 1, 1]], dtype=np.float16)
+    c = swiglu.column_norms(wdt)
+    assert c[:3].tolist() == [5.0, 1.0, 0.0]
+    assert abs(c[3] - math.sqrt(3)) < 1e-15
+    w = syn.weight_t(64, 48, 2)
+    np.testing.assert_allclose(swiglu.column_norms(w), np.linalg.norm(w.astype(np.float64), axis=1),
+                               rtol=1e-14)
+
+
+@pytest.mark.parametrize("mode", ["cats", "rana"])
+def test_swiglu_t0_is_dense_down(mode):
+    g, u = syn.swiglu_gate_up(256, 64, 1)
+    wdt = syn.weight_t(48, 256, 12)
+    keep, y = swiglu.masked_swiglu_down(g, u, wdt, 0.0, mode)
+    assert keep.all()
+    h = swiglu.silu(g) * u.astype(np.float64)
+    np.testing.assert_allclose(y, h @ wdt.astype(np.float64), rtol=1e-12, atol=1e-13)
+
+
+def test_swiglu_special_cases():
+    g, u = syn.swiglu_gate_up(512, 256, 2)
+    wdt = syn.weight_t(32, 512, 13)
+    h = swiglu.silu(g) * u.astype(np.float64)
+    # all column norms equal: RaNA is a threshold on |h|
+    c = np.full(512, 2.0)
+    sc = swiglu.scores(g, u, "rana", c)
+    assert np.array_equal(sc >= 0.8, np.abs(h) >= 0.4)
+    # u = 1: RaNA score is the CATS score times the column norm
+    ones = np.ones(512, dtype=np.float16)
+    cn = swiglu.column_norms(wdt)
+    np.testing.assert_allclose(swiglu.scores(g, ones, "rana", cn),
+                               swiglu.scores(g, ones, "cats") * cn, rtol=1e-15)
+    # the masked sum is the dense product of the masked hidden vector
+    keep, y = swiglu.masked_swiglu_down(g, u, wdt, 0.3, "cats")
+    assert np.array_equal(keep, np.abs(swiglu.silu(g)) >= 0.3)
+    np.testing.assert_allclose(y, np.where(keep, h, 0.0) @ wdt.astype(np.float64), rtol=1e-12,
+                               atol=1e-13)
+
+
+@pytest.mark.parametrize("rate", [0.5, 0.7])
+def test_mask_rate_threshold(rate):
+    sc = np.random.default_rng(4).random(1000) + 0.1
+    t = swiglu.threshold_for_mask_rate(sc, rate)
+    assert np.count_nonzero(sc < t) == int(rate * 1000)
+    gap = np.min(np.abs(sc - t))
+    assert gap > 0
+    g, u = syn.swiglu_gate_up(14336, 4096, 0)
+    sc = swiglu.scores(g, u, "cats")
+    t = swiglu.threshold_for_mask_rate(sc, rate)
+    masked = np.count_nonzero(sc < t)
+    assert abs(masked / 14336 - rate) < 0.01
+    assert np.min(np.abs(sc - t)) > 1e-6 * t
+
+
+# --------------------------------------------------------------------------
+# batched N:M matmul
+# --------------------------------------------------------------------------
+
+def test_spmm_full_pattern_is_dense_matmul():
+    X = syn.gaussian_f16((6, 32), 1.0, 3)
+    wt = syn.weight_t(24, 32, 4)
+    keep = sparsify.nm_sparsify(X, 4, 4)[0]
+    Y = spmm.nm_spmm(X, keep, wt)
+    np.testing.assert_allclose(Y, X.astype(np.float64) @ wt.astype(np.float64), rtol=1e-12,
+                               atol=1e-13)
+
+
+def test_spmm_rows_are_sparse_gemvs():
+    X = syn.gaussian_f16((5, 64), 1.0, 6)
+    wt = syn.weight_t(40, 64, 7)
+    keep, vals = sparsify.nm_sparsify(X, 2, 4)
+    Y = spmm.nm_spmm(X, keep, wt)
+    for t in range(5):
+        idx = np.flatnonzero(keep[t])
+        assert np.array_equal(Y[t], gemv.sparse_gemv(wt, idx, vals[t]))
+    assert spmm.nm_spmm_flops(4096, 1024, 1024, 2, 4) == 2 * 4096 * 1024 * 512
+
+
+# --------------------------------------------------------------------------
+# calibration
+# --------------------------------------------------------------------------
+
+def test_quantile_hand_cases():
+    assert calibrate.quantile_linear([1, 2, 3, 4], 0.5) == 2.5
+    assert calibrate.quantile_linear([4, 1, 3, 2], 0.0) == 1.0
+    assert calibrate.quantile_linear([4, 1, 3, 2], 1.0) == 4.0
+    assert calibrate.quantile_linear([5], 0.3) == 5.0
+    assert calibrate.quantile_linear([0, 10], 0.25) == 2.5
+
+
+def test_quantile_matches_numpy_linear():
+    v = np.abs(syn.laplace_f16((10_000,), 1.0, 1).astype(np.float64))
+    for s in (0.0, 0.1, 0.4, 0.5, 0.6, 0.9, 1.0):
+        assert calibrate.quantile_linear(v, s) == pytest.approx(np.quantile(v, s), rel=0, abs=1e-15)
+
+
+@pytest.mark.parametrize("s", [0.4, 0.5, 0.6])
+def test_calibration_closed_forms(s):
+    """|N(0,1)| quantile = Phi^-1((1+s)/2); |Laplace(0,1)| quantile = -ln(1-s)."""
+    n = 10_000
+    xg = syn.calibration_samples("attn_in", n)
+    q = stats.norm.ppf((1 + s) / 2)
+    sigma = math.sqrt(s * (1 - s) / n) / (2 * stats.norm.pdf(q))
+    assert abs(float(calibrate.magnitude_threshold(xg, s)) - q) < 5 * sigma + 1e-3
+    xl = syn.calibration_samples("down_in", n)
+    ql = -math.log(1 - s)
+    sigma_l = math.sqrt(s * (1 - s) / n) / math.exp(-ql)
+    assert abs(float(calibrate.magnitude_threshold(xl, s)) - ql) < 5 * sigma_l + 1e-3
+    # a calibrated threshold gives about the target sparsity on a fresh draw
+    t = float(calibrate.magnitude_threshold(xl, s))
+    x = syn.laplace_f16((11008,), 1.0, 42)
+    keep = sparsify.threshold_sparsify(x, t)[0]
+    assert abs((1 - keep.mean()) - s) < 0.03
