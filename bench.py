@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Headline benchmark: activation-sparse GEMV at 50% sparsity on the
+Llama-2-7B down projection (W 4096 x 11008 fp16, batch 1).
+
+One step = one pass of the hot path over one synthetic activation: magnitude
+threshold (calibrated for 50% sparsity from 10k synthetic samples by the
+library's own calibration kernel) and the sparse GEMV over the surviving
+weight columns -- one fused launch, ``sparse_gemv_threshold``.  The weight
+rotates through distinct copies totalling >= 1 GiB so every step streams its
+kept columns from HBM rather than from the 256 MB Infinity Cache.
+
+Prints one JSON line (rank 0).  ``value`` is microseconds per step (lower is
+better); the roofline object gives the effective HBM bandwidth on the bytes
+the method must touch, against the 8 TB/s MI355X peak.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("sparse GEMV µs + effective HBM GB/s (% of peak) at 50% sparsity, "
+          "4096×11008 fp16")
+HBM_PEAK_GBS = 8000.0
+D_OUT, D_IN = 4096, 11008
+SPARSITY = 0.5
+ROTATION_BYTES = 1 << 30
+GEMV_SOURCE = os.path.join(ROOT, "sparse_input_gemv_amd", "csrc", "gemv.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_gemv_threshold_down_4096x11008.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--tiling", type=int, default=-1, help="GEMV tiling override (tuning)")
+    ap.add_argument("--target-wgs", type=int, default=0, help="GEMV workgroup target (tuning)")
+    ap.add_argument("--only", choices=["fused", "unfused", "dense"], default=None,
+                    help="time a single path (for profiler runs)")
+    return ap.parse_args()
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(bytes_per_launch_hint: float):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None.
+
+    The file records the hash of the GEMV source it was measured on; once
+    the kernel changes the counters no longer apply and None is returned.
+    """
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tr.get("gemv_source_sha256_16") != source_hash(GEMV_SOURCE):
+        return None
+    return tr.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sparse GEMV shards by d_out with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_input_gemv_amd as sa
+    import synthetic as syn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = sa.lib()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    # ---- inputs -------------------------------------------------------------
+    wt0 = torch.from_numpy(syn.weight_t(D_OUT, D_IN, syn.weight_seed("down"))).to(dev)
+    copies = max(2, -(-ROTATION_BYTES // wt0.numel() // 2))
+    rot = [wt0] + [torch.roll(wt0, shifts=997 * i, dims=0).contiguous() for i in range(1, copies)]
+    x_np = syn.activation((D_IN,), "laplace", 0)
+    x = torch.from_numpy(x_np).to(dev)
+    samples = torch.from_numpy(syn.calibration_samples("down_in")).to(dev)
+    t = float(sa.act_calibrate_threshold(samples, SPARSITY).cpu()[0])
+    mask, idx, val, nnz_t = sa.act_sparsify_threshold(x, t)
+    nnz = int(nnz_t.cpu()[0])
+    y = torch.empty((D_OUT,), dtype=torch.float16, device=dev)
+    ws_bytes = sa.workspace_bytes(D_OUT, D_IN, 1)
+    ws = sa.workspace(dev, ws_bytes)
+    if args.tiling >= 0 or args.target_wgs > 0:
+        sa.set_gemv_tuning(args.tiling, args.target_wgs)
+    torch.cuda.synchronize()
+
+    # prebuilt C-ABI argument lists: the timed loop does no Python-side work
+    # beyond the ctypes call
+    fused = [(L.sparse_gemv_threshold,
+              (w.data_ptr(), D_OUT, D_IN, x.data_ptr(), 1, t, y.data_ptr(), ws.data_ptr(),
+               ws.numel(), sptr)) for w in rot]
+    sparsify = (L.act_sparsify_threshold,
+                (x.data_ptr(), 1, D_IN, t, mask.data_ptr(), idx.data_ptr(), val.data_ptr(),
+                 nnz_t.data_ptr(), D_IN, sptr))
+    listed = [(L.sparse_gemv,
+               (w.data_ptr(), D_OUT, D_IN, idx.data_ptr(), val.data_ptr(), nnz_t.data_ptr(), 1,
+                D_IN, y.data_ptr(), ws.data_ptr(), ws.numel(), sptr)) for w in rot]
+    dense = [(L.dense_gemv,
+              (w.data_ptr(), D_OUT, D_IN, x.data_ptr(), 1, y.data_ptr(), ws.data_ptr(),
+               ws.numel(), sptr)) for w in rot]
+
+    def run(calls_per_step, steps):
+        n = len(calls_per_step)
+        for i in range(steps):
+            for f, a in calls_per_step[i % n]:
+                st = f(*a)
+                if st != 0:
+                    raise RuntimeError(L.sa_last_error().decode())
+
+    def timed(calls_per_step, steps, warmup):
+        run(calls_per_step, warmup)
+        torch.cuda.synchronize()
+        if args.graph:
+            g = torch.cuda.CUDAGraph()
+            per = len(calls_per_step)
+            with torch.cuda.graph(g):
+                cap_stream = torch.cuda.current_stream().cuda_stream
+                for f, a in [c for step in calls_per_step for c in step]:
+                    a = list(a)
+                    a[-1] = cap_stream
+                    if f(*a) != 0:
+                        raise RuntimeError(L.sa_last_error().decode())
+            reps = max(1, steps // per)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / (reps * per)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(calls_per_step, steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    paths = {
+        "fused": [[c] for c in fused],
+        "unfused": [[sparsify, c] for c in listed],
+        "dense": [[c] for c in dense],
+    }
+    ms = {}
+    for name in ([args.only] if args.only else ["fused", "unfused", "dense"]):
+        ms[name] = timed(paths[name], args.steps, args.warmup)
+    head = args.only or "fused"
+    ms_step = ms[head]
+    us = ms_step * 1000.0
+
+    # correctness of what was timed: the last output vs the library's own
+    # unfused path is checked by the tests; here only sanity of nnz
+    alg_bytes = 2 * D_OUT * nnz + 2 * D_IN + 2 * D_OUT
+    if head == "dense":
+        alg_bytes = 2 * D_OUT * D_IN + 2 * D_IN + 2 * D_OUT
+    elif head == "unfused":
+        alg_bytes = 2 * D_OUT * nnz + 2 * D_IN + 2 * D_OUT + 6 * nnz
+    achieved = alg_bytes / (us * 1e-6) / 1e9
+    traffic = load_traffic(alg_bytes) if head == "fused" else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(us, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama2-7b down_proj W 4096x11008 fp16, batch 1, magnitude threshold "
+                        "at 50% sparsity (calibrated), x ~ Laplace(0,1)",
+            "d_out": D_OUT, "d_in": D_IN, "batch": 1, "target_sparsity": SPARSITY,
+            "threshold": t, "nnz": nnz, "achieved_sparsity": round(1 - nnz / D_IN, 5),
+            "path": head, "launch": "hip_graph" if args.graph else "stream",
+            "weight_copies": copies, "rotation_bytes": copies * wt0.numel() * 2,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
+        },
+    }
+    if "dense" in ms and head != "dense":
+        out["dense_gemv_us"] = round(ms["dense"] * 1000.0, 3)
+        out["speedup_vs_dense"] = round(ms["dense"] / ms_step, 3)
+        dense_bytes = 2 * D_OUT * D_IN + 2 * D_IN + 2 * D_OUT
+        out["dense_gemv_frac_of_peak"] = round(
+            dense_bytes / (ms["dense"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    if "unfused" in ms and head != "unfused":
+        out["unfused_us"] = round(ms["unfused"] * 1000.0, 3)
+
+    if not args.no_cpu_baseline and not args.only:
+        out["cpu_baseline"] = cpu_baseline(rot[0].cpu().numpy(), x_np, t, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wt, x, t, seconds):
+    """The oracle (fp64 numpy, as it stands) on the same step, single thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gemv, sparsify
+
+    calls, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            keep, idx, val, nnz = sparsify.threshold_sparsify(x, t)
+            gemv.sparse_gemv(wt, idx, val)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or calls >= 200:
+                break
+    return {
+        "value": round(el / calls * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
+        "sample": f"{calls} calls of the full headline step (threshold + sparse GEMV, "
+                  f"4096x11008, 50%) in fp64 numpy, one thread, {el:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

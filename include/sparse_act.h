@@ -1,0 +1,266 @@
+/*
+ * sparse_act.h -- C ABI of libsparse_act.so: activation-sparse linear layers
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The hot path shared by TEAL, Q-Sparse, CATS/RaNA and N:M activation
+ * sparsity: choose the surviving entries of an activation by magnitude, then
+ * multiply only the weight columns of those entries.
+ *
+ * Conventions for every function below
+ * ------------------------------------
+ * - Pointers are DEVICE pointers owned by the caller unless stated otherwise.
+ *   The library allocates nothing; scratch space comes in through `ws`.
+ * - fp16 data is passed as uint16_t (IEEE binary16 bit patterns).
+ * - Weights are stored transposed: WT[d_in][d_out] row-major, i.e. W
+ *   column-major, so the weight column multiplied by activation entry k is
+ *   the contiguous run WT + k*d_out of 2*d_out bytes.
+ * - Activations are row-major [rows][d].  Bitmasks are uint32 words
+ *   [rows][ceil(d/32)], bit j of word w <-> entry 32*w + j, padding bits 0.
+ * - Index lists are int32, ascending, rows of length `cap`.
+ * - `stream` is a hipStream_t (NULL = the null stream).  Every call enqueues
+ *   its work and returns; outputs are valid once the stream has reached the
+ *   call.  Nothing blocks the host and nothing is copied to the host.
+ * - Accumulation is fp32; fp16 outputs are rounded to nearest even.
+ * - Return value is a status code (SA_OK on success).  Argument errors are
+ *   detected on the host before any HIP call and leave outputs untouched;
+ *   sa_last_error() then describes the first failing check for the calling
+ *   thread.  No C++ exception crosses this boundary.
+ * - A workspace `ws` (sized by sa_workspace_bytes, 256-byte aligned) holds
+ *   per-call partial sums; its contents on entry do not matter.  Calls that
+ *   share one workspace must be ordered on one stream: concurrent calls race.
+ * - rows == 0 (or batch == 0, T == 0) is a valid empty call and does nothing.
+ *
+ * Pages cited (by title; "replies" = the authors' answers to reviewers):
+ *   [QS]   Q-Sparse: All Large Language Models can be Fully
+ *          Sparsely-Activated (replies)
+ *   [TEAL] TEAL: Training-Free Activation Sparsity in Large Language Models
+ *          (README)
+ *   [RaNA] Adaptive Rank Allocation: Speeding Up Modern Transformers with
+ *          RaNA Adapters (replies)
+ *   [NM]   Motivating Next-Gen Accelerators with Flexible (N:M) Activation
+ *          Sparsity via Benchmarking Lightweight Post-Training
+ *          Sparsification Approaches (summary)
+ */
+#ifndef SPARSE_ACT_H
+#define SPARSE_ACT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status ------------------------------------------------------------ */
+#define SA_OK 0
+#define SA_ERR_INVALID_ARG 1 /* a pointer, size, alignment or value check failed */
+#define SA_ERR_UNSUPPORTED 2 /* valid but outside what the kernels implement */
+#define SA_ERR_WORKSPACE 3   /* ws is NULL or smaller than sa_workspace_bytes() */
+#define SA_ERR_HIP 4         /* the HIP runtime reported an error at launch */
+
+#define SA_MAX_BATCH 8       /* rows per call of the GEMV family */
+
+/* Static string naming a status code. */
+const char* sa_status_string(int status);
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char* sa_last_error(void);
+/* ABI version (major*100 + minor). */
+int sa_version(void);
+
+/* ---- sparsifiers ---------------------------------------------------------- */
+
+/*
+ * act_sparsify_threshold -- per-tensor magnitude threshold.
+ * [TEAL] Abstract: hidden-state entries are zeroed by magnitude with a
+ * calibrated threshold; the comparator is >=, as in the CATS/RaNA masks
+ * ([RaNA] Q3).  keep_i = (|x_i| >= t) && (x_i != 0), so nnz equals the number
+ * of nonzeros of the sparsified row and the sparsity is 1 - nnz/d ([QS]
+ * answer defining activation sparsity).
+ *
+ *   x     [rows][d] fp16            t    fp32 threshold, finite, >= 0
+ *   mask  [rows][ceil(d/32)] or NULL
+ *   idx   [rows][cap] int32: kept indices, ascending (first nnz valid)
+ *   val   [rows][cap] fp16:  x at those indices
+ *   nnz   [rows] int32
+ * Requires d >= 1, cap >= d, d <= 65536.  x must be 2-byte aligned.
+ */
+int act_sparsify_threshold(const uint16_t* x, int64_t rows, int64_t d, float t,
+                           uint32_t* mask, int32_t* idx, uint16_t* val,
+                           int32_t* nnz, int64_t cap, void* stream);
+
+/*
+ * act_sparsify_topk -- per-token Top-K by magnitude.
+ * [QS] answer comparing with MoE: per token, entries of smaller magnitude are
+ * pruned.  Exactly k entries survive per row: the k largest |x|, ties to the
+ * lower index (fp16 magnitudes compared exactly; -0 == +0).  Outputs as for
+ * act_sparsify_threshold with nnz[r] = k.
+ * Requires 0 <= k <= d, cap >= max(k,1), 1 <= d <= 65536.
+ */
+int act_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k,
+                      uint32_t* mask, int32_t* idx, uint16_t* val,
+                      int32_t* nnz, int64_t cap, void* stream);
+
+/*
+ * act_sparsify_nm -- N:M activation sparsity.
+ * [QS] answer on batched inference (Block Q-Sparse): N:M over M consecutive
+ * entries; [NM] section 2 (methodology): N nonzeros kept per block of M,
+ * scored by |activation|.  Per aligned group of m entries of each row the n
+ * largest |x| survive, ties to the lower position.
+ *
+ *   x     [rows][d] fp16, 16-byte aligned
+ *   mask  [rows][d/32]: exactly n bits set per group
+ *   val   [rows][d*n/m] fp16: kept values, group by group, in position order
+ * Requires m in {4,8,16,32}, 1 <= n <= m, d % 32 == 0, d >= 32.
+ */
+int act_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
+                    uint32_t* mask, uint16_t* val, void* stream);
+
+/*
+ * act_calibrate_threshold -- threshold for a target sparsity from samples.
+ * [TEAL] Inference Usage and Accuracy Usage step 1: thresholds come from
+ * per-layer activation histograms.  The histogram here has one bin per fp16
+ * magnitude, so the result is the exact linearly interpolated s-quantile of
+ * |samples|: with the magnitudes sorted v_0 <= ... <= v_{n-1}, h = (n-1)s,
+ * lo = floor(h), t = v_lo + (h - lo)(v_{lo+1} - v_lo) in fp64, rounded to fp32.
+ *
+ *   samples [n] fp16 (device)    s in [0,1]    t_out: one fp32 (device)
+ * Requires 1 <= n <= 2^31 - 1.  NaN samples are outside the contract.
+ */
+int act_calibrate_threshold(const uint16_t* samples, int64_t n, double s,
+                            float* t_out, void* stream);
+
+/* ---- sparse-input GEMV family ------------------------------------------- */
+
+/*
+ * Bytes of workspace needed by the GEMV family (sparse_gemv,
+ * sparse_gemv_threshold, masked_gemv, dense_gemv, masked_swiglu_down) for
+ * an output length d_out, input length d_in and up to `batch` rows.  The
+ * same size serves every call whose sizes do not exceed these.
+ */
+size_t sa_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch);
+
+/*
+ * sparse_gemv -- y[b] = sum_{j < nnz[b]} W[:, idx[b][j]] * val[b][j].
+ * [RaNA] Q5.1: with a sparse activation the products with the weight columns
+ * of its zero entries are skipped; [QS] answer A3: the matmul costs
+ * 2*d_out*nnz FLOPs.  Only the listed rows of WT are read.
+ *
+ *   wt  [d_in][d_out] fp16, 16-byte aligned, d_out % 8 == 0
+ *   idx [batch][cap] int32 ascending, values in [0, d_in)
+ *   val [batch][cap] fp16; nnz [batch] int32 (device), 0 <= nnz <= min(cap,d_in)
+ *   y   [batch][d_out] fp16, 16-byte aligned
+ * Requires 1 <= batch <= SA_MAX_BATCH.  With batch > 1 every weight row in
+ * the union of the lists is read once for all rows.  Out-of-range indices or
+ * counts in device memory are clamped/skipped by the kernel, never faulted.
+ */
+int sparse_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in,
+                const int32_t* idx, const uint16_t* val, const int32_t* nnz,
+                int64_t batch, int64_t cap, uint16_t* y, void* ws,
+                size_t ws_bytes, void* stream);
+
+/*
+ * sparse_gemv_threshold -- the threshold sparsifier and the sparse GEMV in
+ * one launch: y[b] = W (keep_b .* x[b]) with keep as in
+ * act_sparsify_threshold.  Each workgroup thresholds its own slice of x and
+ * streams only the kept rows of WT.
+ *   x [batch][d_in] fp16 (2-byte aligned); other arguments as sparse_gemv.
+ */
+int sparse_gemv_threshold(const uint16_t* wt, int64_t d_out, int64_t d_in,
+                          const uint16_t* x, int64_t batch, float t,
+                          uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * masked_gemv -- y[b] = W (mask_b .* x[b]) for a bitmask from any
+ * sparsifier (the "masked GEMV" of [RaNA] Q5.1/Q7).  With batch > 1 the
+ * union of the masks decides which weight rows are read.
+ *   x [batch][d_in] fp16; mask [batch][ceil(d_in/32)].
+ */
+int masked_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in,
+                const uint16_t* x, const uint32_t* mask, int64_t batch,
+                uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * masked_swiglu_down -- CATS / RaNA masked down projection of a SwiGLU MLP.
+ * [RaNA] Q3 (Eqn. 12 for RaNA), Q5.1: with s = SiLU(g) = g/(1+exp(-g)) and
+ * h = s*u,
+ *   mode 0 (CATS): keep i iff |s_i| >= t
+ *   mode 1 (RaNA): keep i iff |h_i| * colnorm_i >= t, colnorm_i = ||W_down[:,i]||
+ * and y = sum_{kept i} W_down[:, i] h_i.  The mask decision is taken in fp64.
+ *
+ *   g, u    [d_ff] fp16 (gate and up projection outputs)
+ *   wdt     [d_ff][d_model] fp16 = W_down transposed, 16-byte aligned
+ *   colnorm [d_ff] fp64 (from weight_col_norms); may be NULL for mode 0
+ *   t       fp64 threshold, finite, >= 0
+ *   y       [d_model] fp16; mask [ceil(d_ff/32)] or NULL; nnz [1] or NULL
+ * Requires d_model % 8 == 0.
+ */
+int masked_swiglu_down(const uint16_t* g, const uint16_t* u,
+                       const uint16_t* wdt, const double* colnorm,
+                       int64_t d_ff, int64_t d_model, double t, int mode,
+                       uint16_t* y, uint32_t* mask, int32_t* nnz, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * weight_col_norms -- out[k] = ||WT[k][:]||_2 in fp64 (the norm of the weight
+ * column multiplied by activation entry k; colnorm of [RaNA] Eqn. 12).
+ *   wt [d_in][d_out] fp16 16-byte aligned, d_out % 8 == 0; out [d_in] fp64.
+ */
+int weight_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out,
+                     double* out, void* stream);
+
+/*
+ * dense_gemv -- y[b] = W x[b] over every column: the dense baseline, same
+ * layout and kernel skeleton as the sparse path.  Arguments as masked_gemv.
+ */
+int dense_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in,
+               const uint16_t* x, int64_t batch, uint16_t* y, void* ws,
+               size_t ws_bytes, void* stream);
+
+/* ---- batched N:M matmul ---------------------------------------------------- */
+
+/*
+ * nm_act_spmm -- Y[t] = W (mask_t .* x_t) for T tokens whose activations are
+ * N:M sparse, given in the compressed form act_sparsify_nm produces.
+ * [QS] answer on batched inference: N:M activation sparsity for large
+ * batches, measured against a dense matmul.  Runs on MFMA; 2:4 uses the
+ * gfx950 sparse MFMA.
+ *
+ *   xval [T][d_in*n/m] fp16;  mask [T][d_in/32] (exactly n bits per group)
+ *   wt   [d_in][d_out] fp16;  y [T][d_out] fp16
+ * Requires m in {4,8,16,32}, 1 <= n <= m, d_in % 32 == 0, d_out % 8 == 0,
+ * wt/y 16-byte aligned.
+ */
+int nm_act_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
+                int64_t d_in, int n, int m, const uint16_t* wt, int64_t d_out,
+                uint16_t* y, void* stream);
+
+/*
+ * dense_gemm -- Y[t][o] = sum_k X[t][k] WT[k][o] (Y = X W^T) on MFMA: the
+ * dense baseline of nm_act_spmm.
+ *   x [T][d_in] fp16 (d_in % 8 == 0, 16-byte aligned); wt as above;
+ *   y [T][d_out] fp16.
+ */
+int dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
+               int64_t d_out, uint16_t* y, void* stream);
+
+/* ---- tuning hook -------------------------------------------------------- */
+
+/*
+ * Process-wide launch override for the GEMV family, for tuning sweeps:
+ * `tiling` picks one of the compiled tile shapes (-1 = automatic) and
+ * `target_wgs` the number of workgroups of the split-K stream launch to aim
+ * for (0 = automatic).  Every tiling computes the same result up to fp32
+ * summation order.
+ * Returns SA_ERR_INVALID_ARG for an unknown tiling.  Not thread-safe.
+ */
+int sa_set_gemv_tuning(int tiling, int target_wgs);
+/* Describe tiling `i` (tile_o, threads, unroll); tile_o is negative for a
+ * full-K tiling (one launch, no split of d_in).  Returns SA_ERR_INVALID_ARG
+ * past the last one.  Output pointers are HOST pointers (may be NULL). */
+int sa_gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ACT_H */

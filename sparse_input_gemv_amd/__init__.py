@@ -1,0 +1,348 @@
+"""Activation-sparse linear layers on AMD Instinct MI355X (gfx950).
+
+Python binding of ``libsparse_act.so`` (ctypes).  It only marshals
+arguments: every step runs in the library's HIP kernels, on the caller's
+current torch stream.  torch supplies device memory and streams; the C ABI is
+declared in ``include/sparse_act.h``, and each wrapper below has the name of
+the C function it calls.
+
+Layouts: weights are ``WT[d_in][d_out]`` fp16 (W column-major); activations
+are fp16 ``[rows][d]``; bitmasks are int32 tensors holding the uint32 words
+``[rows][ceil(d/32)]`` (bit ``j`` of word ``w`` is entry ``32*w + j``).
+
+There is no CPU fallback: if the library is missing, or a tensor is not on a
+GPU, these functions raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "SparseActError", "lib", "workspace",
+    "act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm",
+    "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold", "masked_gemv",
+    "dense_gemv", "masked_swiglu_down", "weight_col_norms", "nm_act_spmm", "dense_gemm",
+    "set_gemv_tuning", "gemv_tiling_info", "workspace_bytes", "MAX_BATCH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_act.so")
+MAX_BATCH = 8
+
+_vp, _i64, _i32, _f32, _f64, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+
+_SIGNATURES = {
+    "sa_status_string": (ctypes.c_char_p, [_i32]),
+    "sa_last_error": (ctypes.c_char_p, []),
+    "sa_version": (_i32, []),
+    "act_sparsify_threshold": (_i32, [_vp, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "act_sparsify_topk": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "act_sparsify_nm": (_i32, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp]),
+    "act_calibrate_threshold": (_i32, [_vp, _i64, _f64, _vp, _vp]),
+    "sa_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "sparse_gemv": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "sparse_gemv_threshold": (_i32, [_vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _sz, _vp]),
+    "masked_gemv": (_i32, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "dense_gemv": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "masked_swiglu_down": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _f64, _i32, _vp, _vp, _vp,
+                                  _vp, _sz, _vp]),
+    "weight_col_norms": (_i32, [_vp, _i64, _i64, _vp, _vp]),
+    "nm_act_spmm": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp]),
+    "dense_gemm": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "sa_set_gemv_tuning": (_i32, [_i32, _i32]),
+    "sa_gemv_tiling_info": (_i32, [_i32, _vp, _vp, _vp]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class SparseActError(RuntimeError):
+    """A C entry point returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {detail or 'error'} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library, with argument types declared."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(
+                        f"{LIB_PATH} is not built; run `python -m sparse_input_gemv_amd.build`")
+                L = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in _SIGNATURES.items():
+                    f = getattr(L, name)
+                    f.restype = res
+                    f.argtypes = args
+                _lib = L
+    return _lib
+
+
+def _check(status: int, fn: str) -> None:
+    if status != 0:
+        detail = lib().sa_last_error().decode(errors="replace")
+        raise SparseActError(fn, status, detail)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a torch tensor on a GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+_ws: dict = {}
+
+
+def workspace_bytes(d_out: int, d_in: int, batch: int = 1) -> int:
+    return int(lib().sa_workspace_bytes(d_out, d_in, batch))
+
+
+def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """Per-device workspace for partial sums, grown on demand and reused.
+
+    Calls on one device share it, so they must be ordered on one stream.
+    """
+    key = torch.device(device).index or 0
+    ws = _ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws[key] = ws
+    return ws
+
+
+def _rows(x: torch.Tensor):
+    return (1, x.shape[0]) if x.dim() == 1 else (x.shape[0], x.shape[1])
+
+
+# ---- sparsifiers ------------------------------------------------------------
+
+def act_sparsify_threshold(x: torch.Tensor, t: float, with_mask: bool = True, cap: int | None = None):
+    """Returns ``(mask, idx, val, nnz)``; see the C declaration."""
+    _dev(x, "x", torch.float16)
+    rows, d = _rows(x)
+    cap = d if cap is None else cap
+    dev = x.device
+    shape = (rows,) if x.dim() == 2 else ()
+    mask = torch.empty(shape + ((d + 31) // 32,), dtype=torch.int32, device=dev) if with_mask else None
+    idx = torch.empty(shape + (cap,), dtype=torch.int32, device=dev)
+    val = torch.empty(shape + (cap,), dtype=torch.float16, device=dev)
+    nnz = torch.empty((rows,), dtype=torch.int32, device=dev)
+    _check(lib().act_sparsify_threshold(_ptr(x), rows, d, float(t), _ptr(mask), _ptr(idx), _ptr(val),
+                                        _ptr(nnz), cap, _stream(x)), "act_sparsify_threshold")
+    return mask, idx, val, nnz
+
+
+def act_sparsify_topk(x: torch.Tensor, k: int, with_mask: bool = True, cap: int | None = None):
+    """Returns ``(mask, idx, val, nnz)`` with exactly ``k`` kept per row."""
+    _dev(x, "x", torch.float16)
+    rows, d = _rows(x)
+    cap = max(k, 1) if cap is None else cap
+    dev = x.device
+    shape = (rows,) if x.dim() == 2 else ()
+    mask = torch.empty(shape + ((d + 31) // 32,), dtype=torch.int32, device=dev) if with_mask else None
+    idx = torch.empty(shape + (cap,), dtype=torch.int32, device=dev)
+    val = torch.empty(shape + (cap,), dtype=torch.float16, device=dev)
+    nnz = torch.empty((rows,), dtype=torch.int32, device=dev)
+    _check(lib().act_sparsify_topk(_ptr(x), rows, d, int(k), _ptr(mask), _ptr(idx), _ptr(val),
+                                   _ptr(nnz), cap, _stream(x)), "act_sparsify_topk")
+    return mask, idx, val, nnz
+
+
+def act_sparsify_nm(x: torch.Tensor, n: int, m: int):
+    """Returns ``(mask, val)``: bitmask words and the compressed kept values."""
+    _dev(x, "x", torch.float16)
+    rows, d = _rows(x)
+    shape = (rows,) if x.dim() == 2 else ()
+    mask = torch.empty(shape + (d // 32,), dtype=torch.int32, device=x.device)
+    val = torch.empty(shape + (d * n // m,), dtype=torch.float16, device=x.device)
+    _check(lib().act_sparsify_nm(_ptr(x), rows, d, n, m, _ptr(mask), _ptr(val), _stream(x)),
+           "act_sparsify_nm")
+    return mask, val
+
+
+def act_calibrate_threshold(samples: torch.Tensor, s: float) -> torch.Tensor:
+    """Threshold (fp32, one-element device tensor) for sparsity ``s``."""
+    _dev(samples, "samples", torch.float16)
+    out = torch.empty((1,), dtype=torch.float32, device=samples.device)
+    _check(lib().act_calibrate_threshold(_ptr(samples), samples.numel(), float(s), _ptr(out),
+                                         _stream(samples)), "act_calibrate_threshold")
+    return out
+
+
+# ---- GEMV family ------------------------------------------------------------
+
+def _gemv_out(wt, batch, squeeze, y):
+    d_out = wt.shape[1]
+    if y is None:
+        y = torch.empty((batch, d_out), dtype=torch.float16, device=wt.device)
+    else:
+        _dev(y, "y", torch.float16)
+    return y
+
+
+def _ret(y, squeeze):
+    return y[0] if squeeze else y
+
+
+def sparse_gemv(wt: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, nnz: torch.Tensor,
+                y: torch.Tensor | None = None):
+    """``y[b] = W[:, idx[b, :nnz[b]]] @ val[b, :nnz[b]]`` (lists from a sparsifier)."""
+    _dev(wt, "wt", torch.float16)
+    _dev(idx, "idx", torch.int32)
+    _dev(val, "val", torch.float16)
+    _dev(nnz, "nnz", torch.int32)
+    squeeze = idx.dim() == 1
+    batch, cap = _rows(idx)
+    d_in, d_out = wt.shape
+    y = _gemv_out(wt, batch, squeeze, y)
+    nb = workspace_bytes(d_out, d_in, batch)
+    ws = workspace(wt.device, nb)
+    _check(lib().sparse_gemv(_ptr(wt), d_out, d_in, _ptr(idx), _ptr(val), _ptr(nnz), batch, cap,
+                             _ptr(y), _ptr(ws), ws.numel(), _stream(wt)), "sparse_gemv")
+    return _ret(y, squeeze)
+
+
+def sparse_gemv_threshold(wt: torch.Tensor, x: torch.Tensor, t: float,
+                          y: torch.Tensor | None = None):
+    """Threshold and sparse GEMV in one launch: ``y = W (keep ⊙ x)``."""
+    _dev(wt, "wt", torch.float16)
+    _dev(x, "x", torch.float16)
+    squeeze = x.dim() == 1
+    batch, d_in = _rows(x)
+    d_out = wt.shape[1]
+    y = _gemv_out(wt, batch, squeeze, y)
+    ws = workspace(wt.device, workspace_bytes(d_out, d_in, batch))
+    _check(lib().sparse_gemv_threshold(_ptr(wt), d_out, d_in, _ptr(x), batch, float(t), _ptr(y),
+                                       _ptr(ws), ws.numel(), _stream(wt)), "sparse_gemv_threshold")
+    return _ret(y, squeeze)
+
+
+def masked_gemv(wt: torch.Tensor, x: torch.Tensor, mask: torch.Tensor,
+                y: torch.Tensor | None = None):
+    """``y[b] = W (mask_b ⊙ x_b)`` for bitmask words ``mask``."""
+    _dev(wt, "wt", torch.float16)
+    _dev(x, "x", torch.float16)
+    _dev(mask, "mask", torch.int32)
+    squeeze = x.dim() == 1
+    batch, d_in = _rows(x)
+    d_out = wt.shape[1]
+    y = _gemv_out(wt, batch, squeeze, y)
+    ws = workspace(wt.device, workspace_bytes(d_out, d_in, batch))
+    _check(lib().masked_gemv(_ptr(wt), d_out, d_in, _ptr(x), _ptr(mask), batch, _ptr(y), _ptr(ws),
+                             ws.numel(), _stream(wt)), "masked_gemv")
+    return _ret(y, squeeze)
+
+
+def dense_gemv(wt: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None):
+    """Dense baseline ``y = W x`` on the same kernel skeleton."""
+    _dev(wt, "wt", torch.float16)
+    _dev(x, "x", torch.float16)
+    squeeze = x.dim() == 1
+    batch, d_in = _rows(x)
+    d_out = wt.shape[1]
+    y = _gemv_out(wt, batch, squeeze, y)
+    ws = workspace(wt.device, workspace_bytes(d_out, d_in, batch))
+    _check(lib().dense_gemv(_ptr(wt), d_out, d_in, _ptr(x), batch, _ptr(y), _ptr(ws), ws.numel(),
+                            _stream(wt)), "dense_gemv")
+    return _ret(y, squeeze)
+
+
+def masked_swiglu_down(g: torch.Tensor, u: torch.Tensor, wdt: torch.Tensor, t: float, mode: str,
+                       colnorm: torch.Tensor | None = None, y: torch.Tensor | None = None,
+                       with_mask: bool = True):
+    """CATS (``mode='cats'``) or RaNA (``mode='rana'``) masked down projection.
+
+    Returns ``(y, mask, nnz)``; ``mask``/``nnz`` are None when not requested.
+    """
+    _dev(g, "g", torch.float16)
+    _dev(u, "u", torch.float16)
+    _dev(wdt, "wdt", torch.float16)
+    m = {"cats": 0, "rana": 1}[mode]
+    if colnorm is not None:
+        _dev(colnorm, "colnorm", torch.float64)
+    d_ff, d_model = wdt.shape
+    if y is None:
+        y = torch.empty((d_model,), dtype=torch.float16, device=wdt.device)
+    mask = torch.empty(((d_ff + 31) // 32,), dtype=torch.int32, device=wdt.device) if with_mask else None
+    nnz = torch.empty((1,), dtype=torch.int32, device=wdt.device) if with_mask else None
+    ws = workspace(wdt.device, workspace_bytes(d_model, d_ff, 1))
+    _check(lib().masked_swiglu_down(_ptr(g), _ptr(u), _ptr(wdt), _ptr(colnorm), d_ff, d_model,
+                                    float(t), m, _ptr(y), _ptr(mask), _ptr(nnz), _ptr(ws),
+                                    ws.numel(), _stream(wdt)), "masked_swiglu_down")
+    return y, mask, nnz
+
+
+def weight_col_norms(wt: torch.Tensor) -> torch.Tensor:
+    """fp64 ``||WT[k, :]||_2`` per input index ``k``."""
+    _dev(wt, "wt", torch.float16)
+    d_in, d_out = wt.shape
+    out = torch.empty((d_in,), dtype=torch.float64, device=wt.device)
+    _check(lib().weight_col_norms(_ptr(wt), d_in, d_out, _ptr(out), _stream(wt)),
+           "weight_col_norms")
+    return out
+
+
+# ---- batched matmuls ---------------------------------------------------------
+
+def nm_act_spmm(xval: torch.Tensor, mask: torch.Tensor, n: int, m: int, wt: torch.Tensor,
+                y: torch.Tensor | None = None):
+    """``Y = (mask ⊙ X) W^T`` from the compressed N:M activations."""
+    _dev(xval, "xval", torch.float16)
+    _dev(mask, "mask", torch.int32)
+    _dev(wt, "wt", torch.float16)
+    T = mask.shape[0]
+    d_in, d_out = wt.shape
+    if y is None:
+        y = torch.empty((T, d_out), dtype=torch.float16, device=wt.device)
+    _check(lib().nm_act_spmm(_ptr(xval), _ptr(mask), T, d_in, n, m, _ptr(wt), d_out, _ptr(y),
+                             _stream(wt)), "nm_act_spmm")
+    return y
+
+
+def dense_gemm(x: torch.Tensor, wt: torch.Tensor, y: torch.Tensor | None = None):
+    """Dense baseline ``Y = X W^T`` on MFMA."""
+    _dev(x, "x", torch.float16)
+    _dev(wt, "wt", torch.float16)
+    T, d_in = x.shape
+    d_out = wt.shape[1]
+    if y is None:
+        y = torch.empty((T, d_out), dtype=torch.float16, device=wt.device)
+    _check(lib().dense_gemm(_ptr(x), T, d_in, _ptr(wt), d_out, _ptr(y), _stream(wt)), "dense_gemm")
+    return y
+
+
+# ---- tuning -------------------------------------------------------------------
+
+def set_gemv_tuning(tiling: int = -1, target_wgs: int = 0) -> None:
+    _check(lib().sa_set_gemv_tuning(tiling, target_wgs), "sa_set_gemv_tuning")
+
+
+def gemv_tiling_info(i: int):
+    """``(tile_o, threads, unroll)`` of compiled tiling ``i``, or None past the end."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = lib().sa_gemv_tiling_info(i, ctypes.addressof(a), ctypes.addressof(b), ctypes.addressof(c))
+    if st != 0:
+        return None
+    return a.value, b.value, c.value

@@ -1,0 +1,275 @@
+// extern "C" entry points of libsparse_act.so (declared in
+// include/sparse_act.h): validate on the host, then enqueue on the caller's
+// stream.  No allocation, no synchronisation, no exceptions across the ABI.
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/sparse_act.h"
+#include "launch.hpp"
+#include "validate.hpp"
+
+namespace {
+
+int hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return SA_OK;
+  sa::set_error("%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  return SA_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID_ARG: return "SA_ERR_INVALID_ARG";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
+    case SA_ERR_HIP: return "SA_ERR_HIP";
+    default: return "SA_ERR_UNKNOWN";
+  }
+}
+
+const char* sa_last_error(void) { return sa::last_error(); }
+
+int sa_version(void) { return 100; }
+
+int act_sparsify_threshold(const uint16_t* x, int64_t rows, int64_t d, float t, uint32_t* mask,
+                           int32_t* idx, uint16_t* val, int32_t* nnz, int64_t cap,
+                           void* stream) {
+  sa::clear_error();
+  int st = sa::check_threshold(x, rows, d, t, mask, idx, val, nnz, cap);
+  if (st != SA_OK) return st;
+  if (rows == 0) return SA_OK;
+  return hip_status(
+      sa::launch_sparsify_threshold(x, rows, d, t, mask, idx, val, nnz, cap, as_stream(stream)),
+      "act_sparsify_threshold");
+}
+
+int act_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k, uint32_t* mask,
+                      int32_t* idx, uint16_t* val, int32_t* nnz, int64_t cap, void* stream) {
+  sa::clear_error();
+  int st = sa::check_topk(x, rows, d, k, mask, idx, val, nnz, cap);
+  if (st != SA_OK) return st;
+  if (rows == 0) return SA_OK;
+  return hip_status(
+      sa::launch_sparsify_topk(x, rows, d, k, mask, idx, val, nnz, cap, as_stream(stream)),
+      "act_sparsify_topk");
+}
+
+int act_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m, uint32_t* mask,
+                    uint16_t* val, void* stream) {
+  sa::clear_error();
+  int st = sa::check_nm(x, rows, d, n, m, mask, val);
+  if (st != SA_OK) return st;
+  if (rows == 0) return SA_OK;
+  return hip_status(sa::launch_sparsify_nm(x, rows, d, n, m, mask, val, as_stream(stream)),
+                    "act_sparsify_nm");
+}
+
+int act_calibrate_threshold(const uint16_t* samples, int64_t n, double s, float* t_out,
+                            void* stream) {
+  sa::clear_error();
+  int st = sa::check_calibrate(samples, n, s, t_out);
+  if (st != SA_OK) return st;
+  return hip_status(sa::launch_calibrate(samples, n, s, t_out, as_stream(stream)),
+                    "act_calibrate_threshold");
+}
+
+size_t sa_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
+  if (d_out < 1 || d_in < 1) return 0;
+  if (batch < 1) batch = 1;
+  if (batch > SA_MAX_BATCH) batch = SA_MAX_BATCH;
+  return sa::gemv_workspace_bytes(d_out, d_in, batch);
+}
+
+static int run_gemv(const sa::GemvCall& c, const char* fn, void* stream) {
+  if (c.batch == 0) return SA_OK;
+  return hip_status(sa::launch_gemv(c, as_stream(stream)), fn);
+}
+
+int sparse_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in, const int32_t* idx,
+                const uint16_t* val, const int32_t* nnz, int64_t batch, int64_t cap,
+                uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_out, d_in, batch < 1 ? 1 : batch);
+  int st = sa::check_gemv_common(wt, d_out, d_in, batch, y, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_sparse_gemv(idx, val, nnz, batch, cap);
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeList;
+  c.wt = wt;
+  c.d_out = d_out;
+  c.d_in = d_in;
+  c.batch = (int)batch;
+  c.idx = idx;
+  c.val = val;
+  c.nnz = nnz;
+  c.cap = cap;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return run_gemv(c, "sparse_gemv", stream);
+}
+
+int sparse_gemv_threshold(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint16_t* x,
+                          int64_t batch, float t, uint16_t* y, void* ws, size_t ws_bytes,
+                          void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_out, d_in, batch < 1 ? 1 : batch);
+  int st = sa::check_gemv_common(wt, d_out, d_in, batch, y, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_activation(x, "sparse_gemv_threshold: x");
+  if (st == SA_OK) st = sa::check_threshold_value(t);
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeThreshold;
+  c.wt = wt;
+  c.d_out = d_out;
+  c.d_in = d_in;
+  c.batch = (int)batch;
+  c.x = x;
+  c.t = t;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return run_gemv(c, "sparse_gemv_threshold", stream);
+}
+
+int masked_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint16_t* x,
+                const uint32_t* mask, int64_t batch, uint16_t* y, void* ws, size_t ws_bytes,
+                void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_out, d_in, batch < 1 ? 1 : batch);
+  int st = sa::check_gemv_common(wt, d_out, d_in, batch, y, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_activation(x, "masked_gemv: x");
+  if (st == SA_OK && (mask == nullptr || (reinterpret_cast<uintptr_t>(mask) & 3u) != 0)) {
+    sa::set_error("masked_gemv: mask must be a non-NULL 4-byte aligned pointer");
+    st = SA_ERR_INVALID_ARG;
+  }
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeMasked;
+  c.wt = wt;
+  c.d_out = d_out;
+  c.d_in = d_in;
+  c.batch = (int)batch;
+  c.x = x;
+  c.xmask = mask;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return run_gemv(c, "masked_gemv", stream);
+}
+
+int dense_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint16_t* x, int64_t batch,
+               uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_out, d_in, batch < 1 ? 1 : batch);
+  int st = sa::check_gemv_common(wt, d_out, d_in, batch, y, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_activation(x, "dense_gemv: x");
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeDense;
+  c.wt = wt;
+  c.d_out = d_out;
+  c.d_in = d_in;
+  c.batch = (int)batch;
+  c.x = x;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return run_gemv(c, "dense_gemv", stream);
+}
+
+int masked_swiglu_down(const uint16_t* g, const uint16_t* u, const uint16_t* wdt,
+                       const double* colnorm, int64_t d_ff, int64_t d_model, double t, int mode,
+                       uint16_t* y, uint32_t* mask, int32_t* nnz, void* ws, size_t ws_bytes,
+                       void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_model, d_ff, 1);
+  int st = sa::check_gemv_common(wdt, d_model, d_ff, 1, y, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_swiglu(g, u, colnorm, d_ff, t, mode);
+  if (st == SA_OK && ((reinterpret_cast<uintptr_t>(mask) & 3u) != 0 ||
+                      (reinterpret_cast<uintptr_t>(nnz) & 3u) != 0)) {
+    sa::set_error("masked_swiglu_down: mask and nnz must be 4-byte aligned");
+    st = SA_ERR_INVALID_ARG;
+  }
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeSwiglu;
+  c.wt = wdt;
+  c.d_out = d_model;
+  c.d_in = d_ff;
+  c.batch = 1;
+  c.g = g;
+  c.u = u;
+  c.colnorm = colnorm;
+  c.t64 = t;
+  c.swiglu_mode = mode;
+  c.out_mask = mask;
+  c.out_nnz = nnz;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return run_gemv(c, "masked_swiglu_down", stream);
+}
+
+int weight_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* out,
+                     void* stream) {
+  sa::clear_error();
+  int st = sa::check_col_norms(wt, d_in, d_out, out);
+  if (st != SA_OK) return st;
+  if (d_in == 0) return SA_OK;
+  return hip_status(sa::launch_col_norms(wt, d_in, d_out, out, as_stream(stream)),
+                    "weight_col_norms");
+}
+
+int nm_act_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in, int n,
+                int m, const uint16_t* wt, int64_t d_out, uint16_t* y, void* stream) {
+  sa::clear_error();
+  int st = sa::check_nm_spmm(xval, mask, T, d_in, n, m, wt, d_out, y);
+  if (st != SA_OK) return st;
+  if (T == 0) return SA_OK;
+  hipError_t e = sa::launch_nm_spmm(xval, mask, T, d_in, n, m, wt, d_out, y, as_stream(stream));
+  if (e == hipErrorNotSupported) {
+    sa::set_error("nm_act_spmm: shape not supported by the compiled kernels");
+    return SA_ERR_UNSUPPORTED;
+  }
+  return hip_status(e, "nm_act_spmm");
+}
+
+int dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt, int64_t d_out,
+               uint16_t* y, void* stream) {
+  sa::clear_error();
+  int st = sa::check_dense_gemm(x, T, d_in, wt, d_out, y);
+  if (st != SA_OK) return st;
+  if (T == 0) return SA_OK;
+  hipError_t e = sa::launch_dense_gemm(x, T, d_in, wt, d_out, y, as_stream(stream));
+  if (e == hipErrorNotSupported) {
+    sa::set_error("dense_gemm: shape not supported by the compiled kernels");
+    return SA_ERR_UNSUPPORTED;
+  }
+  return hip_status(e, "dense_gemm");
+}
+
+int sa_set_gemv_tuning(int tiling, int target_wgs) {
+  sa::clear_error();
+  if (sa::gemv_set_tuning(tiling, target_wgs) != 0) {
+    sa::set_error("sa_set_gemv_tuning: unknown tiling %d or negative target", tiling);
+    return SA_ERR_INVALID_ARG;
+  }
+  return SA_OK;
+}
+
+int sa_gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll) {
+  sa::clear_error();
+  if (sa::gemv_tiling_info(i, tile_o, threads, unroll) != 0) {
+    sa::set_error("sa_gemv_tiling_info: no tiling %d", i);
+    return SA_ERR_INVALID_ARG;
+  }
+  return SA_OK;
+}
+
+}  // extern "C"

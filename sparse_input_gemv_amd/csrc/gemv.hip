@@ -1,0 +1,851 @@
+// Sparse-input GEMV family for gfx950.
+//
+// y[b] = sum over kept k of WT[k][:] * v[b][k], with WT = W^T stored
+// row-major, so each kept activation entry selects one contiguous
+// 2*d_out-byte run of weights and every skipped entry skips one.
+// (RaNA author replies, Q5.1: the columns of zero activation entries are
+// skipped; TEAL README / Q-Sparse replies: decode is a batch-1 GEMV.)
+//
+// Two kernel designs serve every entry point of the family.
+//
+// Split-K (large weights).  Launch 1, k_gemv: workgroup i owns output tile
+// i % go and input slice i / go.
+//   phase 1  it builds the list of kept rows of its slice in LDS: threshold /
+//            mask / SwiGLU score decided per element, compacted with wave64
+//            ballot + mbcnt and an LDS scan of wave totals (ascending);
+//   phase 2  its threads stream the listed rows for the output tile with
+//            16-byte loads (8 fp16 per lane; a 128-output tile is one
+//            256-byte run per row), U rows in flight per thread, fp32 FMA;
+//   phase 3  row lanes are summed in LDS and the fp32 partial tile is stored
+//            with plain stores -- no waiting, no atomics.
+// Launch 2, k_reduce: sums the partial tiles of every output in slice order
+// and writes fp16 y (deterministic).  The kernel boundary orders the two.
+// Measured on MI355X, a second back-to-back launch costs less than a
+// cross-workgroup "last block" hand-off: device-scope atomics on one
+// counter serialise (~0.1-0.2 us each) and every workgroup reaches that
+// hand-off at the same moment.
+//
+// Full-K (small weights, batch <= 2).  k_gemv_fk: each workgroup owns
+// 8*LPR outputs and walks all of d_in; no partials, one launch.
+//
+// With go a multiple of 8, all slices of one output tile run on one XCD
+// (workgroups are dispatched round-robin over the 8 XCDs), and the
+// concurrently running workgroups of one slice read the same weight rows.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sa {
+namespace {
+
+struct Tiling {
+  int tile_o;   // outputs per workgroup
+  int threads;  // workgroup size
+  int unroll;   // rows in flight per thread
+  int full_k;   // 0: split-K (k_gemv + k_reduce), 1: full-K (k_gemv_fk)
+};
+// Compiled tile shapes (for batch 1; other batches use index 0 / 8).
+constexpr Tiling kTilings[] = {
+    {128, 256, 8, 0},  {256, 256, 8, 0}, {256, 512, 8, 0}, {128, 512, 8, 0},
+    {512, 256, 8, 0},  {128, 256, 16, 0}, {64, 256, 8, 0}, {256, 256, 4, 0},
+    {16, 1024, 8, 1},  {16, 512, 16, 1},  {8, 512, 16, 1},
+};
+constexpr int kNumTilings = (int)(sizeof(kTilings) / sizeof(kTilings[0]));
+constexpr int kDefaultSplitK = 0;     // any batch / mode
+constexpr int kDefaultSplitKHot = 2;  // batch 1 of threshold / dense / list (measured best)
+constexpr int kDefaultFullK = 8;
+constexpr int kSliceAlign = 64;
+constexpr int kDefaultTargetWgs = 1024;
+constexpr size_t kMaxListLds = 48 * 1024;
+// weights up to this size run full-K in one launch (latency-bound anyway)
+constexpr int64_t kFullKMaxWeightBytes = 8 << 20;
+
+int g_tiling = -1;     // -1: automatic
+int g_target_wgs = 0;  // 0: automatic
+
+struct KParams {
+  const uint16_t* wt;
+  int64_t d_out, d_in;
+  const uint16_t* x;
+  const uint32_t* xmask;
+  float t;
+  const int32_t* idx;
+  const uint16_t* val;
+  const int32_t* nnz;
+  int64_t cap;
+  const uint16_t* g;
+  const uint16_t* u;
+  const double* colnorm;
+  double t64;
+  int swiglu_mode;
+  uint32_t* out_mask;
+  int32_t* out_nnz;
+  uint16_t* y;
+  int batch;
+  float* part;
+  int32_t* slice_cnt;
+  int go, gk, slice;
+};
+
+constexpr int kModeListBatched = 5;  // kModeList with batch > 1
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Slot of this thread in a chunk compaction (ascending thread order) and the
+// chunk total.  `wsum` holds NT/64 ints of LDS.
+template <int NT>
+__device__ __forceinline__ int chunk_slot(bool keep, int* wsum, int& total, uint64_t& wmask) {
+  const uint64_t m = __ballot(keep);
+  const int w = (int)threadIdx.x / kWave;
+  if (lane_id() == 0) wsum[w] = (int)__popcll(m);
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    const int c = wsum[i];
+    off += (i < w) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  wmask = m;
+  return off + lanes_below(m);
+}
+
+// s = SiLU(g) = g / (1 + exp(-g)), h = s*u and the masker score, in fp64 and
+// in the order written (no contraction), as the pages' masks are defined.
+__device__ __forceinline__ bool swiglu_keep(uint16_t gb, uint16_t ub, const double* colnorm,
+                                            int64_t k, int mode, double t, float& hv) {
+#pragma clang fp contract(off)
+  const double gg = (double)h2f(gb);
+  const double uu = (double)h2f(ub);
+  const double s = gg / (1.0 + exp(-gg));
+  const double h = s * uu;
+  const double score = (mode == 0) ? fabs(s) : fabs(h) * colnorm[k];
+  hv = (float)h;
+  return score >= t;
+}
+
+// Sampled lower bound in an ascending int32 list: number of entries < key.
+// Two rounds of wave loads (64 samples, then one segment) instead of a
+// serial binary search.  Whole wave participates; result is wave-uniform.
+__device__ __forceinline__ int64_t wave_lower_bound(const int32_t* __restrict__ a, int64_t n,
+                                                    int64_t key) {
+  if (n <= 0) return 0;
+  const int lane = lane_id();
+  const int64_t q = ((int64_t)lane * n) / kWave;  // ascending sample positions, q_0 = 0
+  const bool below = (int64_t)a[q] < key;
+  const int c = (int)__popcll(__ballot(below));  // samples < key form a prefix
+  if (c == 0) return 0;
+  const int64_t lo = ((int64_t)(c - 1) * n) / kWave;               // a[lo] < key
+  const int64_t hi = (c < kWave) ? ((int64_t)c * n) / kWave : n;  // a[hi] >= key (or end)
+  int add = 0;
+  for (int64_t p0 = lo + 1; p0 < hi; p0 += kWave) {
+    const int64_t p = p0 + lane;
+    const bool b = p < hi && (int64_t)a[p] < key;
+    add += (int)__popcll(__ballot(b));
+  }
+  return lo + 1 + add;  // a[0..lo] are all < key
+}
+
+// ---------------------------------------------------------------------------
+// split-K, launch 1
+// ---------------------------------------------------------------------------
+template <int MODE, int TILE_O, int NT, int U, int B>
+__global__ __launch_bounds__(NT) void k_gemv(KParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int wsum[NT / kWave];
+  constexpr int OL = TILE_O / 8;  // lanes across the output tile
+  constexpr int R = NT / OL;      // row lanes
+  static_assert(R >= 1 && NT % OL == 0, "tile shape");
+
+  const int tid = (int)threadIdx.x;
+  const int oblk = (int)(blockIdx.x % (unsigned)p.go);
+  const int kblk = (int)(blockIdx.x / (unsigned)p.go);
+  const int SL = p.slice;
+  int* lk = reinterpret_cast<int*>(smem);
+  float* lv = reinterpret_cast<float*>(smem + (size_t)SL * 4);
+
+  // ---------------- phase 1: kept rows of this workgroup -> LDS ----------
+  int cnt = 0;
+  if constexpr (MODE == kModeList) {
+    int64_t nn = p.nnz[0];
+    const int64_t lim = p.cap < p.d_in ? p.cap : p.d_in;
+    nn = nn < 0 ? 0 : (nn > lim ? lim : nn);
+    const int64_t p0 = ((int64_t)kblk * nn) / p.gk;
+    const int64_t p1 = ((int64_t)(kblk + 1) * nn) / p.gk;
+    cnt = (int)(p1 - p0);
+    for (int j = tid; j < cnt; j += NT) {
+      const int32_t kk = p.idx[p0 + j];
+      const bool ok = kk >= 0 && (int64_t)kk < p.d_in;
+      lk[j] = ok ? kk : 0;
+      lv[j] = ok ? h2f(p.val[p0 + j]) : 0.f;
+    }
+    __syncthreads();
+  } else if constexpr (MODE == kModeListBatched) {
+    // Rows of the slice present in any list: mark them in a dense LDS
+    // staging area, then compact.
+    const int64_t k0 = (int64_t)kblk * SL;
+    const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
+    const int span = (int)(k1 - k0);
+    int* flag = reinterpret_cast<int*>(smem + (size_t)SL * 4 * (1 + B));
+    float* dv = reinterpret_cast<float*>(smem + (size_t)SL * 4 * (2 + B));
+    for (int j = tid; j < SL; j += NT) {
+      flag[j] = 0;
+#pragma unroll
+      for (int b = 0; b < B; ++b) dv[b * SL + j] = 0.f;
+    }
+    __syncthreads();
+    const int w = tid / kWave;
+    for (int b = w; b < p.batch; b += NT / kWave) {
+      const int32_t* ib = p.idx + (int64_t)b * p.cap;
+      const uint16_t* vb = p.val + (int64_t)b * p.cap;
+      int64_t nn = p.nnz[b];
+      const int64_t lim = p.cap < p.d_in ? p.cap : p.d_in;
+      nn = nn < 0 ? 0 : (nn > lim ? lim : nn);
+      const int64_t lo = wave_lower_bound(ib, nn, k0);
+      const int64_t hi = wave_lower_bound(ib, nn, k1);
+      for (int64_t q = lo + lane_id(); q < hi; q += kWave) {
+        const int64_t kk = ib[q];
+        if (kk >= k0 && kk < k1) {
+          flag[kk - k0] = 1;
+          dv[b * SL + (kk - k0)] = h2f(vb[q]);
+        }
+      }
+    }
+    __syncthreads();
+    for (int c = 0; c < span; c += NT) {
+      const int j = c + tid;
+      const bool keep = j < span && flag[j] != 0;
+      int total;
+      uint64_t wm;
+      const int slot = chunk_slot<NT>(keep, wsum, total, wm);
+      if (keep) {
+        lk[cnt + slot] = (int)(k0 + j);
+#pragma unroll
+        for (int b = 0; b < B; ++b) lv[b * SL + cnt + slot] = dv[b * SL + j];
+      }
+      cnt += total;
+    }
+    __syncthreads();
+  } else {
+    const int64_t k0 = (int64_t)kblk * SL;
+    const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
+    const int64_t words = (p.d_in + 31) >> 5;
+    for (int64_t c = k0; c < k1; c += NT) {
+      const int64_t k = c + tid;
+      const bool in = k < k1;
+      float vb[B];
+      bool any = false;
+      if constexpr (MODE == kModeSwiglu) {
+        float hv = 0.f;
+        any = in && swiglu_keep(p.g[k], p.u[k], p.colnorm, k, p.swiglu_mode, p.t64, hv);
+        vb[0] = hv;
+      } else {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          vb[b] = 0.f;
+          if (b < p.batch && in) {
+            const uint16_t xb = p.x[(int64_t)b * p.d_in + k];
+            bool kb;
+            if constexpr (MODE == kModeThreshold) {
+              kb = mag_key(xb) != 0 && fabsf(h2f(xb)) >= p.t;
+            } else if constexpr (MODE == kModeMasked) {
+              kb = ((p.xmask[(int64_t)b * words + (k >> 5)] >> (k & 31)) & 1u) != 0;
+            } else {
+              kb = true;
+            }
+            if (kb) vb[b] = h2f(xb);
+            any = any || kb;
+          }
+        }
+        if constexpr (MODE == kModeDense) any = in;
+      }
+      int total;
+      uint64_t wm;
+      const int slot = chunk_slot<NT>(any, wsum, total, wm);
+      if (any) {
+        lk[cnt + slot] = (int)k;
+#pragma unroll
+        for (int b = 0; b < B; ++b) lv[b * SL + cnt + slot] = vb[b];
+      }
+      if constexpr (MODE == kModeSwiglu) {
+        // each wave covers 64 consecutive entries starting at a multiple of 64
+        if (p.out_mask != nullptr && oblk == 0 && lane_id() == 0) {
+          const int64_t kw = c + (int64_t)(tid / kWave) * kWave;
+          if (kw < k1) {
+            p.out_mask[kw >> 5] = (uint32_t)wm;
+            if (kw + 32 < p.d_in) p.out_mask[(kw >> 5) + 1] = (uint32_t)(wm >> 32);
+          }
+        }
+      }
+      cnt += total;
+    }
+    if constexpr (MODE == kModeSwiglu) {
+      if (oblk == 0 && tid == 0) {
+        if (p.gk == 1) {
+          if (p.out_nnz != nullptr) p.out_nnz[0] = cnt;
+        } else {
+          p.slice_cnt[kblk] = cnt;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---------------- phase 2: stream the kept rows --------------------------
+  const int o_lane = tid % OL;
+  const int r_lane = tid / OL;
+  const int64_t o0 = (int64_t)oblk * TILE_O;
+  const int64_t o = o0 + (int64_t)o_lane * 8;
+  const bool o_ok = o < p.d_out;
+  const uint16_t* __restrict__ wcol = p.wt + (o_ok ? o : 0);
+  const int64_t ld = p.d_out;
+
+  float acc[B][8];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
+
+  for (int j0 = r_lane; j0 < cnt; j0 += R * U) {
+    half8 w[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int j = j0 + q * R;
+      if (j < cnt && o_ok) {
+        w[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)lk[j] * ld);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[q][i] = (half_t)0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int j = j0 + q * R;
+      if (j < cnt) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const float vv = lv[b * SL + j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[b][i] = fmaf((float)w[q][i], vv, acc[b][i]);
+        }
+      }
+    }
+  }
+
+  // ---------------- phase 3: reduce row lanes, store the tile --------------
+  __syncthreads();  // the kept list is no longer needed; reuse its LDS
+  float* red = reinterpret_cast<float*>(smem);
+  const bool single = p.gk == 1;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    if (b >= p.batch) break;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[r_lane * TILE_O + o_lane * 8 + i] = acc[b][i];
+    __syncthreads();
+    for (int oo = tid; oo < TILE_O; oo += NT) {
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) s += red[r * TILE_O + oo];
+      const int64_t og = o0 + oo;
+      if (og < p.d_out) {
+        if (single)
+          p.y[(int64_t)b * p.d_out + og] = f2h(s);
+        else
+          p.part[((int64_t)kblk * B + b) * p.d_out + og] = s;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split-K, launch 2: y[b][o] = sum over slices in order of the partials.
+// Thread (g, c) of a 256-thread workgroup adds slices g, g+16, ... of output
+// quad c (float4 loads, all in flight), then the 16 groups are added in
+// fixed order through LDS.
+// ---------------------------------------------------------------------------
+template <int B>
+__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int gk,
+                                                int64_t d_out, uint16_t* __restrict__ y,
+                                                const int32_t* __restrict__ slice_cnt,
+                                                int32_t* __restrict__ out_nnz) {
+  constexpr int C = 16, G = 16, kLoads = 16;
+  __shared__ f4v red[G][C];
+  __shared__ int scan[256 / kWave];
+  const int tid = (int)threadIdx.x;
+  const int c = tid % C;
+  const int g = tid / C;
+  const int b = (int)blockIdx.y;
+  const int64_t o4 = ((int64_t)blockIdx.x * C + c) * 4;
+  f4v s = {0.f, 0.f, 0.f, 0.f};
+  if (o4 < d_out) {
+    const float* base = part + (int64_t)b * d_out + o4;
+    const int64_t stride = (int64_t)B * d_out;
+    for (int k0 = g; k0 < gk; k0 += G * kLoads) {
+      f4v tmp[kLoads];
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) {
+        const int kk = k0 + q * G;
+        tmp[q] = (kk < gk) ? *reinterpret_cast<const f4v*>(base + (int64_t)kk * stride)
+                           : f4v{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) s += tmp[q];
+    }
+  }
+  red[g][c] = s;
+  __syncthreads();
+  if (g == 0 && o4 < d_out) {
+    f4v acc = red[0][c];
+#pragma unroll
+    for (int gg = 1; gg < G; ++gg) acc += red[gg][c];
+    uint16_t* yo = y + (int64_t)b * d_out + o4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yo[i] = f2h(acc[i]);
+  }
+  if (out_nnz != nullptr && blockIdx.x == 0 && b == 0) {
+    int cnt = 0;
+    for (int kk = tid; kk < gk; kk += 256) cnt += slice_cnt[kk];
+    int tot;
+    (void)block_exclusive_scan<256>(cnt, scan, tot);
+    if (tid == 0) out_nnz[0] = tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Full-K: no split of d_in, hence no partial tiles and one launch.  Each
+// workgroup owns TO = 8*LPR outputs (LPR lanes x 16 bytes of every weight
+// row) and walks every input index (or list entry), RL = NT/LPR rows at a
+// time, U rows in flight per thread.  Entries that are not kept switch their
+// lanes' loads off, so no compaction is needed.  Lanes are summed with a
+// fixed xor butterfly and waves through LDS in fixed order.  Workgroups are
+// renumbered so that consecutive output tiles -- which share 128-byte lines
+// of every row -- run on the same XCD and share its L2.
+// ---------------------------------------------------------------------------
+template <int MODE, int NT, int LPR, int U, int B>
+__global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
+  constexpr int TO = LPR * 8;
+  constexpr int RL = NT / LPR;
+  constexpr int NW = NT / kWave;
+  static_assert(MODE != kModeSwiglu || LPR <= 2, "mask words need >= 32 indices per wave");
+  __shared__ float red[NW][B][TO];
+  __shared__ int wcnt[NW];
+  const int tid = (int)threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid / kWave;
+  const unsigned G = gridDim.x;
+  const unsigned bi = blockIdx.x;
+  const int oblk = (G % 8u == 0u) ? (int)((bi % 8u) * (G / 8u) + bi / 8u) : (int)bi;
+  const int sub = tid % LPR;
+  const int rl = tid / LPR;
+  const int64_t o = (int64_t)oblk * TO + sub * 8;
+  const bool o_ok = o < p.d_out;
+  const uint16_t* __restrict__ wcol = p.wt + (o_ok ? o : 0);
+  const int64_t ld = p.d_out;
+  const int64_t words = (p.d_in + 31) >> 5;
+
+  int64_t n = p.d_in;
+  if constexpr (MODE == kModeList) {
+    const int64_t lim = p.cap < p.d_in ? p.cap : p.d_in;
+    n = p.nnz[0];
+    n = n < 0 ? 0 : (n > lim ? lim : n);
+  }
+
+  float acc[B][8];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
+  int kept_count = 0;  // SwiGLU: kept entries seen by this thread (sub 0 only)
+
+  for (int64_t j0 = rl; j0 < n; j0 += (int64_t)RL * U) {
+    int64_t row[U];
+    float v[U][B];
+    bool keep[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int64_t j = j0 + (int64_t)q * RL;
+      const bool in = j < n;
+      row[q] = in ? j : 0;
+      keep[q] = false;
+#pragma unroll
+      for (int b = 0; b < B; ++b) v[q][b] = 0.f;
+      if constexpr (MODE == kModeList) {
+        if (in) {
+          const int32_t kk = p.idx[j];
+          const bool ok = kk >= 0 && (int64_t)kk < p.d_in;
+          row[q] = ok ? kk : 0;
+          keep[q] = ok;
+          v[q][0] = ok ? h2f(p.val[j]) : 0.f;
+        }
+      } else if constexpr (MODE == kModeSwiglu) {
+        float hv = 0.f;
+        keep[q] = in && swiglu_keep(p.g[j], p.u[j], p.colnorm, j, p.swiglu_mode, p.t64, hv);
+        v[q][0] = hv;
+      } else {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          if (in && b < p.batch) {
+            const uint16_t xb = p.x[(int64_t)b * p.d_in + j];
+            bool kb;
+            if constexpr (MODE == kModeThreshold) {
+              kb = mag_key(xb) != 0 && fabsf(h2f(xb)) >= p.t;
+            } else if constexpr (MODE == kModeMasked) {
+              kb = ((p.xmask[(int64_t)b * words + (j >> 5)] >> (j & 31)) & 1u) != 0;
+            } else {
+              kb = true;
+            }
+            if (kb) v[q][b] = h2f(xb);
+            keep[q] = keep[q] || kb;
+          }
+        }
+      }
+    }
+    if constexpr (MODE == kModeSwiglu) {
+      // mask words and kept count, written once (workgroup 0).  A wave's
+      // sub-0 lanes cover 64/LPR consecutive indices starting at a multiple
+      // of 64/LPR.
+      if (bi == 0) {
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+          const uint64_t m = __ballot(keep[q]);
+          if (sub == 0 && keep[q]) ++kept_count;
+          if (p.out_mask != nullptr && lane == 0) {
+            const int64_t base = j0 - rl + (int64_t)q * RL + (int64_t)wv * (kWave / LPR);
+            uint64_t bits = 0;
+#pragma unroll
+            for (int r = 0; r < kWave / LPR; ++r) bits |= ((m >> (r * LPR)) & 1ull) << r;
+            for (int h = 0; h < (kWave / LPR) / 32; ++h)
+              if (base + 32 * h < p.d_in) p.out_mask[(base >> 5) + h] = (uint32_t)(bits >> (32 * h));
+          }
+        }
+      }
+    }
+    half8 w[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      if (keep[q] && o_ok) {
+        w[q] = *reinterpret_cast<const half8*>(wcol + row[q] * ld);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[q][i] = (half_t)0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      if (keep[q]) {
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[b][i] = fmaf((float)w[q][i], v[q][b], acc[b][i]);
+      }
+    }
+  }
+
+  // lanes with the same `sub` hold partial sums of the same outputs
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int off = LPR; off < kWave; off <<= 1) acc[b][i] += __shfl_xor(acc[b][i], off, kWave);
+  if (lane < LPR) {
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wv][b][lane * 8 + i] = acc[b][i];
+  }
+  if constexpr (MODE == kModeSwiglu) {
+    if (bi == 0) {
+      int c = kept_count;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) c += __shfl_xor(c, off, kWave);
+      if (lane == 0) wcnt[wv] = c;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < TO * B; e += NT) {
+    const int b = e / TO;
+    const int oo = e % TO;
+    const int64_t og = (int64_t)oblk * TO + oo;
+    if (b < p.batch && og < p.d_out) {
+      float s = red[0][b][oo];
+#pragma unroll
+      for (int g = 1; g < NW; ++g) s += red[g][b][oo];
+      p.y[(int64_t)b * p.d_out + og] = f2h(s);
+    }
+  }
+  if constexpr (MODE == kModeSwiglu) {
+    if (bi == 0 && tid == 0 && p.out_nnz != nullptr) {
+      int tot = 0;
+      for (int g = 0; g < NW; ++g) tot += wcnt[g];
+      p.out_nnz[0] = tot;
+    }
+  }
+}
+
+// out[k] = sqrt(sum_o WT[k][o]^2) in fp64, one wave per row, fixed-order
+// butterfly reduction (deterministic).
+__global__ __launch_bounds__(256) void k_col_norms(const uint16_t* __restrict__ wt, int64_t d_in,
+                                                   int64_t d_out, double* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (row >= d_in) return;  // uniform per wave
+  const int lane = lane_id();
+  const uint16_t* r = wt + row * d_out;
+  double s = 0.0;
+  for (int64_t o = (int64_t)lane * 8; o < d_out; o += 8 * kWave) {
+    const half8 h = *reinterpret_cast<const half8*>(r + o);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double v = (double)(float)h[i];
+      s += v * v;  // exact product: v has 11 significant bits
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
+  if (lane == 0) out[row] = sqrt(s);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+int batch_pad(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t slicecnt_off, part_off, total;
+};
+
+// Workspace: per-slice kept counts (SwiGLU) and the fp32 partial tiles
+// [slice][batch][d_out].  Everything in it is written before it is read
+// within one call, so its contents between calls do not matter.
+Layout ws_layout(int64_t d_out, int64_t d_in, int64_t batch) {
+  const int64_t gk_max = (d_in + kSliceAlign - 1) / kSliceAlign;
+  Layout L;
+  L.slicecnt_off = 0;
+  L.part_off = align256((size_t)gk_max * 4);
+  L.total = L.part_off + (size_t)gk_max * (size_t)batch_pad((int)batch) * (size_t)d_out * 4;
+  return L;
+}
+
+size_t list_lds_bytes(int mode, int slice, int B) {
+  size_t b = (size_t)slice * 4 * (1 + B);
+  if (mode == kModeListBatched) b += (size_t)slice * 4 * (1 + B);
+  return b;
+}
+
+struct Plan {
+  int go, gk, slice;
+  size_t smem;
+};
+
+Plan make_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
+  Plan pl;
+  const Tiling T = kTilings[tiling];
+  pl.go = (int)((d_out + T.tile_o - 1) / T.tile_o);
+  const int target = g_target_wgs > 0 ? g_target_wgs : kDefaultTargetWgs;
+  int64_t gk_req = (target + pl.go / 2) / pl.go;
+  if (gk_req < 1) gk_req = 1;
+  int64_t slice = (d_in + gk_req - 1) / gk_req;
+  slice = (slice + kSliceAlign - 1) / kSliceAlign * kSliceAlign;
+  while (list_lds_bytes(mode, (int)slice, B) > kMaxListLds && slice > kSliceAlign)
+    slice -= kSliceAlign;
+  pl.slice = (int)slice;
+  pl.gk = (int)((d_in + slice - 1) / slice);
+  const size_t red = (size_t)T.threads * 8 * 4;
+  const size_t lst = list_lds_bytes(mode, pl.slice, B);
+  pl.smem = lst > red ? lst : red;
+  return pl;
+}
+
+template <int MODE, int TO, int NT, int U, int B>
+hipError_t launch_one(const KParams& kp, const Plan& pl, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv<MODE, TO, NT, U, B>), dim3((unsigned)(pl.go * pl.gk)), dim3(NT),
+                     pl.smem, s, kp);
+  return hipGetLastError();
+}
+
+// Every split-K tiling for batch 1 of the hot modes; tiling 0 otherwise.
+template <int MODE, int B>
+hipError_t dispatch_tiling(const KParams& kp, const Plan& pl, int tiling, hipStream_t s) {
+  if constexpr (B == 1 && (MODE == kModeThreshold || MODE == kModeDense || MODE == kModeList)) {
+    switch (tiling) {
+      case 1: return launch_one<MODE, 256, 256, 8, B>(kp, pl, s);
+      case 2: return launch_one<MODE, 256, 512, 8, B>(kp, pl, s);
+      case 3: return launch_one<MODE, 128, 512, 8, B>(kp, pl, s);
+      case 4: return launch_one<MODE, 512, 256, 8, B>(kp, pl, s);
+      case 5: return launch_one<MODE, 128, 256, 16, B>(kp, pl, s);
+      case 6: return launch_one<MODE, 64, 256, 8, B>(kp, pl, s);
+      case 7: return launch_one<MODE, 256, 256, 4, B>(kp, pl, s);
+      default: return launch_one<MODE, 128, 256, 8, B>(kp, pl, s);
+    }
+  } else {
+    return launch_one<MODE, 128, 256, 8, B>(kp, pl, s);
+  }
+}
+
+template <int MODE>
+hipError_t dispatch_batch(const KParams& kp, const Plan& pl, int tiling, int B, hipStream_t s) {
+  switch (B) {
+    case 1: return dispatch_tiling<MODE, 1>(kp, pl, tiling, s);
+    case 2: return dispatch_tiling<MODE, 2>(kp, pl, tiling, s);
+    case 4: return dispatch_tiling<MODE, 4>(kp, pl, tiling, s);
+    default: return dispatch_tiling<MODE, 8>(kp, pl, tiling, s);
+  }
+}
+
+hipError_t launch_reduce(const KParams& kp, const Plan& pl, int B, bool with_nnz, hipStream_t s) {
+  const dim3 grid((unsigned)((kp.d_out / 4 + 15) / 16), (unsigned)kp.batch);
+  int32_t* nnz_out = with_nnz ? kp.out_nnz : nullptr;
+  switch (B) {
+    case 1:
+      hipLaunchKernelGGL(k_reduce<1>, grid, dim3(256), 0, s, kp.part, pl.gk, kp.d_out, kp.y,
+                         kp.slice_cnt, nnz_out);
+      break;
+    case 2:
+      hipLaunchKernelGGL(k_reduce<2>, grid, dim3(256), 0, s, kp.part, pl.gk, kp.d_out, kp.y,
+                         kp.slice_cnt, nnz_out);
+      break;
+    case 4:
+      hipLaunchKernelGGL(k_reduce<4>, grid, dim3(256), 0, s, kp.part, pl.gk, kp.d_out, kp.y,
+                         kp.slice_cnt, nnz_out);
+      break;
+    default:
+      hipLaunchKernelGGL(k_reduce<8>, grid, dim3(256), 0, s, kp.part, pl.gk, kp.d_out, kp.y,
+                         kp.slice_cnt, nnz_out);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int MODE, int NT, int LPR, int U, int B>
+hipError_t launch_fk(const KParams& kp, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv_fk<MODE, NT, LPR, U, B>), dim3(grid), dim3(NT), 0, s, kp);
+  return hipGetLastError();
+}
+
+template <int MODE, int B>
+hipError_t dispatch_fk(const KParams& kp, int tiling, unsigned grid, hipStream_t s) {
+  switch (tiling) {
+    case 9: return launch_fk<MODE, 512, 2, 16, B>(kp, grid, s);
+    case 10: return launch_fk<MODE, 512, 1, 16, B>(kp, grid, s);
+    default: return launch_fk<MODE, 1024, 2, 8, B>(kp, grid, s);
+  }
+}
+
+}  // namespace
+
+size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
+  return ws_layout(d_out, d_in, batch).total;
+}
+
+hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
+  int mode = c.mode;
+  if (mode == kModeList && c.batch > 1) mode = kModeListBatched;
+  const int B = (mode == kModeSwiglu || mode == kModeList) ? 1 : batch_pad(c.batch);
+  // Full-K serves batch <= 2 of every mode except batched lists; by default
+  // only for small weights, where one launch beats two.
+  const bool fk_ok = B <= 2 && mode != kModeListBatched;
+  int tiling = g_tiling;
+  const bool hot = B == 1 && (mode == kModeThreshold || mode == kModeDense || mode == kModeList);
+  if (tiling < 0)
+    tiling = (fk_ok && c.d_in * c.d_out * 2 <= kFullKMaxWeightBytes)
+                 ? kDefaultFullK
+                 : (hot ? kDefaultSplitKHot : kDefaultSplitK);
+  if (kTilings[tiling].full_k && !fk_ok) tiling = kDefaultSplitK;
+  if (!kTilings[tiling].full_k && !hot)
+    tiling = kDefaultSplitK;  // split-K variants exist for the batch-1 hot modes only
+
+  KParams kp{};
+  kp.wt = c.wt;
+  kp.d_out = c.d_out;
+  kp.d_in = c.d_in;
+  kp.x = c.x;
+  kp.xmask = c.xmask;
+  kp.t = c.t;
+  kp.idx = c.idx;
+  kp.val = c.val;
+  kp.nnz = c.nnz;
+  kp.cap = c.cap;
+  kp.g = c.g;
+  kp.u = c.u;
+  kp.colnorm = c.colnorm;
+  kp.t64 = c.t64;
+  kp.swiglu_mode = c.swiglu_mode;
+  kp.out_mask = c.out_mask;
+  kp.out_nnz = c.out_nnz;
+  kp.y = c.y;
+  kp.batch = c.batch;
+
+  if (kTilings[tiling].full_k) {
+    const unsigned grid = (unsigned)((c.d_out + kTilings[tiling].tile_o - 1) /
+                                     kTilings[tiling].tile_o);
+    switch (mode) {
+      case kModeThreshold:
+        return B == 1 ? dispatch_fk<kModeThreshold, 1>(kp, tiling, grid, s)
+                      : dispatch_fk<kModeThreshold, 2>(kp, tiling, grid, s);
+      case kModeDense:
+        return B == 1 ? dispatch_fk<kModeDense, 1>(kp, tiling, grid, s)
+                      : dispatch_fk<kModeDense, 2>(kp, tiling, grid, s);
+      case kModeMasked:
+        return B == 1 ? dispatch_fk<kModeMasked, 1>(kp, tiling, grid, s)
+                      : dispatch_fk<kModeMasked, 2>(kp, tiling, grid, s);
+      case kModeList: return dispatch_fk<kModeList, 1>(kp, tiling, grid, s);
+      case kModeSwiglu: return dispatch_fk<kModeSwiglu, 1>(kp, tiling, grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+
+  const Plan pl = make_plan(mode, tiling, c.d_out, c.d_in, B);
+  const Layout L = ws_layout(c.d_out, c.d_in, c.batch);
+  if (pl.gk > 1 && (c.ws == nullptr || c.ws_bytes < L.total)) return hipErrorInvalidValue;
+  unsigned char* ws = static_cast<unsigned char*>(c.ws);
+  kp.slice_cnt = ws ? reinterpret_cast<int32_t*>(ws + L.slicecnt_off) : nullptr;
+  kp.part = ws ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
+  kp.go = pl.go;
+  kp.gk = pl.gk;
+  kp.slice = pl.slice;
+
+  hipError_t e;
+  switch (mode) {
+    case kModeThreshold: e = dispatch_batch<kModeThreshold>(kp, pl, tiling, B, s); break;
+    case kModeDense: e = dispatch_batch<kModeDense>(kp, pl, tiling, B, s); break;
+    case kModeMasked: e = dispatch_batch<kModeMasked>(kp, pl, tiling, B, s); break;
+    case kModeList: e = dispatch_tiling<kModeList, 1>(kp, pl, tiling, s); break;
+    case kModeListBatched: e = dispatch_batch<kModeListBatched>(kp, pl, tiling, B, s); break;
+    case kModeSwiglu: e = dispatch_tiling<kModeSwiglu, 1>(kp, pl, tiling, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess || pl.gk == 1) return e;
+  return launch_reduce(kp, pl, B, mode == kModeSwiglu && c.out_nnz != nullptr, s);
+}
+
+hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* out,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(k_col_norms, dim3((unsigned)((d_in + 3) / 4)), dim3(256), 0, s, wt, d_in,
+                     d_out, out);
+  return hipGetLastError();
+}
+
+int gemv_set_tuning(int tiling, int target_wgs) {
+  if (tiling < -1 || tiling >= kNumTilings || target_wgs < 0) return 1;
+  g_tiling = tiling;
+  g_target_wgs = target_wgs;
+  return 0;
+}
+
+int gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll) {
+  // tile_o of a full-K tiling is reported negated so callers can tell them apart
+  if (i < 0 || i >= kNumTilings) return 1;
+  if (tile_o) *tile_o = kTilings[i].full_k ? -kTilings[i].tile_o : kTilings[i].tile_o;
+  if (threads) *threads = kTilings[i].threads;
+  if (unroll) *unroll = kTilings[i].unroll;
+  return 0;
+}
+
+}  // namespace sa

@@ -1,0 +1,78 @@
+// Host-side launchers implemented in the .hip files and called by abi.cpp
+// after argument validation.  Each returns a HIP error code (0 = success).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+// ---- sparsifiers (sparsify.hip) -------------------------------------------
+hipError_t launch_sparsify_threshold(const uint16_t* x, int64_t rows, int64_t d, float t,
+                                     uint32_t* mask, int32_t* idx, uint16_t* val,
+                                     int32_t* nnz, int64_t cap, hipStream_t s);
+hipError_t launch_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k,
+                                uint32_t* mask, int32_t* idx, uint16_t* val, int32_t* nnz,
+                                int64_t cap, hipStream_t s);
+hipError_t launch_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
+                              uint32_t* mask, uint16_t* val, hipStream_t s);
+
+// ---- calibration (calibrate.hip) ------------------------------------------
+hipError_t launch_calibrate(const uint16_t* samples, int64_t n, double s, float* t_out,
+                            hipStream_t st);
+
+// ---- GEMV family (gemv.hip) -------------------------------------------------
+enum GemvMode : int {
+  kModeThreshold = 0,  // x + t: fused threshold
+  kModeDense = 1,      // every column
+  kModeMasked = 2,     // x + bitmask
+  kModeList = 3,       // idx/val/nnz lists
+  kModeSwiglu = 4,     // CATS / RaNA masked SwiGLU down
+};
+
+struct GemvCall {
+  int mode = 0;
+  const uint16_t* wt = nullptr;
+  int64_t d_out = 0, d_in = 0;
+  int batch = 1;
+  // threshold / dense / masked
+  const uint16_t* x = nullptr;
+  const uint32_t* xmask = nullptr;
+  float t = 0.f;
+  // lists
+  const int32_t* idx = nullptr;
+  const uint16_t* val = nullptr;
+  const int32_t* nnz = nullptr;
+  int64_t cap = 0;
+  // swiglu
+  const uint16_t* g = nullptr;
+  const uint16_t* u = nullptr;
+  const double* colnorm = nullptr;
+  double t64 = 0.0;
+  int swiglu_mode = 0;
+  uint32_t* out_mask = nullptr;
+  int32_t* out_nnz = nullptr;
+  // output and scratch
+  uint16_t* y = nullptr;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+};
+
+size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch);
+// Returns hipErrorInvalidValue if the workspace is too small for the launch
+// (checked by abi.cpp beforehand, so this is a second line of defence).
+hipError_t launch_gemv(const GemvCall& c, hipStream_t s);
+hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* out,
+                            hipStream_t s);
+int gemv_set_tuning(int tiling, int target_wgs);
+int gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll);
+
+// ---- MFMA matmuls (gemm.hip) ------------------------------------------------
+hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
+                             int64_t d_out, uint16_t* y, hipStream_t s);
+hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
+                          int n, int m, const uint16_t* wt, int64_t d_out, uint16_t* y,
+                          hipStream_t s);
+
+}  // namespace sa

@@ -1,0 +1,375 @@
+// Activation sparsifiers for gfx950: magnitude threshold, per-token Top-K and
+// N:M.  One pass over the activation; kept entries are compacted in ascending
+// order with wave64 ballots, lane prefix counts (mbcnt) and an LDS scan of
+// the per-wave totals.
+//
+// Pages: TEAL (README, Abstract) -- magnitude threshold of hidden states;
+// Q-Sparse (author replies) -- per-token Top-K (answer comparing with MoE)
+// and N:M over consecutive entries (answer on batched inference); the
+// flexible N:M activation-sparsity summary, section 2 (methodology) -- N of
+// every M kept, scored by |activation|.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sa {
+namespace {
+
+constexpr int kSparsifyThreads = 1024;
+
+// Loads E consecutive fp16 bit patterns starting at element k0 of a row.
+// The vector path needs a 16-byte aligned row and k0 a multiple of 8.
+template <int E>
+__device__ __forceinline__ void load_run(const uint16_t* __restrict__ xr, int64_t k0, int64_t d,
+                                         bool vec, uint16_t (&v)[E]) {
+  if (vec && k0 + E <= d) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(xr + k0);
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) {
+      u32x4 r = p[q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[q * 8 + 2 * i] = (uint16_t)(r[i] & 0xffffu);
+        v[q * 8 + 2 * i + 1] = (uint16_t)(r[i] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = (k0 + e < d) ? xr[k0 + e] : (uint16_t)0;
+  }
+}
+
+// Writes the kept entries of one run per thread (bit e of `bits` <-> element
+// k0+e) at their ascending positions, and the bitmask words of the run.
+// Threads cover consecutive runs, so thread order is index order.
+template <int NT, int E>
+__device__ __forceinline__ void compact_run(uint64_t bits, const uint16_t (&v)[E], int64_t k0,
+                                            int64_t d, int& base, int* scan,
+                                            int32_t* __restrict__ ir, uint16_t* __restrict__ vr,
+                                            uint32_t* __restrict__ mr) {
+  int total;
+  int pos = base + block_exclusive_scan<NT>(__popcll(bits), scan, total);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if ((bits >> e) & 1ull) {
+      ir[pos] = (int32_t)(k0 + e);
+      vr[pos] = v[e];
+      ++pos;
+    }
+  }
+  if (mr != nullptr) {
+    if constexpr (E == 16) {
+      // two neighbouring threads hold the two halves of one 32-bit word
+      uint32_t other = (uint32_t)__shfl_xor((int)bits, 1, kWave);
+      if ((threadIdx.x & 1) == 0 && k0 < d) mr[k0 >> 5] = (uint32_t)bits | (other << 16);
+    } else {
+#pragma unroll
+      for (int q = 0; q < E / 32; ++q)
+        if (k0 + 32 * q < d) mr[(k0 >> 5) + q] = (uint32_t)(bits >> (32 * q));
+    }
+  }
+  base += total;
+}
+
+// keep_i = (|x_i| >= t) && (x_i != 0), compared in fp32 (fp16 widening is
+// exact, so this is the exact comparison).  One workgroup per row.
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void k_sparsify_threshold(
+    const uint16_t* __restrict__ x, int64_t d, float t, uint32_t* __restrict__ mask,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int32_t* __restrict__ nnz,
+    int64_t cap, int vec) {
+  __shared__ int scan[NT / kWave];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * d;
+  int32_t* ir = idx + row * cap;
+  uint16_t* vr = val + row * cap;
+  uint32_t* mr = mask ? mask + row * ((d + 31) >> 5) : nullptr;
+  int base = 0;
+  for (int64_t c0 = 0; c0 < d; c0 += (int64_t)NT * E) {
+    const int64_t k0 = c0 + (int64_t)threadIdx.x * E;
+    uint16_t v[E];
+    load_run<E>(xr, k0, d, vec != 0, v);
+    uint64_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint16_t b = v[e];
+      const bool keep = (k0 + e < d) && (mag_key(b) != 0) && (fabsf(h2f(b)) >= t);
+      bits |= (uint64_t)keep << e;
+    }
+    compact_run<NT, E>(bits, v, k0, d, base, scan, ir, vr, mr);
+  }
+  if (threadIdx.x == 0) nnz[row] = base;
+}
+
+// Wave 0 helper for the radix select: given per-lane counts of consecutive
+// bins (lane l holds bins P*l .. P*l+P-1, ascending), find the largest bin b
+// whose suffix count S(b) = sum_{b' >= b} + extra reaches k; also return
+// S(b+1) (count strictly above).  Bins with S >= k form a prefix because S
+// is non-increasing.
+template <int P>
+__device__ __forceinline__ void suffix_select(const int (&c)[P], int extra, int64_t k, int& bin,
+                                              int& above) {
+  const int lane = lane_id();
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) s += c[j];
+  int suf = s;  // inclusive suffix over lanes >= this one
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_down(suf, o, kWave);
+    if (lane + o < kWave) suf += t;
+  }
+  int S[P];
+  S[0] = suf + extra;
+#pragma unroll
+  for (int j = 1; j < P; ++j) S[j] = S[j - 1] - c[j - 1];
+  int nq = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) nq += (S[j] >= k) ? 1 : 0;
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) nq += __shfl_xor(nq, o, kWave);
+  bin = nq - 1;
+  const int nb = bin + 1;  // S(bin+1) lives in lane nb/P, slot nb%P
+  int mine = S[0];
+#pragma unroll
+  for (int j = 1; j < P; ++j)
+    if ((nb % P) == j) mine = S[j];
+  int got = __shfl(mine, (nb / P) & (kWave - 1), kWave);
+  above = (nb >= P * kWave) ? extra : got;
+}
+
+// Exactly k survivors per row: the k largest magnitudes, ties to the lower
+// index.  15-bit magnitude keys; two-level radix select (256 then 128 bins in
+// LDS) gives the k-th largest key tau and the count above it; the first
+// r = k - above entries equal to tau (in index order, by a workgroup scan)
+// complete the set.  One workgroup per row; each thread keeps E keys.
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void k_sparsify_topk(
+    const uint16_t* __restrict__ x, int64_t d, int64_t k, uint32_t* __restrict__ mask,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int32_t* __restrict__ nnz,
+    int64_t cap, int vec) {
+  __shared__ int hist[256];
+  __shared__ int scan[NT / kWave];
+  __shared__ int sel[2];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * d;
+  const int64_t k0 = (int64_t)threadIdx.x * E;
+  uint16_t v[E];
+  load_run<E>(xr, k0, d, vec != 0, v);
+  int key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (k0 + e < d) ? mag_key(v[e]) : -1;
+
+  int tau = 0x8000, r = 0;  // k == 0: nothing survives
+  if (k > 0) {
+    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (key[e] >= 0) atomicAdd(&hist[key[e] >> 7], 1);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      int c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = hist[threadIdx.x * 4 + j];
+      int b1, above;
+      suffix_select<4>(c, 0, k, b1, above);
+      if (threadIdx.x == 0) {
+        sel[0] = b1;
+        sel[1] = above;
+      }
+    }
+    __syncthreads();
+    const int b1 = sel[0];
+    const int above1 = sel[1];
+    for (int i = threadIdx.x; i < 128; i += NT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (key[e] >= 0 && (key[e] >> 7) == b1) atomicAdd(&hist[key[e] & 127], 1);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      int c[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) c[j] = hist[threadIdx.x * 2 + j];
+      int b2, gt;
+      suffix_select<2>(c, above1, k, b2, gt);
+      if (threadIdx.x == 0) {
+        sel[0] = (b1 << 7) | b2;
+        sel[1] = (int)(k - gt);
+      }
+    }
+    __syncthreads();
+    tau = sel[0];
+    r = sel[1];
+  }
+
+  int ties = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) ties += (key[e] == tau) ? 1 : 0;
+  int tie_total;
+  int tr = block_exclusive_scan<NT>(ties, scan, tie_total);
+  uint64_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    bool keep = key[e] > tau;
+    if (key[e] == tau) {
+      keep = tr < r;
+      ++tr;
+    }
+    bits |= (uint64_t)keep << e;
+  }
+  int32_t* ir = idx + row * cap;
+  uint16_t* vr = val + row * cap;
+  uint32_t* mr = mask ? mask + row * ((d + 31) >> 5) : nullptr;
+  int base = 0;
+  compact_run<NT, E>(bits, v, k0, d, base, scan, ir, vr, mr);
+  if (threadIdx.x == 0) nnz[row] = base;
+}
+
+// N:M: each thread owns 8 consecutive entries (one 16-byte load).  For
+// M <= 8 its groups are local; for M = 16 / 32 the M/8 threads of a group
+// exchange their packed 15-bit keys with cross-lane shuffles.  An entry is
+// kept iff fewer than n entries of its group rank before it, where j ranks
+// before i iff |x_j| > |x_i|, or they are equal and j < i.  The flattened
+// array is a sequence of groups because d % M == 0 and d % 32 == 0.
+template <int M>
+__global__ __launch_bounds__(256) void k_sparsify_nm(const uint16_t* __restrict__ x, int64_t n8,
+                                                     int n, uint32_t* __restrict__ mask,
+                                                     uint16_t* __restrict__ val) {
+  const int64_t g8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool active = g8 < n8;
+  const int lane = lane_id();
+  u32x4 raw = {0u, 0u, 0u, 0u};
+  if (active) raw = *reinterpret_cast<const u32x4*>(x + g8 * 8);
+  uint16_t v[8];
+  int key[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = (uint16_t)(raw[i] & 0xffffu);
+    v[2 * i + 1] = (uint16_t)(raw[i] >> 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) key[i] = mag_key(v[i]);
+
+  uint32_t keep = 0;
+  if constexpr (M <= 8) {
+    constexpr int GPT = 8 / M;
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int p = gi * M + i;
+        int rank = 0;
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+          const int q = gi * M + j;
+          rank += (key[q] > key[p] || (key[q] == key[p] && j < i)) ? 1 : 0;
+        }
+        if (rank < n) keep |= 1u << p;
+      }
+      if (active) {
+        const int64_t grp = g8 * GPT + gi;
+        int slot = 0;
+#pragma unroll
+        for (int i = 0; i < M; ++i)
+          if ((keep >> (gi * M + i)) & 1u) val[grp * n + slot++] = v[gi * M + i];
+      }
+    }
+  } else {
+    constexpr int G = M / 8;  // threads per group
+    const int gl = lane & (G - 1);
+    const int base_lane = lane - gl;
+    uint32_t pk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[i] = raw[i] & 0x7fff7fffu;
+    int all[M];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = (uint32_t)__shfl((int)pk[i], base_lane + q, kWave);
+        all[q * 8 + 2 * i] = (int)(w & 0xffffu);
+        all[q * 8 + 2 * i + 1] = (int)(w >> 16);
+      }
+    }
+    const int off = gl * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < M; ++j)
+        rank += (all[j] > key[i] || (all[j] == key[i] && j < off + i)) ? 1 : 0;
+      if (rank < n) keep |= 1u << i;
+    }
+    // kept entries in lower lanes of the group come first
+    const int mine = __popc(keep);
+    int pre = 0;
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const int c = __shfl(mine, base_lane + q, kWave);
+      pre += (q < gl) ? c : 0;
+    }
+    if (active) {
+      const int64_t grp = (g8 * 8) / M;
+      int slot = pre;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((keep >> i) & 1u) val[grp * n + slot++] = v[i];
+    }
+  }
+  // four neighbouring threads make one 32-bit mask word
+  uint32_t w = keep << (8 * (lane & 3));
+  w |= (uint32_t)__shfl_xor((int)w, 1, kWave);
+  w |= (uint32_t)__shfl_xor((int)w, 2, kWave);
+  if (active && (lane & 3) == 0) mask[g8 >> 2] = w;
+}
+
+}  // namespace
+
+hipError_t launch_sparsify_threshold(const uint16_t* x, int64_t rows, int64_t d, float t,
+                                     uint32_t* mask, int32_t* idx, uint16_t* val,
+                                     int32_t* nnz, int64_t cap, hipStream_t s) {
+  const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && (d % 8) == 0) ? 1 : 0;
+  hipLaunchKernelGGL((k_sparsify_threshold<kSparsifyThreads, 16>), dim3((unsigned)rows),
+                     dim3(kSparsifyThreads), 0, s, x, d, t, mask, idx, val, nnz, cap, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k,
+                                uint32_t* mask, int32_t* idx, uint16_t* val, int32_t* nnz,
+                                int64_t cap, hipStream_t s) {
+  const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && (d % 8) == 0) ? 1 : 0;
+  if (d <= (int64_t)kSparsifyThreads * 16) {
+    hipLaunchKernelGGL((k_sparsify_topk<kSparsifyThreads, 16>), dim3((unsigned)rows),
+                       dim3(kSparsifyThreads), 0, s, x, d, k, mask, idx, val, nnz, cap, vec);
+  } else {
+    hipLaunchKernelGGL((k_sparsify_topk<kSparsifyThreads, 64>), dim3((unsigned)rows),
+                       dim3(kSparsifyThreads), 0, s, x, d, k, mask, idx, val, nnz, cap, vec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
+                              uint32_t* mask, uint16_t* val, hipStream_t s) {
+  const int64_t n8 = rows * d / 8;
+  const dim3 grid((unsigned)((n8 + 255) / 256));
+  switch (m) {
+    case 4:
+      hipLaunchKernelGGL(k_sparsify_nm<4>, grid, dim3(256), 0, s, x, n8, n, mask, val);
+      break;
+    case 8:
+      hipLaunchKernelGGL(k_sparsify_nm<8>, grid, dim3(256), 0, s, x, n8, n, mask, val);
+      break;
+    case 16:
+      hipLaunchKernelGGL(k_sparsify_nm<16>, grid, dim3(256), 0, s, x, n8, n, mask, val);
+      break;
+    case 32:
+      hipLaunchKernelGGL(k_sparsify_nm<32>, grid, dim3(256), 0, s, x, n8, n, mask, val);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,151 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and its host-side checks return the documented status codes
+before any HIP call (run with -m "not gpu")."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_act.h")
+LIB = os.path.join(ROOT, "sparse_input_gemv_amd", "libsparse_act.so")
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s+(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def sa():
+    import sparse_input_gemv_amd as m
+    return m.lib()
+
+
+# Plausible, aligned addresses that are never dereferenced: every call below
+# fails a host check first (or is an empty call that returns before HIP).
+P = 1 << 20
+
+
+def test_every_declared_symbol_is_exported(sa):
+    names = declared_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(sa, n), n
+    for n in ("act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm", "sparse_gemv",
+              "masked_swiglu_down", "nm_act_spmm", "act_calibrate_threshold"):
+        assert n in names
+
+
+def test_status_strings(sa):
+    assert sa.sa_status_string(SA_OK) == b"SA_OK"
+    assert sa.sa_status_string(SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
+    assert sa.sa_status_string(99) == b"SA_ERR_UNKNOWN"
+    assert sa.sa_version() == 100
+
+
+def test_threshold_checks(sa):
+    f = sa.act_sparsify_threshold
+    assert f(None, 1, 16, 0.5, None, P, P, P, 16, None) == SA_ERR_INVALID_ARG
+    assert b"x is NULL" in sa.sa_last_error()
+    assert f(P, 1, 0, 0.5, None, P, P, P, 16, None) == SA_ERR_INVALID_ARG
+    assert f(P, 1, 16, 0.5, None, P, P, P, 15, None) == SA_ERR_INVALID_ARG  # cap < d
+    assert f(P, 1, 16, -1.0, None, P, P, P, 16, None) == SA_ERR_INVALID_ARG
+    assert f(P, 1, 16, float("nan"), None, P, P, P, 16, None) == SA_ERR_INVALID_ARG
+    assert f(P, 1, 70000, 0.5, None, P, P, P, 70000, None) == SA_ERR_UNSUPPORTED
+    assert f(P + 1, 1, 16, 0.5, None, P, P, P, 16, None) == SA_ERR_INVALID_ARG  # misaligned
+    assert f(P, 0, 16, 0.5, None, P, P, P, 16, None) == SA_OK  # empty call
+    assert sa.sa_last_error() == b""
+
+
+def test_topk_checks(sa):
+    f = sa.act_sparsify_topk
+    assert f(P, 1, 16, 17, None, P, P, P, 17, None) == SA_ERR_INVALID_ARG  # k > d
+    assert f(P, 1, 16, -1, None, P, P, P, 16, None) == SA_ERR_INVALID_ARG
+    assert f(P, 1, 16, 8, None, P, P, P, 7, None) == SA_ERR_INVALID_ARG  # cap < k
+    assert f(P, 1, 16, 8, None, None, P, P, 8, None) == SA_ERR_INVALID_ARG
+    assert f(P, 0, 16, 8, None, P, P, P, 8, None) == SA_OK
+
+
+def test_nm_checks(sa):
+    f = sa.act_sparsify_nm
+    assert f(P, 1, 64, 2, 6, P, P, None) == SA_ERR_INVALID_ARG  # m not supported
+    assert f(P, 1, 64, 0, 4, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 1, 64, 5, 4, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 1, 48, 2, 4, P, P, None) == SA_ERR_INVALID_ARG  # d % 32
+    assert f(P + 8, 1, 64, 2, 4, P, P, None) == SA_ERR_INVALID_ARG  # x not 16-B aligned
+    assert f(P, 0, 64, 2, 4, P, P, None) == SA_OK
+
+
+def test_calibrate_checks(sa):
+    f = sa.act_calibrate_threshold
+    assert f(P, 0, 0.5, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 10, 1.5, P, None) == SA_ERR_INVALID_ARG
+    assert f(None, 10, 0.5, P, None) == SA_ERR_INVALID_ARG
+
+
+def test_workspace_size(sa):
+    a = sa.sa_workspace_bytes(4096, 11008, 1)
+    b = sa.sa_workspace_bytes(4096, 11008, 8)
+    assert 0 < a < b
+    assert a % 256 == 0 or a > 0
+    assert sa.sa_workspace_bytes(0, 10, 1) == 0
+
+
+def test_gemv_checks(sa):
+    need = sa.sa_workspace_bytes(4096, 11008, 1)
+    f = sa.sparse_gemv
+    assert f(P, 4100, 11008, P, P, P, 1, 11008, P, P, need, None) == SA_ERR_INVALID_ARG  # d_out%8
+    assert f(P, 4096, 11008, P, P, P, 9, 11008, P, P, need * 9, None) == SA_ERR_INVALID_ARG
+    assert f(P, 4096, 11008, P, P, P, 1, 11008, P, P, need - 1, None) == SA_ERR_WORKSPACE
+    assert f(P, 4096, 11008, P, P, P, 1, 11008, P, None, 0, None) == SA_ERR_WORKSPACE
+    assert f(P, 4096, 11008, None, P, P, 1, 11008, P, P, need, None) == SA_ERR_INVALID_ARG
+    assert f(P + 2, 4096, 11008, P, P, P, 1, 11008, P, P, need, None) == SA_ERR_INVALID_ARG
+    assert f(P, 4096, 11008, P, P, P, 0, 11008, P, P, need, None) == SA_OK  # empty batch
+    g = sa.sparse_gemv_threshold
+    assert g(P, 4096, 11008, P, 1, -0.5, P, P, need, None) == SA_ERR_INVALID_ARG
+    assert g(P, 4096, 11008, None, 1, 0.5, P, P, need, None) == SA_ERR_INVALID_ARG
+    h = sa.masked_gemv
+    assert h(P, 4096, 11008, P, None, 1, P, P, need, None) == SA_ERR_INVALID_ARG
+    d = sa.dense_gemv
+    assert d(P, 4096, 11008, None, 1, P, P, need, None) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemv_tuning(99, 0) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemv_tuning(-1, 0) == SA_OK
+
+
+def test_swiglu_checks(sa):
+    need = sa.sa_workspace_bytes(4096, 14336, 1)
+    f = sa.masked_swiglu_down
+    args = [P, P, P, None, 14336, 4096, 0.5, 1, P, None, None, P, need, None]
+    assert f(*args) == SA_ERR_INVALID_ARG  # RaNA needs colnorm
+    args[7] = 2
+    assert f(*args) == SA_ERR_INVALID_ARG  # unknown mode
+    args[7] = 0
+    args[6] = float("inf")
+    assert f(*args) == SA_ERR_INVALID_ARG
+
+
+def test_matmul_checks(sa):
+    f = sa.nm_act_spmm
+    assert f(P, P, 16, 1000, 2, 4, P, 1024, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, P, 16, 1024, 3, 2, P, 1024, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, P, 0, 1024, 2, 4, P, 1024, P, None) == SA_OK
+    g = sa.dense_gemm
+    assert g(P, 16, 1020, P, 1024, P, None) == SA_ERR_INVALID_ARG
+    assert g(P, 0, 1024, P, 1024, P, None) == SA_OK
+
+
+def test_tiling_info(sa):
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert sa.sa_gemv_tiling_info(0, ctypes.addressof(a), ctypes.addressof(b),
+                                  ctypes.addressof(c)) == SA_OK
+    assert (a.value, b.value, c.value) == (128, 256, 8)
+    assert sa.sa_gemv_tiling_info(8, ctypes.addressof(a), None, None) == SA_OK and a.value == -16
+    assert sa.sa_gemv_tiling_info(100, None, None, None) == SA_ERR_INVALID_ARG

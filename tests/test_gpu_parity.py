@@ -1,0 +1,362 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Masks, indices, counts and calibrated thresholds must match bit for bit;
+outputs must satisfy relative L2 error <= 2e-3 and max abs error <= 1e-2
+against the oracle's fp64 result.  Inputs come from ``synthetic`` with the
+shapes and distributions of the workloads (Llama-2-7B / Llama-3-8B layers).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_input_gemv_amd as sa
+import synthetic as syn
+from oracle import calibrate, gemv, sparsify, swiglu
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REL_L2 = 2e-3
+MAX_ABS = 1e-2
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def words(t):
+    return host(t).view(np.uint32)
+
+
+def assert_close(y_gpu, ref):
+    y = host(y_gpu).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert y.shape == ref.shape
+    err = y - ref
+    nrm = np.linalg.norm(ref)
+    rel = np.linalg.norm(err) / (nrm if nrm > 0 else 1.0)
+    mx = float(np.max(np.abs(err))) if err.size else 0.0
+    assert rel <= REL_L2 and mx <= MAX_ABS, f"rel_l2={rel:.3e} max_abs={mx:.3e}"
+
+
+def check_lists(mask_g, idx_g, val_g, nnz_g, x, keep):
+    """Bit-exact comparison of a sparsifier's outputs with the oracle mask."""
+    x2 = np.atleast_2d(x)
+    keep2 = np.atleast_2d(keep)
+    nnz = host(nnz_g)
+    idx = np.atleast_2d(host(idx_g))
+    val = np.atleast_2d(host(val_g))
+    if mask_g is not None:
+        assert np.array_equal(np.atleast_2d(words(mask_g)), sparsify.pack_mask(keep2))
+    for r in range(x2.shape[0]):
+        ref_idx = np.flatnonzero(keep2[r])
+        assert nnz[r] == len(ref_idx)
+        assert np.array_equal(idx[r, :nnz[r]], ref_idx)
+        assert np.array_equal(val[r, :nnz[r]].view(np.uint16), x2[r][ref_idx].view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# threshold sparsifier + sparse GEMV: single 1024 x 1024 layer, seeds 0..9
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(10))
+def test_single_layer_1024(seed):
+    wt = syn.weight_t(1024, 1024, 1000)
+    x = syn.gaussian_f16((1024,), 1.0, seed)
+    t = float(calibrate.magnitude_threshold(x, 0.5))  # 50th percentile of |x|
+    keep, idx, val, nnz = sparsify.threshold_sparsify(x, t)
+    y_ref = gemv.sparse_gemv(wt, idx, val)
+
+    wt_g, x_g = dev(wt), dev(x)
+    m_g, i_g, v_g, n_g = sa.act_sparsify_threshold(x_g, t)
+    check_lists(m_g, i_g, v_g, n_g, x, keep)
+    assert_close(sa.sparse_gemv(wt_g, i_g, v_g, n_g), y_ref)
+    assert_close(sa.sparse_gemv_threshold(wt_g, x_g, t), y_ref)
+    assert_close(sa.masked_gemv(wt_g, x_g, m_g), y_ref)
+    # the GPU calibration of the same percentile gives the same fp32 threshold
+    assert float(host(sa.act_calibrate_threshold(x_g, 0.5))[0]) == t
+
+
+@pytest.mark.parametrize("d", [1, 31, 32, 33, 100, 1000, 4097, 11008, 14336, 16385, 40000])
+def test_threshold_ragged_and_edges(d):
+    rng = np.random.default_rng(d)
+    X = syn.laplace_f16((3, d), 1.0, d)
+    X[0, ::7] = 0
+    X[1, ::5] = np.float16(-0.0)
+    t = float(np.float32(0.6931))
+    X[2, ::3] = np.float16(t)  # ties at t are kept (>=)
+    for tt in (t, 0.0, 1e4):
+        keep = sparsify.threshold_sparsify(X, tt)[0]
+        check_lists(*sa.act_sparsify_threshold(dev(X), tt), X, keep)
+    # a row start that is not 16-byte aligned takes the scalar path
+    big = np.concatenate([np.zeros(1, np.float16), X.reshape(-1)])
+    xg = dev(big)[1:].view(3, d)
+    keep = sparsify.threshold_sparsify(X, t)[0]
+    check_lists(*sa.act_sparsify_threshold(xg, t), X, keep)
+    assert rng is not None
+
+
+# ---------------------------------------------------------------------------
+# Llama-2-7B decoder layer at batch 1: fused threshold + GEMV per projection
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["q", "o", "gate", "down"])
+@pytest.mark.parametrize("sparsity", [0.4, 0.5, 0.6])
+def test_llama2_layer_projection(name, sparsity):
+    d_out, d_in, inp = syn.LLAMA2_7B[name]
+    _, dist = syn.LLAMA2_7B_INPUTS[inp]
+    wt = syn.weight_t(d_out, d_in, syn.weight_seed(name))
+    x = syn.activation((d_in,), dist, 0)
+    samples = syn.calibration_samples(inp)
+    t = float(calibrate.magnitude_threshold(samples, sparsity))
+    keep, idx, val, nnz = sparsify.threshold_sparsify(x, t)
+    y_ref = gemv.sparse_gemv(wt, idx, val)
+
+    wt_g, x_g = dev(wt), dev(x)
+    t_g = float(host(sa.act_calibrate_threshold(dev(samples), sparsity))[0])
+    assert t_g == t
+    assert_close(sa.sparse_gemv_threshold(wt_g, x_g, t), y_ref)
+    m_g, i_g, v_g, n_g = sa.act_sparsify_threshold(x_g, t)
+    check_lists(m_g, i_g, v_g, n_g, x, keep)
+    assert_close(sa.sparse_gemv(wt_g, i_g, v_g, n_g), y_ref)
+
+
+def test_dense_gemv_matches_oracle():
+    for (d_out, d_in) in [(4096, 11008), (11008, 4096), (1024, 1024), (72, 130)]:
+        wt = syn.weight_t(d_out, d_in, 5)
+        x = syn.gaussian_f16((2, d_in), 1.0, 6)
+        y = sa.dense_gemv(dev(wt), dev(x))
+        assert_close(y, np.stack([gemv.dense_gemv(wt, x[b]) for b in range(2)]))
+
+
+def test_threshold_zero_reproduces_dense():
+    wt = syn.weight_t(4096, 4096, 7)
+    x = syn.gaussian_f16((4096,), 1.0, 8)
+    x[::11] = 0
+    y_sparse = sa.sparse_gemv_threshold(dev(wt), dev(x), 0.0)
+    ref = gemv.dense_gemv(wt, x)
+    assert_close(y_sparse, ref)
+    # the dense kernel also multiplies the zero entries, so its rows are split
+    # differently across lanes: same result up to fp32 summation order
+    assert_close(sa.dense_gemv(dev(wt), dev(x)), ref)
+
+
+def test_empty_and_full_lists():
+    wt = syn.weight_t(512, 300, 9)
+    x = syn.gaussian_f16((300,), 1.0, 10)
+    wt_g, x_g = dev(wt), dev(x)
+    y = sa.sparse_gemv_threshold(wt_g, x_g, 1e4)  # nothing survives
+    assert torch.count_nonzero(y).item() == 0
+    m, i, v, n = sa.act_sparsify_threshold(x_g, 1e4)
+    assert host(n)[0] == 0
+    assert torch.count_nonzero(sa.sparse_gemv(wt_g, i, v, n)).item() == 0
+    m, i, v, n = sa.act_sparsify_topk(x_g, 300)  # everything survives
+    assert_close(sa.sparse_gemv(wt_g, i, v, n), gemv.dense_gemv(wt, x))
+
+
+def test_ragged_output_tiles():
+    """d_out not a multiple of any tile width, d_in spanning a ragged slice."""
+    for d_out, d_in in [(8, 5), (136, 777), (1032, 3000), (4104, 11009)]:
+        wt = syn.weight_t(d_out, d_in, 11)
+        x = syn.laplace_f16((3, d_in), 1.0, 12)
+        t = 0.69
+        keep = sparsify.threshold_sparsify(x, t)[0]
+        ref = gemv.batched_masked_gemv(wt, x, keep)
+        assert_close(sa.sparse_gemv_threshold(dev(wt), dev(x), t), ref)
+
+
+def test_deterministic_and_stream():
+    d_out, d_in, _ = syn.LLAMA2_7B["down"]
+    wt = dev(syn.weight_t(d_out, d_in, 13))
+    x = dev(syn.laplace_f16((d_in,), 1.0, 14))
+    y1 = sa.sparse_gemv_threshold(wt, x, 0.69)
+    # calls sharing the per-device workspace must be ordered: the side stream
+    # waits for the default one, and vice versa afterwards
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y2 = sa.sparse_gemv_threshold(wt, x, 0.69)
+        m, i, v, n = sa.act_sparsify_threshold(x, 0.69)
+        y3 = sa.sparse_gemv(wt, i, v, n)
+    torch.cuda.current_stream().wait_stream(s)
+    s.synchronize()
+    assert torch.equal(y1, y2)
+    m2, i2, v2, n2 = sa.act_sparsify_threshold(x, 0.69)
+    torch.cuda.synchronize()
+    assert torch.equal(m, m2) and torch.equal(n, n2)
+    nn = int(host(n)[0])
+    assert torch.equal(i[:nn], i2[:nn])
+    assert_close(y3, host(y1).astype(np.float64))
+
+
+@pytest.mark.parametrize("tiling", range(11))
+def test_every_tiling_headline(tiling):
+    d_out, d_in, _ = syn.LLAMA2_7B["down"]
+    wt = syn.weight_t(d_out, d_in, syn.weight_seed("down"))
+    x = syn.laplace_f16((d_in,), 1.0, 3)
+    t = 0.69
+    keep, idx, val, nnz = sparsify.threshold_sparsify(x, t)
+    ref = gemv.sparse_gemv(wt, idx, val)
+    wt_g, x_g = dev(wt), dev(x)
+    try:
+        for target in (0, 256, 4096):
+            sa.set_gemv_tuning(tiling, target)
+            assert_close(sa.sparse_gemv_threshold(wt_g, x_g, t), ref)
+            m, i, v, n = sa.act_sparsify_threshold(x_g, t)
+            assert_close(sa.sparse_gemv(wt_g, i, v, n), ref)
+            assert_close(sa.dense_gemv(wt_g, x_g), gemv.dense_gemv(wt, x))
+    finally:
+        sa.set_gemv_tuning(-1, 0)
+
+
+# ---------------------------------------------------------------------------
+# Top-K (Q-Sparse) + batched union GEMV
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [4096, 11008])
+@pytest.mark.parametrize("pct", [60, 50, 40])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_topk_and_union_gemv(d, pct, batch):
+    k = syn.topk_k(pct, d)
+    X = syn.laplace_f16((batch, d), 1.0, 100 + batch)
+    keep, idx, val, nnz = sparsify.topk_sparsify(X, k)
+    d_out = 11008 if d == 4096 else 4096
+    wt = syn.weight_t(d_out, d, 20 + d)
+    ref = gemv.batched_masked_gemv(wt, X, keep)
+
+    X_g, wt_g = dev(X), dev(wt)
+    m_g, i_g, v_g, n_g = sa.act_sparsify_topk(X_g, k)
+    check_lists(m_g, i_g, v_g, n_g, X, keep)
+    assert np.all(host(n_g) == k)
+    assert_close(sa.sparse_gemv(wt_g, i_g, v_g, n_g), ref)
+    assert_close(sa.masked_gemv(wt_g, X_g, m_g), ref)
+
+
+@pytest.mark.parametrize("d", [1, 5, 64, 100, 4097, 16384, 16385, 30000])
+def test_topk_edges_and_ties(d):
+    rng = np.random.default_rng(d)
+    pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, 0.25], dtype=np.float16)
+    X = np.stack([pool[rng.integers(0, len(pool), size=d)], syn.laplace_f16((d,), 1.0, d)])
+    for k in sorted({0, 1, d // 3, d // 2, d - 1, d} - {-1}):
+        if k < 0:
+            continue
+        keep = sparsify.topk_sparsify(X, k)[0]
+        check_lists(*sa.act_sparsify_topk(dev(X), k), X, keep)
+
+
+# ---------------------------------------------------------------------------
+# calibration
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("inp", ["attn_in", "o_in", "mlp_in", "down_in"])
+def test_calibration_bit_exact(inp):
+    smp = syn.calibration_samples(inp)
+    g = dev(smp)
+    for s in (0.0, 0.1, 0.4, 0.5, 0.6, 0.7, 0.99, 1.0):
+        t_ref = calibrate.magnitude_threshold(smp, s)
+        t_gpu = host(sa.act_calibrate_threshold(g, s))[0]
+        assert np.float32(t_gpu).view(np.uint32) == np.float32(t_ref).view(np.uint32), (s,)
+
+
+def test_calibration_small_n():
+    for n in (1, 2, 3, 7, 1025):
+        smp = syn.laplace_f16((n,), 1.0, n)
+        for s in (0.0, 0.3, 0.5, 1.0):
+            t_ref = calibrate.magnitude_threshold(smp, s)
+            assert host(sa.act_calibrate_threshold(dev(smp), s))[0] == t_ref
+
+
+# ---------------------------------------------------------------------------
+# N:M sparsifier
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 4), (3, 4), (8, 8),
+                                 (5, 16), (31, 32), (32, 32)])
+def test_nm_small(n, m):
+    X = syn.gaussian_f16((64, 1024), 1.0, n * 100 + m)
+    X[3, :] = np.float16(0.5)  # all ties
+    X[4, ::2] = np.float16(-0.0)
+    keep, vals = sparsify.nm_sparsify(X, n, m)
+    mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
+    assert np.array_equal(words(mask_g), sparsify.pack_mask(keep))
+    assert np.array_equal(host(val_g).view(np.uint16), vals.view(np.uint16))
+
+
+@pytest.mark.parametrize("shape", [(4096, 1024), (2048, 4096)])
+@pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (16, 32)])
+def test_nm_full_shapes(shape, n, m):
+    X = syn.gaussian_f16(shape, 1.0, 7)
+    keep, vals = sparsify.nm_sparsify(X, n, m)
+    mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
+    w = words(mask_g)
+    assert np.array_equal(w, sparsify.pack_mask(keep))
+    assert np.array_equal(host(val_g).view(np.uint16), vals.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# masked SwiGLU down projection (CATS / RaNA), Llama-3-8B MLP shape
+# ---------------------------------------------------------------------------
+
+def test_col_norms():
+    wdt = syn.weight_t(4096, 14336, 30)
+    ref = swiglu.column_norms(wdt)
+    got = host(sa.weight_col_norms(dev(wdt)))
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("mode", ["cats", "rana"])
+@pytest.mark.parametrize("rate", [0.5, 0.7])
+def test_masked_swiglu_down(mode, rate):
+    d_model, d_ff = syn.LLAMA3_8B_MLP["d_model"], syn.LLAMA3_8B_MLP["d_ff"]
+    g, u = syn.swiglu_gate_up(d_ff, d_model, 0)
+    wdt = syn.weight_t(d_model, d_ff, 31)
+    cn = swiglu.column_norms(wdt)
+    sc = swiglu.scores(g, u, mode, cn)
+    t = swiglu.threshold_for_mask_rate(sc, rate)
+    keep, y_ref = swiglu.masked_swiglu_down(g, u, wdt, t, mode, cn)
+
+    wdt_g = dev(wdt)
+    cn_g = sa.weight_col_norms(wdt_g) if mode == "rana" else None
+    y, mask, nnz = sa.masked_swiglu_down(dev(g), dev(u), wdt_g, t, mode, cn_g)
+    got = sparsify.unpack_mask(words(mask), d_ff)
+    # the decision is taken in fp64 on both sides; entries whose score lies
+    # within 1e-12 of t could differ by the last ulp of exp -- none expected
+    ambiguous = np.abs(sc - t) <= 1e-12 * t
+    assert ambiguous.sum() == 0
+    assert np.array_equal(got, keep)
+    assert host(nnz)[0] == keep.sum()
+    assert abs(1 - keep.mean() - rate) < 0.01
+    assert_close(y, y_ref)
+
+
+def test_masked_swiglu_t0_dense():
+    g, u = syn.swiglu_gate_up(1000, 256, 3)
+    wdt = syn.weight_t(256, 1000, 32)
+    keep, y_ref = swiglu.masked_swiglu_down(g, u, wdt, 0.0, "cats")
+    y, mask, nnz = sa.masked_swiglu_down(dev(g), dev(u), dev(wdt), 0.0, "cats")
+    assert host(nnz)[0] == 1000
+    assert_close(y, y_ref)
+
+
+def test_split_k_handoff_is_deterministic():
+    """Many back-to-back split-K calls on rotating weights: every result must
+    equal the first one bit for bit (the cross-workgroup hand-off is exact)."""
+    d_out, d_in, _ = syn.LLAMA2_7B["down"]
+    wt0 = syn.weight_t(d_out, d_in, 15)
+    x = dev(syn.laplace_f16((d_in,), 1.0, 16))
+    wts = [dev(wt0), dev(np.ascontiguousarray(wt0[::-1]))]
+    try:
+        for tiling, target in [(-1, 0), (0, 4096), (6, 1024), (2, 2048), (8, 0), (10, 0)]:
+            sa.set_gemv_tuning(tiling, target)
+            ref = [sa.sparse_gemv_threshold(w, x, 0.69).clone() for w in wts]
+            outs = [sa.sparse_gemv_threshold(wts[i % 2], x, 0.69) for i in range(200)]
+            torch.cuda.synchronize()
+            for i, y in enumerate(outs):
+                assert torch.equal(y, ref[i % 2]), (tiling, target, i)
+    finally:
+        sa.set_gemv_tuning(-1, 0)
