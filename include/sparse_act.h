@@ -228,7 +228,8 @@ int dense_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in,
  *   xval [T][d_in*n/m] fp16;  mask [T][d_in/32] (exactly n bits per group)
  *   wt   [d_in][d_out] fp16;  y [T][d_out] fp16
  * Requires m in {4,8,16,32}, 1 <= n <= m, d_in % 32 == 0, d_out % 8 == 0,
- * wt/y 16-byte aligned.
+ * wt, y and xval 16-byte aligned.  A mask that breaks the N:M contract gives
+ * unspecified values but never an out-of-bounds access.
  */
 int nm_act_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
                 int64_t d_in, int n, int m, const uint16_t* wt, int64_t d_out,

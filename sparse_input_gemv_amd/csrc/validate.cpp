@@ -196,8 +196,8 @@ int check_nm_spmm(const void* xval, const void* mask, int64_t T, int64_t d_in, i
   REQUIRE(d_out >= 8 && d_out % 8 == 0, SA_ERR_INVALID_ARG,
           "%s: d_out must be a positive multiple of 8", fn);
   REQUIRE(xval && mask && wt && y, SA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-  REQUIRE(aligned(wt, 16) && aligned(y, 16) && aligned(mask, 4) && aligned(xval, 2),
-          SA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  REQUIRE(aligned(wt, 16) && aligned(y, 16) && aligned(mask, 4) && aligned(xval, 16),
+          SA_ERR_INVALID_ARG, "%s: wt, y and xval must be 16-byte aligned, mask 4-byte", fn);
   return SA_OK;
 }
 

@@ -360,3 +360,55 @@ def test_split_k_handoff_is_deterministic():
                 assert torch.equal(y, ref[i % 2]), (tiling, target, i)
     finally:
         sa.set_gemv_tuning(-1, 0)
+
+
+# ---------------------------------------------------------------------------
+# batched N:M matmul and the dense MFMA GEMM
+# ---------------------------------------------------------------------------
+
+from oracle import spmm  # noqa: E402
+
+
+@pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 1024), (130, 96, 136), (1, 32, 8),
+                                          (257, 4096, 264)])
+def test_dense_gemm_small(T, d_in, d_out):
+    X = syn.gaussian_f16((T, d_in), 1.0, T)
+    wt = syn.weight_t(d_out, d_in, d_in)
+    Y = sa.dense_gemm(dev(X), dev(wt))
+    assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 4), (3, 4), (5, 16),
+                                 (32, 32)])
+@pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 512), (100, 96, 136)])
+def test_nm_spmm_small(n, m, T, d_in, d_out):
+    if d_in % m:
+        pytest.skip("d_in not a multiple of m")
+    X = syn.gaussian_f16((T, d_in), 1.0, n * 7 + m)
+    wt = syn.weight_t(d_out, d_in, 40 + m)
+    keep, vals = sparsify.nm_sparsify(X, n, m)
+    ref = spmm.nm_spmm(X, keep, wt)
+    mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
+    Y = sa.nm_act_spmm(val_g, mask_g, n, m, dev(wt))
+    assert_close(Y, ref)
+    # each token's row is that token's masked GEMV
+    r = 3
+    assert_close(sa.masked_gemv(dev(wt), dev(X[r]), mask_g[r]), ref[r])
+
+
+@pytest.mark.parametrize("T,d_in,d_out", [(4096, 1024, 1024), (2048, 4096, 11008)])
+@pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (16, 32)])
+def test_nm_spmm_full_shapes_sampled(T, d_in, d_out, n, m):
+    X = syn.gaussian_f16((T, d_in), 1.0, 5)
+    wt = syn.weight_t(d_out, d_in, 41)
+    X_g, wt_g = dev(X), dev(wt)
+    mask_g, val_g = sa.act_sparsify_nm(X_g, n, m)
+    Y = sa.nm_act_spmm(val_g, mask_g, n, m, wt_g)
+    Yd = sa.dense_gemm(X_g, wt_g)
+    rows = np.random.default_rng(T).choice(T, size=6, replace=False)
+    rows = np.concatenate([rows, [0, T - 1]])
+    keep = sparsify.nm_sparsify(X[rows], n, m)[0]
+    assert np.array_equal(sparsify.unpack_mask(words(mask_g)[rows], d_in), keep)
+    ref = spmm.nm_spmm(X[rows], keep, wt)
+    assert_close(Y[torch.from_numpy(rows).to(DEV)], ref)
+    assert_close(Yd[torch.from_numpy(rows).to(DEV)], X[rows].astype(np.float64) @ wt.astype(np.float64))
