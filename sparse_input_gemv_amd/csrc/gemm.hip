@@ -40,7 +40,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16 __attribute__((ext_vector_type(16)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 
-enum AKind : int { kADense = 0, kANM = 1, kA24 = 2 };
+enum AKind : int { kADense = 0, kANM = 1, kA24 = 2, kANMVec = 3 };
 
 struct GParams {
   const uint16_t* x;      // dense: X [T][d_in]; sparse: compressed values [T][d_in*n/m]
@@ -90,8 +90,12 @@ __device__ __forceinline__ void store_b(uint16_t* Bs, const BRegs& r) {
 // one row: its mask bits and the kept values before it in the row tile.
 // 2:4: the same thread loads the 8 compressed values of its 16 dense k and
 // turns the 16 mask bits into the 16-bit sparse-MFMA position code.
+// N:M with m | 4n (every pattern of the workloads): a row tile of 32 dense k
+// holds exactly 32n/m kept values, a whole number of 16-byte words at a
+// 16-byte aligned offset, so thread row = tid (< 128) loads them with vector
+// loads and scatters them by the set bits of the row's mask word.
 struct ARegs {
-  u32x4 v[2];
+  u32x4 v[4];
   uint32_t bits;
 };
 
@@ -109,6 +113,20 @@ __device__ __forceinline__ void load_a(const GParams& p, int64_t m0, int64_t k0,
                    : u32x4{0u, 0u, 0u, 0u};
     }
     r.bits = 0;
+  } else if constexpr (AK == kANMVec) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.v[q] = u32x4{0u, 0u, 0u, 0u};
+    r.bits = 0;
+    const int64_t row = m0 + tid;
+    if (tid < BM && row < p.T && k0 < p.d_in) {
+      const int64_t kc = p.d_in * p.n / p.m;
+      const int C = 32 * p.n / p.m;  // multiple of 8
+      r.bits = p.mask[row * (p.d_in / 32) + k0 / 32];
+      const uint16_t* src = p.x + row * kc + k0 * p.n / p.m;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (8 * q < C) r.v[q] = *reinterpret_cast<const u32x4*>(src + 8 * q);
+    }
   } else {
     const int half = tid % 2;
     const int64_t row = m0 + tid / 2;
@@ -154,6 +172,22 @@ __device__ __forceinline__ void store_a(uint16_t* As, uint32_t* Aidx, const AReg
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       *reinterpret_cast<u32x4*>(As + (tid / 4 + 64 * h) * LDA + 8 * q) = r.v[h];
+  } else if constexpr (AK == kANMVec) {
+    if (tid < BM) {
+      uint16_t* dst = As + tid * LDA;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(dst + 8 * q) = u32x4{0u, 0u, 0u, 0u};
+      uint32_t bits = r.bits;
+#pragma unroll
+      for (int sidx = 0; sidx < 32; ++sidx) {
+        const uint32_t word = r.v[sidx / 8][(sidx % 8) / 2];  // static register index
+        const uint16_t hv = (uint16_t)((sidx & 1) ? (word >> 16) : (word & 0xffffu));
+        if (bits != 0u) {
+          dst[__builtin_ctz(bits)] = hv;
+          bits &= bits - 1u;
+        }
+      }
+    }
   } else if constexpr (AK == kANM) {
     // zero-fill the 16 dense slots, then scatter the kept values (position
     // order) to the positions of the set mask bits, lowest first
@@ -165,11 +199,12 @@ __device__ __forceinline__ void store_a(uint16_t* As, uint32_t* Aidx, const AReg
     uint32_t bits = r.bits;
 #pragma unroll
     for (int sidx = 0; sidx < 16; ++sidx) {
-      if (bits == 0u) break;
-      const int pos = __builtin_ctz(bits);
-      bits &= bits - 1u;
-      const uint32_t word = r.v[sidx / 8][(sidx % 8) / 2];
-      dst[pos] = (uint16_t)((sidx & 1) ? (word >> 16) : (word & 0xffffu));
+      const uint32_t word = r.v[sidx / 8][(sidx % 8) / 2];  // static register index
+      const uint16_t hv = (uint16_t)((sidx & 1) ? (word >> 16) : (word & 0xffffu));
+      if (bits != 0u) {
+        dst[__builtin_ctz(bits)] = hv;
+        bits &= bits - 1u;
+      }
     }
   } else {
     // compressed values: 8 halves per (row, half) -> As[row][8*half .. +8]
@@ -331,9 +366,10 @@ hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
   p.d_out = d_out;
   p.n = n;
   p.m = m;
-  // 2:4 on the sparse MFMA; every other pattern (16 dense k per staging
-  // thread hold at most 16 kept values) through zero-filled dense tiles
+  // 2:4 on the sparse MFMA; every other pattern through zero-filled dense
+  // tiles (vector loads when m divides 4n)
   if (n == 2 && m == 4) return launch_kind<kA24>(p, s);
+  if ((4 * n) % m == 0) return launch_kind<kANMVec>(p, s);
   return launch_kind<kANM>(p, s);
 }
 

@@ -232,11 +232,21 @@ __global__ __launch_bounds__(NT) void k_sparsify_topk(
 // kept iff fewer than n entries of its group rank before it, where j ranks
 // before i iff |x_j| > |x_i|, or they are equal and j < i.  The flattened
 // array is a sequence of groups because d % M == 0 and d % 32 == 0.
+// Every group yields exactly n values, so a workgroup's 2048 entries give a
+// fixed, contiguous run of 2048*n/M outputs: the kept values are placed in
+// LDS at their slots and the run is written out with 16-byte stores.
+constexpr int kNmThreads = 256;
+constexpr int kNmPerBlock = kNmThreads * 8;
+
 template <int M>
-__global__ __launch_bounds__(256) void k_sparsify_nm(const uint16_t* __restrict__ x, int64_t n8,
-                                                     int n, uint32_t* __restrict__ mask,
-                                                     uint16_t* __restrict__ val) {
-  const int64_t g8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __restrict__ x,
+                                                            int64_t n8, int n,
+                                                            uint32_t* __restrict__ mask,
+                                                            uint16_t* __restrict__ val,
+                                                            int vec_out) {
+  __shared__ __align__(16) uint16_t outs[kNmPerBlock];
+  const int tid = (int)threadIdx.x;
+  const int64_t g8 = (int64_t)blockIdx.x * kNmThreads + tid;
   const bool active = g8 < n8;
   const int lane = lane_id();
   u32x4 raw = {0u, 0u, 0u, 0u};
@@ -267,12 +277,12 @@ __global__ __launch_bounds__(256) void k_sparsify_nm(const uint16_t* __restrict_
         }
         if (rank < n) keep |= 1u << p;
       }
+      // local group index gi of thread tid -> slots (tid*GPT + gi)*n ...
       if (active) {
-        const int64_t grp = g8 * GPT + gi;
-        int slot = 0;
+        int slot = (tid * GPT + gi) * n;
 #pragma unroll
         for (int i = 0; i < M; ++i)
-          if ((keep >> (gi * M + i)) & 1u) val[grp * n + slot++] = v[gi * M + i];
+          if ((keep >> (gi * M + i)) & 1u) outs[slot++] = v[gi * M + i];
       }
     }
   } else {
@@ -310,11 +320,10 @@ __global__ __launch_bounds__(256) void k_sparsify_nm(const uint16_t* __restrict_
       pre += (q < gl) ? c : 0;
     }
     if (active) {
-      const int64_t grp = (g8 * 8) / M;
-      int slot = pre;
+      int slot = (tid / G) * n + pre;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if ((keep >> i) & 1u) val[grp * n + slot++] = v[i];
+        if ((keep >> i) & 1u) outs[slot++] = v[i];
     }
   }
   // four neighbouring threads make one 32-bit mask word
@@ -322,6 +331,19 @@ __global__ __launch_bounds__(256) void k_sparsify_nm(const uint16_t* __restrict_
   w |= (uint32_t)__shfl_xor((int)w, 1, kWave);
   w |= (uint32_t)__shfl_xor((int)w, 2, kWave);
   if (active && (lane & 3) == 0) mask[g8 >> 2] = w;
+
+  __syncthreads();
+  // this workgroup's entries and outputs
+  const int64_t first = (int64_t)blockIdx.x * kNmThreads;
+  const int64_t nthr = (n8 - first) < kNmThreads ? (n8 - first) : kNmThreads;
+  const int count = (int)(nthr * 8 / M) * n;
+  uint16_t* dst = val + first * 8 / M * n;
+  if (vec_out && (count % 8) == 0) {
+    for (int i = tid; i < count / 8; i += kNmThreads)
+      *reinterpret_cast<u32x4*>(dst + 8 * i) = *reinterpret_cast<const u32x4*>(outs + 8 * i);
+  } else {
+    for (int i = tid; i < count; i += kNmThreads) dst[i] = outs[i];
+  }
 }
 
 }  // namespace
@@ -352,19 +374,24 @@ hipError_t launch_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int6
 hipError_t launch_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
                               uint32_t* mask, uint16_t* val, hipStream_t s) {
   const int64_t n8 = rows * d / 8;
-  const dim3 grid((unsigned)((n8 + 255) / 256));
+  const dim3 grid((unsigned)((n8 + kNmThreads - 1) / kNmThreads));
+  // whole runs are 16-byte aligned when the output base is (2048*n/M halves
+  // per workgroup is a multiple of 64)
+  const int vec = (reinterpret_cast<uintptr_t>(val) & 15u) == 0 ? 1 : 0;
   switch (m) {
     case 4:
-      hipLaunchKernelGGL(k_sparsify_nm<4>, grid, dim3(256), 0, s, x, n8, n, mask, val);
+      hipLaunchKernelGGL(k_sparsify_nm<4>, grid, dim3(kNmThreads), 0, s, x, n8, n, mask, val, vec);
       break;
     case 8:
-      hipLaunchKernelGGL(k_sparsify_nm<8>, grid, dim3(256), 0, s, x, n8, n, mask, val);
+      hipLaunchKernelGGL(k_sparsify_nm<8>, grid, dim3(kNmThreads), 0, s, x, n8, n, mask, val, vec);
       break;
     case 16:
-      hipLaunchKernelGGL(k_sparsify_nm<16>, grid, dim3(256), 0, s, x, n8, n, mask, val);
+      hipLaunchKernelGGL(k_sparsify_nm<16>, grid, dim3(kNmThreads), 0, s, x, n8, n, mask, val,
+                         vec);
       break;
     case 32:
-      hipLaunchKernelGGL(k_sparsify_nm<32>, grid, dim3(256), 0, s, x, n8, n, mask, val);
+      hipLaunchKernelGGL(k_sparsify_nm<32>, grid, dim3(kNmThreads), 0, s, x, n8, n, mask, val,
+                         vec);
       break;
     default:
       return hipErrorInvalidValue;
