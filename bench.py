@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0
 D_OUT, D_IN = 4096, 11008
 SPARSITY = 0.5
 ROTATION_BYTES = 1 << 30
+COPY_BYTES = 256 << 20
 GEMV_SOURCE = os.path.join(ROOT, "sparse_input_gemv_amd", "csrc", "gemv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_gemv_threshold_down_4096x11008.json")
 
@@ -50,6 +51,9 @@ def parse():
     ap.add_argument("--target-wgs", type=int, default=0, help="GEMV workgroup target (tuning)")
     ap.add_argument("--only", choices=["fused", "unfused", "dense"], default=None,
                     help="time a single path (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy 5 times, so hardware byte "
+                         "counters can be scaled against a kernel of known traffic")
     return ap.parse_args()
 
 
@@ -108,6 +112,12 @@ def main():
     ws = sa.workspace(dev, ws_bytes)
     if args.tiling >= 0 or args.target_wgs > 0:
         sa.set_gemv_tuning(args.tiling, args.target_wgs)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     # prebuilt C-ABI argument lists: the timed loop does no Python-side work
