@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--target-wgs", type=int, default=0, help="GEMV workgroup target (tuning)")
     ap.add_argument("--only", choices=["fused", "unfused", "dense"], default=None,
                     help="time a single path (for profiler runs)")
+    ap.add_argument("--suite", action="store_true",
+                    help="instead of the headline line, time every hot-path row on its "
+                         "workload and print one JSON line per measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy 5 times, so hardware byte "
                          "counters can be scaled against a kernel of known traffic")
@@ -90,6 +93,10 @@ def main():
 
     import sparse_input_gemv_amd as sa
     import synthetic as syn
+
+    if args.suite:
+        run_suite(args)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -235,6 +242,180 @@ def main():
     if not args.no_cpu_baseline and not args.only:
         out["cpu_baseline"] = cpu_baseline(rot[0].cpu().numpy(), x_np, t, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def run_suite(args):
+    """Every hot-path row on its workload; one JSON line per measurement.
+
+    HBM-bound kernels rotate their weights over >= 1 GiB of distinct copies;
+    times are HIP events around back-to-back calls on the launch stream.
+    """
+    import torch
+
+    import sparse_input_gemv_amd as sa
+    import synthetic as syn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def ev_time(fn, steps, warmup=20):
+        """GPU time per call: `per` calls captured in a HIP graph, replayed.
+
+        The graph removes the Python binding's per-call host cost (output
+        allocation, argument checks), which for the smallest kernels would
+        otherwise exceed the kernel time.
+        """
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        per = min(steps, 24)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(per):
+                fn(i)
+        reps = max(2, steps // per)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * per) * 1000.0  # us
+
+    def emit(row, name, us, bytes_=None, flops=None, **extra):
+        rec = {"row": row, "name": name, "us": round(us, 3)}
+        if bytes_ is not None:
+            gbs = bytes_ / (us * 1e-6) / 1e9
+            rec.update(bytes=int(bytes_), GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+        if flops is not None:
+            tf = flops / (us * 1e-6) / 1e12
+            rec.update(flops=int(flops), TFLOPs=round(tf, 1))
+        rec.update(extra)
+        print(json.dumps(rec), flush=True)
+
+    def rotation(d_out, d_in, seed):
+        w0 = torch.from_numpy(syn.weight_t(d_out, d_in, seed)).to(dev)
+        n = max(2, -(-ROTATION_BYTES // (w0.numel() * 2)))
+        return [w0] + [torch.roll(w0, shifts=997 * i, dims=0).contiguous() for i in range(1, n)]
+
+    # ---- a9 calibration; a1 threshold; a4 / a8 GEMVs of the Llama-2-7B layer ----
+    thresholds = {}
+    for inp in syn.LLAMA2_7B_INPUTS:
+        smp = torch.from_numpy(syn.calibration_samples(inp)).to(dev)
+        us = ev_time(lambda i: sa.act_calibrate_threshold(smp, 0.5), 200)
+        thresholds[inp] = {s_: float(sa.act_calibrate_threshold(smp, s_).cpu()[0])
+                           for s_ in (0.4, 0.5, 0.6)}
+        emit("a9", f"act_calibrate_threshold {inp} n=10000", us, bytes_=2 * 10000)
+    layer = {"sparse": 0.0, "dense": 0.0}
+    for name, (d_out, d_in, inp) in syn.LLAMA2_7B.items():
+        _, dist = syn.LLAMA2_7B_INPUTS[inp]
+        rot = rotation(d_out, d_in, syn.weight_seed(name))
+        nr = len(rot)
+        x = torch.from_numpy(syn.activation((d_in,), dist, 0)).to(dev)
+        y = torch.empty((d_out,), dtype=torch.float16, device=dev)
+        for sp in (0.4, 0.5, 0.6):
+            t = thresholds[inp][sp]
+            m_, i_, v_, n_ = sa.act_sparsify_threshold(x, t)
+            nnz = int(n_.cpu()[0])
+            us = ev_time(lambda i: sa.sparse_gemv_threshold(rot[i % nr], x, t, y=y), 1000)
+            emit("a4", f"sparse_gemv_threshold {name} {d_out}x{d_in} sparsity {sp}", us,
+                 bytes_=2 * d_out * nnz + 2 * d_in + 2 * d_out, flops=2 * d_out * nnz,
+                 achieved_sparsity=round(1 - nnz / d_in, 4))
+            if sp == 0.5:
+                layer["sparse"] += us
+                us_l = ev_time(lambda i: sa.sparse_gemv(rot[i % nr], i_, v_, n_, y=y), 1000)
+                emit("a4", f"sparse_gemv (list) {name} {d_out}x{d_in} sparsity 0.5", us_l,
+                     bytes_=2 * d_out * nnz + 6 * nnz + 2 * d_out)
+                us_s = ev_time(lambda i: sa.act_sparsify_threshold(x, t), 1000)
+                emit("a1", f"act_sparsify_threshold d={d_in}", us_s,
+                     bytes_=2 * d_in + 6 * nnz + d_in // 8 + 4)
+        us_d = ev_time(lambda i: sa.dense_gemv(rot[i % nr], x, y=y), 1000)
+        layer["dense"] += us_d
+        emit("a8", f"dense_gemv {name} {d_out}x{d_in}", us_d,
+             bytes_=2 * d_out * d_in + 2 * d_in + 2 * d_out, flops=2 * d_out * d_in)
+        del rot
+        torch.cuda.empty_cache()
+    emit("a4", "Llama-2-7B layer, 7 projections at 50% vs dense (sum of calls)",
+         layer["sparse"], speedup_vs_dense=round(layer["dense"] / layer["sparse"], 3),
+         dense_us=round(layer["dense"], 3))
+
+    # ---- a2 Top-K and a5 batched union GEMV -------------------------------------
+    for d in (4096, 11008):
+        d_out = 11008 if d == 4096 else 4096
+        rot = rotation(d_out, d, 20 + d)
+        nr = len(rot)
+        for batch in (1, 2, 4, 8):
+            X = torch.from_numpy(syn.laplace_f16((batch, d), 1.0, 100 + batch)).to(dev)
+            y = torch.empty((batch, d_out), dtype=torch.float16, device=dev)
+            k = syn.topk_k(50, d)
+            m_, i_, v_, n_ = sa.act_sparsify_topk(X, k)
+            shifts = torch.arange(32, device=dev, dtype=torch.int32)
+            bits = ((m_.unsqueeze(-1) >> shifts) & 1).reshape(batch, -1)[:, :d]
+            union = int(torch.count_nonzero(bits.any(0)).cpu())
+            us_k = ev_time(lambda i: sa.act_sparsify_topk(X, k), 500)
+            emit("a2", f"act_sparsify_topk d={d} K=50% batch={batch}", us_k,
+                 bytes_=batch * (2 * d + 6 * k + d // 8 + 4))
+            us = ev_time(lambda i: sa.sparse_gemv(rot[i % nr], i_, v_, n_, y=y), 500)
+            emit("a5", f"sparse_gemv union {d_out}x{d} K=50% batch={batch}", us,
+                 bytes_=2 * d_out * union + 6 * batch * k + 2 * batch * d_out,
+                 flops=2 * d_out * k * batch, union_frac=round(union / d, 4))
+        del rot
+        torch.cuda.empty_cache()
+
+    # ---- a6 masked SwiGLU down projection (Llama-3-8B MLP) ----------------------
+    d_model, d_ff = syn.LLAMA3_8B_MLP["d_model"], syn.LLAMA3_8B_MLP["d_ff"]
+    rot = rotation(d_model, d_ff, 31)
+    nr = len(rot)
+    g, u = (torch.from_numpy(a).to(dev) for a in syn.swiglu_gate_up(d_ff, d_model, 0))
+    cn = [sa.weight_col_norms(w) for w in rot[:1]][0]
+    y = torch.empty((d_model,), dtype=torch.float16, device=dev)
+    x_dense = torch.from_numpy(syn.gaussian_f16((d_ff,), 1.0, 0)).to(dev)
+    us_d = ev_time(lambda i: sa.dense_gemv(rot[i % nr], x_dense, y=y), 500)
+    emit("a8", f"dense_gemv down {d_model}x{d_ff}", us_d, bytes_=2 * d_model * d_ff + 2 * d_ff + 2 * d_model)
+    for mode in ("cats", "rana"):
+        for rate in (0.5, 0.7):
+            # threshold at the score quantile of this draw (the library's own calibration)
+            if mode == "cats":
+                sc = torch.abs(torch.nn.functional.silu(g.double()))
+            else:
+                sc = torch.abs(torch.nn.functional.silu(g.double()) * u.double()) * cn
+            t = float(torch.quantile(sc.cpu(), rate))
+            yy, mk, nz = sa.masked_swiglu_down(g, u, rot[0], t, mode, cn if mode == "rana" else None)
+            nnz = int(nz.cpu()[0])
+            us = ev_time(lambda i: sa.masked_swiglu_down(g, u, rot[i % nr], t, mode,
+                                                          cn if mode == "rana" else None, y=y,
+                                                          with_mask=False), 500)
+            extra = 8 * d_ff if mode == "rana" else 0
+            emit("a6", f"masked_swiglu_down {mode} mask rate {rate}", us,
+                 bytes_=2 * d_model * nnz + 4 * d_ff + extra + 2 * d_model, flops=2 * d_model * nnz,
+                 kept=nnz, speedup_vs_dense_down=round(us_d / us, 3))
+    us_c = ev_time(lambda i: sa.weight_col_norms(rot[i % nr]), 50)
+    emit("a6", f"weight_col_norms {d_ff}x{d_model}", us_c, bytes_=2 * d_ff * d_model + 8 * d_ff)
+    del rot
+    torch.cuda.empty_cache()
+
+    # ---- a3 N:M sparsify, a7 N:M matmul, a8 dense GEMM -------------------------
+    for (T, d_in, d_out) in [(4096, 1024, 1024), (2048, 4096, 11008)]:
+        X = torch.from_numpy(syn.gaussian_f16((T, d_in), 1.0, 5)).to(dev)
+        wt = torch.from_numpy(syn.weight_t(d_out, d_in, 41)).to(dev)
+        y = torch.empty((T, d_out), dtype=torch.float16, device=dev)
+        dense_flop = 2 * T * d_in * d_out
+        steps = 200 if T * d_in * d_out < 1e10 else 30
+        us_g = ev_time(lambda i: sa.dense_gemm(X, wt, y=y), steps, warmup=3)
+        emit("a8", f"dense_gemm {T}x{d_in}x{d_out}", us_g, flops=dense_flop,
+             frac_mfma=round(dense_flop / (us_g * 1e-6) / 2.5e15, 4))
+        for (n, m) in [(2, 4), (8, 16), (16, 32)]:
+            mask, val = sa.act_sparsify_nm(X, n, m)
+            us_s = ev_time(lambda i: sa.act_sparsify_nm(X, n, m), 200)
+            emit("a3", f"act_sparsify_nm {n}:{m} {T}x{d_in}", us_s,
+                 bytes_=2 * T * d_in + 2 * T * d_in * n // m + T * d_in // 8)
+            us = ev_time(lambda i: sa.nm_act_spmm(val, mask, n, m, wt, y=y), steps, warmup=3)
+            alg = dense_flop * n // m
+            emit("a7", f"nm_act_spmm {n}:{m} {T}x{d_in}x{d_out}", us, flops=alg,
+                 frac_mfma=round(alg / (us * 1e-6) / (2 * 2.5e15 if (n, m) == (2, 4) else 2.5e15), 4),
+                 speedup_vs_dense_gemm=round(us_g / us, 3))
 
 
 def cpu_baseline(wt, x, t, seconds):
