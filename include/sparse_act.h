@@ -255,6 +255,12 @@ int dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
  * Returns SA_ERR_INVALID_ARG for an unknown tiling.  Not thread-safe.
  */
 int sa_set_gemv_tuning(int tiling, int target_wgs);
+/*
+ * Process-wide tile height of dense_gemm / nm_act_spmm, for tuning sweeps:
+ * 0 = automatic (256-row tiles when they fill the chip, else 128), or 128 /
+ * 256.  Same result either way.  Not thread-safe.
+ */
+int sa_set_gemm_tuning(int tile_rows);
 /* Describe tiling `i` (tile_o, threads, unroll); tile_o is negative for a
  * full-K tiling (one launch, no split of d_in).  Returns SA_ERR_INVALID_ARG
  * past the last one.  Output pointers are HOST pointers (may be NULL). */

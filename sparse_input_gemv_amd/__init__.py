@@ -27,7 +27,7 @@ __all__ = [
     "act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm",
     "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold", "masked_gemv",
     "dense_gemv", "masked_swiglu_down", "weight_col_norms", "nm_act_spmm", "dense_gemm",
-    "set_gemv_tuning", "gemv_tiling_info", "workspace_bytes", "MAX_BATCH",
+    "set_gemv_tuning", "set_gemm_tuning", "gemv_tiling_info", "workspace_bytes", "MAX_BATCH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_act.so")
@@ -55,6 +55,7 @@ _SIGNATURES = {
     "nm_act_spmm": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp]),
     "dense_gemm": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "sa_set_gemv_tuning": (_i32, [_i32, _i32]),
+    "sa_set_gemm_tuning": (_i32, [_i32]),
     "sa_gemv_tiling_info": (_i32, [_i32, _vp, _vp, _vp]),
 }
 
@@ -337,6 +338,10 @@ def dense_gemm(x: torch.Tensor, wt: torch.Tensor, y: torch.Tensor | None = None)
 
 def set_gemv_tuning(tiling: int = -1, target_wgs: int = 0) -> None:
     _check(lib().sa_set_gemv_tuning(tiling, target_wgs), "sa_set_gemv_tuning")
+
+
+def set_gemm_tuning(tile_rows: int = 0) -> None:
+    _check(lib().sa_set_gemm_tuning(tile_rows), "sa_set_gemm_tuning")
 
 
 def gemv_tiling_info(i: int):

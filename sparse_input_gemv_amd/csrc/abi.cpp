@@ -263,6 +263,15 @@ int sa_set_gemv_tuning(int tiling, int target_wgs) {
   return SA_OK;
 }
 
+int sa_set_gemm_tuning(int tile_rows) {
+  sa::clear_error();
+  if (sa::gemm_set_tile_rows(tile_rows) != 0) {
+    sa::set_error("sa_set_gemm_tuning: tile_rows must be 0, 128 or 256 (got %d)", tile_rows);
+    return SA_ERR_INVALID_ARG;
+  }
+  return SA_OK;
+}
+
 int sa_gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll) {
   sa::clear_error();
   if (sa::gemv_tiling_info(i, tile_o, threads, unroll) != 0) {

@@ -6,9 +6,10 @@
 // large batches the activations of every token are N:M sparse -- Block
 // Q-Sparse -- and the product is measured against a dense matmul.)
 //
-// One tile engine: a 256-thread workgroup computes a 128 x 128 output tile
-// with four waves (2 x 2), each wave 64 x 64 = 2 x 2 blocks of 32 x 32.  The
-// K loop steps by 32 with double-buffered LDS tiles:
+// One tile engine: a 256-thread workgroup computes a BM x 128 output tile
+// (BM = 256 or 128) with four waves (2 x 2), each wave (BM/2) x 64 = (BM/64)
+// x 2 blocks of 32 x 32.  The K loop steps by 32 with double-buffered LDS
+// tiles:
 //   B (WT, contiguous along the output index) is transposed into LDS as
 //     [n][k] while being staged, two k rows packed per 32-bit LDS word, so
 //     each lane's MFMA B operand is one or two 16-byte LDS reads;
@@ -32,7 +33,7 @@
 namespace sa {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32, NTH = 256;
+constexpr int BN = 128, BK = 32, NTH = 256;
 constexpr int LDA = BK + 8;  // halves per LDS row of A (padding against bank conflicts)
 constexpr int LDB = BK + 8;  // halves per LDS row of B^T
 
@@ -85,63 +86,78 @@ __device__ __forceinline__ void store_b(uint16_t* Bs, const BRegs& r) {
 }
 
 // ---- A staging ---------------------------------------------------------------
-// Dense: thread (q = tid % 4, row = tid / 4 (+64)) loads 8 halves of two rows.
-// N:M (any n, m): thread row = tid / 2, half = tid % 2 handles 16 dense k of
-// one row: its mask bits and the kept values before it in the row tile.
-// 2:4: the same thread loads the 8 compressed values of its 16 dense k and
-// turns the 16 mask bits into the 16-bit sparse-MFMA position code.
-// N:M with m | 4n (every pattern of the workloads): a row tile of 32 dense k
-// holds exactly 32n/m kept values, a whole number of 16-byte words at a
-// 16-byte aligned offset, so thread row = tid (< 128) loads them with vector
-// loads and scatters them by the set bits of the row's mask word.
-struct ARegs {
-  u32x4 v[4];
-  uint32_t bits;
+// Work items of a BM x 32 tile, spread over the 256 threads:
+//   dense   -- (row, 8-wide chunk): BM*4 items, 16-byte loads;
+//   N:M     -- (row, 16-wide half): BM*2 items; the mask bits and the kept
+//              values before the half give where its values start;
+//   2:4     -- (row, half): the 8 compressed values and the 16-bit position
+//              code of the sparse MFMA;
+//   N:M with m | 4n (every pattern of the workloads) -- one row per item: a
+//              32-wide row tile holds exactly 32n/m kept values, a whole number
+//              of 16-byte words at a 16-byte aligned offset, loaded as vectors
+//              and scattered by the set bits of the row's mask word.
+template <int AK>
+struct AItems;
+template <>
+struct AItems<kADense> {
+  static constexpr int kPerRow = 4;
+};
+template <>
+struct AItems<kANM> {
+  static constexpr int kPerRow = 2;
+};
+template <>
+struct AItems<kA24> {
+  static constexpr int kPerRow = 2;
+};
+template <>
+struct AItems<kANMVec> {
+  static constexpr int kPerRow = 1;
 };
 
-template <int AK>
-__device__ __forceinline__ void load_a(const GParams& p, int64_t m0, int64_t k0, ARegs& r) {
+template <int AK, int BM>
+struct ARegs {
+  static constexpr int kItems = (BM * AItems<AK>::kPerRow + NTH - 1) / NTH;
+  static constexpr int kWords = (AK == kANMVec) ? 4 : (AK == kANM ? 2 : 1);
+  u32x4 v[kItems][kWords];
+  uint32_t bits[kItems];
+};
+
+template <int AK, int BM>
+__device__ __forceinline__ void load_a(const GParams& p, int64_t m0, int64_t k0,
+                                       ARegs<AK, BM>& r) {
+  constexpr int PR = AItems<AK>::kPerRow;
   const int tid = (int)threadIdx.x;
-  if constexpr (AK == kADense) {
-    const int q = tid % 4;
+  const int64_t kc = (AK == kADense) ? 0 : p.d_in * p.n / p.m;  // compressed row length
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t row = m0 + tid / 4 + 64 * h;
-      const int64_t k = k0 + 8 * q;
-      r.v[h] = (row < p.T && k < p.d_in)
-                   ? *reinterpret_cast<const u32x4*>(p.x + row * p.d_in + k)
-                   : u32x4{0u, 0u, 0u, 0u};
-    }
-    r.bits = 0;
-  } else if constexpr (AK == kANMVec) {
+  for (int it = 0; it < ARegs<AK, BM>::kItems; ++it) {
+    const int item = tid + it * NTH;
+    const int lrow = item / PR;
+    const int part = item % PR;
+    const int64_t row = m0 + lrow;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r.v[q] = u32x4{0u, 0u, 0u, 0u};
-    r.bits = 0;
-    const int64_t row = m0 + tid;
-    if (tid < BM && row < p.T && k0 < p.d_in) {
-      const int64_t kc = p.d_in * p.n / p.m;
+    for (int q = 0; q < ARegs<AK, BM>::kWords; ++q) r.v[it][q] = u32x4{0u, 0u, 0u, 0u};
+    r.bits[it] = 0;
+    if (lrow >= BM || row >= p.T || k0 >= p.d_in) continue;
+    if constexpr (AK == kADense) {
+      const int64_t k = k0 + 8 * part;
+      if (k < p.d_in) r.v[it][0] = *reinterpret_cast<const u32x4*>(p.x + row * p.d_in + k);
+    } else if constexpr (AK == kANMVec) {
       const int C = 32 * p.n / p.m;  // multiple of 8
-      r.bits = p.mask[row * (p.d_in / 32) + k0 / 32];
+      r.bits[it] = p.mask[row * (p.d_in / 32) + k0 / 32];
       const uint16_t* src = p.x + row * kc + k0 * p.n / p.m;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (8 * q < C) r.v[q] = *reinterpret_cast<const u32x4*>(src + 8 * q);
-    }
-  } else {
-    const int half = tid % 2;
-    const int64_t row = m0 + tid / 2;
-    const int64_t kc = p.d_in * p.n / p.m;  // compressed row length
-    r.v[0] = u32x4{0u, 0u, 0u, 0u};
-    r.v[1] = u32x4{0u, 0u, 0u, 0u};
-    r.bits = 0;
-    if (row < p.T && k0 < p.d_in) {
+        if (8 * q < C) r.v[it][q] = *reinterpret_cast<const u32x4*>(src + 8 * q);
+    } else {
+      const int half = part;
       const uint32_t w = p.mask[row * (p.d_in / 32) + k0 / 32];
       const uint32_t bits = half ? (w >> 16) : (w & 0xffffu);
-      r.bits = bits;
+      r.bits[it] = bits;
       if constexpr (AK == kA24) {
         // exactly 8 kept values per 16 dense k; 16-byte aligned because
         // kc % 16 == 0 and k0/2 + 8*half is a multiple of 8
-        r.v[0] = *reinterpret_cast<const u32x4*>(p.x + row * kc + k0 / 2 + 8 * half);
+        r.v[it][0] = *reinterpret_cast<const u32x4*>(p.x + row * kc + k0 / 2 + 8 * half);
       } else {
         // kept values of this row before dense k0 + 16*half: k0 is a
         // multiple of 32 and of m, so exactly k0*n/m precede the tile.  The
@@ -156,84 +172,75 @@ __device__ __forceinline__ void load_a(const GParams& p, int64_t m0, int64_t k0,
         for (int e = 0; e < 16; ++e) vals[e] = (e < cnt) ? src[e] : (uint16_t)0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          r.v[0][i] = (uint32_t)vals[2 * i] | ((uint32_t)vals[2 * i + 1] << 16);
-          r.v[1][i] = (uint32_t)vals[8 + 2 * i] | ((uint32_t)vals[8 + 2 * i + 1] << 16);
+          r.v[it][0][i] = (uint32_t)vals[2 * i] | ((uint32_t)vals[2 * i + 1] << 16);
+          r.v[it][1][i] = (uint32_t)vals[8 + 2 * i] | ((uint32_t)vals[8 + 2 * i + 1] << 16);
         }
       }
     }
   }
 }
 
-template <int AK>
-__device__ __forceinline__ void store_a(uint16_t* As, uint32_t* Aidx, const ARegs& r) {
+// Scatter the kept values (word-packed, position order) to the set bits of
+// `bits` in dst[0..W), after zero-filling it.
+template <int W, int NV>
+__device__ __forceinline__ void scatter_row(uint16_t* dst, uint32_t bits, const u32x4 (&v)[NV]) {
+#pragma unroll
+  for (int q = 0; q < W / 8; ++q) *reinterpret_cast<u32x4*>(dst + 8 * q) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int sidx = 0; sidx < W; ++sidx) {
+    const uint32_t word = v[sidx / 8][(sidx % 8) / 2];  // static register index
+    const uint16_t hv = (uint16_t)((sidx & 1) ? (word >> 16) : (word & 0xffffu));
+    if (bits != 0u) {
+      dst[__builtin_ctz(bits)] = hv;
+      bits &= bits - 1u;
+    }
+  }
+}
+
+template <int AK, int BM>
+__device__ __forceinline__ void store_a(uint16_t* As, uint32_t* Aidx, const ARegs<AK, BM>& r) {
+  constexpr int PR = AItems<AK>::kPerRow;
   const int tid = (int)threadIdx.x;
-  if constexpr (AK == kADense) {
-    const int q = tid % 4;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<u32x4*>(As + (tid / 4 + 64 * h) * LDA + 8 * q) = r.v[h];
-  } else if constexpr (AK == kANMVec) {
-    if (tid < BM) {
-      uint16_t* dst = As + tid * LDA;
+  for (int it = 0; it < ARegs<AK, BM>::kItems; ++it) {
+    const int item = tid + it * NTH;
+    const int lrow = item / PR;
+    const int part = item % PR;
+    if (lrow >= BM) continue;
+    if constexpr (AK == kADense) {
+      *reinterpret_cast<u32x4*>(As + lrow * LDA + 8 * part) = r.v[it][0];
+    } else if constexpr (AK == kANMVec) {
+      scatter_row<32, 4>(As + lrow * LDA, r.bits[it], r.v[it]);
+    } else if constexpr (AK == kANM) {
+      scatter_row<16, 2>(As + lrow * LDA + 16 * part, r.bits[it], r.v[it]);
+    } else {
+      // compressed values: 8 halves per (row, half) -> As[row][8*half .. +8]
+      *reinterpret_cast<u32x4*>(As + lrow * LDA + 8 * part) = r.v[it][0];
+      // position code: per group of 4, first set position | second << 2
+      uint32_t code = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(dst + 8 * q) = u32x4{0u, 0u, 0u, 0u};
-      uint32_t bits = r.bits;
-#pragma unroll
-      for (int sidx = 0; sidx < 32; ++sidx) {
-        const uint32_t word = r.v[sidx / 8][(sidx % 8) / 2];  // static register index
-        const uint16_t hv = (uint16_t)((sidx & 1) ? (word >> 16) : (word & 0xffffu));
-        if (bits != 0u) {
-          dst[__builtin_ctz(bits)] = hv;
-          bits &= bits - 1u;
-        }
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t nib = (r.bits[it] >> (4 * g)) & 0xfu;
+        const uint32_t p0 = nib ? (uint32_t)__builtin_ctz(nib) : 0u;
+        const uint32_t rest = nib & (nib - 1u);
+        const uint32_t p1 = rest ? (uint32_t)__builtin_ctz(rest) : (p0 == 3u ? 3u : p0 + 1u);
+        code |= (p0 | (p1 << 2)) << (4 * g);
       }
+      Aidx[lrow * 2 + part] = code;
     }
-  } else if constexpr (AK == kANM) {
-    // zero-fill the 16 dense slots, then scatter the kept values (position
-    // order) to the positions of the set mask bits, lowest first
-    const int half = tid % 2;
-    const int row = tid / 2;
-    uint16_t* dst = As + row * LDA + 16 * half;
-    *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(dst + 8) = u32x4{0u, 0u, 0u, 0u};
-    uint32_t bits = r.bits;
-#pragma unroll
-    for (int sidx = 0; sidx < 16; ++sidx) {
-      const uint32_t word = r.v[sidx / 8][(sidx % 8) / 2];  // static register index
-      const uint16_t hv = (uint16_t)((sidx & 1) ? (word >> 16) : (word & 0xffffu));
-      if (bits != 0u) {
-        dst[__builtin_ctz(bits)] = hv;
-        bits &= bits - 1u;
-      }
-    }
-  } else {
-    // compressed values: 8 halves per (row, half) -> As[row][8*half .. +8]
-    const int half = tid % 2;
-    const int row = tid / 2;
-    *reinterpret_cast<u32x4*>(As + row * LDA + 8 * half) = r.v[0];
-    // position code: per group of 4, first set position | second << 2
-    uint32_t code = 0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t nib = (r.bits >> (4 * g)) & 0xfu;
-      const uint32_t p0 = nib ? (uint32_t)__builtin_ctz(nib) : 0u;
-      const uint32_t rest = nib & (nib - 1u);
-      const uint32_t p1 = rest ? (uint32_t)__builtin_ctz(rest) : (p0 == 3u ? 3u : p0 + 1u);
-      code |= (p0 | (p1 << 2)) << (4 * g);
-    }
-    Aidx[row * 2 + half] = code;
   }
 }
 
-template <int AK>
+template <int AK, int BM>
 __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
+  constexpr int MB = BM / 64;  // 32-row MFMA blocks per wave
   __shared__ __align__(16) uint16_t As[2][BM * LDA];
   __shared__ __align__(16) uint16_t Bs[2][BN * LDB];
-  __shared__ uint32_t Aidx[2][BM * 2];
+  __shared__ uint32_t Aidx[2][AK == kA24 ? BM * 2 : 1];
   const int tid = (int)threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  const int wm = wave / 2, wn = wave % 2;  // 2 x 2 waves, 64 x 64 each
+  const int wm = wave / 2, wn = wave % 2;  // 2 x 2 waves, (BM/2) x 64 each
 
   // tile order: all M tiles of one N strip are consecutive, so the strip of
   // WT stays in cache while they run
@@ -241,20 +248,20 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
   const int64_t m0 = (int64_t)(blockIdx.x % mt) * BM;
   const int64_t n0 = (int64_t)(blockIdx.x / mt) * BN;
 
-  f16v acc[2][2];
+  f16v acc[MB][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   const int64_t nk = (p.d_in + BK - 1) / BK;
-  ARegs ar;
+  ARegs<AK, BM> ar;
   BRegs br;
-  load_a<AK>(p, m0, 0, ar);
+  load_a<AK, BM>(p, m0, 0, ar);
   load_b(p, 0, n0, br);
-  store_a<AK>(As[0], Aidx[0], ar);
+  store_a<AK, BM>(As[0], Aidx[0], ar);
   store_b(Bs[0], br);
   __syncthreads();
 
@@ -262,7 +269,7 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
     const int cur = (int)(kt & 1);
     const bool more = kt + 1 < nk;
     if (more) {
-      load_a<AK>(p, m0, (kt + 1) * BK, ar);
+      load_a<AK, BM>(p, m0, (kt + 1) * BK, ar);
       load_b(p, (kt + 1) * BK, n0, br);
     }
     const uint16_t* as = As[cur];
@@ -281,8 +288,8 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
         }
       }
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int row = wm * 64 + a * 32 + lane % 32;
+      for (int a = 0; a < MB; ++a) {
+        const int row = wm * (BM / 2) + a * 32 + lane % 32;
         const h8 aop = *reinterpret_cast<const h8*>(as + row * LDA + 8 * (lane / 32));
         const int code = (int)Aidx[cur][row * 2 + lane / 32];
 #pragma unroll
@@ -292,10 +299,10 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
     } else {
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 16) {
-        h8 aop[2], bop[2];
+        h8 aop[MB], bop[2];
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int row = wm * 64 + a * 32 + lane % 32;
+        for (int a = 0; a < MB; ++a) {
+          const int row = wm * (BM / 2) + a * 32 + lane % 32;
           aop[a] = *reinterpret_cast<const h8*>(as + row * LDA + kk + 8 * (lane / 32));
         }
 #pragma unroll
@@ -304,14 +311,14 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
           bop[b] = *reinterpret_cast<const h8*>(bs + col * LDB + kk + 8 * (lane / 32));
         }
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < MB; ++a)
 #pragma unroll
           for (int b = 0; b < 2; ++b)
             acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[a], bop[b], acc[a][b], 0, 0, 0);
       }
     }
     if (more) {
-      store_a<AK>(As[cur ^ 1], Aidx[cur ^ 1], ar);
+      store_a<AK, BM>(As[cur ^ 1], Aidx[cur ^ 1], ar);
       store_b(Bs[cur ^ 1], br);
     }
     __syncthreads();
@@ -319,27 +326,47 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
 
   // epilogue: fp16 stores; register r of lane l is row 8(r/4)+4(l/32)+r%4
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int64_t col = n0 + wn * 64 + b * 32 + lane % 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        const int64_t row = m0 + wm * (BM / 2) + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
         if (row < p.T && col < p.d_out) p.y[row * p.d_out + col] = f2h(acc[a][b][r]);
       }
     }
 }
 
-template <int AK>
-hipError_t launch_kind(const GParams& p, hipStream_t s) {
+template <int AK, int BM>
+hipError_t launch_tile(const GParams& p, hipStream_t s) {
   const int64_t tiles = ((p.T + BM - 1) / BM) * ((p.d_out + BN - 1) / BN);
   if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
-  hipLaunchKernelGGL(k_gemm<AK>, dim3((unsigned)tiles), dim3(NTH), 0, s, p);
+  hipLaunchKernelGGL((k_gemm<AK, BM>), dim3((unsigned)tiles), dim3(NTH), 0, s, p);
   return hipGetLastError();
 }
 
+int g_gemm_bm = 0;  // tuning override: 0 = automatic, else 128 or 256
+
+// 256-row tiles when there are enough of them to fill the chip, 128 otherwise.
+// The zero-filled N:M staging (any pattern but 2:4) needs more registers per
+// row and measured slower at 256 rows, so it stays at 128 unless overridden.
+template <int AK>
+hipError_t launch_kind(const GParams& p, hipStream_t s) {
+  const int64_t tiles256 = ((p.T + 255) / 256) * ((p.d_out + BN - 1) / BN);
+  const bool tall_ok = (AK == kADense || AK == kA24) && tiles256 >= 256;
+  const int bm = g_gemm_bm ? g_gemm_bm : (tall_ok ? 256 : 128);
+  if (bm == 256) return launch_tile<AK, 256>(p, s);
+  return launch_tile<AK, 128>(p, s);
+}
+
 }  // namespace
+
+int gemm_set_tile_rows(int bm) {
+  if (bm != 0 && bm != 128 && bm != 256) return 1;
+  g_gemm_bm = bm;
+  return 0;
+}
 
 hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
                              int64_t d_out, uint16_t* y, hipStream_t s) {

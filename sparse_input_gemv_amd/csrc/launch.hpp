@@ -74,5 +74,6 @@ hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const u
 hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
                           int n, int m, const uint16_t* wt, int64_t d_out, uint16_t* y,
                           hipStream_t s);
+int gemm_set_tile_rows(int bm);
 
 }  // namespace sa

@@ -118,6 +118,8 @@ def test_gemv_checks(sa):
     assert d(P, 4096, 11008, None, 1, P, P, need, None) == SA_ERR_INVALID_ARG
     assert sa.sa_set_gemv_tuning(99, 0) == SA_ERR_INVALID_ARG
     assert sa.sa_set_gemv_tuning(-1, 0) == SA_OK
+    assert sa.sa_set_gemm_tuning(64) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemm_tuning(0) == SA_OK
 
 
 def test_swiglu_checks(sa):

@@ -369,19 +369,25 @@ def test_split_k_handoff_is_deterministic():
 from oracle import spmm  # noqa: E402
 
 
+@pytest.mark.parametrize("tile_rows", [0, 128, 256])
 @pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 1024), (130, 96, 136), (1, 32, 8),
-                                          (257, 4096, 264)])
-def test_dense_gemm_small(T, d_in, d_out):
+                                          (257, 4096, 264), (600, 256, 1032)])
+def test_dense_gemm_small(T, d_in, d_out, tile_rows):
     X = syn.gaussian_f16((T, d_in), 1.0, T)
     wt = syn.weight_t(d_out, d_in, d_in)
-    Y = sa.dense_gemm(dev(X), dev(wt))
+    try:
+        sa.set_gemm_tuning(tile_rows)
+        Y = sa.dense_gemm(dev(X), dev(wt))
+    finally:
+        sa.set_gemm_tuning(0)
     assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
 
 
+@pytest.mark.parametrize("tile_rows", [128, 256])
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 4), (3, 4), (5, 16),
                                  (32, 32)])
-@pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 512), (100, 96, 136)])
-def test_nm_spmm_small(n, m, T, d_in, d_out):
+@pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 512), (100, 96, 136), (300, 128, 264)])
+def test_nm_spmm_small(n, m, T, d_in, d_out, tile_rows):
     if d_in % m:
         pytest.skip("d_in not a multiple of m")
     X = syn.gaussian_f16((T, d_in), 1.0, n * 7 + m)
@@ -389,7 +395,11 @@ def test_nm_spmm_small(n, m, T, d_in, d_out):
     keep, vals = sparsify.nm_sparsify(X, n, m)
     ref = spmm.nm_spmm(X, keep, wt)
     mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
-    Y = sa.nm_act_spmm(val_g, mask_g, n, m, dev(wt))
+    try:
+        sa.set_gemm_tuning(tile_rows)
+        Y = sa.nm_act_spmm(val_g, mask_g, n, m, dev(wt))
+    finally:
+        sa.set_gemm_tuning(0)
     assert_close(Y, ref)
     # each token's row is that token's masked GEMV
     r = 3
