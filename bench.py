@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--tiling", type=int, default=-1, help="GEMV tiling override (tuning)")
     ap.add_argument("--target-wgs", type=int, default=0, help="GEMV workgroup target (tuning)")
+    ap.add_argument("--handoff", type=int, default=0, choices=[0, 1, 2],
+                    help="split-K partial sum: 0 auto, 1 second launch, 2 same launch (tuning)")
     ap.add_argument("--only", choices=["fused", "unfused", "dense"], default=None,
                     help="time a single path (for profiler runs)")
     ap.add_argument("--suite", action="store_true",
@@ -117,8 +119,8 @@ def main():
     y = torch.empty((D_OUT,), dtype=torch.float16, device=dev)
     ws_bytes = sa.workspace_bytes(D_OUT, D_IN, 1)
     ws = sa.workspace(dev, ws_bytes)
-    if args.tiling >= 0 or args.target_wgs > 0:
-        sa.set_gemv_tuning(args.tiling, args.target_wgs)
+    if args.tiling >= 0 or args.target_wgs > 0 or args.handoff > 0:
+        sa.set_gemv_tuning(args.tiling, args.target_wgs, args.handoff)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

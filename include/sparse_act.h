@@ -26,8 +26,12 @@
  *   sa_last_error() then describes the first failing check for the calling
  *   thread.  No C++ exception crosses this boundary.
  * - A workspace `ws` (sized by sa_workspace_bytes, 256-byte aligned) holds
- *   per-call partial sums; its contents on entry do not matter.  Calls that
- *   share one workspace must be ordered on one stream: concurrent calls race.
+ *   per-call partial sums and, in its first SA_WS_TICKET_BYTES, one arrival
+ *   counter per output tile for the one-launch split-K hand-off.  That
+ *   region must be all zero before the workspace is first used (allocate
+ *   it zero-filled); every call leaves it zero again.  The rest may hold
+ *   anything on entry.  Calls that share one workspace must be ordered on
+ *   one stream: concurrent calls race.
  * - rows == 0 (or batch == 0, T == 0) is a valid empty call and does nothing.
  *
  * Pages cited (by title; "replies" = the authors' answers to reviewers):
@@ -56,6 +60,9 @@ extern "C" {
 #define SA_ERR_INVALID_ARG 1 /* a pointer, size, alignment or value check failed */
 #define SA_ERR_UNSUPPORTED 2 /* valid but outside what the kernels implement */
 #define SA_ERR_WORKSPACE 3   /* ws is NULL or smaller than sa_workspace_bytes() */
+
+/* Leading workspace bytes that must be zero before first use (see above). */
+#define SA_WS_TICKET_BYTES ((size_t)1 << 20)
 #define SA_ERR_HIP 4         /* the HIP runtime reported an error at launch */
 
 #define SA_MAX_BATCH 8       /* rows per call of the GEMV family */
@@ -248,13 +255,16 @@ int dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
 
 /*
  * Process-wide launch override for the GEMV family, for tuning sweeps:
- * `tiling` picks one of the compiled tile shapes (-1 = automatic) and
+ * `tiling` picks one of the compiled tile shapes (-1 = automatic),
  * `target_wgs` the number of workgroups of the split-K stream launch to aim
- * for (0 = automatic).  Every tiling computes the same result up to fp32
- * summation order.
- * Returns SA_ERR_INVALID_ARG for an unknown tiling.  Not thread-safe.
+ * for (0 = automatic) and `handoff` how split-K partials are summed:
+ * 0 = automatic, 1 = a second launch, 2 = in the same launch by the last
+ * workgroup of each output tile.  Every tiling computes the same result up
+ * to fp32 summation order; the two hand-offs give identical bits.
+ * Returns SA_ERR_INVALID_ARG for an unknown tiling or handoff.  Not
+ * thread-safe.
  */
-int sa_set_gemv_tuning(int tiling, int target_wgs);
+int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff);
 /*
  * Process-wide tile height of dense_gemm / nm_act_spmm, for tuning sweeps:
  * 0 = automatic (256-row tiles when they fill the chip, else 128), or 128 /

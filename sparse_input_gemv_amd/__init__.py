@@ -54,7 +54,7 @@ _SIGNATURES = {
     "weight_col_norms": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "nm_act_spmm": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp]),
     "dense_gemm": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
-    "sa_set_gemv_tuning": (_i32, [_i32, _i32]),
+    "sa_set_gemv_tuning": (_i32, [_i32, _i32, _i32]),
     "sa_set_gemm_tuning": (_i32, [_i32]),
     "sa_gemv_tiling_info": (_i32, [_i32, _vp, _vp, _vp]),
 }
@@ -123,12 +123,14 @@ def workspace_bytes(d_out: int, d_in: int, batch: int = 1) -> int:
 def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     """Per-device workspace for partial sums, grown on demand and reused.
 
-    Calls on one device share it, so they must be ordered on one stream.
+    Allocated zero-filled: its leading hand-off counters must start at zero
+    (the library returns them to zero after every call).  Calls on one
+    device share it, so they must be ordered on one stream.
     """
     key = torch.device(device).index or 0
     ws = _ws.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws[key] = ws
     return ws
 
@@ -336,8 +338,8 @@ def dense_gemm(x: torch.Tensor, wt: torch.Tensor, y: torch.Tensor | None = None)
 
 # ---- tuning -------------------------------------------------------------------
 
-def set_gemv_tuning(tiling: int = -1, target_wgs: int = 0) -> None:
-    _check(lib().sa_set_gemv_tuning(tiling, target_wgs), "sa_set_gemv_tuning")
+def set_gemv_tuning(tiling: int = -1, target_wgs: int = 0, handoff: int = 0) -> None:
+    _check(lib().sa_set_gemv_tuning(tiling, target_wgs, handoff), "sa_set_gemv_tuning")
 
 
 def set_gemm_tuning(tile_rows: int = 0) -> None:

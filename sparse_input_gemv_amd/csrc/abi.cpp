@@ -78,6 +78,8 @@ int act_calibrate_threshold(const uint16_t* samples, int64_t n, double s, float*
                     "act_calibrate_threshold");
 }
 
+static_assert(SA_WS_TICKET_BYTES == sa::kGemvTicketBytes, "header and library agree");
+
 size_t sa_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
   if (d_out < 1 || d_in < 1) return 0;
   if (batch < 1) batch = 1;
@@ -254,10 +256,11 @@ int dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt, i
   return hip_status(e, "dense_gemm");
 }
 
-int sa_set_gemv_tuning(int tiling, int target_wgs) {
+int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff) {
   sa::clear_error();
-  if (sa::gemv_set_tuning(tiling, target_wgs) != 0) {
-    sa::set_error("sa_set_gemv_tuning: unknown tiling %d or negative target", tiling);
+  if (sa::gemv_set_tuning(tiling, target_wgs, handoff) != 0) {
+    sa::set_error("sa_set_gemv_tuning: unknown tiling %d, negative target or handoff %d",
+                  tiling, handoff);
     return SA_ERR_INVALID_ARG;
   }
   return SA_OK;

@@ -16,14 +16,21 @@
 //   phase 2  its threads stream the listed rows for the output tile with
 //            16-byte loads (8 fp16 per lane; a 128-output tile is one
 //            256-byte run per row), U rows in flight per thread, fp32 FMA;
-//   phase 3  row lanes are summed in LDS and the fp32 partial tile is stored
-//            with plain stores -- no waiting, no atomics.
-// Launch 2, k_reduce: sums the partial tiles of every output in slice order
-// and writes fp16 y (deterministic).  The kernel boundary orders the two.
-// Measured on MI355X, a second back-to-back launch costs less than a
-// cross-workgroup "last block" hand-off: device-scope atomics on one
-// counter serialise (~0.1-0.2 us each) and every workgroup reaches that
-// hand-off at the same moment.
+//   phase 3  row lanes are summed in LDS and the fp32 partial tile is
+//            stored.
+// The partial tiles are then summed over slices, in slice order, into fp16 y
+// (deterministic), in one of two ways:
+//   two launches  plain partial stores; launch 2, k_reduce, sums them after
+//                 the kernel boundary.
+//   one launch    partials are written with device-coherent stores, every
+//                 wave waits for them to complete, and one thread per
+//                 workgroup takes a ticket from its output tile's counter;
+//                 the workgroup that draws the last ticket sums the tile
+//                 (same grouping and order as k_reduce, so both ways give
+//                 identical bits) and resets the counter for the next call.
+//                 Each counter sits on its own 128-byte line: same-line
+//                 atomics serialise at ~10 ns each on this part, separate
+//                 lines proceed in parallel.
 //
 // Full-K (small weights, batch <= 2).  k_gemv_fk: each workgroup owns
 // 8*LPR outputs and walks all of d_in; no partials, one launch.
@@ -35,6 +42,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "validate.hpp"
 
 namespace sa {
 namespace {
@@ -52,17 +60,35 @@ constexpr Tiling kTilings[] = {
     {16, 1024, 8, 1},  {16, 512, 16, 1},  {8, 512, 16, 1},
 };
 constexpr int kNumTilings = (int)(sizeof(kTilings) / sizeof(kTilings[0]));
+constexpr bool split_tiles_fit_tickets() {
+  for (const Tiling& t : kTilings)
+    if (!t.full_k && t.tile_o < kMinSplitTileO) return false;
+  return true;
+}
+static_assert(split_tiles_fit_tickets(), "a split-K tile narrower than the counter region assumes");
 constexpr int kDefaultSplitK = 0;     // any batch / mode
-constexpr int kDefaultSplitKHot = 2;  // batch 1 of threshold / dense / list (measured best)
+constexpr int kDefaultSplitKHot = 0;  // batch 1 of threshold / dense / list (measured best)
 constexpr int kDefaultFullK = 8;
-constexpr int kSliceAlign = 64;
-constexpr int kDefaultTargetWgs = 1024;
+// SwiGLU slices start on 64-entry boundaries (each wave writes whole mask
+// words); the other modes take any slice length.
+constexpr int kSwigluSliceAlign = 64;
+constexpr int kMaxGk = 256;     // input slices per output tile
+// default split-K grid, in workgroups per CU (measured best: 3 for the
+// sparse modes, 4 for the dense baseline)
+constexpr int kWgsPerCu = 3;
+constexpr int kWgsPerCuDense = 4;
+constexpr bool kDefaultOneLaunch = true;
+constexpr int kReduceGroups = 16;  // slice groups of the final sum (both hand-offs)
+constexpr size_t kTicketBytes = kGemvTicketBytes;
+static_assert((size_t)(kMaxDOut / kMinSplitTileO) * kTicketStride * 4 <= kTicketBytes,
+              "one hand-off counter per output tile of the longest output");
 constexpr size_t kMaxListLds = 48 * 1024;
 // weights up to this size run full-K in one launch (latency-bound anyway)
 constexpr int64_t kFullKMaxWeightBytes = 8 << 20;
 
 int g_tiling = -1;     // -1: automatic
 int g_target_wgs = 0;  // 0: automatic
+int g_handoff = 0;     // 0: automatic, 1: two launches, 2: one launch
 
 struct KParams {
   const uint16_t* wt;
@@ -85,6 +111,7 @@ struct KParams {
   int batch;
   float* part;
   int32_t* slice_cnt;
+  uint32_t* tickets;  // non-null: one-launch hand-off
   int go, gk, slice;
 };
 
@@ -125,6 +152,92 @@ __device__ __forceinline__ bool swiglu_keep(uint16_t gb, uint16_t ub, const doub
   const double score = (mode == 0) ? fabs(s) : fabs(h) * colnorm[k];
   hv = (float)h;
   return score >= t;
+}
+
+// Device-coherent access for the one-launch hand-off.  Each XCD has its own
+// L2, and a device-scope release/acquire fence would write back or
+// invalidate a whole L2 per workgroup.  Instead the values handed over are
+// written and read with relaxed device-scope atomics, which the hardware
+// keeps coherent across XCDs, and each wave waits for its stores to
+// complete before its workgroup takes a ticket: a ticket then certifies
+// that the workgroup's partials are visible to every XCD.
+template <typename T>
+__device__ __forceinline__ void store_coherent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt = expcnt = lgkmcnt = 0
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Final sum of one output tile over the gk partial tiles, by the workgroup
+// that arrived last.  Thread pairs (g, o) -- slice group g of 16, output o
+// -- add slices g, g+16, g+32, ... in increasing order; then the groups are
+// added in order 0..15 through LDS.  Per output this is k_reduce's grouping
+// and order, so both hand-offs round identically.  A wave's 64 lanes take 64
+// consecutive outputs of one slice group, so each load is one wave-uniform
+// address plus the lane: whole lines per wave and few address registers.
+template <int TILE_O, int NT, int B>
+__device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0,
+                                               unsigned char* smem) {
+  constexpr int G = kReduceGroups;
+  constexpr int PAIRS = G * TILE_O;
+  constexpr int PP = (PAIRS + NT - 1) / NT;  // pairs per thread
+  constexpr int KL = PP >= 16 ? 1 : 16 / PP; // loads per pair per batch
+  static_assert(TILE_O % kWave == 0 && NT % kWave == 0, "a wave stays in one slice group");
+  float* red = reinterpret_cast<float*>(smem);  // [G][TILE_O]
+  const int tid = (int)threadIdx.x;
+  const int lane = lane_id();
+  const int w0 = __builtin_amdgcn_readfirstlane(tid - lane);
+  const int64_t stride = (int64_t)B * p.d_out;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    if (b >= p.batch) break;
+    float s[PP];
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp) s[pp] = 0.f;
+    for (int k0 = 0; k0 < p.gk; k0 += G * KL) {
+      float tmp[PP][KL];
+#pragma unroll
+      for (int pp = 0; pp < PP; ++pp) {
+        const int e0 = w0 + pp * NT;  // wave-uniform
+        const int g = e0 / TILE_O;
+        const int col0 = e0 % TILE_O;
+        const bool ok_o = e0 < PAIRS && o0 + col0 + lane < p.d_out;
+        const float* base = p.part + (int64_t)b * p.d_out + o0 + col0;
+#pragma unroll
+        for (int q = 0; q < KL; ++q) {
+          const int kk = k0 + g + q * G;
+          tmp[pp][q] = (ok_o && kk < p.gk)
+                           ? __hip_atomic_load(base + (int64_t)kk * stride + lane,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+        }
+      }
+#pragma unroll
+      for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+        for (int q = 0; q < KL; ++q) s[pp] += tmp[pp][q];
+    }
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp) {
+      const int e = tid + pp * NT;
+      if (e < PAIRS) red[e] = s[pp];
+    }
+    __syncthreads();
+    for (int oo = tid; oo < TILE_O; oo += NT) {
+      const int64_t og = o0 + oo;
+      if (og < p.d_out) {
+        float acc = red[oo];
+#pragma unroll
+        for (int gg = 1; gg < G; ++gg) acc += red[gg * TILE_O + oo];
+        p.y[(int64_t)b * p.d_out + og] = f2h(acc);
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // Sampled lower bound in an ascending int32 list: number of entries < key.
@@ -287,7 +400,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         if (p.gk == 1) {
           if (p.out_nnz != nullptr) p.out_nnz[0] = cnt;
         } else {
-          p.slice_cnt[kblk] = cnt;
+          store_coherent(p.slice_cnt + kblk, (int32_t)cnt);
         }
       }
     }
@@ -309,20 +422,24 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
 
-  for (int j0 = r_lane; j0 < cnt; j0 += R * U) {
-    half8 w[U];
+  // Rows j = r_lane, r_lane + R, ... in two halves of H rows: one half's
+  // loads stay in flight while the other half is consumed.  Rows are added
+  // in increasing j whatever U is.  Loads are unconditional (a branch per
+  // load would make every wait a full drain): past the end of the list a
+  // thread re-reads the list's last row, a cache hit, and consume() skips it.
+  constexpr int H = U / 2;
+  static_assert(U % 2 == 0, "two halves");
+  auto issue = [&](half8 (&w)[H], int j0) {
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
+    for (int q = 0; q < H; ++q) {
       const int j = j0 + q * R;
-      if (j < cnt && o_ok) {
-        w[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)lk[j] * ld);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[q][i] = (half_t)0.f;
-      }
+      const int row = lk[j < cnt ? j : cnt - 1];
+      w[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)row * ld);
     }
+  };
+  auto consume = [&](const half8 (&w)[H], int j0) {
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
+    for (int q = 0; q < H; ++q) {
       const int j = j0 + q * R;
       if (j < cnt) {
 #pragma unroll
@@ -333,12 +450,24 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         }
       }
     }
+  };
+  if (r_lane < cnt) {
+    half8 wa[H], wb[H];
+    issue(wa, r_lane);
+    issue(wb, r_lane + H * R);
+    for (int j0 = r_lane; j0 < cnt; j0 += U * R) {
+      consume(wa, j0);
+      issue(wa, j0 + U * R);
+      consume(wb, j0 + H * R);
+      issue(wb, j0 + U * R + H * R);
+    }
   }
 
   // ---------------- phase 3: reduce row lanes, store the tile --------------
   __syncthreads();  // the kept list is no longer needed; reuse its LDS
   float* red = reinterpret_cast<float*>(smem);
   const bool single = p.gk == 1;
+  const bool handoff = !single && p.tickets != nullptr;
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     if (b >= p.batch) break;
@@ -351,14 +480,43 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       for (int r = 0; r < R; ++r) s += red[r * TILE_O + oo];
       const int64_t og = o0 + oo;
       if (og < p.d_out) {
+        float* dst = p.part + ((int64_t)kblk * B + b) * p.d_out + og;
         if (single)
           p.y[(int64_t)b * p.d_out + og] = f2h(s);
+        else if (handoff)
+          store_coherent(dst, s);
         else
-          p.part[((int64_t)kblk * B + b) * p.d_out + og] = s;
+          *dst = s;
       }
     }
     __syncthreads();
   }
+  if (!handoff) return;
+
+  // ---------------- phase 4: one-launch hand-off ---------------------------
+  __shared__ int s_last;
+  wait_stores();
+  __syncthreads();
+  uint32_t* ticket = p.tickets + (int64_t)oblk * kTicketStride;
+  if (tid == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == (unsigned)(p.gk - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (s_last == 0) return;
+  handoff_reduce<TILE_O, NT, B>(p, o0, smem);
+  if constexpr (MODE == kModeSwiglu) {
+    if (oblk == 0 && p.out_nnz != nullptr) {
+      int c = 0;
+      for (int kk = tid; kk < p.gk; kk += NT)
+        c += __hip_atomic_load(p.slice_cnt + kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int tot;
+      (void)block_exclusive_scan<NT>(c, wsum, tot);
+      if (tid == 0) p.out_nnz[0] = tot;
+    }
+  }
+  if (tid == 0) store_coherent(ticket, 0u);  // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -372,7 +530,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, 
                                                 int64_t d_out, uint16_t* __restrict__ y,
                                                 const int32_t* __restrict__ slice_cnt,
                                                 int32_t* __restrict__ out_nnz) {
-  constexpr int C = 16, G = 16, kLoads = 16;
+  constexpr int C = 16, G = kReduceGroups, kLoads = 16;
   __shared__ f4v red[G][C];
   __shared__ int scan[256 / kWave];
   const int tid = (int)threadIdx.x;
@@ -618,17 +776,19 @@ int batch_pad(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ?
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t slicecnt_off, part_off, total;
+  size_t ticket_off, slicecnt_off, part_off, total;
 };
 
-// Workspace: per-slice kept counts (SwiGLU) and the fp32 partial tiles
-// [slice][batch][d_out].  Everything in it is written before it is read
-// within one call, so its contents between calls do not matter.
+// Workspace: the hand-off counters (a fixed region, zero between calls: the
+// caller zero-fills it once, every call leaves it zero), per-slice kept
+// counts (SwiGLU) and the fp32 partial tiles [slice][batch][d_out].  The
+// counts and partials are written before they are read within one call.
 Layout ws_layout(int64_t d_out, int64_t d_in, int64_t batch) {
-  const int64_t gk_max = (d_in + kSliceAlign - 1) / kSliceAlign;
+  const int64_t gk_max = d_in < kMaxGk ? d_in : kMaxGk;
   Layout L;
-  L.slicecnt_off = 0;
-  L.part_off = align256((size_t)gk_max * 4);
+  L.ticket_off = 0;
+  L.slicecnt_off = kTicketBytes;
+  L.part_off = L.slicecnt_off + align256((size_t)gk_max * 4);
   L.total = L.part_off + (size_t)gk_max * (size_t)batch_pad((int)batch) * (size_t)d_out * 4;
   return L;
 }
@@ -644,20 +804,46 @@ struct Plan {
   size_t smem;
 };
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Split-K grid.  Streaming runs at a per-CU rate, so the call ends when the
+// most loaded CU does: the default grid is kWgsPerCu workgroups per CU with
+// equal slices (go * gk a multiple of the CU count whenever the output
+// tiles allow), every one resident at once.
 Plan make_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
   Plan pl;
   const Tiling T = kTilings[tiling];
   pl.go = (int)((d_out + T.tile_o - 1) / T.tile_o);
-  const int target = g_target_wgs > 0 ? g_target_wgs : kDefaultTargetWgs;
+  const int per_cu = mode == kModeDense ? kWgsPerCuDense : kWgsPerCu;
+  const int64_t target = g_target_wgs > 0 ? g_target_wgs : (int64_t)per_cu * device_cus();
   int64_t gk_req = (target + pl.go / 2) / pl.go;
   if (gk_req < 1) gk_req = 1;
+  if (gk_req > kMaxGk) gk_req = kMaxGk;
+  const int64_t align = mode == kModeSwiglu ? kSwigluSliceAlign : 1;
   int64_t slice = (d_in + gk_req - 1) / gk_req;
-  slice = (slice + kSliceAlign - 1) / kSliceAlign * kSliceAlign;
-  while (list_lds_bytes(mode, (int)slice, B) > kMaxListLds && slice > kSliceAlign)
-    slice -= kSliceAlign;
+  slice = (slice + align - 1) / align * align;
+  // the kept list of a slice must fit the LDS budget
+  const int64_t per_entry = (int64_t)list_lds_bytes(mode, 1, B);
+  const int64_t max_slice = (int64_t)kMaxListLds / per_entry / align * align;
+  if (slice > max_slice) slice = max_slice;
   pl.slice = (int)slice;
   pl.gk = (int)((d_in + slice - 1) / slice);
-  const size_t red = (size_t)T.threads * 8 * 4;
+  size_t red = (size_t)T.threads * 8 * 4;
+  const size_t red4 = (size_t)kReduceGroups * T.tile_o * 4;  // hand-off sum
+  if (red4 > red) red = red4;
   const size_t lst = list_lds_bytes(mode, pl.slice, B);
   pl.smem = lst > red ? lst : red;
   return pl;
@@ -804,9 +990,12 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   const Plan pl = make_plan(mode, tiling, c.d_out, c.d_in, B);
   const Layout L = ws_layout(c.d_out, c.d_in, c.batch);
   if (pl.gk > 1 && (c.ws == nullptr || c.ws_bytes < L.total)) return hipErrorInvalidValue;
+  if (pl.gk > kMaxGk) return hipErrorInvalidValue;  // the workspace holds kMaxGk slices
   unsigned char* ws = static_cast<unsigned char*>(c.ws);
   kp.slice_cnt = ws ? reinterpret_cast<int32_t*>(ws + L.slicecnt_off) : nullptr;
   kp.part = ws ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
+  const bool one_launch = pl.gk > 1 && (g_handoff == 0 ? kDefaultOneLaunch : g_handoff == 2);
+  kp.tickets = one_launch ? reinterpret_cast<uint32_t*>(ws + L.ticket_off) : nullptr;
   kp.go = pl.go;
   kp.gk = pl.gk;
   kp.slice = pl.slice;
@@ -821,7 +1010,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
     case kModeSwiglu: e = dispatch_tiling<kModeSwiglu, 1>(kp, pl, tiling, s); break;
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || pl.gk == 1) return e;
+  if (e != hipSuccess || pl.gk == 1 || one_launch) return e;
   return launch_reduce(kp, pl, B, mode == kModeSwiglu && c.out_nnz != nullptr, s);
 }
 
@@ -832,10 +1021,12 @@ hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, dou
   return hipGetLastError();
 }
 
-int gemv_set_tuning(int tiling, int target_wgs) {
-  if (tiling < -1 || tiling >= kNumTilings || target_wgs < 0) return 1;
+int gemv_set_tuning(int tiling, int target_wgs, int handoff) {
+  if (tiling < -1 || tiling >= kNumTilings || target_wgs < 0 || handoff < 0 || handoff > 2)
+    return 1;
   g_tiling = tiling;
   g_target_wgs = target_wgs;
+  g_handoff = handoff;
   return 0;
 }
 

@@ -59,13 +59,19 @@ struct GemvCall {
   size_t ws_bytes = 0;
 };
 
+// Hand-off counters at the head of the GEMV workspace: one per output tile
+// (d_out <= 524288, split-K tiles of >= 64 outputs), 128 bytes apart.
+constexpr int kTicketStride = 32;  // uint32 words
+constexpr int kMinSplitTileO = 64;
+constexpr size_t kGemvTicketBytes = (size_t)(524288 / kMinSplitTileO) * kTicketStride * 4;
+
 size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch);
 // Returns hipErrorInvalidValue if the workspace is too small for the launch
 // (checked by abi.cpp beforehand, so this is a second line of defence).
 hipError_t launch_gemv(const GemvCall& c, hipStream_t s);
 hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* out,
                             hipStream_t s);
-int gemv_set_tuning(int tiling, int target_wgs);
+int gemv_set_tuning(int tiling, int target_wgs, int handoff);
 int gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll);
 
 // ---- MFMA matmuls (gemm.hip) ------------------------------------------------

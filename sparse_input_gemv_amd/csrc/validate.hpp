@@ -13,7 +13,7 @@ void set_error(const char* fmt, ...);
 const char* last_error();
 
 constexpr int64_t kMaxD = 65536;            // sparsifier row length
-constexpr int64_t kMaxDOut = 524288;        // GEMV output length (ticket region)
+constexpr int64_t kMaxDOut = 524288;        // GEMV output length (sizes the hand-off counters)
 constexpr int64_t kMaxDIn = (int64_t)1 << 30;
 
 int check_threshold(const void* x, int64_t rows, int64_t d, float t, const void* mask,

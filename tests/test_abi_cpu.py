@@ -97,6 +97,8 @@ def test_workspace_size(sa):
     assert 0 < a < b
     assert a % 256 == 0 or a > 0
     assert sa.sa_workspace_bytes(0, 10, 1) == 0
+    # the zero-once hand-off counters lead every workspace
+    assert sa.sa_workspace_bytes(8, 1, 1) > 1 << 20
 
 
 def test_gemv_checks(sa):
@@ -116,8 +118,11 @@ def test_gemv_checks(sa):
     assert h(P, 4096, 11008, P, None, 1, P, P, need, None) == SA_ERR_INVALID_ARG
     d = sa.dense_gemv
     assert d(P, 4096, 11008, None, 1, P, P, need, None) == SA_ERR_INVALID_ARG
-    assert sa.sa_set_gemv_tuning(99, 0) == SA_ERR_INVALID_ARG
-    assert sa.sa_set_gemv_tuning(-1, 0) == SA_OK
+    assert sa.sa_set_gemv_tuning(99, 0, 0) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemv_tuning(-1, 0, 3) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemv_tuning(-1, -1, 0) == SA_ERR_INVALID_ARG
+    for handoff in (1, 2, 0):
+        assert sa.sa_set_gemv_tuning(-1, 0, handoff) == SA_OK
     assert sa.sa_set_gemm_tuning(64) == SA_ERR_INVALID_ARG
     assert sa.sa_set_gemm_tuning(0) == SA_OK
 

@@ -205,13 +205,13 @@ def test_every_tiling_headline(tiling):
     wt_g, x_g = dev(wt), dev(x)
     try:
         for target in (0, 256, 4096):
-            sa.set_gemv_tuning(tiling, target)
+            sa.set_gemv_tuning(tiling, target, 0)
             assert_close(sa.sparse_gemv_threshold(wt_g, x_g, t), ref)
             m, i, v, n = sa.act_sparsify_threshold(x_g, t)
             assert_close(sa.sparse_gemv(wt_g, i, v, n), ref)
             assert_close(sa.dense_gemv(wt_g, x_g), gemv.dense_gemv(wt, x))
     finally:
-        sa.set_gemv_tuning(-1, 0)
+        sa.set_gemv_tuning(-1, 0, 0)
 
 
 # ---------------------------------------------------------------------------
@@ -343,7 +343,8 @@ def test_masked_swiglu_t0_dense():
     assert_close(y, y_ref)
 
 
-def test_split_k_handoff_is_deterministic():
+@pytest.mark.parametrize("handoff", [1, 2])
+def test_split_k_handoff_is_deterministic(handoff):
     """Many back-to-back split-K calls on rotating weights: every result must
     equal the first one bit for bit (the cross-workgroup hand-off is exact)."""
     d_out, d_in, _ = syn.LLAMA2_7B["down"]
@@ -352,14 +353,60 @@ def test_split_k_handoff_is_deterministic():
     wts = [dev(wt0), dev(np.ascontiguousarray(wt0[::-1]))]
     try:
         for tiling, target in [(-1, 0), (0, 4096), (6, 1024), (2, 2048), (8, 0), (10, 0)]:
-            sa.set_gemv_tuning(tiling, target)
+            sa.set_gemv_tuning(tiling, target, handoff)
             ref = [sa.sparse_gemv_threshold(w, x, 0.69).clone() for w in wts]
             outs = [sa.sparse_gemv_threshold(wts[i % 2], x, 0.69) for i in range(200)]
             torch.cuda.synchronize()
             for i, y in enumerate(outs):
                 assert torch.equal(y, ref[i % 2]), (tiling, target, i)
     finally:
-        sa.set_gemv_tuning(-1, 0)
+        sa.set_gemv_tuning(-1, 0, 0)
+
+
+def _every_gemv_entry(wt, x1, xb, lists1, listsb, swiglu_in, t):
+    """One output of every split-K entry point (batch 1 and batched)."""
+    mb, ib, vb, nb = listsb
+    _, i1, v1, n1 = lists1
+    g, u, wdt, cn = swiglu_in
+    outs = [sa.sparse_gemv_threshold(wt, x1, t), sa.sparse_gemv_threshold(wt, xb, t),
+            sa.dense_gemv(wt, x1), sa.dense_gemv(wt, xb), sa.masked_gemv(wt, xb, mb),
+            sa.sparse_gemv(wt, i1, v1, n1), sa.sparse_gemv(wt, ib, vb, nb)]
+    for mode, c in (("cats", None), ("rana", cn)):
+        y, m, n = sa.masked_swiglu_down(g, u, wdt, 0.02 if mode == "cats" else 0.01, mode, c)
+        outs += [y, m, n]
+    return outs
+
+
+@pytest.mark.parametrize("tiling", [-1, 0, 1, 2, 3, 4, 5, 6, 7])
+def test_one_launch_handoff_matches_two_launches(tiling):
+    """The in-launch hand-off (last workgroup per output tile sums the
+    partials) must give the same bits as the second-launch reduction, for
+    every entry point, batch, ragged output tile and change of size between
+    calls (its counters must come back to zero)."""
+    shapes = [(4096, 11008, 5), (1032, 3000, 512), (136, 700, 64), (4096, 11008, 2048)]
+    data = []
+    for d_out, d_in, target in shapes:
+        wt = dev(syn.weight_t(d_out, d_in, d_in + 7))
+        x1 = dev(syn.laplace_f16((d_in,), 1.0, d_out))
+        xb = dev(syn.laplace_f16((4, d_in), 1.0, d_out + 1))
+        g, u = syn.swiglu_gate_up(d_in, d_out, 5)
+        wdt = wt
+        swiglu_in = (dev(g), dev(u), wdt, sa.weight_col_norms(wdt))
+        data.append((target, wt, x1, xb, sa.act_sparsify_threshold(x1, 0.7),
+                     sa.act_sparsify_threshold(xb, 0.7), swiglu_in))
+    try:
+        res = {}
+        for handoff in (1, 2):
+            for k, (target, wt, x1, xb, l1, lb, sw) in enumerate(data):
+                sa.set_gemv_tuning(tiling, target, handoff)
+                res[handoff, k] = [o.clone() for o in _every_gemv_entry(wt, x1, xb, l1, lb, sw,
+                                                                        0.7)]
+        torch.cuda.synchronize()
+        for k in range(len(data)):
+            for j, (a, b) in enumerate(zip(res[1, k], res[2, k])):
+                assert torch.equal(a, b), (tiling, shapes[k], j)
+    finally:
+        sa.set_gemv_tuning(-1, 0, 0)
 
 
 # ---------------------------------------------------------------------------
