@@ -226,11 +226,14 @@ __global__ __launch_bounds__(NT) void k_sparsify_topk(
   if (threadIdx.x == 0) nnz[row] = base;
 }
 
-// N:M: each thread owns 8 consecutive entries (one 16-byte load).  For
-// M <= 8 its groups are local; for M = 16 / 32 the M/8 threads of a group
-// exchange their packed 15-bit keys with cross-lane shuffles.  An entry is
-// kept iff fewer than n entries of its group rank before it, where j ranks
-// before i iff |x_j| > |x_i|, or they are equal and j < i.  The flattened
+// N:M: each thread owns 8 consecutive entries (one 16-byte load).  An entry
+// is kept iff fewer than n entries of its group rank before it, where j
+// ranks before i iff |x_j| > |x_i|, or they are equal and j < i.  For
+// M <= 8 the groups are local and ranked pairwise.  For M = 16 / 32 the M/8
+// threads of a group find the n-th largest 15-bit magnitude key tau by a
+// bitwise binary search (15 steps, each a count of keys >= a candidate,
+// summed over the group with cross-lane shuffles), keep every key > tau and
+// the first n - #(> tau) keys equal to tau in index order.  The flattened
 // array is a sequence of groups because d % M == 0 and d % 32 == 0.
 // Every group yields exactly n values, so a workgroup's 2048 entries give a
 // fixed, contiguous run of 2048*n/M outputs: the kept values are placed in
@@ -286,30 +289,45 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
       }
     }
   } else {
-    constexpr int G = M / 8;  // threads per group
+    constexpr int G = M / 8;  // threads per group, aligned lane runs
     const int gl = lane & (G - 1);
     const int base_lane = lane - gl;
-    uint32_t pk[4];
+    auto group_sum = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pk[i] = raw[i] & 0x7fff7fffu;
-    int all[M];
+      for (int o = 1; o < G; o <<= 1) c += __shfl_xor(c, o, kWave);
+      return c;
+    };
+    // tau = largest key value v with #(keys >= v) >= n: the n-th largest
+    int tau = 0;
 #pragma unroll
-    for (int q = 0; q < G; ++q) {
+    for (int b = 14; b >= 0; --b) {
+      const int cand = tau | (1 << b);
+      int c = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = (uint32_t)__shfl((int)pk[i], base_lane + q, kWave);
-        all[q * 8 + 2 * i] = (int)(w & 0xffffu);
-        all[q * 8 + 2 * i + 1] = (int)(w >> 16);
-      }
+      for (int i = 0; i < 8; ++i) c += key[i] >= cand ? 1 : 0;
+      if (group_sum(c) >= n) tau = cand;
     }
-    const int off = gl * 8;
+    int gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      int rank = 0;
+      gt += key[i] > tau ? 1 : 0;
+      eq += key[i] == tau ? 1 : 0;
+    }
+    const int need = n - group_sum(gt);  // ties at tau still to keep
+    int e = 0;  // ties at tau in lower lanes of the group
 #pragma unroll
-      for (int j = 0; j < M; ++j)
-        rank += (all[j] > key[i] || (all[j] == key[i] && j < off + i)) ? 1 : 0;
-      if (rank < n) keep |= 1u << i;
+    for (int q = 0; q < G; ++q) {
+      const int c = __shfl(eq, base_lane + q, kWave);
+      e += (q < gl) ? c : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (key[i] > tau) {
+        keep |= 1u << i;
+      } else if (key[i] == tau) {
+        if (e < need) keep |= 1u << i;
+        ++e;
+      }
     }
     // kept entries in lower lanes of the group come first
     const int mine = __popc(keep);

@@ -287,6 +287,23 @@ def test_nm_small(n, m):
     assert np.array_equal(host(val_g).view(np.uint16), vals.view(np.uint16))
 
 
+@pytest.mark.parametrize("n,m", [(1, 16), (3, 16), (8, 16), (15, 16), (1, 32), (7, 32),
+                                 (16, 32), (31, 32), (2, 8), (3, 4)])
+def test_nm_heavy_ties(n, m):
+    """Few distinct magnitudes, both signs of zero and infinities: the
+    cutoff among equal magnitudes (lower index first) decides most groups,
+    across the lanes that share a group."""
+    rng = np.random.default_rng(n * 1000 + m)
+    choices = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, np.inf, -np.inf], dtype=np.float16)
+    X = choices[rng.integers(0, 8, size=(96, 1024))]
+    X[5, :] = np.float16(-0.0)
+    X[6, :] = np.float16(2.0)
+    keep, vals = sparsify.nm_sparsify(X, n, m)
+    mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
+    assert np.array_equal(words(mask_g), sparsify.pack_mask(keep))
+    assert np.array_equal(host(val_g).view(np.uint16), vals.view(np.uint16))
+
+
 @pytest.mark.parametrize("shape", [(4096, 1024), (2048, 4096)])
 @pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (16, 32)])
 def test_nm_full_shapes(shape, n, m):
