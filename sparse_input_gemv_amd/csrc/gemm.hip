@@ -338,6 +338,222 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined engine (dense A, d_in a multiple of 64, 16-byte aligned rows).
+// A 256-thread workgroup computes a 256 x 128 output tile, four waves of
+// 128 x 64; the K loop steps by 64 through three LDS stages.  Tiles go from
+// global memory to LDS with direct loads (global_load_lds_dwordx4: lane l's
+// 16 bytes land at the instruction's LDS base + 16 l), two K steps ahead,
+// so no registers hold staged data and the loads of step t+2 overlap the
+// MFMAs of step t.
+//   A (X rows, K-contiguous) is stored [m][64] with its 16-byte chunks
+//     XOR-swizzled by the row, chosen by each lane's global source address,
+//     so the 32 rows one MFMA operand read touches fall in distinct banks.
+//   B (WT, N-contiguous) is stored [k][128] as it lies in memory (chunks
+//     swizzled by k), and the MFMA B operand -- 8 consecutive k of one
+//     column -- comes from two LDS transpose reads (ds_read_b64_tr_b16):
+//     within a 16-lane group, source lane s addresses 4 halves of row
+//     k0 + s/4 at column c0 + 4 (s % 4), and lane i receives column c0 + i
+//     of rows k0 .. k0+3 (layout checked on the device).
+// A stage is reused only after a barrier that follows every wave's reads of
+// it; waits name the exact number of later loads still allowed in flight.
+// ---------------------------------------------------------------------------
+constexpr int PBM = 256, PBN = 128, PBK = 64;
+constexpr int kPipeLoadsPerWave = 8 + 4;  // A, B global_load_lds per wave and K step
+
+typedef short s4v __attribute__((ext_vector_type(4)));
+#define SA_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
+#define SA_LDS4(ptr) ((__attribute__((address_space(3))) s4v*)(ptr))
+
+__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
+
+// s_waitcnt encoding (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt 6:4
+// (7 = no wait), lgkmcnt 11:8 (0 = all LDS reads done)
+template <int VM>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One global_load_lds_dwordx4: 16 bytes from `src` (per lane) to LDS at
+// lds_base + 16 * lane.  Written as inline asm so that the compiler's
+// automatic waits do not treat the load as a pending write to every LDS
+// array (it cannot tell the stages apart and would drain all loads before
+// each read); the waits are stated by stage_barrier instead.  The
+// instruction has no result register, and the memory clobber keeps LDS
+// reads on their side of it.
+__device__ __forceinline__ void load_to_lds16(const uint16_t* src, const uint16_t* lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(base)
+      : "memory", "m0");
+}
+
+// This wave's share of the loads of K step starting at k0 into one stage.
+// Rows past T and columns past d_out read clamped (valid) addresses; their
+// results are never stored.
+__device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t n0, int64_t k0,
+                                           uint16_t* As, uint16_t* Bs) {
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rb = (w * 8 + i) * 8;  // 8 rows of 128 bytes per instruction
+    const int r = rb + lane / 8;
+    const int gc = (lane % 8) ^ swz_a(r);
+    int64_t row = m0 + r;
+    if (row >= p.T) row = p.T - 1;
+    load_to_lds16(p.x + row * p.d_in + k0 + 8 * gc, As + rb * PBK);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kb = (w * 4 + i) * 4;  // 4 k rows of 256 bytes per instruction
+    const int k = kb + lane / 16;
+    const int gc = (lane % 16) ^ swz_b(k);
+    int64_t n = n0 + 8 * gc;
+    if (n >= p.d_out) n = p.d_out - 8;
+    load_to_lds16(p.wt + (k0 + k) * p.d_out + n, Bs + kb * PBN);
+  }
+}
+
+__device__ __forceinline__ void pipe_compute(const uint16_t* As, const uint16_t* Bs,
+                                             f16v (&acc)[4][2], int wm, int wn) {
+  const int lane = lane_id();
+  const int g = lane / 16, i = lane % 16;
+#pragma unroll
+  for (int kk = 0; kk < PBK / 16; ++kk) {
+    h8 aop[4], bop[2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int m = wm * 128 + 32 * a + lane % 32;
+      const int q = 2 * kk + lane / 32;
+      aop[a] = *reinterpret_cast<const h8*>(As + m * PBK + 8 * (q ^ swz_a(m)));
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s4v part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = kk * 16 + 8 * (g >> 1) + 4 * h + (i >> 2);
+        const int n = wn * 64 + 32 * b + 16 * (g & 1) + 4 * (i & 3);
+        const uint16_t* ptr = Bs + k * PBN + 8 * ((n / 8) ^ swz_b(k)) + 4 * ((n / 4) & 1);
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SA_LDS4(ptr));
+      }
+      typedef short s8v __attribute__((ext_vector_type(8)));
+      const s8v both = {part[0][0], part[0][1], part[0][2], part[0][3],
+                        part[1][0], part[1][1], part[1][2], part[1][3]};
+      bop[b] = __builtin_bit_cast(h8, both);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[a], bop[b], acc[a][b], 0, 0, 0);
+  }
+}
+
+// The whole K loop over the three stages.  The stage pointers are
+// __restrict__ parameters of one function, so after inlining every access
+// carries alias-scope metadata saying which stage it touches: the compiler
+// then waits, before each read, only for the loads into that stage -- the
+// wait already named by stage_barrier -- and not for the refill in flight.
+__device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_t n0,
+                                            uint16_t* __restrict__ S0, uint16_t* __restrict__ S1,
+                                            uint16_t* __restrict__ S2, f16v (&acc)[4][2], int wm,
+                                            int wn) {
+  uint16_t* const As0 = S0;
+  uint16_t* const As1 = S1;
+  uint16_t* const As2 = S2;
+  uint16_t* const Bs0 = S0 + PBM * PBK;
+  uint16_t* const Bs1 = S1 + PBM * PBK;
+  uint16_t* const Bs2 = S2 + PBM * PBK;
+  const int64_t nk = p.d_in / PBK;
+  pipe_issue(p, m0, n0, 0, As0, Bs0);
+  if (nk > 1) pipe_issue(p, m0, n0, PBK, As1, Bs1);
+  // Step t computes stage t % 3 and refills stage (t + 2) % 3.  The main
+  // loop runs while every refill exists, with no branch inside; the last
+  // one to four steps run in the tail with their own waits.
+  int64_t kt = 0;
+  for (; kt + 4 < nk; kt += 3) {
+    stage_barrier<kPipeLoadsPerWave>();
+    pipe_issue(p, m0, n0, (kt + 2) * PBK, As2, Bs2);
+    pipe_compute(As0, Bs0, acc, wm, wn);
+    stage_barrier<kPipeLoadsPerWave>();
+    pipe_issue(p, m0, n0, (kt + 3) * PBK, As0, Bs0);
+    pipe_compute(As1, Bs1, acc, wm, wn);
+    stage_barrier<kPipeLoadsPerWave>();
+    pipe_issue(p, m0, n0, (kt + 4) * PBK, As1, Bs1);
+    pipe_compute(As2, Bs2, acc, wm, wn);
+  }
+#define SA_PIPE_TAIL(t, CA, CB, NA, NB)                                \
+  if ((t) < nk) {                                                      \
+    if ((t) + 1 < nk)                                                  \
+      stage_barrier<kPipeLoadsPerWave>();                              \
+    else                                                               \
+      stage_barrier<0>();                                              \
+    if ((t) + 2 < nk) pipe_issue(p, m0, n0, ((t) + 2) * PBK, NA, NB);   \
+    pipe_compute(CA, CB, acc, wm, wn);                                 \
+  }
+  SA_PIPE_TAIL(kt, As0, Bs0, As2, Bs2)
+  SA_PIPE_TAIL(kt + 1, As1, Bs1, As0, Bs0)
+  SA_PIPE_TAIL(kt + 2, As2, Bs2, As1, Bs1)
+  SA_PIPE_TAIL(kt + 3, As0, Bs0, As2, Bs2)
+#undef SA_PIPE_TAIL
+}
+
+__global__ __launch_bounds__(NTH) void k_gemm_pipe(GParams p) {
+  // one array per stage (A then B)
+  constexpr int kStageHalves = PBM * PBK + PBK * PBN;
+  __shared__ __align__(16) uint16_t S0[kStageHalves], S1[kStageHalves], S2[kStageHalves];
+  const int lane = lane_id();
+  const int wave = (int)threadIdx.x / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  const int64_t mt = (p.T + PBM - 1) / PBM;
+  const int64_t m0 = (int64_t)(blockIdx.x % mt) * PBM;
+  const int64_t n0 = (int64_t)(blockIdx.x / mt) * PBN;
+
+  f16v acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  pipe_k_loop(p, m0, n0, S0, S1, S2, acc, wm, wn);
+
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = n0 + wn * 64 + b * 32 + lane % 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 128 + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        if (row < p.T && col < p.d_out) p.y[row * p.d_out + col] = f2h(acc[a][b][r]);
+      }
+    }
+}
+
+bool pipe_ok(const GParams& p) {
+  return p.d_in % PBK == 0 && p.d_out % 8 == 0 && p.d_out >= 8 && p.T >= 1 &&
+         (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 &&
+         (reinterpret_cast<uintptr_t>(p.wt) & 15u) == 0;
+}
+
+int g_gemm_engine = 0;  // tuning override: 0 = automatic, 1 = staged-register engine, 2 = pipelined
+
 template <int AK, int BM>
 hipError_t launch_tile(const GParams& p, hipStream_t s) {
   const int64_t tiles = ((p.T + BM - 1) / BM) * ((p.d_out + BN - 1) / BN);
@@ -365,6 +581,8 @@ hipError_t launch_kind(const GParams& p, hipStream_t s) {
 int gemm_set_tile_rows(int bm) {
   if (bm != 0 && bm != 128 && bm != 256) return 1;
   g_gemm_bm = bm;
+  // an explicit tile height selects the staged-register engine
+  g_gemm_engine = bm == 0 ? 0 : 1;
   return 0;
 }
 
@@ -377,6 +595,12 @@ hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const u
   p.T = T;
   p.d_in = d_in;
   p.d_out = d_out;
+  if (g_gemm_engine != 1 && pipe_ok(p)) {
+    const int64_t tiles = ((T + PBM - 1) / PBM) * ((d_out + PBN - 1) / PBN);
+    if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
+    hipLaunchKernelGGL(k_gemm_pipe, dim3((unsigned)tiles), dim3(NTH), 0, s, p);
+    return hipGetLastError();
+  }
   return launch_kind<kADense>(p, s);
 }
 

@@ -447,6 +447,18 @@ def test_dense_gemm_small(T, d_in, d_out, tile_rows):
     assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
 
 
+@pytest.mark.parametrize("T,d_in,d_out", [(256, 64, 128), (300, 128, 136), (17, 192, 8),
+                                          (513, 256, 264), (256, 320, 128), (70, 448, 1000),
+                                          (260, 1088, 392)])
+def test_dense_gemm_k_pipeline_lengths(T, d_in, d_out):
+    """K a multiple of 64 takes the pipelined engine: 1 to 7 and 17 K steps
+    cover the steady loop and every tail length, with ragged rows/columns."""
+    X = syn.gaussian_f16((T, d_in), 1.0, T + d_in)
+    wt = syn.weight_t(d_out, d_in, d_out)
+    Y = sa.dense_gemm(dev(X), dev(wt))
+    assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
+
+
 @pytest.mark.parametrize("tile_rows", [128, 256])
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 4), (3, 4), (5, 16),
                                  (32, 32)])
