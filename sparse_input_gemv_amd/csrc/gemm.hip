@@ -339,33 +339,59 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined engine (dense A, d_in a multiple of 64, 16-byte aligned rows).
-// A 256-thread workgroup computes a 256 x 128 output tile, four waves of
-// 128 x 64; the K loop steps by 64 through three LDS stages.  Tiles go from
-// global memory to LDS with direct loads (global_load_lds_dwordx4: lane l's
-// 16 bytes land at the instruction's LDS base + 16 l), two K steps ahead,
-// so no registers hold staged data and the loads of step t+2 overlap the
-// MFMAs of step t.
-//   A (X rows, K-contiguous) is stored [m][64] with its 16-byte chunks
-//     XOR-swizzled by the row, chosen by each lane's global source address,
-//     so the 32 rows one MFMA operand read touches fall in distinct banks.
+// Pipelined engine (dense and 2:4 A, d_in a multiple of 64, 16-byte aligned
+// rows).  A 256-thread workgroup computes a 256 x 128 output tile, four
+// waves of 128 x 64; the K loop steps by 64 through three LDS stages.
+// Tiles go from global memory to LDS with direct loads (global_load_lds:
+// lane l's bytes land at the instruction's LDS base + size * l), two K steps
+// ahead, so no registers hold staged data and the loads of step t+2 overlap
+// the MFMAs of step t.
+//   A, dense: X rows, K-contiguous, stored [m][64] with 16-byte chunks
+//     XOR-swizzled by the row (chosen through each lane's source address) so
+//     the 32 rows one operand read touches fall in distinct banks.
+//   A, 2:4: the compressed values, [m][32] (swizzled the same way for
+//     64-byte rows), and the row's two 32-bit mask words [m][2]; each lane
+//     turns its 16 mask bits into the position code of the sparse MFMA.
 //   B (WT, N-contiguous) is stored [k][128] as it lies in memory (chunks
-//     swizzled by k), and the MFMA B operand -- 8 consecutive k of one
-//     column -- comes from two LDS transpose reads (ds_read_b64_tr_b16):
-//     within a 16-lane group, source lane s addresses 4 halves of row
-//     k0 + s/4 at column c0 + 4 (s % 4), and lane i receives column c0 + i
-//     of rows k0 .. k0+3 (layout checked on the device).
+//     swizzled by k); the MFMA B operand -- consecutive k of one column --
+//     comes from LDS transpose reads (ds_read_b64_tr_b16): within a 16-lane
+//     group, source lane s addresses 4 halves of row k0 + s/4 at column
+//     c0 + 4 (s % 4), and lane i receives column c0 + i of rows k0 .. k0+3
+//     (layout checked on the device).
 // A stage is reused only after a barrier that follows every wave's reads of
-// it; waits name the exact number of later loads still allowed in flight.
+// it; each wait names the exact number of later loads allowed in flight.
+// The MFMA sequence per output block is the staged-register engine's, so
+// both engines give identical results.
 // ---------------------------------------------------------------------------
 constexpr int PBM = 256, PBN = 128, PBK = 64;
-constexpr int kPipeLoadsPerWave = 8 + 4;  // A, B global_load_lds per wave and K step
 
 typedef short s4v __attribute__((ext_vector_type(4)));
-#define SA_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
 #define SA_LDS4(ptr) ((__attribute__((address_space(3))) s4v*)(ptr))
 
+template <int AK>
+struct Pipe;
+template <>
+struct Pipe<kADense> {
+  static constexpr int kAHalves = PBM * PBK;  // [256][64]
+  static constexpr int kMaskWords = 0;
+  static constexpr int kLoadsPerWave = 8 + 4;  // A, B
+};
+template <>
+struct Pipe<kA24> {
+  static constexpr int kAHalves = PBM * PBK / 2;  // [256][32] compressed
+  static constexpr int kMaskWords = PBM * 2;      // [256][2]
+  static constexpr int kLoadsPerWave = 4 + 4 + 2;  // A, B, mask
+};
+template <int AK>
+constexpr int pipe_stage_halves() {
+  return Pipe<AK>::kAHalves + PBK * PBN + 2 * Pipe<AK>::kMaskWords;
+}
+
+// 16-byte chunk swizzles: A rows of 128 bytes (dense), of 64 bytes (2:4),
+// B rows of 256 bytes.  Each spreads the rows one operand read touches over
+// distinct banks for 32 or 64 LDS banks.
 __device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_a24(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
 
 // s_waitcnt encoding (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt 6:4
@@ -381,40 +407,77 @@ __device__ __forceinline__ void stage_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// One global_load_lds_dwordx4: 16 bytes from `src` (per lane) to LDS at
-// lds_base + 16 * lane.  Written as inline asm so that the compiler's
-// automatic waits do not treat the load as a pending write to every LDS
-// array (it cannot tell the stages apart and would drain all loads before
-// each read); the waits are stated by stage_barrier instead.  The
+// One global_load_lds of 16 (or 4) bytes per lane: from `src` to LDS at
+// lds_base + 16 * lane (4 * lane).  Written as inline asm so that the
+// compiler's automatic waits do not treat the load as a pending write to
+// every LDS array (it cannot tell the stages apart and would drain all loads
+// before each read); the waits are stated by stage_barrier instead.  The
 // instruction has no result register, and the memory clobber keeps LDS
 // reads on their side of it.
-__device__ __forceinline__ void load_to_lds16(const uint16_t* src, const uint16_t* lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+__device__ __forceinline__ void load_to_lds16(const void* src, const void* lds_base) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, off"
       :
-      : "v"(src), "s"(base)
+      : "v"(src), "s"(lds_addr(lds_base))
+      : "memory", "m0");
+}
+__device__ __forceinline__ void load_to_lds4(const void* src, const void* lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(src), "s"(lds_addr(lds_base))
       : "memory", "m0");
 }
 
-// This wave's share of the loads of K step starting at k0 into one stage.
-// Rows past T and columns past d_out read clamped (valid) addresses; their
-// results are never stored.
+// This wave's share of the loads of the K step starting at k0 into one stage
+// (A, then B, then for 2:4 the mask words).  Rows past T and columns past
+// d_out read clamped (valid) addresses; their results are never stored.
+template <int AK>
 __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t n0, int64_t k0,
-                                           uint16_t* As, uint16_t* Bs) {
+                                           uint16_t* S) {
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  uint16_t* As = S;
+  uint16_t* Bs = S + Pipe<AK>::kAHalves;
+  if constexpr (AK == kADense) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rb = (w * 8 + i) * 8;  // 8 rows of 128 bytes per instruction
-    const int r = rb + lane / 8;
-    const int gc = (lane % 8) ^ swz_a(r);
-    int64_t row = m0 + r;
-    if (row >= p.T) row = p.T - 1;
-    load_to_lds16(p.x + row * p.d_in + k0 + 8 * gc, As + rb * PBK);
+    for (int i = 0; i < 8; ++i) {
+      const int rb = (w * 8 + i) * 8;  // 8 rows of 128 bytes per instruction
+      const int r = rb + lane / 8;
+      const int gc = (lane % 8) ^ swz_a(r);
+      int64_t row = m0 + r;
+      if (row >= p.T) row = p.T - 1;
+      load_to_lds16(p.x + row * p.d_in + k0 + 8 * gc, As + rb * PBK);
+    }
+  } else {
+    const int64_t kc = p.d_in / 2;  // compressed row length
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rb = (w * 4 + i) * 16;  // 16 rows of 64 bytes per instruction
+      const int r = rb + lane / 4;
+      const int gc = (lane % 4) ^ swz_a24(r);
+      int64_t row = m0 + r;
+      if (row >= p.T) row = p.T - 1;
+      load_to_lds16(p.x + row * kc + k0 / 2 + 8 * gc, As + rb * (PBK / 2));
+    }
+    uint32_t* Ms = reinterpret_cast<uint32_t*>(Bs + PBK * PBN);
+    const int64_t words = p.d_in / 32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rb = (w * 2 + i) * 32;  // 32 rows of 2 words per instruction
+      const int r = rb + lane / 2;
+      int64_t row = m0 + r;
+      if (row >= p.T) row = p.T - 1;
+      load_to_lds4(p.mask + row * words + k0 / 32 + (lane % 2), Ms + rb * 2);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -427,94 +490,142 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
   }
 }
 
-__device__ __forceinline__ void pipe_compute(const uint16_t* As, const uint16_t* Bs,
-                                             f16v (&acc)[4][2], int wm, int wn) {
+// Four consecutive k (kq .. kq+3, plus 8 for lanes 32..63) of this lane's
+// column of the 32-column block starting at c0, by one transpose read.
+__device__ __forceinline__ s4v b_quad(const uint16_t* Bs, int kq, int c0) {
   const int lane = lane_id();
   const int g = lane / 16, i = lane % 16;
+  const int k = kq + 8 * (g >> 1) + (i >> 2);
+  const int n = c0 + 16 * (g & 1) + 4 * (i & 3);
+  const uint16_t* ptr = Bs + k * PBN + 8 * ((n / 8) ^ swz_b(k)) + 4 * ((n / 4) & 1);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(SA_LDS4(ptr));
+}
+
+// Sparse MFMA position code of 16 mask bits: per group of 4, the first kept
+// position | the second << 2 (as the staged-register engine forms it).
+__device__ __forceinline__ int code_of(uint32_t bits) {
+  uint32_t code = 0;
 #pragma unroll
-  for (int kk = 0; kk < PBK / 16; ++kk) {
-    h8 aop[4], bop[2];
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t nib = (bits >> (4 * g)) & 0xfu;
+    const uint32_t p0 = nib ? (uint32_t)__builtin_ctz(nib) : 0u;
+    const uint32_t rest = nib & (nib - 1u);
+    const uint32_t p1 = rest ? (uint32_t)__builtin_ctz(rest) : (p0 == 3u ? 3u : p0 + 1u);
+    code |= (p0 | (p1 << 2)) << (4 * g);
+  }
+  return (int)code;
+}
+
+template <int AK>
+__device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* code_lut,
+                                             f16v (&acc)[4][2], int wm, int wn) {
+  const int lane = lane_id();
+  const uint16_t* As = S;
+  const uint16_t* Bs = S + Pipe<AK>::kAHalves;
+  if constexpr (AK == kADense) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int m = wm * 128 + 32 * a + lane % 32;
-      const int q = 2 * kk + lane / 32;
-      aop[a] = *reinterpret_cast<const h8*>(As + m * PBK + 8 * (q ^ swz_a(m)));
-    }
+    for (int kk = 0; kk < PBK / 16; ++kk) {
+      h8 aop[4], bop[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s4v part[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = kk * 16 + 8 * (g >> 1) + 4 * h + (i >> 2);
-        const int n = wn * 64 + 32 * b + 16 * (g & 1) + 4 * (i & 3);
-        const uint16_t* ptr = Bs + k * PBN + 8 * ((n / 8) ^ swz_b(k)) + 4 * ((n / 4) & 1);
-        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SA_LDS4(ptr));
+      for (int a = 0; a < 4; ++a) {
+        const int m = wm * 128 + 32 * a + lane % 32;
+        const int q = 2 * kk + lane / 32;
+        aop[a] = *reinterpret_cast<const h8*>(As + m * PBK + 8 * (q ^ swz_a(m)));
       }
-      typedef short s8v __attribute__((ext_vector_type(8)));
-      const s8v both = {part[0][0], part[0][1], part[0][2], part[0][3],
-                        part[1][0], part[1][1], part[1][2], part[1][3]};
-      bop[b] = __builtin_bit_cast(h8, both);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int c0 = wn * 64 + 32 * b;
+        const s4v q0 = b_quad(Bs, kk * 16, c0), q1 = b_quad(Bs, kk * 16 + 4, c0);
+        typedef short s8v __attribute__((ext_vector_type(8)));
+        const s8v both = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+        bop[b] = __builtin_bit_cast(h8, both);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[a], bop[b], acc[a][b], 0, 0, 0);
     }
+  } else {
+    const uint32_t* Ms = reinterpret_cast<const uint32_t*>(Bs + PBK * PBN);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int kk = 0; kk < PBK / 32; ++kk) {
+      h8 aop[4];
+      int code[4];
+      h16 bop[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[a], bop[b], acc[a][b], 0, 0, 0);
+      for (int a = 0; a < 4; ++a) {
+        const int m = wm * 128 + 32 * a + lane % 32;
+        const int q = 2 * kk + lane / 32;
+        aop[a] = *reinterpret_cast<const h8*>(As + m * (PBK / 2) + 8 * (q ^ swz_a24(m)));
+        // position code of this lane's 16 mask bits, a byte at a time
+        const uint32_t bits = Ms[m * 2 + kk] >> (16 * (lane / 32));
+        code[a] = (int)code_lut[bits & 0xffu] | ((int)code_lut[(bits >> 8) & 0xffu] << 8);
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int c0 = wn * 64 + 32 * b;
+        const s4v q0 = b_quad(Bs, kk * 32, c0), q1 = b_quad(Bs, kk * 32 + 4, c0);
+        const s4v q2 = b_quad(Bs, kk * 32 + 16, c0), q3 = b_quad(Bs, kk * 32 + 20, c0);
+        typedef short s16v __attribute__((ext_vector_type(16)));
+        const s16v all = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3],
+                          q2[0], q2[1], q2[2], q2[3], q3[0], q3[1], q3[2], q3[3]};
+        bop[b] = __builtin_bit_cast(h16, all);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] =
+              __builtin_amdgcn_smfmac_f32_32x32x32_f16(aop[a], bop[b], acc[a][b], code[a], 0, 0);
+    }
   }
 }
 
-// The whole K loop over the three stages.  The stage pointers are
-// __restrict__ parameters of one function, so after inlining every access
-// carries alias-scope metadata saying which stage it touches: the compiler
-// then waits, before each read, only for the loads into that stage -- the
-// wait already named by stage_barrier -- and not for the refill in flight.
+// The whole K loop over the three stages.  Step t computes stage t % 3 and
+// refills stage (t + 2) % 3.  The main loop runs while every refill exists,
+// with no branch inside; the last one to four steps run in the tail with
+// their own waits.
+template <int AK>
 __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_t n0,
-                                            uint16_t* __restrict__ S0, uint16_t* __restrict__ S1,
-                                            uint16_t* __restrict__ S2, f16v (&acc)[4][2], int wm,
+                                            uint16_t* S0, uint16_t* S1, uint16_t* S2,
+                                            const uint8_t* code_lut, f16v (&acc)[4][2], int wm,
                                             int wn) {
-  uint16_t* const As0 = S0;
-  uint16_t* const As1 = S1;
-  uint16_t* const As2 = S2;
-  uint16_t* const Bs0 = S0 + PBM * PBK;
-  uint16_t* const Bs1 = S1 + PBM * PBK;
-  uint16_t* const Bs2 = S2 + PBM * PBK;
+  constexpr int LPW = Pipe<AK>::kLoadsPerWave;
   const int64_t nk = p.d_in / PBK;
-  pipe_issue(p, m0, n0, 0, As0, Bs0);
-  if (nk > 1) pipe_issue(p, m0, n0, PBK, As1, Bs1);
-  // Step t computes stage t % 3 and refills stage (t + 2) % 3.  The main
-  // loop runs while every refill exists, with no branch inside; the last
-  // one to four steps run in the tail with their own waits.
+  pipe_issue<AK>(p, m0, n0, 0, S0);
+  if (nk > 1) pipe_issue<AK>(p, m0, n0, PBK, S1);
   int64_t kt = 0;
   for (; kt + 4 < nk; kt += 3) {
-    stage_barrier<kPipeLoadsPerWave>();
-    pipe_issue(p, m0, n0, (kt + 2) * PBK, As2, Bs2);
-    pipe_compute(As0, Bs0, acc, wm, wn);
-    stage_barrier<kPipeLoadsPerWave>();
-    pipe_issue(p, m0, n0, (kt + 3) * PBK, As0, Bs0);
-    pipe_compute(As1, Bs1, acc, wm, wn);
-    stage_barrier<kPipeLoadsPerWave>();
-    pipe_issue(p, m0, n0, (kt + 4) * PBK, As1, Bs1);
-    pipe_compute(As2, Bs2, acc, wm, wn);
+    stage_barrier<LPW>();
+    pipe_issue<AK>(p, m0, n0, (kt + 2) * PBK, S2);
+    pipe_compute<AK>(S0, code_lut, acc, wm, wn);
+    stage_barrier<LPW>();
+    pipe_issue<AK>(p, m0, n0, (kt + 3) * PBK, S0);
+    pipe_compute<AK>(S1, code_lut, acc, wm, wn);
+    stage_barrier<LPW>();
+    pipe_issue<AK>(p, m0, n0, (kt + 4) * PBK, S1);
+    pipe_compute<AK>(S2, code_lut, acc, wm, wn);
   }
-#define SA_PIPE_TAIL(t, CA, CB, NA, NB)                                \
-  if ((t) < nk) {                                                      \
-    if ((t) + 1 < nk)                                                  \
-      stage_barrier<kPipeLoadsPerWave>();                              \
-    else                                                               \
-      stage_barrier<0>();                                              \
-    if ((t) + 2 < nk) pipe_issue(p, m0, n0, ((t) + 2) * PBK, NA, NB);   \
-    pipe_compute(CA, CB, acc, wm, wn);                                 \
+#define SA_PIPE_TAIL(t, CS, NS)                                       \
+  if ((t) < nk) {                                                     \
+    if ((t) + 1 < nk)                                                 \
+      stage_barrier<LPW>();                                           \
+    else                                                              \
+      stage_barrier<0>();                                             \
+    if ((t) + 2 < nk) pipe_issue<AK>(p, m0, n0, ((t) + 2) * PBK, NS); \
+    pipe_compute<AK>(CS, code_lut, acc, wm, wn);                      \
   }
-  SA_PIPE_TAIL(kt, As0, Bs0, As2, Bs2)
-  SA_PIPE_TAIL(kt + 1, As1, Bs1, As0, Bs0)
-  SA_PIPE_TAIL(kt + 2, As2, Bs2, As1, Bs1)
-  SA_PIPE_TAIL(kt + 3, As0, Bs0, As2, Bs2)
+  SA_PIPE_TAIL(kt, S0, S2)
+  SA_PIPE_TAIL(kt + 1, S1, S0)
+  SA_PIPE_TAIL(kt + 2, S2, S1)
+  SA_PIPE_TAIL(kt + 3, S0, S2)
 #undef SA_PIPE_TAIL
 }
 
+template <int AK>
 __global__ __launch_bounds__(NTH) void k_gemm_pipe(GParams p) {
-  // one array per stage (A then B)
-  constexpr int kStageHalves = PBM * PBK + PBK * PBN;
+  constexpr int kStageHalves = pipe_stage_halves<AK>();
   __shared__ __align__(16) uint16_t S0[kStageHalves], S1[kStageHalves], S2[kStageHalves];
   const int lane = lane_id();
   const int wave = (int)threadIdx.x / kWave;
@@ -531,7 +642,11 @@ __global__ __launch_bounds__(NTH) void k_gemm_pipe(GParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  pipe_k_loop(p, m0, n0, S0, S1, S2, acc, wm, wn);
+  // 2:4: position code of every mask byte (two groups of 4), built once;
+  // the first stage barrier orders these writes before any read
+  __shared__ uint8_t code_lut[AK == kA24 ? 256 : 1];
+  if constexpr (AK == kA24) code_lut[threadIdx.x] = (uint8_t)code_of(threadIdx.x);
+  pipe_k_loop<AK>(p, m0, n0, S0, S1, S2, code_lut, acc, wm, wn);
 
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -549,7 +664,16 @@ __global__ __launch_bounds__(NTH) void k_gemm_pipe(GParams p) {
 bool pipe_ok(const GParams& p) {
   return p.d_in % PBK == 0 && p.d_out % 8 == 0 && p.d_out >= 8 && p.T >= 1 &&
          (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 &&
-         (reinterpret_cast<uintptr_t>(p.wt) & 15u) == 0;
+         (reinterpret_cast<uintptr_t>(p.wt) & 15u) == 0 &&
+         (reinterpret_cast<uintptr_t>(p.mask) & 3u) == 0;
+}
+
+template <int AK>
+hipError_t launch_pipe(const GParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.T + PBM - 1) / PBM) * ((p.d_out + PBN - 1) / PBN);
+  if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
+  hipLaunchKernelGGL(k_gemm_pipe<AK>, dim3((unsigned)tiles), dim3(NTH), 0, s, p);
+  return hipGetLastError();
 }
 
 int g_gemm_engine = 0;  // tuning override: 0 = automatic, 1 = staged-register engine, 2 = pipelined
@@ -595,12 +719,7 @@ hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const u
   p.T = T;
   p.d_in = d_in;
   p.d_out = d_out;
-  if (g_gemm_engine != 1 && pipe_ok(p)) {
-    const int64_t tiles = ((T + PBM - 1) / PBM) * ((d_out + PBN - 1) / PBN);
-    if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
-    hipLaunchKernelGGL(k_gemm_pipe, dim3((unsigned)tiles), dim3(NTH), 0, s, p);
-    return hipGetLastError();
-  }
+  if (g_gemm_engine != 1 && pipe_ok(p)) return launch_pipe<kADense>(p, s);
   return launch_kind<kADense>(p, s);
 }
 
@@ -619,7 +738,10 @@ hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
   p.m = m;
   // 2:4 on the sparse MFMA; every other pattern through zero-filled dense
   // tiles (vector loads when m divides 4n)
-  if (n == 2 && m == 4) return launch_kind<kA24>(p, s);
+  if (n == 2 && m == 4) {
+    if (g_gemm_engine != 1 && pipe_ok(p)) return launch_pipe<kA24>(p, s);
+    return launch_kind<kA24>(p, s);
+  }
   if ((4 * n) % m == 0) return launch_kind<kANMVec>(p, s);
   return launch_kind<kANM>(p, s);
 }

@@ -459,7 +459,7 @@ def test_dense_gemm_k_pipeline_lengths(T, d_in, d_out):
     assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
 
 
-@pytest.mark.parametrize("tile_rows", [128, 256])
+@pytest.mark.parametrize("tile_rows", [0, 128, 256])
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 4), (3, 4), (5, 16),
                                  (32, 32)])
 @pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 512), (100, 96, 136), (300, 128, 264)])
@@ -480,6 +480,28 @@ def test_nm_spmm_small(n, m, T, d_in, d_out, tile_rows):
     # each token's row is that token's masked GEMV
     r = 3
     assert_close(sa.masked_gemv(dev(wt), dev(X[r]), mask_g[r]), ref[r])
+
+
+@pytest.mark.parametrize("T,d_in,d_out", [(256, 64, 128), (300, 192, 136), (513, 320, 264),
+                                          (70, 1088, 1000), (1024, 1024, 1024)])
+def test_gemm_engines_agree(T, d_in, d_out):
+    """The pipelined engine (default when K is a multiple of 64) and the
+    staged-register engine (forced by a tile height) issue the same MFMA
+    sequence per output block: dense and 2:4 results must be identical."""
+    X = syn.gaussian_f16((T, d_in), 1.0, T * 7 + d_in)
+    X_g, wt_g = dev(X), dev(syn.weight_t(d_out, d_in, d_out + 3))
+    mask_g, val_g = sa.act_sparsify_nm(X_g, 2, 4)
+    out = {}
+    try:
+        for tr in (0, 128, 256):
+            sa.set_gemm_tuning(tr)
+            out[tr] = (sa.dense_gemm(X_g, wt_g).clone(),
+                       sa.nm_act_spmm(val_g, mask_g, 2, 4, wt_g).clone())
+    finally:
+        sa.set_gemm_tuning(0)
+    for tr in (128, 256):
+        assert torch.equal(out[0][0], out[tr][0]), ("dense", tr)
+        assert torch.equal(out[0][1], out[tr][1]), ("2:4", tr)
 
 
 @pytest.mark.parametrize("T,d_in,d_out", [(4096, 1024, 1024), (2048, 4096, 11008)])
