@@ -234,13 +234,23 @@ int dense_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in,
  *
  *   xval [T][d_in*n/m] fp16;  mask [T][d_in/32] (exactly n bits per group)
  *   wt   [d_in][d_out] fp16;  y [T][d_out] fp16
+ *   ws   NULL, or a device workspace of sa_nm_spmm_workspace_bytes() bytes
+ *        (16-byte aligned; its contents on entry do not matter).  With it,
+ *        patterns other than 2:4 take two passes -- expand the compressed
+ *        values into a zero-filled dense copy in ws, then the dense MFMA
+ *        engine -- which is much faster than the single pass without it.
+ *        Both give the same result.
  * Requires m in {4,8,16,32}, 1 <= n <= m, d_in % 32 == 0, d_out % 8 == 0,
- * wt, y and xval 16-byte aligned.  A mask that breaks the N:M contract gives
- * unspecified values but never an out-of-bounds access.
+ * wt, y and xval 16-byte aligned.  SA_ERR_WORKSPACE if ws is too small.  A
+ * mask that breaks the N:M contract gives unspecified values but never an
+ * out-of-bounds access.
  */
 int nm_act_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
                 int64_t d_in, int n, int m, const uint16_t* wt, int64_t d_out,
-                uint16_t* y, void* stream);
+                uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+/* Workspace bytes for nm_act_spmm's two-pass path (0 for 2:4, which has
+ * none; 0 for invalid sizes). */
+size_t sa_nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m);
 
 /*
  * dense_gemm -- Y[t][o] = sum_k X[t][k] WT[k][o] (Y = X W^T) on MFMA: the

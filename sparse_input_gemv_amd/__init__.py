@@ -52,7 +52,8 @@ _SIGNATURES = {
     "masked_swiglu_down": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _f64, _i32, _vp, _vp, _vp,
                                   _vp, _sz, _vp]),
     "weight_col_norms": (_i32, [_vp, _i64, _i64, _vp, _vp]),
-    "nm_act_spmm": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp]),
+    "nm_act_spmm": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "sa_nm_spmm_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "dense_gemm": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "sa_set_gemv_tuning": (_i32, [_i32, _i32, _i32]),
     "sa_set_gemm_tuning": (_i32, [_i32]),
@@ -309,9 +310,18 @@ def weight_col_norms(wt: torch.Tensor) -> torch.Tensor:
 
 # ---- batched matmuls ---------------------------------------------------------
 
+# The GEMV workspace starts with hand-off counters that must stay zero; the
+# matmul's scratch copy goes after them in the same per-device buffer.
+WS_TICKET_BYTES = 1 << 20
+
+
 def nm_act_spmm(xval: torch.Tensor, mask: torch.Tensor, n: int, m: int, wt: torch.Tensor,
-                y: torch.Tensor | None = None):
-    """``Y = (mask ⊙ X) W^T`` from the compressed N:M activations."""
+                y: torch.Tensor | None = None, use_workspace: bool = True):
+    """``Y = (mask ⊙ X) W^T`` from the compressed N:M activations.
+
+    With ``use_workspace`` (the default) patterns other than 2:4 take the
+    library's two-pass path through the per-device workspace.
+    """
     _dev(xval, "xval", torch.float16)
     _dev(mask, "mask", torch.int32)
     _dev(wt, "wt", torch.float16)
@@ -319,8 +329,13 @@ def nm_act_spmm(xval: torch.Tensor, mask: torch.Tensor, n: int, m: int, wt: torc
     d_in, d_out = wt.shape
     if y is None:
         y = torch.empty((T, d_out), dtype=torch.float16, device=wt.device)
+    ws_ptr, ws_bytes = None, 0
+    need = int(lib().sa_nm_spmm_workspace_bytes(T, d_in, n, m))
+    if use_workspace and need > 0:
+        ws = workspace(wt.device, WS_TICKET_BYTES + need)
+        ws_ptr, ws_bytes = ws.data_ptr() + WS_TICKET_BYTES, ws.numel() - WS_TICKET_BYTES
     _check(lib().nm_act_spmm(_ptr(xval), _ptr(mask), T, d_in, n, m, _ptr(wt), d_out, _ptr(y),
-                             _stream(wt)), "nm_act_spmm")
+                             ws_ptr, ws_bytes, _stream(wt)), "nm_act_spmm")
     return y
 
 

@@ -228,13 +228,31 @@ int weight_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* ou
                     "weight_col_norms");
 }
 
+size_t sa_nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m) {
+  if (T < 1 || d_in < 1 || m < 1 || n < 1 || n > m) return 0;
+  return sa::nm_spmm_workspace_bytes(T, d_in, n, m);
+}
+
 int nm_act_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in, int n,
-                int m, const uint16_t* wt, int64_t d_out, uint16_t* y, void* stream) {
+                int m, const uint16_t* wt, int64_t d_out, uint16_t* y, void* ws, size_t ws_bytes,
+                void* stream) {
   sa::clear_error();
   int st = sa::check_nm_spmm(xval, mask, T, d_in, n, m, wt, d_out, y);
   if (st != SA_OK) return st;
+  if (ws != nullptr) {
+    const size_t need = T > 0 ? sa::nm_spmm_workspace_bytes(T, d_in, n, m) : 0;
+    if (ws_bytes < need) {
+      sa::set_error("nm_act_spmm: workspace of %zu bytes, %zu needed", ws_bytes, need);
+      return SA_ERR_WORKSPACE;
+    }
+    if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) {
+      sa::set_error("nm_act_spmm: workspace must be 16-byte aligned");
+      return SA_ERR_INVALID_ARG;
+    }
+  }
   if (T == 0) return SA_OK;
-  hipError_t e = sa::launch_nm_spmm(xval, mask, T, d_in, n, m, wt, d_out, y, as_stream(stream));
+  hipError_t e = sa::launch_nm_spmm(xval, mask, T, d_in, n, m, wt, d_out, y, ws, ws_bytes,
+                                    as_stream(stream));
   if (e == hipErrorNotSupported) {
     sa::set_error("nm_act_spmm: shape not supported by the compiled kernels");
     return SA_ERR_UNSUPPORTED;

@@ -668,6 +668,77 @@ bool pipe_ok(const GParams& p) {
          (reinterpret_cast<uintptr_t>(p.mask) & 3u) == 0;
 }
 
+// ---------------------------------------------------------------------------
+// N:M patterns other than 2:4, two-pass path: the compressed values are
+// expanded into a zero-filled dense [T][d_in] copy (the "gathered dense"
+// operand written out once), then the pipelined dense engine runs on it.
+// One thread per 32-entry mask word: a word holds exactly 32n/m kept values
+// (m divides 32), at a fixed offset of the compressed array; they are
+// scattered to their set bits in an LDS tile and the workgroup's run of the
+// dense copy is written with 16-byte stores.  A mask word with more set bits
+// than that places only the first 32n/m values (no read past its run).
+// ---------------------------------------------------------------------------
+constexpr int kExpandThreads = 256;
+
+template <int NV>  // 16-byte vectors of kept values per word (per = 8 NV); 0 = scalar loads
+__global__ __launch_bounds__(kExpandThreads) void k_nm_expand(const uint16_t* __restrict__ xval,
+                                                              const uint32_t* __restrict__ mask,
+                                                              int64_t nwords, int per,
+                                                              uint16_t* __restrict__ xd) {
+  __shared__ __align__(16) uint16_t tile[kExpandThreads * 32];
+  const int tid = (int)threadIdx.x;
+  const int64_t w0 = (int64_t)blockIdx.x * kExpandThreads;
+  const int64_t w = w0 + tid;
+  uint16_t* mine = tile + tid * 32;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(mine + 8 * q) = u32x4{0u, 0u, 0u, 0u};
+  if (w < nwords) {
+    uint32_t bits = mask[w];
+    const uint16_t* src = xval + w * per;
+    if constexpr (NV > 0) {
+      u32x4 v[NV];
+#pragma unroll
+      for (int q = 0; q < NV; ++q) v[q] = *reinterpret_cast<const u32x4*>(src + 8 * q);
+#pragma unroll
+      for (int r = 0; r < 8 * NV; ++r) {
+        const uint32_t word = v[r / 8][(r % 8) / 2];  // static register index
+        if (bits != 0u) {
+          mine[__builtin_ctz(bits)] = (uint16_t)((r & 1) ? (word >> 16) : (word & 0xffffu));
+          bits &= bits - 1u;
+        }
+      }
+    } else {
+      for (int r = 0; r < per && bits != 0u; ++r) {
+        mine[__builtin_ctz(bits)] = src[r];
+        bits &= bits - 1u;
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t left = nwords - w0;
+  const int nthr = left < kExpandThreads ? (int)left : kExpandThreads;
+  uint16_t* dst = xd + w0 * 32;
+  for (int i = tid; i < nthr * 4; i += kExpandThreads)
+    *reinterpret_cast<u32x4*>(dst + 8 * i) = *reinterpret_cast<const u32x4*>(tile + 8 * i);
+}
+
+hipError_t launch_nm_expand(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
+                            int n, int m, uint16_t* xd, hipStream_t s) {
+  const int64_t nwords = T * (d_in / 32);
+  const int per = 32 * n / m;
+  const int64_t blocks = (nwords + kExpandThreads - 1) / kExpandThreads;
+  if (blocks > 0x7fffffffLL) return hipErrorNotSupported;
+  const dim3 grid((unsigned)blocks), block(kExpandThreads);
+  switch (per % 8 == 0 ? per / 8 : 0) {
+    case 1: hipLaunchKernelGGL(k_nm_expand<1>, grid, block, 0, s, xval, mask, nwords, per, xd); break;
+    case 2: hipLaunchKernelGGL(k_nm_expand<2>, grid, block, 0, s, xval, mask, nwords, per, xd); break;
+    case 3: hipLaunchKernelGGL(k_nm_expand<3>, grid, block, 0, s, xval, mask, nwords, per, xd); break;
+    case 4: hipLaunchKernelGGL(k_nm_expand<4>, grid, block, 0, s, xval, mask, nwords, per, xd); break;
+    default: hipLaunchKernelGGL(k_nm_expand<0>, grid, block, 0, s, xval, mask, nwords, per, xd);
+  }
+  return hipGetLastError();
+}
+
 template <int AK>
 hipError_t launch_pipe(const GParams& p, hipStream_t s) {
   const int64_t tiles = ((p.T + PBM - 1) / PBM) * ((p.d_out + PBN - 1) / PBN);
@@ -723,9 +794,14 @@ hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const u
   return launch_kind<kADense>(p, s);
 }
 
+size_t nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m) {
+  if (n == 2 && m == 4) return 0;
+  return (size_t)T * (size_t)d_in * 2;
+}
+
 hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
                           int n, int m, const uint16_t* wt, int64_t d_out, uint16_t* y,
-                          hipStream_t s) {
+                          void* ws, size_t ws_bytes, hipStream_t s) {
   GParams p{};
   p.x = xval;
   p.mask = mask;
@@ -741,6 +817,18 @@ hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
   if (n == 2 && m == 4) {
     if (g_gemm_engine != 1 && pipe_ok(p)) return launch_pipe<kA24>(p, s);
     return launch_kind<kA24>(p, s);
+  }
+  // two passes through the dense pipelined engine when a workspace is given
+  if (g_gemm_engine != 1 && ws != nullptr && ws_bytes >= nm_spmm_workspace_bytes(T, d_in, n, m) &&
+      (reinterpret_cast<uintptr_t>(ws) & 15u) == 0) {
+    GParams pd = p;
+    pd.x = static_cast<const uint16_t*>(ws);
+    pd.mask = nullptr;
+    if (pipe_ok(pd)) {
+      hipError_t e = launch_nm_expand(xval, mask, T, d_in, n, m, static_cast<uint16_t*>(ws), s);
+      if (e != hipSuccess) return e;
+      return launch_pipe<kADense>(pd, s);
+    }
   }
   if ((4 * n) % m == 0) return launch_kind<kANMVec>(p, s);
   return launch_kind<kANM>(p, s);

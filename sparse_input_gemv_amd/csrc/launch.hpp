@@ -77,9 +77,10 @@ int gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll);
 // ---- MFMA matmuls (gemm.hip) ------------------------------------------------
 hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
                              int64_t d_out, uint16_t* y, hipStream_t s);
+size_t nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m);
 hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
                           int n, int m, const uint16_t* wt, int64_t d_out, uint16_t* y,
-                          hipStream_t s);
+                          void* ws, size_t ws_bytes, hipStream_t s);
 int gemm_set_tile_rows(int bm);
 
 }  // namespace sa

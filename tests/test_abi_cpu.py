@@ -141,9 +141,15 @@ def test_swiglu_checks(sa):
 
 def test_matmul_checks(sa):
     f = sa.nm_act_spmm
-    assert f(P, P, 16, 1000, 2, 4, P, 1024, P, None) == SA_ERR_INVALID_ARG
-    assert f(P, P, 16, 1024, 3, 2, P, 1024, P, None) == SA_ERR_INVALID_ARG
-    assert f(P, P, 0, 1024, 2, 4, P, 1024, P, None) == SA_OK
+    assert f(P, P, 16, 1000, 2, 4, P, 1024, P, None, 0, None) == SA_ERR_INVALID_ARG
+    assert f(P, P, 16, 1024, 3, 2, P, 1024, P, None, 0, None) == SA_ERR_INVALID_ARG
+    assert f(P, P, 0, 1024, 2, 4, P, 1024, P, None, 0, None) == SA_OK
+    need = sa.sa_nm_spmm_workspace_bytes(16, 1024, 8, 16)
+    assert need == 16 * 1024 * 2
+    assert sa.sa_nm_spmm_workspace_bytes(16, 1024, 2, 4) == 0  # 2:4 needs none
+    assert sa.sa_nm_spmm_workspace_bytes(16, 1024, 5, 4) == 0  # invalid pattern
+    assert f(P, P, 16, 1024, 8, 16, P, 1024, P, P, need - 1, None) == SA_ERR_WORKSPACE
+    assert f(P, P, 16, 1024, 8, 16, P, 1024, P, P + 8, need, None) == SA_ERR_INVALID_ARG
     g = sa.dense_gemm
     assert g(P, 16, 1020, P, 1024, P, None) == SA_ERR_INVALID_ARG
     assert g(P, 0, 1024, P, 1024, P, None) == SA_OK

@@ -504,6 +504,26 @@ def test_gemm_engines_agree(T, d_in, d_out):
         assert torch.equal(out[0][1], out[tr][1]), ("2:4", tr)
 
 
+@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (4, 8), (1, 4), (3, 4), (5, 16), (7, 32),
+                                 (32, 32)])
+@pytest.mark.parametrize("T,d_in,d_out", [(256, 64, 128), (300, 192, 136), (70, 1088, 1000)])
+def test_nm_spmm_two_pass_matches_single_pass(T, d_in, d_out, n, m):
+    """With a workspace, N:M patterns other than 2:4 are expanded to a dense
+    copy and run on the dense engine; without one, they are scattered into
+    LDS tiles in one pass.  The MFMA sequence is the same: identical bits,
+    and both match the oracle."""
+    X = syn.gaussian_f16((T, d_in), 1.0, T + n * 31 + m)
+    X[1, :] = np.float16(0.25)  # ties
+    wt = syn.weight_t(d_out, d_in, d_out + m)
+    X_g, wt_g = dev(X), dev(wt)
+    mask_g, val_g = sa.act_sparsify_nm(X_g, n, m)
+    y2 = sa.nm_act_spmm(val_g, mask_g, n, m, wt_g)
+    y1 = sa.nm_act_spmm(val_g, mask_g, n, m, wt_g, use_workspace=False)
+    assert torch.equal(y1, y2)
+    keep = sparsify.nm_sparsify(X, n, m)[0]
+    assert_close(y2, spmm.nm_spmm(X, keep, wt))
+
+
 @pytest.mark.parametrize("T,d_in,d_out", [(4096, 1024, 1024), (2048, 4096, 11008)])
 @pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (16, 32)])
 def test_nm_spmm_full_shapes_sampled(T, d_in, d_out, n, m):
