@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--target-wgs", type=int, default=0, help="GEMV workgroup target (tuning)")
     ap.add_argument("--handoff", type=int, default=0, choices=[0, 1, 2],
                     help="split-K partial sum: 0 auto, 1 second launch, 2 same launch (tuning)")
-    ap.add_argument("--only", choices=["fused", "unfused", "dense"], default=None,
+    ap.add_argument("--only", choices=["fused", "unfused", "dense", "read"], default=None,
                     help="time a single path (for profiler runs)")
     ap.add_argument("--rows", default=None,
                     help="with --suite: comma-separated rows to run (a1..a9); default all")
@@ -145,6 +145,11 @@ def main():
     dense = [(L.dense_gemv,
               (w.data_ptr(), D_OUT, D_IN, x.data_ptr(), 1, y.data_ptr(), ws.data_ptr(),
                ws.numel(), sptr)) for w in rot]
+    # achievable read rate: a plain contiguous read of the headline's
+    # algorithmic bytes from the same rotation
+    read_bytes = (2 * D_OUT * nnz + 2 * D_IN + 2 * D_OUT) // 16 * 16
+    sink = torch.empty(sa.READ_STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+    readp = [(L.sa_read_stream, (w.data_ptr(), read_bytes, sink.data_ptr(), sptr)) for w in rot]
 
     def run(calls_per_step, steps):
         n = len(calls_per_step)
@@ -188,9 +193,10 @@ def main():
         "fused": [[c] for c in fused],
         "unfused": [[sparsify, c] for c in listed],
         "dense": [[c] for c in dense],
+        "read": [[c] for c in readp],
     }
     ms = {}
-    for name in ([args.only] if args.only else ["fused", "unfused", "dense"]):
+    for name in ([args.only] if args.only else ["fused", "unfused", "dense", "read"]):
         ms[name] = timed(paths[name], args.steps, args.warmup)
     head = args.only or "fused"
     ms_step = ms[head]
@@ -242,6 +248,14 @@ def main():
             dense_bytes / (ms["dense"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     if "unfused" in ms and head != "unfused":
         out["unfused_us"] = round(ms["unfused"] * 1000.0, 3)
+    if "read" in ms:
+        rgbs = read_bytes / (ms["read"] * 1e-3) / 1e9
+        out["read_stream_peak"] = {
+            "what": "plain contiguous read of the same byte count (sa_read_stream), same rotation",
+            "bytes": read_bytes, "us": round(ms["read"] * 1000.0, 3), "GBps": round(rgbs, 1),
+            "frac_of_8TBs": round(rgbs / HBM_PEAK_GBS, 4),
+            "headline_frac_of_read_peak": round(achieved / rgbs, 4) if head == "fused" else None,
+        }
 
     if not args.no_cpu_baseline and not args.only:
         out["cpu_baseline"] = cpu_baseline(rot[0].cpu().numpy(), x_np, t, args.cpu_seconds)

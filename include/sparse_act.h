@@ -261,6 +261,21 @@ size_t sa_nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m);
 int dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
                int64_t d_out, uint16_t* y, void* stream);
 
+/* ---- roofline calibration ----------------------------------------------- */
+
+/* Words of `sink` that sa_read_stream writes (one per wave of its grid). */
+#define SA_READ_STREAM_SINK_WORDS 8192
+
+/*
+ * sa_read_stream -- read every byte of src once with 16-byte loads (a fixed
+ * grid of 2048 x 256 threads, grid-stride) and fold it into sink, so that
+ * the achievable HBM read rate can be timed beside the nominal peak.  Not
+ * part of the method; bench-only.
+ *   src  device, 16-byte aligned, `bytes` a positive multiple of 16
+ *   sink device, SA_READ_STREAM_SINK_WORDS uint32 (contents meaningless)
+ */
+int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* ---- tuning hook -------------------------------------------------------- */
 
 /*

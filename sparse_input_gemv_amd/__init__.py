@@ -54,6 +54,7 @@ _SIGNATURES = {
     "weight_col_norms": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "nm_act_spmm": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp]),
     "sa_nm_spmm_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
+    "sa_read_stream": (_i32, [_vp, _sz, _vp, _vp]),
     "dense_gemm": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "sa_set_gemv_tuning": (_i32, [_i32, _i32, _i32]),
     "sa_set_gemm_tuning": (_i32, [_i32]),
@@ -313,6 +314,17 @@ def weight_col_norms(wt: torch.Tensor) -> torch.Tensor:
 # The GEMV workspace starts with hand-off counters that must stay zero; the
 # matmul's scratch copy goes after them in the same per-device buffer.
 WS_TICKET_BYTES = 1 << 20
+READ_STREAM_SINK_WORDS = 8192  # SA_READ_STREAM_SINK_WORDS
+
+
+def read_stream(src: torch.Tensor, nbytes: int | None = None) -> torch.Tensor:
+    """Bench-only: read ``nbytes`` of ``src`` once (roofline calibration);
+    returns the sink, whose xor equals the xor of the bytes read."""
+    _dev(src, "src", None)
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    sink = torch.empty(READ_STREAM_SINK_WORDS, dtype=torch.int32, device=src.device)
+    _check(lib().sa_read_stream(_ptr(src), n, _ptr(sink), _stream(src)), "sa_read_stream")
+    return sink
 
 
 def nm_act_spmm(xval: torch.Tensor, mask: torch.Tensor, n: int, m: int, wt: torch.Tensor,

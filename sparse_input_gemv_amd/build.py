@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_act.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sparsify.hip", "gemv.hip", "calibrate.hip", "gemm.hip", "abi.cpp", "validate.cpp"]
+SOURCES = ["sparsify.hip", "gemv.hip", "calibrate.hip", "gemm.hip", "stream.hip", "abi.cpp",
+           "validate.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include")]
 DEVICE = ["-x", "hip", "--offload-arch=gfx950",

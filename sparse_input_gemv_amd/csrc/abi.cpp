@@ -228,6 +228,22 @@ int weight_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* ou
                     "weight_col_norms");
 }
 
+static_assert(SA_READ_STREAM_SINK_WORDS == sa::kReadStreamBlocks * sa::kReadStreamThreads / 64,
+              "one sink word per wave of the read-stream grid");
+
+int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  sa::clear_error();
+  if (src == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(src) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) {
+    sa::set_error("sa_read_stream: src and sink must be non-NULL and aligned, bytes a positive "
+                  "multiple of 16");
+    return SA_ERR_INVALID_ARG;
+  }
+  return hip_status(sa::launch_read_stream(src, bytes, sink, as_stream(stream)),
+                    "sa_read_stream");
+}
+
 size_t sa_nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m) {
   if (T < 1 || d_in < 1 || m < 1 || n < 1 || n > m) return 0;
   return sa::nm_spmm_workspace_bytes(T, d_in, n, m);

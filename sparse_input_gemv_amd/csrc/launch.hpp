@@ -74,6 +74,11 @@ hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, dou
 int gemv_set_tuning(int tiling, int target_wgs, int handoff);
 int gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll);
 
+// ---- read-stream calibration (stream.hip) -----------------------------------
+constexpr int kReadStreamBlocks = 2048;  // measured best grid for a 45 MB read
+constexpr int kReadStreamThreads = 256;
+hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+
 // ---- MFMA matmuls (gemm.hip) ------------------------------------------------
 hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
                              int64_t d_out, uint16_t* y, hipStream_t s);

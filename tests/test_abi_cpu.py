@@ -155,6 +155,15 @@ def test_matmul_checks(sa):
     assert g(P, 0, 1024, P, 1024, P, None) == SA_OK
 
 
+def test_read_stream_checks(sa):
+    f = sa.sa_read_stream
+    assert f(None, 16, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 0, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 24, P, None) == SA_ERR_INVALID_ARG
+    assert f(P + 8, 16, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 16, None, None) == SA_ERR_INVALID_ARG
+
+
 def test_tiling_info(sa):
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     assert sa.sa_gemv_tiling_info(0, ctypes.addressof(a), ctypes.addressof(b),

@@ -540,3 +540,21 @@ def test_nm_spmm_full_shapes_sampled(T, d_in, d_out, n, m):
     ref = spmm.nm_spmm(X[rows], keep, wt)
     assert_close(Y[torch.from_numpy(rows).to(DEV)], ref)
     assert_close(Yd[torch.from_numpy(rows).to(DEV)], X[rows].astype(np.float64) @ wt.astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# roofline calibration kernel
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nbytes", [16, 1 << 20, 45_020_672, (1 << 25) + 48])
+def test_read_stream_reads_every_byte_once(nbytes):
+    """The xor of the sink words equals the xor of every 32-bit word read:
+    each 16-byte chunk is loaded exactly once, and nothing past nbytes."""
+    words = nbytes // 4 + 64
+    a = np.random.default_rng(nbytes % 997).integers(-2**31, 2**31 - 1, size=words,
+                                                     dtype=np.int64).astype(np.int32)
+    src = torch.from_numpy(a).to(DEV)
+    sink = sa.read_stream(src, nbytes)
+    got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
+    want = np.bitwise_xor.reduce(a[: nbytes // 4].view(np.uint32))
+    assert got == want
