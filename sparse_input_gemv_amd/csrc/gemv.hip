@@ -40,6 +40,8 @@
 // concurrently running workgroups of one slice read the same weight rows.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "validate.hpp"
@@ -73,10 +75,11 @@ constexpr int kDefaultFullK = 8;
 // words); the other modes take any slice length.
 constexpr int kSwigluSliceAlign = 64;
 constexpr int kMaxGk = 256;     // input slices per output tile
-// default split-K grid, in workgroups per CU (measured best: 3 for the
-// sparse modes, 4 for the dense baseline)
-constexpr int kWgsPerCu = 3;
-constexpr int kWgsPerCuDense = 4;
+// default split-K grid: about one workgroup per 64 KB a CU streams, 2 to 4
+// workgroups per CU (measured)
+constexpr double kBytesPerWorkgroup = 65536.0;
+constexpr int kMinWgsPerCu = 2;
+constexpr int kMaxWgsPerCu = 4;
 constexpr bool kDefaultOneLaunch = true;
 constexpr int kReduceGroups = 16;  // slice groups of the final sum (both hand-offs)
 constexpr size_t kTicketBytes = kGemvTicketBytes;
@@ -819,17 +822,89 @@ int device_cus() {
   return cache[dev];
 }
 
-// Split-K grid.  Streaming runs at a per-CU rate, so the call ends when the
-// most loaded CU does: the default grid is kWgsPerCu workgroups per CU with
-// equal slices (go * gk a multiple of the CU count whenever the output
-// tiles allow), every one resident at once.
-Plan make_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
+// The split-K kernel instance for a mode, tiling and batch (split-K tilings
+// exist for batch 1 of the hot modes; everything else uses tiling 0).
+using KFn = void (*)(KParams);
+
+template <int MODE, int B>
+KFn kernel_tiling(int tiling) {
+  if constexpr (B == 1 && (MODE == kModeThreshold || MODE == kModeDense || MODE == kModeList)) {
+    switch (tiling) {
+      case 1: return k_gemv<MODE, 256, 256, 8, B>;
+      case 2: return k_gemv<MODE, 256, 512, 8, B>;
+      case 3: return k_gemv<MODE, 128, 512, 8, B>;
+      case 4: return k_gemv<MODE, 512, 256, 8, B>;
+      case 5: return k_gemv<MODE, 128, 256, 16, B>;
+      case 6: return k_gemv<MODE, 64, 256, 8, B>;
+      case 7: return k_gemv<MODE, 256, 256, 4, B>;
+      default: return k_gemv<MODE, 128, 256, 8, B>;
+    }
+  } else {
+    (void)tiling;
+    return k_gemv<MODE, 128, 256, 8, B>;
+  }
+}
+
+template <int MODE>
+KFn kernel_batch(int tiling, int B) {
+  switch (B) {
+    case 1: return kernel_tiling<MODE, 1>(tiling);
+    case 2: return kernel_tiling<MODE, 2>(tiling);
+    case 4: return kernel_tiling<MODE, 4>(tiling);
+    default: return kernel_tiling<MODE, 8>(tiling);
+  }
+}
+
+KFn select_kernel(int mode, int tiling, int B) {
+  switch (mode) {
+    case kModeThreshold: return kernel_batch<kModeThreshold>(tiling, B);
+    case kModeDense: return kernel_batch<kModeDense>(tiling, B);
+    case kModeMasked: return kernel_batch<kModeMasked>(tiling, B);
+    case kModeList: return kernel_tiling<kModeList, 1>(tiling);
+    case kModeListBatched: return kernel_batch<kModeListBatched>(tiling, B);
+    case kModeSwiglu: return kernel_tiling<kModeSwiglu, 1>(tiling);
+    default: return nullptr;
+  }
+}
+
+// Workgroups of `fn` that fit on one CU at once (cached).
+int resident_per_cu(KFn fn, int nt, size_t smem) {
+  static std::mutex mu;
+  static struct {
+    KFn fn;
+    int nt;
+    size_t smem;
+    int dev, occ;
+  } cache[32];
+  static int next = 0;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : cache)
+    if (e.fn == fn && e.nt == nt && e.smem == smem && e.dev == dev) return e.occ;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(fn), nt,
+                                                   smem) != hipSuccess ||
+      occ < 1)
+    occ = 1;
+  cache[next] = {fn, nt, smem, dev, occ};
+  next = (next + 1) % 32;
+  return occ;
+}
+
+// Split-K grid.  Streaming runs at a per-CU rate and the call ends when the
+// most loaded CU does; each further workgroup on a CU adds fixed cost
+// (x load, compaction, hand-off) of its own.  Measured over slice counts on
+// this part, the best grids put k workgroups on every CU (or just under it),
+// with k growing with the bytes a CU streams: about one workgroup per 64 KB,
+// at least 2 and at most 4.  The bytes are estimated before the call (the
+// sparse modes at half the weight), and no grid exceeds what is resident at
+// once (a workgroup waiting for a free slot would start only after the
+// others finish).
+Plan plan_for(int mode, int tiling, int64_t d_out, int64_t d_in, int B, int64_t gk_req) {
   Plan pl;
   const Tiling T = kTilings[tiling];
   pl.go = (int)((d_out + T.tile_o - 1) / T.tile_o);
-  const int per_cu = mode == kModeDense ? kWgsPerCuDense : kWgsPerCu;
-  const int64_t target = g_target_wgs > 0 ? g_target_wgs : (int64_t)per_cu * device_cus();
-  int64_t gk_req = (target + pl.go / 2) / pl.go;
   if (gk_req < 1) gk_req = 1;
   if (gk_req > kMaxGk) gk_req = kMaxGk;
   const int64_t align = mode == kModeSwiglu ? kSwigluSliceAlign : 1;
@@ -849,40 +924,59 @@ Plan make_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
   return pl;
 }
 
-template <int MODE, int TO, int NT, int U, int B>
-hipError_t launch_one(const KParams& kp, const Plan& pl, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv<MODE, TO, NT, U, B>), dim3((unsigned)(pl.go * pl.gk)), dim3(NT),
-                     pl.smem, s, kp);
-  return hipGetLastError();
+Plan choose_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
+  const int nt = kTilings[tiling].threads;
+  const int64_t go = (d_out + kTilings[tiling].tile_o - 1) / kTilings[tiling].tile_o;
+  if (g_target_wgs > 0)  // tuning: the grid asked for
+    return plan_for(mode, tiling, d_out, d_in, B, (g_target_wgs + go / 2) / go);
+  const int64_t cus = device_cus();
+  const double bytes = 2.0 * (double)d_in * (double)d_out * (mode == kModeDense ? 1.0 : 0.5);
+  int64_t k = (int64_t)(bytes / (double)cus / kBytesPerWorkgroup + 0.5);
+  k = k < kMinWgsPerCu ? kMinWgsPerCu : (k > kMaxWgsPerCu ? kMaxWgsPerCu : k);
+  const KFn fn = select_kernel(mode, tiling, B);
+  Plan pl = plan_for(mode, tiling, d_out, d_in, B, (k * cus) / go);
+  // at most one resident wave of workgroups
+  for (int i = 0; i < 4 && pl.gk > 1; ++i) {
+    const int64_t cap = (int64_t)resident_per_cu(fn, nt, pl.smem) * cus;
+    if ((int64_t)pl.go * pl.gk <= cap) break;
+    pl = plan_for(mode, tiling, d_out, d_in, B, cap / go);
+  }
+  return pl;
 }
 
-// Every split-K tiling for batch 1 of the hot modes; tiling 0 otherwise.
-template <int MODE, int B>
-hipError_t dispatch_tiling(const KParams& kp, const Plan& pl, int tiling, hipStream_t s) {
-  if constexpr (B == 1 && (MODE == kModeThreshold || MODE == kModeDense || MODE == kModeList)) {
-    switch (tiling) {
-      case 1: return launch_one<MODE, 256, 256, 8, B>(kp, pl, s);
-      case 2: return launch_one<MODE, 256, 512, 8, B>(kp, pl, s);
-      case 3: return launch_one<MODE, 128, 512, 8, B>(kp, pl, s);
-      case 4: return launch_one<MODE, 512, 256, 8, B>(kp, pl, s);
-      case 5: return launch_one<MODE, 128, 256, 16, B>(kp, pl, s);
-      case 6: return launch_one<MODE, 64, 256, 8, B>(kp, pl, s);
-      case 7: return launch_one<MODE, 256, 256, 4, B>(kp, pl, s);
-      default: return launch_one<MODE, 128, 256, 8, B>(kp, pl, s);
-    }
-  } else {
-    return launch_one<MODE, 128, 256, 8, B>(kp, pl, s);
+// Plans are cached per call shape, so a steady stream of calls pays one
+// lookup on the host.
+Plan make_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
+  static std::mutex mu;
+  struct Entry {
+    int mode, tiling, B, target, dev;
+    int64_t d_out, d_in;
+    Plan pl;
+    bool used;
+  };
+  static Entry cache[64];
+  static int next = 0;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& e : cache)
+      if (e.used && e.mode == mode && e.tiling == tiling && e.B == B && e.d_out == d_out &&
+          e.d_in == d_in && e.target == g_target_wgs && e.dev == dev)
+        return e.pl;
   }
+  const Plan pl = choose_plan(mode, tiling, d_out, d_in, B);
+  std::lock_guard<std::mutex> lock(mu);
+  cache[next] = {mode, tiling, B, g_target_wgs, dev, d_out, d_in, pl, true};
+  next = (next + 1) % 64;
+  return pl;
 }
 
-template <int MODE>
-hipError_t dispatch_batch(const KParams& kp, const Plan& pl, int tiling, int B, hipStream_t s) {
-  switch (B) {
-    case 1: return dispatch_tiling<MODE, 1>(kp, pl, tiling, s);
-    case 2: return dispatch_tiling<MODE, 2>(kp, pl, tiling, s);
-    case 4: return dispatch_tiling<MODE, 4>(kp, pl, tiling, s);
-    default: return dispatch_tiling<MODE, 8>(kp, pl, tiling, s);
-  }
+hipError_t launch_split(KFn fn, int nt, const KParams& kp, const Plan& pl, hipStream_t s) {
+  KParams arg = kp;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)(pl.go * pl.gk)),
+                         dim3(nt), args, pl.smem, s);
 }
 
 hipError_t launch_reduce(const KParams& kp, const Plan& pl, int B, bool with_nnz, hipStream_t s) {
@@ -994,22 +1088,18 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   unsigned char* ws = static_cast<unsigned char*>(c.ws);
   kp.slice_cnt = ws ? reinterpret_cast<int32_t*>(ws + L.slicecnt_off) : nullptr;
   kp.part = ws ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
-  const bool one_launch = pl.gk > 1 && (g_handoff == 0 ? kDefaultOneLaunch : g_handoff == 2);
+  // one launch for batch 1 and 2; at batch 4 and 8 the last workgroup's sum
+  // over B rows costs more than a second launch (measured)
+  const bool one_launch =
+      pl.gk > 1 && (g_handoff == 0 ? (kDefaultOneLaunch && B <= 2) : g_handoff == 2);
   kp.tickets = one_launch ? reinterpret_cast<uint32_t*>(ws + L.ticket_off) : nullptr;
   kp.go = pl.go;
   kp.gk = pl.gk;
   kp.slice = pl.slice;
 
-  hipError_t e;
-  switch (mode) {
-    case kModeThreshold: e = dispatch_batch<kModeThreshold>(kp, pl, tiling, B, s); break;
-    case kModeDense: e = dispatch_batch<kModeDense>(kp, pl, tiling, B, s); break;
-    case kModeMasked: e = dispatch_batch<kModeMasked>(kp, pl, tiling, B, s); break;
-    case kModeList: e = dispatch_tiling<kModeList, 1>(kp, pl, tiling, s); break;
-    case kModeListBatched: e = dispatch_batch<kModeListBatched>(kp, pl, tiling, B, s); break;
-    case kModeSwiglu: e = dispatch_tiling<kModeSwiglu, 1>(kp, pl, tiling, s); break;
-    default: return hipErrorInvalidValue;
-  }
+  const KFn fn = select_kernel(mode, tiling, B);
+  if (fn == nullptr) return hipErrorInvalidValue;
+  const hipError_t e = launch_split(fn, kTilings[tiling].threads, kp, pl, s);
   if (e != hipSuccess || pl.gk == 1 || one_launch) return e;
   return launch_reduce(kp, pl, B, mode == kModeSwiglu && c.out_nnz != nullptr, s);
 }
