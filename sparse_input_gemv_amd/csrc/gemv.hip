@@ -282,6 +282,12 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   const int SL = p.slice;
   int* lk = reinterpret_cast<int*>(smem);
   float* lv = reinterpret_cast<float*>(smem + (size_t)SL * 4);
+  // Batch > 1: the values are the activations' fp16 bits, [B][SLH] with SLH
+  // even and > SL, so two consecutive kept entries are one 32-bit read; a
+  // zero after the last kept entry pairs an odd count.
+  constexpr bool kPairs = B > 1;
+  const int SLH = (SL + 2) & ~1;
+  uint16_t* lvh = reinterpret_cast<uint16_t*>(smem + (size_t)SL * 4);
 
   // ---------------- phase 1: kept rows of this workgroup -> LDS ----------
   int cnt = 0;
@@ -305,12 +311,12 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     const int64_t k0 = (int64_t)kblk * SL;
     const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
     const int span = (int)(k1 - k0);
-    int* flag = reinterpret_cast<int*>(smem + (size_t)SL * 4 * (1 + B));
-    float* dv = reinterpret_cast<float*>(smem + (size_t)SL * 4 * (2 + B));
+    int* flag = reinterpret_cast<int*>(smem + (size_t)SL * 4 + (size_t)B * SLH * 2);
+    uint16_t* dv = reinterpret_cast<uint16_t*>(smem + (size_t)SL * 8 + (size_t)B * SLH * 2);
     for (int j = tid; j < SL; j += NT) {
       flag[j] = 0;
 #pragma unroll
-      for (int b = 0; b < B; ++b) dv[b * SL + j] = 0.f;
+      for (int b = 0; b < B; ++b) dv[b * SL + j] = 0;
     }
     __syncthreads();
     const int w = tid / kWave;
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         const int64_t kk = ib[q];
         if (kk >= k0 && kk < k1) {
           flag[kk - k0] = 1;
-          dv[b * SL + (kk - k0)] = h2f(vb[q]);
+          dv[b * SL + (kk - k0)] = vb[q];
         }
       }
     }
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       if (keep) {
         lk[cnt + slot] = (int)(k0 + j);
 #pragma unroll
-        for (int b = 0; b < B; ++b) lv[b * SL + cnt + slot] = dv[b * SL + j];
+        for (int b = 0; b < B; ++b) lvh[b * SLH + cnt + slot] = dv[b * SL + j];
       }
       cnt += total;
     }
@@ -353,26 +359,42 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       const int64_t k = c + tid;
       const bool in = k < k1;
       float vb[B];
+      uint16_t hb[B];  // fp16 bits of kept values (0 otherwise), batch > 1
       bool any = false;
       if constexpr (MODE == kModeSwiglu) {
         float hv = 0.f;
         any = in && swiglu_keep(p.g[k], p.u[k], p.colnorm, k, p.swiglu_mode, p.t64, hv);
         vb[0] = hv;
       } else {
+        // every row's load first, from in-range addresses (k0 < d_in), so
+        // they are in flight together; then the decisions
+        const int64_t kc = in ? k : k0;
+        uint16_t xr[B];
+        uint32_t mw[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const int64_t bb = b < p.batch ? b : 0;
+          xr[b] = p.x[bb * p.d_in + kc];
+          if constexpr (MODE == kModeMasked) mw[b] = p.xmask[bb * words + (kc >> 5)];
+        }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           vb[b] = 0.f;
+          hb[b] = 0;
           if (b < p.batch && in) {
-            const uint16_t xb = p.x[(int64_t)b * p.d_in + k];
+            const uint16_t xb = xr[b];
             bool kb;
             if constexpr (MODE == kModeThreshold) {
               kb = mag_key(xb) != 0 && fabsf(h2f(xb)) >= p.t;
             } else if constexpr (MODE == kModeMasked) {
-              kb = ((p.xmask[(int64_t)b * words + (k >> 5)] >> (k & 31)) & 1u) != 0;
+              kb = ((mw[b] >> (k & 31)) & 1u) != 0;
             } else {
               kb = true;
             }
-            if (kb) vb[b] = h2f(xb);
+            if (kb) {
+              vb[b] = h2f(xb);
+              hb[b] = xb;
+            }
             any = any || kb;
           }
         }
@@ -383,8 +405,12 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       const int slot = chunk_slot<NT>(any, wsum, total, wm);
       if (any) {
         lk[cnt + slot] = (int)k;
+        if constexpr (kPairs) {
 #pragma unroll
-        for (int b = 0; b < B; ++b) lv[b * SL + cnt + slot] = vb[b];
+          for (int b = 0; b < B; ++b) lvh[b * SLH + cnt + slot] = hb[b];
+        } else {
+          lv[cnt + slot] = vb[0];
+        }
       }
       if constexpr (MODE == kModeSwiglu) {
         // each wave covers 64 consecutive entries starting at a multiple of 64
@@ -410,6 +436,11 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     __syncthreads();
   }
 
+  if constexpr (kPairs) {
+    if (tid < B) lvh[tid * SLH + cnt] = 0;  // the pad after the last kept entry
+    __syncthreads();
+  }
+
   // ---------------- phase 2: stream the kept rows --------------------------
   const int o_lane = tid % OL;
   const int r_lane = tid / OL;
@@ -425,44 +456,94 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
 
-  // Rows j = r_lane, r_lane + R, ... in two halves of H rows: one half's
-  // loads stay in flight while the other half is consumed.  Rows are added
-  // in increasing j whatever U is.  Loads are unconditional (a branch per
-  // load would make every wait a full drain): past the end of the list a
-  // thread re-reads the list's last row, a cache hit, and consume() skips it.
-  constexpr int H = U / 2;
-  static_assert(U % 2 == 0, "two halves");
-  auto issue = [&](half8 (&w)[H], int j0) {
-#pragma unroll
-    for (int q = 0; q < H; ++q) {
-      const int j = j0 + q * R;
-      const int row = lk[j < cnt ? j : cnt - 1];
-      w[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)row * ld);
-    }
-  };
-  auto consume = [&](const half8 (&w)[H], int j0) {
-#pragma unroll
-    for (int q = 0; q < H; ++q) {
-      const int j = j0 + q * R;
-      if (j < cnt) {
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const float vv = lv[b * SL + j];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[b][i] = fmaf((float)w[q][i], vv, acc[b][i]);
+  if constexpr (!kPairs) {
+    // Rows j = r_lane, r_lane + R, ... in two halves of H rows: one half's
+    // loads stay in flight while the other half is consumed.  Rows are added
+    // in increasing j whatever U is.  Loads are unconditional (a branch per
+    // load would make every wait a full drain): past the end of the list a
+    // thread re-reads the list's last row, a cache hit, and consume() skips it.
+    constexpr int H = U / 2;
+    static_assert(U % 2 == 0, "two halves");
+    auto issue = [&](half8 (&w)[H], int j0) {
+  #pragma unroll
+      for (int q = 0; q < H; ++q) {
+        const int j = j0 + q * R;
+        const int row = lk[j < cnt ? j : cnt - 1];
+        w[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)row * ld);
+      }
+    };
+    auto consume = [&](const half8 (&w)[H], int j0) {
+  #pragma unroll
+      for (int q = 0; q < H; ++q) {
+        const int j = j0 + q * R;
+        if (j < cnt) {
+  #pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const float vv = lv[b * SL + j];
+  #pragma unroll
+            for (int i = 0; i < 8; ++i) acc[b][i] = fmaf((float)w[q][i], vv, acc[b][i]);
+          }
         }
       }
+    };
+    if (r_lane < cnt) {
+      half8 wa[H], wb[H];
+      issue(wa, r_lane);
+      issue(wb, r_lane + H * R);
+      for (int j0 = r_lane; j0 < cnt; j0 += U * R) {
+        consume(wa, j0);
+        issue(wa, j0 + U * R);
+        consume(wb, j0 + H * R);
+        issue(wb, j0 + U * R + H * R);
+      }
     }
-  };
-  if (r_lane < cnt) {
-    half8 wa[H], wb[H];
-    issue(wa, r_lane);
-    issue(wb, r_lane + H * R);
-    for (int j0 = r_lane; j0 < cnt; j0 += U * R) {
-      consume(wa, j0);
-      issue(wa, j0 + U * R);
-      consume(wb, j0 + H * R);
-      issue(wb, j0 + U * R + H * R);
+  } else {
+    // Batch > 1: kept entries in pairs (2m, 2m+1), m = r_lane, r_lane + R,
+    // ...; v_dot2_f32_f16 adds both rows' products for one output and batch
+    // row in one instruction (fp32 accumulate), half the VALU work of one
+    // FMA per row.  An odd count pairs its last entry with the zero pad (the
+    // row is read twice, its second value is 0).  Same halves as above.
+    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+    const int npair = (cnt + 1) >> 1;
+    constexpr int HP = U / 4;  // pairs per half: U rows in flight
+    static_assert(U % 4 == 0, "two halves of pairs");
+    auto issue2 = [&](half8 (&wa)[HP], half8 (&wb)[HP], int m0) {
+#pragma unroll
+      for (int q = 0; q < HP; ++q) {
+        const int m = m0 + q * R;
+        const int mm = m < npair ? m : npair - 1;
+        const int ja = 2 * mm, jb = 2 * mm + 1 < cnt ? 2 * mm + 1 : 2 * mm;
+        wa[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)lk[ja] * ld);
+        wb[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)lk[jb] * ld);
+      }
+    };
+    auto consume2 = [&](const half8 (&wa)[HP], const half8 (&wb)[HP], int m0) {
+#pragma unroll
+      for (int q = 0; q < HP; ++q) {
+        const int m = m0 + q * R;
+        if (m < npair) {
+          h2v wp[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wp[i] = h2v{wa[q][i], wb[q][i]};
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const h2v xp = *reinterpret_cast<const h2v*>(lvh + b * SLH + 2 * m);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[b][i] = __builtin_amdgcn_fdot2(wp[i], xp, acc[b][i], false);
+          }
+        }
+      }
+    };
+    if (r_lane < npair) {
+      half8 a0[HP], b0[HP], a1[HP], b1[HP];
+      issue2(a0, b0, r_lane);
+      issue2(a1, b1, r_lane + HP * R);
+      for (int m0 = r_lane; m0 < npair; m0 += 2 * HP * R) {
+        consume2(a0, b0, m0);
+        issue2(a0, b0, m0 + 2 * HP * R);
+        consume2(a1, b1, m0 + HP * R);
+        issue2(a1, b1, m0 + 2 * HP * R + HP * R);
+      }
     }
   }
 
@@ -796,9 +877,12 @@ Layout ws_layout(int64_t d_out, int64_t d_in, int64_t batch) {
   return L;
 }
 
+// LDS of the kept list: indices, then values (fp32 at batch 1; fp16 [B][SLH]
+// at batch > 1), then for batched lists the dense staging (flags, fp16).
 size_t list_lds_bytes(int mode, int slice, int B) {
-  size_t b = (size_t)slice * 4 * (1 + B);
-  if (mode == kModeListBatched) b += (size_t)slice * 4 * (1 + B);
+  const size_t slh = (size_t)((slice + 2) & ~1);
+  size_t b = (size_t)slice * 4 + (B > 1 ? (size_t)B * slh * 2 : (size_t)slice * 4);
+  if (mode == kModeListBatched) b += (size_t)slice * 4 + (size_t)B * slice * 2;
   return b;
 }
 
