@@ -15,7 +15,11 @@
 //            ballot + mbcnt and an LDS scan of wave totals (ascending);
 //   phase 2  its threads stream the listed rows for the output tile with
 //            16-byte loads (8 fp16 per lane; a 128-output tile is one
-//            256-byte run per row), U rows in flight per thread, fp32 FMA;
+//            256-byte run per row), U rows in flight per thread, fp32 FMA.
+//            The loads carry the non-temporal hint: each weight byte is
+//            read once per call, and streaming it through L2 at normal
+//            priority would evict x, the partial tiles and the counters
+//            (measured: 13.0 -> 12.3 us on the 4096 x 11008 call);
 //   phase 3  row lanes are summed in LDS and the fp32 partial tile is
 //            stored.
 // The partial tiles are then summed over slices, in slice order, into fp16 y
@@ -119,6 +123,11 @@ struct KParams {
 };
 
 constexpr int kModeListBatched = 5;  // kModeList with batch > 1
+
+// Chunks of x a workgroup loads before deciding (one-pass phase 1); longer
+// slices, and batch 8 (whose registers are full), take the chunk loop.
+template <int B>
+constexpr int kOnePassChunks = B == 1 ? 4 : (B <= 4 ? 2 : 0);
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
@@ -291,6 +300,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
 
   // ---------------- phase 1: kept rows of this workgroup -> LDS ----------
   int cnt = 0;
+  const int64_t slice_k0 = (int64_t)kblk * SL;
+  const int64_t slice_span = (slice_k0 + SL < p.d_in ? slice_k0 + SL : p.d_in) - slice_k0;
   if constexpr (MODE == kModeList) {
     int64_t nn = p.nnz[0];
     const int64_t lim = p.cap < p.d_in ? p.cap : p.d_in;
@@ -349,6 +360,86 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         for (int b = 0; b < B; ++b) lvh[b * SLH + cnt + slot] = dv[b * SL + j];
       }
       cnt += total;
+    }
+    __syncthreads();
+  } else if (kOnePassChunks<B> > 0 && MODE != kModeSwiglu &&
+             slice_span <= (int64_t)kOnePassChunks<B> * NT) {
+    // One pass: every chunk's x (and mask word) loads are issued before any
+    // decision, so the slice costs one memory round trip; the kept slots of
+    // all chunks come from one table of per-chunk, per-wave ballot counts
+    // (one barrier).  Entry k0 + c*NT + tid of chunk c; chunk-major order
+    // keeps the list ascending.
+    constexpr int PC = kOnePassChunks<B> > 0 ? kOnePassChunks<B> : 1;
+    constexpr int NW = NT / kWave;
+    __shared__ int wtab[PC * NW];
+    const int64_t k0 = (int64_t)kblk * SL;
+    const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
+    const int64_t words = (p.d_in + 31) >> 5;
+    const int nch = (int)((slice_span + NT - 1) / NT);  // chunks this slice has
+    uint16_t xr[PC][B];
+    uint32_t mw[PC][B];
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+      if (c > 0 && c >= nch) break;
+      const int64_t k = k0 + (int64_t)c * NT + tid;
+      const int64_t kc = k < k1 ? k : k0;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int64_t bb = b < p.batch ? b : 0;
+        xr[c][b] = p.x[bb * p.d_in + kc];
+        if constexpr (MODE == kModeMasked) mw[c][b] = p.xmask[bb * words + (kc >> 5)];
+      }
+    }
+    const int w = tid / kWave;
+    bool keep[PC];
+    uint64_t bm[PC];
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+      if (c > 0 && c >= nch) break;
+      const int64_t k = k0 + (int64_t)c * NT + tid;
+      bool any = false;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const uint16_t xb = xr[c][b];
+        bool kb = false;
+        if (b < p.batch && k < k1) {
+          if constexpr (MODE == kModeThreshold) {
+            kb = mag_key(xb) != 0 && fabsf(h2f(xb)) >= p.t;
+          } else if constexpr (MODE == kModeMasked) {
+            kb = ((mw[c][b] >> (k & 31)) & 1u) != 0;
+          } else {
+            kb = true;
+          }
+        }
+        if (!kb) xr[c][b] = 0;  // what a skipped entry (or absent row) contributes
+        any = any || kb;
+      }
+      keep[c] = any;
+      bm[c] = __ballot(any);
+      if (lane_id() == 0) wtab[c * NW + w] = (int)__popcll(bm[c]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+      if (c > 0 && c >= nch) break;
+      int before = 0, tot = 0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const int v = wtab[c * NW + i];
+        before += (i < w) ? v : 0;
+        tot += v;
+      }
+      if (keep[c]) {
+        const int slot = cnt + before + lanes_below(bm[c]);
+        lk[slot] = (int)(k0 + (int64_t)c * NT + tid);
+        if constexpr (kPairs) {
+#pragma unroll
+          for (int b = 0; b < B; ++b) lvh[b * SLH + slot] = xr[c][b];
+        } else {
+          lv[slot] = h2f(xr[c][0]);
+        }
+      }
+      cnt += tot;
     }
     __syncthreads();
   } else {
@@ -469,7 +560,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       for (int q = 0; q < H; ++q) {
         const int j = j0 + q * R;
         const int row = lk[j < cnt ? j : cnt - 1];
-        w[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)row * ld);
+        w[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + (int64_t)row * ld));
       }
     };
     auto consume = [&](const half8 (&w)[H], int j0) {
@@ -513,8 +604,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         const int m = m0 + q * R;
         const int mm = m < npair ? m : npair - 1;
         const int ja = 2 * mm, jb = 2 * mm + 1 < cnt ? 2 * mm + 1 : 2 * mm;
-        wa[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)lk[ja] * ld);
-        wb[q] = *reinterpret_cast<const half8*>(wcol + (int64_t)lk[jb] * ld);
+        wa[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + (int64_t)lk[ja] * ld));
+        wb[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + (int64_t)lk[jb] * ld));
       }
     };
     auto consume2 = [&](const half8 (&wa)[HP], const half8 (&wb)[HP], int m0) {
@@ -770,7 +861,7 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
 #pragma unroll
     for (int q = 0; q < U; ++q) {
       if (keep[q] && o_ok) {
-        w[q] = *reinterpret_cast<const half8*>(wcol + row[q] * ld);
+        w[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + row[q] * ld));
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) w[q][i] = (half_t)0.f;

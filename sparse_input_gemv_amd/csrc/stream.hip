@@ -1,8 +1,10 @@
 // Read-stream calibration kernel: the achievable HBM read rate of this GPU,
 // reported beside the 8 TB/s nominal peak so that the GEMV kernels' roofline
 // fractions can be read against both.  Every byte of the buffer is read once
-// with 16-byte loads, grid-stride; each wave folds what it read into one
-// word (xor) so the loads cannot be dropped.
+// with 16-byte non-temporal loads (the hint the GEMV's weight stream uses;
+// measured faster than plain loads, and than unrolled grid-stride loads),
+// grid-stride; each wave folds what it read into one word (xor) so the loads
+// cannot be dropped.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -15,7 +17,7 @@ __global__ __launch_bounds__(kReadStreamThreads) void k_read_stream(const u32x4*
   uint32_t acc = 0;
   const int64_t stride = (int64_t)gridDim.x * kReadStreamThreads;
   for (int64_t i = (int64_t)blockIdx.x * kReadStreamThreads + threadIdx.x; i < n16; i += stride) {
-    const u32x4 v = src[i];
+    const u32x4 v = __builtin_nontemporal_load(src + i);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
 #pragma unroll
