@@ -339,19 +339,24 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined engine (dense and 2:4 A, d_in a multiple of 64, 16-byte aligned
-// rows).  A 256-thread workgroup computes a 256 x 128 output tile, four
-// waves of 128 x 64; the K loop steps by 64 through three LDS stages.
+// Pipelined engine (dense and 2:4 A, d_in a multiple of the kind's K step,
+// 16-byte aligned rows).  A 256-thread workgroup computes a 256 x 128 output
+// tile, four waves of 128 x 64; the K loop steps through three LDS stages.
 // Tiles go from global memory to LDS with direct loads (global_load_lds:
 // lane l's bytes land at the instruction's LDS base + size * l), two K steps
 // ahead, so no registers hold staged data and the loads of step t+2 overlap
 // the MFMAs of step t.
-//   A, dense: X rows, K-contiguous, stored [m][64] with 16-byte chunks
+//   Dense: K steps of 32 (72 KB of LDS), so two workgroups share a CU and
+//     one's barrier and load waits are covered by the other's MFMAs
+//     (measured 8% faster than steps of 64 with one workgroup per CU).
+//     X rows, K-contiguous, are stored [m][32] with 16-byte chunks
 //     XOR-swizzled by the row (chosen through each lane's source address) so
 //     the 32 rows one operand read touches fall in distinct banks.
-//   A, 2:4: the compressed values, [m][32] (swizzled the same way for
-//     64-byte rows), and the row's two 32-bit mask words [m][2]; each lane
-//     turns its 16 mask bits into the position code of the sparse MFMA.
+//   2:4: K steps of 64, one workgroup per CU (steps of 32 leave too few
+//     sparse MFMAs per barrier: measured slower).  The compressed values,
+//     [m][32] (64-byte rows, swizzled as the dense A), and the row's two
+//     32-bit mask words [m][2]; each lane turns its 16 mask bits into the
+//     position code of the sparse MFMA.
 //   B (WT, N-contiguous) is stored [k][128] as it lies in memory (chunks
 //     swizzled by k); the MFMA B operand -- consecutive k of one column --
 //     comes from LDS transpose reads (ds_read_b64_tr_b16): within a 16-lane
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
 // The MFMA sequence per output block is the staged-register engine's, so
 // both engines give identical results.
 // ---------------------------------------------------------------------------
-constexpr int PBM = 256, PBN = 128, PBK = 64;
+constexpr int PBM = 256, PBN = 128;
 
 typedef short s4v __attribute__((ext_vector_type(4)));
 #define SA_LDS4(ptr) ((__attribute__((address_space(3))) s4v*)(ptr))
@@ -372,26 +377,29 @@ template <int AK>
 struct Pipe;
 template <>
 struct Pipe<kADense> {
-  static constexpr int kAHalves = PBM * PBK;  // [256][64]
+  static constexpr int kBK = 32;                  // K step
+  static constexpr int kAHalves = PBM * kBK;      // [256][32]
   static constexpr int kMaskWords = 0;
-  static constexpr int kLoadsPerWave = 8 + 4;  // A, B
+  static constexpr int kLoadsPerWave = 4 + 2;     // A, B
+  static constexpr int kWgsPerCu = 2;
 };
 template <>
 struct Pipe<kA24> {
-  static constexpr int kAHalves = PBM * PBK / 2;  // [256][32] compressed
+  static constexpr int kBK = 64;
+  static constexpr int kAHalves = PBM * kBK / 2;  // [256][32] compressed
   static constexpr int kMaskWords = PBM * 2;      // [256][2]
   static constexpr int kLoadsPerWave = 4 + 4 + 2;  // A, B, mask
+  static constexpr int kWgsPerCu = 1;
 };
 template <int AK>
 constexpr int pipe_stage_halves() {
-  return Pipe<AK>::kAHalves + PBK * PBN + 2 * Pipe<AK>::kMaskWords;
+  return Pipe<AK>::kAHalves + Pipe<AK>::kBK * PBN + 2 * Pipe<AK>::kMaskWords;
 }
 
-// 16-byte chunk swizzles: A rows of 128 bytes (dense), of 64 bytes (2:4),
-// B rows of 256 bytes.  Each spreads the rows one operand read touches over
-// distinct banks for 32 or 64 LDS banks.
-__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_a24(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// 16-byte chunk swizzles: A rows of 64 bytes (dense and 2:4), B rows of 256
+// bytes.  Each spreads the rows one operand read touches over distinct banks
+// for 32 or 64 LDS banks.
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
 
 // s_waitcnt encoding (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt 6:4
@@ -447,15 +455,16 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   uint16_t* As = S;
   uint16_t* Bs = S + Pipe<AK>::kAHalves;
+  constexpr int BK = Pipe<AK>::kBK;
   if constexpr (AK == kADense) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rb = (w * 8 + i) * 8;  // 8 rows of 128 bytes per instruction
-      const int r = rb + lane / 8;
-      const int gc = (lane % 8) ^ swz_a(r);
+    for (int i = 0; i < 4; ++i) {
+      const int rb = (w * 4 + i) * 16;  // 16 rows of 64 bytes per instruction
+      const int r = rb + lane / 4;
+      const int gc = (lane % 4) ^ swz_a(r);
       int64_t row = m0 + r;
       if (row >= p.T) row = p.T - 1;
-      load_to_lds16(p.x + row * p.d_in + k0 + 8 * gc, As + rb * PBK);
+      load_to_lds16(p.x + row * p.d_in + k0 + 8 * gc, As + rb * BK);
     }
   } else {
     const int64_t kc = p.d_in / 2;  // compressed row length
@@ -463,12 +472,12 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
     for (int i = 0; i < 4; ++i) {
       const int rb = (w * 4 + i) * 16;  // 16 rows of 64 bytes per instruction
       const int r = rb + lane / 4;
-      const int gc = (lane % 4) ^ swz_a24(r);
+      const int gc = (lane % 4) ^ swz_a(r);
       int64_t row = m0 + r;
       if (row >= p.T) row = p.T - 1;
-      load_to_lds16(p.x + row * kc + k0 / 2 + 8 * gc, As + rb * (PBK / 2));
+      load_to_lds16(p.x + row * kc + k0 / 2 + 8 * gc, As + rb * (BK / 2));
     }
-    uint32_t* Ms = reinterpret_cast<uint32_t*>(Bs + PBK * PBN);
+    uint32_t* Ms = reinterpret_cast<uint32_t*>(Bs + BK * PBN);
     const int64_t words = p.d_in / 32;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -480,8 +489,8 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kb = (w * 4 + i) * 4;  // 4 k rows of 256 bytes per instruction
+  for (int i = 0; i < BK / 16; ++i) {
+    const int kb = (w * (BK / 16) + i) * 4;  // 4 k rows of 256 bytes per instruction
     const int k = kb + lane / 16;
     const int gc = (lane % 16) ^ swz_b(k);
     int64_t n = n0 + 8 * gc;
@@ -520,17 +529,18 @@ template <int AK>
 __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* code_lut,
                                              f16v (&acc)[4][2], int wm, int wn) {
   const int lane = lane_id();
+  constexpr int BK = Pipe<AK>::kBK;
   const uint16_t* As = S;
   const uint16_t* Bs = S + Pipe<AK>::kAHalves;
   if constexpr (AK == kADense) {
 #pragma unroll
-    for (int kk = 0; kk < PBK / 16; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       h8 aop[4], bop[2];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int m = wm * 128 + 32 * a + lane % 32;
         const int q = 2 * kk + lane / 32;
-        aop[a] = *reinterpret_cast<const h8*>(As + m * PBK + 8 * (q ^ swz_a(m)));
+        aop[a] = *reinterpret_cast<const h8*>(As + m * BK + 8 * (q ^ swz_a(m)));
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -547,9 +557,9 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* c
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[a], bop[b], acc[a][b], 0, 0, 0);
     }
   } else {
-    const uint32_t* Ms = reinterpret_cast<const uint32_t*>(Bs + PBK * PBN);
+    const uint32_t* Ms = reinterpret_cast<const uint32_t*>(Bs + BK * PBN);
 #pragma unroll
-    for (int kk = 0; kk < PBK / 32; ++kk) {
+    for (int kk = 0; kk < BK / 32; ++kk) {
       h8 aop[4];
       int code[4];
       h16 bop[2];
@@ -557,7 +567,7 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* c
       for (int a = 0; a < 4; ++a) {
         const int m = wm * 128 + 32 * a + lane % 32;
         const int q = 2 * kk + lane / 32;
-        aop[a] = *reinterpret_cast<const h8*>(As + m * (PBK / 2) + 8 * (q ^ swz_a24(m)));
+        aop[a] = *reinterpret_cast<const h8*>(As + m * (BK / 2) + 8 * (q ^ swz_a(m)));
         // position code of this lane's 16 mask bits, a byte at a time
         const uint32_t bits = Ms[m * 2 + kk] >> (16 * (lane / 32));
         code[a] = (int)code_lut[bits & 0xffu] | ((int)code_lut[(bits >> 8) & 0xffu] << 8);
@@ -592,19 +602,20 @@ __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_
                                             const uint8_t* code_lut, f16v (&acc)[4][2], int wm,
                                             int wn) {
   constexpr int LPW = Pipe<AK>::kLoadsPerWave;
-  const int64_t nk = p.d_in / PBK;
+  constexpr int BK = Pipe<AK>::kBK;
+  const int64_t nk = p.d_in / BK;
   pipe_issue<AK>(p, m0, n0, 0, S0);
-  if (nk > 1) pipe_issue<AK>(p, m0, n0, PBK, S1);
+  if (nk > 1) pipe_issue<AK>(p, m0, n0, BK, S1);
   int64_t kt = 0;
   for (; kt + 4 < nk; kt += 3) {
     stage_barrier<LPW>();
-    pipe_issue<AK>(p, m0, n0, (kt + 2) * PBK, S2);
+    pipe_issue<AK>(p, m0, n0, (kt + 2) * BK, S2);
     pipe_compute<AK>(S0, code_lut, acc, wm, wn);
     stage_barrier<LPW>();
-    pipe_issue<AK>(p, m0, n0, (kt + 3) * PBK, S0);
+    pipe_issue<AK>(p, m0, n0, (kt + 3) * BK, S0);
     pipe_compute<AK>(S1, code_lut, acc, wm, wn);
     stage_barrier<LPW>();
-    pipe_issue<AK>(p, m0, n0, (kt + 4) * PBK, S1);
+    pipe_issue<AK>(p, m0, n0, (kt + 4) * BK, S1);
     pipe_compute<AK>(S2, code_lut, acc, wm, wn);
   }
 #define SA_PIPE_TAIL(t, CS, NS)                                       \
@@ -613,7 +624,7 @@ __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_
       stage_barrier<LPW>();                                           \
     else                                                              \
       stage_barrier<0>();                                             \
-    if ((t) + 2 < nk) pipe_issue<AK>(p, m0, n0, ((t) + 2) * PBK, NS); \
+    if ((t) + 2 < nk) pipe_issue<AK>(p, m0, n0, ((t) + 2) * BK, NS);  \
     pipe_compute<AK>(CS, code_lut, acc, wm, wn);                      \
   }
   SA_PIPE_TAIL(kt, S0, S2)
@@ -623,16 +634,38 @@ __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_
 #undef SA_PIPE_TAIL
 }
 
+// Workgroup -> output tile.  Workgroups are dispatched round-robin over the
+// 8 XCDs, so workgroup b runs on XCD b % 8; each XCD is given a contiguous
+// run of a grouped tile order (kGroupM row tiles across all column tiles,
+// row tile fastest), so the workgroups one XCD runs together share their A
+// row tiles and B column tiles in its L2.  Any dispatch order gives the
+// same results (the map is a bijection); this one only places the reuse.
+constexpr int64_t kGroupM = 4;
+__device__ __forceinline__ void pipe_tile(int64_t b, int64_t mt, int64_t ntl, int64_t& m,
+                                          int64_t& n) {
+  const int64_t G = mt * ntl;
+  const int64_t x = b % 8, l = b / 8;
+  const int64_t per = G / 8, rem = G % 8;
+  const int64_t t = x * per + (x < rem ? x : rem) + l;  // position in the grouped order
+  const int64_t gsz = kGroupM * ntl;
+  const int64_t first = (t / gsz) * kGroupM;
+  const int64_t gm = (mt - first < kGroupM) ? mt - first : kGroupM;
+  m = first + (t % gsz) % gm;
+  n = (t % gsz) / gm;
+}
+
 template <int AK>
-__global__ __launch_bounds__(NTH) void k_gemm_pipe(GParams p) {
+__global__ __launch_bounds__(NTH, Pipe<AK>::kWgsPerCu) void k_gemm_pipe(GParams p) {
   constexpr int kStageHalves = pipe_stage_halves<AK>();
   __shared__ __align__(16) uint16_t S0[kStageHalves], S1[kStageHalves], S2[kStageHalves];
   const int lane = lane_id();
   const int wave = (int)threadIdx.x / kWave;
   const int wm = wave / 2, wn = wave % 2;
   const int64_t mt = (p.T + PBM - 1) / PBM;
-  const int64_t m0 = (int64_t)(blockIdx.x % mt) * PBM;
-  const int64_t n0 = (int64_t)(blockIdx.x / mt) * PBN;
+  const int64_t ntl = (p.d_out + PBN - 1) / PBN;
+  int64_t mi, ni;
+  pipe_tile(blockIdx.x, mt, ntl, mi, ni);
+  const int64_t m0 = mi * PBM, n0 = ni * PBN;
 
   f16v acc[4][2];
 #pragma unroll
@@ -661,8 +694,9 @@ __global__ __launch_bounds__(NTH) void k_gemm_pipe(GParams p) {
     }
 }
 
+template <int AK>
 bool pipe_ok(const GParams& p) {
-  return p.d_in % PBK == 0 && p.d_out % 8 == 0 && p.d_out >= 8 && p.T >= 1 &&
+  return p.d_in % Pipe<AK>::kBK == 0 && p.d_out % 8 == 0 && p.d_out >= 8 && p.T >= 1 &&
          (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 &&
          (reinterpret_cast<uintptr_t>(p.wt) & 15u) == 0 &&
          (reinterpret_cast<uintptr_t>(p.mask) & 3u) == 0;
@@ -790,7 +824,7 @@ hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const u
   p.T = T;
   p.d_in = d_in;
   p.d_out = d_out;
-  if (g_gemm_engine != 1 && pipe_ok(p)) return launch_pipe<kADense>(p, s);
+  if (g_gemm_engine != 1 && pipe_ok<kADense>(p)) return launch_pipe<kADense>(p, s);
   return launch_kind<kADense>(p, s);
 }
 
@@ -815,7 +849,7 @@ hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
   // 2:4 on the sparse MFMA; every other pattern through zero-filled dense
   // tiles (vector loads when m divides 4n)
   if (n == 2 && m == 4) {
-    if (g_gemm_engine != 1 && pipe_ok(p)) return launch_pipe<kA24>(p, s);
+    if (g_gemm_engine != 1 && pipe_ok<kA24>(p)) return launch_pipe<kA24>(p, s);
     return launch_kind<kA24>(p, s);
   }
   // two passes through the dense pipelined engine when a workspace is given
@@ -824,7 +858,7 @@ hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
     GParams pd = p;
     pd.x = static_cast<const uint16_t*>(ws);
     pd.mask = nullptr;
-    if (pipe_ok(pd)) {
+    if (pipe_ok<kADense>(pd)) {
       hipError_t e = launch_nm_expand(xval, mask, T, d_in, n, m, static_cast<uint16_t*>(ws), s);
       if (e != hipSuccess) return e;
       return launch_pipe<kADense>(pd, s);

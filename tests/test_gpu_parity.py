@@ -447,12 +447,14 @@ def test_dense_gemm_small(T, d_in, d_out, tile_rows):
     assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
 
 
-@pytest.mark.parametrize("T,d_in,d_out", [(256, 64, 128), (300, 128, 136), (17, 192, 8),
-                                          (513, 256, 264), (256, 320, 128), (70, 448, 1000),
-                                          (260, 1088, 392)])
+@pytest.mark.parametrize("T,d_in,d_out", [(64, 32, 128), (256, 64, 128), (40, 96, 136),
+                                          (300, 128, 136), (300, 160, 264), (17, 192, 8),
+                                          (129, 224, 72), (513, 256, 264), (256, 320, 128),
+                                          (70, 448, 1000), (260, 1088, 392)])
 def test_dense_gemm_k_pipeline_lengths(T, d_in, d_out):
-    """K a multiple of 64 takes the pipelined engine: 1 to 7 and 17 K steps
-    cover the steady loop and every tail length, with ragged rows/columns."""
+    """K a multiple of 32 takes the pipelined dense engine (K steps of 32):
+    1 to 8, 10, 14 and 34 K steps cover the steady loop and every tail
+    length, with ragged rows/columns."""
     X = syn.gaussian_f16((T, d_in), 1.0, T + d_in)
     wt = syn.weight_t(d_out, d_in, d_out)
     Y = sa.dense_gemm(dev(X), dev(wt))
@@ -485,9 +487,10 @@ def test_nm_spmm_small(n, m, T, d_in, d_out, tile_rows):
 @pytest.mark.parametrize("T,d_in,d_out", [(256, 64, 128), (300, 192, 136), (513, 320, 264),
                                           (70, 1088, 1000), (1024, 1024, 1024)])
 def test_gemm_engines_agree(T, d_in, d_out):
-    """The pipelined engine (default when K is a multiple of 64) and the
-    staged-register engine (forced by a tile height) issue the same MFMA
-    sequence per output block: dense and 2:4 results must be identical."""
+    """The pipelined engine (default when K is a multiple of its step: 32
+    dense, 64 for 2:4) and the staged-register engine (forced by a tile
+    height) issue the same MFMA sequence per output block: dense and 2:4
+    results must be identical."""
     X = syn.gaussian_f16((T, d_in), 1.0, T * 7 + d_in)
     X_g, wt_g = dev(X), dev(syn.weight_t(d_out, d_in, d_out + 3))
     mask_g, val_g = sa.act_sparsify_nm(X_g, 2, 4)
