@@ -291,11 +291,18 @@ int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
  */
 int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff);
 /*
- * Process-wide tile height of dense_gemm / nm_act_spmm, for tuning sweeps:
- * 0 = automatic (256-row tiles when they fill the chip, else 128), or 128 /
- * 256.  Same result either way.  Not thread-safe.
+ * Process-wide matmul choices of dense_gemm / nm_act_spmm, for tuning sweeps
+ * and cross-checks.
+ *   tile_rows: 0 = automatic (dense: 256-row tiles when they give at least
+ *     one workgroup per CU, else 128; 2:4: 128), or 128 / 256.
+ *   engine: 0 = automatic, 1 = the staged-register engine, 2 = the
+ *     pipelined engine (which applies when d_in is a multiple of its K
+ *     step, 32 for dense and the expanded N:M patterns, 64 for 2:4, with
+ *     16-byte aligned rows; other calls take the staged-register engine).
+ * Every choice issues the same MFMA sequence per output element: identical
+ * results.  Returns SA_ERR_INVALID_ARG for other values.  Not thread-safe.
  */
-int sa_set_gemm_tuning(int tile_rows);
+int sa_set_gemm_tuning(int tile_rows, int engine);
 /* Describe tiling `i` (tile_o, threads, unroll); tile_o is negative for a
  * full-K tiling (one launch, no split of d_in).  Returns SA_ERR_INVALID_ARG
  * past the last one.  Output pointers are HOST pointers (may be NULL). */

@@ -300,10 +300,11 @@ int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff) {
   return SA_OK;
 }
 
-int sa_set_gemm_tuning(int tile_rows) {
+int sa_set_gemm_tuning(int tile_rows, int engine) {
   sa::clear_error();
-  if (sa::gemm_set_tile_rows(tile_rows) != 0) {
-    sa::set_error("sa_set_gemm_tuning: tile_rows must be 0, 128 or 256 (got %d)", tile_rows);
+  if (sa::gemm_set_tuning(tile_rows, engine) != 0) {
+    sa::set_error("sa_set_gemm_tuning: tile_rows must be 0, 128 or 256 (got %d) and engine 0, 1 "
+                  "or 2 (got %d)", tile_rows, engine);
     return SA_ERR_INVALID_ARG;
   }
   return SA_OK;

@@ -340,23 +340,24 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
 
 // ---------------------------------------------------------------------------
 // Pipelined engine (dense and 2:4 A, d_in a multiple of the kind's K step,
-// 16-byte aligned rows).  A 256-thread workgroup computes a 256 x 128 output
-// tile, four waves of 128 x 64; the K loop steps through three LDS stages.
-// Tiles go from global memory to LDS with direct loads (global_load_lds:
-// lane l's bytes land at the instruction's LDS base + size * l), two K steps
-// ahead, so no registers hold staged data and the loads of step t+2 overlap
-// the MFMAs of step t.
-//   Dense: K steps of 32 (72 KB of LDS), so two workgroups share a CU and
-//     one's barrier and load waits are covered by the other's MFMAs
-//     (measured 8% faster than steps of 64 with one workgroup per CU).
-//     X rows, K-contiguous, are stored [m][32] with 16-byte chunks
-//     XOR-swizzled by the row (chosen through each lane's source address) so
-//     the 32 rows one operand read touches fall in distinct banks.
-//   2:4: K steps of 64, one workgroup per CU (steps of 32 leave too few
-//     sparse MFMAs per barrier: measured slower).  The compressed values,
-//     [m][32] (64-byte rows, swizzled as the dense A), and the row's two
-//     32-bit mask words [m][2]; each lane turns its 16 mask bits into the
-//     position code of the sparse MFMA.
+// 16-byte aligned rows).  A 256-thread workgroup computes a BM x 128 output
+// tile (BM = 256 or 128, chosen per call at launch), four waves of BM/2 x 64;
+// the K loop steps through three LDS stages.  Tiles go from global memory to
+// LDS with direct loads (global_load_lds: lane l's bytes land at the
+// instruction's LDS base + size * l), two K steps ahead, so no registers
+// hold staged data and the loads of step t+2 overlap the MFMAs of step t.
+// Two or three workgroups share a CU wherever LDS and registers allow, so
+// one's barrier and load waits are covered by the others' MFMAs.
+//   Dense: K steps of 32 (72 KB of LDS at BM = 256: two workgroups per CU;
+//     measured 8% faster than steps of 64 with one).  X rows, K-contiguous,
+//     are stored [m][32] with 16-byte chunks XOR-swizzled by the row (chosen
+//     through each lane's source address) so the 32 rows one operand read
+//     touches fall in distinct banks.
+//   2:4: K steps of 64 (steps of 32 leave too few sparse MFMAs per barrier:
+//     measured slower); 128-row tiles take 75 KB, two workgroups per CU.
+//     The compressed values, [m][32] (64-byte rows, swizzled as the dense
+//     A), and the row's two 32-bit mask words [m][2]; each lane turns its 16
+//     mask bits into the position code of the sparse MFMA.
 //   B (WT, N-contiguous) is stored [k][128] as it lies in memory (chunks
 //     swizzled by k); the MFMA B operand -- consecutive k of one column --
 //     comes from LDS transpose reads (ds_read_b64_tr_b16): within a 16-lane
@@ -373,27 +374,29 @@ constexpr int PBM = 256, PBN = 128;
 typedef short s4v __attribute__((ext_vector_type(4)));
 #define SA_LDS4(ptr) ((__attribute__((address_space(3))) s4v*)(ptr))
 
-template <int AK>
+template <int AK, int BM>
 struct Pipe;
-template <>
-struct Pipe<kADense> {
-  static constexpr int kBK = 32;                  // K step
-  static constexpr int kAHalves = PBM * kBK;      // [256][32]
+template <int BM>
+struct Pipe<kADense, BM> {
+  static constexpr int kBK = 32;                       // K step
+  static constexpr int kMB = BM / 64;                  // 32-row A blocks per wave
+  static constexpr int kAHalves = BM * kBK;            // [BM][32]
   static constexpr int kMaskWords = 0;
-  static constexpr int kLoadsPerWave = 4 + 2;     // A, B
-  static constexpr int kWgsPerCu = 2;
+  static constexpr int kLoadsPerWave = BM / 64 + 2;    // A, B
+  static constexpr int kWgsPerCu = BM == 256 ? 2 : 3;
 };
-template <>
-struct Pipe<kA24> {
+template <int BM>
+struct Pipe<kA24, BM> {
   static constexpr int kBK = 64;
-  static constexpr int kAHalves = PBM * kBK / 2;  // [256][32] compressed
-  static constexpr int kMaskWords = PBM * 2;      // [256][2]
-  static constexpr int kLoadsPerWave = 4 + 4 + 2;  // A, B, mask
-  static constexpr int kWgsPerCu = 1;
+  static constexpr int kMB = BM / 64;
+  static constexpr int kAHalves = BM * kBK / 2;        // [BM][32] compressed
+  static constexpr int kMaskWords = BM * 2;            // [BM][2]
+  static constexpr int kLoadsPerWave = BM / 64 + 4 + BM / 128;  // A, B, mask
+  static constexpr int kWgsPerCu = BM == 256 ? 1 : 2;
 };
-template <int AK>
+template <int AK, int BM>
 constexpr int pipe_stage_halves() {
-  return Pipe<AK>::kAHalves + Pipe<AK>::kBK * PBN + 2 * Pipe<AK>::kMaskWords;
+  return Pipe<AK, BM>::kAHalves + Pipe<AK, BM>::kBK * PBN + 2 * Pipe<AK, BM>::kMaskWords;
 }
 
 // 16-byte chunk swizzles: A rows of 64 bytes (dense and 2:4), B rows of 256
@@ -448,18 +451,19 @@ __device__ __forceinline__ void load_to_lds4(const void* src, const void* lds_ba
 // This wave's share of the loads of the K step starting at k0 into one stage
 // (A, then B, then for 2:4 the mask words).  Rows past T and columns past
 // d_out read clamped (valid) addresses; their results are never stored.
-template <int AK>
+template <int AK, int BM>
 __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t n0, int64_t k0,
                                            uint16_t* S) {
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   uint16_t* As = S;
-  uint16_t* Bs = S + Pipe<AK>::kAHalves;
-  constexpr int BK = Pipe<AK>::kBK;
+  uint16_t* Bs = S + Pipe<AK, BM>::kAHalves;
+  constexpr int BK = Pipe<AK, BM>::kBK;
+  constexpr int AI = BM / 64;  // A instructions per wave
   if constexpr (AK == kADense) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rb = (w * 4 + i) * 16;  // 16 rows of 64 bytes per instruction
+    for (int i = 0; i < AI; ++i) {
+      const int rb = (w * AI + i) * 16;  // 16 rows of 64 bytes per instruction
       const int r = rb + lane / 4;
       const int gc = (lane % 4) ^ swz_a(r);
       int64_t row = m0 + r;
@@ -469,8 +473,8 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
   } else {
     const int64_t kc = p.d_in / 2;  // compressed row length
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rb = (w * 4 + i) * 16;  // 16 rows of 64 bytes per instruction
+    for (int i = 0; i < AI; ++i) {
+      const int rb = (w * AI + i) * 16;  // 16 rows of 64 bytes per instruction
       const int r = rb + lane / 4;
       const int gc = (lane % 4) ^ swz_a(r);
       int64_t row = m0 + r;
@@ -479,9 +483,10 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
     }
     uint32_t* Ms = reinterpret_cast<uint32_t*>(Bs + BK * PBN);
     const int64_t words = p.d_in / 32;
+    constexpr int MI = BM / 128;  // mask instructions per wave
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rb = (w * 2 + i) * 32;  // 32 rows of 2 words per instruction
+    for (int i = 0; i < MI; ++i) {
+      const int rb = (w * MI + i) * 32;  // 32 rows of 2 words per instruction
       const int r = rb + lane / 2;
       int64_t row = m0 + r;
       if (row >= p.T) row = p.T - 1;
@@ -525,20 +530,21 @@ __device__ __forceinline__ int code_of(uint32_t bits) {
   return (int)code;
 }
 
-template <int AK>
+template <int AK, int BM>
 __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* code_lut,
-                                             f16v (&acc)[4][2], int wm, int wn) {
+                                             f16v (&acc)[Pipe<AK, BM>::kMB][2], int wm, int wn) {
   const int lane = lane_id();
-  constexpr int BK = Pipe<AK>::kBK;
+  constexpr int BK = Pipe<AK, BM>::kBK;
+  constexpr int MB = Pipe<AK, BM>::kMB;
   const uint16_t* As = S;
-  const uint16_t* Bs = S + Pipe<AK>::kAHalves;
+  const uint16_t* Bs = S + Pipe<AK, BM>::kAHalves;
   if constexpr (AK == kADense) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      h8 aop[4], bop[2];
+      h8 aop[MB], bop[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int m = wm * 128 + 32 * a + lane % 32;
+      for (int a = 0; a < MB; ++a) {
+        const int m = wm * (BM / 2) + 32 * a + lane % 32;
         const int q = 2 * kk + lane / 32;
         aop[a] = *reinterpret_cast<const h8*>(As + m * BK + 8 * (q ^ swz_a(m)));
       }
@@ -551,7 +557,7 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* c
         bop[b] = __builtin_bit_cast(h8, both);
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < MB; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[a], bop[b], acc[a][b], 0, 0, 0);
@@ -560,12 +566,12 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* c
     const uint32_t* Ms = reinterpret_cast<const uint32_t*>(Bs + BK * PBN);
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
-      h8 aop[4];
-      int code[4];
+      h8 aop[MB];
+      int code[MB];
       h16 bop[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int m = wm * 128 + 32 * a + lane % 32;
+      for (int a = 0; a < MB; ++a) {
+        const int m = wm * (BM / 2) + 32 * a + lane % 32;
         const int q = 2 * kk + lane / 32;
         aop[a] = *reinterpret_cast<const h8*>(As + m * (BK / 2) + 8 * (q ^ swz_a(m)));
         // position code of this lane's 16 mask bits, a byte at a time
@@ -583,7 +589,7 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* c
         bop[b] = __builtin_bit_cast(h16, all);
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < MB; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
           acc[a][b] =
@@ -596,36 +602,36 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* c
 // refills stage (t + 2) % 3.  The main loop runs while every refill exists,
 // with no branch inside; the last one to four steps run in the tail with
 // their own waits.
-template <int AK>
+template <int AK, int BM>
 __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_t n0,
                                             uint16_t* S0, uint16_t* S1, uint16_t* S2,
-                                            const uint8_t* code_lut, f16v (&acc)[4][2], int wm,
-                                            int wn) {
-  constexpr int LPW = Pipe<AK>::kLoadsPerWave;
-  constexpr int BK = Pipe<AK>::kBK;
+                                            const uint8_t* code_lut,
+                                            f16v (&acc)[Pipe<AK, BM>::kMB][2], int wm, int wn) {
+  constexpr int LPW = Pipe<AK, BM>::kLoadsPerWave;
+  constexpr int BK = Pipe<AK, BM>::kBK;
   const int64_t nk = p.d_in / BK;
-  pipe_issue<AK>(p, m0, n0, 0, S0);
-  if (nk > 1) pipe_issue<AK>(p, m0, n0, BK, S1);
+  pipe_issue<AK, BM>(p, m0, n0, 0, S0);
+  if (nk > 1) pipe_issue<AK, BM>(p, m0, n0, BK, S1);
   int64_t kt = 0;
   for (; kt + 4 < nk; kt += 3) {
     stage_barrier<LPW>();
-    pipe_issue<AK>(p, m0, n0, (kt + 2) * BK, S2);
-    pipe_compute<AK>(S0, code_lut, acc, wm, wn);
+    pipe_issue<AK, BM>(p, m0, n0, (kt + 2) * BK, S2);
+    pipe_compute<AK, BM>(S0, code_lut, acc, wm, wn);
     stage_barrier<LPW>();
-    pipe_issue<AK>(p, m0, n0, (kt + 3) * BK, S0);
-    pipe_compute<AK>(S1, code_lut, acc, wm, wn);
+    pipe_issue<AK, BM>(p, m0, n0, (kt + 3) * BK, S0);
+    pipe_compute<AK, BM>(S1, code_lut, acc, wm, wn);
     stage_barrier<LPW>();
-    pipe_issue<AK>(p, m0, n0, (kt + 4) * BK, S1);
-    pipe_compute<AK>(S2, code_lut, acc, wm, wn);
+    pipe_issue<AK, BM>(p, m0, n0, (kt + 4) * BK, S1);
+    pipe_compute<AK, BM>(S2, code_lut, acc, wm, wn);
   }
-#define SA_PIPE_TAIL(t, CS, NS)                                       \
-  if ((t) < nk) {                                                     \
-    if ((t) + 1 < nk)                                                 \
-      stage_barrier<LPW>();                                           \
-    else                                                              \
-      stage_barrier<0>();                                             \
-    if ((t) + 2 < nk) pipe_issue<AK>(p, m0, n0, ((t) + 2) * BK, NS);  \
-    pipe_compute<AK>(CS, code_lut, acc, wm, wn);                      \
+#define SA_PIPE_TAIL(t, CS, NS)                                           \
+  if ((t) < nk) {                                                         \
+    if ((t) + 1 < nk)                                                     \
+      stage_barrier<LPW>();                                               \
+    else                                                                  \
+      stage_barrier<0>();                                                 \
+    if ((t) + 2 < nk) pipe_issue<AK, BM>(p, m0, n0, ((t) + 2) * BK, NS);  \
+    pipe_compute<AK, BM>(CS, code_lut, acc, wm, wn);                      \
   }
   SA_PIPE_TAIL(kt, S0, S2)
   SA_PIPE_TAIL(kt + 1, S1, S0)
@@ -654,22 +660,23 @@ __device__ __forceinline__ void pipe_tile(int64_t b, int64_t mt, int64_t ntl, in
   n = (t % gsz) / gm;
 }
 
-template <int AK>
-__global__ __launch_bounds__(NTH, Pipe<AK>::kWgsPerCu) void k_gemm_pipe(GParams p) {
-  constexpr int kStageHalves = pipe_stage_halves<AK>();
+template <int AK, int BM>
+__global__ __launch_bounds__(NTH, (Pipe<AK, BM>::kWgsPerCu)) void k_gemm_pipe(GParams p) {
+  constexpr int kStageHalves = pipe_stage_halves<AK, BM>();
+  constexpr int MB = Pipe<AK, BM>::kMB;
   __shared__ __align__(16) uint16_t S0[kStageHalves], S1[kStageHalves], S2[kStageHalves];
   const int lane = lane_id();
   const int wave = (int)threadIdx.x / kWave;
   const int wm = wave / 2, wn = wave % 2;
-  const int64_t mt = (p.T + PBM - 1) / PBM;
+  const int64_t mt = (p.T + BM - 1) / BM;
   const int64_t ntl = (p.d_out + PBN - 1) / PBN;
   int64_t mi, ni;
   pipe_tile(blockIdx.x, mt, ntl, mi, ni);
-  const int64_t m0 = mi * PBM, n0 = ni * PBN;
+  const int64_t m0 = mi * BM, n0 = ni * PBN;
 
-  f16v acc[4][2];
+  f16v acc[MB][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -679,16 +686,16 @@ __global__ __launch_bounds__(NTH, Pipe<AK>::kWgsPerCu) void k_gemm_pipe(GParams 
   // the first stage barrier orders these writes before any read
   __shared__ uint8_t code_lut[AK == kA24 ? 256 : 1];
   if constexpr (AK == kA24) code_lut[threadIdx.x] = (uint8_t)code_of(threadIdx.x);
-  pipe_k_loop<AK>(p, m0, n0, S0, S1, S2, code_lut, acc, wm, wn);
+  pipe_k_loop<AK, BM>(p, m0, n0, S0, S1, S2, code_lut, acc, wm, wn);
 
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int64_t col = n0 + wn * 64 + b * 32 + lane % 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        const int64_t row = m0 + wm * (BM / 2) + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
         if (row < p.T && col < p.d_out) p.y[row * p.d_out + col] = f2h(acc[a][b][r]);
       }
     }
@@ -696,7 +703,7 @@ __global__ __launch_bounds__(NTH, Pipe<AK>::kWgsPerCu) void k_gemm_pipe(GParams 
 
 template <int AK>
 bool pipe_ok(const GParams& p) {
-  return p.d_in % Pipe<AK>::kBK == 0 && p.d_out % 8 == 0 && p.d_out >= 8 && p.T >= 1 &&
+  return p.d_in % Pipe<AK, 256>::kBK == 0 && p.d_out % 8 == 0 && p.d_out >= 8 && p.T >= 1 &&
          (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 &&
          (reinterpret_cast<uintptr_t>(p.wt) & 15u) == 0 &&
          (reinterpret_cast<uintptr_t>(p.mask) & 3u) == 0;
@@ -773,15 +780,27 @@ hipError_t launch_nm_expand(const uint16_t* xval, const uint32_t* mask, int64_t 
   return hipGetLastError();
 }
 
+int g_gemm_bm = 0;      // tuning override of the tile height: 0 = automatic, else 128 or 256
+int g_gemm_engine = 0;  // tuning override: 0 = automatic, 1 = staged-register engine, 2 = pipelined
+
+// Pipelined engine tile height (measured): dense 256 rows, or 128 when
+// 256-row tiles would give fewer workgroups than the device has CUs; 2:4
+// always 128, where two workgroups share a CU (faster at both configured
+// shapes).
 template <int AK>
 hipError_t launch_pipe(const GParams& p, hipStream_t s) {
-  const int64_t tiles = ((p.T + PBM - 1) / PBM) * ((p.d_out + PBN - 1) / PBN);
+  const int64_t ntl = (p.d_out + PBN - 1) / PBN;
+  const int64_t tiles256 = ((p.T + 255) / 256) * ntl;
+  const int bm =
+      g_gemm_bm ? g_gemm_bm : ((AK == kA24 || tiles256 < device_cus()) ? 128 : 256);
+  const int64_t tiles = ((p.T + bm - 1) / bm) * ntl;
   if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
-  hipLaunchKernelGGL(k_gemm_pipe<AK>, dim3((unsigned)tiles), dim3(NTH), 0, s, p);
+  if (bm == 256)
+    hipLaunchKernelGGL((k_gemm_pipe<AK, 256>), dim3((unsigned)tiles), dim3(NTH), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemm_pipe<AK, 128>), dim3((unsigned)tiles), dim3(NTH), 0, s, p);
   return hipGetLastError();
 }
-
-int g_gemm_engine = 0;  // tuning override: 0 = automatic, 1 = staged-register engine, 2 = pipelined
 
 template <int AK, int BM>
 hipError_t launch_tile(const GParams& p, hipStream_t s) {
@@ -791,7 +810,6 @@ hipError_t launch_tile(const GParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-int g_gemm_bm = 0;  // tuning override: 0 = automatic, else 128 or 256
 
 // 256-row tiles when there are enough of them to fill the chip, 128 otherwise.
 // The zero-filled N:M staging (any pattern but 2:4) needs more registers per
@@ -807,11 +825,10 @@ hipError_t launch_kind(const GParams& p, hipStream_t s) {
 
 }  // namespace
 
-int gemm_set_tile_rows(int bm) {
-  if (bm != 0 && bm != 128 && bm != 256) return 1;
+int gemm_set_tuning(int bm, int engine) {
+  if ((bm != 0 && bm != 128 && bm != 256) || engine < 0 || engine > 2) return 1;
   g_gemm_bm = bm;
-  // an explicit tile height selects the staged-register engine
-  g_gemm_engine = bm == 0 ? 0 : 1;
+  g_gemm_engine = engine;
   return 0;
 }
 

@@ -982,6 +982,8 @@ struct Plan {
   size_t smem;
 };
 
+}  // namespace
+
 // Compute units of the current device (cached per device).
 int device_cus() {
   static int cache[64] = {0};
@@ -996,6 +998,8 @@ int device_cus() {
   }
   return cache[dev];
 }
+
+namespace {
 
 // The split-K kernel instance for a mode, tiling and batch (split-K tilings
 // exist for batch 1 of the hot modes; everything else uses tiling 0).

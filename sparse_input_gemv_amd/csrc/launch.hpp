@@ -80,12 +80,15 @@ constexpr int kReadStreamThreads = 256;
 hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
 // ---- MFMA matmuls (gemm.hip) ------------------------------------------------
+// Compute units of the current device (cached per device).
+int device_cus();
+
 hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
                              int64_t d_out, uint16_t* y, hipStream_t s);
 size_t nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m);
 hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
                           int n, int m, const uint16_t* wt, int64_t d_out, uint16_t* y,
                           void* ws, size_t ws_bytes, hipStream_t s);
-int gemm_set_tile_rows(int bm);
+int gemm_set_tuning(int bm, int engine);
 
 }  // namespace sa

@@ -123,8 +123,11 @@ def test_gemv_checks(sa):
     assert sa.sa_set_gemv_tuning(-1, -1, 0) == SA_ERR_INVALID_ARG
     for handoff in (1, 2, 0):
         assert sa.sa_set_gemv_tuning(-1, 0, handoff) == SA_OK
-    assert sa.sa_set_gemm_tuning(64) == SA_ERR_INVALID_ARG
-    assert sa.sa_set_gemm_tuning(0) == SA_OK
+    assert sa.sa_set_gemm_tuning(64, 0) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemm_tuning(0, 3) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemm_tuning(0, -1) == SA_ERR_INVALID_ARG
+    for rows, engine in ((128, 1), (256, 2), (0, 0)):
+        assert sa.sa_set_gemm_tuning(rows, engine) == SA_OK
 
 
 def test_swiglu_checks(sa):

@@ -433,17 +433,21 @@ def test_one_launch_handoff_matches_two_launches(tiling):
 from oracle import spmm  # noqa: E402
 
 
-@pytest.mark.parametrize("tile_rows", [0, 128, 256])
+# (tile rows, engine): automatic, then each engine at each tile height
+GEMM_CHOICES = [(0, 0), (128, 1), (256, 1), (128, 2), (256, 2)]
+
+
+@pytest.mark.parametrize("tile_rows,engine", GEMM_CHOICES)
 @pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 1024), (130, 96, 136), (1, 32, 8),
                                           (257, 4096, 264), (600, 256, 1032)])
-def test_dense_gemm_small(T, d_in, d_out, tile_rows):
+def test_dense_gemm_small(T, d_in, d_out, tile_rows, engine):
     X = syn.gaussian_f16((T, d_in), 1.0, T)
     wt = syn.weight_t(d_out, d_in, d_in)
     try:
-        sa.set_gemm_tuning(tile_rows)
+        sa.set_gemm_tuning(tile_rows, engine)
         Y = sa.dense_gemm(dev(X), dev(wt))
     finally:
-        sa.set_gemm_tuning(0)
+        sa.set_gemm_tuning(0, 0)
     assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
 
 
@@ -461,11 +465,11 @@ def test_dense_gemm_k_pipeline_lengths(T, d_in, d_out):
     assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
 
 
-@pytest.mark.parametrize("tile_rows", [0, 128, 256])
+@pytest.mark.parametrize("tile_rows,engine", GEMM_CHOICES)
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 4), (3, 4), (5, 16),
                                  (32, 32)])
 @pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 512), (100, 96, 136), (300, 128, 264)])
-def test_nm_spmm_small(n, m, T, d_in, d_out, tile_rows):
+def test_nm_spmm_small(n, m, T, d_in, d_out, tile_rows, engine):
     if d_in % m:
         pytest.skip("d_in not a multiple of m")
     X = syn.gaussian_f16((T, d_in), 1.0, n * 7 + m)
@@ -474,10 +478,10 @@ def test_nm_spmm_small(n, m, T, d_in, d_out, tile_rows):
     ref = spmm.nm_spmm(X, keep, wt)
     mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
     try:
-        sa.set_gemm_tuning(tile_rows)
+        sa.set_gemm_tuning(tile_rows, engine)
         Y = sa.nm_act_spmm(val_g, mask_g, n, m, dev(wt))
     finally:
-        sa.set_gemm_tuning(0)
+        sa.set_gemm_tuning(0, 0)
     assert_close(Y, ref)
     # each token's row is that token's masked GEMV
     r = 3
@@ -488,23 +492,23 @@ def test_nm_spmm_small(n, m, T, d_in, d_out, tile_rows):
                                           (70, 1088, 1000), (1024, 1024, 1024)])
 def test_gemm_engines_agree(T, d_in, d_out):
     """The pipelined engine (default when K is a multiple of its step: 32
-    dense, 64 for 2:4) and the staged-register engine (forced by a tile
-    height) issue the same MFMA sequence per output block: dense and 2:4
+    dense, 64 for 2:4) and the staged-register engine, each at both tile
+    heights, issue the same MFMA sequence per output block: dense and 2:4
     results must be identical."""
     X = syn.gaussian_f16((T, d_in), 1.0, T * 7 + d_in)
     X_g, wt_g = dev(X), dev(syn.weight_t(d_out, d_in, d_out + 3))
     mask_g, val_g = sa.act_sparsify_nm(X_g, 2, 4)
     out = {}
     try:
-        for tr in (0, 128, 256):
-            sa.set_gemm_tuning(tr)
-            out[tr] = (sa.dense_gemm(X_g, wt_g).clone(),
-                       sa.nm_act_spmm(val_g, mask_g, 2, 4, wt_g).clone())
+        for choice in GEMM_CHOICES:
+            sa.set_gemm_tuning(*choice)
+            out[choice] = (sa.dense_gemm(X_g, wt_g).clone(),
+                           sa.nm_act_spmm(val_g, mask_g, 2, 4, wt_g).clone())
     finally:
-        sa.set_gemm_tuning(0)
-    for tr in (128, 256):
-        assert torch.equal(out[0][0], out[tr][0]), ("dense", tr)
-        assert torch.equal(out[0][1], out[tr][1]), ("2:4", tr)
+        sa.set_gemm_tuning(0, 0)
+    for choice in GEMM_CHOICES[1:]:
+        assert torch.equal(out[(0, 0)][0], out[choice][0]), ("dense", choice)
+        assert torch.equal(out[(0, 0)][1], out[choice][1]), ("2:4", choice)
 
 
 @pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (4, 8), (1, 4), (3, 4), (5, 16), (7, 32),
