@@ -336,7 +336,7 @@ def run_suite(args):
         return wanted is None or any(r in wanted for r in rows)
 
     # ---- a9 calibration; a1 threshold; a4 / a8 GEMVs of the Llama-2-7B layer ----
-    if section("a9", "a1", "a4", "a8"):
+    if section("a9", "a1", "a4", "a8", "next1"):
         suite_layer(sa, syn, dev, ev_time, emit, rotation)
     if section("a2", "a5"):
         suite_topk(sa, syn, dev, ev_time, emit, rotation)
@@ -357,6 +357,7 @@ def suite_layer(sa, syn, dev, ev_time, emit, rotation):
                            for s_ in (0.4, 0.5, 0.6)}
         emit("a9", f"act_calibrate_threshold {inp} n=10000", us, bytes_=2 * 10000)
     layer = {"sparse": 0.0, "dense": 0.0}
+    per = {}  # projection -> (sparse us at 50%, dense us)
     for name, (d_out, d_in, inp) in syn.LLAMA2_7B.items():
         _, dist = syn.LLAMA2_7B_INPUTS[inp]
         rot = rotation(d_out, d_in, syn.weight_seed(name))
@@ -373,6 +374,7 @@ def suite_layer(sa, syn, dev, ev_time, emit, rotation):
                  achieved_sparsity=round(1 - nnz / d_in, 4))
             if sp == 0.5:
                 layer["sparse"] += us
+                per[name] = [us, 0.0]
                 us_l = ev_time(lambda i: sa.sparse_gemv(rot[i % nr], i_, v_, n_, y=y), 1000)
                 emit("a4", f"sparse_gemv (list) {name} {d_out}x{d_in} sparsity 0.5", us_l,
                      bytes_=2 * d_out * nnz + 6 * nnz + 2 * d_out)
@@ -381,6 +383,7 @@ def suite_layer(sa, syn, dev, ev_time, emit, rotation):
                      bytes_=2 * d_in + 6 * nnz + d_in // 8 + 4)
         us_d = ev_time(lambda i: sa.dense_gemv(rot[i % nr], x, y=y), 1000)
         layer["dense"] += us_d
+        per[name][1] = us_d
         emit("a8", f"dense_gemv {name} {d_out}x{d_in}", us_d,
              bytes_=2 * d_out * d_in + 2 * d_in + 2 * d_out, flops=2 * d_out * d_in)
         del rot
@@ -388,6 +391,38 @@ def suite_layer(sa, syn, dev, ev_time, emit, rotation):
     emit("a4", "Llama-2-7B layer, 7 projections at 50% vs dense (sum of calls)",
          layer["sparse"], speedup_vs_dense=round(layer["dense"] / layer["sparse"], 3),
          dense_us=round(layer["dense"], 3))
+
+    # shared-input fused projections: one sparsified input, the members'
+    # weights side by side (q|k|v, gate|up), one call
+    fused = {"sparse": per["o"][0] + per["down"][0], "dense": per["o"][1] + per["down"][1]}
+    for name, (members, inp) in syn.LLAMA2_7B_FUSED.items():
+        _, dist = syn.LLAMA2_7B_INPUTS[inp]
+        w0 = torch.from_numpy(syn.fused_weight_t(name)).to(dev)
+        d_in, d_out = w0.shape
+        n = max(2, -(-ROTATION_BYTES // (w0.numel() * 2)))
+        rot = [w0] + [torch.roll(w0, shifts=997 * i, dims=0).contiguous() for i in range(1, n)]
+        nr = len(rot)
+        x = torch.from_numpy(syn.activation((d_in,), dist, 0)).to(dev)
+        y = torch.empty((d_out,), dtype=torch.float16, device=dev)
+        t = thresholds[inp][0.5]
+        nnz = int(sa.act_sparsify_threshold(x, t)[3].cpu()[0])
+        us = ev_time(lambda i: sa.sparse_gemv_threshold(rot[i % nr], x, t, y=y), 1000)
+        sep = sum(per[m][0] for m in members)
+        emit("next1", f"fused sparse_gemv_threshold {'|'.join(members)} {d_out}x{d_in} sparsity 0.5",
+             us, bytes_=2 * d_out * nnz + 2 * d_in + 2 * d_out, flops=2 * d_out * nnz,
+             separate_calls_us=round(sep, 3), speedup_vs_separate=round(sep / us, 3))
+        us_d = ev_time(lambda i: sa.dense_gemv(rot[i % nr], x, y=y), 1000)
+        emit("next1", f"fused dense_gemv {'|'.join(members)} {d_out}x{d_in}", us_d,
+             bytes_=2 * d_out * d_in + 2 * d_in + 2 * d_out, flops=2 * d_out * d_in,
+             separate_calls_us=round(sum(per[m][1] for m in members), 3))
+        fused["sparse"] += us
+        fused["dense"] += us_d
+        del rot, w0
+        torch.cuda.empty_cache()
+    emit("next1", "Llama-2-7B layer with fused q|k|v and gate|up at 50% (4 calls) vs the same "
+         "fused dense", fused["sparse"], speedup_vs_fused_dense=round(fused["dense"] / fused["sparse"], 3),
+         fused_dense_us=round(fused["dense"], 3),
+         speedup_vs_separate_dense=round(layer["dense"] / fused["sparse"], 3))
 
 
 

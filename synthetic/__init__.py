@@ -28,6 +28,8 @@ __all__ = [
     "weight_t",
     "LLAMA2_7B",
     "LLAMA2_7B_INPUTS",
+    "LLAMA2_7B_FUSED",
+    "fused_weight_t",
     "LLAMA3_8B_MLP",
     "weight_seed",
     "calib_seed",
@@ -73,6 +75,12 @@ LLAMA2_7B_INPUTS = {
     "mlp_in": (4096, "gaussian"),
     "down_in": (11008, "laplace"),
 }
+# Projections that read the same input, fused into one weight whose outputs
+# are the members' outputs in order: name -> (members, input name).
+LLAMA2_7B_FUSED = {
+    "qkv": (("q", "k", "v"), "attn_in"),
+    "gateup": (("gate", "up"), "mlp_in"),
+}
 _WEIGHT_ORDER = ["q", "k", "v", "o", "gate", "up", "down"]
 _INPUT_ORDER = ["attn_in", "o_in", "mlp_in", "down_in"]
 
@@ -82,6 +90,14 @@ LLAMA3_8B_MLP = {"d_model": 4096, "d_ff": 14336}
 
 def weight_seed(name: str) -> int:
     return 1000 + _WEIGHT_ORDER.index(name)
+
+
+def fused_weight_t(name: str) -> np.ndarray:
+    """``WT`` of a fused projection: the members' seeded ``WT[d_in][d_out]``
+    side by side, so output block j is member j's output."""
+    members, _ = LLAMA2_7B_FUSED[name]
+    return np.concatenate(
+        [weight_t(LLAMA2_7B[m][0], LLAMA2_7B[m][1], weight_seed(m)) for m in members], axis=1)
 
 
 def calib_seed(input_name: str) -> int:

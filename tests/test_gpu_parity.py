@@ -126,6 +126,33 @@ def test_llama2_layer_projection(name, sparsity):
     assert_close(sa.sparse_gemv(wt_g, i_g, v_g, n_g), y_ref)
 
 
+@pytest.mark.parametrize("name", ["qkv", "gateup"])
+@pytest.mark.parametrize("sparsity", [0.5, 0.6])
+def test_fused_projection(name, sparsity):
+    """One sparsified block input through the members' weights side by side
+    (q|k|v 4096 -> 12288, gate|up 4096 -> 22016) in one call: the oracle's
+    result, and each member's block within tolerance of its own call."""
+    members, inp = syn.LLAMA2_7B_FUSED[name]
+    _, dist = syn.LLAMA2_7B_INPUTS[inp]
+    wt = syn.fused_weight_t(name)
+    x = syn.activation((wt.shape[0],), dist, 1)
+    t = float(calibrate.magnitude_threshold(syn.calibration_samples(inp), sparsity))
+    keep, idx, val, nnz = sparsify.threshold_sparsify(x, t)
+    y_ref = gemv.sparse_gemv(wt, idx, val)
+    wt_g, x_g = dev(wt), dev(x)
+    y = sa.sparse_gemv_threshold(wt_g, x_g, t)
+    assert_close(y, y_ref)
+    m_g, i_g, v_g, n_g = sa.act_sparsify_threshold(x_g, t)
+    assert_close(sa.sparse_gemv(wt_g, i_g, v_g, n_g), y_ref)
+    o = 0
+    for m in members:
+        d_out = syn.LLAMA2_7B[m][0]
+        part = sa.sparse_gemv_threshold(wt_g[:, o:o + d_out].contiguous(), x_g, t)
+        assert_close(y[o:o + d_out], y_ref[o:o + d_out])
+        assert_close(part, y_ref[o:o + d_out])
+        o += d_out
+
+
 def test_dense_gemv_matches_oracle():
     for (d_out, d_in) in [(4096, 11008), (11008, 4096), (1024, 1024), (72, 130)]:
         wt = syn.weight_t(d_out, d_in, 5)

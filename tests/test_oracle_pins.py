@@ -242,6 +242,30 @@ def test_batched_union_and_rows():
 # SiLU / masked SwiGLU down
 # --------------------------------------------------------------------------
 
+def test_fused_projection_is_the_members_side_by_side():
+    """A fused projection (one sparsified input, the members' weights side by
+    side) gives each member's own sparse GEMV in its output block, computed
+    here member by member with numpy's matmul on the masked input."""
+    x = syn.activation((4096,), "gaussian", 3)
+    t = 0.6745
+    keep, idx, val, nnz = sparsify.threshold_sparsify(x, t)
+    xs = np.where(keep, x.astype(np.float64), 0.0)
+    for name, (members, inp) in syn.LLAMA2_7B_FUSED.items():
+        assert syn.LLAMA2_7B_INPUTS[inp][0] == 4096
+        wt = syn.fused_weight_t(name)
+        y = gemv.sparse_gemv(wt, idx, val)
+        o = 0
+        for m in members:
+            d_out, d_in, m_inp = syn.LLAMA2_7B[m]
+            assert (d_in, m_inp) == (4096, inp)
+            w = syn.weight_t(d_out, d_in, syn.weight_seed(m))
+            assert np.array_equal(wt[:, o:o + d_out], w)
+            np.testing.assert_allclose(y[o:o + d_out], xs @ w.astype(np.float64), rtol=1e-12,
+                                       atol=1e-12)
+            o += d_out
+        assert o == wt.shape[1] == len(y)
+
+
 def test_silu_closed_forms():
     assert swiglu.silu(np.array([0.0]))[0] == 0.0
     # sigmoid(ln 3) = 3/4
