@@ -344,6 +344,8 @@ def run_suite(args):
         suite_swiglu(sa, syn, dev, ev_time, emit, rotation)
     if section("a3", "a7", "a8"):
         suite_matmul(sa, syn, dev, ev_time, emit)
+    if section("next2"):
+        suite_rank_adapter(sa, syn, dev, ev_time, emit)
 
 
 def suite_layer(sa, syn, dev, ev_time, emit, rotation):
@@ -452,6 +454,42 @@ def suite_topk(sa, syn, dev, ev_time, emit, rotation):
         del rot
         torch.cuda.empty_cache()
 
+
+
+def suite_rank_adapter(sa, syn, dev, ev_time, emit):
+    """RaNA linear-layer rank adapter A (m ⊙ B x) on the gate projection
+    (11008 x 4096) at rank 2048, 50% mask rate, against the dense gate GEMV."""
+    import torch
+
+    d_out, d_in, r = 11008, 4096, 2048
+    bt0, at0 = (torch.from_numpy(w).to(dev) for w in syn.rank_adapter_weights(d_out, d_in, r, 3000))
+    pair = (bt0.numel() + at0.numel()) * 2
+    n = max(2, -(-ROTATION_BYTES // pair))
+    # copy i permutes the rank index (B's rows and A's columns alike): other
+    # bytes in memory, the same adapter, mask size and y
+    rot = [(bt0, at0)] + [(torch.roll(bt0, 97 * i, 1).contiguous(),
+                           torch.roll(at0, 97 * i, 0).contiguous()) for i in range(1, n)]
+    wt_gate = torch.from_numpy(syn.weight_t(d_out, d_in, syn.weight_seed("gate"))).to(dev)
+    ng = max(2, -(-ROTATION_BYTES // (wt_gate.numel() * 2)))
+    rot_g = [wt_gate] + [torch.roll(wt_gate, 997 * i, 0).contiguous() for i in range(1, ng)]
+    x = torch.from_numpy(syn.activation((d_in,), "gaussian", 0)).to(dev)
+    v = torch.empty((r,), dtype=torch.float16, device=dev)
+    y = torch.empty((d_out,), dtype=torch.float16, device=dev)
+    nr = len(rot)
+    sq = torch.sort(sa.rana_adapter_gemv(bt0, at0, x, 0.0)[0].double() ** 2).values
+    for rate in (0.5, 0.7):
+        k = int(rate * r)
+        t = float(0.5 * (sq[k - 1] + sq[k]))
+        kept = int((sq >= t).sum())
+        us = ev_time(lambda i: sa.rana_adapter_gemv(rot[i % nr][0], rot[i % nr][1], x, t, v=v, y=y),
+                     1000)
+        bytes_ = 2 * d_in * r + 2 * d_out * kept + 2 * d_in + 2 * 2 * r + 2 * d_out
+        us_d = ev_time(lambda i: sa.dense_gemv(rot_g[i % len(rot_g)], x, y=y), 1000)
+        emit("next2", f"rana_adapter_gemv gate {d_out}x{d_in} rank {r} mask rate {rate}", us,
+             bytes_=bytes_, flops=2 * d_in * r + 2 * d_out * kept, kept=kept,
+             dense_gate_us=round(us_d, 3), speedup_vs_dense_gate=round(us_d / us, 3))
+    del rot, rot_g
+    torch.cuda.empty_cache()
 
 
 def suite_swiglu(sa, syn, dev, ev_time, emit, rotation):

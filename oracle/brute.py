@@ -62,3 +62,21 @@ def threshold_loop(x, t: float) -> np.ndarray:
     """Threshold mask with a plain Python loop, one comparison per entry."""
     return np.array([abs(float(v)) >= t and float(v) != 0.0 for v in np.asarray(x)],
                     dtype=bool)
+
+
+def rank_adapter_loop(bt, at, x, t: float) -> np.ndarray:
+    """The rank adapter ``A (m ⊙ B x)`` as scalar loops: ``v_i`` summed in
+    fp64 and stored as fp16, kept iff ``v_i * v_i >= t``, then each kept
+    ``v_i`` times row ``i`` of ``AT`` added into ``y``."""
+    d_in, r = len(bt), len(bt[0])
+    d_out = len(at[0])
+    y = [0.0] * d_out
+    for i in range(r):
+        s = 0.0
+        for k in range(d_in):
+            s += float(bt[k][i]) * float(x[k])
+        vi = float(np.float16(s))
+        if vi * vi >= t:
+            for o in range(d_out):
+                y[o] += vi * float(at[i][o])
+    return np.array(y)

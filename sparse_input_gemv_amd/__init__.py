@@ -25,7 +25,8 @@ import torch
 __all__ = [
     "SparseActError", "lib", "workspace",
     "act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm",
-    "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold", "masked_gemv",
+    "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold", "rana_adapter_gemv",
+    "masked_gemv",
     "dense_gemv", "masked_swiglu_down", "weight_col_norms", "nm_act_spmm", "dense_gemm",
     "set_gemv_tuning", "set_gemm_tuning", "gemv_tiling_info", "workspace_bytes", "MAX_BATCH",
 ]
@@ -47,6 +48,8 @@ _SIGNATURES = {
     "sa_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "sparse_gemv": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "sparse_gemv_threshold": (_i32, [_vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _sz, _vp]),
+    "rana_adapter_gemv": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _f32, _vp, _vp, _vp,
+                                 _sz, _vp]),
     "masked_gemv": (_i32, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "dense_gemv": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
     "masked_swiglu_down": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _f64, _i32, _vp, _vp, _vp,
@@ -204,6 +207,8 @@ def _gemv_out(wt, batch, squeeze, y):
         y = torch.empty((batch, d_out), dtype=torch.float16, device=wt.device)
     else:
         _dev(y, "y", torch.float16)
+        if y.numel() < batch * d_out:
+            raise ValueError(f"y holds {y.numel()} values, {batch * d_out} needed")
     return y
 
 
@@ -242,6 +247,29 @@ def sparse_gemv_threshold(wt: torch.Tensor, x: torch.Tensor, t: float,
     _check(lib().sparse_gemv_threshold(_ptr(wt), d_out, d_in, _ptr(x), batch, float(t), _ptr(y),
                                        _ptr(ws), ws.numel(), _stream(wt)), "sparse_gemv_threshold")
     return _ret(y, squeeze)
+
+
+def rana_adapter_gemv(bt: torch.Tensor, at: torch.Tensor, x: torch.Tensor, t: float,
+                      v: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """RaNA linear-layer rank adapter: ``v = B x``, ``y = A (m ⊙ v)`` with
+    ``m_i = v_i**2 >= t``; ``bt`` is ``B^T [d_in][r]``, ``at`` is
+    ``A^T [r][d_out]``.  Returns ``(v, y)``."""
+    _dev(bt, "bt", torch.float16)
+    _dev(at, "at", torch.float16)
+    _dev(x, "x", torch.float16)
+    squeeze = x.dim() == 1
+    batch, d_in = _rows(x)
+    r, d_out = bt.shape[1], at.shape[1]
+    if bt.shape[0] != d_in or at.shape[0] != r:
+        raise ValueError(f"shapes: bt {tuple(bt.shape)}, at {tuple(at.shape)}, x rows of {d_in}")
+    v = _gemv_out(bt, batch, squeeze, v)
+    y = _gemv_out(at, batch, squeeze, y)
+    need = max(workspace_bytes(r, d_in, batch), workspace_bytes(d_out, r, batch))
+    ws = workspace(bt.device, need)
+    _check(lib().rana_adapter_gemv(_ptr(bt), r, d_in, _ptr(at), d_out, _ptr(x), batch, float(t),
+                                   _ptr(v), _ptr(y), _ptr(ws), ws.numel(), _stream(bt)),
+           "rana_adapter_gemv")
+    return _ret(v, squeeze), _ret(y, squeeze)
 
 
 def masked_gemv(wt: torch.Tensor, x: torch.Tensor, mask: torch.Tensor,

@@ -139,6 +139,42 @@ int sparse_gemv_threshold(const uint16_t* wt, int64_t d_out, int64_t d_in, const
   return run_gemv(c, "sparse_gemv_threshold", stream);
 }
 
+int rana_adapter_gemv(const uint16_t* bt, int64_t r, int64_t d_in, const uint16_t* at,
+                      int64_t d_out, const uint16_t* x, int64_t batch, float t, uint16_t* v,
+                      uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  sa::clear_error();
+  const int64_t b1 = batch < 1 ? 1 : batch;
+  const size_t n1 = sa::gemv_workspace_bytes(r, d_in, b1);
+  const size_t n2 = sa::gemv_workspace_bytes(d_out, r, b1);
+  const size_t need = n1 > n2 ? n1 : n2;
+  int st = sa::check_gemv_common(bt, r, d_in, batch, v, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_gemv_common(at, d_out, r, batch, y, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_activation(x, "rana_adapter_gemv: x");
+  if (st == SA_OK) st = sa::check_threshold_value(t);
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeDense;
+  c.wt = bt;
+  c.d_out = r;
+  c.d_in = d_in;
+  c.batch = (int)batch;
+  c.x = x;
+  c.y = v;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  st = run_gemv(c, "rana_adapter_gemv", stream);
+  if (st != SA_OK) return st;
+  c.mode = sa::kModeThreshold;
+  c.square = 1;
+  c.wt = at;
+  c.d_out = d_out;
+  c.d_in = r;
+  c.x = v;
+  c.t = t;
+  c.y = y;
+  return run_gemv(c, "rana_adapter_gemv", stream);
+}
+
 int masked_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint16_t* x,
                 const uint32_t* mask, int64_t batch, uint16_t* y, void* ws, size_t ws_bytes,
                 void* stream) {

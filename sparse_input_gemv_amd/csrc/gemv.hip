@@ -120,6 +120,7 @@ struct KParams {
   int32_t* slice_cnt;
   uint32_t* tickets;  // non-null: one-launch hand-off
   int go, gk, slice;
+  int square;  // threshold mode: keep x_k iff x_k^2 >= t (rank-adapter masker)
 };
 
 constexpr int kModeListBatched = 5;  // kModeList with batch > 1
@@ -130,6 +131,14 @@ template <int B>
 constexpr int kOnePassChunks = B == 1 ? 4 : (B <= 4 ? 2 : 0);
 
 typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Threshold decision on one fp16 activation entry: the magnitude threshold
+// (|x| >= t and x != 0), or the rank adapter's masker, x^2 >= t.  The square
+// of an fp16 value is exact in fp32, so no rounding takes the decision.
+__device__ __forceinline__ bool keep_entry(uint16_t xb, float t, int square) {
+  const float v = h2f(xb);
+  return square ? v * v >= t : (mag_key(xb) != 0 && fabsf(v) >= t);
+}
 
 // Slot of this thread in a chunk compaction (ascending thread order) and the
 // chunk total.  `wsum` holds NT/64 ints of LDS.
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         bool kb = false;
         if (b < p.batch && k < k1) {
           if constexpr (MODE == kModeThreshold) {
-            kb = mag_key(xb) != 0 && fabsf(h2f(xb)) >= p.t;
+            kb = keep_entry(xb, p.t, p.square);
           } else if constexpr (MODE == kModeMasked) {
             kb = ((mw[c][b] >> (k & 31)) & 1u) != 0;
           } else {
@@ -476,7 +485,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
             const uint16_t xb = xr[b];
             bool kb;
             if constexpr (MODE == kModeThreshold) {
-              kb = mag_key(xb) != 0 && fabsf(h2f(xb)) >= p.t;
+              kb = keep_entry(xb, p.t, p.square);
             } else if constexpr (MODE == kModeMasked) {
               kb = ((mw[b] >> (k & 31)) & 1u) != 0;
             } else {
@@ -825,7 +834,7 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
             const uint16_t xb = p.x[(int64_t)b * p.d_in + j];
             bool kb;
             if constexpr (MODE == kModeThreshold) {
-              kb = mag_key(xb) != 0 && fabsf(h2f(xb)) >= p.t;
+              kb = keep_entry(xb, p.t, p.square);
             } else if constexpr (MODE == kModeMasked) {
               kb = ((p.xmask[(int64_t)b * words + (j >> 5)] >> (j & 31)) & 1u) != 0;
             } else {
@@ -1240,6 +1249,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   kp.out_nnz = c.out_nnz;
   kp.y = c.y;
   kp.batch = c.batch;
+  kp.square = c.square;
 
   if (kTilings[tiling].full_k) {
     const unsigned grid = (unsigned)((c.d_out + kTilings[tiling].tile_o - 1) /

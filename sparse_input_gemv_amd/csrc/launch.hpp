@@ -40,6 +40,7 @@ struct GemvCall {
   const uint16_t* x = nullptr;
   const uint32_t* xmask = nullptr;
   float t = 0.f;
+  int square = 0;  // threshold mode: keep x_k iff x_k^2 >= t instead of |x_k| >= t
   // lists
   const int32_t* idx = nullptr;
   const uint16_t* val = nullptr;

@@ -30,6 +30,7 @@ __all__ = [
     "LLAMA2_7B_INPUTS",
     "LLAMA2_7B_FUSED",
     "fused_weight_t",
+    "rank_adapter_weights",
     "LLAMA3_8B_MLP",
     "weight_seed",
     "calib_seed",
@@ -98,6 +99,13 @@ def fused_weight_t(name: str) -> np.ndarray:
     members, _ = LLAMA2_7B_FUSED[name]
     return np.concatenate(
         [weight_t(LLAMA2_7B[m][0], LLAMA2_7B[m][1], weight_seed(m)) for m in members], axis=1)
+
+
+def rank_adapter_weights(d_out: int, d_in: int, r: int, seed: int, std: float = 0.02):
+    """Seeded rank-adapter factors as stored: ``(BT[d_in][r], AT[r][d_out])``
+    for ``y = A (m ⊙ B x)`` with ``B`` r x d_in and ``A`` d_out x r, both
+    N(0, std) (the pages give no trained factors)."""
+    return weight_t(r, d_in, seed, std), weight_t(d_out, r, seed + 1, std)
 
 
 def calib_seed(input_name: str) -> int:

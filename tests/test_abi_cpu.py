@@ -130,6 +130,33 @@ def test_gemv_checks(sa):
         assert sa.sa_set_gemm_tuning(rows, engine) == SA_OK
 
 
+def test_rana_adapter_checks(sa):
+    need = max(sa.sa_workspace_bytes(2048, 4096, 1), sa.sa_workspace_bytes(11008, 2048, 1))
+    f = sa.rana_adapter_gemv
+    ok = [P, 2048, 4096, P, 11008, P, 1, 0.5, P, P, P, need, None]
+    args = list(ok)
+    args[1] = 2044  # r % 8
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[4] = 11004  # d_out % 8
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[7] = -1.0
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[11] = need - 1
+    assert f(*args) == SA_ERR_WORKSPACE
+    args = list(ok)
+    args[5] = None  # x
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[8] = P + 2  # v misaligned
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[6] = 0  # empty batch: nothing to do
+    assert f(*args) == SA_OK
+
+
 def test_swiglu_checks(sa):
     need = sa.sa_workspace_bytes(4096, 14336, 1)
     f = sa.masked_swiglu_down

@@ -12,7 +12,7 @@ import torch
 
 import sparse_input_gemv_amd as sa
 import synthetic as syn
-from oracle import calibrate, gemv, sparsify, swiglu
+from oracle import calibrate, gemv, rana, sparsify, swiglu
 
 pytestmark = pytest.mark.gpu
 
@@ -451,6 +451,60 @@ def test_one_launch_handoff_matches_two_launches(tiling):
                 assert torch.equal(a, b), (tiling, shapes[k], j)
     finally:
         sa.set_gemv_tuning(-1, 0, 0)
+
+
+# ---------------------------------------------------------------------------
+# RaNA linear-layer rank adapter A (m ⊙ B x), m_i = v_i^2 >= t
+# ---------------------------------------------------------------------------
+
+def check_adapter(bt, at, X, t, v_g, y_g):
+    """v against the oracle's fp64 B x; y against the oracle run on the
+    GPU's own fp16 v, so both sides take the mask decision on the same
+    values (its square is exact)."""
+    v_g, y_g = v_g.reshape(len(X), -1), y_g.reshape(len(X), -1)
+    for b in range(len(X)):
+        assert_close(v_g[b], rana.adapter_v(bt, X[b]))
+        _, _, keep, y_ref = rana.rank_adapter(bt, at, X[b], t, v16=host(v_g[b]))
+        assert_close(y_g[b], y_ref)
+    return keep
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3])
+@pytest.mark.parametrize("r,d_in,d_out", [(136, 130, 72), (1024, 512, 264), (8, 33, 2056)])
+def test_rana_adapter_small(r, d_in, d_out, batch):
+    bt, at = syn.rank_adapter_weights(d_out, d_in, r, r + d_in, std=0.1)
+    X = syn.gaussian_f16((batch, d_in), 1.0, batch + d_out)
+    for t in (0.0, 0.5, 4.0, 1e6):
+        v_g, y_g = sa.rana_adapter_gemv(dev(bt), dev(at), dev(X), t)
+        check_adapter(bt, at, X, t, v_g, y_g)
+
+
+def test_rana_adapter_exact_square_threshold():
+    """B = A = I (r = d_in = d_out = 64): v = x, y = m ⊙ x.  At t = 0.25 the
+    entries +-0.5 are kept and their fp16 neighbours below 0.5 are not."""
+    eye = np.eye(64, dtype=np.float16)
+    below = np.nextafter(np.float16(0.5), np.float16(0))
+    x = np.tile(np.array([0.5, -0.5, below, -below, 0.0, 2.0, -0.25, 0.75], np.float16), 8)
+    v_g, y_g = sa.rana_adapter_gemv(dev(eye), dev(eye), dev(x), 0.25)
+    assert np.array_equal(host(v_g), x)
+    assert np.array_equal(host(y_g), np.where(x.astype(np.float64) ** 2 >= 0.25, x, 0))
+
+
+def test_rana_adapter_llama_gate():
+    """The gate projection (11008 x 4096) as a rank-2048 adapter at a 50%
+    mask rate (t between the middle order statistics of v^2), batch 1."""
+    bt, at = syn.rank_adapter_weights(11008, 4096, 2048, 3000)
+    x = syn.activation((4096,), "gaussian", 7)
+    v0, _ = sa.rana_adapter_gemv(dev(bt), dev(at), dev(x), 0.0)
+    sq = np.sort(host(v0).astype(np.float64) ** 2)
+    # the nearest split at or above the median between two distinct squares
+    k = next(i for i in range(1024, 2048) if sq[i - 1] < sq[i])
+    t = float(np.float32(0.5 * (sq[k - 1] + sq[k])))
+    assert sq[k - 1] < t < sq[k]
+    v_g, y_g = sa.rana_adapter_gemv(dev(bt), dev(at), dev(x), t)
+    assert np.array_equal(host(v_g), host(v0))  # the first GEMV is deterministic
+    keep = check_adapter(bt, at, x[None], t, v_g, y_g)
+    assert int(keep.sum()) == 2048 - k
 
 
 # ---------------------------------------------------------------------------

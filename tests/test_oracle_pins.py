@@ -14,7 +14,7 @@ import pytest
 from scipy import stats
 
 import synthetic as syn
-from oracle import brute, calibrate, gemv, sparsify, spmm, swiglu
+from oracle import brute, calibrate, gemv, rana, sparsify, spmm, swiglu
 
 
 # --------------------------------------------------------------------------
@@ -264,6 +264,65 @@ def test_fused_projection_is_the_members_side_by_side():
                                        atol=1e-12)
             o += d_out
         assert o == wt.shape[1] == len(y)
+
+
+# --------------------------------------------------------------------------
+# RaNA linear-layer rank adapter
+# --------------------------------------------------------------------------
+
+def test_rank_adapter_t0_is_the_dense_chain_and_large_t_is_zero():
+    """t = 0 keeps every entry: y = A fp16(B x) by numpy's matmul; a
+    threshold above every v_i^2 keeps none: y = 0."""
+    bt, at = syn.weight_t(64, 96, 1), syn.weight_t(40, 64, 2)
+    x = syn.gaussian_f16((96,), 1.0, 3)
+    v, v16, keep, y = rana.rank_adapter(bt, at, x, 0.0)
+    np.testing.assert_allclose(v, x.astype(np.float64) @ bt.astype(np.float64), rtol=1e-12,
+                               atol=1e-14)
+    assert keep.all() and np.array_equal(v16, v.astype(np.float16))
+    np.testing.assert_allclose(y, v16.astype(np.float64) @ at.astype(np.float64), rtol=1e-12,
+                               atol=1e-14)
+    _, _, keep, y = rana.rank_adapter(bt, at, x, 1e6)
+    assert not keep.any() and np.all(y == 0)
+
+
+def test_rank_adapter_mask_at_an_exact_square():
+    """With B = A = I, v = x and y = m ⊙ x.  At t = 0.25 the mask is
+    |x| >= 0.5 exactly: +-0.5 are kept, the fp16 neighbours below are not."""
+    below = float(np.nextafter(np.float16(0.5), np.float16(0)))
+    x = np.array([0.5, -0.5, below, -below, 0.0, 2.0, -0.25, 0.75], dtype=np.float16)
+    eye = np.eye(8, dtype=np.float16)
+    v, v16, keep, y = rana.rank_adapter(eye, eye, x, 0.25)
+    assert np.array_equal(v16, x)
+    assert keep.tolist() == [True, True, False, False, False, True, False, True]
+    assert np.array_equal(y, np.where(keep, x.astype(np.float64), 0.0))
+
+
+def test_rank_adapter_given_v_decides_the_mask():
+    """A v from another implementation (fp16) is masked and multiplied as
+    given; here it differs from the oracle's own rounding by one ulp at one
+    entry placed exactly on the threshold."""
+    bt, at = syn.weight_t(16, 32, 4), syn.weight_t(24, 16, 5)
+    x = syn.gaussian_f16((32,), 1.0, 6)
+    v, v16, _, _ = rana.rank_adapter(bt, at, x, 0.0)
+    other = v16.copy()
+    other[3] = np.nextafter(v16[3], np.float16(np.inf) if v16[3] >= 0 else np.float16(-np.inf))
+    t = float(np.float64(other[3]) ** 2)
+    _, _, keep_o, y_o = rana.rank_adapter(bt, at, x, t, v16=other)
+    assert keep_o[3]
+    idx = np.flatnonzero(keep_o)
+    np.testing.assert_allclose(y_o, other[idx].astype(np.float64) @ at[idx].astype(np.float64),
+                               rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_rank_adapter_matches_scalar_loops(seed):
+    r, d_in, d_out = 12, 20, 9 + seed
+    bt, at = syn.weight_t(r, d_in, 10 + seed, std=0.3), syn.weight_t(d_out, r, 20 + seed)
+    x = syn.gaussian_f16((d_in,), 1.0, 30 + seed)
+    v, v16, keep, y = rana.rank_adapter(bt, at, x, 0.5)
+    assert 0 < keep.sum() < r
+    np.testing.assert_allclose(y, brute.rank_adapter_loop(bt, at, x, 0.5), rtol=1e-12,
+                               atol=1e-13)
 
 
 def test_silu_closed_forms():
