@@ -346,6 +346,8 @@ def run_suite(args):
         suite_matmul(sa, syn, dev, ev_time, emit)
     if section("next2"):
         suite_rank_adapter(sa, syn, dev, ev_time, emit)
+    if section("next3"):
+        suite_corrected(sa, syn, dev, ev_time, emit, rotation)
 
 
 def suite_layer(sa, syn, dev, ev_time, emit, rotation):
@@ -454,6 +456,50 @@ def suite_topk(sa, syn, dev, ev_time, emit, rotation):
         del rot
         torch.cuda.empty_cache()
 
+
+
+def suite_corrected(sa, syn, dev, ev_time, emit, rotation):
+    """Weight-aware selection with the static shift and the variance
+    correction on the down projection (4096 x 11008): the scored sparsifier
+    then the corrected list GEMV, against the plain fused threshold call."""
+    import torch
+
+    d_out, d_in, inp = syn.LLAMA2_7B["down"]
+    _, dist = syn.LLAMA2_7B_INPUTS[inp]
+    rot = rotation(d_out, d_in, syn.weight_seed("down"))
+    nr = len(rot)
+    x = torch.from_numpy(syn.activation((d_in,), dist, 0)).to(dev)
+    mu = torch.from_numpy(syn.gaussian_f16((d_in,), 0.25, 13)).to(dev)
+    cn = sa.weight_col_norms(rot[0])
+    bias = sa.dense_gemv(rot[0], mu)
+    y = torch.empty((d_out,), dtype=torch.float16, device=dev)
+    xs = (x.float() - mu.float()).half().double().abs()
+    sc = torch.sort(xs * cn).values
+    t = float(0.5 * (sc[d_in // 2 - 1] + sc[d_in // 2]))
+    t_plain = float(torch.sort(x.float().abs()).values[d_in // 2])
+    us_p = ev_time(lambda i: sa.sparse_gemv_threshold(rot[i % nr], x, t_plain, y=y), 1000)
+    kept_f = int((sc >= t).sum())
+    us_f = ev_time(lambda i: sa.sparse_gemv_scored(rot[i % nr], x, t, mu=mu, colnorm=cn, var=True,
+                                                   bias=bias, y=y), 1000)
+    emit("next3", f"sparse_gemv_scored down {d_out}x{d_in} weight-aware threshold 50%, shift + "
+         "VAR, one launch", us_f,
+         bytes_=2 * d_out * kept_f + 2 * d_in * 2 + 8 * d_in + 2 * d_out * 2,
+         flops=2 * d_out * kept_f, kept=kept_f, plain_fused_us=round(us_p, 3))
+    for label, (tt, n, m) in (("threshold 50%", (t, 0, 0)), ("8:16", (0.0, 8, 16))):
+        out = sa.act_sparsify_scored(x, t=tt, n=n, m=m, mu=mu, colnorm=cn, with_mask=False)
+        _, idx, val, nnz, alpha = out
+        kept = int(nnz.cpu()[0])
+        us_s = ev_time(lambda i: sa.act_sparsify_scored(x, t=tt, n=n, m=m, mu=mu, colnorm=cn,
+                                                        with_mask=False), 1000)
+        us_g = ev_time(lambda i: sa.sparse_gemv_corrected(rot[i % nr], idx, val, nnz, alpha=alpha,
+                                                          bias=bias, y=y), 1000)
+        emit("next3", f"act_sparsify_scored + sparse_gemv_corrected down {d_out}x{d_in} "
+             f"weight-aware {label}, shift + VAR", us_s + us_g,
+             bytes_=2 * d_out * kept + 6 * kept + 2 * d_in * 2 + 8 * d_in + 2 * d_out * 2,
+             flops=2 * d_out * kept, kept=kept, sparsify_us=round(us_s, 3), gemv_us=round(us_g, 3),
+             plain_fused_us=round(us_p, 3))
+    del rot
+    torch.cuda.empty_cache()
 
 
 def suite_rank_adapter(sa, syn, dev, ev_time, emit):

@@ -123,6 +123,37 @@ int act_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
                     uint32_t* mask, uint16_t* val, void* stream);
 
 /*
+ * act_sparsify_scored -- weight-aware selection with a static shift and the
+ * variance-correction scale.  [NM] section 2 (methodology): entries scored
+ * by the size of the weight they multiply (WT, Amber-Pruner), static
+ * per-token shifts that centre activations (S-PTS), a variance correction
+ * after sparsification that restores the output scale (VAR); section 3 names
+ * S-PTS and VAR the strongest light corrections.  The page gives no
+ * formulas; per row and entry this computes
+ *   x' = fp16(fp32(x) - fp32(mu))          (mu NULL: x' = x)
+ *   score = |x'| * colnorm in fp64        (colnorm NULL: |x'|)
+ *   m == 0: keep iff score >= t and x' != 0
+ *   m  > 0: keep the n largest scores of every m consecutive entries, ties
+ *           to the lower index (exactly n per group)
+ *   alpha = sqrt(sum x'^2 / sum_kept x'^2), 1 when nothing is kept
+ * and writes the kept x' as lists (ascending, as act_sparsify_threshold).
+ * The corrected output is then sparse_gemv_corrected with alpha and the
+ * shift's product W mu as the bias.
+ *
+ *   x       [rows][d] fp16; mu [d] fp16 or NULL; colnorm [d] fp64 or NULL
+ *           (weight_col_norms gives ||W[:, i]||)
+ *   mask    [rows][ceil(d/32)] uint32 or NULL; idx [rows][cap] int32;
+ *           val [rows][cap] fp16 (the shifted values); nnz [rows] int32
+ *   alpha   [rows] fp32 or NULL
+ * Requires t finite >= 0 and cap >= d when m == 0; m in {4,8,16,32},
+ * 1 <= n <= m, d % m == 0 and cap >= d*n/m otherwise.
+ */
+int act_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d, const uint16_t* mu,
+                        const double* colnorm, int n, int m, double t, uint32_t* mask,
+                        int32_t* idx, uint16_t* val, int32_t* nnz, int64_t cap, float* alpha,
+                        void* stream);
+
+/*
  * act_calibrate_threshold -- threshold for a target sparsity from samples.
  * [TEAL] Inference Usage and Accuracy Usage step 1: thresholds come from
  * per-layer activation histograms.  The histogram here has one bin per fp16
@@ -175,6 +206,37 @@ int sparse_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in,
 int sparse_gemv_threshold(const uint16_t* wt, int64_t d_out, int64_t d_in,
                           const uint16_t* x, int64_t batch, float t,
                           uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_gemv_corrected -- sparse_gemv with an output correction:
+ * y[b][o] = fp16(alpha[b] * sum_j W[o][idx[b][j]] * val[b][j] + bias[o]),
+ * one fp32 fused multiply-add.  alpha (fp32 [batch], e.g. the variance
+ * correction of act_sparsify_scored) and bias (fp16 [d_out], e.g. W mu,
+ * the static shift's product, from dense_gemv) may each be NULL.  Other
+ * arguments and errors as sparse_gemv.
+ */
+int sparse_gemv_corrected(const uint16_t* wt, int64_t d_out, int64_t d_in,
+                          const int32_t* idx, const uint16_t* val, const int32_t* nnz,
+                          int64_t batch, int64_t cap, const float* alpha,
+                          const uint16_t* bias, uint16_t* y, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * sparse_gemv_scored -- act_sparsify_scored (threshold kind) and
+ * sparse_gemv_corrected in one launch, for one row:
+ *   x' = fp16(fp32(x) - fp32(mu)), keep iff |x'| * colnorm >= t (fp64) and
+ *   x' != 0, y = fp16(alpha * W (keep .* x') + bias) with alpha the variance
+ *   correction sqrt(sum x'^2 / sum_kept x'^2) when var != 0 (else 1).
+ * Each workgroup decides its own slice of x; the slices' sums reach the
+ * workgroup that finishes each output tile with the partial tiles.
+ *   x [d_in] fp16; mu [d_in] fp16 or NULL; colnorm [d_in] fp64 or NULL;
+ *   bias [d_out] fp16 or NULL (e.g. W mu from dense_gemv); other arguments
+ *   as sparse_gemv_threshold with batch 1.
+ */
+int sparse_gemv_scored(const uint16_t* wt, int64_t d_out, int64_t d_in,
+                       const uint16_t* x, const uint16_t* mu, const double* colnorm,
+                       double t, int var, const uint16_t* bias, uint16_t* y,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /*
  * rana_adapter_gemv -- the RaNA linear-layer rank adapter

@@ -26,6 +26,7 @@ Modules:
 * ``gemv``      sparse / dense / batched-union GEMV; FLOP count
 * ``swiglu``    SiLU, CATS and RaNA neuron masks, masked down projection
 * ``rana``      RaNA linear-layer rank adapter A (m ⊙ B x)
+* ``correct``   weight-aware selection, static shift, variance correction
 * ``spmm``      batched N:M activation-sparse matmul
 * ``calibrate`` empirical-quantile thresholds
 * ``brute``     exhaustive enumeration for tiny inputs
@@ -34,4 +35,4 @@ Every function is pinned by ``tests/test_oracle_*.py`` (run with
 ``-m "not gpu"``); none is "parity unpinned".
 """
 
-from . import brute, calibrate, gemv, rana, sparsify, spmm, swiglu  # noqa: F401
+from . import brute, calibrate, correct, gemv, rana, sparsify, spmm, swiglu  # noqa: F401

@@ -25,6 +25,7 @@ import torch
 __all__ = [
     "SparseActError", "lib", "workspace",
     "act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm",
+    "act_sparsify_scored", "sparse_gemv_corrected", "sparse_gemv_scored",
     "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold", "rana_adapter_gemv",
     "masked_gemv",
     "dense_gemv", "masked_swiglu_down", "weight_col_norms", "nm_act_spmm", "dense_gemm",
@@ -48,6 +49,12 @@ _SIGNATURES = {
     "sa_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "sparse_gemv": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "sparse_gemv_threshold": (_i32, [_vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _sz, _vp]),
+    "act_sparsify_scored": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _f64, _vp, _vp, _vp,
+                                   _vp, _i64, _vp, _vp]),
+    "sparse_gemv_scored": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _f64, _i32, _vp, _vp, _vp, _sz,
+                                  _vp]),
+    "sparse_gemv_corrected": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
+                                     _vp, _sz, _vp]),
     "rana_adapter_gemv": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _f32, _vp, _vp, _vp,
                                  _sz, _vp]),
     "masked_gemv": (_i32, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
@@ -162,6 +169,36 @@ def act_sparsify_threshold(x: torch.Tensor, t: float, with_mask: bool = True, ca
     return mask, idx, val, nnz
 
 
+def act_sparsify_scored(x: torch.Tensor, t: float = 0.0, n: int = 0, m: int = 0,
+                        mu: torch.Tensor | None = None, colnorm: torch.Tensor | None = None,
+                        with_mask: bool = True):
+    """Weight-aware selection of the shifted activation ``x - mu``: a
+    threshold on ``|x'| * colnorm`` (``m == 0``) or ``n`` of every ``m``.
+    Returns ``(mask, idx, val, nnz, alpha)``; see the C declaration."""
+    _dev(x, "x", torch.float16)
+    rows, d = _rows(x)
+    if mu is not None:
+        _dev(mu, "mu", torch.float16)
+        if mu.numel() != d:
+            raise ValueError(f"mu holds {mu.numel()} values, {d} needed")
+    if colnorm is not None:
+        _dev(colnorm, "colnorm", torch.float64)
+        if colnorm.numel() != d:
+            raise ValueError(f"colnorm holds {colnorm.numel()} values, {d} needed")
+    cap = d if m == 0 else d // m * n
+    dev = x.device
+    shape = (rows,) if x.dim() == 2 else ()
+    mask = torch.empty(shape + ((d + 31) // 32,), dtype=torch.int32, device=dev) if with_mask else None
+    idx = torch.empty(shape + (max(cap, 1),), dtype=torch.int32, device=dev)
+    val = torch.empty(shape + (max(cap, 1),), dtype=torch.float16, device=dev)
+    nnz = torch.empty((rows,), dtype=torch.int32, device=dev)
+    alpha = torch.empty((rows,), dtype=torch.float32, device=dev)
+    _check(lib().act_sparsify_scored(_ptr(x), rows, d, _ptr(mu), _ptr(colnorm), int(n), int(m),
+                                     float(t), _ptr(mask), _ptr(idx), _ptr(val), _ptr(nnz),
+                                     max(cap, 1), _ptr(alpha), _stream(x)), "act_sparsify_scored")
+    return mask, idx, val, nnz, alpha
+
+
 def act_sparsify_topk(x: torch.Tensor, k: int, with_mask: bool = True, cap: int | None = None):
     """Returns ``(mask, idx, val, nnz)`` with exactly ``k`` kept per row."""
     _dev(x, "x", torch.float16)
@@ -247,6 +284,58 @@ def sparse_gemv_threshold(wt: torch.Tensor, x: torch.Tensor, t: float,
     _check(lib().sparse_gemv_threshold(_ptr(wt), d_out, d_in, _ptr(x), batch, float(t), _ptr(y),
                                        _ptr(ws), ws.numel(), _stream(wt)), "sparse_gemv_threshold")
     return _ret(y, squeeze)
+
+
+def sparse_gemv_corrected(wt: torch.Tensor, idx: torch.Tensor, val: torch.Tensor,
+                          nnz: torch.Tensor, alpha: torch.Tensor | None = None,
+                          bias: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """``y[b] = alpha[b] * W[:, idx[b]] @ val[b] + bias`` (either may be None)."""
+    _dev(wt, "wt", torch.float16)
+    _dev(idx, "idx", torch.int32)
+    _dev(val, "val", torch.float16)
+    _dev(nnz, "nnz", torch.int32)
+    squeeze = idx.dim() == 1
+    batch, cap = _rows(idx)
+    d_in, d_out = wt.shape
+    if alpha is not None:
+        _dev(alpha, "alpha", torch.float32)
+        if alpha.numel() < batch:
+            raise ValueError(f"alpha holds {alpha.numel()} values, {batch} needed")
+    if bias is not None:
+        _dev(bias, "bias", torch.float16)
+        if bias.numel() != d_out:
+            raise ValueError(f"bias holds {bias.numel()} values, {d_out} needed")
+    y = _gemv_out(wt, batch, squeeze, y)
+    ws = workspace(wt.device, workspace_bytes(d_out, d_in, batch))
+    _check(lib().sparse_gemv_corrected(_ptr(wt), d_out, d_in, _ptr(idx), _ptr(val), _ptr(nnz),
+                                       batch, cap, _ptr(alpha), _ptr(bias), _ptr(y), _ptr(ws),
+                                       ws.numel(), _stream(wt)), "sparse_gemv_corrected")
+    return _ret(y, squeeze)
+
+
+def sparse_gemv_scored(wt: torch.Tensor, x: torch.Tensor, t: float,
+                       mu: torch.Tensor | None = None, colnorm: torch.Tensor | None = None,
+                       var: bool = True, bias: torch.Tensor | None = None,
+                       y: torch.Tensor | None = None):
+    """One launch: shift, weight-aware threshold, sparse GEMV, variance
+    correction and bias, for one row ``x``."""
+    _dev(wt, "wt", torch.float16)
+    _dev(x, "x", torch.float16)
+    d_in, d_out = wt.shape
+    if x.numel() != d_in:
+        raise ValueError(f"x holds {x.numel()} values, {d_in} needed")
+    for name, tt, dt, n in (("mu", mu, torch.float16, d_in), ("colnorm", colnorm, torch.float64, d_in),
+                            ("bias", bias, torch.float16, d_out)):
+        if tt is not None:
+            _dev(tt, name, dt)
+            if tt.numel() != n:
+                raise ValueError(f"{name} holds {tt.numel()} values, {n} needed")
+    y = _gemv_out(wt, 1, True, y)
+    ws = workspace(wt.device, workspace_bytes(d_out, d_in, 1))
+    _check(lib().sparse_gemv_scored(_ptr(wt), d_out, d_in, _ptr(x), _ptr(mu), _ptr(colnorm),
+                                    float(t), int(bool(var)), _ptr(bias), _ptr(y), _ptr(ws),
+                                    ws.numel(), _stream(wt)), "sparse_gemv_scored")
+    return _ret(y, True)
 
 
 def rana_adapter_gemv(bt: torch.Tensor, at: torch.Tensor, x: torch.Tensor, t: float,

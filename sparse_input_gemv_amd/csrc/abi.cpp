@@ -48,6 +48,19 @@ int act_sparsify_threshold(const uint16_t* x, int64_t rows, int64_t d, float t, 
       "act_sparsify_threshold");
 }
 
+int act_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d, const uint16_t* mu,
+                        const double* colnorm, int n, int m, double t, uint32_t* mask,
+                        int32_t* idx, uint16_t* val, int32_t* nnz, int64_t cap, float* alpha,
+                        void* stream) {
+  sa::clear_error();
+  int st = sa::check_scored(x, rows, d, mu, colnorm, n, m, t, mask, idx, val, nnz, cap, alpha);
+  if (st != SA_OK) return st;
+  if (rows == 0) return SA_OK;
+  return hip_status(sa::launch_sparsify_scored(x, rows, d, mu, colnorm, n, m, t, mask, idx, val,
+                                               nnz, alpha, cap, as_stream(stream)),
+                    "act_sparsify_scored");
+}
+
 int act_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k, uint32_t* mask,
                       int32_t* idx, uint16_t* val, int32_t* nnz, int64_t cap, void* stream) {
   sa::clear_error();
@@ -137,6 +150,71 @@ int sparse_gemv_threshold(const uint16_t* wt, int64_t d_out, int64_t d_in, const
   c.ws = ws;
   c.ws_bytes = ws_bytes;
   return run_gemv(c, "sparse_gemv_threshold", stream);
+}
+
+int sparse_gemv_scored(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint16_t* x,
+                       const uint16_t* mu, const double* colnorm, double t, int var,
+                       const uint16_t* bias, uint16_t* y, void* ws, size_t ws_bytes,
+                       void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_out, d_in, 1);
+  int st = sa::check_gemv_common(wt, d_out, d_in, 1, y, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_activation(x, "sparse_gemv_scored: x");
+  if (st == SA_OK && (!(t >= 0.0) || t > 1e300 || (reinterpret_cast<uintptr_t>(mu) & 1u) != 0 ||
+                      (reinterpret_cast<uintptr_t>(colnorm) & 7u) != 0 ||
+                      (reinterpret_cast<uintptr_t>(bias) & 1u) != 0)) {
+    sa::set_error("sparse_gemv_scored: t must be finite and >= 0; mu, colnorm, bias aligned");
+    st = SA_ERR_INVALID_ARG;
+  }
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeScored;
+  c.wt = wt;
+  c.d_out = d_out;
+  c.d_in = d_in;
+  c.batch = 1;
+  c.x = x;
+  c.mu = mu;
+  c.colnorm = colnorm;
+  c.t64 = t;
+  c.var = var != 0;
+  c.bias = bias;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return run_gemv(c, "sparse_gemv_scored", stream);
+}
+
+int sparse_gemv_corrected(const uint16_t* wt, int64_t d_out, int64_t d_in, const int32_t* idx,
+                          const uint16_t* val, const int32_t* nnz, int64_t batch, int64_t cap,
+                          const float* alpha, const uint16_t* bias, uint16_t* y, void* ws,
+                          size_t ws_bytes, void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_out, d_in, batch < 1 ? 1 : batch);
+  int st = sa::check_gemv_common(wt, d_out, d_in, batch, y, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_sparse_gemv(idx, val, nnz, batch, cap);
+  if (st == SA_OK &&
+      ((reinterpret_cast<uintptr_t>(alpha) & 3u) != 0 || (reinterpret_cast<uintptr_t>(bias) & 1u) != 0)) {
+    sa::set_error("sparse_gemv_corrected: misaligned alpha or bias");
+    st = SA_ERR_INVALID_ARG;
+  }
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeList;
+  c.wt = wt;
+  c.d_out = d_out;
+  c.d_in = d_in;
+  c.batch = (int)batch;
+  c.idx = idx;
+  c.val = val;
+  c.nnz = nnz;
+  c.cap = cap;
+  c.alpha = alpha;
+  c.bias = bias;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return run_gemv(c, "sparse_gemv_corrected", stream);
 }
 
 int rana_adapter_gemv(const uint16_t* bt, int64_t r, int64_t d_in, const uint16_t* at,

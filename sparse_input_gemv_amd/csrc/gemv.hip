@@ -121,6 +121,14 @@ struct KParams {
   uint32_t* tickets;  // non-null: one-launch hand-off
   int go, gk, slice;
   int square;  // threshold mode: keep x_k iff x_k^2 >= t (rank-adapter masker)
+  const float* alpha;    // [batch] output scale per row, or null
+  const uint16_t* bias;  // [d_out] fp16 added to every row, or null
+  // scored mode (batch 1): shift, weight norms (colnorm), fp64 threshold
+  // (t64) and, with the variance correction, per-(slice, tile) sums
+  // [gk][go][2] of x'^2 and kept x'^2 (null: no correction)
+  const uint16_t* mu;
+  double* vsum;
+  int var;  // scored mode: apply the variance correction
 };
 
 constexpr int kModeListBatched = 5;  // kModeList with batch > 1
@@ -138,6 +146,39 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bool keep_entry(uint16_t xb, float t, int square) {
   const float v = h2f(xb);
   return square ? v * v >= t : (mag_key(xb) != 0 && fabsf(v) >= t);
+}
+
+// Scored mode, one entry: the shifted value x' = fp16(fp32(x) - fp32(mu))
+// (returned in xb), kept iff |x'| * colnorm >= t in fp64 and x' != 0; its
+// square joins the variance-correction sums.  m and c are the entry's shift
+// and weight norm, loaded with x.
+__device__ __forceinline__ bool scored_keep(const KParams& p, uint16_t& xb, uint16_t m, double c,
+                                            bool in, double& s_all, double& s_kept) {
+  if (p.mu != nullptr) xb = f2h(h2f(xb) - h2f(m));
+  const float v = h2f(xb);
+  const double a = fabs((double)v);
+  const bool kb = in && (p.colnorm != nullptr ? a * c : a) >= p.t64 && v != 0.f;
+  const double q = (double)v * (double)v;
+  s_all += in ? q : 0.0;
+  s_kept += kb ? q : 0.0;
+  return kb;
+}
+
+// The variance correction from the sums: sqrt(all / kept), 1 if none kept.
+__device__ __forceinline__ float var_alpha(double all, double kept) {
+  return kept > 0.0 ? (float)sqrt(all / kept) : 1.f;
+}
+
+// One output value: the fp32 sum, scaled by its row's alpha and shifted by its
+// output's bias when the call gives them (the corrected GEMV: variance
+// correction and the static shift's product), rounded to fp16.  Without
+// either it is the plain rounding, bit for bit.
+__device__ __forceinline__ uint16_t finish(float acc, const float* alpha, const uint16_t* bias,
+                                           int b, int64_t o) {
+  if (alpha == nullptr && bias == nullptr) return f2h(acc);
+  const float a = alpha != nullptr ? alpha[b] : 1.f;
+  const float c = bias != nullptr ? h2f(bias[o]) : 0.f;
+  return f2h(fmaf(acc, a, c));
 }
 
 // Slot of this thread in a chunk compaction (ascending thread order) and the
@@ -201,8 +242,8 @@ __device__ __forceinline__ void wait_stores() {
 // consecutive outputs of one slice group, so each load is one wave-uniform
 // address plus the lane: whole lines per wave and few address registers.
 template <int TILE_O, int NT, int B>
-__device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0,
-                                               unsigned char* smem) {
+__device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0, unsigned char* smem,
+                                               const float* alpha) {
   constexpr int G = kReduceGroups;
   constexpr int PAIRS = G * TILE_O;
   constexpr int PP = (PAIRS + NT - 1) / NT;  // pairs per thread
@@ -254,7 +295,7 @@ __device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0,
         float acc = red[oo];
 #pragma unroll
         for (int gg = 1; gg < G; ++gg) acc += red[gg * TILE_O + oo];
-        p.y[(int64_t)b * p.d_out + og] = f2h(acc);
+        p.y[(int64_t)b * p.d_out + og] = finish(acc, alpha, p.bias, b, og);
       }
     }
     __syncthreads();
@@ -309,6 +350,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
 
   // ---------------- phase 1: kept rows of this workgroup -> LDS ----------
   int cnt = 0;
+  double s_all = 0.0, s_kept = 0.0;  // scored mode: variance-correction sums
   const int64_t slice_k0 = (int64_t)kblk * SL;
   const int64_t slice_span = (slice_k0 + SL < p.d_in ? slice_k0 + SL : p.d_in) - slice_k0;
   if constexpr (MODE == kModeList) {
@@ -387,6 +429,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     const int nch = (int)((slice_span + NT - 1) / NT);  // chunks this slice has
     uint16_t xr[PC][B];
     uint32_t mw[PC][B];
+    uint16_t ms[PC];  // scored: shift
+    double cs[PC];    // scored: weight norm
 #pragma unroll
     for (int c = 0; c < PC; ++c) {
       if (c > 0 && c >= nch) break;
@@ -397,6 +441,10 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         const int64_t bb = b < p.batch ? b : 0;
         xr[c][b] = p.x[bb * p.d_in + kc];
         if constexpr (MODE == kModeMasked) mw[c][b] = p.xmask[bb * words + (kc >> 5)];
+      }
+      if constexpr (MODE == kModeScored) {
+        ms[c] = p.mu != nullptr ? p.mu[kc] : (uint16_t)0;
+        cs[c] = p.colnorm != nullptr ? p.colnorm[kc] : 1.0;
       }
     }
     const int w = tid / kWave;
@@ -411,7 +459,9 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       for (int b = 0; b < B; ++b) {
         const uint16_t xb = xr[c][b];
         bool kb = false;
-        if (b < p.batch && k < k1) {
+        if constexpr (MODE == kModeScored) {
+          kb = scored_keep(p, xr[c][b], ms[c], cs[c], b < p.batch && k < k1, s_all, s_kept);
+        } else if (b < p.batch && k < k1) {
           if constexpr (MODE == kModeThreshold) {
             kb = keep_entry(xb, p.t, p.square);
           } else if constexpr (MODE == kModeMasked) {
@@ -471,17 +521,29 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         const int64_t kc = in ? k : k0;
         uint16_t xr[B];
         uint32_t mw[B];
+        uint16_t ms = 0;  // scored: shift and weight norm
+        double cs = 1.0;
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           const int64_t bb = b < p.batch ? b : 0;
           xr[b] = p.x[bb * p.d_in + kc];
           if constexpr (MODE == kModeMasked) mw[b] = p.xmask[bb * words + (kc >> 5)];
         }
+        if constexpr (MODE == kModeScored) {
+          if (p.mu != nullptr) ms = p.mu[kc];
+          if (p.colnorm != nullptr) cs = p.colnorm[kc];
+        }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           vb[b] = 0.f;
           hb[b] = 0;
-          if (b < p.batch && in) {
+          if constexpr (MODE == kModeScored) {
+            if (scored_keep(p, xr[b], ms, cs, in && b < p.batch, s_all, s_kept)) {
+              vb[b] = h2f(xr[b]);
+              hb[b] = xr[b];
+              any = true;
+            }
+          } else if (b < p.batch && in) {
             const uint16_t xb = xr[b];
             bool kb;
             if constexpr (MODE == kModeThreshold) {
@@ -540,6 +602,48 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     if (tid < B) lvh[tid * SLH + cnt] = 0;  // the pad after the last kept entry
     __syncthreads();
   }
+
+  // Scored mode with the variance correction: this slice's sums of x'^2 and
+  // kept x'^2.  One slice is the whole input: alpha now.  Otherwise the sums
+  // go beside this workgroup's partial (written before its ticket, so the
+  // tile's last workgroup reads every slice's sums with the partials).
+  __shared__ float s_alpha;
+  if constexpr (MODE == kModeScored) {
+    if (p.var) {
+      __shared__ double vred[2][NT / kWave];
+#pragma unroll
+      for (int off = kWave / 2; off >= 1; off >>= 1) {
+        s_all += __shfl_xor(s_all, off, kWave);
+        s_kept += __shfl_xor(s_kept, off, kWave);
+      }
+      if (lane_id() == 0) {
+        vred[0][tid / kWave] = s_all;
+        vred[1][tid / kWave] = s_kept;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        double a = 0.0, k = 0.0;
+        for (int i = 0; i < NT / kWave; ++i) {
+          a += vred[0][i];
+          k += vred[1][i];
+        }
+        if (p.gk == 1) {
+          s_alpha = var_alpha(a, k);
+        } else {
+          double* dst = p.vsum + ((int64_t)kblk * p.go + oblk) * 2;
+          if (p.tickets != nullptr) {
+            store_coherent(dst, a);
+            store_coherent(dst + 1, k);
+          } else {
+            dst[0] = a;
+            dst[1] = k;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const float* alpha_out = (MODE == kModeScored && p.var) ? &s_alpha : p.alpha;
 
   // ---------------- phase 2: stream the kept rows --------------------------
   const int o_lane = tid % OL;
@@ -666,7 +770,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       if (og < p.d_out) {
         float* dst = p.part + ((int64_t)kblk * B + b) * p.d_out + og;
         if (single)
-          p.y[(int64_t)b * p.d_out + og] = f2h(s);
+          p.y[(int64_t)b * p.d_out + og] = finish(s, alpha_out, p.bias, b, og);
         else if (handoff)
           store_coherent(dst, s);
         else
@@ -689,7 +793,38 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   }
   __syncthreads();
   if (s_last == 0) return;
-  handoff_reduce<TILE_O, NT, B>(p, o0, smem);
+  if constexpr (MODE == kModeScored) {
+    if (p.var) {
+      // every slice's sums for this tile (written before their tickets)
+      double a = 0.0, k = 0.0;
+      for (int kk = tid; kk < p.gk; kk += NT) {
+        const double* src = p.vsum + ((int64_t)kk * p.go + oblk) * 2;
+        a += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        k += __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __shared__ double vr2[2][NT / kWave];
+#pragma unroll
+      for (int off = kWave / 2; off >= 1; off >>= 1) {
+        a += __shfl_xor(a, off, kWave);
+        k += __shfl_xor(k, off, kWave);
+      }
+      if (lane_id() == 0) {
+        vr2[0][tid / kWave] = a;
+        vr2[1][tid / kWave] = k;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        double ta = 0.0, tk = 0.0;
+        for (int i = 0; i < NT / kWave; ++i) {
+          ta += vr2[0][i];
+          tk += vr2[1][i];
+        }
+        s_alpha = var_alpha(ta, tk);
+      }
+      __syncthreads();
+    }
+  }
+  handoff_reduce<TILE_O, NT, B>(p, o0, smem, alpha_out);
   if constexpr (MODE == kModeSwiglu) {
     if (oblk == 0 && p.out_nnz != nullptr) {
       int c = 0;
@@ -713,11 +848,45 @@ template <int B>
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int gk,
                                                 int64_t d_out, uint16_t* __restrict__ y,
                                                 const int32_t* __restrict__ slice_cnt,
-                                                int32_t* __restrict__ out_nnz) {
+                                                int32_t* __restrict__ out_nnz,
+                                                const float* __restrict__ alpha,
+                                                const uint16_t* __restrict__ bias,
+                                                const double* __restrict__ vsum, int go) {
   constexpr int C = 16, G = kReduceGroups, kLoads = 16;
   __shared__ f4v red[G][C];
   __shared__ int scan[256 / kWave];
+  __shared__ float s_alpha;
   const int tid = (int)threadIdx.x;
+  if (vsum != nullptr) {
+    // the variance correction of the (single) row from every slice's sums
+    // (tile 0's copies; every tile's are the same)
+    __shared__ double vr[2][256 / kWave];
+    double a = 0.0, k = 0.0;
+    for (int kk = tid; kk < gk; kk += 256) {
+      a += vsum[(int64_t)kk * go * 2];
+      k += vsum[(int64_t)kk * go * 2 + 1];
+    }
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+      a += __shfl_xor(a, off, kWave);
+      k += __shfl_xor(k, off, kWave);
+    }
+    if (lane_id() == 0) {
+      vr[0][tid / kWave] = a;
+      vr[1][tid / kWave] = k;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double ta = 0.0, tk = 0.0;
+      for (int i = 0; i < 256 / kWave; ++i) {
+        ta += vr[0][i];
+        tk += vr[1][i];
+      }
+      s_alpha = var_alpha(ta, tk);
+    }
+    __syncthreads();
+    alpha = &s_alpha;
+  }
   const int c = tid % C;
   const int g = tid / C;
   const int b = (int)blockIdx.y;
@@ -746,7 +915,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, 
     for (int gg = 1; gg < G; ++gg) acc += red[gg][c];
     uint16_t* yo = y + (int64_t)b * d_out + o4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) yo[i] = f2h(acc[i]);
+    for (int i = 0; i < 4; ++i) yo[i] = finish(acc[i], alpha, bias, b, o4 + i);
   }
   if (out_nnz != nullptr && blockIdx.x == 0 && b == 0) {
     int cnt = 0;
@@ -802,6 +971,7 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
   int kept_count = 0;  // SwiGLU: kept entries seen by this thread (sub 0 only)
+  double s_all = 0.0, s_kept = 0.0;  // scored: variance-correction sums (sub 0 only)
 
   for (int64_t j0 = rl; j0 < n; j0 += (int64_t)RL * U) {
     int64_t row[U];
@@ -827,6 +997,17 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
         float hv = 0.f;
         keep[q] = in && swiglu_keep(p.g[j], p.u[j], p.colnorm, j, p.swiglu_mode, p.t64, hv);
         v[q][0] = hv;
+      } else if constexpr (MODE == kModeScored) {
+        const int64_t jc = in ? j : 0;
+        uint16_t xb = p.x[jc];
+        double a = 0.0, k = 0.0;
+        keep[q] = scored_keep(p, xb, p.mu != nullptr ? p.mu[jc] : (uint16_t)0,
+                              p.colnorm != nullptr ? p.colnorm[jc] : 1.0, in, a, k);
+        v[q][0] = keep[q] ? h2f(xb) : 0.f;
+        if (sub == 0) {
+          s_all += a;
+          s_kept += k;
+        }
       } else {
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -908,7 +1089,31 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
       if (lane == 0) wcnt[wv] = c;
     }
   }
+  __shared__ float s_alpha;
+  __shared__ double vred[2][NW];
+  const bool var = MODE == kModeScored && p.var != 0;
+  if (var) {
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+      s_all += __shfl_xor(s_all, off, kWave);
+      s_kept += __shfl_xor(s_kept, off, kWave);
+    }
+    if (lane == 0) {
+      vred[0][wv] = s_all;
+      vred[1][wv] = s_kept;
+    }
+  }
   __syncthreads();
+  if (var && tid == 0) {
+    double a = 0.0, k = 0.0;
+    for (int g = 0; g < NW; ++g) {
+      a += vred[0][g];
+      k += vred[1][g];
+    }
+    s_alpha = var_alpha(a, k);
+  }
+  if (var) __syncthreads();
+  const float* alpha_out = var ? &s_alpha : p.alpha;
   for (int e = tid; e < TO * B; e += NT) {
     const int b = e / TO;
     const int oo = e % TO;
@@ -917,7 +1122,7 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
       float s = red[0][b][oo];
 #pragma unroll
       for (int g = 1; g < NW; ++g) s += red[g][b][oo];
-      p.y[(int64_t)b * p.d_out + og] = f2h(s);
+      p.y[(int64_t)b * p.d_out + og] = finish(s, alpha_out, p.bias, b, og);
     }
   }
   if constexpr (MODE == kModeSwiglu) {
@@ -960,7 +1165,7 @@ int batch_pad(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ?
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t ticket_off, slicecnt_off, part_off, total;
+  size_t ticket_off, slicecnt_off, part_off, vsum_off, total;
 };
 
 // Workspace: the hand-off counters (a fixed region, zero between calls: the
@@ -973,7 +1178,10 @@ Layout ws_layout(int64_t d_out, int64_t d_in, int64_t batch) {
   L.ticket_off = 0;
   L.slicecnt_off = kTicketBytes;
   L.part_off = L.slicecnt_off + align256((size_t)gk_max * 4);
-  L.total = L.part_off + (size_t)gk_max * (size_t)batch_pad((int)batch) * (size_t)d_out * 4;
+  L.vsum_off = L.part_off + align256((size_t)gk_max * (size_t)batch_pad((int)batch) *
+                                     (size_t)d_out * 4);
+  const size_t go_max = (size_t)((d_out + kMinSplitTileO - 1) / kMinSplitTileO);
+  L.total = L.vsum_off + (size_t)gk_max * go_max * 2 * sizeof(double);
   return L;
 }
 
@@ -1051,6 +1259,7 @@ KFn select_kernel(int mode, int tiling, int B) {
     case kModeList: return kernel_tiling<kModeList, 1>(tiling);
     case kModeListBatched: return kernel_batch<kModeListBatched>(tiling, B);
     case kModeSwiglu: return kernel_tiling<kModeSwiglu, 1>(tiling);
+    case kModeScored: return kernel_tiling<kModeScored, 1>(tiling);
     default: return nullptr;
   }
 }
@@ -1173,19 +1382,19 @@ hipError_t launch_reduce(const KParams& kp, const Plan& pl, int B, bool with_nnz
   switch (B) {
     case 1:
       hipLaunchKernelGGL(k_reduce<1>, grid, dim3(256), 0, s, kp.part, pl.gk, kp.d_out, kp.y,
-                         kp.slice_cnt, nnz_out);
+                         kp.slice_cnt, nnz_out, kp.alpha, kp.bias, kp.vsum, kp.go);
       break;
     case 2:
       hipLaunchKernelGGL(k_reduce<2>, grid, dim3(256), 0, s, kp.part, pl.gk, kp.d_out, kp.y,
-                         kp.slice_cnt, nnz_out);
+                         kp.slice_cnt, nnz_out, kp.alpha, kp.bias, kp.vsum, kp.go);
       break;
     case 4:
       hipLaunchKernelGGL(k_reduce<4>, grid, dim3(256), 0, s, kp.part, pl.gk, kp.d_out, kp.y,
-                         kp.slice_cnt, nnz_out);
+                         kp.slice_cnt, nnz_out, kp.alpha, kp.bias, kp.vsum, kp.go);
       break;
     default:
       hipLaunchKernelGGL(k_reduce<8>, grid, dim3(256), 0, s, kp.part, pl.gk, kp.d_out, kp.y,
-                         kp.slice_cnt, nnz_out);
+                         kp.slice_cnt, nnz_out, kp.alpha, kp.bias, kp.vsum, kp.go);
       break;
   }
   return hipGetLastError();
@@ -1250,6 +1459,10 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   kp.y = c.y;
   kp.batch = c.batch;
   kp.square = c.square;
+  kp.alpha = c.alpha;
+  kp.bias = c.bias;
+  kp.mu = c.mu;
+  kp.var = (mode == kModeScored && c.var) ? 1 : 0;
 
   if (kTilings[tiling].full_k) {
     const unsigned grid = (unsigned)((c.d_out + kTilings[tiling].tile_o - 1) /
@@ -1266,6 +1479,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
                       : dispatch_fk<kModeMasked, 2>(kp, tiling, grid, s);
       case kModeList: return dispatch_fk<kModeList, 1>(kp, tiling, grid, s);
       case kModeSwiglu: return dispatch_fk<kModeSwiglu, 1>(kp, tiling, grid, s);
+      case kModeScored: return dispatch_fk<kModeScored, 1>(kp, tiling, grid, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1277,6 +1491,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   unsigned char* ws = static_cast<unsigned char*>(c.ws);
   kp.slice_cnt = ws ? reinterpret_cast<int32_t*>(ws + L.slicecnt_off) : nullptr;
   kp.part = ws ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
+  kp.vsum = (kp.var && ws) ? reinterpret_cast<double*>(ws + L.vsum_off) : nullptr;
   // one launch for batch 1 and 2; at batch 4 and 8 the last workgroup's sum
   // over B rows costs more than a second launch (measured)
   const bool one_launch =

@@ -12,6 +12,10 @@ namespace sa {
 hipError_t launch_sparsify_threshold(const uint16_t* x, int64_t rows, int64_t d, float t,
                                      uint32_t* mask, int32_t* idx, uint16_t* val,
                                      int32_t* nnz, int64_t cap, hipStream_t s);
+hipError_t launch_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d,
+                                  const uint16_t* mu, const double* colnorm, int n, int m,
+                                  double t, uint32_t* mask, int32_t* idx, uint16_t* val,
+                                  int32_t* nnz, float* alpha, int64_t cap, hipStream_t s);
 hipError_t launch_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k,
                                 uint32_t* mask, int32_t* idx, uint16_t* val, int32_t* nnz,
                                 int64_t cap, hipStream_t s);
@@ -29,6 +33,7 @@ enum GemvMode : int {
   kModeMasked = 2,     // x + bitmask
   kModeList = 3,       // idx/val/nnz lists
   kModeSwiglu = 4,     // CATS / RaNA masked SwiGLU down
+  kModeScored = 6,     // x + shift + weight norms: weight-aware threshold (batch 1)
 };
 
 struct GemvCall {
@@ -41,6 +46,8 @@ struct GemvCall {
   const uint32_t* xmask = nullptr;
   float t = 0.f;
   int square = 0;  // threshold mode: keep x_k iff x_k^2 >= t instead of |x_k| >= t
+  const uint16_t* mu = nullptr;  // scored mode: static shift [d_in] (or none)
+  int var = 0;                   // scored mode: apply the variance correction
   // lists
   const int32_t* idx = nullptr;
   const uint16_t* val = nullptr;
@@ -54,6 +61,9 @@ struct GemvCall {
   int swiglu_mode = 0;
   uint32_t* out_mask = nullptr;
   int32_t* out_nnz = nullptr;
+  // output correction (null: none): y[b][o] = alpha[b] * sum + bias[o]
+  const float* alpha = nullptr;
+  const uint16_t* bias = nullptr;
   // output and scratch
   uint16_t* y = nullptr;
   void* ws = nullptr;

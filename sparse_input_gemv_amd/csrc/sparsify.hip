@@ -100,6 +100,112 @@ __global__ __launch_bounds__(NT) void k_sparsify_threshold(
   if (threadIdx.x == 0) nnz[row] = base;
 }
 
+// Weight-aware selection with a static shift (the flexible N:M
+// activation-sparsity summary, section 2: WT and Amber-Pruner score entries
+// by the weight they multiply; S-PTS shifts activations towards zero; VAR
+// restores the output scale).  Per row, per entry:
+//   x' = fp16(fp32(x) - fp32(mu))   (mu null: x' = x)
+//   score = |x'| * c in fp64         (c null: |x'|; the fp64 product is
+//                                     correctly rounded, one operation)
+//   M == 0: keep iff score >= t and x' != 0
+//   M  > 0: keep the n largest scores of every M consecutive entries, ties to
+//           the lower index (n rounds of taking each group's largest score
+//           not yet taken; groups lie inside one thread's run, E % M == 0)
+// The kept x' are compacted as the threshold sparsifier does.  alpha[row] =
+// sqrt(sum x'^2 / sum_kept x'^2) (1 when nothing is kept), in fp64.
+template <int NT, int E, int M>
+__global__ __launch_bounds__(NT) void k_sparsify_scored(
+    const uint16_t* __restrict__ x, int64_t d, const uint16_t* __restrict__ mu,
+    const double* __restrict__ cn, double t, int n, uint32_t* __restrict__ mask,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int32_t* __restrict__ nnz,
+    float* __restrict__ alpha, int64_t cap, int vec, int vec_mu) {
+  static_assert(M == 0 || E % M == 0, "groups inside one run");
+  __shared__ int scan[NT / kWave];
+  __shared__ double sums[2][NT / kWave];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * d;
+  int32_t* ir = idx + row * cap;
+  uint16_t* vr = val + row * cap;
+  uint32_t* mr = mask ? mask + row * ((d + 31) >> 5) : nullptr;
+  int base = 0;
+  double s_all = 0.0, s_kept = 0.0;
+  for (int64_t c0 = 0; c0 < d; c0 += (int64_t)NT * E) {
+    const int64_t k0 = c0 + (int64_t)threadIdx.x * E;
+    uint16_t v[E];
+    load_run<E>(xr, k0, d, vec != 0, v);
+    if (mu != nullptr) {
+      uint16_t m[E];
+      load_run<E>(mu, k0, d, vec_mu != 0, m);
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[e] = (k0 + e < d) ? f2h(h2f(v[e]) - h2f(m[e])) : (uint16_t)0;
+    }
+    double sc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double a = fabs((double)h2f(v[e]));
+      sc[e] = (k0 + e < d) ? (cn != nullptr ? a * cn[k0 + e] : a) : 0.0;
+    }
+    uint64_t bits = 0;
+    if constexpr (M == 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool keep = (k0 + e < d) && sc[e] >= t && h2f(v[e]) != 0.f;
+        bits |= (uint64_t)keep << e;
+      }
+    } else {
+      // n rounds; each takes, in every group, the largest score not yet
+      // taken (strict >, scanning upwards: ties go to the lower index)
+      for (int it = 0; it < n; ++it) {
+#pragma unroll
+        for (int g = 0; g < E / M; ++g) {
+          int best = g * M;
+          double bs = -1.0;  // scores are >= 0
+#pragma unroll
+          for (int j = 0; j < M; ++j) {
+            const int e = g * M + j;
+            const bool take = ((bits >> e) & 1ull) == 0 && sc[e] > bs;
+            bs = take ? sc[e] : bs;
+            best = take ? e : best;
+          }
+          bits |= 1ull << best;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (k0 + e >= d) bits &= ~(1ull << e);  // groups past the row end
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double q = (double)h2f(v[e]) * (double)h2f(v[e]);
+      s_all += (k0 + e < d) ? q : 0.0;
+      s_kept += ((bits >> e) & 1ull) ? q : 0.0;
+    }
+    compact_run<NT, E>(bits, v, k0, d, base, scan, ir, vr, mr);
+  }
+  if (alpha != nullptr) {
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      s_all += __shfl_xor(s_all, o, kWave);
+      s_kept += __shfl_xor(s_kept, o, kWave);
+    }
+    const int w = (int)threadIdx.x / kWave;
+    if (lane_id() == 0) {
+      sums[0][w] = s_all;
+      sums[1][w] = s_kept;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double a = 0.0, k = 0.0;
+      for (int i = 0; i < NT / kWave; ++i) {
+        a += sums[0][i];
+        k += sums[1][i];
+      }
+      alpha[row] = k > 0.0 ? (float)sqrt(a / k) : 1.f;
+    }
+  }
+  if (threadIdx.x == 0) nnz[row] = base;
+}
+
 // Wave 0 helper for the radix select: given per-lane counts of consecutive
 // bins (lane l holds bins P*l .. P*l+P-1, ascending), find the largest bin b
 // whose suffix count S(b) = sum_{b' >= b} + extra reaches k; also return
@@ -372,6 +478,31 @@ hipError_t launch_sparsify_threshold(const uint16_t* x, int64_t rows, int64_t d,
   const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && (d % 8) == 0) ? 1 : 0;
   hipLaunchKernelGGL((k_sparsify_threshold<kSparsifyThreads, 16>), dim3((unsigned)rows),
                      dim3(kSparsifyThreads), 0, s, x, d, t, mask, idx, val, nnz, cap, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d,
+                                  const uint16_t* mu, const double* colnorm, int n, int m,
+                                  double t, uint32_t* mask, int32_t* idx, uint16_t* val,
+                                  int32_t* nnz, float* alpha, int64_t cap, hipStream_t s) {
+  const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && (d % 8) == 0) ? 1 : 0;
+  const int vec_mu = ((reinterpret_cast<uintptr_t>(mu) & 15u) == 0) ? 1 : 0;
+  const dim3 grid((unsigned)rows);
+  // Groups of 32 need runs of 32 fp64 scores per thread: 256-thread
+  // workgroups (one wave per SIMD, up to 512 registers) hold them without
+  // spilling; the other kinds fit the 128 registers of 1024 threads.
+#define SA_SCORED(NT, E, M)                                                                  \
+  hipLaunchKernelGGL((k_sparsify_scored<NT, E, M>), grid, dim3(NT), 0, s, x, d, mu, colnorm, t, \
+                     n, mask, idx, val, nnz, alpha, cap, vec, vec_mu)
+  switch (m) {
+    case 0: SA_SCORED(kSparsifyThreads, 16, 0); break;
+    case 4: SA_SCORED(kSparsifyThreads, 16, 4); break;
+    case 8: SA_SCORED(kSparsifyThreads, 16, 8); break;
+    case 16: SA_SCORED(kSparsifyThreads, 16, 16); break;
+    case 32: SA_SCORED(256, 32, 32); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SA_SCORED
   return hipGetLastError();
 }
 

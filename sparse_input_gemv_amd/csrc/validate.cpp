@@ -74,6 +74,32 @@ int check_threshold(const void* x, int64_t rows, int64_t d, float t, const void*
   return SA_OK;
 }
 
+int check_scored(const void* x, int64_t rows, int64_t d, const void* mu, const void* colnorm,
+                 int n, int m, double t, const void* mask, const void* idx, const void* val,
+                 const void* nnz, int64_t cap, const void* alpha) {
+  const char* fn = "act_sparsify_scored";
+  int st = check_rows_d(rows, d, fn);
+  if (st) return st;
+  st = check_list_outputs(x, mask, idx, val, nnz, fn);
+  if (st) return st;
+  REQUIRE(aligned(mu, 2) && aligned(colnorm, 8) && aligned(alpha, 4), SA_ERR_INVALID_ARG,
+          "%s: misaligned mu, colnorm or alpha", fn);
+  if (m == 0) {
+    REQUIRE(isfinite(t) && t >= 0.0, SA_ERR_INVALID_ARG, "%s: t must be finite and >= 0", fn);
+    REQUIRE(cap >= d, SA_ERR_INVALID_ARG, "%s: cap (%lld) must be >= d (%lld)", fn,
+            (long long)cap, (long long)d);
+  } else {
+    REQUIRE(m == 4 || m == 8 || m == 16 || m == 32, SA_ERR_INVALID_ARG,
+            "%s: m must be 0 (threshold), 4, 8, 16 or 32 (got %d)", fn, m);
+    REQUIRE(n >= 1 && n <= m, SA_ERR_INVALID_ARG, "%s: n must be in [1, m] (got %d)", fn, n);
+    REQUIRE(d % m == 0, SA_ERR_INVALID_ARG, "%s: d (%lld) must be a multiple of m", fn,
+            (long long)d);
+    REQUIRE(cap >= d / m * n, SA_ERR_INVALID_ARG, "%s: cap (%lld) must be >= d*n/m", fn,
+            (long long)cap);
+  }
+  return SA_OK;
+}
+
 int check_topk(const void* x, int64_t rows, int64_t d, int64_t k, const void* mask,
                const void* idx, const void* val, const void* nnz, int64_t cap) {
   const char* fn = "act_sparsify_topk";

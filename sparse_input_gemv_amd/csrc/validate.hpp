@@ -18,6 +18,9 @@ constexpr int64_t kMaxDIn = (int64_t)1 << 30;
 
 int check_threshold(const void* x, int64_t rows, int64_t d, float t, const void* mask,
                     const void* idx, const void* val, const void* nnz, int64_t cap);
+int check_scored(const void* x, int64_t rows, int64_t d, const void* mu, const void* colnorm,
+                 int n, int m, double t, const void* mask, const void* idx, const void* val,
+                 const void* nnz, int64_t cap, const void* alpha);
 int check_topk(const void* x, int64_t rows, int64_t d, int64_t k, const void* mask,
                const void* idx, const void* val, const void* nnz, int64_t cap);
 int check_nm(const void* x, int64_t rows, int64_t d, int n, int m, const void* mask,

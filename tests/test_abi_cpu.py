@@ -130,6 +130,62 @@ def test_gemv_checks(sa):
         assert sa.sa_set_gemm_tuning(rows, engine) == SA_OK
 
 
+def test_scored_and_corrected_checks(sa):
+    f = sa.act_sparsify_scored
+    ok = [P, 1, 64, None, None, 0, 0, 0.5, P, P, P, P, 64, None, None]  # never called as is
+    args = list(ok)
+    args[7] = -1.0
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[5], args[6] = 2, 6  # m not supported
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[2], args[5], args[6] = 60, 2, 8  # d % m
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[5], args[6], args[12] = 8, 16, 31  # cap < d*n/m = 32
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[4] = P + 4  # colnorm not 8-byte aligned
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[1] = 0
+    assert f(*args) == SA_OK
+    g = sa.sparse_gemv_corrected
+    need = sa.sa_workspace_bytes(4096, 11008, 1)
+    okg = [P, 4096, 11008, P, P, P, 1, 11008, None, None, P, P, need, None]
+    args = list(okg)
+    args[8] = P + 2  # alpha misaligned
+    assert g(*args) == SA_ERR_INVALID_ARG
+    args = list(okg)
+    args[12] = need - 1
+    assert g(*args) == SA_ERR_WORKSPACE
+    args = list(okg)
+    args[6] = 0
+    assert g(*args) == SA_OK
+
+
+def test_scored_gemv_checks(sa):
+    need = sa.sa_workspace_bytes(4096, 11008, 1)
+    f = sa.sparse_gemv_scored
+    ok = [P, 4096, 11008, P, None, None, 0.5, 1, None, P, P, need, None]  # never called as is
+    args = list(ok)
+    args[6] = -0.5
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[6] = float("nan")
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[5] = P + 4  # colnorm not 8-byte aligned
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[11] = need - 1
+    assert f(*args) == SA_ERR_WORKSPACE
+    args = list(ok)
+    args[3] = None
+    assert f(*args) == SA_ERR_INVALID_ARG
+
+
 def test_rana_adapter_checks(sa):
     need = max(sa.sa_workspace_bytes(2048, 4096, 1), sa.sa_workspace_bytes(11008, 2048, 1))
     f = sa.rana_adapter_gemv

@@ -12,7 +12,7 @@ import torch
 
 import sparse_input_gemv_amd as sa
 import synthetic as syn
-from oracle import calibrate, gemv, rana, sparsify, swiglu
+from oracle import calibrate, correct, gemv, rana, sparsify, swiglu
 
 pytestmark = pytest.mark.gpu
 
@@ -451,6 +451,104 @@ def test_one_launch_handoff_matches_two_launches(tiling):
                 assert torch.equal(a, b), (tiling, shapes[k], j)
     finally:
         sa.set_gemv_tuning(-1, 0, 0)
+
+
+# ---------------------------------------------------------------------------
+# weight-aware selection, static shift (S-PTS), variance correction (VAR)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nm", [(0, 0), (2, 4), (4, 8), (8, 16), (16, 32)])
+@pytest.mark.parametrize("d,rows", [(64, 1), (1024, 3), (4096, 2), (11008, 1), (40000, 2)])
+@pytest.mark.parametrize("shifted,weighted", [(False, False), (True, False), (True, True)])
+def test_scored_sparsify(d, rows, nm, shifted, weighted):
+    n, m = nm
+    X = syn.laplace_f16((rows, d), 1.0, d + rows + m)
+    X[0, ::11] = np.float16(0.5)  # ties
+    mu = syn.gaussian_f16((d,), 0.25, d) if shifted else None
+    cn = correct.column_norms(syn.weight_t(16, d, 3)) if weighted else None
+    t = 0.7 if not weighted else 0.7 * float(np.median(cn))
+    g = sa.act_sparsify_scored(dev(X), t=t, n=n, m=m, mu=None if mu is None else dev(mu),
+                               colnorm=None if cn is None else torch.from_numpy(cn).to(DEV))
+    mask_g, idx_g, val_g, nnz_g, alpha_g = g
+    XS = np.stack([correct.shift(X[r], mu) for r in range(rows)])
+    keep = np.stack([correct.threshold_keep(XS[r], cn, t) if m == 0 else
+                     correct.nm_keep(XS[r], cn, n, m) for r in range(rows)])
+    check_lists(mask_g, idx_g, val_g, nnz_g, XS, keep)
+    alpha = host(alpha_g)
+    for r in range(rows):
+        assert alpha[r] == pytest.approx(correct.var_alpha(XS[r], keep[r]), rel=2e-6)
+
+
+@pytest.mark.parametrize("kind", ["threshold", "8:16"])
+@pytest.mark.parametrize("d_out,d_in", [(4096, 11008), (264, 1024), (11008, 4096)])
+def test_corrected_gemv(d_out, d_in, kind):
+    """The whole corrected step against the oracle: shift, weight-aware
+    selection, the sparse GEMV scaled by alpha plus the bias W mu."""
+    wt = syn.weight_t(d_out, d_in, d_out + d_in)
+    x = syn.laplace_f16((d_in,), 1.0, 12)
+    mu = syn.gaussian_f16((d_in,), 0.25, 13)
+    wt_g = dev(wt)
+    cn_g = sa.weight_col_norms(wt_g)
+    cn = host(cn_g)
+    np.testing.assert_allclose(cn, correct.column_norms(wt), rtol=1e-12)
+    xs = correct.shift(x, mu)
+    if kind == "threshold":
+        sc = np.sort(correct.scores(xs, cn))
+        t = float(0.5 * (sc[d_in // 2 - 1] + sc[d_in // 2]))
+        n, m = 0, 0
+        keep_fn = lambda v, c: correct.threshold_keep(v, c, t)  # noqa: E731
+    else:
+        t, n, m = 0.0, 8, 16
+        keep_fn = lambda v, c: correct.nm_keep(v, c, 8, 16)  # noqa: E731
+    mask_g, idx_g, val_g, nnz_g, alpha_g = sa.act_sparsify_scored(
+        dev(x), t=t, n=n, m=m, mu=dev(mu), colnorm=cn_g)
+    bias_g = sa.dense_gemv(wt_g, dev(mu))
+    y = sa.sparse_gemv_corrected(wt_g, idx_g, val_g, nnz_g, alpha=alpha_g, bias=bias_g)
+    _, keep, alpha, y_ref = correct.corrected_gemv(wt, x, mu, cn, keep_fn, var=True)
+    check_lists(mask_g, idx_g, val_g, nnz_g, xs, keep)
+    assert_close(y, y_ref)
+    # without the corrections the same call is the plain list GEMV
+    y0 = sa.sparse_gemv_corrected(wt_g, idx_g, val_g, nnz_g)
+    assert torch.equal(y0, sa.sparse_gemv(wt_g, idx_g, val_g, nnz_g))
+
+
+@pytest.mark.parametrize("d_out,d_in", [(4096, 11008), (264, 1024), (11008, 4096), (72, 40000)])
+@pytest.mark.parametrize("shifted,weighted,var,biased", [(True, True, True, True),
+                                                        (False, True, False, False),
+                                                        (True, False, True, False),
+                                                        (False, False, False, True)])
+def test_scored_fused(d_out, d_in, shifted, weighted, var, biased):
+    """sparse_gemv_scored (one launch) against the oracle, with the one- and
+    two-launch hand-offs giving identical bits."""
+    wt = syn.weight_t(d_out, d_in, d_out + 7 * d_in)
+    x = syn.laplace_f16((d_in,), 1.0, 21)
+    mu = syn.gaussian_f16((d_in,), 0.25, 22) if shifted else None
+    wt_g = dev(wt)
+    cn_g = sa.weight_col_norms(wt_g) if weighted else None
+    cn = host(cn_g) if weighted else None
+    xs = correct.shift(x, mu)
+    sc = np.sort(correct.scores(xs, cn))
+    t = float(0.5 * (sc[d_in // 2 - 1] + sc[d_in // 2]))
+    bias_g = sa.dense_gemv(wt_g, dev(mu if mu is not None else x)) if biased else None
+    # the oracle's alpha * W s (its own W mu left out), plus the bias passed
+    _, keep, alpha, y_ref = correct.corrected_gemv(
+        wt, x, None if mu is None else mu, cn, lambda v, c: correct.threshold_keep(v, c, t),
+        var=var)
+    if mu is not None:
+        y_ref = y_ref - gemv.dense_gemv(wt, mu)
+    if biased:
+        y_ref = y_ref + host(bias_g).astype(np.float64)
+    mu_g = dev(mu) if mu is not None else None
+    out = {}
+    try:
+        for handoff in (2, 1):
+            sa.set_gemv_tuning(-1, 0, handoff)
+            out[handoff] = sa.sparse_gemv_scored(wt_g, dev(x), t, mu=mu_g, colnorm=cn_g, var=var,
+                                                 bias=bias_g).clone()
+    finally:
+        sa.set_gemv_tuning(-1, 0, 0)
+    assert torch.equal(out[1], out[2])
+    assert_close(out[2], y_ref)
 
 
 # ---------------------------------------------------------------------------

@@ -14,7 +14,7 @@ import pytest
 from scipy import stats
 
 import synthetic as syn
-from oracle import brute, calibrate, gemv, rana, sparsify, spmm, swiglu
+from oracle import brute, calibrate, correct, gemv, rana, sparsify, spmm, swiglu
 
 
 # --------------------------------------------------------------------------
@@ -323,6 +323,68 @@ def test_rank_adapter_matches_scalar_loops(seed):
     assert 0 < keep.sum() < r
     np.testing.assert_allclose(y, brute.rank_adapter_loop(bt, at, x, 0.5), rtol=1e-12,
                                atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# weight-aware selection, static shift, variance correction
+# --------------------------------------------------------------------------
+
+def test_scored_selection_reduces_to_the_plain_rules():
+    """No shift and no weights: the scored threshold and N:M are the plain
+    magnitude threshold and N:M; weights all equal to 2 halve the threshold."""
+    x = syn.laplace_f16((256,), 1.0, 8)
+    for t in (0.0, 0.5, 1.25):
+        plain = sparsify.threshold_sparsify(x, t)[0]
+        assert np.array_equal(correct.threshold_keep(correct.shift(x, None), None, t), plain)
+        assert np.array_equal(correct.threshold_keep(x, np.full(256, 2.0), 2 * t), plain)
+    x[::9] = np.float16(0.5)  # ties
+    for n, m in ((2, 4), (8, 16), (16, 32)):
+        plain = sparsify.nm_sparsify(x[None], n, m)[0][0]
+        assert np.array_equal(correct.nm_keep(x, None, n, m), plain)
+        assert np.array_equal(correct.nm_keep(x, np.full(256, 3.0), n, m), plain)
+
+
+def test_scored_selection_hand_case():
+    """Weights reorder the choice: entry 1 is smaller than entry 0 but its
+    column is three times as large; equal scores keep the lower index."""
+    x = np.array([2.0, -1.0, 0.5, -0.5], dtype=np.float16)
+    c = np.array([1.0, 3.0, 4.0, 2.0])
+    assert correct.scores(x, c).tolist() == [2.0, 3.0, 2.0, 1.0]
+    assert correct.nm_keep(x, c, 2, 4).tolist() == [True, True, False, False]
+    assert correct.threshold_keep(x, c, 2.0).tolist() == [True, True, True, False]
+
+
+def test_shift_and_bias_give_back_the_dense_product():
+    """t = 0 and an exactly representable shift: W s(x - mu) + W mu = W x,
+    checked against numpy's matmul (the bias term and the shift's sign)."""
+    wt = syn.weight_t(48, 64, 9)
+    rng = np.random.default_rng(10)
+    x = (rng.integers(-64, 64, size=64) / 16.0).astype(np.float16)  # multiples of 1/16
+    mu = np.full(64, 0.5, dtype=np.float16)
+    xs = correct.shift(x, mu)
+    np.testing.assert_array_equal(xs.astype(np.float64), x.astype(np.float64) - 0.5)
+    _, keep, alpha, y = correct.corrected_gemv(
+        wt, x, mu, None, lambda v, c: correct.threshold_keep(v, c, 0.0), var=True)
+    assert alpha == 1.0  # only exact zeros are dropped
+    np.testing.assert_allclose(y, x.astype(np.float64) @ wt.astype(np.float64), rtol=1e-12,
+                               atol=1e-13)
+
+
+def test_variance_correction_hand_case():
+    """x' = [3, 4, 0, 0] keeping only 3: alpha = sqrt(25 / 9) = 5/3, so the
+    output is 5 times column 0 of W."""
+    x = np.array([3.0, 4.0, 0.0, 0.0], dtype=np.float16)
+    wt = syn.weight_t(8, 4, 11)
+    keep1 = np.array([True, False, False, False])
+    assert correct.var_alpha(x, keep1) == pytest.approx(5.0 / 3.0, rel=1e-15)
+    assert correct.var_alpha(x, np.zeros(4, bool)) == 1.0
+    _, _, alpha1, y1 = correct.corrected_gemv(wt, x, None, None, lambda v, c: keep1, var=True)
+    np.testing.assert_allclose(y1, 5.0 * wt[0].astype(np.float64), rtol=1e-14)
+
+
+def test_column_norms_match_the_swiglu_oracle():
+    wt = syn.weight_t(24, 40, 12)
+    np.testing.assert_allclose(correct.column_norms(wt), swiglu.column_norms(wt), rtol=1e-15)
 
 
 def test_silu_closed_forms():
