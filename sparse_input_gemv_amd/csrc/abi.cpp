@@ -242,8 +242,7 @@ int rana_adapter_gemv(const uint16_t* bt, int64_t r, int64_t d_in, const uint16_
   c.ws_bytes = ws_bytes;
   st = run_gemv(c, "rana_adapter_gemv", stream);
   if (st != SA_OK) return st;
-  c.mode = sa::kModeThreshold;
-  c.square = 1;
+  c.mode = sa::kModeSquare;
   c.wt = at;
   c.d_out = d_out;
   c.d_in = r;

@@ -120,7 +120,6 @@ struct KParams {
   int32_t* slice_cnt;
   uint32_t* tickets;  // non-null: one-launch hand-off
   int go, gk, slice;
-  int square;  // threshold mode: keep x_k iff x_k^2 >= t (rank-adapter masker)
   const float* alpha;    // [batch] output scale per row, or null
   const uint16_t* bias;  // [d_out] fp16 added to every row, or null
   // scored mode (batch 1): shift, weight norms (colnorm), fp64 threshold
@@ -143,10 +142,17 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 // Threshold decision on one fp16 activation entry: the magnitude threshold
 // (|x| >= t and x != 0), or the rank adapter's masker, x^2 >= t.  The square
 // of an fp16 value is exact in fp32, so no rounding takes the decision.
-__device__ __forceinline__ bool keep_entry(uint16_t xb, float t, int square) {
+template <int MODE>
+__device__ __forceinline__ bool keep_entry(uint16_t xb, float t) {
   const float v = h2f(xb);
-  return square ? v * v >= t : (mag_key(xb) != 0 && fabsf(v) >= t);
+  if constexpr (MODE == kModeSquare) return v * v >= t;
+  return mag_key(xb) != 0 && fabsf(v) >= t;
 }
+
+// Modes whose output takes the correction alpha * sum + bias (the list GEMV
+// and the scored mode); every other mode stores the plain rounding.
+template <int MODE>
+constexpr bool kCorrected = MODE == kModeList || MODE == kModeListBatched || MODE == kModeScored;
 
 // Scored mode, one entry: the shifted value x' = fp16(fp32(x) - fp32(mu))
 // (returned in xb), kept iff |x'| * colnorm >= t in fp64 and x' != 0; its
@@ -243,7 +249,7 @@ __device__ __forceinline__ void wait_stores() {
 // address plus the lane: whole lines per wave and few address registers.
 template <int TILE_O, int NT, int B>
 __device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0, unsigned char* smem,
-                                               const float* alpha) {
+                                               const float* alpha, const uint16_t* bias) {
   constexpr int G = kReduceGroups;
   constexpr int PAIRS = G * TILE_O;
   constexpr int PP = (PAIRS + NT - 1) / NT;  // pairs per thread
@@ -295,7 +301,7 @@ __device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0, uns
         float acc = red[oo];
 #pragma unroll
         for (int gg = 1; gg < G; ++gg) acc += red[gg * TILE_O + oo];
-        p.y[(int64_t)b * p.d_out + og] = finish(acc, alpha, p.bias, b, og);
+        p.y[(int64_t)b * p.d_out + og] = finish(acc, alpha, bias, b, og);
       }
     }
     __syncthreads();
@@ -331,6 +337,17 @@ template <int MODE, int TILE_O, int NT, int U, int B>
 __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int wsum[NT / kWave];
+  // The output-correction pointers are read here, with the other arguments:
+  // left to the compiler, their scalar load lands where they are first
+  // needed, and its wait then holds back the weight stream (measured: +0.25
+  // us per call).
+  const float* alpha_arg = nullptr;
+  const uint16_t* bias_arg = nullptr;
+  if constexpr (kCorrected<MODE>) {
+    alpha_arg = p.alpha;
+    bias_arg = p.bias;
+    asm volatile("" : "+s"(alpha_arg), "+s"(bias_arg));
+  }
   constexpr int OL = TILE_O / 8;  // lanes across the output tile
   constexpr int R = NT / OL;      // row lanes
   static_assert(R >= 1 && NT % OL == 0, "tile shape");
@@ -462,8 +479,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         if constexpr (MODE == kModeScored) {
           kb = scored_keep(p, xr[c][b], ms[c], cs[c], b < p.batch && k < k1, s_all, s_kept);
         } else if (b < p.batch && k < k1) {
-          if constexpr (MODE == kModeThreshold) {
-            kb = keep_entry(xb, p.t, p.square);
+          if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
+            kb = keep_entry<MODE>(xb, p.t);
           } else if constexpr (MODE == kModeMasked) {
             kb = ((mw[c][b] >> (k & 31)) & 1u) != 0;
           } else {
@@ -546,8 +563,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
           } else if (b < p.batch && in) {
             const uint16_t xb = xr[b];
             bool kb;
-            if constexpr (MODE == kModeThreshold) {
-              kb = keep_entry(xb, p.t, p.square);
+            if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
+              kb = keep_entry<MODE>(xb, p.t);
             } else if constexpr (MODE == kModeMasked) {
               kb = ((mw[b] >> (k & 31)) & 1u) != 0;
             } else {
@@ -643,7 +660,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       __syncthreads();
     }
   }
-  const float* alpha_out = (MODE == kModeScored && p.var) ? &s_alpha : p.alpha;
+  const float* alpha_out = (MODE == kModeScored && p.var) ? &s_alpha : alpha_arg;
 
   // ---------------- phase 2: stream the kept rows --------------------------
   const int o_lane = tid % OL;
@@ -770,7 +787,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       if (og < p.d_out) {
         float* dst = p.part + ((int64_t)kblk * B + b) * p.d_out + og;
         if (single)
-          p.y[(int64_t)b * p.d_out + og] = finish(s, alpha_out, p.bias, b, og);
+          p.y[(int64_t)b * p.d_out + og] = finish(s, alpha_out, bias_arg, b, og);
         else if (handoff)
           store_coherent(dst, s);
         else
@@ -824,7 +841,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       __syncthreads();
     }
   }
-  handoff_reduce<TILE_O, NT, B>(p, o0, smem, alpha_out);
+  handoff_reduce<TILE_O, NT, B>(p, o0, smem, alpha_out, bias_arg);
   if constexpr (MODE == kModeSwiglu) {
     if (oblk == 0 && p.out_nnz != nullptr) {
       int c = 0;
@@ -942,6 +959,13 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
   constexpr int RL = NT / LPR;
   constexpr int NW = NT / kWave;
   static_assert(MODE != kModeSwiglu || LPR <= 2, "mask words need >= 32 indices per wave");
+  const float* alpha_arg = nullptr;  // read with the other arguments (see k_gemv)
+  const uint16_t* bias_arg = nullptr;
+  if constexpr (kCorrected<MODE>) {
+    alpha_arg = p.alpha;
+    bias_arg = p.bias;
+    asm volatile("" : "+s"(alpha_arg), "+s"(bias_arg));
+  }
   __shared__ float red[NW][B][TO];
   __shared__ int wcnt[NW];
   const int tid = (int)threadIdx.x;
@@ -1014,8 +1038,8 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
           if (in && b < p.batch) {
             const uint16_t xb = p.x[(int64_t)b * p.d_in + j];
             bool kb;
-            if constexpr (MODE == kModeThreshold) {
-              kb = keep_entry(xb, p.t, p.square);
+            if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
+              kb = keep_entry<MODE>(xb, p.t);
             } else if constexpr (MODE == kModeMasked) {
               kb = ((p.xmask[(int64_t)b * words + (j >> 5)] >> (j & 31)) & 1u) != 0;
             } else {
@@ -1113,7 +1137,7 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
     s_alpha = var_alpha(a, k);
   }
   if (var) __syncthreads();
-  const float* alpha_out = var ? &s_alpha : p.alpha;
+  const float* alpha_out = var ? &s_alpha : alpha_arg;
   for (int e = tid; e < TO * B; e += NT) {
     const int b = e / TO;
     const int oo = e % TO;
@@ -1122,7 +1146,7 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
       float s = red[0][b][oo];
 #pragma unroll
       for (int g = 1; g < NW; ++g) s += red[g][b][oo];
-      p.y[(int64_t)b * p.d_out + og] = finish(s, alpha_out, p.bias, b, og);
+      p.y[(int64_t)b * p.d_out + og] = finish(s, alpha_out, bias_arg, b, og);
     }
   }
   if constexpr (MODE == kModeSwiglu) {
@@ -1260,6 +1284,7 @@ KFn select_kernel(int mode, int tiling, int B) {
     case kModeListBatched: return kernel_batch<kModeListBatched>(tiling, B);
     case kModeSwiglu: return kernel_tiling<kModeSwiglu, 1>(tiling);
     case kModeScored: return kernel_tiling<kModeScored, 1>(tiling);
+    case kModeSquare: return kernel_batch<kModeSquare>(tiling, B);
     default: return nullptr;
   }
 }
@@ -1458,7 +1483,6 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   kp.out_nnz = c.out_nnz;
   kp.y = c.y;
   kp.batch = c.batch;
-  kp.square = c.square;
   kp.alpha = c.alpha;
   kp.bias = c.bias;
   kp.mu = c.mu;
@@ -1480,6 +1504,9 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
       case kModeList: return dispatch_fk<kModeList, 1>(kp, tiling, grid, s);
       case kModeSwiglu: return dispatch_fk<kModeSwiglu, 1>(kp, tiling, grid, s);
       case kModeScored: return dispatch_fk<kModeScored, 1>(kp, tiling, grid, s);
+      case kModeSquare:
+        return B == 1 ? dispatch_fk<kModeSquare, 1>(kp, tiling, grid, s)
+                      : dispatch_fk<kModeSquare, 2>(kp, tiling, grid, s);
       default: return hipErrorInvalidValue;
     }
   }

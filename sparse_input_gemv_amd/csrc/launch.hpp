@@ -34,6 +34,7 @@ enum GemvMode : int {
   kModeList = 3,       // idx/val/nnz lists
   kModeSwiglu = 4,     // CATS / RaNA masked SwiGLU down
   kModeScored = 6,     // x + shift + weight norms: weight-aware threshold (batch 1)
+  kModeSquare = 7,     // x + t: keep x_k iff x_k^2 >= t (the rank adapter's masker)
 };
 
 struct GemvCall {
@@ -45,7 +46,6 @@ struct GemvCall {
   const uint16_t* x = nullptr;
   const uint32_t* xmask = nullptr;
   float t = 0.f;
-  int square = 0;  // threshold mode: keep x_k iff x_k^2 >= t instead of |x_k| >= t
   const uint16_t* mu = nullptr;  // scored mode: static shift [d_in] (or none)
   int var = 0;                   // scored mode: apply the variance correction
   // lists
