@@ -387,10 +387,13 @@ int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff);
  *     pipelined engine (which applies when d_in is a multiple of its K
  *     step, 32 for dense and the expanded N:M patterns, 64 for 2:4, with
  *     16-byte aligned rows; other calls take the staged-register engine).
+ *   stages: the pipelined engine's LDS stage count, 0 = automatic, or 3..6
+ *     (loads run stages - 1 K steps ahead); a count whose stages exceed the
+ *     160 KB of LDS for the tile is lowered to the most that fit.
  * Every choice issues the same MFMA sequence per output element: identical
  * results.  Returns SA_ERR_INVALID_ARG for other values.  Not thread-safe.
  */
-int sa_set_gemm_tuning(int tile_rows, int engine);
+int sa_set_gemm_tuning(int tile_rows, int engine, int stages);
 /* Describe tiling `i` (tile_o, threads, unroll); tile_o is negative for a
  * full-K tiling (one launch, no split of d_in).  Returns SA_ERR_INVALID_ARG
  * past the last one.  Output pointers are HOST pointers (may be NULL). */

@@ -67,7 +67,7 @@ _SIGNATURES = {
     "sa_read_stream": (_i32, [_vp, _sz, _vp, _vp]),
     "dense_gemm": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "sa_set_gemv_tuning": (_i32, [_i32, _i32, _i32]),
-    "sa_set_gemm_tuning": (_i32, [_i32, _i32]),
+    "sa_set_gemm_tuning": (_i32, [_i32, _i32, _i32]),
     "sa_gemv_tiling_info": (_i32, [_i32, _vp, _vp, _vp]),
 }
 
@@ -486,8 +486,8 @@ def set_gemv_tuning(tiling: int = -1, target_wgs: int = 0, handoff: int = 0) -> 
     _check(lib().sa_set_gemv_tuning(tiling, target_wgs, handoff), "sa_set_gemv_tuning")
 
 
-def set_gemm_tuning(tile_rows: int = 0, engine: int = 0) -> None:
-    _check(lib().sa_set_gemm_tuning(tile_rows, engine), "sa_set_gemm_tuning")
+def set_gemm_tuning(tile_rows: int = 0, engine: int = 0, stages: int = 0) -> None:
+    _check(lib().sa_set_gemm_tuning(tile_rows, engine, stages), "sa_set_gemm_tuning")
 
 
 def gemv_tiling_info(i: int):

@@ -413,11 +413,11 @@ int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff) {
   return SA_OK;
 }
 
-int sa_set_gemm_tuning(int tile_rows, int engine) {
+int sa_set_gemm_tuning(int tile_rows, int engine, int stages) {
   sa::clear_error();
-  if (sa::gemm_set_tuning(tile_rows, engine) != 0) {
-    sa::set_error("sa_set_gemm_tuning: tile_rows must be 0, 128 or 256 (got %d) and engine 0, 1 "
-                  "or 2 (got %d)", tile_rows, engine);
+  if (sa::gemm_set_tuning(tile_rows, engine, stages) != 0) {
+    sa::set_error("sa_set_gemm_tuning: tile_rows must be 0, 128 or 256 (got %d), engine 0, 1 "
+                  "or 2 (got %d) and stages 0 or 3..6 (got %d)", tile_rows, engine, stages);
     return SA_ERR_INVALID_ARG;
   }
   return SA_OK;

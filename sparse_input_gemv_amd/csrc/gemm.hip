@@ -383,7 +383,7 @@ struct Pipe<kADense, BM> {
   static constexpr int kAHalves = BM * kBK;            // [BM][32]
   static constexpr int kMaskWords = 0;
   static constexpr int kLoadsPerWave = BM / 64 + 2;    // A, B
-  static constexpr int kWgsPerCu = BM == 256 ? 2 : 3;
+  static constexpr int kWgsByRegs = BM == 256 ? 2 : 3;  // workgroups per CU the registers allow
 };
 template <int BM>
 struct Pipe<kA24, BM> {
@@ -392,11 +392,20 @@ struct Pipe<kA24, BM> {
   static constexpr int kAHalves = BM * kBK / 2;        // [BM][32] compressed
   static constexpr int kMaskWords = BM * 2;            // [BM][2]
   static constexpr int kLoadsPerWave = BM / 64 + 4 + BM / 128;  // A, B, mask
-  static constexpr int kWgsPerCu = BM == 256 ? 1 : 2;
+  static constexpr int kWgsByRegs = 2;
 };
 template <int AK, int BM>
 constexpr int pipe_stage_halves() {
   return Pipe<AK, BM>::kAHalves + Pipe<AK, BM>::kBK * PBN + 2 * Pipe<AK, BM>::kMaskWords;
+}
+// Workgroups per CU with NS stages: what the 160 KB of LDS (the stages plus
+// the 2:4 code table) and the registers both allow.
+template <int AK, int BM, int NS>
+constexpr int pipe_wgs_per_cu() {
+  constexpr int lds = NS * pipe_stage_halves<AK, BM>() * 2 + (AK == kA24 ? 256 : 0);
+  constexpr int by_lds = 160 * 1024 / lds;
+  static_assert(by_lds >= 1, "stages exceed the LDS");
+  return by_lds < Pipe<AK, BM>::kWgsByRegs ? by_lds : Pipe<AK, BM>::kWgsByRegs;
 }
 
 // 16-byte chunk swizzles: A rows of 64 bytes (dense and 2:4), B rows of 256
@@ -598,46 +607,58 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* c
   }
 }
 
-// The whole K loop over the three stages.  Step t computes stage t % 3 and
-// refills stage (t + 2) % 3.  The main loop runs while every refill exists,
-// with no branch inside; the last one to four steps run in the tail with
-// their own waits.
-template <int AK, int BM>
-__device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_t n0,
-                                            uint16_t* S0, uint16_t* S1, uint16_t* S2,
+// Stage wait with a run-time count: all but min(n, N) later stages' loads
+// landed (n is uniform, so the choice is a scalar branch).
+template <int LPW, int N>
+__device__ __forceinline__ void stage_barrier_upto(int n) {
+  if constexpr (N == 0) {
+    stage_barrier<0>();
+  } else {
+    if (n >= N)
+      stage_barrier<N * LPW>();
+    else
+      stage_barrier_upto<LPW, N - 1>(n);
+  }
+}
+
+// The whole K loop over NS stages, loads NS - 1 steps ahead.  Step t waits
+// for its own stage (t % NS), refills stage (t - 1) % NS -- read by step t - 1,
+// which every wave finished before the barrier -- with step t + NS - 1, then
+// computes.  The main loop runs while every refill exists, with no branch
+// inside; the last steps (fewer than 2 NS - 1) run in the tail, each waiting
+// for exactly the later loads that exist.
+template <int AK, int BM, int NS>
+__device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_t n0, uint16_t* S,
                                             const uint8_t* code_lut,
                                             f16v (&acc)[Pipe<AK, BM>::kMB][2], int wm, int wn) {
   constexpr int LPW = Pipe<AK, BM>::kLoadsPerWave;
   constexpr int BK = Pipe<AK, BM>::kBK;
+  constexpr int SH = pipe_stage_halves<AK, BM>();
+  constexpr int D = NS - 1;  // prefetch distance in steps
+  static_assert(NS >= 3 && (D - 1) * LPW < 64, "stage count / vmcnt range");
   const int64_t nk = p.d_in / BK;
-  pipe_issue<AK, BM>(p, m0, n0, 0, S0);
-  if (nk > 1) pipe_issue<AK, BM>(p, m0, n0, BK, S1);
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nk) pipe_issue<AK, BM>(p, m0, n0, j * BK, S + j * SH);
   int64_t kt = 0;
-  for (; kt + 4 < nk; kt += 3) {
-    stage_barrier<LPW>();
-    pipe_issue<AK, BM>(p, m0, n0, (kt + 2) * BK, S2);
-    pipe_compute<AK, BM>(S0, code_lut, acc, wm, wn);
-    stage_barrier<LPW>();
-    pipe_issue<AK, BM>(p, m0, n0, (kt + 3) * BK, S0);
-    pipe_compute<AK, BM>(S1, code_lut, acc, wm, wn);
-    stage_barrier<LPW>();
-    pipe_issue<AK, BM>(p, m0, n0, (kt + 4) * BK, S1);
-    pipe_compute<AK, BM>(S2, code_lut, acc, wm, wn);
+  for (; kt + NS + D - 1 < nk; kt += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      stage_barrier<(D - 1) * LPW>();
+      pipe_issue<AK, BM>(p, m0, n0, (kt + j + D) * BK, S + ((j + D) % NS) * SH);
+      pipe_compute<AK, BM>(S + j * SH, code_lut, acc, wm, wn);
+    }
   }
-#define SA_PIPE_TAIL(t, CS, NS)                                           \
-  if ((t) < nk) {                                                         \
-    if ((t) + 1 < nk)                                                     \
-      stage_barrier<LPW>();                                               \
-    else                                                                  \
-      stage_barrier<0>();                                                 \
-    if ((t) + 2 < nk) pipe_issue<AK, BM>(p, m0, n0, ((t) + 2) * BK, NS);  \
-    pipe_compute<AK, BM>(CS, code_lut, acc, wm, wn);                      \
+#pragma unroll
+  for (int j = 0; j < NS + D - 1; ++j) {
+    const int64_t t = kt + j;
+    if (t < nk) {
+      const int64_t later = nk - 1 - t;
+      stage_barrier_upto<LPW, D - 1>(later < D - 1 ? (int)later : D - 1);
+      if (t + D < nk) pipe_issue<AK, BM>(p, m0, n0, (t + D) * BK, S + ((j + D) % NS) * SH);
+      pipe_compute<AK, BM>(S + (j % NS) * SH, code_lut, acc, wm, wn);
+    }
   }
-  SA_PIPE_TAIL(kt, S0, S2)
-  SA_PIPE_TAIL(kt + 1, S1, S0)
-  SA_PIPE_TAIL(kt + 2, S2, S1)
-  SA_PIPE_TAIL(kt + 3, S0, S2)
-#undef SA_PIPE_TAIL
 }
 
 // Workgroup -> output tile.  Workgroups are dispatched round-robin over the
@@ -660,11 +681,10 @@ __device__ __forceinline__ void pipe_tile(int64_t b, int64_t mt, int64_t ntl, in
   n = (t % gsz) / gm;
 }
 
-template <int AK, int BM>
-__global__ __launch_bounds__(NTH, (Pipe<AK, BM>::kWgsPerCu)) void k_gemm_pipe(GParams p) {
-  constexpr int kStageHalves = pipe_stage_halves<AK, BM>();
+template <int AK, int BM, int NS>
+__global__ __launch_bounds__(NTH, (pipe_wgs_per_cu<AK, BM, NS>())) void k_gemm_pipe(GParams p) {
   constexpr int MB = Pipe<AK, BM>::kMB;
-  __shared__ __align__(16) uint16_t S0[kStageHalves], S1[kStageHalves], S2[kStageHalves];
+  __shared__ __align__(16) uint16_t S[NS * pipe_stage_halves<AK, BM>()];
   const int lane = lane_id();
   const int wave = (int)threadIdx.x / kWave;
   const int wm = wave / 2, wn = wave % 2;
@@ -686,7 +706,7 @@ __global__ __launch_bounds__(NTH, (Pipe<AK, BM>::kWgsPerCu)) void k_gemm_pipe(GP
   // the first stage barrier orders these writes before any read
   __shared__ uint8_t code_lut[AK == kA24 ? 256 : 1];
   if constexpr (AK == kA24) code_lut[threadIdx.x] = (uint8_t)code_of(threadIdx.x);
-  pipe_k_loop<AK, BM>(p, m0, n0, S0, S1, S2, code_lut, acc, wm, wn);
+  pipe_k_loop<AK, BM, NS>(p, m0, n0, S, code_lut, acc, wm, wn);
 
 #pragma unroll
   for (int a = 0; a < MB; ++a)
@@ -782,6 +802,23 @@ hipError_t launch_nm_expand(const uint16_t* xval, const uint32_t* mask, int64_t 
 
 int g_gemm_bm = 0;      // tuning override of the tile height: 0 = automatic, else 128 or 256
 int g_gemm_engine = 0;  // tuning override: 0 = automatic, 1 = staged-register engine, 2 = pipelined
+int g_gemm_stages = 0;  // tuning override of the pipelined stage count: 0 = automatic, else 3..6
+constexpr int kMaxStages = 6;
+
+template <int AK, int BM, int NS>
+constexpr bool pipe_fits() {
+  return NS * pipe_stage_halves<AK, BM>() * 2 + (AK == kA24 ? 256 : 0) <= 160 * 1024;
+}
+
+// Launch with ns stages (clamped down to the most the tile's LDS holds).
+template <int AK, int BM, int NS = 3>
+hipError_t launch_pipe_stages(const GParams& p, int64_t tiles, int ns, hipStream_t s) {
+  if constexpr (NS < kMaxStages && pipe_fits<AK, BM, NS + 1>()) {
+    if (ns > NS) return launch_pipe_stages<AK, BM, NS + 1>(p, tiles, ns, s);
+  }
+  hipLaunchKernelGGL((k_gemm_pipe<AK, BM, NS>), dim3((unsigned)tiles), dim3(NTH), 0, s, p);
+  return hipGetLastError();
+}
 
 // Pipelined engine tile height (measured): dense 256 rows, or 128 when
 // 256-row tiles would give fewer workgroups than the device has CUs; 2:4
@@ -795,11 +832,9 @@ hipError_t launch_pipe(const GParams& p, hipStream_t s) {
       g_gemm_bm ? g_gemm_bm : ((AK == kA24 || tiles256 < device_cus()) ? 128 : 256);
   const int64_t tiles = ((p.T + bm - 1) / bm) * ntl;
   if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
-  if (bm == 256)
-    hipLaunchKernelGGL((k_gemm_pipe<AK, 256>), dim3((unsigned)tiles), dim3(NTH), 0, s, p);
-  else
-    hipLaunchKernelGGL((k_gemm_pipe<AK, 128>), dim3((unsigned)tiles), dim3(NTH), 0, s, p);
-  return hipGetLastError();
+  const int ns = g_gemm_stages ? g_gemm_stages : 3;
+  if (bm == 256) return launch_pipe_stages<AK, 256>(p, tiles, ns, s);
+  return launch_pipe_stages<AK, 128>(p, tiles, ns, s);
 }
 
 template <int AK, int BM>
@@ -825,10 +860,13 @@ hipError_t launch_kind(const GParams& p, hipStream_t s) {
 
 }  // namespace
 
-int gemm_set_tuning(int bm, int engine) {
-  if ((bm != 0 && bm != 128 && bm != 256) || engine < 0 || engine > 2) return 1;
+int gemm_set_tuning(int bm, int engine, int stages) {
+  if ((bm != 0 && bm != 128 && bm != 256) || engine < 0 || engine > 2 ||
+      (stages != 0 && (stages < 3 || stages > kMaxStages)))
+    return 1;
   g_gemm_bm = bm;
   g_gemm_engine = engine;
+  g_gemm_stages = stages;
   return 0;
 }
 

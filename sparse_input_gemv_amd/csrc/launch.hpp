@@ -100,6 +100,6 @@ size_t nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m);
 hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
                           int n, int m, const uint16_t* wt, int64_t d_out, uint16_t* y,
                           void* ws, size_t ws_bytes, hipStream_t s);
-int gemm_set_tuning(int bm, int engine);
+int gemm_set_tuning(int bm, int engine, int stages);
 
 }  // namespace sa

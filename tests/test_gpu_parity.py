@@ -612,43 +612,76 @@ def test_rana_adapter_llama_gate():
 from oracle import spmm  # noqa: E402
 
 
-# (tile rows, engine): automatic, then each engine at each tile height
-GEMM_CHOICES = [(0, 0), (128, 1), (256, 1), (128, 2), (256, 2)]
+# (tile rows, engine, pipelined stages): automatic, then each engine at each
+# tile height, then deeper pipelines
+GEMM_CHOICES = [(0, 0, 0), (128, 1, 0), (256, 1, 0), (128, 2, 0), (256, 2, 0), (128, 2, 4),
+                (256, 2, 5), (128, 2, 6)]
+STAGES = [3, 4, 5, 6]
 
 
-@pytest.mark.parametrize("tile_rows,engine", GEMM_CHOICES)
+@pytest.mark.parametrize("choice", GEMM_CHOICES)
 @pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 1024), (130, 96, 136), (1, 32, 8),
                                           (257, 4096, 264), (600, 256, 1032)])
-def test_dense_gemm_small(T, d_in, d_out, tile_rows, engine):
+def test_dense_gemm_small(T, d_in, d_out, choice):
     X = syn.gaussian_f16((T, d_in), 1.0, T)
     wt = syn.weight_t(d_out, d_in, d_in)
     try:
-        sa.set_gemm_tuning(tile_rows, engine)
+        sa.set_gemm_tuning(*choice)
         Y = sa.dense_gemm(dev(X), dev(wt))
     finally:
-        sa.set_gemm_tuning(0, 0)
+        sa.set_gemm_tuning(0, 0, 0)
     assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
 
 
+@pytest.mark.parametrize("stages", STAGES)
+@pytest.mark.parametrize("tile_rows", [128, 256])
 @pytest.mark.parametrize("T,d_in,d_out", [(64, 32, 128), (256, 64, 128), (40, 96, 136),
                                           (300, 128, 136), (300, 160, 264), (17, 192, 8),
                                           (129, 224, 72), (513, 256, 264), (256, 320, 128),
-                                          (70, 448, 1000), (260, 1088, 392)])
-def test_dense_gemm_k_pipeline_lengths(T, d_in, d_out):
+                                          (70, 448, 1000), (260, 1088, 392), (33, 352, 64),
+                                          (64, 384, 136), (96, 416, 64), (31, 480, 200)])
+def test_dense_gemm_k_pipeline_lengths(T, d_in, d_out, tile_rows, stages):
     """K a multiple of 32 takes the pipelined dense engine (K steps of 32):
-    1 to 8, 10, 14 and 34 K steps cover the steady loop and every tail
-    length, with ragged rows/columns."""
+    1 to 15 and 34 K steps cover, for every stage count, runs shorter than
+    the prefetch distance, the steady loop and every tail length, with
+    ragged rows/columns."""
     X = syn.gaussian_f16((T, d_in), 1.0, T + d_in)
     wt = syn.weight_t(d_out, d_in, d_out)
-    Y = sa.dense_gemm(dev(X), dev(wt))
+    try:
+        sa.set_gemm_tuning(tile_rows, 2, stages)
+        Y = sa.dense_gemm(dev(X), dev(wt))
+    finally:
+        sa.set_gemm_tuning(0, 0, 0)
     assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
 
 
-@pytest.mark.parametrize("tile_rows,engine", GEMM_CHOICES)
+@pytest.mark.parametrize("stages", STAGES)
+@pytest.mark.parametrize("tile_rows", [128, 256])
+@pytest.mark.parametrize("T,d_in,d_out", [(64, 64, 128), (40, 192, 136), (300, 320, 264),
+                                          (129, 448, 72), (70, 576, 200), (256, 704, 128),
+                                          (33, 832, 64), (100, 960, 136), (17, 2176, 8)])
+def test_nm24_k_pipeline_lengths(T, d_in, d_out, tile_rows, stages):
+    """2:4 steps K by 64: 1, 3, 5, 7, 9, 11, 13, 15 and 34 K steps at every
+    stage count (at 256-row tiles, stage counts past what LDS holds run the
+    most that fit)."""
+    X = syn.gaussian_f16((T, d_in), 1.0, 3 * T + d_in)
+    wt = syn.weight_t(d_out, d_in, d_out + 1)
+    keep, _ = sparsify.nm_sparsify(X, 2, 4)
+    ref = spmm.nm_spmm(X, keep, wt)
+    mask_g, val_g = sa.act_sparsify_nm(dev(X), 2, 4)
+    try:
+        sa.set_gemm_tuning(tile_rows, 2, stages)
+        Y = sa.nm_act_spmm(val_g, mask_g, 2, 4, dev(wt))
+    finally:
+        sa.set_gemm_tuning(0, 0, 0)
+    assert_close(Y, ref)
+
+
+@pytest.mark.parametrize("choice", GEMM_CHOICES)
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 4), (3, 4), (5, 16),
                                  (32, 32)])
 @pytest.mark.parametrize("T,d_in,d_out", [(64, 1024, 512), (100, 96, 136), (300, 128, 264)])
-def test_nm_spmm_small(n, m, T, d_in, d_out, tile_rows, engine):
+def test_nm_spmm_small(n, m, T, d_in, d_out, choice):
     if d_in % m:
         pytest.skip("d_in not a multiple of m")
     X = syn.gaussian_f16((T, d_in), 1.0, n * 7 + m)
@@ -657,10 +690,10 @@ def test_nm_spmm_small(n, m, T, d_in, d_out, tile_rows, engine):
     ref = spmm.nm_spmm(X, keep, wt)
     mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
     try:
-        sa.set_gemm_tuning(tile_rows, engine)
+        sa.set_gemm_tuning(*choice)
         Y = sa.nm_act_spmm(val_g, mask_g, n, m, dev(wt))
     finally:
-        sa.set_gemm_tuning(0, 0)
+        sa.set_gemm_tuning(0, 0, 0)
     assert_close(Y, ref)
     # each token's row is that token's masked GEMV
     r = 3
@@ -684,10 +717,10 @@ def test_gemm_engines_agree(T, d_in, d_out):
             out[choice] = (sa.dense_gemm(X_g, wt_g).clone(),
                            sa.nm_act_spmm(val_g, mask_g, 2, 4, wt_g).clone())
     finally:
-        sa.set_gemm_tuning(0, 0)
+        sa.set_gemm_tuning(0, 0, 0)
     for choice in GEMM_CHOICES[1:]:
-        assert torch.equal(out[(0, 0)][0], out[choice][0]), ("dense", choice)
-        assert torch.equal(out[(0, 0)][1], out[choice][1]), ("2:4", choice)
+        assert torch.equal(out[GEMM_CHOICES[0]][0], out[choice][0]), ("dense", choice)
+        assert torch.equal(out[GEMM_CHOICES[0]][1], out[choice][1]), ("2:4", choice)
 
 
 @pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (4, 8), (1, 4), (3, 4), (5, 16), (7, 32),
