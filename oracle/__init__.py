@@ -22,12 +22,13 @@ Pages cited (by title; "replies" = the authors' answers to reviewers):
 
 Modules:
 
-* ``sparsify``  threshold, per-token Top-K and N:M masks; sparsity; mask packing
+* ``sparsify``  threshold, per-token Top-K and N:M masks, tile-shared N:M;
+  sparsity; mask packing
 * ``gemv``      sparse / dense / batched-union GEMV; FLOP count
 * ``swiglu``    SiLU, CATS and RaNA neuron masks, masked down projection
 * ``rana``      RaNA linear-layer rank adapter A (m ⊙ B x)
 * ``correct``   weight-aware selection, static shift, variance correction
-* ``spmm``      batched N:M activation-sparse matmul
+* ``spmm``      batched N:M activation-sparse matmul (per-token and tile-shared)
 * ``calibrate`` empirical-quantile thresholds
 * ``brute``     exhaustive enumeration for tiny inputs
 

@@ -94,6 +94,50 @@ def nm_sparsify(x, n: int, m: int):
     return keep, vals
 
 
+def nm_shared_sparsify(x, n: int, m: int, tt: int = 32):
+    """Tile-shared (vector-wise) N:M: one N:M pattern for each run of ``tt``
+    consecutive tokens.
+
+    Q-Sparse replies (answer on batched inference): Block Q-Sparse keeps N of
+    every M consecutive activations, and the batched kernel the reply times is
+    nmSPARSE's VW32 form, in which one N:M pattern is shared by a vector of 32
+    (the cited nmSPARSE paper defines the vector-wise form for weights; here
+    the activations carry it).  The pages give no selection rule for a shared
+    pattern.  Readings taken here:
+    * the vector is ``tt`` consecutive tokens (rows of ``x``); the last tile
+      holds the remaining ``T mod tt`` tokens when ``tt`` does not divide T;
+    * a position's score is the sum of the tile's magnitudes at it (the ACT
+      criterion of the N:M summary, section 2, summed over the tile: the L1
+      norm of the column segment).  The fp64 sum is exact: every fp16
+      magnitude is an integer multiple of 2^-24 below 2^16, so any partial sum
+      of at most 256 of them is an integer multiple of 2^-24 below 2^24, which
+      fp64 holds exactly; the order of the additions does not matter;
+    * in each aligned group of ``m`` positions the ``n`` largest scores are
+      kept, ties to the lower position (the per-token rule on the scores).
+
+    ``x``: fp16 ``[T][d]``, ``d % m == 0``, ``1 <= tt <= 256``.  Returns
+    ``keep`` bool ``[T][d]`` (equal rows within a tile), ``tile_keep`` bool
+    ``[ceil(T/tt)][d]`` and the compressed values ``[T][d*n/m]``: each token's
+    entries at its tile's kept positions, in position order.
+    """
+    x2 = _rows(x)
+    T, d = x2.shape
+    if d % m or not 1 <= n <= m or not 1 <= tt <= 256:
+        raise ValueError("bad shared N:M shape")
+    tiles = (T + tt - 1) // tt
+    tile_keep = np.zeros((tiles, d), dtype=bool)
+    for g in range(tiles):
+        score = np.abs(x2[g * tt:(g + 1) * tt].astype(np.float64)).sum(axis=0)
+        groups = score.reshape(d // m, m)
+        order = np.argsort(-groups, axis=-1, kind="stable")[:, :n]
+        kg = np.zeros(groups.shape, dtype=bool)
+        np.put_along_axis(kg, order, True, axis=-1)
+        tile_keep[g] = kg.reshape(d)
+    keep = tile_keep[np.arange(T) // tt]
+    vals = x2[keep].reshape(T, d * n // m)
+    return keep, tile_keep, vals
+
+
 def apply_mask(x, keep):
     """``keep ⊙ x`` as fp64 (the sparsified activation)."""
     return np.where(keep, np.asarray(x).astype(np.float64), 0.0)

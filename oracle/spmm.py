@@ -27,6 +27,20 @@ def nm_spmm(X, keep, wt) -> np.ndarray:
     return Y
 
 
+def nm_shared_spmm(vals, tile_keep, tt: int, wt) -> np.ndarray:
+    """The same product from the tile-shared compressed form: token t of tile
+    ``g = t // tt`` holds its values at the kept positions of ``tile_keep[g]``
+    (ascending), and ``Y[t] = sum_j vals[t][j] * WT[pos_g[j]]`` in fp64."""
+    vals = np.asarray(vals)
+    tile_keep = np.asarray(tile_keep)
+    wt = np.asarray(wt)
+    Y = np.empty((vals.shape[0], wt.shape[1]), dtype=np.float64)
+    for t in range(vals.shape[0]):
+        pos = np.flatnonzero(tile_keep[t // tt])
+        Y[t] = (wt[pos].astype(np.float64) * vals[t].astype(np.float64)[:, None]).sum(axis=0)
+    return Y
+
+
 def nm_spmm_flops(T: int, d_in: int, d_out: int, n: int, m: int) -> int:
     """Algorithmic FLOPs: ``2 * T * d_out * d_in * n / m`` (kept columns only)."""
     return 2 * T * d_out * (d_in * n // m)

@@ -166,6 +166,100 @@ def test_nm_whole_row_equals_topk_and_full_is_dense():
 
 
 # --------------------------------------------------------------------------
+# tile-shared N:M
+# --------------------------------------------------------------------------
+
+def test_nm_shared_hand_case():
+    # per token the 2:4 choices differ ({0,2} / {1,3} in the first group); the
+    # tile's summed magnitudes are [4, 3, 2, 2] and [2, 2, 5, 3]
+    X = np.array([[4, 0, 1, 0, 1, 2, 0, 3],
+                  [0, 3, -1, 2, -1, 0, 5, 0]], dtype=np.float16)
+    keep, tile_keep, vals = sparsify.nm_shared_sparsify(X, 2, 4, 2)
+    assert tile_keep.tolist() == [[True, True, False, False, False, False, True, True]]
+    assert np.array_equal(keep, np.repeat(tile_keep, 2, axis=0))
+    assert vals.astype(np.float64).tolist() == [[4, 0, 0, 3], [0, 3, 5, 0]]
+    # equal scores: the lower positions
+    ties = np.array([[1, -1, 1, 1], [-1, 1, 1, 1]], dtype=np.float16)
+    assert sparsify.nm_shared_sparsify(ties, 2, 4, 2)[1].tolist() == [[True, True, False, False]]
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (8, 16), (16, 32), (4, 8)])
+def test_nm_shared_one_token_tiles_are_per_token(n, m):
+    X = syn.gaussian_f16((9, 64), 1.0, 11)
+    keep, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, 1)
+    k1, v1 = sparsify.nm_sparsify(X, n, m)
+    assert np.array_equal(keep, k1) and np.array_equal(tile_keep, k1)
+    assert np.array_equal(vals, v1)
+
+
+def test_nm_shared_identical_rows_take_the_row_pattern():
+    row = syn.gaussian_f16((1, 64), 1.0, 12)
+    X = np.repeat(row, 32, axis=0)
+    keep, tile_keep, _ = sparsify.nm_shared_sparsify(X, 8, 16, 32)
+    assert np.array_equal(tile_keep[0], sparsify.nm_sparsify(row, 8, 16)[0][0])
+
+
+@pytest.mark.parametrize("n,m,tt,T", [(2, 4, 2, 5), (1, 4, 3, 7), (3, 8, 4, 9), (8, 16, 32, 40),
+                                      (5, 8, 6, 6)])
+def test_nm_shared_brute_force(n, m, tt, T):
+    """Exhaustive layouts on the tile scores, summed by a plain loop; ragged
+    last tiles and tied scores included."""
+    rng = np.random.default_rng(n * 97 + m * 7 + tt)
+    pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, 0.25], dtype=np.float16)
+    d = 2 * m
+    X = pool[rng.integers(0, len(pool), size=T * d)].reshape(T, d)
+    keep, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+    tiles = (T + tt - 1) // tt
+    assert tile_keep.shape == (tiles, d)
+    for g in range(tiles):
+        rows = range(g * tt, min(T, (g + 1) * tt))
+        scores = np.array([sum(abs(float(X[t][k])) for t in rows) for k in range(d)])
+        assert np.array_equal(tile_keep[g], brute.nm_brute(scores, n, m))
+        for t in rows:
+            assert np.array_equal(keep[t], tile_keep[g])
+            assert np.array_equal(vals[t], X[t][tile_keep[g]])
+    assert np.all(keep.reshape(T, -1, m).sum(axis=-1) == n)
+
+
+def test_nm_shared_score_is_exact():
+    """The largest and smallest fp16 magnitudes in one 256-token tile: the
+    exact sums (rational arithmetic) decide, where an fp32 sum would tie."""
+    from fractions import Fraction
+    T = 256
+    X = np.zeros((T, 4), dtype=np.float16)
+    X[:255, 0] = 65504.0
+    X[:255, 1] = -65504.0
+    X[255, 1] = np.float16(2.0 ** -24)   # smallest subnormal
+    X[:, 2] = np.float16(2.0 ** -14)
+    X[7, 3] = np.float16(-3.0)
+    exact = [sum(Fraction(abs(float(v))) for v in X[:, k]) for k in range(4)]
+    assert exact[1] > exact[0]
+    f32 = np.float32(0)
+    for v in X[:, 1]:
+        f32 = np.float32(f32 + np.float32(abs(float(v))))
+    assert f32 == np.float32(255 * 65504.0)   # fp32 loses the last term
+    _, tile_keep, _ = sparsify.nm_shared_sparsify(X, 1, 4, 256)
+    assert tile_keep.tolist() == [[False, True, False, False]]
+    _, tile_keep, _ = sparsify.nm_shared_sparsify(X, 2, 4, 256)
+    assert tile_keep.tolist() == [[True, True, False, False]]
+    _, tile_keep, _ = sparsify.nm_shared_sparsify(X, 3, 4, 256)
+    assert tile_keep.tolist() == [[True, True, False, True]]  # 3 > 256 * 2^-14
+
+
+def test_nm_shared_spmm_is_the_masked_matmul():
+    X = syn.gaussian_f16((40, 64), 1.0, 13)
+    wt = syn.weight_t(24, 64, 14)
+    for (n, m, tt) in [(8, 16, 16), (2, 4, 32), (1, 4, 7)]:
+        keep, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+        np.testing.assert_allclose(spmm.nm_shared_spmm(vals, tile_keep, tt, wt),
+                                   spmm.nm_spmm(X, keep, wt), rtol=1e-12, atol=1e-13)
+    keep, tile_keep, vals = sparsify.nm_shared_sparsify(X, 4, 4, 32)
+    np.testing.assert_allclose(spmm.nm_shared_spmm(vals, tile_keep, 32, wt),
+                               X.astype(np.float64) @ wt.astype(np.float64), rtol=1e-12,
+                               atol=1e-13)
+
+
+# --------------------------------------------------------------------------
 # mask packing
 # --------------------------------------------------------------------------
 
