@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--only", choices=["fused", "unfused", "dense", "read"], default=None,
                     help="time a single path (for profiler runs)")
     ap.add_argument("--rows", default=None,
-                    help="with --suite: comma-separated rows to run (a1..a9); default all")
+                    help="with --suite: comma-separated rows to run (a1..a9, next1..next4); "
+                         "default all")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the headline line, time every hot-path row on its "
                          "workload and print one JSON line per measurement")
@@ -348,6 +349,8 @@ def run_suite(args):
         suite_rank_adapter(sa, syn, dev, ev_time, emit)
     if section("next3"):
         suite_corrected(sa, syn, dev, ev_time, emit, rotation)
+    if section("next4"):
+        suite_shared_nm(sa, syn, dev, ev_time, emit)
 
 
 def suite_layer(sa, syn, dev, ev_time, emit, rotation):
@@ -599,6 +602,37 @@ def suite_matmul(sa, syn, dev, ev_time, emit):
             emit("a7", f"nm_act_spmm {n}:{m} {T}x{d_in}x{d_out}", us, flops=alg,
                  frac_mfma=round(alg / (us * 1e-6) / 2.5e15, 4),
                  speedup_vs_dense_gemm=round(us_g / us, 3))
+
+
+def suite_shared_nm(sa, syn, dev, ev_time, emit):
+    """Tile-shared N:M: one pattern per tile of tt tokens (VW32 is tt = 32),
+    sparsify and matmul, against the dense GEMM of the same shape.  Algorithmic
+    FLOPs are the kept columns' (n/m of dense), priced against the dense fp16
+    peak."""
+    import torch
+
+    for (T, d_in, d_out) in [(4096, 1024, 1024), (2048, 4096, 11008)]:
+        X = torch.from_numpy(syn.gaussian_f16((T, d_in), 1.0, 5)).to(dev)
+        wt = torch.from_numpy(syn.weight_t(d_out, d_in, 41)).to(dev)
+        y = torch.empty((T, d_out), dtype=torch.float16, device=dev)
+        dense_flop = 2 * T * d_in * d_out
+        steps = 200 if T * d_in * d_out < 1e10 else 30
+        us_g = ev_time(lambda i: sa.dense_gemm(X, wt, y=y), steps, warmup=3)
+        for tt in (32, 128, 256):
+            for (n, m) in [(8, 16), (16, 32), (2, 4), (1, 4), (4, 16)]:
+                if tt == 256 and (n, m) not in ((8, 16), (1, 4)):
+                    continue
+                mask, val = sa.act_sparsify_nm_shared(X, n, m, tt)
+                if (n, m) == (8, 16):
+                    us_s = ev_time(lambda i: sa.act_sparsify_nm_shared(X, n, m, tt), 200)
+                    emit("next4", f"act_sparsify_nm_shared {n}:{m} tt={tt} {T}x{d_in}", us_s,
+                         bytes_=2 * T * d_in + 2 * T * d_in * n // m + -(-T // tt) * d_in // 8)
+                us = ev_time(lambda i: sa.nm_shared_spmm(val, mask, n, m, tt, wt, y=y), steps,
+                             warmup=3)
+                alg = dense_flop * n // m
+                emit("next4", f"nm_shared_spmm {n}:{m} tt={tt} {T}x{d_in}x{d_out}", us, flops=alg,
+                     frac_mfma=round(alg / (us * 1e-6) / 2.5e15, 4),
+                     speedup_vs_dense_gemm=round(us_g / us, 3), dense_gemm_us=round(us_g, 3))
 
 
 def cpu_baseline(wt, x, t, seconds):

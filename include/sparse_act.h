@@ -123,6 +123,26 @@ int act_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
                     uint32_t* mask, uint16_t* val, void* stream);
 
 /*
+ * act_sparsify_nm_shared -- tile-shared (vector-wise) N:M sparsity.
+ * [QS] answer on batched inference: the batched N:M kernel timed there is
+ * nmSPARSE's VW32 form, one N:M pattern shared by a vector of 32.  The page
+ * gives no rule for a shared pattern; here, per tile of tt consecutive rows
+ * (the last tile holds the rest) and per aligned group of m positions, the
+ * n positions with the largest sum of the tile's |x| are kept, ties to the
+ * lower position.  The sum is exact (fp64 over at most 256 fp16
+ * magnitudes), so the masks are exact.
+ *
+ *   x     [rows][d] fp16, 16-byte aligned
+ *   mask  [ceil(rows/tt)][d/32]: one mask row per tile, n bits per group
+ *   val   [rows][d*n/m] fp16: each row's values at its tile's kept
+ *         positions, in position order
+ * Requires m in {4,8,16,32}, 1 <= n <= m, 1 <= tt <= 256, d % 32 == 0,
+ * d >= 32.  Inputs are finite.
+ */
+int act_sparsify_nm_shared(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
+                           int tt, uint32_t* mask, uint16_t* val, void* stream);
+
+/*
  * act_sparsify_scored -- weight-aware selection with a static shift and the
  * variance-correction scale.  [NM] section 2 (methodology): entries scored
  * by the size of the weight they multiply (WT, Amber-Pruner), static
@@ -339,6 +359,39 @@ int nm_act_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
 /* Workspace bytes for nm_act_spmm's two-pass path (0 for 2:4, which has
  * none; 0 for invalid sizes). */
 size_t sa_nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m);
+
+/*
+ * nm_shared_spmm -- Y[t] = W (mask_{t / tt} .* x_t): the matmul over
+ * tile-shared N:M activations in act_sparsify_nm_shared's form.
+ * [QS] answer on batched inference (VW32: one pattern per vector of 32, the
+ * form that gives N:M savings beyond 2:4).  Three kernels, by tile size:
+ *   tt a multiple of 128, n dividing 32, d_in <= 32768 and d_in n / m a
+ *     multiple of 32: a whole row tile of the matmul shares one pattern, so
+ *     it loads only the kept rows of WT and runs the dense MFMA matmul over
+ *     the d_in n / m compressed entries: every byte and FLOP is n/m of dense;
+ *   else tt a multiple of 32, n dividing 32 and m / n 2 or 4, d_in a multiple
+ *     of 32 m / n: each 32-row MFMA block has one pattern; the kernel stages
+ *     whole WT slabs and gathers each block's kept rows on the fly, so only
+ *     the MFMA work falls to n/m of dense;
+ *   else: the values are expanded into a zero-filled dense copy in ws and
+ *     the dense MFMA matmul runs on it.
+ * The first two need no workspace.
+ *
+ *   xval [T][d_in*n/m] fp16; mask [ceil(T/tt)][d_in/32]
+ *   wt   [d_in][d_out] fp16;  y [T][d_out] fp16
+ *   ws   device workspace of sa_nm_shared_spmm_workspace_bytes() bytes,
+ *        16-byte aligned (NULL allowed when that is 0)
+ * Requires m in {4,8,16,32}, 1 <= n <= m, 1 <= tt <= 256, d_in % 32 == 0,
+ * d_out % 8 == 0, wt, y and xval 16-byte aligned.  SA_ERR_WORKSPACE if a
+ * needed workspace is missing or too small.  A mask that breaks the N:M
+ * contract gives unspecified values but never an out-of-bounds access.
+ */
+int nm_shared_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
+                   int n, int m, int tt, const uint16_t* wt, int64_t d_out, uint16_t* y,
+                   void* ws, size_t ws_bytes, void* stream);
+/* Workspace bytes nm_shared_spmm needs: 0 where one of the gathering kernels
+ * applies (see above), T * d_in * 2 otherwise; 0 for invalid sizes. */
+size_t sa_nm_shared_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m, int tt);
 
 /*
  * dense_gemm -- Y[t][o] = sum_k X[t][k] WT[k][o] (Y = X W^T) on MFMA: the

@@ -24,11 +24,12 @@ import torch
 
 __all__ = [
     "SparseActError", "lib", "workspace",
-    "act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm",
+    "act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm", "act_sparsify_nm_shared",
     "act_sparsify_scored", "sparse_gemv_corrected", "sparse_gemv_scored",
     "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold", "rana_adapter_gemv",
     "masked_gemv",
-    "dense_gemv", "masked_swiglu_down", "weight_col_norms", "nm_act_spmm", "dense_gemm",
+    "dense_gemv", "masked_swiglu_down", "weight_col_norms", "nm_act_spmm", "nm_shared_spmm",
+    "dense_gemm",
     "set_gemv_tuning", "set_gemm_tuning", "gemv_tiling_info", "workspace_bytes", "MAX_BATCH",
 ]
 
@@ -45,6 +46,7 @@ _SIGNATURES = {
     "act_sparsify_threshold": (_i32, [_vp, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _i64, _vp]),
     "act_sparsify_topk": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
     "act_sparsify_nm": (_i32, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp]),
+    "act_sparsify_nm_shared": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "act_calibrate_threshold": (_i32, [_vp, _i64, _f64, _vp, _vp]),
     "sa_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "sparse_gemv": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
@@ -64,6 +66,9 @@ _SIGNATURES = {
     "weight_col_norms": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "nm_act_spmm": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp]),
     "sa_nm_spmm_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
+    "nm_shared_spmm": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _sz,
+                              _vp]),
+    "sa_nm_shared_spmm_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32]),
     "sa_read_stream": (_i32, [_vp, _sz, _vp, _vp]),
     "dense_gemm": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "sa_set_gemv_tuning": (_i32, [_i32, _i32, _i32]),
@@ -224,6 +229,20 @@ def act_sparsify_nm(x: torch.Tensor, n: int, m: int):
     val = torch.empty(shape + (d * n // m,), dtype=torch.float16, device=x.device)
     _check(lib().act_sparsify_nm(_ptr(x), rows, d, n, m, _ptr(mask), _ptr(val), _stream(x)),
            "act_sparsify_nm")
+    return mask, val
+
+
+def act_sparsify_nm_shared(x: torch.Tensor, n: int, m: int, tt: int = 32):
+    """Returns ``(mask, val)``: one mask row per tile of ``tt`` rows and each
+    row's values at its tile's kept positions."""
+    _dev(x, "x", torch.float16)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows][d]")
+    rows, d = x.shape
+    mask = torch.empty(((rows + tt - 1) // tt, d // 32), dtype=torch.int32, device=x.device)
+    val = torch.empty((rows, d * n // m), dtype=torch.float16, device=x.device)
+    _check(lib().act_sparsify_nm_shared(_ptr(x), rows, d, n, m, tt, _ptr(mask), _ptr(val),
+                                        _stream(x)), "act_sparsify_nm_shared")
     return mask, val
 
 
@@ -465,6 +484,27 @@ def nm_act_spmm(xval: torch.Tensor, mask: torch.Tensor, n: int, m: int, wt: torc
         ws_ptr, ws_bytes = ws.data_ptr() + WS_TICKET_BYTES, ws.numel() - WS_TICKET_BYTES
     _check(lib().nm_act_spmm(_ptr(xval), _ptr(mask), T, d_in, n, m, _ptr(wt), d_out, _ptr(y),
                              ws_ptr, ws_bytes, _stream(wt)), "nm_act_spmm")
+    return y
+
+
+def nm_shared_spmm(xval: torch.Tensor, mask: torch.Tensor, n: int, m: int, tt: int,
+                   wt: torch.Tensor, y: torch.Tensor | None = None):
+    """``Y[t] = W (mask[t // tt] ⊙ x_t)`` from the tile-shared compressed form
+    (the per-device workspace serves the tiles and patterns that need one)."""
+    _dev(xval, "xval", torch.float16)
+    _dev(mask, "mask", torch.int32)
+    _dev(wt, "wt", torch.float16)
+    T = xval.shape[0]
+    d_in, d_out = wt.shape
+    if y is None:
+        y = torch.empty((T, d_out), dtype=torch.float16, device=wt.device)
+    ws_ptr, ws_bytes = None, 0
+    need = int(lib().sa_nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt))
+    if need > 0:
+        ws = workspace(wt.device, WS_TICKET_BYTES + need)
+        ws_ptr, ws_bytes = ws.data_ptr() + WS_TICKET_BYTES, ws.numel() - WS_TICKET_BYTES
+    _check(lib().nm_shared_spmm(_ptr(xval), _ptr(mask), T, d_in, n, m, tt, _ptr(wt), d_out,
+                                _ptr(y), ws_ptr, ws_bytes, _stream(wt)), "nm_shared_spmm")
     return y
 
 

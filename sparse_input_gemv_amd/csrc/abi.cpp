@@ -82,6 +82,21 @@ int act_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m, ui
                     "act_sparsify_nm");
 }
 
+int act_sparsify_nm_shared(const uint16_t* x, int64_t rows, int64_t d, int n, int m, int tt,
+                           uint32_t* mask, uint16_t* val, void* stream) {
+  sa::clear_error();
+  int st = sa::check_nm_shared(x, rows, d, n, m, tt, mask, val);
+  if (st != SA_OK) return st;
+  if (rows == 0) return SA_OK;
+  hipError_t e =
+      sa::launch_sparsify_nm_shared(x, rows, d, n, m, tt, mask, val, as_stream(stream));
+  if (e == hipErrorNotSupported) {
+    sa::set_error("act_sparsify_nm_shared: shape not supported by the compiled kernels");
+    return SA_ERR_UNSUPPORTED;
+  }
+  return hip_status(e, "act_sparsify_nm_shared");
+}
+
 int act_calibrate_threshold(const uint16_t* samples, int64_t n, double s, float* t_out,
                             void* stream) {
   sa::clear_error();
@@ -387,6 +402,37 @@ int nm_act_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d
     return SA_ERR_UNSUPPORTED;
   }
   return hip_status(e, "nm_act_spmm");
+}
+
+size_t sa_nm_shared_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m, int tt) {
+  if (T < 1 || d_in < 1 || m < 1 || n < 1 || n > m || tt < 1) return 0;
+  return sa::nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt);
+}
+
+int nm_shared_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in, int n,
+                   int m, int tt, const uint16_t* wt, int64_t d_out, uint16_t* y, void* ws,
+                   size_t ws_bytes, void* stream) {
+  sa::clear_error();
+  int st = sa::check_nm_shared_spmm(xval, mask, T, d_in, n, m, tt, wt, d_out, y);
+  if (st != SA_OK) return st;
+  const size_t need = T > 0 ? sa::nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt) : 0;
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) {
+    sa::set_error("nm_shared_spmm: this tile size and pattern need a workspace of %zu bytes "
+                  "(%zu given)", need, ws == nullptr ? (size_t)0 : ws_bytes);
+    return SA_ERR_WORKSPACE;
+  }
+  if (need > 0 && (reinterpret_cast<uintptr_t>(ws) & 15u) != 0) {
+    sa::set_error("nm_shared_spmm: workspace must be 16-byte aligned");
+    return SA_ERR_INVALID_ARG;
+  }
+  if (T == 0) return SA_OK;
+  hipError_t e = sa::launch_nm_shared_spmm(xval, mask, T, d_in, n, m, tt, wt, d_out, y, ws,
+                                           ws_bytes, as_stream(stream));
+  if (e == hipErrorNotSupported) {
+    sa::set_error("nm_shared_spmm: shape not supported by the compiled kernels");
+    return SA_ERR_UNSUPPORTED;
+  }
+  return hip_status(e, "nm_shared_spmm");
 }
 
 int dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt, int64_t d_out,

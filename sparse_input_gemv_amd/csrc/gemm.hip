@@ -41,15 +41,16 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16 __attribute__((ext_vector_type(16)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 
-enum AKind : int { kADense = 0, kANM = 1, kA24 = 2, kANMVec = 3 };
+enum AKind : int { kADense = 0, kANM = 1, kA24 = 2, kANMVec = 3, kAGather = 4 };
 
 struct GParams {
   const uint16_t* x;      // dense: X [T][d_in]; sparse: compressed values [T][d_in*n/m]
-  const uint32_t* mask;   // sparse: [T][d_in/32]
+  const uint32_t* mask;   // sparse: [T][d_in/32]; tile-shared: [ceil(T/tt)][d_in/32]
   const uint16_t* wt;     // [d_in][d_out]
   uint16_t* y;            // [T][d_out]
   int64_t T, d_in, d_out;
   int n, m;
+  int tt;                 // tile-shared: rows per pattern
 };
 
 // ---- B staging: 32 k rows x 128 n columns -> LDS Bs[n][k] ------------------
@@ -394,6 +395,12 @@ struct Pipe<kA24, BM> {
   static constexpr int kLoadsPerWave = BM / 64 + 4 + BM / 128;  // A, B, mask
   static constexpr int kWgsByRegs = 2;
 };
+// Tile-shared N:M with one pattern for the whole row tile: the dense engine
+// on the compressed values and the kept rows of WT (see pipe_issue).
+template <int BM>
+struct Pipe<kAGather, BM> : Pipe<kADense, BM> {};
+constexpr int kGatherMaskWords = 1024;  // the tile's mask row in LDS: d_in <= 32768
+
 template <int AK, int BM>
 constexpr int pipe_stage_halves() {
   return Pipe<AK, BM>::kAHalves + Pipe<AK, BM>::kBK * PBN + 2 * Pipe<AK, BM>::kMaskWords;
@@ -402,7 +409,8 @@ constexpr int pipe_stage_halves() {
 // the 2:4 code table) and the registers both allow.
 template <int AK, int BM, int NS>
 constexpr int pipe_wgs_per_cu() {
-  constexpr int lds = NS * pipe_stage_halves<AK, BM>() * 2 + (AK == kA24 ? 256 : 0);
+  constexpr int lds = NS * pipe_stage_halves<AK, BM>() * 2 + (AK == kA24 ? 256 : 0) +
+                      (AK == kAGather ? 4 * kGatherMaskWords : 0);
   constexpr int by_lds = 160 * 1024 / lds;
   static_assert(by_lds >= 1, "stages exceed the LDS");
   return by_lds < Pipe<AK, BM>::kWgsByRegs ? by_lds : Pipe<AK, BM>::kWgsByRegs;
@@ -457,19 +465,37 @@ __device__ __forceinline__ void load_to_lds4(const void* src, const void* lds_ba
       : "memory", "m0");
 }
 
+// Position of the r-th set bit (r from 0) of a field of at most 32 bits, by
+// halving; a field with fewer set bits gives some position below 32.
+__device__ __forceinline__ int select_bit(uint32_t b, int r) {
+  int pos = 0;
+#pragma unroll
+  for (int half = 16; half >= 1; half /= 2) {
+    const int c = __builtin_popcount(b & ((1u << half) - 1u));
+    if (r >= c) {
+      r -= c;
+      b >>= half;
+      pos += half;
+    }
+  }
+  return pos;
+}
+
 // This wave's share of the loads of the K step starting at k0 into one stage
 // (A, then B, then for 2:4 the mask words).  Rows past T and columns past
 // d_out read clamped (valid) addresses; their results are never stored.
 template <int AK, int BM>
 __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t n0, int64_t k0,
-                                           uint16_t* S) {
+                                           uint16_t* S, const uint32_t* mrow) {
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   uint16_t* As = S;
   uint16_t* Bs = S + Pipe<AK, BM>::kAHalves;
   constexpr int BK = Pipe<AK, BM>::kBK;
   constexpr int AI = BM / 64;  // A instructions per wave
-  if constexpr (AK == kADense) {
+  if constexpr (AK == kADense || AK == kAGather) {
+    // gather: A rows are the compressed values, d_in n / m long
+    const int64_t lda = AK == kAGather ? p.d_in / p.m * p.n : p.d_in;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int rb = (w * AI + i) * 16;  // 16 rows of 64 bytes per instruction
@@ -477,7 +503,7 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
       const int gc = (lane % 4) ^ swz_a(r);
       int64_t row = m0 + r;
       if (row >= p.T) row = p.T - 1;
-      load_to_lds16(p.x + row * p.d_in + k0 + 8 * gc, As + rb * BK);
+      load_to_lds16(p.x + row * lda + k0 + 8 * gc, As + rb * BK);
     }
   } else {
     const int64_t kc = p.d_in / 2;  // compressed row length
@@ -509,7 +535,16 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
     const int gc = (lane % 16) ^ swz_b(k);
     int64_t n = n0 + 8 * gc;
     if (n >= p.d_out) n = p.d_out - 8;
-    load_to_lds16(p.wt + (k0 + k) * p.d_out + n, Bs + kb * PBN);
+    int64_t row = k0 + k;
+    if constexpr (AK == kAGather) {
+      // compressed entry j = k0 + k: mask word j / per (per = 32 n / m kept
+      // entries per word, a power of two), its (j mod per)-th set bit
+      const int lper = __builtin_ctz((unsigned)(32 / p.m * p.n));
+      const int64_t wd = row >> lper;
+      row = 32 * wd + select_bit(mrow[wd], (int)(row & ((1 << lper) - 1)));
+      if (row > p.d_in - 1) row = p.d_in - 1;
+    }
+    load_to_lds16(p.wt + row * p.d_out + n, Bs + kb * PBN);
   }
 }
 
@@ -547,7 +582,7 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* S, const uint8_t* c
   constexpr int MB = Pipe<AK, BM>::kMB;
   const uint16_t* As = S;
   const uint16_t* Bs = S + Pipe<AK, BM>::kAHalves;
-  if constexpr (AK == kADense) {
+  if constexpr (AK == kADense || AK == kAGather) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       h8 aop[MB], bop[2];
@@ -629,23 +664,23 @@ __device__ __forceinline__ void stage_barrier_upto(int n) {
 // for exactly the later loads that exist.
 template <int AK, int BM, int NS>
 __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_t n0, uint16_t* S,
-                                            const uint8_t* code_lut,
+                                            const uint8_t* code_lut, const uint32_t* mrow,
                                             f16v (&acc)[Pipe<AK, BM>::kMB][2], int wm, int wn) {
   constexpr int LPW = Pipe<AK, BM>::kLoadsPerWave;
   constexpr int BK = Pipe<AK, BM>::kBK;
   constexpr int SH = pipe_stage_halves<AK, BM>();
   constexpr int D = NS - 1;  // prefetch distance in steps
   static_assert(NS >= 3 && (D - 1) * LPW < 64, "stage count / vmcnt range");
-  const int64_t nk = p.d_in / BK;
+  const int64_t nk = (AK == kAGather ? p.d_in / p.m * p.n : p.d_in) / BK;
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (j < nk) pipe_issue<AK, BM>(p, m0, n0, j * BK, S + j * SH);
+    if (j < nk) pipe_issue<AK, BM>(p, m0, n0, j * BK, S + j * SH, mrow);
   int64_t kt = 0;
   for (; kt + NS + D - 1 < nk; kt += NS) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       stage_barrier<(D - 1) * LPW>();
-      pipe_issue<AK, BM>(p, m0, n0, (kt + j + D) * BK, S + ((j + D) % NS) * SH);
+      pipe_issue<AK, BM>(p, m0, n0, (kt + j + D) * BK, S + ((j + D) % NS) * SH, mrow);
       pipe_compute<AK, BM>(S + j * SH, code_lut, acc, wm, wn);
     }
   }
@@ -655,7 +690,8 @@ __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_
     if (t < nk) {
       const int64_t later = nk - 1 - t;
       stage_barrier_upto<LPW, D - 1>(later < D - 1 ? (int)later : D - 1);
-      if (t + D < nk) pipe_issue<AK, BM>(p, m0, n0, (t + D) * BK, S + ((j + D) % NS) * SH);
+      if (t + D < nk)
+        pipe_issue<AK, BM>(p, m0, n0, (t + D) * BK, S + ((j + D) % NS) * SH, mrow);
       pipe_compute<AK, BM>(S + (j % NS) * SH, code_lut, acc, wm, wn);
     }
   }
@@ -706,7 +742,222 @@ __global__ __launch_bounds__(NTH, (pipe_wgs_per_cu<AK, BM, NS>())) void k_gemm_p
   // the first stage barrier orders these writes before any read
   __shared__ uint8_t code_lut[AK == kA24 ? 256 : 1];
   if constexpr (AK == kA24) code_lut[threadIdx.x] = (uint8_t)code_of(threadIdx.x);
-  pipe_k_loop<AK, BM, NS>(p, m0, n0, S, code_lut, acc, wm, wn);
+  // gather: the row tile's mask row (one pattern for all its rows), read by
+  // every B load of the K loop
+  __shared__ uint32_t mrow[AK == kAGather ? kGatherMaskWords : 1];
+  if constexpr (AK == kAGather) {
+    const int64_t wpr = p.d_in / 32;
+    const uint32_t* src = p.mask + (m0 / p.tt) * wpr;
+    for (int64_t i = threadIdx.x; i < wpr; i += NTH) mrow[i] = src[i];
+    __syncthreads();
+  }
+  pipe_k_loop<AK, BM, NS>(p, m0, n0, S, code_lut, mrow, acc, wm, wn);
+
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = n0 + wn * 64 + b * 32 + lane % 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * (BM / 2) + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        if (row < p.T && col < p.d_out) p.y[row * p.d_out + col] = f2h(acc[a][b][r]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tile-shared N:M engine.  Every 32-row block of tokens lies in one tile of
+// tt rows (tt a multiple of 32), so its rows share one N:M pattern; over one
+// K step the block's product is a dense MFMA product of the compressed values
+// (32 per row per step) with the kept rows of WT.  A K step covers KB =
+// 32 m / n dense rows of WT, staged whole as the dense engine stages B, and
+// 32 compressed values of each A row.  The gather costs no extra LDS reads:
+// the MFMA B operand comes from transpose reads in which every source lane
+// addresses its own row, so a lane points at the kept row of its k slot
+// rather than at the slot's own row.  Per K step each wave turns its row
+// blocks' mask words into a table of kept-row offsets, one lane per kept
+// slot (the r-th set bit of its group), stored so that the four offsets a
+// lane reads in a step share one 32-bit word.
+//   Stage: A [BM][32] (64-byte rows, swizzled as the dense A), B [KB][128]
+//   (as the dense B), and one 64-word mask area per wave (lane l of wave w
+//   loads word l % (KB/32) of its row block l / (KB/32)).
+// Only the MFMA work shrinks (to n/m of dense): every step still stages the
+// whole WT slab, and B operands are read per 32-row block (no reuse across
+// the blocks of a wave), so the engine pays off where MFMAs, not loads, bound
+// the dense product.
+// ---------------------------------------------------------------------------
+template <int KB, int BM>
+struct Shared {
+  static constexpr int kMB = BM / 64;               // 32-row blocks per wave
+  static constexpr int kAHalves = BM * 32;
+  static constexpr int kBHalves = KB * PBN;
+  static constexpr int kMaskWords = 4 * 64;         // one 64-word area per wave
+  static constexpr int kStageHalves = kAHalves + kBHalves + 2 * kMaskWords;
+  static constexpr int kLoadsPerWave = BM / 64 + KB / 16 + 1;
+  static constexpr int kStages = 3;
+  static constexpr int kLdsBytes = kStages * kStageHalves * 2 + 4 * kMB * 32;
+  static constexpr int kWgsPerCu = (160 * 1024 / kLdsBytes) < 2 ? (160 * 1024 / kLdsBytes) : 2;
+  static_assert(kWgsPerCu >= 1, "stages exceed the LDS");
+};
+
+template <int KB, int BM>
+__device__ __forceinline__ void shared_issue(const GParams& p, int64_t m0, int64_t n0,
+                                             int64_t step, uint16_t* S) {
+  using C = Shared<KB, BM>;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  uint16_t* As = S;
+  uint16_t* Bs = S + C::kAHalves;
+  uint32_t* Ms = reinterpret_cast<uint32_t*>(Bs + C::kBHalves) + 64 * w;
+  const int64_t kc = p.d_in / KB * 32;  // compressed row length
+  constexpr int AI = BM / 64;
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int rb = (w * AI + i) * 16;  // 16 rows of 64 bytes per instruction
+    const int r = rb + lane / 4;
+    const int gc = (lane % 4) ^ swz_a(r);
+    int64_t row = m0 + r;
+    if (row >= p.T) row = p.T - 1;
+    load_to_lds16(p.x + row * kc + step * 32 + 8 * gc, As + rb * 32);
+  }
+#pragma unroll
+  for (int i = 0; i < KB / 16; ++i) {
+    const int kb = (w * (KB / 16) + i) * 4;  // 4 k rows of 256 bytes per instruction
+    const int k = kb + lane / 16;
+    const int gc = (lane % 16) ^ swz_b(k);
+    int64_t n = n0 + 8 * gc;
+    if (n >= p.d_out) n = p.d_out - 8;
+    load_to_lds16(p.wt + (step * KB + k) * p.d_out + n, Bs + kb * PBN);
+  }
+  constexpr int W = KB / 32;  // mask words per row block per step
+  int bl = lane / W;
+  if (bl >= C::kMB) bl = C::kMB - 1;  // spare lanes repeat a valid word
+  int64_t row = m0 + (w / 2) * (BM / 2) + 32 * bl;
+  if (row >= p.T) row = p.T - 1;
+  const int64_t words = p.d_in / 32;
+  load_to_lds4(p.mask + (row / p.tt) * words + step * W + lane % W, Ms);
+}
+
+// This wave's kept-row offsets for the step: lane -> (block a, slot j).
+// Slot j = 16 kk + 8 h + 4 q + r (MFMA kk, lane half h, quad q, row r of
+// the quad) is stored at byte 4 (4 h + r) + 2 kk + q of the block's 32.
+template <int KB, int BM>
+__device__ __forceinline__ void shared_positions(const GParams& p, const uint32_t* Ms,
+                                                 uint8_t* tab) {
+  using C = Shared<KB, BM>;
+  const int lane = lane_id();
+  const int ln = __builtin_ctz((unsigned)p.n), lm = __builtin_ctz((unsigned)p.m);
+  const uint32_t fmask = p.m == 32 ? 0xffffffffu : ((1u << p.m) - 1u);
+#pragma unroll
+  for (int a0 = 0; a0 < C::kMB; a0 += 2) {
+    const int a = a0 + lane / 32, j = lane % 32;
+    const int bit0 = (j >> ln) << lm;  // first dense row of the slot's group
+    const uint32_t bits = (Ms[a * (KB / 32) + bit0 / 32] >> (bit0 % 32)) & fmask;
+    int off = bit0 + select_bit(bits, j & (p.n - 1));
+    if (off > KB - 1) off = KB - 1;
+    const int kk = j >> 4, h = (j >> 3) & 1, q = (j >> 2) & 1, r = j & 3;
+    tab[a * 32 + 4 * (4 * h + r) + 2 * kk + q] = (uint8_t)off;
+  }
+}
+
+// Four halves of row k (this lane's own source row) for a transpose read.
+__device__ __forceinline__ s4v b_quad_row(const uint16_t* Bs, int k, int c0) {
+  const int lane = lane_id();
+  const int g = lane / 16, i = lane % 16;
+  const int n = c0 + 16 * (g & 1) + 4 * (i & 3);
+  const uint16_t* ptr = Bs + k * PBN + 8 * ((n / 8) ^ swz_b(k)) + 4 * ((n / 4) & 1);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(SA_LDS4(ptr));
+}
+
+template <int KB, int BM>
+__device__ __forceinline__ void shared_compute(const uint16_t* S, const uint8_t* tab,
+                                               f16v (&acc)[Shared<KB, BM>::kMB][2], int wm,
+                                               int wn) {
+  using C = Shared<KB, BM>;
+  constexpr int MB = C::kMB;
+  const int lane = lane_id();
+  const uint16_t* As = S;
+  const uint16_t* Bs = S + C::kAHalves;
+  uint32_t P[MB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+    P[a] = *reinterpret_cast<const uint32_t*>(tab + a * 32 + 4 * (4 * (lane / 32) + (lane % 16) / 4));
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    h8 aop[MB];
+#pragma unroll
+    for (int a = 0; a < MB; ++a) {
+      const int m = wm * (BM / 2) + 32 * a + lane % 32;
+      const int q = 2 * kk + lane / 32;
+      aop[a] = *reinterpret_cast<const h8*>(As + m * 32 + 8 * (q ^ swz_a(m)));
+    }
+#pragma unroll
+    for (int a = 0; a < MB; ++a) {
+      const int r0 = (int)((P[a] >> (16 * kk)) & 0xffu), r1 = (int)((P[a] >> (16 * kk + 8)) & 0xffu);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int c0 = wn * 64 + 32 * b;
+        const s4v q0 = b_quad_row(Bs, r0, c0), q1 = b_quad_row(Bs, r1, c0);
+        typedef short s8v __attribute__((ext_vector_type(8)));
+        const s8v both = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[a], __builtin_bit_cast(h8, both),
+                                                           acc[a][b], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int KB, int BM>
+__global__ __launch_bounds__(NTH, (Shared<KB, BM>::kWgsPerCu)) void k_gemm_shared(GParams p) {
+  using C = Shared<KB, BM>;
+  constexpr int MB = C::kMB;
+  constexpr int SH = C::kStageHalves;
+  constexpr int LPW = C::kLoadsPerWave;
+  __shared__ __align__(16) uint16_t S[C::kStages * SH];
+  __shared__ __align__(4) uint8_t tabs[4 * MB * 32];
+  const int lane = lane_id();
+  const int wave = (int)threadIdx.x / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  const int64_t mt = (p.T + BM - 1) / BM;
+  const int64_t ntl = (p.d_out + PBN - 1) / PBN;
+  int64_t mi, ni;
+  pipe_tile(blockIdx.x, mt, ntl, mi, ni);
+  const int64_t m0 = mi * BM, n0 = ni * PBN;
+  uint8_t* tab = tabs + wave * MB * 32;
+
+  f16v acc[MB][2];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // Three stages, loads two steps ahead (the dense engine's loop).  After
+  // each stage wait the wave builds its offset table from its own mask words
+  // (its own loads, so the wait alone orders them), then computes.
+  auto step = [&](int64_t t, int stage) {
+    const uint16_t* St = S + stage * SH;
+    shared_positions<KB, BM>(p, reinterpret_cast<const uint32_t*>(St + C::kAHalves + C::kBHalves) +
+                                    64 * wave, tab);
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    shared_compute<KB, BM>(St, tab, acc, wm, wn);
+    (void)t;
+  };
+  const int64_t nk = p.d_in / KB;
+  shared_issue<KB, BM>(p, m0, n0, 0, S);
+  if (nk > 1) shared_issue<KB, BM>(p, m0, n0, 1, S + SH);
+  for (int64_t t = 0; t < nk; ++t) {
+    const int stage = (int)(t % 3);
+    if (t + 1 < nk)
+      stage_barrier<LPW>();
+    else
+      stage_barrier<0>();
+    if (t + 2 < nk) shared_issue<KB, BM>(p, m0, n0, t + 2, S + ((stage + 2) % 3) * SH);
+    step(t, stage);
+  }
 
 #pragma unroll
   for (int a = 0; a < MB; ++a)
@@ -738,13 +989,16 @@ bool pipe_ok(const GParams& p) {
 // scattered to their set bits in an LDS tile and the workgroup's run of the
 // dense copy is written with 16-byte stores.  A mask word with more set bits
 // than that places only the first 32n/m values (no read past its run).
+// Token t reads mask row t / tt (tt = 1: per-token masks; tt > 1: one mask
+// row per tile of tt tokens).
 // ---------------------------------------------------------------------------
 constexpr int kExpandThreads = 256;
 
 template <int NV>  // 16-byte vectors of kept values per word (per = 8 NV); 0 = scalar loads
 __global__ __launch_bounds__(kExpandThreads) void k_nm_expand(const uint16_t* __restrict__ xval,
                                                               const uint32_t* __restrict__ mask,
-                                                              int64_t nwords, int per,
+                                                              int64_t nwords, int64_t wpr,
+                                                              int tt, int per,
                                                               uint16_t* __restrict__ xd) {
   __shared__ __align__(16) uint16_t tile[kExpandThreads * 32];
   const int tid = (int)threadIdx.x;
@@ -754,7 +1008,8 @@ __global__ __launch_bounds__(kExpandThreads) void k_nm_expand(const uint16_t* __
 #pragma unroll
   for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(mine + 8 * q) = u32x4{0u, 0u, 0u, 0u};
   if (w < nwords) {
-    uint32_t bits = mask[w];
+    const int64_t t = w / wpr;
+    uint32_t bits = mask[tt == 1 ? w : (t / tt) * wpr + (w - t * wpr)];
     const uint16_t* src = xval + w * per;
     if constexpr (NV > 0) {
       u32x4 v[NV];
@@ -784,19 +1039,23 @@ __global__ __launch_bounds__(kExpandThreads) void k_nm_expand(const uint16_t* __
 }
 
 hipError_t launch_nm_expand(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
-                            int n, int m, uint16_t* xd, hipStream_t s) {
-  const int64_t nwords = T * (d_in / 32);
+                            int n, int m, int tt, uint16_t* xd, hipStream_t s) {
+  const int64_t wpr = d_in / 32;
+  const int64_t nwords = T * wpr;
   const int per = 32 * n / m;
   const int64_t blocks = (nwords + kExpandThreads - 1) / kExpandThreads;
   if (blocks > 0x7fffffffLL) return hipErrorNotSupported;
   const dim3 grid((unsigned)blocks), block(kExpandThreads);
+#define SA_EXPAND(NV) \
+  hipLaunchKernelGGL(k_nm_expand<NV>, grid, block, 0, s, xval, mask, nwords, wpr, tt, per, xd)
   switch (per % 8 == 0 ? per / 8 : 0) {
-    case 1: hipLaunchKernelGGL(k_nm_expand<1>, grid, block, 0, s, xval, mask, nwords, per, xd); break;
-    case 2: hipLaunchKernelGGL(k_nm_expand<2>, grid, block, 0, s, xval, mask, nwords, per, xd); break;
-    case 3: hipLaunchKernelGGL(k_nm_expand<3>, grid, block, 0, s, xval, mask, nwords, per, xd); break;
-    case 4: hipLaunchKernelGGL(k_nm_expand<4>, grid, block, 0, s, xval, mask, nwords, per, xd); break;
-    default: hipLaunchKernelGGL(k_nm_expand<0>, grid, block, 0, s, xval, mask, nwords, per, xd);
+    case 1: SA_EXPAND(1); break;
+    case 2: SA_EXPAND(2); break;
+    case 3: SA_EXPAND(3); break;
+    case 4: SA_EXPAND(4); break;
+    default: SA_EXPAND(0);
   }
+#undef SA_EXPAND
   return hipGetLastError();
 }
 
@@ -858,7 +1117,84 @@ hipError_t launch_kind(const GParams& p, hipStream_t s) {
   return launch_tile<AK, 128>(p, s);
 }
 
+// Tile-shared engine: K step KB = 32 m / n dense rows (64 or 128), tile
+// height as the dense engine picks it (256 rows when they fill the CUs).
+bool shared_engine_ok(int64_t d_in, int n, int m, int tt) {
+  if (tt % 32 != 0 || n < 1 || 32 % n != 0 || (m != 2 * n && m != 4 * n)) return false;
+  return d_in % (32 * m / n) == 0;
+}
+
+template <int KB>
+hipError_t launch_shared_kb(const GParams& p, hipStream_t s) {
+  const int64_t ntl = (p.d_out + PBN - 1) / PBN;
+  const int64_t tiles256 = ((p.T + 255) / 256) * ntl;
+  const int bm = g_gemm_bm ? g_gemm_bm : (tiles256 < device_cus() ? 128 : 256);
+  const int64_t tiles = ((p.T + bm - 1) / bm) * ntl;
+  if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
+  if (bm == 256)
+    hipLaunchKernelGGL((k_gemm_shared<KB, 256>), dim3((unsigned)tiles), dim3(NTH), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemm_shared<KB, 128>), dim3((unsigned)tiles), dim3(NTH), 0, s, p);
+  return hipGetLastError();
+}
+
+// Whole-tile gather (one pattern per row tile: tt a multiple of 128): the
+// dense engine over d_in n / m compressed K, loading only the kept WT rows.
+bool gather_shape_ok(int64_t d_in, int n, int m, int tt) {
+  return tt % 128 == 0 && n >= 1 && 32 % n == 0 && n <= m && d_in % m == 0 &&
+         d_in <= 32 * kGatherMaskWords && (d_in / m * n) % 32 == 0;
+}
+
+hipError_t launch_gather(const GParams& p, hipStream_t s) {
+  const int64_t ntl = (p.d_out + PBN - 1) / PBN;
+  const int64_t tiles256 = ((p.T + 255) / 256) * ntl;
+  int bm = g_gemm_bm ? g_gemm_bm : ((p.tt % 256 == 0 && tiles256 >= device_cus()) ? 256 : 128);
+  if (p.tt % bm != 0) bm = 128;  // a tile of rows must share one pattern
+  const int64_t tiles = ((p.T + bm - 1) / bm) * ntl;
+  if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
+  const int ns = g_gemm_stages ? g_gemm_stages : 3;
+  if (bm == 256) return launch_pipe_stages<kAGather, 256>(p, tiles, ns, s);
+  return launch_pipe_stages<kAGather, 128>(p, tiles, ns, s);
+}
+
 }  // namespace
+
+size_t nm_shared_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m, int tt) {
+  if (gather_shape_ok(d_in, n, m, tt) || shared_engine_ok(d_in, n, m, tt)) return 0;
+  return (size_t)T * (size_t)d_in * 2;
+}
+
+hipError_t launch_nm_shared_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
+                                 int64_t d_in, int n, int m, int tt, const uint16_t* wt,
+                                 int64_t d_out, uint16_t* y, void* ws, size_t ws_bytes,
+                                 hipStream_t s) {
+  GParams p{};
+  p.x = xval;
+  p.mask = mask;
+  p.wt = wt;
+  p.y = y;
+  p.T = T;
+  p.d_in = d_in;
+  p.d_out = d_out;
+  p.n = n;
+  p.m = m;
+  p.tt = tt;
+  if (gather_shape_ok(d_in, n, m, tt)) return launch_gather(p, s);
+  if (shared_engine_ok(d_in, n, m, tt)) {
+    if (32 * m / n == 64) return launch_shared_kb<64>(p, s);
+    return launch_shared_kb<128>(p, s);
+  }
+  // any other tile or pattern: expand into the workspace, then dense
+  if (ws == nullptr || ws_bytes < nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt))
+    return hipErrorInvalidValue;
+  GParams pd = p;
+  pd.x = static_cast<const uint16_t*>(ws);
+  pd.mask = nullptr;
+  hipError_t e = launch_nm_expand(xval, mask, T, d_in, n, m, tt, static_cast<uint16_t*>(ws), s);
+  if (e != hipSuccess) return e;
+  if (g_gemm_engine != 1 && pipe_ok<kADense>(pd)) return launch_pipe<kADense>(pd, s);
+  return launch_kind<kADense>(pd, s);
+}
 
 int gemm_set_tuning(int bm, int engine, int stages) {
   if ((bm != 0 && bm != 128 && bm != 256) || engine < 0 || engine > 2 ||
@@ -914,7 +1250,8 @@ hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
     pd.x = static_cast<const uint16_t*>(ws);
     pd.mask = nullptr;
     if (pipe_ok<kADense>(pd)) {
-      hipError_t e = launch_nm_expand(xval, mask, T, d_in, n, m, static_cast<uint16_t*>(ws), s);
+      hipError_t e =
+          launch_nm_expand(xval, mask, T, d_in, n, m, 1, static_cast<uint16_t*>(ws), s);
       if (e != hipSuccess) return e;
       return launch_pipe<kADense>(pd, s);
     }

@@ -21,6 +21,8 @@ hipError_t launch_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int6
                                 int64_t cap, hipStream_t s);
 hipError_t launch_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
                               uint32_t* mask, uint16_t* val, hipStream_t s);
+hipError_t launch_sparsify_nm_shared(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
+                                     int tt, uint32_t* mask, uint16_t* val, hipStream_t s);
 
 // ---- calibration (calibrate.hip) ------------------------------------------
 hipError_t launch_calibrate(const uint16_t* samples, int64_t n, double s, float* t_out,
@@ -100,6 +102,11 @@ size_t nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m);
 hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
                           int n, int m, const uint16_t* wt, int64_t d_out, uint16_t* y,
                           void* ws, size_t ws_bytes, hipStream_t s);
+size_t nm_shared_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m, int tt);
+hipError_t launch_nm_shared_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
+                                 int64_t d_in, int n, int m, int tt, const uint16_t* wt,
+                                 int64_t d_out, uint16_t* y, void* ws, size_t ws_bytes,
+                                 hipStream_t s);
 int gemm_set_tuning(int bm, int engine, int stages);
 
 }  // namespace sa

@@ -520,6 +520,117 @@ hipError_t launch_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int6
   return hipGetLastError();
 }
 
+// ---- tile-shared N:M --------------------------------------------------------
+// One N:M pattern for each tile of tt consecutive rows.  A workgroup takes
+// one tile and 64 columns: thread (r, c) of its 4 x 64 covers column c in
+// rows r, r + 4, r + 8, ... of the tile.  A column's score is the sum of the
+// tile's |x| in fp64, which is exact (every fp16 magnitude is an integer
+// multiple of 2^-24 below 2^16; at most 256 of them sum below 2^24), so
+// neither the split over threads nor the order of the additions can change
+// a decision.  The first wave ranks each column within its group of M (kept
+// iff fewer than n of the group rank before it: a larger score, or an equal
+// one at a lower position) and a ballot gives the two mask words; then every
+// thread writes its rows' values at their compressed positions (the group's
+// first slot plus the kept bits before).
+constexpr int kSharedThreads = 256;
+constexpr int kSharedCols = 64;
+constexpr int kSharedSlices = kSharedThreads / kSharedCols;
+
+__device__ __forceinline__ double mag_f64(uint16_t b) {
+  return (double)__builtin_bit_cast(_Float16, (uint16_t)(b & 0x7fffu));
+}
+
+template <int M>
+__global__ __launch_bounds__(kSharedThreads) void k_sparsify_nm_shared(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t d, int n, int tt,
+    uint32_t* __restrict__ mask, uint16_t* __restrict__ val) {
+  __shared__ double part[kSharedSlices][kSharedCols];
+  __shared__ uint32_t words[2];
+  const int tid = (int)threadIdx.x;
+  const int r = tid / kSharedCols, c = tid % kSharedCols;
+  const int64_t t0 = (int64_t)blockIdx.x * tt;
+  const int64_t t1 = t0 + tt < rows ? t0 + tt : rows;
+  const int64_t k = (int64_t)blockIdx.y * kSharedCols + c;
+  const bool active = k < d;  // d % 32 == 0: whole mask words
+  constexpr int R = kSharedSlices;
+  double sc = 0.0;
+  if (active) {
+    const uint16_t* xp = x + (t0 + r) * d + k;
+    int64_t t = t0 + r;
+    for (; t + 3 * R < t1; t += 4 * R, xp += 4 * R * d) {
+      uint16_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = xp[u * R * d];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sc += mag_f64(v[u]);
+    }
+    for (; t < t1; t += R, xp += R * d) sc += mag_f64(*xp);
+  }
+  part[r][c] = sc;
+  __syncthreads();
+  if (r == 0) {
+    double own = 0.0;
+#pragma unroll
+    for (int q = 0; q < R; ++q) own += part[q][c];
+    part[0][c] = own;  // each lane reads and writes only its own column
+  }
+  __syncthreads();
+  if (r == 0) {
+    const double own = part[0][c];
+    const int g0 = c - c % M;
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < M; ++q) {
+      const double o = part[0][g0 + q];
+      rank += (o > own || (o == own && g0 + q < c)) ? 1 : 0;
+    }
+    const uint64_t ball = __ballot(active && rank < n);
+    if (c == 0) {
+      words[0] = (uint32_t)ball;
+      words[1] = (uint32_t)(ball >> 32);
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  const uint32_t word = words[c / 32];
+  const int b = c % 32;
+  if (r == 0 && b == 0) mask[(int64_t)blockIdx.x * (d / 32) + k / 32] = word;
+  if (((word >> b) & 1u) == 0u) return;
+  const int gb = b - b % M;
+  const int64_t slot = (k / M) * n + __builtin_popcount((word >> gb) & ((1u << (b - gb)) - 1u));
+  const int64_t vpr = d / M * n;
+  const uint16_t* xp = x + (t0 + r) * d + k;
+  uint16_t* vp = val + (t0 + r) * vpr + slot;
+  int64_t t = t0 + r;
+  for (; t + 3 * R < t1; t += 4 * R, xp += 4 * R * d, vp += 4 * R * vpr) {
+    uint16_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = xp[u * R * d];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vp[u * R * vpr] = v[u];
+  }
+  for (; t < t1; t += R, xp += R * d, vp += R * vpr) *vp = *xp;
+}
+
+hipError_t launch_sparsify_nm_shared(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
+                                     int tt, uint32_t* mask, uint16_t* val, hipStream_t s) {
+  const int64_t tiles = (rows + tt - 1) / tt;
+  const int64_t chunks = (d + kSharedCols - 1) / kSharedCols;
+  if (tiles > 0x7fffffffLL || chunks > 65535) return hipErrorNotSupported;
+  const dim3 grid((unsigned)tiles, (unsigned)chunks), block(kSharedThreads);
+#define SA_SHARED(MM) \
+  hipLaunchKernelGGL(k_sparsify_nm_shared<MM>, grid, block, 0, s, x, rows, d, n, tt, mask, val)
+  switch (m) {
+    case 4: SA_SHARED(4); break;
+    case 8: SA_SHARED(8); break;
+    case 16: SA_SHARED(16); break;
+    case 32: SA_SHARED(32); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SA_SHARED
+  return hipGetLastError();
+}
+
 hipError_t launch_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
                               uint32_t* mask, uint16_t* val, hipStream_t s) {
   const int64_t n8 = rows * d / 8;

@@ -132,6 +132,25 @@ int check_nm(const void* x, int64_t rows, int64_t d, int n, int m, const void* m
   return SA_OK;
 }
 
+int check_nm_shared(const void* x, int64_t rows, int64_t d, int n, int m, int tt,
+                    const void* mask, const void* val) {
+  const char* fn = "act_sparsify_nm_shared";
+  REQUIRE(rows >= 0, SA_ERR_INVALID_ARG, "%s: rows must be >= 0", fn);
+  REQUIRE(m == 4 || m == 8 || m == 16 || m == 32, SA_ERR_INVALID_ARG,
+          "%s: m must be 4, 8, 16 or 32 (got %d)", fn, m);
+  REQUIRE(n >= 1 && n <= m, SA_ERR_INVALID_ARG, "%s: n = %d not in [1, m = %d]", fn, n, m);
+  REQUIRE(tt >= 1 && tt <= 256, SA_ERR_INVALID_ARG, "%s: tt = %d not in [1, 256]", fn, tt);
+  REQUIRE(d >= 32 && d % 32 == 0, SA_ERR_INVALID_ARG,
+          "%s: d must be a positive multiple of 32 (got %lld)", fn, (long long)d);
+  REQUIRE(x != nullptr && mask != nullptr && val != nullptr, SA_ERR_INVALID_ARG,
+          "%s: x, mask and val must not be NULL", fn);
+  REQUIRE(aligned(x, 16), SA_ERR_INVALID_ARG, "%s: x must be 16-byte aligned", fn);
+  REQUIRE(aligned(mask, 4) && aligned(val, 2), SA_ERR_INVALID_ARG,
+          "%s: mask must be 4-byte and val 2-byte aligned", fn);
+  REQUIRE(d <= (int64_t)65535 * 64, SA_ERR_UNSUPPORTED, "%s: d too large", fn);
+  return SA_OK;
+}
+
 int check_calibrate(const void* samples, int64_t n, double s, const void* t_out) {
   const char* fn = "act_calibrate_threshold";
   REQUIRE(samples != nullptr && t_out != nullptr, SA_ERR_INVALID_ARG,
@@ -213,6 +232,24 @@ int check_col_norms(const void* wt, int64_t d_in, int64_t d_out, const void* out
 int check_nm_spmm(const void* xval, const void* mask, int64_t T, int64_t d_in, int n, int m,
                   const void* wt, int64_t d_out, const void* y) {
   const char* fn = "nm_act_spmm";
+  REQUIRE(T >= 0, SA_ERR_INVALID_ARG, "%s: T must be >= 0", fn);
+  REQUIRE(m == 4 || m == 8 || m == 16 || m == 32, SA_ERR_INVALID_ARG,
+          "%s: m must be 4, 8, 16 or 32", fn);
+  REQUIRE(n >= 1 && n <= m, SA_ERR_INVALID_ARG, "%s: n not in [1, m]", fn);
+  REQUIRE(d_in >= 32 && d_in % 32 == 0, SA_ERR_INVALID_ARG,
+          "%s: d_in must be a positive multiple of 32", fn);
+  REQUIRE(d_out >= 8 && d_out % 8 == 0, SA_ERR_INVALID_ARG,
+          "%s: d_out must be a positive multiple of 8", fn);
+  REQUIRE(xval && mask && wt && y, SA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  REQUIRE(aligned(wt, 16) && aligned(y, 16) && aligned(mask, 4) && aligned(xval, 16),
+          SA_ERR_INVALID_ARG, "%s: wt, y and xval must be 16-byte aligned, mask 4-byte", fn);
+  return SA_OK;
+}
+
+int check_nm_shared_spmm(const void* xval, const void* mask, int64_t T, int64_t d_in, int n,
+                         int m, int tt, const void* wt, int64_t d_out, const void* y) {
+  const char* fn = "nm_shared_spmm";
+  REQUIRE(tt >= 1 && tt <= 256, SA_ERR_INVALID_ARG, "%s: tt = %d not in [1, 256]", fn, tt);
   REQUIRE(T >= 0, SA_ERR_INVALID_ARG, "%s: T must be >= 0", fn);
   REQUIRE(m == 4 || m == 8 || m == 16 || m == 32, SA_ERR_INVALID_ARG,
           "%s: m must be 4, 8, 16 or 32", fn);

@@ -25,6 +25,8 @@ int check_topk(const void* x, int64_t rows, int64_t d, int64_t k, const void* ma
                const void* idx, const void* val, const void* nnz, int64_t cap);
 int check_nm(const void* x, int64_t rows, int64_t d, int n, int m, const void* mask,
              const void* val);
+int check_nm_shared(const void* x, int64_t rows, int64_t d, int n, int m, int tt,
+                    const void* mask, const void* val);
 int check_calibrate(const void* samples, int64_t n, double s, const void* t_out);
 
 // GEMV family.  `need_ws` is the workspace the call requires.
@@ -39,6 +41,8 @@ int check_swiglu(const void* g, const void* u, const void* colnorm, int64_t d_ff
 int check_col_norms(const void* wt, int64_t d_in, int64_t d_out, const void* out);
 int check_nm_spmm(const void* xval, const void* mask, int64_t T, int64_t d_in, int n, int m,
                   const void* wt, int64_t d_out, const void* y);
+int check_nm_shared_spmm(const void* xval, const void* mask, int64_t T, int64_t d_in, int n,
+                         int m, int tt, const void* wt, int64_t d_out, const void* y);
 int check_dense_gemm(const void* x, int64_t T, int64_t d_in, const void* wt, int64_t d_out,
                      const void* y);
 

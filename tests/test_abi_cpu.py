@@ -84,6 +84,50 @@ def test_nm_checks(sa):
     assert f(P, 0, 64, 2, 4, P, P, None) == SA_OK
 
 
+def test_nm_shared_checks(sa):
+    f = sa.act_sparsify_nm_shared  # (x, rows, d, n, m, tt, mask, val, stream)
+    assert f(P, 4, 64, 2, 4, 0, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 4, 64, 2, 4, 257, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 4, 64, 2, 6, 32, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 4, 64, 5, 4, 32, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 4, 64, 0, 4, 32, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 4, 48, 2, 4, 32, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(None, 4, 64, 2, 4, 32, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P + 8, 4, 64, 2, 4, 32, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 4, 64, 2, 4, 32, P + 2, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, -1, 64, 2, 4, 32, P, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 0, 64, 2, 4, 32, P, P, None) == SA_OK  # nothing to do
+
+    g = sa.nm_shared_spmm  # (xval, mask, T, d_in, n, m, tt, wt, d_out, y, ws, ws_bytes, stream)
+    assert g(P, P, 4, 64, 2, 4, 0, P, 64, P, None, 0, None) == SA_ERR_INVALID_ARG
+    assert g(P, P, 4, 64, 2, 4, 300, P, 64, P, None, 0, None) == SA_ERR_INVALID_ARG
+    assert g(P, P, 4, 64, 2, 5, 32, P, 64, P, None, 0, None) == SA_ERR_INVALID_ARG
+    assert g(P, P, 4, 40, 2, 4, 32, P, 64, P, None, 0, None) == SA_ERR_INVALID_ARG
+    assert g(P, P, 4, 64, 2, 4, 32, P, 60, P, None, 0, None) == SA_ERR_INVALID_ARG
+    assert g(P, P, 4, 64, 2, 4, 32, P + 8, 64, P, None, 0, None) == SA_ERR_INVALID_ARG
+    assert g(P, None, 4, 64, 2, 4, 32, P, 64, P, None, 0, None) == SA_ERR_INVALID_ARG
+    # the expansion path needs a workspace: refused on the host, before any launch
+    assert g(P, P, 4, 64, 3, 4, 32, P, 64, P, None, 0, None) == SA_ERR_WORKSPACE
+    assert g(P, P, 4, 64, 3, 4, 32, P, 64, P, P, 100, None) == SA_ERR_WORKSPACE
+    assert g(P, P, 4, 64, 8, 16, 16, P, 64, P, None, 0, None) == SA_ERR_WORKSPACE
+    assert g(P, P, 4, 64, 3, 4, 32, P, 64, P, P + 8, 4 * 64 * 2, None) == SA_ERR_INVALID_ARG
+    assert g(P, P, 0, 64, 2, 4, 32, P, 64, P, None, 0, None) == SA_OK  # nothing to do
+
+    ws = sa.sa_nm_shared_spmm_workspace_bytes  # (T, d_in, n, m, tt)
+    assert ws(100, 1024, 8, 16, 32) == 0
+    assert ws(100, 1024, 4, 16, 64) == 0
+    assert ws(100, 1024, 8, 16, 16) == 100 * 1024 * 2
+    assert ws(100, 1056, 8, 16, 32) == 100 * 1056 * 2  # d_in not a multiple of the K step
+    assert ws(100, 1024, 3, 4, 32) == 100 * 1024 * 2
+    assert ws(100, 1024, 1, 8, 32) == 100 * 1024 * 2   # m / n = 8
+    assert ws(100, 1024, 32, 32, 32) == 100 * 1024 * 2  # m / n = 1
+    assert ws(100, 1024, 1, 8, 128) == 0               # whole-tile gather
+    assert ws(100, 1024, 3, 4, 128) == 100 * 1024 * 2   # n does not divide 32
+    assert ws(10, 65536, 1, 8, 128) == 10 * 65536 * 2   # mask row beyond the LDS copy
+    assert ws(0, 1024, 8, 16, 32) == 0
+    assert ws(100, 1024, 8, 16, 0) == 0
+
+
 def test_calibrate_checks(sa):
     f = sa.act_calibrate_threshold
     assert f(P, 0, 0.5, P, None) == SA_ERR_INVALID_ARG

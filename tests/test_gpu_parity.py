@@ -762,6 +762,162 @@ def test_nm_spmm_full_shapes_sampled(T, d_in, d_out, n, m):
 
 
 # ---------------------------------------------------------------------------
+# tile-shared N:M: sparsifier and matmul
+# ---------------------------------------------------------------------------
+
+SHARED_PATTERNS = [(2, 4), (1, 4), (3, 4), (4, 8), (2, 8), (7, 8), (8, 16), (4, 16), (5, 16),
+                   (16, 32), (8, 32), (32, 32)]
+
+
+def shared_whole_tile(d_in, n, m, tt):
+    """Conditions of the whole-tile gather (one pattern per row tile)."""
+    return (tt % 128 == 0 and 32 % n == 0 and d_in % m == 0 and d_in <= 32768
+            and (d_in // m * n) % 32 == 0)
+
+
+def shared_per_block(d_in, n, m, tt):
+    """Conditions of the per-32-row-block gather."""
+    return tt % 32 == 0 and 32 % n == 0 and m in (2 * n, 4 * n) and d_in % (32 * m // n) == 0
+
+
+@pytest.mark.parametrize("n,m", SHARED_PATTERNS)
+@pytest.mark.parametrize("T,d,tt", [(1, 32, 32), (70, 1056, 32), (33, 64, 1), (100, 2048, 7),
+                                    (300, 1024, 64), (257, 96, 256), (64, 3072, 32)])
+def test_nm_shared_sparsify(T, d, tt, n, m):
+    """Masks and values bit-exact: ragged last tiles, partial column chunks,
+    one-row tiles and the largest tile."""
+    X = syn.gaussian_f16((T, d), 1.0, T * 13 + d + tt)
+    _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+    mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), n, m, tt)
+    assert np.array_equal(words(mask_g), sparsify.pack_mask(tile_keep))
+    assert np.array_equal(host(val_g).view(np.uint16), vals.view(np.uint16))
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (3, 8), (8, 16), (16, 32), (5, 32)])
+def test_nm_shared_sparsify_ties(n, m):
+    """Few distinct magnitudes (tied tile sums decide most groups), a tile
+    of equal magnitudes (the first n of each group) and signed zeros."""
+    rng = np.random.default_rng(n * 100 + m)
+    pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0], dtype=np.float16)
+    X = pool[rng.integers(0, len(pool), size=(100, 1024))]
+    X[32:64] = np.float16(-0.25)
+    X[64:96] = np.float16(-0.0)
+    _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, 32)
+    mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), n, m, 32)
+    assert np.array_equal(words(mask_g), sparsify.pack_mask(tile_keep))
+    assert np.array_equal(host(val_g).view(np.uint16), vals.view(np.uint16))
+    first_n = np.tile(np.arange(m) < n, 1024 // m)
+    assert np.array_equal(tile_keep[1], first_n) and np.array_equal(tile_keep[2], first_n)
+
+
+@pytest.mark.parametrize("tile_rows", [0, 128, 256])
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (4, 8), (2, 8), (8, 16), (4, 16), (16, 32),
+                                 (8, 32)])
+@pytest.mark.parametrize("T,d_in,d_out,tt", [(64, 1024, 512, 32), (100, 256, 136, 32),
+                                             (300, 384, 264, 64), (33, 128, 8, 32),
+                                             (1, 512, 1000, 32), (257, 640, 128, 96)])
+def test_nm_shared_spmm_gathering_kernel(T, d_in, d_out, tt, n, m, tile_rows):
+    """The kernel that gathers WT rows per 32-row block: 1 to 16 K steps of
+    64 or 128 dense rows, ragged rows and columns, tiles of 32 to 96 rows,
+    both tile heights."""
+    assert shared_per_block(d_in, n, m, tt) and not shared_whole_tile(d_in, n, m, tt)
+    assert sa.lib().sa_nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt) == 0
+    X = syn.gaussian_f16((T, d_in), 1.0, T + d_in + n)
+    wt = syn.weight_t(d_out, d_in, d_out + m)
+    _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+    mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), n, m, tt)
+    try:
+        sa.set_gemm_tuning(tile_rows, 0, 0)
+        Y = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, dev(wt))
+    finally:
+        sa.set_gemm_tuning(0, 0, 0)
+    assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
+
+
+@pytest.mark.parametrize("n,m,tt", [(3, 4, 32), (5, 16, 32), (7, 8, 64), (8, 16, 1), (8, 16, 16),
+                                    (2, 4, 7), (16, 32, 48), (1, 8, 32), (4, 32, 32), (32, 32, 32),
+                                    (4, 4, 64), (3, 4, 128), (5, 8, 256)])
+def test_nm_shared_spmm_expanded(n, m, tt):
+    """Tiles and patterns outside the gathering kernels: expansion into the
+    workspace, then the dense matmul."""
+    T, d_in, d_out = 130, 256, 264
+    assert not shared_per_block(d_in, n, m, tt) and not shared_whole_tile(d_in, n, m, tt)
+    assert sa.lib().sa_nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt) == T * d_in * 2
+    X = syn.gaussian_f16((T, d_in), 1.0, n * 7 + m + tt)
+    wt = syn.weight_t(d_out, d_in, 3 * m)
+    _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+    mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), n, m, tt)
+    Y = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, dev(wt))
+    assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
+
+
+@pytest.mark.parametrize("tile_rows", [0, 128, 256])
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (8, 16), (4, 16), (16, 32), (8, 32), (1, 8),
+                                 (2, 32), (32, 32), (4, 8)])
+@pytest.mark.parametrize("T,d_in,d_out,tt", [(256, 1024, 512, 128), (300, 512, 136, 128),
+                                             (129, 2048, 264, 256), (1, 4096, 8, 128),
+                                             (513, 768, 1000, 256), (640, 256, 128, 128)])
+def test_nm_shared_spmm_whole_tile(T, d_in, d_out, tt, n, m, tile_rows):
+    """One pattern per row tile: only the kept WT rows are loaded and the
+    dense engine runs over d_in n / m compressed entries (1 to 64 K steps
+    of 32), ragged rows and columns, both tile heights where the tile
+    allows them."""
+    if not shared_whole_tile(d_in, n, m, tt):
+        pytest.skip("d_in n / m not a multiple of 32")
+    assert sa.lib().sa_nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt) == 0
+    X = syn.gaussian_f16((T, d_in), 1.0, 2 * T + d_in + n)
+    wt = syn.weight_t(d_out, d_in, d_out + m + 1)
+    _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+    mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), n, m, tt)
+    assert np.array_equal(words(mask_g), sparsify.pack_mask(tile_keep))
+    try:
+        sa.set_gemm_tuning(tile_rows, 0, 0)
+        Y = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, dev(wt))
+    finally:
+        sa.set_gemm_tuning(0, 0, 0)
+    assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
+
+
+@pytest.mark.parametrize("stages", [3, 4, 6])
+def test_nm_shared_whole_tile_stages_agree(stages):
+    """Every stage count gives the same bits (the MFMA sequence does not
+    depend on it)."""
+    T, d_in, d_out, tt = 384, 2048, 264, 128
+    X = syn.gaussian_f16((T, d_in), 1.0, 77)
+    wt_g = dev(syn.weight_t(d_out, d_in, 78))
+    mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), 8, 16, tt)
+    base = sa.nm_shared_spmm(val_g, mask_g, 8, 16, tt, wt_g).clone()
+    try:
+        sa.set_gemm_tuning(0, 0, stages)
+        Y = sa.nm_shared_spmm(val_g, mask_g, 8, 16, tt, wt_g)
+    finally:
+        sa.set_gemm_tuning(0, 0, 0)
+    assert torch.equal(Y, base)
+
+
+@pytest.mark.parametrize("T,d_in,d_out", [(4096, 1024, 1024), (2048, 4096, 11008)])
+@pytest.mark.parametrize("n,m,tt", [(2, 4, 32), (8, 16, 32), (16, 32, 32), (4, 16, 32),
+                                    (8, 16, 128), (4, 16, 128), (8, 16, 256), (2, 4, 256)])
+def test_nm_shared_full_shapes_sampled(T, d_in, d_out, n, m, tt):
+    """Full sizes in the benchmarked launches: the masks of sampled tiles
+    bit-exact, sampled rows against the oracle."""
+    X = syn.gaussian_f16((T, d_in), 1.0, 5)
+    wt = syn.weight_t(d_out, d_in, 41)
+    X_g, wt_g = dev(X), dev(wt)
+    mask_g, val_g = sa.act_sparsify_nm_shared(X_g, n, m, tt)
+    Y = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, wt_g)
+    rows = np.random.default_rng(T + n + tt).choice(T, size=6, replace=False)
+    rows = np.concatenate([rows, [0, T - 1]])
+    mw = words(mask_g)
+    for r in rows:
+        g = int(r) // tt
+        _, tile_keep, vals = sparsify.nm_shared_sparsify(X[g * tt:(g + 1) * tt], n, m, tt)
+        assert np.array_equal(mw[g], sparsify.pack_mask(tile_keep)[0])
+        ref = spmm.nm_shared_spmm(vals[int(r) - g * tt][None], tile_keep, tt, wt)
+        assert_close(Y[int(r)][None], ref)
+
+
+# ---------------------------------------------------------------------------
 # roofline calibration kernel
 # ---------------------------------------------------------------------------
 
