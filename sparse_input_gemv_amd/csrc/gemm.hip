@@ -399,7 +399,11 @@ struct Pipe<kA24, BM> {
 // on the compressed values and the kept rows of WT (see pipe_issue).
 template <int BM>
 struct Pipe<kAGather, BM> : Pipe<kADense, BM> {};
-constexpr int kGatherMaskWords = 1024;  // the tile's mask row in LDS: d_in <= 32768
+// The tile's pattern in LDS, 4 KB: a byte per kept entry (its position in
+// its 32-column mask word) when d_in n / m <= 4096, else the mask row
+// itself (d_in <= 32768), searched per load.
+constexpr int kGatherMaskWords = 1024;
+constexpr int kGatherTableBytes = 4 * kGatherMaskWords;
 
 template <int AK, int BM>
 constexpr int pipe_stage_halves() {
@@ -493,6 +497,16 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
   uint16_t* Bs = S + Pipe<AK, BM>::kAHalves;
   constexpr int BK = Pipe<AK, BM>::kBK;
   constexpr int AI = BM / 64;  // A instructions per wave
+  // gather, byte-table mode: this lane's two B rows of the step in one read,
+  // issued before the A loads so that its latency overlaps them
+  static_assert(AK != kAGather || BK / 16 == 2, "two B loads per lane and step");
+  uint32_t pair = 0;
+  const bool table = AK == kAGather && p.d_in / p.m * p.n <= kGatherTableBytes;
+  if constexpr (AK == kAGather) {
+    if (table)
+      pair = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(mrow) + k0 +
+                                                 8 * w + 2 * (lane / 16));
+  }
   if constexpr (AK == kADense || AK == kAGather) {
     // gather: A rows are the compressed values, d_in n / m long
     const int64_t lda = AK == kAGather ? p.d_in / p.m * p.n : p.d_in;
@@ -538,10 +552,13 @@ __device__ __forceinline__ void pipe_issue(const GParams& p, int64_t m0, int64_t
     int64_t row = k0 + k;
     if constexpr (AK == kAGather) {
       // compressed entry j = k0 + k: mask word j / per (per = 32 n / m kept
-      // entries per word, a power of two), its (j mod per)-th set bit
+      // entries per word, a power of two), its (j mod per)-th set bit, read
+      // from the byte table or found in the mask word
       const int lper = __builtin_ctz((unsigned)(32 / p.m * p.n));
       const int64_t wd = row >> lper;
-      row = 32 * wd + select_bit(mrow[wd], (int)(row & ((1 << lper) - 1)));
+      const int pos = table ? (int)((pair >> (8 * i)) & 0xffu)
+                            : select_bit(mrow[wd], (int)(row & ((1 << lper) - 1)));
+      row = 32 * wd + pos;
       if (row > p.d_in - 1) row = p.d_in - 1;
     }
     load_to_lds16(p.wt + row * p.d_out + n, Bs + kb * PBN);
@@ -658,8 +675,8 @@ __device__ __forceinline__ void stage_barrier_upto(int n) {
 
 // The whole K loop over NS stages, loads NS - 1 steps ahead.  Step t waits
 // for its own stage (t % NS), refills stage (t - 1) % NS -- read by step t - 1,
-// which every wave finished before the barrier -- with step t + NS - 1, then
-// computes.  The main loop runs while every refill exists, with no branch
+// which every wave finished before the barrier -- with step t + NS - 1, and
+// computes (the gather kind computes first, then refills).  The main loop runs while every refill exists, with no branch
 // inside; the last steps (fewer than 2 NS - 1) run in the tail, each waiting
 // for exactly the later loads that exist.
 template <int AK, int BM, int NS>
@@ -672,6 +689,9 @@ __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_
   constexpr int D = NS - 1;  // prefetch distance in steps
   static_assert(NS >= 3 && (D - 1) * LPW < 64, "stage count / vmcnt range");
   const int64_t nk = (AK == kAGather ? p.d_in / p.m * p.n : p.d_in) / BK;
+  // gather: the B rows need a table lookup before their loads; issued after
+  // the step's MFMAs, that latency overlaps them instead of delaying them
+  constexpr bool kIssueLate = AK == kAGather;
 #pragma unroll
   for (int j = 0; j < D; ++j)
     if (j < nk) pipe_issue<AK, BM>(p, m0, n0, j * BK, S + j * SH, mrow);
@@ -680,8 +700,13 @@ __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       stage_barrier<(D - 1) * LPW>();
-      pipe_issue<AK, BM>(p, m0, n0, (kt + j + D) * BK, S + ((j + D) % NS) * SH, mrow);
-      pipe_compute<AK, BM>(S + j * SH, code_lut, acc, wm, wn);
+      if constexpr (kIssueLate) {
+        pipe_compute<AK, BM>(S + j * SH, code_lut, acc, wm, wn);
+        pipe_issue<AK, BM>(p, m0, n0, (kt + j + D) * BK, S + ((j + D) % NS) * SH, mrow);
+      } else {
+        pipe_issue<AK, BM>(p, m0, n0, (kt + j + D) * BK, S + ((j + D) % NS) * SH, mrow);
+        pipe_compute<AK, BM>(S + j * SH, code_lut, acc, wm, wn);
+      }
     }
   }
 #pragma unroll
@@ -690,9 +715,11 @@ __device__ __forceinline__ void pipe_k_loop(const GParams& p, int64_t m0, int64_
     if (t < nk) {
       const int64_t later = nk - 1 - t;
       stage_barrier_upto<LPW, D - 1>(later < D - 1 ? (int)later : D - 1);
-      if (t + D < nk)
+      if (!kIssueLate && t + D < nk)
         pipe_issue<AK, BM>(p, m0, n0, (t + D) * BK, S + ((j + D) % NS) * SH, mrow);
       pipe_compute<AK, BM>(S + (j % NS) * SH, code_lut, acc, wm, wn);
+      if (kIssueLate && t + D < nk)
+        pipe_issue<AK, BM>(p, m0, n0, (t + D) * BK, S + ((j + D) % NS) * SH, mrow);
     }
   }
 }
@@ -742,13 +769,31 @@ __global__ __launch_bounds__(NTH, (pipe_wgs_per_cu<AK, BM, NS>())) void k_gemm_p
   // the first stage barrier orders these writes before any read
   __shared__ uint8_t code_lut[AK == kA24 ? 256 : 1];
   if constexpr (AK == kA24) code_lut[threadIdx.x] = (uint8_t)code_of(threadIdx.x);
-  // gather: the row tile's mask row (one pattern for all its rows), read by
-  // every B load of the K loop
+  // gather: the row tile's pattern (one for all its rows), read by every B
+  // load of the K loop: the byte table of kept positions, built here one
+  // mask word per thread (a word holds per = 32 n / m kept entries, at a
+  // fixed offset of the table), or the mask row itself
   __shared__ uint32_t mrow[AK == kAGather ? kGatherMaskWords : 1];
   if constexpr (AK == kAGather) {
     const int64_t wpr = p.d_in / 32;
     const uint32_t* src = p.mask + (m0 / p.tt) * wpr;
-    for (int64_t i = threadIdx.x; i < wpr; i += NTH) mrow[i] = src[i];
+    if (p.d_in / p.m * p.n <= kGatherTableBytes) {
+      // entry j at byte (j & ~7) | (j & 3) << 1 | (j >> 2) & 1: the entries
+      // j and j + 4 that one lane loads in a step sit side by side
+      const int per = 32 / p.m * p.n;
+      uint8_t* tab = reinterpret_cast<uint8_t*>(mrow);
+      for (int64_t i = threadIdx.x; i < wpr; i += NTH) {
+        uint32_t bits = src[i];
+        for (int e = 0; e < per; ++e) {
+          const int64_t j = i * per + e;
+          tab[(j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1)] =
+              (uint8_t)(bits ? __builtin_ctz(bits) : 31);
+          bits &= bits - 1u;
+        }
+      }
+    } else {
+      for (int64_t i = threadIdx.x; i < wpr; i += NTH) mrow[i] = src[i];
+    }
     __syncthreads();
   }
   pipe_k_loop<AK, BM, NS>(p, m0, n0, S, code_lut, mrow, acc, wm, wn);

@@ -878,6 +878,22 @@ def test_nm_shared_spmm_whole_tile(T, d_in, d_out, tt, n, m, tile_rows):
     assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
 
 
+@pytest.mark.parametrize("n,m", [(8, 16), (1, 4), (16, 32), (2, 4), (4, 8)])
+@pytest.mark.parametrize("d_in", [8256, 16384])
+def test_nm_shared_whole_tile_long_k(d_in, n, m):
+    """The kept positions come from a byte table up to 4096 kept entries per
+    row and from the mask words beyond: both sides of that limit."""
+    T, d_out, tt = 130, 264, 128
+    if not shared_whole_tile(d_in, n, m, tt):
+        pytest.skip("d_in n / m not a multiple of 32")
+    X = syn.gaussian_f16((T, d_in), 1.0, d_in + n)
+    wt = syn.weight_t(d_out, d_in, 9 + m)
+    _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+    mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), n, m, tt)
+    Y = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, dev(wt))
+    assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
+
+
 @pytest.mark.parametrize("stages", [3, 4, 6])
 def test_nm_shared_whole_tile_stages_agree(stages):
     """Every stage count gives the same bits (the MFMA sequence does not
