@@ -347,6 +347,21 @@ __global__ __launch_bounds__(NT) void k_sparsify_topk(
 constexpr int kNmThreads = 256;
 constexpr int kNmPerBlock = kNmThreads * 8;
 
+// Exchanges within an aligned quad of lanes by DPP quad permutes (a VALU
+// operand modifier, no LDS round trip).  quad_perm control: lane i of the
+// quad reads lane ((ctrl >> 2i) & 3).
+template <int CTRL>
+__device__ __forceinline__ int quad_perm(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+constexpr int kQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
+// lane q of each aligned group of G (G = 2 or 4) lanes, to every lane of it
+template <int G, int Q>
+constexpr int quad_bcast() {
+  return G == 4 ? Q * 0x55 : (Q | (Q << 2) | ((2 + Q) << 4) | ((2 + Q) << 6));
+}
+
 template <int M>
 __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __restrict__ x,
                                                             int64_t n8, int n,
@@ -397,11 +412,24 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
   } else {
     constexpr int G = M / 8;  // threads per group, aligned lane runs
     const int gl = lane & (G - 1);
-    const int base_lane = lane - gl;
+    static_assert(G == 2 || G == 4, "groups within a lane quad");
     auto group_sum = [&](int c) {
-#pragma unroll
-      for (int o = 1; o < G; o <<= 1) c += __shfl_xor(c, o, kWave);
+      c += quad_perm<kQuadXor1>(c);
+      if constexpr (G == 4) c += quad_perm<kQuadXor2>(c);
       return c;
+    };
+    // exclusive prefix over the group's lanes of a per-lane count
+    auto group_prefix = [&](int x) {
+      int e = 0;
+      const int x0 = quad_perm<quad_bcast<G, 0>()>(x);
+      e += gl > 0 ? x0 : 0;
+      if constexpr (G == 4) {
+        const int x1 = quad_perm<quad_bcast<G, 1>()>(x);
+        const int x2 = quad_perm<quad_bcast<G, 2>()>(x);
+        e += gl > 1 ? x1 : 0;
+        e += gl > 2 ? x2 : 0;
+      }
+      return e;
     };
     // tau = largest key value v with #(keys >= v) >= n: the n-th largest
     int tau = 0;
@@ -420,12 +448,7 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
       eq += key[i] == tau ? 1 : 0;
     }
     const int need = n - group_sum(gt);  // ties at tau still to keep
-    int e = 0;  // ties at tau in lower lanes of the group
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-      const int c = __shfl(eq, base_lane + q, kWave);
-      e += (q < gl) ? c : 0;
-    }
+    int e = group_prefix(eq);             // ties at tau in lower lanes of the group
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (key[i] > tau) {
@@ -436,13 +459,7 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
       }
     }
     // kept entries in lower lanes of the group come first
-    const int mine = __popc(keep);
-    int pre = 0;
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-      const int c = __shfl(mine, base_lane + q, kWave);
-      pre += (q < gl) ? c : 0;
-    }
+    const int pre = group_prefix(__popc(keep));
     if (active) {
       int slot = (tid / G) * n + pre;
 #pragma unroll
@@ -450,10 +467,10 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
         if ((keep >> i) & 1u) outs[slot++] = v[i];
     }
   }
-  // four neighbouring threads make one 32-bit mask word
+  // four neighbouring threads (a lane quad) make one 32-bit mask word
   uint32_t w = keep << (8 * (lane & 3));
-  w |= (uint32_t)__shfl_xor((int)w, 1, kWave);
-  w |= (uint32_t)__shfl_xor((int)w, 2, kWave);
+  w |= (uint32_t)quad_perm<kQuadXor1>((int)w);
+  w |= (uint32_t)quad_perm<kQuadXor2>((int)w);
   if (active && (lane & 3) == 0) mask[g8 >> 2] = w;
 
   __syncthreads();
