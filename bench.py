@@ -554,6 +554,15 @@ def suite_swiglu(sa, syn, dev, ev_time, emit, rotation):
     x_dense = torch.from_numpy(syn.gaussian_f16((d_ff,), 1.0, 0)).to(dev)
     us_d = ev_time(lambda i: sa.dense_gemv(rot[i % nr], x_dense, y=y), 500)
     emit("a8", f"dense_gemv down {d_model}x{d_ff}", us_d, bytes_=2 * d_model * d_ff + 2 * d_ff + 2 * d_model)
+    # the MLP's two dense projections (gate, up: d_ff x d_model), for the MLP totals
+    rot_gu = rotation(d_ff, d_model, 32)
+    x_in = torch.from_numpy(syn.gaussian_f16((d_model,), 1.0, 1)).to(dev)
+    y_ff = torch.empty((d_ff,), dtype=torch.float16, device=dev)
+    us_gu = ev_time(lambda i: sa.dense_gemv(rot_gu[i % len(rot_gu)], x_in, y=y_ff), 500)
+    emit("a8", f"dense_gemv gate/up {d_ff}x{d_model}", us_gu,
+         bytes_=2 * d_model * d_ff + 2 * d_ff + 2 * d_model)
+    del rot_gu
+    mlp_dense = 2 * us_gu + us_d
     for mode in ("cats", "rana"):
         for rate in (0.5, 0.7):
             # threshold at the score quantile of this draw (the library's own calibration)
@@ -571,6 +580,9 @@ def suite_swiglu(sa, syn, dev, ev_time, emit, rotation):
             emit("a6", f"masked_swiglu_down {mode} mask rate {rate}", us,
                  bytes_=2 * d_model * nnz + 4 * d_ff + extra + 2 * d_model, flops=2 * d_model * nnz,
                  kept=nnz, speedup_vs_dense_down=round(us_d / us, 3))
+            emit("a6", f"Llama-3-8B MLP: dense gate + up, {mode} masked down at {rate} "
+                 "vs the dense MLP (sum of calls)", 2 * us_gu + us, dense_mlp_us=round(mlp_dense, 3),
+                 speedup_vs_dense_mlp=round(mlp_dense / (2 * us_gu + us), 3))
     us_c = ev_time(lambda i: sa.weight_col_norms(rot[i % nr]), 50)
     emit("a6", f"weight_col_norms {d_ff}x{d_model}", us_c, bytes_=2 * d_ff * d_model + 8 * d_ff)
     del rot
