@@ -6,10 +6,16 @@
 // large batches the activations of every token are N:M sparse -- Block
 // Q-Sparse -- and the product is measured against a dense matmul.)
 //
-// One tile engine: a 256-thread workgroup computes a BM x 128 output tile
-// (BM = 256 or 128) with four waves (2 x 2), each wave (BM/2) x 64 = (BM/64)
-// x 2 blocks of 32 x 32.  The K loop steps by 32 with double-buffered LDS
-// tiles:
+// Three engines live here: the pipelined engine (k_gemm_pipe: dense, 2:4 on
+// the sparse MFMA, and the whole-tile gather of tile-shared N:M), the
+// per-32-row-block gather of tile-shared N:M (k_gemm_shared), and the
+// staged-register engine described next (k_gemm), which takes every shape
+// the others do not.
+//
+// Staged-register engine: a 256-thread workgroup computes a BM x 128 output
+// tile (BM = 256 or 128) with four waves (2 x 2), each wave (BM/2) x 64 =
+// (BM/64) x 2 blocks of 32 x 32.  The K loop steps by 32 with double-buffered
+// LDS tiles:
 //   B (WT, contiguous along the output index) is transposed into LDS as
 //     [n][k] while being staged, two k rows packed per 32-bit LDS word, so
 //     each lane's MFMA B operand is one or two 16-byte LDS reads;
@@ -343,10 +349,11 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
 // Pipelined engine (dense and 2:4 A, d_in a multiple of the kind's K step,
 // 16-byte aligned rows).  A 256-thread workgroup computes a BM x 128 output
 // tile (BM = 256 or 128, chosen per call at launch), four waves of BM/2 x 64;
-// the K loop steps through three LDS stages.  Tiles go from global memory to
-// LDS with direct loads (global_load_lds: lane l's bytes land at the
-// instruction's LDS base + size * l), two K steps ahead, so no registers
-// hold staged data and the loads of step t+2 overlap the MFMAs of step t.
+// the K loop steps through NS LDS stages (three unless tuned).  Tiles go from
+// global memory to LDS with direct loads (global_load_lds: lane l's bytes
+// land at the instruction's LDS base + size * l), NS - 1 K steps ahead, so no
+// registers hold staged data and the loads of step t+2 overlap the MFMAs of
+// step t.
 // Two or three workgroups share a CU wherever LDS and registers allow, so
 // one's barrier and load waits are covered by the others' MFMAs.
 //   Dense: K steps of 32 (72 KB of LDS at BM = 256: two workgroups per CU;
