@@ -90,7 +90,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the sparse GEMV shards by d_out with no exchange; see DESIGN.md)",
+              "(the sparse GEMV would shard by d_out with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
