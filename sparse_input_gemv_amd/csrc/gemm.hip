@@ -377,7 +377,7 @@ __global__ __launch_bounds__(NTH) void k_gemm(GParams p) {
 // The MFMA sequence per output block is the staged-register engine's, so
 // both engines give identical results.
 // ---------------------------------------------------------------------------
-constexpr int PBM = 256, PBN = 128;
+constexpr int PBN = 128;
 
 typedef short s4v __attribute__((ext_vector_type(4)));
 #define SA_LDS4(ptr) ((__attribute__((address_space(3))) s4v*)(ptr))
@@ -452,28 +452,28 @@ __device__ __forceinline__ void stage_barrier() {
 // every LDS array (it cannot tell the stages apart and would drain all loads
 // before each read); the waits are stated by stage_barrier instead.  The
 // instruction has no result register, and the memory clobber keeps LDS
-// reads on their side of it.
+// reads on their side of it.  The LDS base goes in M0 as an input operand
+// (the compiler writes M0 itself, so no reserved register is clobbered);
+// the s_nop covers the wait state between an M0 write and the load.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
 }
 __device__ __forceinline__ void load_to_lds16(const void* src, const void* lds_base) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, off"
       :
-      : "v"(src), "s"(lds_addr(lds_base))
-      : "memory", "m0");
+      : "v"(src), "{m0}"(lds_addr(lds_base))
+      : "memory");
 }
 __device__ __forceinline__ void load_to_lds4(const void* src, const void* lds_base) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dword %0, off"
       :
-      : "v"(src), "s"(lds_addr(lds_base))
-      : "memory", "m0");
+      : "v"(src), "{m0}"(lds_addr(lds_base))
+      : "memory");
 }
 
 // Position of the r-th set bit (r from 0) of a field of at most 32 bits, by
