@@ -34,7 +34,11 @@
 //                 identical bits) and resets the counter for the next call.
 //                 Each counter sits on its own 128-byte line: same-line
 //                 atomics serialise at ~10 ns each on this part, separate
-//                 lines proceed in parallel.
+//                 lines proceed in parallel.  When every slice of a tile
+//                 runs on one XCD (output tiles a multiple of 8), the
+//                 partials stay in that XCD's L2 instead of being written
+//                 through, and the ticket verifies the placement
+//                 (store_handoff).
 //
 // Full-K (small weights, batch <= 2).  k_gemv_fk: each workgroup owns
 // 8*LPR outputs and walks all of d_in; no partials, one launch.
@@ -95,7 +99,8 @@ constexpr int64_t kFullKMaxWeightBytes = 8 << 20;
 
 int g_tiling = -1;     // -1: automatic
 int g_target_wgs = 0;  // 0: automatic
-int g_handoff = 0;     // 0: automatic, 1: two launches, 2: one launch
+int g_handoff = 0;     // 0: automatic, 1: two launches, 2: one launch, 3: one launch, in L2
+                        // where every slice of a tile shares an XCD
 
 struct KParams {
   const uint16_t* wt;
@@ -234,6 +239,39 @@ __device__ __forceinline__ void store_coherent(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The L2-local form.  Workgroups are dispatched to the 8 XCDs round-robin,
+// workgroup b on XCD (b + r) mod 8 for one r per launch (measured on every
+// grid size tried, also beside a concurrent kernel), so when the number of
+// output tiles go is a multiple of 8, every slice of a tile runs on one XCD.
+// Its partials then only need that XCD's L2: workgroup-scope atomic stores
+// and loads (sc0) skip the L1 but are not written through to memory, which
+// saves the write-through's wait before the ticket.  Kernel boundaries write
+// back and invalidate L2, so nothing stale outlives a call, and the ticket's
+// reset may stay in L2 as well.  The ticket checks the premise: with x its
+// XCD, every workgroup adds one arrival, x and x^2 in separate fields, and
+// the last one sees one XCD exactly when sum x = gk x_last and
+// sum x^2 = gk x_last^2 (zero variance); otherwise it writes NaN to its tile
+// rather than a sum of partials it cannot see.
+template <typename T>
+__device__ __forceinline__ void store_handoff(T* p, T v, int local) {
+  if (local)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_handoff(const T* p, int local) {
+  return local ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+               : __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr int kLocalMaxGk = 64;  // the ticket's fields (k_gemv) hold this many slices
+static_assert((kLocalMaxGk - 1) * 15 + 15 < 1024 && kLocalMaxGk * 225 < 65536,
+              "the ticket's sum fields must not overflow");
+// XCD of the calling workgroup (hardware register XCC_ID, bits 3:0)
+__device__ __forceinline__ uint32_t xcd_id() {
+  return (uint32_t)__builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & 0xfu;
+}
+
 __device__ __forceinline__ void wait_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt = expcnt = lgkmcnt = 0
@@ -247,7 +285,7 @@ __device__ __forceinline__ void wait_stores() {
 // and order, so both hand-offs round identically.  A wave's 64 lanes take 64
 // consecutive outputs of one slice group, so each load is one wave-uniform
 // address plus the lane: whole lines per wave and few address registers.
-template <int TILE_O, int NT, int B>
+template <int TILE_O, int NT, int B, bool LOCAL>
 __device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0, unsigned char* smem,
                                                const float* alpha, const uint16_t* bias) {
   constexpr int G = kReduceGroups;
@@ -279,8 +317,7 @@ __device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0, uns
         for (int q = 0; q < KL; ++q) {
           const int kk = k0 + g + q * G;
           tmp[pp][q] = (ok_o && kk < p.gk)
-                           ? __hip_atomic_load(base + (int64_t)kk * stride + lane,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           ? load_handoff(base + (int64_t)kk * stride + lane, (int)LOCAL)
                            : 0.f;
         }
       }
@@ -333,7 +370,7 @@ __device__ __forceinline__ int64_t wave_lower_bound(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // split-K, launch 1
 // ---------------------------------------------------------------------------
-template <int MODE, int TILE_O, int NT, int U, int B>
+template <int MODE, int TILE_O, int NT, int U, int B, bool LOCAL = false>
 __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int wsum[NT / kWave];
@@ -608,7 +645,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         if (p.gk == 1) {
           if (p.out_nnz != nullptr) p.out_nnz[0] = cnt;
         } else {
-          store_coherent(p.slice_cnt + kblk, (int32_t)cnt);
+          store_handoff(p.slice_cnt + kblk, (int32_t)cnt, LOCAL);
         }
       }
     }
@@ -649,8 +686,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         } else {
           double* dst = p.vsum + ((int64_t)kblk * p.go + oblk) * 2;
           if (p.tickets != nullptr) {
-            store_coherent(dst, a);
-            store_coherent(dst + 1, k);
+            store_handoff(dst, a, LOCAL);
+            store_handoff(dst + 1, k, LOCAL);
           } else {
             dst[0] = a;
             dst[1] = k;
@@ -789,7 +826,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         if (single)
           p.y[(int64_t)b * p.d_out + og] = finish(s, alpha_out, bias_arg, b, og);
         else if (handoff)
-          store_coherent(dst, s);
+          store_handoff(dst, s, LOCAL);
         else
           *dst = s;
       }
@@ -804,20 +841,41 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   __syncthreads();
   uint32_t* ticket = p.tickets + (int64_t)oblk * kTicketStride;
   if (tid == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned)(p.gk - 1)) ? 1 : 0;
+    if constexpr (LOCAL) {
+      // fields: arrivals [5:0], sum x [15:6], sum x^2 [31:16]; every one
+      // stays in its field up to the last arrival (gk <= kLocalMaxGk)
+      const uint32_t x = xcd_id();
+      const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u | (x << 6) | ((x * x) << 16),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t gk = (uint32_t)p.gk;
+      const uint32_t sx = ((prev >> 6) & 1023u) + x;
+      const uint32_t sxx = (prev >> 16) + x * x;
+      s_last = ((prev & 63u) != gk - 1) ? 0 : (sx == gk * x && sxx == gk * x * x) ? 1 : 2;
+    } else {
+      const unsigned prev =
+          __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (prev == (unsigned)(p.gk - 1)) ? 1 : 0;
+    }
   }
   __syncthreads();
   if (s_last == 0) return;
+  if (LOCAL && s_last == 2) {
+    // the tile's slices ran on more than one XCD: its partials are not all
+    // visible here; NaN marks the tile instead of a wrong sum
+    for (int oo = tid; oo < TILE_O; oo += NT)
+      for (int b = 0; b < p.batch; ++b)
+        if (o0 + oo < p.d_out) p.y[(int64_t)b * p.d_out + o0 + oo] = (uint16_t)0x7e00u;
+    if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return;
+  }
   if constexpr (MODE == kModeScored) {
     if (p.var) {
       // every slice's sums for this tile (written before their tickets)
       double a = 0.0, k = 0.0;
       for (int kk = tid; kk < p.gk; kk += NT) {
         const double* src = p.vsum + ((int64_t)kk * p.go + oblk) * 2;
-        a += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        k += __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a += load_handoff(src, LOCAL);
+        k += load_handoff(src + 1, LOCAL);
       }
       __shared__ double vr2[2][NT / kWave];
 #pragma unroll
@@ -841,18 +899,23 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       __syncthreads();
     }
   }
-  handoff_reduce<TILE_O, NT, B>(p, o0, smem, alpha_out, bias_arg);
+  handoff_reduce<TILE_O, NT, B, LOCAL>(p, o0, smem, alpha_out, bias_arg);
   if constexpr (MODE == kModeSwiglu) {
     if (oblk == 0 && p.out_nnz != nullptr) {
       int c = 0;
       for (int kk = tid; kk < p.gk; kk += NT)
-        c += __hip_atomic_load(p.slice_cnt + kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        c += load_handoff(p.slice_cnt + kk, LOCAL);
       int tot;
       (void)block_exclusive_scan<NT>(c, wsum, tot);
       if (tid == 0) p.out_nnz[0] = tot;
     }
   }
-  if (tid == 0) store_coherent(ticket, 0u);  // ready for the next call
+  if (tid == 0) {  // ready for the next call
+    if constexpr (LOCAL)  // in L2; written back when the kernel ends, before the next call
+      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else
+      store_coherent(ticket, 0u);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1246,45 +1309,54 @@ namespace {
 // exist for batch 1 of the hot modes; everything else uses tiling 0).
 using KFn = void (*)(KParams);
 
-template <int MODE, int B>
-KFn kernel_tiling(int tiling) {
+template <int MODE, int B, bool LOCAL>
+KFn kernel_tiling_scope(int tiling) {
   if constexpr (B == 1 && (MODE == kModeThreshold || MODE == kModeDense || MODE == kModeList)) {
     switch (tiling) {
-      case 1: return k_gemv<MODE, 256, 256, 8, B>;
-      case 2: return k_gemv<MODE, 256, 512, 8, B>;
-      case 3: return k_gemv<MODE, 128, 512, 8, B>;
-      case 4: return k_gemv<MODE, 512, 256, 8, B>;
-      case 5: return k_gemv<MODE, 128, 256, 16, B>;
-      case 6: return k_gemv<MODE, 64, 256, 8, B>;
-      case 7: return k_gemv<MODE, 256, 256, 4, B>;
-      default: return k_gemv<MODE, 128, 256, 8, B>;
+      case 1: return k_gemv<MODE, 256, 256, 8, B, LOCAL>;
+      case 2: return k_gemv<MODE, 256, 512, 8, B, LOCAL>;
+      case 3: return k_gemv<MODE, 128, 512, 8, B, LOCAL>;
+      case 4: return k_gemv<MODE, 512, 256, 8, B, LOCAL>;
+      case 5: return k_gemv<MODE, 128, 256, 16, B, LOCAL>;
+      case 6: return k_gemv<MODE, 64, 256, 8, B, LOCAL>;
+      case 7: return k_gemv<MODE, 256, 256, 4, B, LOCAL>;
+      default: return k_gemv<MODE, 128, 256, 8, B, LOCAL>;
     }
   } else {
     (void)tiling;
-    return k_gemv<MODE, 128, 256, 8, B>;
+    return k_gemv<MODE, 128, 256, 8, B, LOCAL>;
   }
+}
+
+// The L2-local hand-off exists for batch 1 and 2 (the one-launch batches).
+template <int MODE, int B>
+KFn kernel_tiling(int tiling, bool local) {
+  if constexpr (B <= 2) {
+    if (local) return kernel_tiling_scope<MODE, B, true>(tiling);
+  }
+  return kernel_tiling_scope<MODE, B, false>(tiling);
 }
 
 template <int MODE>
-KFn kernel_batch(int tiling, int B) {
+KFn kernel_batch(int tiling, int B, bool local) {
   switch (B) {
-    case 1: return kernel_tiling<MODE, 1>(tiling);
-    case 2: return kernel_tiling<MODE, 2>(tiling);
-    case 4: return kernel_tiling<MODE, 4>(tiling);
-    default: return kernel_tiling<MODE, 8>(tiling);
+    case 1: return kernel_tiling<MODE, 1>(tiling, local);
+    case 2: return kernel_tiling<MODE, 2>(tiling, local);
+    case 4: return kernel_tiling<MODE, 4>(tiling, local);
+    default: return kernel_tiling<MODE, 8>(tiling, local);
   }
 }
 
-KFn select_kernel(int mode, int tiling, int B) {
+KFn select_kernel(int mode, int tiling, int B, bool local = false) {
   switch (mode) {
-    case kModeThreshold: return kernel_batch<kModeThreshold>(tiling, B);
-    case kModeDense: return kernel_batch<kModeDense>(tiling, B);
-    case kModeMasked: return kernel_batch<kModeMasked>(tiling, B);
-    case kModeList: return kernel_tiling<kModeList, 1>(tiling);
-    case kModeListBatched: return kernel_batch<kModeListBatched>(tiling, B);
-    case kModeSwiglu: return kernel_tiling<kModeSwiglu, 1>(tiling);
-    case kModeScored: return kernel_tiling<kModeScored, 1>(tiling);
-    case kModeSquare: return kernel_batch<kModeSquare>(tiling, B);
+    case kModeThreshold: return kernel_batch<kModeThreshold>(tiling, B, local);
+    case kModeDense: return kernel_batch<kModeDense>(tiling, B, local);
+    case kModeMasked: return kernel_batch<kModeMasked>(tiling, B, local);
+    case kModeList: return kernel_tiling<kModeList, 1>(tiling, local);
+    case kModeListBatched: return kernel_batch<kModeListBatched>(tiling, B, local);
+    case kModeSwiglu: return kernel_tiling<kModeSwiglu, 1>(tiling, local);
+    case kModeScored: return kernel_tiling<kModeScored, 1>(tiling, local);
+    case kModeSquare: return kernel_batch<kModeSquare>(tiling, B, local);
     default: return nullptr;
   }
 }
@@ -1522,13 +1594,16 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   // one launch for batch 1 and 2; at batch 4 and 8 the last workgroup's sum
   // over B rows costs more than a second launch (measured)
   const bool one_launch =
-      pl.gk > 1 && (g_handoff == 0 ? (kDefaultOneLaunch && B <= 2) : g_handoff == 2);
+      pl.gk > 1 && (g_handoff == 0 ? (kDefaultOneLaunch && B <= 2) : g_handoff >= 2);
   kp.tickets = one_launch ? reinterpret_cast<uint32_t*>(ws + L.ticket_off) : nullptr;
+  // partials kept in L2 when every slice of a tile runs on one XCD
+  const bool local =
+      one_launch && g_handoff != 2 && B <= 2 && pl.go % 8 == 0 && pl.gk <= kLocalMaxGk;
   kp.go = pl.go;
   kp.gk = pl.gk;
   kp.slice = pl.slice;
 
-  const KFn fn = select_kernel(mode, tiling, B);
+  const KFn fn = select_kernel(mode, tiling, B, local);
   if (fn == nullptr) return hipErrorInvalidValue;
   const hipError_t e = launch_split(fn, kTilings[tiling].threads, kp, pl, s);
   if (e != hipSuccess || pl.gk == 1 || one_launch) return e;
@@ -1543,7 +1618,7 @@ hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, dou
 }
 
 int gemv_set_tuning(int tiling, int target_wgs, int handoff) {
-  if (tiling < -1 || tiling >= kNumTilings || target_wgs < 0 || handoff < 0 || handoff > 2)
+  if (tiling < -1 || tiling >= kNumTilings || target_wgs < 0 || handoff < 0 || handoff > 3)
     return 1;
   g_tiling = tiling;
   g_target_wgs = target_wgs;

@@ -163,9 +163,9 @@ def test_gemv_checks(sa):
     d = sa.dense_gemv
     assert d(P, 4096, 11008, None, 1, P, P, need, None) == SA_ERR_INVALID_ARG
     assert sa.sa_set_gemv_tuning(99, 0, 0) == SA_ERR_INVALID_ARG
-    assert sa.sa_set_gemv_tuning(-1, 0, 3) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemv_tuning(-1, 0, 4) == SA_ERR_INVALID_ARG
     assert sa.sa_set_gemv_tuning(-1, -1, 0) == SA_ERR_INVALID_ARG
-    for handoff in (1, 2, 0):
+    for handoff in (1, 2, 3, 0):
         assert sa.sa_set_gemv_tuning(-1, 0, handoff) == SA_OK
     assert sa.sa_set_gemm_tuning(64, 0, 0) == SA_ERR_INVALID_ARG
     assert sa.sa_set_gemm_tuning(0, 3, 0) == SA_ERR_INVALID_ARG

@@ -387,7 +387,7 @@ def test_masked_swiglu_t0_dense():
     assert_close(y, y_ref)
 
 
-@pytest.mark.parametrize("handoff", [1, 2])
+@pytest.mark.parametrize("handoff", [1, 2, 3])
 def test_split_k_handoff_is_deterministic(handoff):
     """Many back-to-back split-K calls on rotating weights: every result must
     equal the first one bit for bit (the cross-workgroup hand-off is exact)."""
@@ -440,15 +440,16 @@ def test_one_launch_handoff_matches_two_launches(tiling):
                      sa.act_sparsify_threshold(xb, 0.7), swiglu_in))
     try:
         res = {}
-        for handoff in (1, 2):
+        for handoff in (1, 2, 3):
             for k, (target, wt, x1, xb, l1, lb, sw) in enumerate(data):
                 sa.set_gemv_tuning(tiling, target, handoff)
                 res[handoff, k] = [o.clone() for o in _every_gemv_entry(wt, x1, xb, l1, lb, sw,
                                                                         0.7)]
         torch.cuda.synchronize()
         for k in range(len(data)):
-            for j, (a, b) in enumerate(zip(res[1, k], res[2, k])):
-                assert torch.equal(a, b), (tiling, shapes[k], j)
+            for h in (2, 3):
+                for j, (a, b) in enumerate(zip(res[1, k], res[h, k])):
+                    assert torch.equal(a, b), (tiling, shapes[k], h, j)
     finally:
         sa.set_gemv_tuning(-1, 0, 0)
 
@@ -541,13 +542,13 @@ def test_scored_fused(d_out, d_in, shifted, weighted, var, biased):
     mu_g = dev(mu) if mu is not None else None
     out = {}
     try:
-        for handoff in (2, 1):
+        for handoff in (2, 1, 3):
             sa.set_gemv_tuning(-1, 0, handoff)
             out[handoff] = sa.sparse_gemv_scored(wt_g, dev(x), t, mu=mu_g, colnorm=cn_g, var=var,
                                                  bias=bias_g).clone()
     finally:
         sa.set_gemv_tuning(-1, 0, 0)
-    assert torch.equal(out[1], out[2])
+    assert torch.equal(out[1], out[2]) and torch.equal(out[1], out[3])
     assert_close(out[2], y_ref)
 
 
