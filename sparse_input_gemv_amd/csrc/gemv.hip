@@ -215,14 +215,14 @@ __device__ __forceinline__ int chunk_slot(bool keep, int* wsum, int& total, uint
 
 // s = SiLU(g) = g / (1 + exp(-g)), h = s*u and the masker score, in fp64 and
 // in the order written (no contraction), as the pages' masks are defined.
-__device__ __forceinline__ bool swiglu_keep(uint16_t gb, uint16_t ub, const double* colnorm,
-                                            int64_t k, int mode, double t, float& hv) {
+__device__ __forceinline__ bool swiglu_keep(uint16_t gb, uint16_t ub, double cn, int mode,
+                                            double t, float& hv) {
 #pragma clang fp contract(off)
   const double gg = (double)h2f(gb);
   const double uu = (double)h2f(ub);
   const double s = gg / (1.0 + exp(-gg));
   const double h = s * uu;
-  const double score = (mode == 0) ? fabs(s) : fabs(h) * colnorm[k];
+  const double score = (mode == 0) ? fabs(s) : fabs(h) * cn;
   hv = (float)h;
   return score >= t;
 }
@@ -467,13 +467,12 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       cnt += total;
     }
     __syncthreads();
-  } else if (kOnePassChunks<B> > 0 && MODE != kModeSwiglu &&
-             slice_span <= (int64_t)kOnePassChunks<B> * NT) {
-    // One pass: every chunk's x (and mask word) loads are issued before any
-    // decision, so the slice costs one memory round trip; the kept slots of
-    // all chunks come from one table of per-chunk, per-wave ballot counts
-    // (one barrier).  Entry k0 + c*NT + tid of chunk c; chunk-major order
-    // keeps the list ascending.
+  } else if (kOnePassChunks<B> > 0 && slice_span <= (int64_t)kOnePassChunks<B> * NT) {
+    // One pass: every chunk's x (and mask word; SwiGLU: gate, up and norm)
+    // loads are issued before any decision, so the slice costs one memory
+    // round trip; the kept slots of all chunks come from one table of
+    // per-chunk, per-wave ballot counts (one barrier).  Entry k0 + c*NT + tid
+    // of chunk c; chunk-major order keeps the list ascending.
     constexpr int PC = kOnePassChunks<B> > 0 ? kOnePassChunks<B> : 1;
     constexpr int NW = NT / kWave;
     __shared__ int wtab[PC * NW];
@@ -483,18 +482,27 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     const int nch = (int)((slice_span + NT - 1) / NT);  // chunks this slice has
     uint16_t xr[PC][B];
     uint32_t mw[PC][B];
-    uint16_t ms[PC];  // scored: shift
-    double cs[PC];    // scored: weight norm
+    uint16_t ms[PC];  // scored: shift; SwiGLU: up
+    double cs[PC];    // scored, SwiGLU mode 1: weight norm
+    float hv[PC];     // SwiGLU: the kept value h
+    // Every chunk's loads, also past the slice (clamped to its first entry):
+    // leaving the loop early would put a wait for each load before the
+    // branch, one round trip per chunk.
 #pragma unroll
     for (int c = 0; c < PC; ++c) {
-      if (c > 0 && c >= nch) break;
       const int64_t k = k0 + (int64_t)c * NT + tid;
       const int64_t kc = k < k1 ? k : k0;
+      if constexpr (MODE == kModeSwiglu) {
+        xr[c][0] = p.g[kc];
+        ms[c] = p.u[kc];
+        cs[c] = p.swiglu_mode != 0 ? p.colnorm[kc] : 0.0;
+      } else {
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const int64_t bb = b < p.batch ? b : 0;
-        xr[c][b] = p.x[bb * p.d_in + kc];
-        if constexpr (MODE == kModeMasked) mw[c][b] = p.xmask[bb * words + (kc >> 5)];
+        for (int b = 0; b < B; ++b) {
+          const int64_t bb = b < p.batch ? b : 0;
+          xr[c][b] = p.x[bb * p.d_in + kc];
+          if constexpr (MODE == kModeMasked) mw[c][b] = p.xmask[bb * words + (kc >> 5)];
+        }
       }
       if constexpr (MODE == kModeScored) {
         ms[c] = p.mu != nullptr ? p.mu[kc] : (uint16_t)0;
@@ -515,6 +523,9 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         bool kb = false;
         if constexpr (MODE == kModeScored) {
           kb = scored_keep(p, xr[c][b], ms[c], cs[c], b < p.batch && k < k1, s_all, s_kept);
+        } else if constexpr (MODE == kModeSwiglu) {
+          hv[c] = 0.f;
+          kb = k < k1 && swiglu_keep(xb, ms[c], cs[c], p.swiglu_mode, p.t64, hv[c]);
         } else if (b < p.batch && k < k1) {
           if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
             kb = keep_entry<MODE>(xb, p.t);
@@ -530,6 +541,15 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       keep[c] = any;
       bm[c] = __ballot(any);
       if (lane_id() == 0) wtab[c * NW + w] = (int)__popcll(bm[c]);
+      if constexpr (MODE == kModeSwiglu) {
+        // the mask: a wave covers 64 entries from a multiple of 64 (slices
+        // are aligned to 64), so its two words are its own
+        const int64_t kw = k0 + (int64_t)c * NT + (int64_t)w * kWave;
+        if (p.out_mask != nullptr && oblk == 0 && lane_id() == 0 && kw < k1) {
+          p.out_mask[kw >> 5] = (uint32_t)bm[c];
+          if (kw + 32 < p.d_in) p.out_mask[(kw >> 5) + 1] = (uint32_t)(bm[c] >> 32);
+        }
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -548,11 +568,22 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
         if constexpr (kPairs) {
 #pragma unroll
           for (int b = 0; b < B; ++b) lvh[b * SLH + slot] = xr[c][b];
+        } else if constexpr (MODE == kModeSwiglu) {
+          lv[slot] = hv[c];
         } else {
           lv[slot] = h2f(xr[c][0]);
         }
       }
       cnt += tot;
+    }
+    if constexpr (MODE == kModeSwiglu) {
+      if (oblk == 0 && tid == 0) {
+        if (p.gk == 1) {
+          if (p.out_nnz != nullptr) p.out_nnz[0] = cnt;
+        } else {
+          store_handoff(p.slice_cnt + kblk, (int32_t)cnt, LOCAL);
+        }
+      }
     }
     __syncthreads();
   } else {
@@ -567,7 +598,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       bool any = false;
       if constexpr (MODE == kModeSwiglu) {
         float hv = 0.f;
-        any = in && swiglu_keep(p.g[k], p.u[k], p.colnorm, k, p.swiglu_mode, p.t64, hv);
+        any = in && swiglu_keep(p.g[k], p.u[k], p.swiglu_mode != 0 ? p.colnorm[k] : 0.0,
+                                p.swiglu_mode, p.t64, hv);
         vb[0] = hv;
       } else {
         // every row's load first, from in-range addresses (k0 < d_in), so
@@ -1064,6 +1096,39 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
     int64_t row[U];
     float v[U][B];
     bool keep[U];
+    // Every load of the U entries first, from in-range addresses (entry 0
+    // past the end), so that they are in flight together; then the
+    // decisions.  A load inside a divergent branch would wait before the
+    // branch joins: one round trip per entry.
+    uint16_t xa[U][B];  // x; list values; SwiGLU gate
+    uint16_t xu[U];     // SwiGLU up; scored shift
+    uint32_t mw[U][B];  // masked: mask words
+    int32_t ix[U];      // list indices
+    double cn[U];       // scored, SwiGLU mode 1: weight norms
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int64_t j = j0 + (int64_t)q * RL;
+      const int64_t jc = j < n ? j : 0;
+      if constexpr (MODE == kModeList) {
+        ix[q] = p.idx[jc];
+        xa[q][0] = p.val[jc];
+      } else if constexpr (MODE == kModeSwiglu) {
+        xa[q][0] = p.g[jc];
+        xu[q] = p.u[jc];
+        cn[q] = p.swiglu_mode != 0 ? p.colnorm[jc] : 0.0;
+      } else if constexpr (MODE == kModeScored) {
+        xa[q][0] = p.x[jc];
+        xu[q] = p.mu != nullptr ? p.mu[jc] : (uint16_t)0;
+        cn[q] = p.colnorm != nullptr ? p.colnorm[jc] : 1.0;
+      } else {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const int64_t bb = b < p.batch ? b : 0;
+          xa[q][b] = p.x[bb * p.d_in + jc];
+          if constexpr (MODE == kModeMasked) mw[q][b] = p.xmask[bb * words + (jc >> 5)];
+        }
+      }
+    }
 #pragma unroll
     for (int q = 0; q < U; ++q) {
       const int64_t j = j0 + (int64_t)q * RL;
@@ -1074,23 +1139,20 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
       for (int b = 0; b < B; ++b) v[q][b] = 0.f;
       if constexpr (MODE == kModeList) {
         if (in) {
-          const int32_t kk = p.idx[j];
+          const int32_t kk = ix[q];
           const bool ok = kk >= 0 && (int64_t)kk < p.d_in;
           row[q] = ok ? kk : 0;
           keep[q] = ok;
-          v[q][0] = ok ? h2f(p.val[j]) : 0.f;
+          v[q][0] = ok ? h2f(xa[q][0]) : 0.f;
         }
       } else if constexpr (MODE == kModeSwiglu) {
         float hv = 0.f;
-        keep[q] = in && swiglu_keep(p.g[j], p.u[j], p.colnorm, j, p.swiglu_mode, p.t64, hv);
+        keep[q] = in && swiglu_keep(xa[q][0], xu[q], cn[q], p.swiglu_mode, p.t64, hv);
         v[q][0] = hv;
       } else if constexpr (MODE == kModeScored) {
-        const int64_t jc = in ? j : 0;
-        uint16_t xb = p.x[jc];
         double a = 0.0, k = 0.0;
-        keep[q] = scored_keep(p, xb, p.mu != nullptr ? p.mu[jc] : (uint16_t)0,
-                              p.colnorm != nullptr ? p.colnorm[jc] : 1.0, in, a, k);
-        v[q][0] = keep[q] ? h2f(xb) : 0.f;
+        keep[q] = scored_keep(p, xa[q][0], xu[q], cn[q], in, a, k);
+        v[q][0] = keep[q] ? h2f(xa[q][0]) : 0.f;
         if (sub == 0) {
           s_all += a;
           s_kept += k;
@@ -1099,12 +1161,12 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           if (in && b < p.batch) {
-            const uint16_t xb = p.x[(int64_t)b * p.d_in + j];
+            const uint16_t xb = xa[q][b];
             bool kb;
             if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
               kb = keep_entry<MODE>(xb, p.t);
             } else if constexpr (MODE == kModeMasked) {
-              kb = ((p.xmask[(int64_t)b * words + (j >> 5)] >> (j & 31)) & 1u) != 0;
+              kb = ((mw[q][b] >> (j & 31)) & 1u) != 0;
             } else {
               kb = true;
             }
