@@ -399,6 +399,33 @@ def suite_layer(sa, syn, dev, ev_time, emit, rotation):
          layer["sparse"], speedup_vs_dense=round(layer["dense"] / layer["sparse"], 3),
          dense_us=round(layer["dense"], 3))
 
+    # Llama-3-8B k / v projection: an 8 MB weight, served by the full-K
+    # kernel (one workgroup walks all of d_in), batch 1 and 2
+    kv = syn.LLAMA3_8B_KV
+    d_out, d_in = kv["d_out"], kv["d_in"]
+    _, dist = syn.LLAMA2_7B_INPUTS[kv["input"]]
+    t = thresholds[kv["input"]][0.5]
+    rot = rotation(d_out, d_in, 41)
+    nr = len(rot)
+    for b in (1, 2):
+        xb = torch.from_numpy(syn.activation((b, d_in), dist, 7)).to(dev)
+        yb = torch.empty((b, d_out), dtype=torch.float16, device=dev)
+        # rows kept by any batch row (the union the kernel reads), from the
+        # sparsifier's bitmasks
+        words = np.bitwise_or.reduce(np.stack([
+            sa.act_sparsify_threshold(xb[r], t)[0].cpu().numpy().view(np.uint32).ravel()
+            for r in range(b)]), axis=0)
+        rows = int(np.unpackbits(words.view(np.uint8)).sum())
+        us = ev_time(lambda i: sa.sparse_gemv_threshold(rot[i % nr], xb, t, y=yb), 1000)
+        us_d = ev_time(lambda i: sa.dense_gemv(rot[i % nr], xb, y=yb), 1000)
+        emit("a4", f"sparse_gemv_threshold Llama-3-8B k/v {d_out}x{d_in} batch {b} sparsity 0.5", us,
+             bytes_=2 * d_out * rows + 2 * b * (d_in + d_out), rows_read=rows,
+             speedup_vs_dense=round(us_d / us, 3))
+        emit("a8", f"dense_gemv Llama-3-8B k/v {d_out}x{d_in} batch {b}", us_d,
+             bytes_=2 * d_out * d_in + 2 * b * (d_in + d_out), flops=2 * b * d_out * d_in)
+    del rot
+    torch.cuda.empty_cache()
+
     # shared-input fused projections: one sparsified input, the members'
     # weights side by side (q|k|v, gate|up), one call
     fused = {"sparse": per["o"][0] + per["down"][0], "dense": per["o"][1] + per["down"][1]}

@@ -41,7 +41,9 @@
 //                 (store_handoff).
 //
 // Full-K (small weights, batch <= 2).  k_gemv_fk: each workgroup owns
-// 8*LPR outputs and walks all of d_in; no partials, one launch.
+// 8*LPR outputs and walks all of d_in; no partials, one launch.  Chosen
+// only where its grid covers every CU or the walk is short; other small
+// weights take split-K with one workgroup per CU.
 //
 // With go a multiple of 8, all slices of one output tile run on one XCD
 // (workgroups are dispatched round-robin over the 8 XCDs), and the
@@ -96,6 +98,19 @@ static_assert((size_t)(kMaxDOut / kMinSplitTileO) * kTicketStride * 4 <= kTicket
 constexpr size_t kMaxListLds = 48 * 1024;
 // weights up to this size run full-K in one launch (latency-bound anyway)
 constexpr int64_t kFullKMaxWeightBytes = 8 << 20;
+// Small weights (<= kSmallSplitMaxWeightBytes) on split-K: one workgroup per
+// CU and slices of at least kSmallMinSlice rows (shorter ones cost more in
+// the hand-off than they gain), 64-wide tiles up to kSmallNarrowDout outputs.
+// Full-K serves them only when its grid (one workgroup per 16 outputs)
+// covers every CU or a walk is short (d_in <= kFullKShortDin): one
+// workgroup streams at a per-CU rate, so a small grid leaves most of the
+// chip's bandwidth unused (measured: 1024 x 4096 dense 15.1 us full-K,
+// 6.0 us split-K).
+constexpr int64_t kSmallSplitMaxWeightBytes = 16 << 20;
+constexpr int kSmallMinSlice = 128;
+constexpr int64_t kSmallNarrowDout = 1024;
+constexpr int kSplitNarrowTiling = 6;
+constexpr int64_t kFullKShortDin = 1024;
 
 int g_tiling = -1;     // -1: automatic
 int g_target_wgs = 0;  // 0: automatic
@@ -1489,8 +1504,14 @@ Plan choose_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
   const double bytes = 2.0 * (double)d_in * (double)d_out * (mode == kModeDense ? 1.0 : 0.5);
   int64_t k = (int64_t)(bytes / (double)cus / kBytesPerWorkgroup + 0.5);
   k = k < kMinWgsPerCu ? kMinWgsPerCu : (k > kMaxWgsPerCu ? kMaxWgsPerCu : k);
+  int64_t gk_req = (k * cus) / go;
+  if (2 * d_in * d_out <= kSmallSplitMaxWeightBytes) {
+    gk_req = cus / go;
+    const int64_t most = d_in / kSmallMinSlice;
+    if (gk_req > most) gk_req = most;
+  }
   const KFn fn = select_kernel(mode, tiling, B);
-  Plan pl = plan_for(mode, tiling, d_out, d_in, B, (k * cus) / go);
+  Plan pl = plan_for(mode, tiling, d_out, d_in, B, gk_req);
   // at most one resident wave of workgroups
   for (int i = 0; i < 4 && pl.gk > 1; ++i) {
     const int64_t cap = (int64_t)resident_per_cu(fn, nt, pl.smem) * cus;
@@ -1589,10 +1610,20 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   const bool fk_ok = B <= 2 && mode != kModeListBatched;
   int tiling = g_tiling;
   const bool hot = B == 1 && (mode == kModeThreshold || mode == kModeDense || mode == kModeList);
-  if (tiling < 0)
-    tiling = (fk_ok && c.d_in * c.d_out * 2 <= kFullKMaxWeightBytes)
-                 ? kDefaultFullK
-                 : (hot ? kDefaultSplitKHot : kDefaultSplitK);
+  if (tiling < 0) {
+    const int64_t wbytes = c.d_in * c.d_out * 2;
+    const bool fk_fills = (c.d_out + kTilings[kDefaultFullK].tile_o - 1) /
+                              kTilings[kDefaultFullK].tile_o >= device_cus() ||
+                          c.d_in <= kFullKShortDin;
+    if (fk_ok && wbytes <= kFullKMaxWeightBytes && fk_fills)
+      tiling = kDefaultFullK;
+    else if (hot)
+      tiling = (wbytes <= kSmallSplitMaxWeightBytes && c.d_out <= kSmallNarrowDout)
+                   ? kSplitNarrowTiling
+                   : kDefaultSplitKHot;
+    else
+      tiling = kDefaultSplitK;
+  }
   if (kTilings[tiling].full_k && !fk_ok) tiling = kDefaultSplitK;
   if (!kTilings[tiling].full_k && !hot)
     tiling = kDefaultSplitK;  // split-K variants exist for the batch-1 hot modes only

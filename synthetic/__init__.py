@@ -32,6 +32,7 @@ __all__ = [
     "fused_weight_t",
     "rank_adapter_weights",
     "LLAMA3_8B_MLP",
+    "LLAMA3_8B_KV",
     "weight_seed",
     "calib_seed",
     "calibration_samples",
@@ -87,6 +88,9 @@ _INPUT_ORDER = ["attn_in", "o_in", "mlp_in", "down_in"]
 
 # Llama-3-8B MLP: d_model 4096, d_ff 14336.
 LLAMA3_8B_MLP = {"d_model": 4096, "d_ff": 14336}
+# Llama-3-8B k and v projections (grouped-query attention, 8 key/value heads
+# of 128): d_out 1024, d_in 4096, input like the Llama-2-7B block input.
+LLAMA3_8B_KV = {"d_out": 1024, "d_in": 4096, "input": "attn_in"}
 
 
 def weight_seed(name: str) -> int:

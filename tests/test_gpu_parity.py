@@ -197,6 +197,26 @@ def test_ragged_output_tiles():
         assert_close(sa.sparse_gemv_threshold(dev(wt), dev(x), t), ref)
 
 
+@pytest.mark.parametrize("d_out,d_in", [(1024, 4096), (512, 4096), (264, 4096), (2048, 2048),
+                                         (4096, 1024), (1000, 1000), (4096, 512), (200, 3000)])
+@pytest.mark.parametrize("batch", [1, 2])
+def test_small_weight_shapes(d_out, d_in, batch):
+    """Weights up to 8 MB, where the automatic choice picks full-K (wide,
+    short-K shapes) or one-workgroup-per-CU split-K with narrow tiles."""
+    wt = syn.weight_t(d_out, d_in, 13)
+    x = syn.gaussian_f16((batch, d_in), 1.0, 14)
+    t = 0.6745
+    keep = sparsify.threshold_sparsify(x, t)[0]
+    wt_g, x_g = dev(wt), dev(x)
+    assert_close(sa.sparse_gemv_threshold(wt_g, x_g, t), gemv.batched_masked_gemv(wt, x, keep))
+    assert_close(sa.dense_gemv(wt_g, x_g), np.stack([gemv.dense_gemv(wt, x[b]) for b in range(batch)]))
+    m_g = sa.act_sparsify_threshold(x_g, t)[0]
+    assert_close(sa.masked_gemv(wt_g, x_g, m_g), gemv.batched_masked_gemv(wt, x, keep))
+    if batch == 1:
+        _, i_g, v_g, n_g = sa.act_sparsify_threshold(x_g[0], t)
+        assert_close(sa.sparse_gemv(wt_g, i_g, v_g, n_g), gemv.batched_masked_gemv(wt, x, keep)[0])
+
+
 def test_deterministic_and_stream():
     d_out, d_in, _ = syn.LLAMA2_7B["down"]
     wt = dev(syn.weight_t(d_out, d_in, 13))
