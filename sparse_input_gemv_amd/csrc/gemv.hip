@@ -1405,12 +1405,9 @@ KFn kernel_tiling_scope(int tiling) {
   }
 }
 
-// The L2-local hand-off exists for batch 1 and 2 (the one-launch batches).
 template <int MODE, int B>
 KFn kernel_tiling(int tiling, bool local) {
-  if constexpr (B <= 2) {
-    if (local) return kernel_tiling_scope<MODE, B, true>(tiling);
-  }
+  if (local) return kernel_tiling_scope<MODE, B, true>(tiling);
   return kernel_tiling_scope<MODE, B, false>(tiling);
 }
 
@@ -1707,8 +1704,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
       pl.gk > 1 && (g_handoff == 0 ? (kDefaultOneLaunch && B <= 2) : g_handoff >= 2);
   kp.tickets = one_launch ? reinterpret_cast<uint32_t*>(ws + L.ticket_off) : nullptr;
   // partials kept in L2 when every slice of a tile runs on one XCD
-  const bool local =
-      one_launch && g_handoff != 2 && B <= 2 && pl.go % 8 == 0 && pl.gk <= kLocalMaxGk;
+  const bool local = one_launch && g_handoff != 2 && pl.go % 8 == 0 && pl.gk <= kLocalMaxGk;
   kp.go = pl.go;
   kp.gk = pl.gk;
   kp.slice = pl.slice;
