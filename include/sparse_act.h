@@ -458,6 +458,38 @@ int sa_set_gemm_tuning(int tile_rows, int engine, int stages);
  * past the last one.  Output pointers are HOST pointers (may be NULL). */
 int sa_gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll);
 
+/* GEMV entry points, as named by sa_gemv_plan. */
+enum {
+  SA_GEMV_THRESHOLD = 0, /* sparse_gemv_threshold */
+  SA_GEMV_DENSE = 1,     /* dense_gemv */
+  SA_GEMV_MASKED = 2,    /* masked_gemv */
+  SA_GEMV_LIST = 3,      /* sparse_gemv, sparse_gemv_corrected */
+  SA_GEMV_SWIGLU = 4,    /* masked_swiglu_down */
+  SA_GEMV_SCORED = 6,    /* sparse_gemv_scored */
+  SA_GEMV_SQUARE = 7     /* the second GEMV of rana_adapter_gemv */
+};
+/*
+ * The decomposition a GEMV entry point would use for a call shape, under the
+ * current sa_set_gemv_tuning choices, for inspection and performance work.
+ * It computes nothing on the GPU.
+ *   op: SA_GEMV_*; d_out, d_in >= 1; batch 1..SA_MAX_BATCH.
+ *   cus: compute units of the device to plan for (0: the current device's).
+ *   resident: workgroups of the split-K kernel that fit on one CU (0: ask
+ *     the current device, which needs one).
+ * Outputs (HOST pointers, none NULL):
+ *   kernel: 0 split-K (k_gemv), 1 full-K (k_gemv_fk);
+ *   tile_o: outputs per workgroup;
+ *   grid_o: output tiles;
+ *   slices: input slices per output tile (1 for full-K);
+ *   handoff: 0 none (one slice or full-K), 1 a second launch sums the
+ *     partials, 2 the last workgroup of a tile sums them in the same launch,
+ *     3 the same with the partials kept in L2.
+ * Returns SA_ERR_INVALID_ARG for an unknown op, a size out of range, a
+ * negative count or a NULL output.
+ */
+int sa_gemv_plan(int op, int64_t d_out, int64_t d_in, int64_t batch, int cus, int resident,
+                 int* kernel, int* tile_o, int* grid_o, int* slices, int* handoff);
+
 #ifdef __cplusplus
 }
 #endif

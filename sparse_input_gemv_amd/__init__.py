@@ -74,6 +74,7 @@ _SIGNATURES = {
     "sa_set_gemv_tuning": (_i32, [_i32, _i32, _i32]),
     "sa_set_gemm_tuning": (_i32, [_i32, _i32, _i32]),
     "sa_gemv_tiling_info": (_i32, [_i32, _vp, _vp, _vp]),
+    "sa_gemv_plan": (_i32, [_i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -528,6 +529,23 @@ def set_gemv_tuning(tiling: int = -1, target_wgs: int = 0, handoff: int = 0) -> 
 
 def set_gemm_tuning(tile_rows: int = 0, engine: int = 0, stages: int = 0) -> None:
     _check(lib().sa_set_gemm_tuning(tile_rows, engine, stages), "sa_set_gemm_tuning")
+
+
+GEMV_OPS = {"threshold": 0, "dense": 1, "masked": 2, "list": 3, "swiglu": 4, "scored": 6,
+            "square": 7}
+
+
+def gemv_plan(op: str, d_out: int, d_in: int, batch: int = 1, cus: int = 0, resident: int = 0):
+    """The decomposition a GEMV entry point would use: a dict with ``kernel``
+    ("split-K" or "full-K"), ``tile_o``, ``grid_o``, ``slices`` and ``handoff``
+    (0 none, 1 second launch, 2 same launch, 3 same launch in L2).  ``cus`` /
+    ``resident`` 0 ask the current device."""
+    out = [ctypes.c_int() for _ in range(5)]
+    _check(lib().sa_gemv_plan(GEMV_OPS[op], d_out, d_in, batch, cus, resident,
+                              *[ctypes.addressof(o) for o in out]), "sa_gemv_plan")
+    k, t, g, sl, h = (o.value for o in out)
+    return {"kernel": "full-K" if k else "split-K", "tile_o": t, "grid_o": g, "slices": sl,
+            "handoff": h}
 
 
 def gemv_tiling_info(i: int):

@@ -469,6 +469,24 @@ int sa_set_gemm_tuning(int tile_rows, int engine, int stages) {
   return SA_OK;
 }
 
+int sa_gemv_plan(int op, int64_t d_out, int64_t d_in, int64_t batch, int cus, int resident,
+                 int* kernel, int* tile_o, int* grid_o, int* slices, int* handoff) {
+  sa::clear_error();
+  const bool known = op == SA_GEMV_THRESHOLD || op == SA_GEMV_DENSE || op == SA_GEMV_MASKED ||
+                     op == SA_GEMV_LIST || op == SA_GEMV_SWIGLU || op == SA_GEMV_SCORED ||
+                     op == SA_GEMV_SQUARE;
+  if (!known || d_out < 1 || d_in < 1 || batch < 1 || batch > SA_MAX_BATCH || cus < 0 ||
+      resident < 0 || kernel == nullptr || tile_o == nullptr || grid_o == nullptr ||
+      slices == nullptr || handoff == nullptr) {
+    sa::set_error("sa_gemv_plan: unknown op %d, a size out of range (d_out %lld, d_in %lld, "
+                  "batch %lld), a negative count or a NULL output", op, (long long)d_out,
+                  (long long)d_in, (long long)batch);
+    return SA_ERR_INVALID_ARG;
+  }
+  sa::gemv_plan(op, d_out, d_in, batch, cus, resident, kernel, tile_o, grid_o, slices, handoff);
+  return SA_OK;
+}
+
 int sa_gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll) {
   sa::clear_error();
   if (sa::gemv_tiling_info(i, tile_o, threads, unroll) != 0) {

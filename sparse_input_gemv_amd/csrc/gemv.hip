@@ -1492,12 +1492,14 @@ Plan plan_for(int mode, int tiling, int64_t d_out, int64_t d_in, int B, int64_t 
   return pl;
 }
 
-Plan choose_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
+// cus: compute units; resident: workgroups of the kernel that fit on one CU
+// (0: ask the device).
+Plan choose_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B, int64_t cus,
+                 int resident) {
   const int nt = kTilings[tiling].threads;
   const int64_t go = (d_out + kTilings[tiling].tile_o - 1) / kTilings[tiling].tile_o;
   if (g_target_wgs > 0)  // tuning: the grid asked for
     return plan_for(mode, tiling, d_out, d_in, B, (g_target_wgs + go / 2) / go);
-  const int64_t cus = device_cus();
   const double bytes = 2.0 * (double)d_in * (double)d_out * (mode == kModeDense ? 1.0 : 0.5);
   int64_t k = (int64_t)(bytes / (double)cus / kBytesPerWorkgroup + 0.5);
   k = k < kMinWgsPerCu ? kMinWgsPerCu : (k > kMaxWgsPerCu ? kMaxWgsPerCu : k);
@@ -1528,7 +1530,7 @@ Plan choose_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
   }
   // at most one resident wave of workgroups
   for (int i = 0; i < 4 && pl.gk > 1; ++i) {
-    const int64_t cap = (int64_t)resident_per_cu(fn, nt, pl.smem) * cus;
+    const int64_t cap = (int64_t)(resident > 0 ? resident : resident_per_cu(fn, nt, pl.smem)) * cus;
     if ((int64_t)pl.go * pl.gk <= cap) break;
     pl = plan_for(mode, tiling, d_out, d_in, B, cap / go);
   }
@@ -1556,7 +1558,7 @@ Plan make_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
           e.d_in == d_in && e.target == g_target_wgs && e.dev == dev)
         return e.pl;
   }
-  const Plan pl = choose_plan(mode, tiling, d_out, d_in, B);
+  const Plan pl = choose_plan(mode, tiling, d_out, d_in, B, device_cus(), 0);
   std::lock_guard<std::mutex> lock(mu);
   cache[next] = {mode, tiling, B, g_target_wgs, dev, d_out, d_in, pl, true};
   next = (next + 1) % 64;
@@ -1615,24 +1617,40 @@ size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
   return ws_layout(d_out, d_in, batch).total;
 }
 
-hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
-  int mode = c.mode;
-  if (mode == kModeList && c.batch > 1) mode = kModeListBatched;
-  const int B = (mode == kModeSwiglu || mode == kModeList) ? 1 : batch_pad(c.batch);
-  // Full-K serves batch <= 2 of every mode except batched lists; by default
-  // only for small weights, where one launch beats two.
+namespace {
+
+// The kernel and decomposition of one call shape.  cus / resident: the
+// device's compute units and the split-K kernel's workgroups per CU (0: ask
+// the device); make_plan's cache serves the launcher's own calls.
+struct Decision {
+  int mode;  // internal mode (batched lists have their own)
+  int B;     // compiled batch
+  int tiling;
+  bool full_k;
+  Plan pl;  // split-K only
+  bool one_launch;
+  bool local;
+};
+
+Decision decide_gemv(int mode, int64_t d_out, int64_t d_in, int64_t batch, int64_t cus,
+                     int resident, bool cached) {
+  Decision d{};
+  if (mode == kModeList && batch > 1) mode = kModeListBatched;
+  const int B = (mode == kModeSwiglu || mode == kModeList) ? 1 : batch_pad((int)batch);
+  // Full-K serves batch <= 2 of every mode except batched lists, for small
+  // weights whose grid fills the chip or whose walk is short.
   const bool fk_ok = B <= 2 && mode != kModeListBatched;
   int tiling = g_tiling;
   const bool hot = B == 1 && (mode == kModeThreshold || mode == kModeDense || mode == kModeList);
   if (tiling < 0) {
-    const int64_t wbytes = c.d_in * c.d_out * 2;
-    const bool fk_fills = (c.d_out + kTilings[kDefaultFullK].tile_o - 1) /
-                              kTilings[kDefaultFullK].tile_o >= device_cus() ||
-                          c.d_in <= kFullKShortDin;
+    const int64_t wbytes = d_in * d_out * 2;
+    const bool fk_fills = (d_out + kTilings[kDefaultFullK].tile_o - 1) /
+                              kTilings[kDefaultFullK].tile_o >= cus ||
+                          d_in <= kFullKShortDin;
     if (fk_ok && wbytes <= kFullKMaxWeightBytes && fk_fills)
       tiling = kDefaultFullK;
     else if (hot)
-      tiling = (wbytes <= kSmallSplitMaxWeightBytes && c.d_out <= kSmallNarrowDout)
+      tiling = (wbytes <= kSmallSplitMaxWeightBytes && d_out <= kSmallNarrowDout)
                    ? kSplitNarrowTiling
                    : kDefaultSplitKHot;
     else
@@ -1641,6 +1659,28 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   if (kTilings[tiling].full_k && !fk_ok) tiling = kDefaultSplitK;
   if (!kTilings[tiling].full_k && !hot)
     tiling = kDefaultSplitK;  // split-K variants exist for the batch-1 hot modes only
+  d.mode = mode;
+  d.B = B;
+  d.tiling = tiling;
+  d.full_k = kTilings[tiling].full_k != 0;
+  if (d.full_k) return d;
+  d.pl = cached ? make_plan(mode, tiling, d_out, d_in, B)
+                : choose_plan(mode, tiling, d_out, d_in, B, cus, resident);
+  // one launch for batch 1 and 2; from batch 3 (padded to 4) on the last
+  // workgroup's sum over B rows costs more than a second launch (measured)
+  d.one_launch = d.pl.gk > 1 && (g_handoff == 0 ? (kDefaultOneLaunch && B <= 2) : g_handoff >= 2);
+  // partials kept in L2 when every slice of a tile runs on one XCD
+  d.local = d.one_launch && g_handoff != 2 && d.pl.go % 8 == 0 && d.pl.gk <= kLocalMaxGk;
+  return d;
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
+  const Decision dc = decide_gemv(c.mode, c.d_out, c.d_in, c.batch, device_cus(), 0, true);
+  const int mode = dc.mode;
+  const int B = dc.B;
+  const int tiling = dc.tiling;
 
   KParams kp{};
   kp.wt = c.wt;
@@ -1667,7 +1707,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   kp.mu = c.mu;
   kp.var = (mode == kModeScored && c.var) ? 1 : 0;
 
-  if (kTilings[tiling].full_k) {
+  if (dc.full_k) {
     const unsigned grid = (unsigned)((c.d_out + kTilings[tiling].tile_o - 1) /
                                      kTilings[tiling].tile_o);
     switch (mode) {
@@ -1690,7 +1730,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
     }
   }
 
-  const Plan pl = make_plan(mode, tiling, c.d_out, c.d_in, B);
+  const Plan& pl = dc.pl;
   const Layout L = ws_layout(c.d_out, c.d_in, c.batch);
   if (pl.gk > 1 && (c.ws == nullptr || c.ws_bytes < L.total)) return hipErrorInvalidValue;
   if (pl.gk > kMaxGk) return hipErrorInvalidValue;  // the workspace holds kMaxGk slices
@@ -1698,13 +1738,9 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   kp.slice_cnt = ws ? reinterpret_cast<int32_t*>(ws + L.slicecnt_off) : nullptr;
   kp.part = ws ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
   kp.vsum = (kp.var && ws) ? reinterpret_cast<double*>(ws + L.vsum_off) : nullptr;
-  // one launch for batch 1 and 2; at batch 4 and 8 the last workgroup's sum
-  // over B rows costs more than a second launch (measured)
-  const bool one_launch =
-      pl.gk > 1 && (g_handoff == 0 ? (kDefaultOneLaunch && B <= 2) : g_handoff >= 2);
+  const bool one_launch = dc.one_launch;
+  const bool local = dc.local;
   kp.tickets = one_launch ? reinterpret_cast<uint32_t*>(ws + L.ticket_off) : nullptr;
-  // partials kept in L2 when every slice of a tile runs on one XCD
-  const bool local = one_launch && g_handoff != 2 && pl.go % 8 == 0 && pl.gk <= kLocalMaxGk;
   kp.go = pl.go;
   kp.gk = pl.gk;
   kp.slice = pl.slice;
@@ -1721,6 +1757,19 @@ hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, dou
   hipLaunchKernelGGL(k_col_norms, dim3((unsigned)((d_in + 3) / 4)), dim3(256), 0, s, wt, d_in,
                      d_out, out);
   return hipGetLastError();
+}
+
+int gemv_plan(int mode, int64_t d_out, int64_t d_in, int64_t batch, int cus, int resident,
+              int* kernel, int* tile_o, int* go, int* gk, int* handoff) {
+  const Decision d = decide_gemv(mode, d_out, d_in, batch, cus > 0 ? cus : device_cus(), resident,
+                                 false);
+  const Tiling& T = kTilings[d.tiling];
+  *kernel = d.full_k ? 1 : 0;
+  *tile_o = T.tile_o;
+  *go = d.full_k ? (int)((d_out + T.tile_o - 1) / T.tile_o) : d.pl.go;
+  *gk = d.full_k ? 1 : d.pl.gk;
+  *handoff = (d.full_k || d.pl.gk == 1) ? 0 : (!d.one_launch ? 1 : (d.local ? 3 : 2));
+  return 0;
 }
 
 int gemv_set_tuning(int tiling, int target_wgs, int handoff) {

@@ -303,3 +303,77 @@ def test_tiling_info(sa):
     assert (a.value, b.value, c.value) == (128, 256, 8)
     assert sa.sa_gemv_tiling_info(8, ctypes.addressof(a), None, None) == SA_OK and a.value == -16
     assert sa.sa_gemv_tiling_info(100, None, None, None) == SA_ERR_INVALID_ARG
+
+
+def _plan(op, d_out, d_in, batch=1):
+    """The decomposition on a 256-CU part with 8 resident workgroups per CU,
+    computed on the host (no device involved)."""
+    import sparse_input_gemv_amd as m
+    return m.gemv_plan(op, d_out, d_in, batch, cus=256, resident=8)
+
+
+def test_plan_headline_and_llama_shapes():
+    # the headline: 32 tiles x 24 slices, one launch, partials in L2
+    assert _plan("threshold", 4096, 11008) == {"kernel": "split-K", "tile_o": 128, "grid_o": 32,
+                                               "slices": 24, "handoff": 3}
+    assert _plan("dense", 4096, 11008)["slices"] == 32
+    # 86 tiles are not a multiple of 8: the hand-off is written through
+    p = _plan("threshold", 11008, 4096)
+    assert (p["grid_o"], p["slices"], p["handoff"]) == (86, 8, 2)
+    # balance: 4 slices (688 workgroups, <= 3 per CU) rather than 5 (860, <= 4)
+    assert _plan("threshold", 22016, 4096)["slices"] == 4
+    assert _plan("dense", 22016, 4096)["slices"] == 4
+    assert _plan("dense", 12288, 4096)["slices"] == 8
+    # batch 3..8: a second launch sums the partials
+    assert _plan("threshold", 4096, 4096, 4)["handoff"] == 1
+    assert _plan("masked", 4096, 4096, 8)["handoff"] == 1
+    assert _plan("threshold", 4096, 4096, 2)["handoff"] == 3
+
+
+def test_plan_small_weights():
+    # tall-K small weights: split-K, one workgroup per CU, 64-wide tiles at batch 1
+    p = _plan("threshold", 1024, 4096)
+    assert (p["kernel"], p["tile_o"], p["grid_o"], p["slices"]) == ("split-K", 64, 16, 16)
+    p = _plan("threshold", 1024, 4096, 2)
+    assert (p["kernel"], p["tile_o"], p["grid_o"], p["slices"]) == ("split-K", 128, 8, 32)
+    # slices of at least 128 rows
+    p = _plan("dense", 256, 4096)
+    assert p["kernel"] == "split-K" and 4096 // p["slices"] >= 128
+    # full-K where its grid covers every CU or d_in is short
+    assert _plan("threshold", 4096, 1024)["kernel"] == "full-K"
+    assert _plan("list", 1024, 1024)["kernel"] == "full-K"
+    assert _plan("dense", 4096, 512, 2)["kernel"] == "full-K"
+    # not for batched lists or batch > 2
+    assert _plan("list", 1024, 1024, 2)["kernel"] == "split-K"
+    assert _plan("threshold", 4096, 1024, 4)["kernel"] == "split-K"
+    # 8-16 MB: split-K, one workgroup per CU
+    p = _plan("dense", 1024, 8192)
+    assert (p["tile_o"], p["grid_o"] * p["slices"]) == (64, 256)
+
+
+def test_plan_follows_tuning(sa):
+    import sparse_input_gemv_amd as m
+    try:
+        m.set_gemv_tuning(-1, 0, 2)
+        assert _plan("threshold", 4096, 11008)["handoff"] == 2
+        m.set_gemv_tuning(-1, 0, 1)
+        assert _plan("threshold", 4096, 11008)["handoff"] == 1
+        m.set_gemv_tuning(8, 0, 0)
+        assert _plan("threshold", 4096, 11008)["kernel"] == "full-K"
+        m.set_gemv_tuning(0, 1024, 0)
+        p = _plan("threshold", 4096, 11008)
+        assert p["grid_o"] * p["slices"] == 1024
+    finally:
+        m.set_gemv_tuning(-1, 0, 0)
+
+
+def test_plan_checks(sa):
+    o = [ctypes.c_int() for _ in range(5)]
+    a = [ctypes.addressof(x) for x in o]
+    assert sa.sa_gemv_plan(0, 4096, 11008, 1, 256, 8, *a) == SA_OK
+    assert sa.sa_gemv_plan(5, 4096, 11008, 1, 256, 8, *a) == SA_ERR_INVALID_ARG  # unknown op
+    assert sa.sa_gemv_plan(0, 0, 11008, 1, 256, 8, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemv_plan(0, 4096, 11008, 0, 256, 8, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemv_plan(0, 4096, 11008, 9, 256, 8, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemv_plan(0, 4096, 11008, 1, -1, 8, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemv_plan(0, 4096, 11008, 1, 256, 8, None, *a[1:]) == SA_ERR_INVALID_ARG

@@ -970,3 +970,13 @@ def test_read_stream_reads_every_byte_once(nbytes):
     got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
     want = np.bitwise_xor.reduce(a[: nbytes // 4].view(np.uint32))
     assert got == want
+
+
+def test_plan_query_matches_the_device():
+    """The host-side plan with this device's facts equals the one computed
+    for a 256-CU part with 8 resident workgroups (what the CPU tests pin)."""
+    for op, d_out, d_in, b in [("threshold", 4096, 11008, 1), ("dense", 1024, 4096, 1),
+                               ("threshold", 22016, 4096, 1), ("masked", 4096, 4096, 8)]:
+        here = sa.gemv_plan(op, d_out, d_in, b)
+        fixed = sa.gemv_plan(op, d_out, d_in, b, cus=256, resident=8)
+        assert here == fixed, (op, d_out, d_in, b, here, fixed)
