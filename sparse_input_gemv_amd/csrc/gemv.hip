@@ -1468,7 +1468,9 @@ int resident_per_cu(KFn fn, int nt, size_t smem) {
 // at least 2 and at most 4.  The bytes are estimated before the call (the
 // sparse modes at half the weight), and no grid exceeds what is resident at
 // once (a workgroup waiting for a free slot would start only after the
-// others finish).
+// others finish).  Weights up to kSmallSplitMaxWeightBytes take one
+// workgroup per CU instead, and larger ones the best-balanced slice count
+// up to k per CU (choose_plan).
 Plan plan_for(int mode, int tiling, int64_t d_out, int64_t d_in, int B, int64_t gk_req) {
   Plan pl;
   const Tiling T = kTilings[tiling];
