@@ -398,6 +398,28 @@ def test_masked_swiglu_down(mode, rate):
     assert_close(y, y_ref)
 
 
+@pytest.mark.parametrize("d_model,d_ff", [(1024, 4096), (4096, 1024), (512, 3000), (264, 14336),
+                                           (2048, 2048), (4096, 6000)])
+@pytest.mark.parametrize("mode", ["cats", "rana"])
+def test_masked_swiglu_shapes(d_model, d_ff, mode):
+    """Full-K, one-pass split-K (slices of whole 64-entry words, a ragged
+    last one) and small-weight plans of the masked SwiGLU down projection;
+    the mask is bit-exact, kept count and output as the oracle."""
+    g, u = syn.swiglu_gate_up(d_ff, d_model, 5)
+    wdt = syn.weight_t(d_model, d_ff, 33)
+    cn = swiglu.column_norms(wdt)
+    sc = swiglu.scores(g, u, mode, cn)
+    t = swiglu.threshold_for_mask_rate(sc, 0.6)
+    keep, y_ref = swiglu.masked_swiglu_down(g, u, wdt, t, mode, cn)
+    wdt_g = dev(wdt)
+    cn_g = sa.weight_col_norms(wdt_g) if mode == "rana" else None
+    y, mask, nnz = sa.masked_swiglu_down(dev(g), dev(u), wdt_g, t, mode, cn_g)
+    assert (np.abs(sc - t) <= 1e-12 * t).sum() == 0
+    assert np.array_equal(sparsify.unpack_mask(words(mask), d_ff), keep)
+    assert host(nnz)[0] == keep.sum()
+    assert_close(y, y_ref)
+
+
 def test_masked_swiglu_t0_dense():
     g, u = syn.swiglu_gate_up(1000, 256, 3)
     wdt = syn.weight_t(256, 1000, 32)
