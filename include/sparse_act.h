@@ -428,9 +428,10 @@ int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
  * workgroup of each output tile, with partials written through to memory,
  * 3 = the same, but with partials kept in L2 when every slice of an output
  * tile runs on one XCD (the number of output tiles a multiple of 8, at most
- * 64 input slices; else as 2).  Automatic takes 3 at batch 1 and 2, else 1
- * (from batch 3 on, one workgroup's final sum over B rows costs more than
- * a second launch).  Every tiling computes
+ * 64 input slices; else as 2).  Automatic takes 3 (or 2 where the
+ * partials cannot stay in L2) at batch 1; at batch 2, 3 where it applies
+ * with at most 24 slices, else 1; from batch 3 on, 1 (one workgroup's final
+ * sum grows with slices x rows and then costs more than a second launch).  Every tiling computes
  * the same result up to fp32 summation order; the hand-offs give identical
  * bits.
  * Returns SA_ERR_INVALID_ARG for an unknown tiling or handoff.  Not

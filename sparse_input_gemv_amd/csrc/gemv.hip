@@ -90,7 +90,7 @@ constexpr int kMaxGk = 256;     // input slices per output tile
 constexpr double kBytesPerWorkgroup = 65536.0;
 constexpr int kMinWgsPerCu = 2;
 constexpr int kMaxWgsPerCu = 4;
-constexpr bool kDefaultOneLaunch = true;
+constexpr int kBatch2OneLaunchMaxGk = 24;  // batch 2: one launch up to this many slices
 constexpr int kReduceGroups = 16;  // slice groups of the final sum (both hand-offs)
 constexpr size_t kTicketBytes = kGemvTicketBytes;
 static_assert((size_t)(kMaxDOut / kMinSplitTileO) * kTicketStride * 4 <= kTicketBytes,
@@ -1668,11 +1668,16 @@ Decision decide_gemv(int mode, int64_t d_out, int64_t d_in, int64_t batch, int64
   if (d.full_k) return d;
   d.pl = cached ? make_plan(mode, tiling, d_out, d_in, B)
                 : choose_plan(mode, tiling, d_out, d_in, B, cus, resident);
-  // one launch for batch 1 and 2; from batch 3 (padded to 4) on the last
-  // workgroup's sum over B rows costs more than a second launch (measured)
-  d.one_launch = d.pl.gk > 1 && (g_handoff == 0 ? (kDefaultOneLaunch && B <= 2) : g_handoff >= 2);
+  // One launch at batch 1.  The last workgroup's final sum grows with
+  // slices x rows, so at batch 2 one launch pays only with the partials in
+  // L2 and few slices, and from batch 3 (padded to 4) a second launch is
+  // faster (measured: 11008 x 4096 batch 2, 86 tiles, 17.0 us two launches,
+  // 17.6 us one; 12288 x 4096 batch 2, in L2, 17.9 against 18.3 us).
+  const bool l2_ok = d.pl.go % 8 == 0 && d.pl.gk <= kLocalMaxGk;
+  const bool auto_one = B == 1 || (B == 2 && l2_ok && d.pl.gk <= kBatch2OneLaunchMaxGk);
+  d.one_launch = d.pl.gk > 1 && (g_handoff == 0 ? auto_one : g_handoff >= 2);
   // partials kept in L2 when every slice of a tile runs on one XCD
-  d.local = d.one_launch && g_handoff != 2 && d.pl.go % 8 == 0 && d.pl.gk <= kLocalMaxGk;
+  d.local = d.one_launch && g_handoff != 2 && l2_ok;
   return d;
 }
 

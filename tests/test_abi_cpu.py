@@ -328,6 +328,11 @@ def test_plan_headline_and_llama_shapes():
     assert _plan("threshold", 4096, 4096, 4)["handoff"] == 1
     assert _plan("masked", 4096, 4096, 8)["handoff"] == 1
     assert _plan("threshold", 4096, 4096, 2)["handoff"] == 3
+    # batch 2: one launch only in L2 with at most 24 slices
+    assert _plan("threshold", 4096, 11008, 2)["handoff"] == 3
+    assert _plan("threshold", 11008, 4096, 2)["handoff"] == 1  # 86 tiles
+    assert _plan("dense", 1024, 4096, 2)["handoff"] == 1  # 32 slices
+    assert _plan("threshold", 11008, 4096, 1)["handoff"] == 2
 
 
 def test_plan_small_weights():
