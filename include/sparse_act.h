@@ -439,6 +439,16 @@ int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
  */
 int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff);
 /*
+ * Process-wide fault injection for tests of the L2-local hand-off (mode 3).
+ * flags bit 0: the first input slice of every output tile reports a
+ * different XCD to the hand-off's placement check, as if it had run on
+ * another XCD.  Every tile of a call in that form then comes out NaN (the
+ * check's fallback) and its counter is reset; kernels exit normally.  0 (the
+ * default) turns it off.  Returns SA_ERR_INVALID_ARG for other flags.  Not
+ * thread-safe.
+ */
+int sa_set_gemv_test_hooks(int flags);
+/*
  * Process-wide matmul choices of dense_gemm / nm_act_spmm, for tuning sweeps
  * and cross-checks.
  *   tile_rows: 0 = automatic (dense: 256-row tiles when they give at least

@@ -75,6 +75,7 @@ _SIGNATURES = {
     "sa_set_gemm_tuning": (_i32, [_i32, _i32, _i32]),
     "sa_gemv_tiling_info": (_i32, [_i32, _vp, _vp, _vp]),
     "sa_gemv_plan": (_i32, [_i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "sa_set_gemv_test_hooks": (_i32, [_i32]),
 }
 
 _lib = None
@@ -525,6 +526,10 @@ def dense_gemm(x: torch.Tensor, wt: torch.Tensor, y: torch.Tensor | None = None)
 
 def set_gemv_tuning(tiling: int = -1, target_wgs: int = 0, handoff: int = 0) -> None:
     _check(lib().sa_set_gemv_tuning(tiling, target_wgs, handoff), "sa_set_gemv_tuning")
+
+
+def set_gemv_test_hooks(flags: int = 0) -> None:
+    _check(lib().sa_set_gemv_test_hooks(flags), "sa_set_gemv_test_hooks")
 
 
 def set_gemm_tuning(tile_rows: int = 0, engine: int = 0, stages: int = 0) -> None:

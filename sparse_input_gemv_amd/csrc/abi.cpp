@@ -459,6 +459,15 @@ int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff) {
   return SA_OK;
 }
 
+int sa_set_gemv_test_hooks(int flags) {
+  sa::clear_error();
+  if (sa::gemv_set_test_hooks(flags) != 0) {
+    sa::set_error("sa_set_gemv_test_hooks: flags must be 0 or 1 (got %d)", flags);
+    return SA_ERR_INVALID_ARG;
+  }
+  return SA_OK;
+}
+
 int sa_set_gemm_tuning(int tile_rows, int engine, int stages) {
   sa::clear_error();
   if (sa::gemm_set_tuning(tile_rows, engine, stages) != 0) {

@@ -116,6 +116,7 @@ int g_tiling = -1;     // -1: automatic
 int g_target_wgs = 0;  // 0: automatic
 int g_handoff = 0;     // 0: automatic, 1: two launches, 2: one launch, 3: one launch, in L2
                         // where every slice of a tile shares an XCD
+int g_test_hooks = 0;  // bit 0: slice 0 of each tile reports XCD id ^ 1 (placement check)
 
 struct KParams {
   const uint16_t* wt;
@@ -139,6 +140,7 @@ struct KParams {
   float* part;
   int32_t* slice_cnt;
   uint32_t* tickets;  // non-null: one-launch hand-off
+  int xcd_skew;       // test hook: slice 0 reports XCD id ^ 1 to the placement check
   int go, gk, slice;
   const float* alpha;    // [batch] output scale per row, or null
   const uint16_t* bias;  // [d_out] fp16 added to every row, or null
@@ -891,7 +893,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     if constexpr (LOCAL) {
       // fields: arrivals [5:0], sum x [15:6], sum x^2 [31:16]; every one
       // stays in its field up to the last arrival (gk <= kLocalMaxGk)
-      const uint32_t x = xcd_id();
+      const uint32_t x = xcd_id() ^ ((p.xcd_skew != 0 && kblk == 0) ? 1u : 0u);
       const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u | (x << 6) | ((x * x) << 16),
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const uint32_t gk = (uint32_t)p.gk;
@@ -1748,6 +1750,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   const bool one_launch = dc.one_launch;
   const bool local = dc.local;
   kp.tickets = one_launch ? reinterpret_cast<uint32_t*>(ws + L.ticket_off) : nullptr;
+  kp.xcd_skew = g_test_hooks & 1;
   kp.go = pl.go;
   kp.gk = pl.gk;
   kp.slice = pl.slice;
@@ -1776,6 +1779,12 @@ int gemv_plan(int mode, int64_t d_out, int64_t d_in, int64_t batch, int cus, int
   *go = d.full_k ? (int)((d_out + T.tile_o - 1) / T.tile_o) : d.pl.go;
   *gk = d.full_k ? 1 : d.pl.gk;
   *handoff = (d.full_k || d.pl.gk == 1) ? 0 : (!d.one_launch ? 1 : (d.local ? 3 : 2));
+  return 0;
+}
+
+int gemv_set_test_hooks(int flags) {
+  if (flags < 0 || flags > 1) return 1;
+  g_test_hooks = flags;
   return 0;
 }
 

@@ -85,6 +85,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s);
 hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* out,
                             hipStream_t s);
 int gemv_set_tuning(int tiling, int target_wgs, int handoff);
+int gemv_set_test_hooks(int flags);
 // The decomposition launch_gemv would use (cus, resident: 0 = ask the device).
 int gemv_plan(int mode, int64_t d_out, int64_t d_in, int64_t batch, int cus, int resident,
               int* kernel, int* tile_o, int* go, int* gk, int* handoff);

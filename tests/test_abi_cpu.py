@@ -382,3 +382,10 @@ def test_plan_checks(sa):
     assert sa.sa_gemv_plan(0, 4096, 11008, 9, 256, 8, *a) == SA_ERR_INVALID_ARG
     assert sa.sa_gemv_plan(0, 4096, 11008, 1, -1, 8, *a) == SA_ERR_INVALID_ARG
     assert sa.sa_gemv_plan(0, 4096, 11008, 1, 256, 8, None, *a[1:]) == SA_ERR_INVALID_ARG
+
+
+def test_test_hook_checks(sa):
+    assert sa.sa_set_gemv_test_hooks(2) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemv_test_hooks(-1) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemv_test_hooks(1) == SA_OK
+    assert sa.sa_set_gemv_test_hooks(0) == SA_OK

@@ -1002,3 +1002,37 @@ def test_plan_query_matches_the_device():
         here = sa.gemv_plan(op, d_out, d_in, b)
         fixed = sa.gemv_plan(op, d_out, d_in, b, cus=256, resident=8)
         assert here == fixed, (op, d_out, d_in, b, here, fixed)
+
+
+def test_l2_handoff_placement_check_fallback():
+    """The L2-local hand-off checks that every slice of a tile ran on one
+    XCD.  With the placement reported wrong on purpose (host-set hook; every
+    kernel still exits normally) each tile comes out NaN instead of a sum of
+    partials the last workgroup cannot see, and its counter is reset: the
+    next calls are exact again."""
+    d_out, d_in, _ = syn.LLAMA2_7B["down"]
+    wt = syn.weight_t(d_out, d_in, 21)
+    x = syn.laplace_f16((d_in,), 1.0, 22)
+    t = 0.69
+    keep = sparsify.threshold_sparsify(x, t)[0]
+    y_ref = gemv.masked_gemv(wt, x, keep)
+    wt_g, x_g = dev(wt), dev(x)
+    assert sa.gemv_plan("threshold", d_out, d_in)["handoff"] == 3
+    assert sa.gemv_plan("dense", d_out, d_in)["handoff"] == 3
+    y0 = sa.sparse_gemv_threshold(wt_g, x_g, t).clone()
+    try:
+        sa.set_gemv_test_hooks(1)
+        for _ in range(3):
+            assert torch.isnan(sa.sparse_gemv_threshold(wt_g, x_g, t).float()).all()
+            assert torch.isnan(sa.dense_gemv(wt_g, x_g).float()).all()
+        # the hook only concerns the L2 form: written-through hand-offs are exact
+        sa.set_gemv_tuning(-1, 0, 2)
+        assert torch.equal(sa.sparse_gemv_threshold(wt_g, x_g, t), y0)
+    finally:
+        sa.set_gemv_test_hooks(0)
+        sa.set_gemv_tuning(-1, 0, 0)
+    for _ in range(3):
+        y = sa.sparse_gemv_threshold(wt_g, x_g, t)
+        assert torch.equal(y, y0)
+    assert_close(y, y_ref)
+    assert_close(sa.dense_gemv(wt_g, x_g), gemv.dense_gemv(wt, x))
