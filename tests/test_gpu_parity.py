@@ -1036,3 +1036,55 @@ def test_l2_handoff_placement_check_fallback():
         assert torch.equal(y, y0)
     assert_close(y, y_ref)
     assert_close(sa.dense_gemv(wt_g, x_g), gemv.dense_gemv(wt, x))
+
+
+def test_graph_replays_match_eager():
+    """Calls captured in a HIP graph and replayed several times, with eager
+    calls and synchronisations between the replays, give the eager results
+    bit for bit: the one-launch hand-off's counters, in L2 or written
+    through, come back to zero on every replay, and the two-launch and
+    full-K paths hold no state."""
+    d_out, d_in = 4096, 11008
+    wt = dev(syn.weight_t(d_out, d_in, 41))
+    x = dev(syn.laplace_f16((d_in,), 1.0, 42))
+    xb = dev(syn.laplace_f16((4, d_in), 1.0, 43))
+    t = 0.69
+    _, i1, v1, n1 = sa.act_sparsify_threshold(x, t)
+    mb = sa.act_sparsify_threshold(xb, t)[0]
+    tall = dev(syn.weight_t(11008, 4096, 44))
+    xt = dev(syn.gaussian_f16((2, 4096), 1.0, 45))
+    small = dev(syn.weight_t(1024, 4096, 46))
+    xs = dev(syn.gaussian_f16((4096,), 1.0, 47))
+    g, u = (dev(a) for a in syn.swiglu_gate_up(d_in, d_out, 6))
+    X = dev(syn.gaussian_f16((256, 1024), 1.0, 48))
+    W = dev(syn.weight_t(512, 1024, 49))
+    xm, xv = sa.act_sparsify_nm(X, 2, 4)
+
+    def run():
+        outs = [sa.sparse_gemv_threshold(wt, x, t),          # one launch, in L2
+                sa.dense_gemv(wt, x),
+                sa.sparse_gemv_threshold(tall, xt[0], 0.6745),  # one launch, written through
+                sa.sparse_gemv_threshold(tall, xt, 0.6745),     # batch 2: two launches
+                sa.masked_gemv(wt, xb, mb),                     # batch 4: two launches
+                sa.sparse_gemv(wt, i1, v1, n1),
+                sa.sparse_gemv_threshold(small, xs, 0.6745),    # small weight, narrow tiles
+                sa.nm_act_spmm(xv, xm, 2, 4, W)]
+        outs += list(sa.masked_swiglu_down(g, u, wt, 0.02, "cats"))
+        outs += list(sa.act_sparsify_topk(xb, 5504))
+        return outs
+
+    eager = [o.clone() for o in run()]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = run()
+    for r in range(4):
+        sa.sparse_gemv_threshold(wt, x, t)  # eager work on the same workspace
+        sa.masked_gemv(wt, xb, mb)
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), (r, j)
