@@ -431,15 +431,31 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
       }
       return e;
     };
+    // Keys two to a register: with 15-bit keys and 1 <= cand <= 0x7fff, bit
+    // 15 of each 16-bit half of key + (0x8000 - cand) is set exactly when
+    // key >= cand (no carry leaves the half), so one packed add per two
+    // keys, a mask and a popcount count the lane's keys >= cand.
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 kp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kp[i] = u16x2{(unsigned short)key[2 * i], (unsigned short)key[2 * i + 1]};
+    auto count_ge = [&](int cand) {
+      const unsigned short off = (unsigned short)(0x8000 - cand);
+      const u16x2 o = {off, off};
+      uint32_t t = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u16x2 sum = kp[i] + o;
+        t |= (__builtin_bit_cast(uint32_t, sum) & 0x80008000u) >> i;
+      }
+      return __builtin_popcount(t);
+    };
     // tau = largest key value v with #(keys >= v) >= n: the n-th largest
     int tau = 0;
 #pragma unroll
     for (int b = 14; b >= 0; --b) {
       const int cand = tau | (1 << b);
-      int c = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c += key[i] >= cand ? 1 : 0;
-      if (group_sum(c) >= n) tau = cand;
+      if (group_sum(count_ge(cand)) >= n) tau = cand;
     }
     int gt = 0, eq = 0;
 #pragma unroll
