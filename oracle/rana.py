@@ -1,15 +1,15 @@
 """RaNA linear-layer rank adapter, plain fp64 steps (test infrastructure only).
 
 RaNA replies:
-* Q5.1: the Up-Project, Gate-Project and QKV layers are approximated as
-  ``Linear'(x) = A (m(x) ⊙ B x)`` (Eq. 11), with ``m(x)`` a binary mask over
-  the ``r`` entries of ``B x``; the columns of ``A`` at the mask's zeros are
-  skipped.
-* Q4: the adapter's masker squares ``B x`` element-wise and compares each
-  entry with a threshold (eqn. 9); ``B x`` itself is still used in the output
+* Q5.1 (Eq. 11): the rank adapter replaces each of the up, gate and QKV
+  projections by the product ``A (m(x) ⊙ B x)``, where ``m(x)`` is a 0/1
+  mask over the ``r`` entries of ``B x``; columns of ``A`` whose mask entry
+  is zero take no part.
+* Q4 (eqn. 9): the mask compares the element-wise square of ``B x`` with a
+  threshold; the unsquared ``B x`` is what the masked product multiplies
   (eqn. 4).
-* Q2 (on replacing one GEMV with two): one plain GEMV gives ``v = B x``, one
-  masked GEMV gives ``A (m(x) ⊙ v)``.
+* Q2 (two GEMVs in place of one): a plain GEMV computes ``v = B x``, then a
+  masked GEMV computes ``A (m(x) ⊙ v)``.
 
 Readings taken here (the pages leave them open):
 * ``m_i = 1`` iff ``v_i ** 2 >= t`` (the comparator the pages print for

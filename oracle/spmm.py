@@ -27,6 +27,22 @@ def nm_spmm(X, keep, wt) -> np.ndarray:
     return Y
 
 
+def masked_matmul(X, keep, wt) -> np.ndarray:
+    """The same product as ``nm_spmm`` for every token at once:
+    ``Y = (keep ⊙ X) @ WT`` in fp64, with numpy's matmul as the one library
+    step (the masked activations, widened exactly, times the widened
+    weight).  It serves the full-size workloads, where the per-token sums
+    above would take minutes.  ``keep`` may be any boolean mask of ``X``'s
+    shape (per-token N:M, or a tile-shared mask expanded to its tokens).
+    """
+    X = np.asarray(X)
+    keep = np.asarray(keep, dtype=bool)
+    if keep.shape != X.shape:
+        raise ValueError("keep must have X's shape")
+    xs = np.where(keep, X.astype(np.float64), 0.0)
+    return xs @ np.asarray(wt).astype(np.float64)
+
+
 def nm_shared_spmm(vals, tile_keep, tt: int, wt) -> np.ndarray:
     """The same product from the tile-shared compressed form: token t of tile
     ``g = t // tt`` holds its values at the kept positions of ``tile_keep[g]``

@@ -328,8 +328,22 @@ def test_batched_union_and_rows():
     for b in range(4):
         ref = sparsify.apply_mask(X[b], keep[b]) @ wt.astype(np.float64)
         np.testing.assert_allclose(Y[b], ref, rtol=1e-12, atol=1e-13)
-    assert gemv.union_columns(keep) == int(np.count_nonzero(keep.any(axis=0)))
     assert gemv.union_columns(keep[:1]) == 40
+
+
+def test_union_columns_hand_case():
+    """Rows {0, 1}, {1, 2} and {4} of 5 columns: the union has 4 columns, the
+    intersection of the first two 1 and no single row more than 2, so a
+    union/intersection or row slip gives another count."""
+    keep = np.zeros((3, 5), dtype=bool)
+    keep[0, [0, 1]] = True
+    keep[1, [1, 2]] = True
+    keep[2, 4] = True
+    assert gemv.union_columns(keep) == 4
+    assert gemv.union_columns(keep[:2]) == 3
+    assert gemv.union_columns(keep[[0, 2]]) == 3
+    assert gemv.union_columns(keep[2:]) == 1
+    assert gemv.union_columns(np.zeros((2, 5), dtype=bool)) == 0
 
 
 # --------------------------------------------------------------------------
@@ -560,6 +574,38 @@ def test_spmm_full_pattern_is_dense_matmul():
     keep = sparsify.nm_sparsify(X, 4, 4)[0]
     Y = spmm.nm_spmm(X, keep, wt)
     np.testing.assert_allclose(Y, X.astype(np.float64) @ wt.astype(np.float64), rtol=1e-12,
+                               atol=1e-13)
+
+
+def test_masked_matmul_hand_case():
+    """Token 0 keeps column 0 and token 1 column 1 of X = [[1, 2], [3, 4]];
+    WT = [[1, 2, 3], [4, 5, 6]] gives Y = [[1, 2, 3], [16, 20, 24]].  A
+    transposed operand or an unapplied mask gives other values."""
+    X = np.array([[1, 2], [3, 4]], dtype=np.float16)
+    keep = np.array([[True, False], [False, True]])
+    wt = np.array([[1, 2, 3], [4, 5, 6]], dtype=np.float16)
+    Y = spmm.masked_matmul(X, keep, wt)
+    assert Y.tolist() == [[1.0, 2.0, 3.0], [16.0, 20.0, 24.0]]
+    assert spmm.nm_spmm(X, keep, wt).tolist() == Y.tolist()
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (16, 32)])
+def test_masked_matmul_is_the_per_token_sum(n, m):
+    """The one-matmul form equals the per-token sums over kept columns, for
+    N:M masks, for an arbitrary mask, and for a tile-shared mask expanded to
+    its tokens."""
+    X = syn.gaussian_f16((37, 96), 1.0, 40 + m)
+    wt = syn.weight_t(56, 96, 41 + m)
+    keep = sparsify.nm_sparsify(X, n, m)[0]
+    np.testing.assert_allclose(spmm.masked_matmul(X, keep, wt), spmm.nm_spmm(X, keep, wt),
+                               rtol=1e-12, atol=1e-13)
+    rnd = np.random.default_rng(m).random(X.shape) < 0.3
+    np.testing.assert_allclose(spmm.masked_matmul(X, rnd, wt), spmm.nm_spmm(X, rnd, wt),
+                               rtol=1e-12, atol=1e-13)
+    _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, 8)
+    expanded = np.repeat(tile_keep, 8, axis=0)[:X.shape[0]]
+    np.testing.assert_allclose(spmm.masked_matmul(X, expanded, wt),
+                               spmm.nm_shared_spmm(vals, tile_keep, 8, wt), rtol=1e-12,
                                atol=1e-13)
 
 
