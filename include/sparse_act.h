@@ -25,11 +25,12 @@
  *   detected on the host before any HIP call and leave outputs untouched;
  *   sa_last_error() then describes the first failing check for the calling
  *   thread.  No C++ exception crosses this boundary.
- * - A workspace `ws` (sized by sa_workspace_bytes, 256-byte aligned) holds
- *   per-call partial sums and, in its first SA_WS_TICKET_BYTES, one arrival
- *   counter per output tile for the one-launch split-K hand-off.  That
- *   region must be all zero before the workspace is first used (allocate
- *   it zero-filled); every call leaves it zero again.  The rest may hold
+ * - A workspace `ws` (sized by sparse_gemv_workspace_bytes, 256-byte
+ *   aligned) holds per-call partial sums and, in its first
+ *   SA_WS_TICKET_BYTES (= sa_workspace_zero_bytes()), one arrival counter
+ *   per output tile for the one-launch split-K hand-off.  That region must
+ *   be all zero before the workspace is first used (allocate it
+ *   zero-filled); every call leaves it zero again.  The rest may hold
  *   anything on entry.  Calls that share one workspace must be ordered on
  *   one stream: concurrent calls race.
  * - rows == 0 (or batch == 0, T == 0) is a valid empty call and does nothing.
@@ -191,11 +192,22 @@ int act_calibrate_threshold(const uint16_t* samples, int64_t n, double s,
 
 /*
  * Bytes of workspace needed by the GEMV family (sparse_gemv,
- * sparse_gemv_threshold, masked_gemv, dense_gemv, masked_swiglu_down) for
- * an output length d_out, input length d_in and up to `batch` rows.  The
- * same size serves every call whose sizes do not exceed these.
+ * sparse_gemv_threshold, sparse_gemv_corrected, sparse_gemv_scored,
+ * masked_gemv, dense_gemv, masked_swiglu_down, rana_adapter_gemv) for an
+ * output length d_out, input length d_in and up to `batch` rows (batch is
+ * clamped to 1..SA_MAX_BATCH); 0 for d_out or d_in < 1.  The same size
+ * serves every call whose sizes do not exceed these.
+ * sparse_gemv_workspace_bytes is the name the hot-path contract uses;
+ * sa_workspace_bytes is the same function.
  */
+size_t sparse_gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch);
 size_t sa_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch);
+/*
+ * Leading bytes of that workspace that must be zero before a call and that
+ * every call leaves zero: the hand-off counters, SA_WS_TICKET_BYTES for
+ * every size (the arguments are accepted for symmetry).
+ */
+size_t sa_workspace_zero_bytes(int64_t d_out, int64_t d_in, int64_t batch);
 
 /*
  * sparse_gemv -- y[b] = sum_{j < nnz[b]} W[:, idx[b][j]] * val[b][j].
@@ -426,26 +438,28 @@ int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
  * for (0 = automatic) and `handoff` how split-K partials are summed:
  * 0 = automatic, 1 = a second launch, 2 = in the same launch by the last
  * workgroup of each output tile, with partials written through to memory,
- * 3 = the same, but with partials kept in L2 when every slice of an output
- * tile runs on one XCD (the number of output tiles a multiple of 8, at most
- * 64 input slices; else as 2).  Automatic takes 3 (or 2 where the
- * partials cannot stay in L2) at batch 1; at batch 2, 3 where it applies
+ * 3 = the same, but with partials kept in L2 when the tile count lets every
+ * slice of an output tile run on one XCD (a multiple of 8 tiles, at most 64
+ * input slices; else as 2).  In form 3 the last workgroup checks where the
+ * slices ran; if they ran on more than one XCD, it recomputes the other
+ * slices' partials itself (same bits, much slower), so the result never
+ * depends on where the hardware placed the workgroups.  Automatic takes 3
+ * (or 2 where it does not apply) at batch 1; at batch 2, 3 where it applies
  * with at most 24 slices, else 1; from batch 3 on, 1 (one workgroup's final
- * sum grows with slices x rows and then costs more than a second launch).  Every tiling computes
- * the same result up to fp32 summation order; the hand-offs give identical
- * bits.
+ * sum grows with slices x rows and then costs more than a second launch).
+ * Every tiling computes the same result up to fp32 summation order; the
+ * hand-offs give identical bits.
  * Returns SA_ERR_INVALID_ARG for an unknown tiling or handoff.  Not
  * thread-safe.
  */
 int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff);
 /*
- * Process-wide fault injection for tests of the L2-local hand-off (mode 3).
+ * Process-wide fault injection for tests of the L2-local hand-off (form 3).
  * flags bit 0: the first input slice of every output tile reports a
  * different XCD to the hand-off's placement check, as if it had run on
- * another XCD.  Every tile of a call in that form then comes out NaN (the
- * check's fallback) and its counter is reset; kernels exit normally.  0 (the
- * default) turns it off.  Returns SA_ERR_INVALID_ARG for other flags.  Not
- * thread-safe.
+ * another XCD.  The last workgroup of every tile then takes the recompute
+ * path; results are unchanged, bit for bit.  0 (the default) turns it off.
+ * Returns SA_ERR_INVALID_ARG for other flags.  Not thread-safe.
  */
 int sa_set_gemv_test_hooks(int flags);
 /*

@@ -30,7 +30,8 @@ __all__ = [
     "masked_gemv",
     "dense_gemv", "masked_swiglu_down", "weight_col_norms", "nm_act_spmm", "nm_shared_spmm",
     "dense_gemm",
-    "set_gemv_tuning", "set_gemm_tuning", "gemv_tiling_info", "workspace_bytes", "MAX_BATCH",
+    "set_gemv_tuning", "set_gemm_tuning", "gemv_tiling_info", "workspace_bytes",
+    "workspace_zero_bytes", "scratch", "MAX_BATCH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_act.so")
@@ -49,6 +50,8 @@ _SIGNATURES = {
     "act_sparsify_nm_shared": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "act_calibrate_threshold": (_i32, [_vp, _i64, _f64, _vp, _vp]),
     "sa_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "sparse_gemv_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "sa_workspace_zero_bytes": (_sz, [_i64, _i64, _i64]),
     "sparse_gemv": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "sparse_gemv_threshold": (_i32, [_vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _sz, _vp]),
     "act_sparsify_scored": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _f64, _vp, _vp, _vp,
@@ -132,26 +135,55 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
     return t
 
 
-_ws: dict = {}
+_ws: dict = {}       # device index -> the GEMV workspace in use
+_scratch: dict = {}  # device index -> the matmuls' scratch in use
+# Superseded buffers stay allocated until the process ends: a HIP graph
+# captured before a buffer grew still holds the old buffer's address, and
+# its replays must find memory that is theirs (and, for a GEMV workspace,
+# still zero where the library keeps it zero).
+_retired: list = []
 
 
 def workspace_bytes(d_out: int, d_in: int, batch: int = 1) -> int:
-    return int(lib().sa_workspace_bytes(d_out, d_in, batch))
+    return int(lib().sparse_gemv_workspace_bytes(d_out, d_in, batch))
+
+
+def workspace_zero_bytes(d_out: int, d_in: int, batch: int = 1) -> int:
+    return int(lib().sa_workspace_zero_bytes(d_out, d_in, batch))
+
+
+def _grow(table: dict, device, nbytes: int, zero: bool, what: str) -> torch.Tensor:
+    key = torch.device(device).index or 0
+    buf = table.get(key)
+    if buf is None or buf.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(
+                f"the {what} must grow to {nbytes} bytes while a HIP graph is being captured; "
+                "make one eager call of the largest shape before capturing")
+        size = max(nbytes, 1 << 20, 0 if buf is None else 2 * buf.numel())
+        new = (torch.zeros if zero else torch.empty)(size, dtype=torch.uint8, device=device)
+        if buf is not None:
+            _retired.append(buf)
+        table[key] = buf = new
+    return buf
 
 
 def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """Per-device workspace for partial sums, grown on demand and reused.
+    """Per-device GEMV workspace, grown on demand (at least doubling) and reused.
 
-    Allocated zero-filled: its leading hand-off counters must start at zero
-    (the library returns them to zero after every call).  Calls on one
-    device share it, so they must be ordered on one stream.
+    Allocated zero-filled: its leading region (hand-off counters and slots)
+    must start at zero, and the library returns it to zero after every call.
+    Only the GEMV family uses it.  Calls on one device share it, so they must
+    be ordered on one stream.  Growth is refused during graph capture.
     """
-    key = torch.device(device).index or 0
-    ws = _ws.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        _ws[key] = ws
-    return ws
+    return _grow(_ws, device, nbytes, True, "GEMV workspace")
+
+
+def scratch(device: torch.device, nbytes: int) -> torch.Tensor:
+    """Per-device scratch of the matmuls (contents undefined), grown on
+    demand; separate from the GEMV workspace, whose zero region it must not
+    touch."""
+    return _grow(_scratch, device, nbytes, False, "matmul scratch")
 
 
 def _rows(x: torch.Tensor):
@@ -449,9 +481,7 @@ def weight_col_norms(wt: torch.Tensor) -> torch.Tensor:
 
 # ---- batched matmuls ---------------------------------------------------------
 
-# The GEMV workspace starts with hand-off counters that must stay zero; the
-# matmul's scratch copy goes after them in the same per-device buffer.
-WS_TICKET_BYTES = 1 << 20
+WS_TICKET_BYTES = 1 << 20  # SA_WS_TICKET_BYTES
 READ_STREAM_SINK_WORDS = 8192  # SA_READ_STREAM_SINK_WORDS
 
 
@@ -482,8 +512,8 @@ def nm_act_spmm(xval: torch.Tensor, mask: torch.Tensor, n: int, m: int, wt: torc
     ws_ptr, ws_bytes = None, 0
     need = int(lib().sa_nm_spmm_workspace_bytes(T, d_in, n, m))
     if use_workspace and need > 0:
-        ws = workspace(wt.device, WS_TICKET_BYTES + need)
-        ws_ptr, ws_bytes = ws.data_ptr() + WS_TICKET_BYTES, ws.numel() - WS_TICKET_BYTES
+        ws = scratch(wt.device, need)
+        ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     _check(lib().nm_act_spmm(_ptr(xval), _ptr(mask), T, d_in, n, m, _ptr(wt), d_out, _ptr(y),
                              ws_ptr, ws_bytes, _stream(wt)), "nm_act_spmm")
     return y
@@ -503,8 +533,8 @@ def nm_shared_spmm(xval: torch.Tensor, mask: torch.Tensor, n: int, m: int, tt: i
     ws_ptr, ws_bytes = None, 0
     need = int(lib().sa_nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt))
     if need > 0:
-        ws = workspace(wt.device, WS_TICKET_BYTES + need)
-        ws_ptr, ws_bytes = ws.data_ptr() + WS_TICKET_BYTES, ws.numel() - WS_TICKET_BYTES
+        ws = scratch(wt.device, need)
+        ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     _check(lib().nm_shared_spmm(_ptr(xval), _ptr(mask), T, d_in, n, m, tt, _ptr(wt), d_out,
                                 _ptr(y), ws_ptr, ws_bytes, _stream(wt)), "nm_shared_spmm")
     return y

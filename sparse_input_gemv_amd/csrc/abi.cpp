@@ -115,6 +115,17 @@ size_t sa_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
   return sa::gemv_workspace_bytes(d_out, d_in, batch);
 }
 
+size_t sparse_gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
+  return sa_workspace_bytes(d_out, d_in, batch);
+}
+
+size_t sa_workspace_zero_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
+  if (d_out < 1 || d_in < 1) return 0;
+  if (batch < 1) batch = 1;
+  if (batch > SA_MAX_BATCH) batch = SA_MAX_BATCH;
+  return sa::gemv_workspace_zero_bytes(d_out, d_in, batch);
+}
+
 static int run_gemv(const sa::GemvCall& c, const char* fn, void* stream) {
   if (c.batch == 0) return SA_OK;
   return hip_status(sa::launch_gemv(c, as_stream(stream)), fn);

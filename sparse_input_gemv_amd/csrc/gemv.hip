@@ -418,504 +418,521 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   constexpr bool kPairs = B > 1;
   const int SLH = (SL + 2) & ~1;
   uint16_t* lvh = reinterpret_cast<uint16_t*>(smem + (size_t)SL * 4);
+  uint32_t* const ticket = p.tickets + (int64_t)oblk * kTicketStride;
+  const int64_t o0 = (int64_t)oblk * TILE_O;
+  // scored mode with the variance correction: alpha of the row (set below)
+  __shared__ float s_alpha;
+  const float* alpha_out = (MODE == kModeScored && p.var) ? &s_alpha : alpha_arg;
+  __shared__ int s_last;
 
-  // ---------------- phase 1: kept rows of this workgroup -> LDS ----------
-  int cnt = 0;
-  double s_all = 0.0, s_kept = 0.0;  // scored mode: variance-correction sums
-  const int64_t slice_k0 = (int64_t)kblk * SL;
-  const int64_t slice_span = (slice_k0 + SL < p.d_in ? slice_k0 + SL : p.d_in) - slice_k0;
-  if constexpr (MODE == kModeList) {
-    int64_t nn = p.nnz[0];
-    const int64_t lim = p.cap < p.d_in ? p.cap : p.d_in;
-    nn = nn < 0 ? 0 : (nn > lim ? lim : nn);
-    const int64_t p0 = ((int64_t)kblk * nn) / p.gk;
-    const int64_t p1 = ((int64_t)(kblk + 1) * nn) / p.gk;
-    cnt = (int)(p1 - p0);
-    for (int j = tid; j < cnt; j += NT) {
-      const int32_t kk = p.idx[p0 + j];
-      const bool ok = kk >= 0 && (int64_t)kk < p.d_in;
-      lk[j] = ok ? kk : 0;
-      lv[j] = ok ? h2f(p.val[p0 + j]) : 0.f;
-    }
-    __syncthreads();
-  } else if constexpr (MODE == kModeListBatched) {
-    // Rows of the slice present in any list: mark them in a dense LDS
-    // staging area, then compact.
-    const int64_t k0 = (int64_t)kblk * SL;
-    const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
-    const int span = (int)(k1 - k0);
-    int* flag = reinterpret_cast<int*>(smem + (size_t)SL * 4 + (size_t)B * SLH * 2);
-    uint16_t* dv = reinterpret_cast<uint16_t*>(smem + (size_t)SL * 8 + (size_t)B * SLH * 2);
-    for (int j = tid; j < SL; j += NT) {
-      flag[j] = 0;
-#pragma unroll
-      for (int b = 0; b < B; ++b) dv[b * SL + j] = 0;
-    }
-    __syncthreads();
-    const int w = tid / kWave;
-    for (int b = w; b < p.batch; b += NT / kWave) {
-      const int32_t* ib = p.idx + (int64_t)b * p.cap;
-      const uint16_t* vb = p.val + (int64_t)b * p.cap;
-      int64_t nn = p.nnz[b];
+  // One pass per slice this workgroup computes: its own slice kblk, and only
+  // where the tile's slices turned out to run on more than one XCD (see the
+  // hand-off), every other slice of the tile as well.
+  int kb = kblk;
+  bool recompute = false;
+  for (;;) {
+    // ---------------- phase 1: kept rows of this workgroup -> LDS ----------
+    int cnt = 0;
+    double s_all = 0.0, s_kept = 0.0;  // scored mode: variance-correction sums
+    const int64_t slice_k0 = (int64_t)kb * SL;
+    const int64_t slice_span = (slice_k0 + SL < p.d_in ? slice_k0 + SL : p.d_in) - slice_k0;
+    if constexpr (MODE == kModeList) {
+      int64_t nn = p.nnz[0];
       const int64_t lim = p.cap < p.d_in ? p.cap : p.d_in;
       nn = nn < 0 ? 0 : (nn > lim ? lim : nn);
-      const int64_t lo = wave_lower_bound(ib, nn, k0);
-      const int64_t hi = wave_lower_bound(ib, nn, k1);
-      for (int64_t q = lo + lane_id(); q < hi; q += kWave) {
-        const int64_t kk = ib[q];
-        if (kk >= k0 && kk < k1) {
-          flag[kk - k0] = 1;
-          dv[b * SL + (kk - k0)] = vb[q];
-        }
+      const int64_t p0 = ((int64_t)kb * nn) / p.gk;
+      const int64_t p1 = ((int64_t)(kb + 1) * nn) / p.gk;
+      cnt = (int)(p1 - p0);
+      for (int j = tid; j < cnt; j += NT) {
+        const int32_t kk = p.idx[p0 + j];
+        const bool ok = kk >= 0 && (int64_t)kk < p.d_in;
+        lk[j] = ok ? kk : 0;
+        lv[j] = ok ? h2f(p.val[p0 + j]) : 0.f;
       }
-    }
-    __syncthreads();
-    for (int c = 0; c < span; c += NT) {
-      const int j = c + tid;
-      const bool keep = j < span && flag[j] != 0;
-      int total;
-      uint64_t wm;
-      const int slot = chunk_slot<NT>(keep, wsum, total, wm);
-      if (keep) {
-        lk[cnt + slot] = (int)(k0 + j);
+      __syncthreads();
+    } else if constexpr (MODE == kModeListBatched) {
+      // Rows of the slice present in any list: mark them in a dense LDS
+      // staging area, then compact.
+      const int64_t k0 = (int64_t)kb * SL;
+      const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
+      const int span = (int)(k1 - k0);
+      int* flag = reinterpret_cast<int*>(smem + (size_t)SL * 4 + (size_t)B * SLH * 2);
+      uint16_t* dv = reinterpret_cast<uint16_t*>(smem + (size_t)SL * 8 + (size_t)B * SLH * 2);
+      for (int j = tid; j < SL; j += NT) {
+        flag[j] = 0;
 #pragma unroll
-        for (int b = 0; b < B; ++b) lvh[b * SLH + cnt + slot] = dv[b * SL + j];
+        for (int b = 0; b < B; ++b) dv[b * SL + j] = 0;
       }
-      cnt += total;
-    }
-    __syncthreads();
-  } else if (kOnePassChunks<B> > 0 && slice_span <= (int64_t)kOnePassChunks<B> * NT) {
-    // One pass: every chunk's x (and mask word; SwiGLU: gate, up and norm)
-    // loads are issued before any decision, so the slice costs one memory
-    // round trip; the kept slots of all chunks come from one table of
-    // per-chunk, per-wave ballot counts (one barrier).  Entry k0 + c*NT + tid
-    // of chunk c; chunk-major order keeps the list ascending.
-    constexpr int PC = kOnePassChunks<B> > 0 ? kOnePassChunks<B> : 1;
-    constexpr int NW = NT / kWave;
-    __shared__ int wtab[PC * NW];
-    const int64_t k0 = (int64_t)kblk * SL;
-    const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
-    const int64_t words = (p.d_in + 31) >> 5;
-    const int nch = (int)((slice_span + NT - 1) / NT);  // chunks this slice has
-    uint16_t xr[PC][B];
-    uint32_t mw[PC][B];
-    uint16_t ms[PC];  // scored: shift; SwiGLU: up
-    double cs[PC];    // scored, SwiGLU mode 1: weight norm
-    float hv[PC];     // SwiGLU: the kept value h
-    // Every chunk's loads, also past the slice (clamped to its first entry):
-    // leaving the loop early would put a wait for each load before the
-    // branch, one round trip per chunk.
-#pragma unroll
-    for (int c = 0; c < PC; ++c) {
-      const int64_t k = k0 + (int64_t)c * NT + tid;
-      const int64_t kc = k < k1 ? k : k0;
-      if constexpr (MODE == kModeSwiglu) {
-        xr[c][0] = p.g[kc];
-        ms[c] = p.u[kc];
-        cs[c] = p.swiglu_mode != 0 ? p.colnorm[kc] : 0.0;
-      } else {
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const int64_t bb = b < p.batch ? b : 0;
-          xr[c][b] = p.x[bb * p.d_in + kc];
-          if constexpr (MODE == kModeMasked) mw[c][b] = p.xmask[bb * words + (kc >> 5)];
-        }
-      }
-      if constexpr (MODE == kModeScored) {
-        ms[c] = p.mu != nullptr ? p.mu[kc] : (uint16_t)0;
-        cs[c] = p.colnorm != nullptr ? p.colnorm[kc] : 1.0;
-      }
-    }
-    const int w = tid / kWave;
-    bool keep[PC];
-    uint64_t bm[PC];
-#pragma unroll
-    for (int c = 0; c < PC; ++c) {
-      if (c > 0 && c >= nch) break;
-      const int64_t k = k0 + (int64_t)c * NT + tid;
-      bool any = false;
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const uint16_t xb = xr[c][b];
-        bool kb = false;
-        if constexpr (MODE == kModeScored) {
-          kb = scored_keep(p, xr[c][b], ms[c], cs[c], b < p.batch && k < k1, s_all, s_kept);
-        } else if constexpr (MODE == kModeSwiglu) {
-          hv[c] = 0.f;
-          kb = k < k1 && swiglu_keep(xb, ms[c], cs[c], p.swiglu_mode, p.t64, hv[c]);
-        } else if (b < p.batch && k < k1) {
-          if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
-            kb = keep_entry<MODE>(xb, p.t);
-          } else if constexpr (MODE == kModeMasked) {
-            kb = ((mw[c][b] >> (k & 31)) & 1u) != 0;
-          } else {
-            kb = true;
+      __syncthreads();
+      const int w = tid / kWave;
+      for (int b = w; b < p.batch; b += NT / kWave) {
+        const int32_t* ib = p.idx + (int64_t)b * p.cap;
+        const uint16_t* vb = p.val + (int64_t)b * p.cap;
+        int64_t nn = p.nnz[b];
+        const int64_t lim = p.cap < p.d_in ? p.cap : p.d_in;
+        nn = nn < 0 ? 0 : (nn > lim ? lim : nn);
+        const int64_t lo = wave_lower_bound(ib, nn, k0);
+        const int64_t hi = wave_lower_bound(ib, nn, k1);
+        for (int64_t q = lo + lane_id(); q < hi; q += kWave) {
+          const int64_t kk = ib[q];
+          if (kk >= k0 && kk < k1) {
+            flag[kk - k0] = 1;
+            dv[b * SL + (kk - k0)] = vb[q];
           }
         }
-        if (!kb) xr[c][b] = 0;  // what a skipped entry (or absent row) contributes
-        any = any || kb;
       }
-      keep[c] = any;
-      bm[c] = __ballot(any);
-      if (lane_id() == 0) wtab[c * NW + w] = (int)__popcll(bm[c]);
-      if constexpr (MODE == kModeSwiglu) {
-        // the mask: a wave covers 64 entries from a multiple of 64 (slices
-        // are aligned to 64), so its two words are its own
-        const int64_t kw = k0 + (int64_t)c * NT + (int64_t)w * kWave;
-        if (p.out_mask != nullptr && oblk == 0 && lane_id() == 0 && kw < k1) {
-          p.out_mask[kw >> 5] = (uint32_t)bm[c];
-          if (kw + 32 < p.d_in) p.out_mask[(kw >> 5) + 1] = (uint32_t)(bm[c] >> 32);
+      __syncthreads();
+      for (int c = 0; c < span; c += NT) {
+        const int j = c + tid;
+        const bool keep = j < span && flag[j] != 0;
+        int total;
+        uint64_t wm;
+        const int slot = chunk_slot<NT>(keep, wsum, total, wm);
+        if (keep) {
+          lk[cnt + slot] = (int)(k0 + j);
+#pragma unroll
+          for (int b = 0; b < B; ++b) lvh[b * SLH + cnt + slot] = dv[b * SL + j];
         }
+        cnt += total;
       }
-    }
-    __syncthreads();
+      __syncthreads();
+    } else if (kOnePassChunks<B> > 0 && slice_span <= (int64_t)kOnePassChunks<B> * NT) {
+      // One pass: every chunk's x (and mask word; SwiGLU: gate, up and norm)
+      // loads are issued before any decision, so the slice costs one memory
+      // round trip; the kept slots of all chunks come from one table of
+      // per-chunk, per-wave ballot counts (one barrier).  Entry k0 + c*NT + tid
+      // of chunk c; chunk-major order keeps the list ascending.
+      constexpr int PC = kOnePassChunks<B> > 0 ? kOnePassChunks<B> : 1;
+      constexpr int NW = NT / kWave;
+      __shared__ int wtab[PC * NW];
+      const int64_t k0 = (int64_t)kb * SL;
+      const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
+      const int64_t words = (p.d_in + 31) >> 5;
+      const int nch = (int)((slice_span + NT - 1) / NT);  // chunks this slice has
+      uint16_t xr[PC][B];
+      uint32_t mw[PC][B];
+      uint16_t ms[PC];  // scored: shift; SwiGLU: up
+      double cs[PC];    // scored, SwiGLU mode 1: weight norm
+      float hv[PC];     // SwiGLU: the kept value h
+      // Every chunk's loads, also past the slice (clamped to its first entry):
+      // leaving the loop early would put a wait for each load before the
+      // branch, one round trip per chunk.
 #pragma unroll
-    for (int c = 0; c < PC; ++c) {
-      if (c > 0 && c >= nch) break;
-      int before = 0, tot = 0;
-#pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        const int v = wtab[c * NW + i];
-        before += (i < w) ? v : 0;
-        tot += v;
-      }
-      if (keep[c]) {
-        const int slot = cnt + before + lanes_below(bm[c]);
-        lk[slot] = (int)(k0 + (int64_t)c * NT + tid);
-        if constexpr (kPairs) {
-#pragma unroll
-          for (int b = 0; b < B; ++b) lvh[b * SLH + slot] = xr[c][b];
-        } else if constexpr (MODE == kModeSwiglu) {
-          lv[slot] = hv[c];
+      for (int c = 0; c < PC; ++c) {
+        const int64_t k = k0 + (int64_t)c * NT + tid;
+        const int64_t kc = k < k1 ? k : k0;
+        if constexpr (MODE == kModeSwiglu) {
+          xr[c][0] = p.g[kc];
+          ms[c] = p.u[kc];
+          cs[c] = p.swiglu_mode != 0 ? p.colnorm[kc] : 0.0;
         } else {
-          lv[slot] = h2f(xr[c][0]);
-        }
-      }
-      cnt += tot;
-    }
-    if constexpr (MODE == kModeSwiglu) {
-      if (oblk == 0 && tid == 0) {
-        if (p.gk == 1) {
-          if (p.out_nnz != nullptr) p.out_nnz[0] = cnt;
-        } else {
-          store_handoff(p.slice_cnt + kblk, (int32_t)cnt, LOCAL);
-        }
-      }
-    }
-    __syncthreads();
-  } else {
-    const int64_t k0 = (int64_t)kblk * SL;
-    const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
-    const int64_t words = (p.d_in + 31) >> 5;
-    for (int64_t c = k0; c < k1; c += NT) {
-      const int64_t k = c + tid;
-      const bool in = k < k1;
-      float vb[B];
-      uint16_t hb[B];  // fp16 bits of kept values (0 otherwise), batch > 1
-      bool any = false;
-      if constexpr (MODE == kModeSwiglu) {
-        float hv = 0.f;
-        any = in && swiglu_keep(p.g[k], p.u[k], p.swiglu_mode != 0 ? p.colnorm[k] : 0.0,
-                                p.swiglu_mode, p.t64, hv);
-        vb[0] = hv;
-      } else {
-        // every row's load first, from in-range addresses (k0 < d_in), so
-        // they are in flight together; then the decisions
-        const int64_t kc = in ? k : k0;
-        uint16_t xr[B];
-        uint32_t mw[B];
-        uint16_t ms = 0;  // scored: shift and weight norm
-        double cs = 1.0;
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const int64_t bb = b < p.batch ? b : 0;
-          xr[b] = p.x[bb * p.d_in + kc];
-          if constexpr (MODE == kModeMasked) mw[b] = p.xmask[bb * words + (kc >> 5)];
+          for (int b = 0; b < B; ++b) {
+            const int64_t bb = b < p.batch ? b : 0;
+            xr[c][b] = p.x[bb * p.d_in + kc];
+            if constexpr (MODE == kModeMasked) mw[c][b] = p.xmask[bb * words + (kc >> 5)];
+          }
         }
         if constexpr (MODE == kModeScored) {
-          if (p.mu != nullptr) ms = p.mu[kc];
-          if (p.colnorm != nullptr) cs = p.colnorm[kc];
+          ms[c] = p.mu != nullptr ? p.mu[kc] : (uint16_t)0;
+          cs[c] = p.colnorm != nullptr ? p.colnorm[kc] : 1.0;
         }
+      }
+      const int w = tid / kWave;
+      bool keep[PC];
+      uint64_t bm[PC];
+#pragma unroll
+      for (int c = 0; c < PC; ++c) {
+        if (c > 0 && c >= nch) break;
+        const int64_t k = k0 + (int64_t)c * NT + tid;
+        bool any = false;
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-          vb[b] = 0.f;
-          hb[b] = 0;
+          const uint16_t xb = xr[c][b];
+          bool kb = false;
           if constexpr (MODE == kModeScored) {
-            if (scored_keep(p, xr[b], ms, cs, in && b < p.batch, s_all, s_kept)) {
-              vb[b] = h2f(xr[b]);
-              hb[b] = xr[b];
-              any = true;
-            }
-          } else if (b < p.batch && in) {
-            const uint16_t xb = xr[b];
-            bool kb;
+            kb = scored_keep(p, xr[c][b], ms[c], cs[c], b < p.batch && k < k1, s_all, s_kept);
+          } else if constexpr (MODE == kModeSwiglu) {
+            hv[c] = 0.f;
+            kb = k < k1 && swiglu_keep(xb, ms[c], cs[c], p.swiglu_mode, p.t64, hv[c]);
+          } else if (b < p.batch && k < k1) {
             if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
               kb = keep_entry<MODE>(xb, p.t);
             } else if constexpr (MODE == kModeMasked) {
-              kb = ((mw[b] >> (k & 31)) & 1u) != 0;
+              kb = ((mw[c][b] >> (k & 31)) & 1u) != 0;
             } else {
               kb = true;
             }
-            if (kb) {
-              vb[b] = h2f(xb);
-              hb[b] = xb;
-            }
-            any = any || kb;
+          }
+          if (!kb) xr[c][b] = 0;  // what a skipped entry (or absent row) contributes
+          any = any || kb;
+        }
+        keep[c] = any;
+        bm[c] = __ballot(any);
+        if (lane_id() == 0) wtab[c * NW + w] = (int)__popcll(bm[c]);
+        if constexpr (MODE == kModeSwiglu) {
+          // the mask: a wave covers 64 entries from a multiple of 64 (slices
+          // are aligned to 64), so its two words are its own
+          const int64_t kw = k0 + (int64_t)c * NT + (int64_t)w * kWave;
+          if (p.out_mask != nullptr && oblk == 0 && lane_id() == 0 && kw < k1) {
+            p.out_mask[kw >> 5] = (uint32_t)bm[c];
+            if (kw + 32 < p.d_in) p.out_mask[(kw >> 5) + 1] = (uint32_t)(bm[c] >> 32);
           }
         }
-        if constexpr (MODE == kModeDense) any = in;
       }
-      int total;
-      uint64_t wm;
-      const int slot = chunk_slot<NT>(any, wsum, total, wm);
-      if (any) {
-        lk[cnt + slot] = (int)k;
-        if constexpr (kPairs) {
+      __syncthreads();
 #pragma unroll
-          for (int b = 0; b < B; ++b) lvh[b * SLH + cnt + slot] = hb[b];
-        } else {
-          lv[cnt + slot] = vb[0];
+      for (int c = 0; c < PC; ++c) {
+        if (c > 0 && c >= nch) break;
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+          const int v = wtab[c * NW + i];
+          before += (i < w) ? v : 0;
+          tot += v;
         }
+        if (keep[c]) {
+          const int slot = cnt + before + lanes_below(bm[c]);
+          lk[slot] = (int)(k0 + (int64_t)c * NT + tid);
+          if constexpr (kPairs) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) lvh[b * SLH + slot] = xr[c][b];
+          } else if constexpr (MODE == kModeSwiglu) {
+            lv[slot] = hv[c];
+          } else {
+            lv[slot] = h2f(xr[c][0]);
+          }
+        }
+        cnt += tot;
       }
       if constexpr (MODE == kModeSwiglu) {
-        // each wave covers 64 consecutive entries starting at a multiple of 64
-        if (p.out_mask != nullptr && oblk == 0 && lane_id() == 0) {
-          const int64_t kw = c + (int64_t)(tid / kWave) * kWave;
-          if (kw < k1) {
-            p.out_mask[kw >> 5] = (uint32_t)wm;
-            if (kw + 32 < p.d_in) p.out_mask[(kw >> 5) + 1] = (uint32_t)(wm >> 32);
+        if (oblk == 0 && tid == 0) {
+          if (p.gk == 1) {
+            if (p.out_nnz != nullptr) p.out_nnz[0] = cnt;
+          } else {
+            store_handoff(p.slice_cnt + kb, (int32_t)cnt, LOCAL);
           }
         }
       }
-      cnt += total;
-    }
-    if constexpr (MODE == kModeSwiglu) {
-      if (oblk == 0 && tid == 0) {
-        if (p.gk == 1) {
-          if (p.out_nnz != nullptr) p.out_nnz[0] = cnt;
+      __syncthreads();
+    } else {
+      const int64_t k0 = (int64_t)kb * SL;
+      const int64_t k1 = (k0 + SL < p.d_in) ? k0 + SL : p.d_in;
+      const int64_t words = (p.d_in + 31) >> 5;
+      for (int64_t c = k0; c < k1; c += NT) {
+        const int64_t k = c + tid;
+        const bool in = k < k1;
+        float vb[B];
+        uint16_t hb[B];  // fp16 bits of kept values (0 otherwise), batch > 1
+        bool any = false;
+        if constexpr (MODE == kModeSwiglu) {
+          float hv = 0.f;
+          any = in && swiglu_keep(p.g[k], p.u[k], p.swiglu_mode != 0 ? p.colnorm[k] : 0.0,
+                                  p.swiglu_mode, p.t64, hv);
+          vb[0] = hv;
         } else {
-          store_handoff(p.slice_cnt + kblk, (int32_t)cnt, LOCAL);
+          // every row's load first, from in-range addresses (k0 < d_in), so
+          // they are in flight together; then the decisions
+          const int64_t kc = in ? k : k0;
+          uint16_t xr[B];
+          uint32_t mw[B];
+          uint16_t ms = 0;  // scored: shift and weight norm
+          double cs = 1.0;
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const int64_t bb = b < p.batch ? b : 0;
+            xr[b] = p.x[bb * p.d_in + kc];
+            if constexpr (MODE == kModeMasked) mw[b] = p.xmask[bb * words + (kc >> 5)];
+          }
+          if constexpr (MODE == kModeScored) {
+            if (p.mu != nullptr) ms = p.mu[kc];
+            if (p.colnorm != nullptr) cs = p.colnorm[kc];
+          }
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            vb[b] = 0.f;
+            hb[b] = 0;
+            if constexpr (MODE == kModeScored) {
+              if (scored_keep(p, xr[b], ms, cs, in && b < p.batch, s_all, s_kept)) {
+                vb[b] = h2f(xr[b]);
+                hb[b] = xr[b];
+                any = true;
+              }
+            } else if (b < p.batch && in) {
+              const uint16_t xb = xr[b];
+              bool kb;
+              if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
+                kb = keep_entry<MODE>(xb, p.t);
+              } else if constexpr (MODE == kModeMasked) {
+                kb = ((mw[b] >> (k & 31)) & 1u) != 0;
+              } else {
+                kb = true;
+              }
+              if (kb) {
+                vb[b] = h2f(xb);
+                hb[b] = xb;
+              }
+              any = any || kb;
+            }
+          }
+          if constexpr (MODE == kModeDense) any = in;
+        }
+        int total;
+        uint64_t wm;
+        const int slot = chunk_slot<NT>(any, wsum, total, wm);
+        if (any) {
+          lk[cnt + slot] = (int)k;
+          if constexpr (kPairs) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) lvh[b * SLH + cnt + slot] = hb[b];
+          } else {
+            lv[cnt + slot] = vb[0];
+          }
+        }
+        if constexpr (MODE == kModeSwiglu) {
+          // each wave covers 64 consecutive entries starting at a multiple of 64
+          if (p.out_mask != nullptr && oblk == 0 && lane_id() == 0) {
+            const int64_t kw = c + (int64_t)(tid / kWave) * kWave;
+            if (kw < k1) {
+              p.out_mask[kw >> 5] = (uint32_t)wm;
+              if (kw + 32 < p.d_in) p.out_mask[(kw >> 5) + 1] = (uint32_t)(wm >> 32);
+            }
+          }
+        }
+        cnt += total;
+      }
+      if constexpr (MODE == kModeSwiglu) {
+        if (oblk == 0 && tid == 0) {
+          if (p.gk == 1) {
+            if (p.out_nnz != nullptr) p.out_nnz[0] = cnt;
+          } else {
+            store_handoff(p.slice_cnt + kb, (int32_t)cnt, LOCAL);
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+    if constexpr (kPairs) {
+      if (tid < B) lvh[tid * SLH + cnt] = 0;  // the pad after the last kept entry
+      __syncthreads();
+    }
+
+    // Scored mode with the variance correction: this slice's sums of x'^2 and
+    // kept x'^2.  One slice is the whole input: alpha now.  Otherwise the sums
+    // go beside this workgroup's partial (written before its ticket, so the
+    // tile's last workgroup reads every slice's sums with the partials).
+    if constexpr (MODE == kModeScored) {
+      if (p.var) {
+        __shared__ double vred[2][NT / kWave];
+#pragma unroll
+        for (int off = kWave / 2; off >= 1; off >>= 1) {
+          s_all += __shfl_xor(s_all, off, kWave);
+          s_kept += __shfl_xor(s_kept, off, kWave);
+        }
+        if (lane_id() == 0) {
+          vred[0][tid / kWave] = s_all;
+          vred[1][tid / kWave] = s_kept;
+        }
+        __syncthreads();
+        if (tid == 0) {
+          double a = 0.0, k = 0.0;
+          for (int i = 0; i < NT / kWave; ++i) {
+            a += vred[0][i];
+            k += vred[1][i];
+          }
+          if (p.gk == 1) {
+            s_alpha = var_alpha(a, k);
+          } else {
+            double* dst = p.vsum + ((int64_t)kb * p.go + oblk) * 2;
+            if (p.tickets != nullptr) {
+              store_handoff(dst, a, LOCAL);
+              store_handoff(dst + 1, k, LOCAL);
+            } else {
+              dst[0] = a;
+              dst[1] = k;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+
+    // ---------------- phase 2: stream the kept rows --------------------------
+    const int o_lane = tid % OL;
+    const int r_lane = tid / OL;
+    const int64_t o = o0 + (int64_t)o_lane * 8;
+    const bool o_ok = o < p.d_out;
+    const uint16_t* __restrict__ wcol = p.wt + (o_ok ? o : 0);
+    const int64_t ld = p.d_out;
+
+    float acc[B][8];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
+
+    if constexpr (!kPairs) {
+      // Rows j = r_lane, r_lane + R, ... in two halves of H rows: one half's
+      // loads stay in flight while the other half is consumed.  Rows are added
+      // in increasing j whatever U is.  Loads are unconditional (a branch per
+      // load would make every wait a full drain): past the end of the list a
+      // thread re-reads the list's last row, a cache hit, and consume() skips it.
+      constexpr int H = U / 2;
+      static_assert(U % 2 == 0, "two halves");
+      auto issue = [&](half8 (&w)[H], int j0) {
+    #pragma unroll
+        for (int q = 0; q < H; ++q) {
+          const int j = j0 + q * R;
+          const int row = lk[j < cnt ? j : cnt - 1];
+          w[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + (int64_t)row * ld));
+        }
+      };
+      auto consume = [&](const half8 (&w)[H], int j0) {
+    #pragma unroll
+        for (int q = 0; q < H; ++q) {
+          const int j = j0 + q * R;
+          if (j < cnt) {
+    #pragma unroll
+            for (int b = 0; b < B; ++b) {
+              const float vv = lv[b * SL + j];
+    #pragma unroll
+              for (int i = 0; i < 8; ++i) acc[b][i] = fmaf((float)w[q][i], vv, acc[b][i]);
+            }
+          }
+        }
+      };
+      if (r_lane < cnt) {
+        half8 wa[H], wb[H];
+        issue(wa, r_lane);
+        issue(wb, r_lane + H * R);
+        for (int j0 = r_lane; j0 < cnt; j0 += U * R) {
+          consume(wa, j0);
+          issue(wa, j0 + U * R);
+          consume(wb, j0 + H * R);
+          issue(wb, j0 + U * R + H * R);
+        }
+      }
+    } else {
+      // Batch > 1: kept entries in pairs (2m, 2m+1), m = r_lane, r_lane + R,
+      // ...; v_dot2_f32_f16 adds both rows' products for one output and batch
+      // row in one instruction (fp32 accumulate), half the VALU work of one
+      // FMA per row.  An odd count pairs its last entry with the zero pad (the
+      // row is read twice, its second value is 0).  Same halves as above.
+      typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+      const int npair = (cnt + 1) >> 1;
+      constexpr int HP = U / 4;  // pairs per half: U rows in flight
+      static_assert(U % 4 == 0, "two halves of pairs");
+      auto issue2 = [&](half8 (&wa)[HP], half8 (&wb)[HP], int m0) {
+#pragma unroll
+        for (int q = 0; q < HP; ++q) {
+          const int m = m0 + q * R;
+          const int mm = m < npair ? m : npair - 1;
+          const int ja = 2 * mm, jb = 2 * mm + 1 < cnt ? 2 * mm + 1 : 2 * mm;
+          wa[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + (int64_t)lk[ja] * ld));
+          wb[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + (int64_t)lk[jb] * ld));
+        }
+      };
+      auto consume2 = [&](const half8 (&wa)[HP], const half8 (&wb)[HP], int m0) {
+#pragma unroll
+        for (int q = 0; q < HP; ++q) {
+          const int m = m0 + q * R;
+          if (m < npair) {
+            h2v wp[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wp[i] = h2v{wa[q][i], wb[q][i]};
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+              const h2v xp = *reinterpret_cast<const h2v*>(lvh + b * SLH + 2 * m);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[b][i] = __builtin_amdgcn_fdot2(wp[i], xp, acc[b][i], false);
+            }
+          }
+        }
+      };
+      if (r_lane < npair) {
+        half8 a0[HP], b0[HP], a1[HP], b1[HP];
+        issue2(a0, b0, r_lane);
+        issue2(a1, b1, r_lane + HP * R);
+        for (int m0 = r_lane; m0 < npair; m0 += 2 * HP * R) {
+          consume2(a0, b0, m0);
+          issue2(a0, b0, m0 + 2 * HP * R);
+          consume2(a1, b1, m0 + HP * R);
+          issue2(a1, b1, m0 + 2 * HP * R + HP * R);
         }
       }
     }
-    __syncthreads();
-  }
 
-  if constexpr (kPairs) {
-    if (tid < B) lvh[tid * SLH + cnt] = 0;  // the pad after the last kept entry
-    __syncthreads();
-  }
-
-  // Scored mode with the variance correction: this slice's sums of x'^2 and
-  // kept x'^2.  One slice is the whole input: alpha now.  Otherwise the sums
-  // go beside this workgroup's partial (written before its ticket, so the
-  // tile's last workgroup reads every slice's sums with the partials).
-  __shared__ float s_alpha;
-  if constexpr (MODE == kModeScored) {
-    if (p.var) {
-      __shared__ double vred[2][NT / kWave];
+    // ---------------- phase 3: reduce row lanes, store the tile --------------
+    __syncthreads();  // the kept list is no longer needed; reuse its LDS
+    float* red = reinterpret_cast<float*>(smem);
+    const bool single = p.gk == 1;
+    const bool handoff = !single && p.tickets != nullptr;
 #pragma unroll
-      for (int off = kWave / 2; off >= 1; off >>= 1) {
-        s_all += __shfl_xor(s_all, off, kWave);
-        s_kept += __shfl_xor(s_kept, off, kWave);
+    for (int b = 0; b < B; ++b) {
+      if (b >= p.batch) break;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[r_lane * TILE_O + o_lane * 8 + i] = acc[b][i];
+      __syncthreads();
+      for (int oo = tid; oo < TILE_O; oo += NT) {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) s += red[r * TILE_O + oo];
+        const int64_t og = o0 + oo;
+        if (og < p.d_out) {
+          float* dst = p.part + ((int64_t)kb * B + b) * p.d_out + og;
+          if (single)
+            p.y[(int64_t)b * p.d_out + og] = finish(s, alpha_out, bias_arg, b, og);
+          else if (handoff)
+            store_handoff(dst, s, LOCAL);
+          else
+            *dst = s;
+        }
       }
-      if (lane_id() == 0) {
-        vred[0][tid / kWave] = s_all;
-        vred[1][tid / kWave] = s_kept;
-      }
+      __syncthreads();
+    }
+    if (!handoff) return;
+
+    // ---------------- phase 4: one-launch hand-off ---------------------------
+    if (!recompute) {
+      wait_stores();
       __syncthreads();
       if (tid == 0) {
-        double a = 0.0, k = 0.0;
-        for (int i = 0; i < NT / kWave; ++i) {
-          a += vred[0][i];
-          k += vred[1][i];
-        }
-        if (p.gk == 1) {
-          s_alpha = var_alpha(a, k);
+        if constexpr (LOCAL) {
+          // fields: arrivals [5:0], sum x [15:6], sum x^2 [31:16]; every one
+          // stays in its field up to the last arrival (gk <= kLocalMaxGk)
+          const uint32_t x = xcd_id() ^ ((p.xcd_skew != 0 && kblk == 0) ? 1u : 0u);
+          const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u | (x << 6) | ((x * x) << 16),
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint32_t gk = (uint32_t)p.gk;
+          const uint32_t sx = ((prev >> 6) & 1023u) + x;
+          const uint32_t sxx = (prev >> 16) + x * x;
+          s_last = ((prev & 63u) != gk - 1) ? 0 : (sx == gk * x && sxx == gk * x * x) ? 1 : 2;
         } else {
-          double* dst = p.vsum + ((int64_t)kblk * p.go + oblk) * 2;
-          if (p.tickets != nullptr) {
-            store_handoff(dst, a, LOCAL);
-            store_handoff(dst + 1, k, LOCAL);
-          } else {
-            dst[0] = a;
-            dst[1] = k;
-          }
+          const unsigned prev =
+              __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_last = (prev == (unsigned)(p.gk - 1)) ? 1 : 0;
         }
       }
       __syncthreads();
+      if (s_last == 0) return;
+      if (s_last == 1) break;
+      // The tile's slices ran on more than one XCD (possible only in the L2
+      // form): the other XCDs' partials sit in their own L2s, out of reach.
+      // Recompute every other slice here instead, storing each partial into
+      // this XCD's L2 exactly as its own workgroup would have: a partial is a
+      // fixed function of the inputs, so the sum below comes out bit for bit
+      // as it would have.  Slow, and never taken under round-robin dispatch.
+      recompute = true;
+      kb = -1;
     }
-  }
-  const float* alpha_out = (MODE == kModeScored && p.var) ? &s_alpha : alpha_arg;
-
-  // ---------------- phase 2: stream the kept rows --------------------------
-  const int o_lane = tid % OL;
-  const int r_lane = tid / OL;
-  const int64_t o0 = (int64_t)oblk * TILE_O;
-  const int64_t o = o0 + (int64_t)o_lane * 8;
-  const bool o_ok = o < p.d_out;
-  const uint16_t* __restrict__ wcol = p.wt + (o_ok ? o : 0);
-  const int64_t ld = p.d_out;
-
-  float acc[B][8];
-#pragma unroll
-  for (int b = 0; b < B; ++b)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
-
-  if constexpr (!kPairs) {
-    // Rows j = r_lane, r_lane + R, ... in two halves of H rows: one half's
-    // loads stay in flight while the other half is consumed.  Rows are added
-    // in increasing j whatever U is.  Loads are unconditional (a branch per
-    // load would make every wait a full drain): past the end of the list a
-    // thread re-reads the list's last row, a cache hit, and consume() skips it.
-    constexpr int H = U / 2;
-    static_assert(U % 2 == 0, "two halves");
-    auto issue = [&](half8 (&w)[H], int j0) {
-  #pragma unroll
-      for (int q = 0; q < H; ++q) {
-        const int j = j0 + q * R;
-        const int row = lk[j < cnt ? j : cnt - 1];
-        w[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + (int64_t)row * ld));
-      }
-    };
-    auto consume = [&](const half8 (&w)[H], int j0) {
-  #pragma unroll
-      for (int q = 0; q < H; ++q) {
-        const int j = j0 + q * R;
-        if (j < cnt) {
-  #pragma unroll
-          for (int b = 0; b < B; ++b) {
-            const float vv = lv[b * SL + j];
-  #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[b][i] = fmaf((float)w[q][i], vv, acc[b][i]);
-          }
-        }
-      }
-    };
-    if (r_lane < cnt) {
-      half8 wa[H], wb[H];
-      issue(wa, r_lane);
-      issue(wb, r_lane + H * R);
-      for (int j0 = r_lane; j0 < cnt; j0 += U * R) {
-        consume(wa, j0);
-        issue(wa, j0 + U * R);
-        consume(wb, j0 + H * R);
-        issue(wb, j0 + U * R + H * R);
-      }
-    }
-  } else {
-    // Batch > 1: kept entries in pairs (2m, 2m+1), m = r_lane, r_lane + R,
-    // ...; v_dot2_f32_f16 adds both rows' products for one output and batch
-    // row in one instruction (fp32 accumulate), half the VALU work of one
-    // FMA per row.  An odd count pairs its last entry with the zero pad (the
-    // row is read twice, its second value is 0).  Same halves as above.
-    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
-    const int npair = (cnt + 1) >> 1;
-    constexpr int HP = U / 4;  // pairs per half: U rows in flight
-    static_assert(U % 4 == 0, "two halves of pairs");
-    auto issue2 = [&](half8 (&wa)[HP], half8 (&wb)[HP], int m0) {
-#pragma unroll
-      for (int q = 0; q < HP; ++q) {
-        const int m = m0 + q * R;
-        const int mm = m < npair ? m : npair - 1;
-        const int ja = 2 * mm, jb = 2 * mm + 1 < cnt ? 2 * mm + 1 : 2 * mm;
-        wa[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + (int64_t)lk[ja] * ld));
-        wb[q] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(wcol + (int64_t)lk[jb] * ld));
-      }
-    };
-    auto consume2 = [&](const half8 (&wa)[HP], const half8 (&wb)[HP], int m0) {
-#pragma unroll
-      for (int q = 0; q < HP; ++q) {
-        const int m = m0 + q * R;
-        if (m < npair) {
-          h2v wp[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) wp[i] = h2v{wa[q][i], wb[q][i]};
-#pragma unroll
-          for (int b = 0; b < B; ++b) {
-            const h2v xp = *reinterpret_cast<const h2v*>(lvh + b * SLH + 2 * m);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[b][i] = __builtin_amdgcn_fdot2(wp[i], xp, acc[b][i], false);
-          }
-        }
-      }
-    };
-    if (r_lane < npair) {
-      half8 a0[HP], b0[HP], a1[HP], b1[HP];
-      issue2(a0, b0, r_lane);
-      issue2(a1, b1, r_lane + HP * R);
-      for (int m0 = r_lane; m0 < npair; m0 += 2 * HP * R) {
-        consume2(a0, b0, m0);
-        issue2(a0, b0, m0 + 2 * HP * R);
-        consume2(a1, b1, m0 + HP * R);
-        issue2(a1, b1, m0 + 2 * HP * R + HP * R);
-      }
-    }
-  }
-
-  // ---------------- phase 3: reduce row lanes, store the tile --------------
-  __syncthreads();  // the kept list is no longer needed; reuse its LDS
-  float* red = reinterpret_cast<float*>(smem);
-  const bool single = p.gk == 1;
-  const bool handoff = !single && p.tickets != nullptr;
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    if (b >= p.batch) break;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) red[r_lane * TILE_O + o_lane * 8 + i] = acc[b][i];
+    kb = kb + 1 == kblk ? kb + 2 : kb + 1;
+    if (kb >= p.gk) break;
     __syncthreads();
-    for (int oo = tid; oo < TILE_O; oo += NT) {
-      float s = 0.f;
-#pragma unroll
-      for (int r = 0; r < R; ++r) s += red[r * TILE_O + oo];
-      const int64_t og = o0 + oo;
-      if (og < p.d_out) {
-        float* dst = p.part + ((int64_t)kblk * B + b) * p.d_out + og;
-        if (single)
-          p.y[(int64_t)b * p.d_out + og] = finish(s, alpha_out, bias_arg, b, og);
-        else if (handoff)
-          store_handoff(dst, s, LOCAL);
-        else
-          *dst = s;
-      }
-    }
+  }  // one pass per slice
+  if (recompute) {  // the recomputed partials, visible to every wave of this workgroup
+    wait_stores();
     __syncthreads();
-  }
-  if (!handoff) return;
-
-  // ---------------- phase 4: one-launch hand-off ---------------------------
-  __shared__ int s_last;
-  wait_stores();
-  __syncthreads();
-  uint32_t* ticket = p.tickets + (int64_t)oblk * kTicketStride;
-  if (tid == 0) {
-    if constexpr (LOCAL) {
-      // fields: arrivals [5:0], sum x [15:6], sum x^2 [31:16]; every one
-      // stays in its field up to the last arrival (gk <= kLocalMaxGk)
-      const uint32_t x = xcd_id() ^ ((p.xcd_skew != 0 && kblk == 0) ? 1u : 0u);
-      const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u | (x << 6) | ((x * x) << 16),
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t gk = (uint32_t)p.gk;
-      const uint32_t sx = ((prev >> 6) & 1023u) + x;
-      const uint32_t sxx = (prev >> 16) + x * x;
-      s_last = ((prev & 63u) != gk - 1) ? 0 : (sx == gk * x && sxx == gk * x * x) ? 1 : 2;
-    } else {
-      const unsigned prev =
-          __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (prev == (unsigned)(p.gk - 1)) ? 1 : 0;
-    }
-  }
-  __syncthreads();
-  if (s_last == 0) return;
-  if (LOCAL && s_last == 2) {
-    // the tile's slices ran on more than one XCD: its partials are not all
-    // visible here; NaN marks the tile instead of a wrong sum
-    for (int oo = tid; oo < TILE_O; oo += NT)
-      for (int b = 0; b < p.batch; ++b)
-        if (o0 + oo < p.d_out) p.y[(int64_t)b * p.d_out + o0 + oo] = (uint16_t)0x7e00u;
-    if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return;
   }
   if constexpr (MODE == kModeScored) {
     if (p.var) {
@@ -1619,6 +1636,13 @@ hipError_t dispatch_fk(const KParams& kp, int tiling, unsigned grid, hipStream_t
 
 size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
   return ws_layout(d_out, d_in, batch).total;
+}
+
+size_t gemv_workspace_zero_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
+  (void)d_out;
+  (void)d_in;
+  (void)batch;
+  return kTicketBytes;  // the hand-off counters; the rest is written before it is read
 }
 
 namespace {

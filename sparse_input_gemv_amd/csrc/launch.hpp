@@ -79,6 +79,9 @@ constexpr int kMinSplitTileO = 64;
 constexpr size_t kGemvTicketBytes = (size_t)(524288 / kMinSplitTileO) * kTicketStride * 4;
 
 size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch);
+// Leading bytes of that workspace that must be zero before a call (and are
+// zero after it): the hand-off counters, the status word and the slots.
+size_t gemv_workspace_zero_bytes(int64_t d_out, int64_t d_in, int64_t batch);
 // Returns hipErrorInvalidValue if the workspace is too small for the launch
 // (checked by abi.cpp beforehand, so this is a second line of defence).
 hipError_t launch_gemv(const GemvCall& c, hipStream_t s);

@@ -39,8 +39,10 @@ def test_every_declared_symbol_is_exported(sa):
     assert len(names) >= 18
     for n in names:
         assert hasattr(sa, n), n
+    # the hot path's six calls and its workspace query, by the contract's names
     for n in ("act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm", "sparse_gemv",
-              "masked_swiglu_down", "nm_act_spmm", "act_calibrate_threshold"):
+              "masked_swiglu_down", "nm_act_spmm", "sparse_gemv_workspace_bytes",
+              "act_calibrate_threshold", "sa_workspace_zero_bytes"):
         assert n in names
 
 
@@ -143,6 +145,11 @@ def test_workspace_size(sa):
     assert sa.sa_workspace_bytes(0, 10, 1) == 0
     # the zero-once hand-off counters lead every workspace
     assert sa.sa_workspace_bytes(8, 1, 1) > 1 << 20
+    # the contract's name is the same function
+    for shape in ((4096, 11008, 1), (4096, 11008, 8), (22016, 4096, 2), (8, 1, 1), (0, 10, 1)):
+        assert sa.sparse_gemv_workspace_bytes(*shape) == sa.sa_workspace_bytes(*shape)
+    assert sa.sa_workspace_zero_bytes(4096, 11008, 1) == 1 << 20
+    assert sa.sa_workspace_zero_bytes(4096, 11008, 1) < sa.sa_workspace_bytes(4096, 11008, 1)
 
 
 def test_gemv_checks(sa):

@@ -26,7 +26,7 @@ def dev(a):
 
 
 def host(t):
-    return t.detach().cpu().numpy()
+    return t if isinstance(t, np.ndarray) else t.detach().cpu().numpy()
 
 
 def words(t):
@@ -429,15 +429,18 @@ def test_masked_swiglu_t0_dense():
     assert_close(y, y_ref)
 
 
-@pytest.mark.parametrize("handoff", [1, 2, 3])
-def test_split_k_handoff_is_deterministic(handoff):
+@pytest.mark.parametrize("handoff,skew", [(1, 0), (2, 0), (3, 0), (3, 1)])
+def test_split_k_handoff_is_deterministic(handoff, skew):
     """Many back-to-back split-K calls on rotating weights: every result must
-    equal the first one bit for bit (the cross-workgroup hand-off is exact)."""
+    equal the first one bit for bit (the cross-workgroup hand-off is exact),
+    also when the L2 form's placement check is made to fail (the last
+    workgroup of each tile then recomputes the other slices)."""
     d_out, d_in, _ = syn.LLAMA2_7B["down"]
     wt0 = syn.weight_t(d_out, d_in, 15)
     x = dev(syn.laplace_f16((d_in,), 1.0, 16))
     wts = [dev(wt0), dev(np.ascontiguousarray(wt0[::-1]))]
     try:
+        sa.set_gemv_test_hooks(skew)
         for tiling, target in [(-1, 0), (0, 4096), (6, 1024), (2, 2048), (8, 0), (10, 0)]:
             sa.set_gemv_tuning(tiling, target, handoff)
             ref = [sa.sparse_gemv_threshold(w, x, 0.69).clone() for w in wts]
@@ -446,6 +449,7 @@ def test_split_k_handoff_is_deterministic(handoff):
             for i, y in enumerate(outs):
                 assert torch.equal(y, ref[i % 2]), (tiling, target, i)
     finally:
+        sa.set_gemv_test_hooks(0)
         sa.set_gemv_tuning(-1, 0, 0)
 
 
@@ -482,17 +486,19 @@ def test_one_launch_handoff_matches_two_launches(tiling):
                      sa.act_sparsify_threshold(xb, 0.7), swiglu_in))
     try:
         res = {}
-        for handoff in (1, 2, 3):
+        for handoff, skew in ((1, 0), (2, 0), (3, 0), (3, 1)):
+            sa.set_gemv_test_hooks(skew)
             for k, (target, wt, x1, xb, l1, lb, sw) in enumerate(data):
                 sa.set_gemv_tuning(tiling, target, handoff)
-                res[handoff, k] = [o.clone() for o in _every_gemv_entry(wt, x1, xb, l1, lb, sw,
-                                                                        0.7)]
+                res[(handoff, skew), k] = [o.clone() for o in _every_gemv_entry(
+                    wt, x1, xb, l1, lb, sw, 0.7)]
         torch.cuda.synchronize()
         for k in range(len(data)):
-            for h in (2, 3):
-                for j, (a, b) in enumerate(zip(res[1, k], res[h, k])):
+            for h in ((2, 0), (3, 0), (3, 1)):
+                for j, (a, b) in enumerate(zip(res[(1, 0), k], res[h, k])):
                     assert torch.equal(a, b), (tiling, shapes[k], h, j)
     finally:
+        sa.set_gemv_test_hooks(0)
         sa.set_gemv_tuning(-1, 0, 0)
 
 
@@ -598,16 +604,83 @@ def test_scored_fused(d_out, d_in, shifted, weighted, var, biased):
 # RaNA linear-layer rank adapter A (m ⊙ B x), m_i = v_i^2 >= t
 # ---------------------------------------------------------------------------
 
+def oracle_v16(bt, X):
+    """The oracle's fp16 v = B x, one row per token (fp64 sums, rounded once)."""
+    return np.stack([rana.adapter_v(bt, X[b]).astype(np.float16) for b in range(len(X))])
+
+
+def fp16_order(a):
+    """fp16 values as integers in their numeric order, adjacent values one
+    apart (+0 and -0 both 0)."""
+    b = np.asarray(a, dtype=np.float16).view(np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def gap_threshold(v16, rate):
+    """A threshold between two adjacent squares of the oracle's |v| such that
+    a value one fp16 ulp away from any oracle v stays on the same side: an
+    implementation whose v is within one ulp of the oracle's (fp32 instead of
+    fp64 sums, rounded to fp16) then takes exactly the oracle's decisions.
+    Searched outward from the split that masks `rate` of the entries; rate 0
+    gives t = 0 (keep all), rate 1 a t above every reachable square."""
+    a = np.sort(np.abs(np.asarray(v16, dtype=np.float16).ravel()))
+    if rate <= 0.0:
+        return 0.0
+    up = np.nextafter(a, np.float16(np.inf)).astype(np.float64)
+    if rate >= 1.0:
+        return float(np.float32(4.0 * up[-1] ** 2 + 1.0))
+    dn = np.nextafter(a, np.float16(0)).astype(np.float64)
+    k0 = int(rate * len(a))
+    for k in sorted(range(1, len(a)), key=lambda k: (abs(k - k0), k)):
+        lo, hi = up[k - 1] ** 2, dn[k] ** 2
+        t = float(np.float32(0.5 * (lo + hi)))
+        if lo < t < hi:
+            return t
+    raise AssertionError("no gap between the oracle's squares")
+
+
+def gpu_adapter_mask(bt, X, t):
+    """The mask the kernel applies, read out exactly: with A = I the second
+    GEMV returns m ⊙ v with every kept entry unchanged (one product by 1.0)
+    and every dropped entry 0, so the kept set is where y is nonzero (t > 0:
+    a kept entry has v^2 >= t > 0)."""
+    r = bt.shape[1]
+    eye = np.eye(r, dtype=np.float16)
+    v_g, y_g = sa.rana_adapter_gemv(dev(bt), dev(eye), dev(X), t)
+    v, y = host(v_g).reshape(len(X), r), host(y_g).reshape(len(X), r)
+    keep = y != 0
+    assert np.array_equal(y[keep].view(np.uint16), v[keep].view(np.uint16))
+    return keep, v
+
+
 def check_adapter(bt, at, X, t, v_g, y_g):
-    """v against the oracle's fp64 B x; y against the oracle run on the
-    GPU's own fp16 v, so both sides take the mask decision on the same
-    values (its square is exact)."""
-    v_g, y_g = v_g.reshape(len(X), -1), y_g.reshape(len(X), -1)
+    """The whole chain against the oracle's own: its fp16 v (the GPU's within
+    one ulp, so t in a gap of the oracle's squares decides alike), its mask
+    (the kernel's mask, read out through A = I, bit for bit) and its y over
+    the kept columns of A (within tolerance).  No GPU value enters the
+    oracle."""
+    v_g, y_g = host(v_g).reshape(len(X), -1), host(y_g).reshape(len(X), -1)
+    v16 = oracle_v16(bt, X)
+    keep_ref = v16.astype(np.float64) ** 2 >= t
+    # fp32 sums against fp64 sums, each rounded once to fp16: at most one ulp
+    # apart wherever |v| is well above the sums' absolute error (near zero
+    # the fp32 error can span several of the tiny ulps there); every split
+    # gap_threshold picks lies far above that
+    big = np.abs(v16.astype(np.float64)) >= 2.0 ** -4
+    assert np.all(np.abs(fp16_order(v_g) - fp16_order(v16))[big] <= 1)
+    assert t == 0.0 or np.sqrt(t) >= 2.0 ** -3
+    if t > 0:
+        keep_g, v_probe = gpu_adapter_mask(bt, X, t)
+        assert np.array_equal(v_probe.view(np.uint16), v_g.view(np.uint16))
+        assert np.array_equal(keep_g, keep_ref)
     for b in range(len(X)):
-        assert_close(v_g[b], rana.adapter_v(bt, X[b]))
-        _, _, keep, y_ref = rana.rank_adapter(bt, at, X[b], t, v16=host(v_g[b]))
+        v, v16b, keep, y_ref = rana.rank_adapter(bt, at, X[b], t)
+        assert np.array_equal(v16b.view(np.uint16), v16[b].view(np.uint16))
+        assert np.array_equal(keep, keep_ref[b])
+        assert_close(v_g[b], v)
         assert_close(y_g[b], y_ref)
-    return keep
+    return keep_ref
 
 
 @pytest.mark.parametrize("batch", [1, 2, 3])
@@ -615,7 +688,9 @@ def check_adapter(bt, at, X, t, v_g, y_g):
 def test_rana_adapter_small(r, d_in, d_out, batch):
     bt, at = syn.rank_adapter_weights(d_out, d_in, r, r + d_in, std=0.1)
     X = syn.gaussian_f16((batch, d_in), 1.0, batch + d_out)
-    for t in (0.0, 0.5, 4.0, 1e6):
+    v16 = oracle_v16(bt, X)
+    for rate in (0.0, 0.3, 0.5, 0.8, 1.0):
+        t = gap_threshold(v16, rate)
         v_g, y_g = sa.rana_adapter_gemv(dev(bt), dev(at), dev(X), t)
         check_adapter(bt, at, X, t, v_g, y_g)
 
@@ -631,21 +706,18 @@ def test_rana_adapter_exact_square_threshold():
     assert np.array_equal(host(y_g), np.where(x.astype(np.float64) ** 2 >= 0.25, x, 0))
 
 
-def test_rana_adapter_llama_gate():
-    """The gate projection (11008 x 4096) as a rank-2048 adapter at a 50%
-    mask rate (t between the middle order statistics of v^2), batch 1."""
+@pytest.mark.parametrize("rate", [0.5, 0.7])
+def test_rana_adapter_llama_gate(rate):
+    """The gate projection (11008 x 4096) as a rank-2048 adapter at 50% and
+    70% mask rates, batch 1: t from the oracle's own squares (a gap near the
+    rate), the kernel's mask equal to the oracle's, y against the oracle's
+    end-to-end chain."""
     bt, at = syn.rank_adapter_weights(11008, 4096, 2048, 3000)
-    x = syn.activation((4096,), "gaussian", 7)
-    v0, _ = sa.rana_adapter_gemv(dev(bt), dev(at), dev(x), 0.0)
-    sq = np.sort(host(v0).astype(np.float64) ** 2)
-    # the nearest split at or above the median between two distinct squares
-    k = next(i for i in range(1024, 2048) if sq[i - 1] < sq[i])
-    t = float(np.float32(0.5 * (sq[k - 1] + sq[k])))
-    assert sq[k - 1] < t < sq[k]
+    x = syn.activation((4096,), "gaussian", 7)[None]
+    t = gap_threshold(oracle_v16(bt, x), rate)
     v_g, y_g = sa.rana_adapter_gemv(dev(bt), dev(at), dev(x), t)
-    assert np.array_equal(host(v_g), host(v0))  # the first GEMV is deterministic
-    keep = check_adapter(bt, at, x[None], t, v_g, y_g)
-    assert int(keep.sum()) == 2048 - k
+    keep = check_adapter(bt, at, x, t, v_g, y_g)
+    assert abs(int(keep.sum()) - round((1 - rate) * 2048)) <= 64
 
 
 # ---------------------------------------------------------------------------
@@ -788,20 +860,21 @@ def test_nm_spmm_two_pass_matches_single_pass(T, d_in, d_out, n, m):
 
 @pytest.mark.parametrize("T,d_in,d_out", [(4096, 1024, 1024), (2048, 4096, 11008)])
 @pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (16, 32)])
-def test_nm_spmm_full_shapes_sampled(T, d_in, d_out, n, m):
+def test_nm_spmm_full_shapes(T, d_in, d_out, n, m):
+    """The benchmarked launches at full size: every mask row bit-exact and
+    every output row (so every row and column tile of the matmul's grid)
+    against the oracle's fp64 masked matmul; the dense GEMM likewise."""
     X = syn.gaussian_f16((T, d_in), 1.0, 5)
     wt = syn.weight_t(d_out, d_in, 41)
     X_g, wt_g = dev(X), dev(wt)
     mask_g, val_g = sa.act_sparsify_nm(X_g, n, m)
     Y = sa.nm_act_spmm(val_g, mask_g, n, m, wt_g)
     Yd = sa.dense_gemm(X_g, wt_g)
-    rows = np.random.default_rng(T).choice(T, size=6, replace=False)
-    rows = np.concatenate([rows, [0, T - 1]])
-    keep = sparsify.nm_sparsify(X[rows], n, m)[0]
-    assert np.array_equal(sparsify.unpack_mask(words(mask_g)[rows], d_in), keep)
-    ref = spmm.nm_spmm(X[rows], keep, wt)
-    assert_close(Y[torch.from_numpy(rows).to(DEV)], ref)
-    assert_close(Yd[torch.from_numpy(rows).to(DEV)], X[rows].astype(np.float64) @ wt.astype(np.float64))
+    keep, vals = sparsify.nm_sparsify(X, n, m)
+    assert np.array_equal(words(mask_g), sparsify.pack_mask(keep))
+    assert np.array_equal(host(val_g).view(np.uint16), vals.view(np.uint16))
+    assert_close(Y, spmm.masked_matmul(X, keep, wt))
+    assert_close(Yd, spmm.masked_matmul(X, np.ones(X.shape, dtype=bool), wt))
 
 
 # ---------------------------------------------------------------------------
@@ -957,23 +1030,19 @@ def test_nm_shared_whole_tile_stages_agree(stages):
 @pytest.mark.parametrize("T,d_in,d_out", [(4096, 1024, 1024), (2048, 4096, 11008)])
 @pytest.mark.parametrize("n,m,tt", [(2, 4, 32), (8, 16, 32), (16, 32, 32), (4, 16, 32),
                                     (8, 16, 128), (4, 16, 128), (8, 16, 256), (2, 4, 256)])
-def test_nm_shared_full_shapes_sampled(T, d_in, d_out, n, m, tt):
-    """Full sizes in the benchmarked launches: the masks of sampled tiles
-    bit-exact, sampled rows against the oracle."""
+def test_nm_shared_full_shapes(T, d_in, d_out, n, m, tt):
+    """Full sizes in the benchmarked launches: every tile's mask and every
+    row's values bit-exact, every output row against the oracle's fp64
+    masked matmul with each tile's mask applied to its tokens."""
     X = syn.gaussian_f16((T, d_in), 1.0, 5)
     wt = syn.weight_t(d_out, d_in, 41)
     X_g, wt_g = dev(X), dev(wt)
     mask_g, val_g = sa.act_sparsify_nm_shared(X_g, n, m, tt)
     Y = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, wt_g)
-    rows = np.random.default_rng(T + n + tt).choice(T, size=6, replace=False)
-    rows = np.concatenate([rows, [0, T - 1]])
-    mw = words(mask_g)
-    for r in rows:
-        g = int(r) // tt
-        _, tile_keep, vals = sparsify.nm_shared_sparsify(X[g * tt:(g + 1) * tt], n, m, tt)
-        assert np.array_equal(mw[g], sparsify.pack_mask(tile_keep)[0])
-        ref = spmm.nm_shared_spmm(vals[int(r) - g * tt][None], tile_keep, tt, wt)
-        assert_close(Y[int(r)][None], ref)
+    keep, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+    assert np.array_equal(words(mask_g), sparsify.pack_mask(tile_keep))
+    assert np.array_equal(host(val_g).view(np.uint16), vals.view(np.uint16))
+    assert_close(Y, spmm.masked_matmul(X, keep, wt))
 
 
 # ---------------------------------------------------------------------------
@@ -1004,38 +1073,96 @@ def test_plan_query_matches_the_device():
         assert here == fixed, (op, d_out, d_in, b, here, fixed)
 
 
-def test_l2_handoff_placement_check_fallback():
+def _zero_region_is_zero(shapes):
+    """The workspace's leading region (the hand-off counters) is all zero, as
+    every call must leave it, for each (d_out, d_in, batch)."""
+    torch.cuda.synchronize()
+    ws = sa.workspace(DEV, 0)
+    for d_out, d_in, b in shapes:
+        nz = sa.workspace_zero_bytes(d_out, d_in, b)
+        assert int(torch.count_nonzero(ws[:nz]).cpu()) == 0, (d_out, d_in, b)
+
+
+def test_l2_handoff_recomputes_mixed_tiles():
     """The L2-local hand-off checks that every slice of a tile ran on one
     XCD.  With the placement reported wrong on purpose (host-set hook; every
-    kernel still exits normally) each tile comes out NaN instead of a sum of
-    partials the last workgroup cannot see, and its counter is reset: the
-    next calls are exact again."""
+    kernel still exits normally) the last workgroup of each tile recomputes
+    the other slices' partials itself: every one-launch entry point gives
+    its normal bits, and the counters come back to zero."""
     d_out, d_in, _ = syn.LLAMA2_7B["down"]
     wt = syn.weight_t(d_out, d_in, 21)
     x = syn.laplace_f16((d_in,), 1.0, 22)
     t = 0.69
     keep = sparsify.threshold_sparsify(x, t)[0]
-    y_ref = gemv.masked_gemv(wt, x, keep)
     wt_g, x_g = dev(wt), dev(x)
-    assert sa.gemv_plan("threshold", d_out, d_in)["handoff"] == 3
-    assert sa.gemv_plan("dense", d_out, d_in)["handoff"] == 3
-    y0 = sa.sparse_gemv_threshold(wt_g, x_g, t).clone()
+    xb = dev(syn.laplace_f16((2, d_in), 1.0, 23))
+    g, u = (dev(a) for a in syn.swiglu_gate_up(d_in, d_out, 24))
+    cn = sa.weight_col_norms(wt_g)
+    mu = dev(syn.gaussian_f16((d_in,), 0.25, 25))
+    _, i1, v1, n1 = sa.act_sparsify_threshold(x_g, t)
+    for op in ("threshold", "dense", "list"):
+        assert sa.gemv_plan(op, d_out, d_in)["handoff"] == 3
+    assert sa.gemv_plan("threshold", d_out, d_in, 2)["handoff"] == 3
+
+    def run():
+        return [sa.sparse_gemv_threshold(wt_g, x_g, t), sa.dense_gemv(wt_g, x_g),
+                sa.sparse_gemv_threshold(wt_g, xb, t), sa.sparse_gemv(wt_g, i1, v1, n1),
+                *sa.masked_swiglu_down(g, u, wt_g, 0.02, "rana", cn),
+                *sa.masked_swiglu_down(g, u, wt_g, 0.02, "cats"),
+                sa.sparse_gemv_scored(wt_g, x_g, 0.7, mu=mu, colnorm=cn, var=True)]
+
+    ref = [o.clone() for o in run()]
     try:
         sa.set_gemv_test_hooks(1)
         for _ in range(3):
-            assert torch.isnan(sa.sparse_gemv_threshold(wt_g, x_g, t).float()).all()
-            assert torch.isnan(sa.dense_gemv(wt_g, x_g).float()).all()
-        # the hook only concerns the L2 form: written-through hand-offs are exact
-        sa.set_gemv_tuning(-1, 0, 2)
-        assert torch.equal(sa.sparse_gemv_threshold(wt_g, x_g, t), y0)
+            for j, (a, b) in enumerate(zip(run(), ref)):
+                assert torch.equal(a, b), j
     finally:
         sa.set_gemv_test_hooks(0)
-        sa.set_gemv_tuning(-1, 0, 0)
+    for _ in range(2):
+        for j, (a, b) in enumerate(zip(run(), ref)):
+            assert torch.equal(a, b), j
+    _zero_region_is_zero([(d_out, d_in, 1), (d_out, d_in, 2)])
+    assert_close(ref[0], gemv.masked_gemv(wt, x, keep))
+    assert_close(ref[1], gemv.dense_gemv(wt, x))
+
+
+def test_workspace_growth_keeps_graphs_valid():
+    """A graph captured with the GEMV workspace at one size keeps replaying
+    correctly after a larger eager call has grown the workspace (the old
+    buffer stays allocated and zero); growing during a capture is refused;
+    the matmul scratch does not touch the GEMV workspace."""
+    small = dev(syn.weight_t(1024, 2048, 51))
+    xs = dev(syn.laplace_f16((2048,), 1.0, 52))
+    big = dev(syn.weight_t(8192, 16384, 53))
+    xl = dev(syn.laplace_f16((16384,), 1.0, 54))
+    sa.sparse_gemv_threshold(small, xs, 0.7)
+    eager = sa.sparse_gemv_threshold(small, xs, 0.7).clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = sa.sparse_gemv_threshold(small, xs, 0.7)
+    before = sa.workspace(DEV, 0)
+    sa.workspace(DEV, before.numel() + 1)  # an eager call of a larger shape grows it like this
+    y_big = sa.sparse_gemv_threshold(big, xl, 0.7)
+    X = dev(syn.gaussian_f16((256, 1024), 1.0, 55))
+    W = dev(syn.weight_t(512, 1024, 56))
+    xm, xv = sa.act_sparsify_nm(X, 8, 16)
+    sa.nm_act_spmm(xv, xm, 8, 16, W)  # scratch of its own
+    torch.cuda.synchronize()
+    assert sa.workspace(DEV, 0).data_ptr() != before.data_ptr()
     for _ in range(3):
-        y = sa.sparse_gemv_threshold(wt_g, x_g, t)
-        assert torch.equal(y, y0)
-    assert_close(y, y_ref)
-    assert_close(sa.dense_gemv(wt_g, x_g), gemv.dense_gemv(wt, x))
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        assert torch.equal(sa.sparse_gemv_threshold(big, xl, 0.7), y_big)
+    need = sa.workspace(DEV, 0).numel() + 1
+    g2 = torch.cuda.CUDAGraph()
+    with pytest.raises(RuntimeError):
+        with torch.cuda.graph(g2):
+            sa.workspace(DEV, need)
+    _zero_region_is_zero([(1024, 2048, 1), (8192, 16384, 1)])
 
 
 def test_graph_replays_match_eager():
