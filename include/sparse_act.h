@@ -240,6 +240,26 @@ int sparse_gemv_threshold(const uint16_t* wt, int64_t d_out, int64_t d_in,
                           uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sparse_gemv_threshold_noalloc -- sparse_gemv_threshold without a
+ * workspace, for callers that cannot allocate device memory around the call
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments (minus ws), same kernels, same result bit for
+ * bit.  Its scratch is a fixed array of SA_NOALLOC_SCRATCH_BYTES in device
+ * memory, one copy per GPU the library runs on, held until the process
+ * ends; the call itself allocates nothing.  Shapes whose
+ * sparse_gemv_workspace_bytes(d_out, d_in, batch) exceeds that size return
+ * SA_ERR_UNSUPPORTED before any launch (the Llama-2-7B projections fit at
+ * batch 1: 4096 x 11008 and 4096 x 4096 also at batch 2, 11008 x 4096 at
+ * batch 1 only).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race; order
+ * them on one stream.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int sparse_gemv_threshold_noalloc(const uint16_t* wt, int64_t d_out, int64_t d_in,
+                                  const uint16_t* x, int64_t batch, float t, uint16_t* y,
+                                  void* stream);
+
+/*
  * sparse_gemv_corrected -- sparse_gemv with an output correction:
  * y[b][o] = fp16(alpha[b] * sum_j W[o][idx[b][j]] * val[b][j] + bias[o]),
  * one fp32 fused multiply-add.  alpha (fp32 [batch], e.g. the variance

@@ -26,7 +26,8 @@ __all__ = [
     "SparseActError", "lib", "workspace",
     "act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm", "act_sparsify_nm_shared",
     "act_sparsify_scored", "sparse_gemv_corrected", "sparse_gemv_scored",
-    "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold", "rana_adapter_gemv",
+    "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold",
+    "sparse_gemv_threshold_noalloc", "rana_adapter_gemv",
     "masked_gemv",
     "dense_gemv", "masked_swiglu_down", "weight_col_norms", "nm_act_spmm", "nm_shared_spmm",
     "dense_gemm",
@@ -54,6 +55,7 @@ _SIGNATURES = {
     "sa_workspace_zero_bytes": (_sz, [_i64, _i64, _i64]),
     "sparse_gemv": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "sparse_gemv_threshold": (_i32, [_vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _sz, _vp]),
+    "sparse_gemv_threshold_noalloc": (_i32, [_vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp]),
     "act_sparsify_scored": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _f64, _vp, _vp, _vp,
                                    _vp, _i64, _vp, _vp]),
     "sparse_gemv_scored": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _f64, _i32, _vp, _vp, _vp, _sz,
@@ -337,6 +339,23 @@ def sparse_gemv_threshold(wt: torch.Tensor, x: torch.Tensor, t: float,
     _check(lib().sparse_gemv_threshold(_ptr(wt), d_out, d_in, _ptr(x), batch, float(t), _ptr(y),
                                        _ptr(ws), ws.numel(), _stream(wt)), "sparse_gemv_threshold")
     return _ret(y, squeeze)
+
+
+def sparse_gemv_threshold_noalloc(wt: torch.Tensor, x: torch.Tensor, t: float,
+                                  y: torch.Tensor):
+    """``sparse_gemv_threshold`` on the library's fixed per-GPU scratch: the
+    call allocates nothing (``y`` is the caller's).  Calls on one GPU share
+    that scratch and must be ordered on one stream."""
+    _dev(wt, "wt", torch.float16)
+    _dev(x, "x", torch.float16)
+    squeeze = x.dim() == 1
+    batch, d_in = _rows(x)
+    d_out = wt.shape[1]
+    _gemv_out(wt, batch, squeeze, y)
+    _check(lib().sparse_gemv_threshold_noalloc(_ptr(wt), d_out, d_in, _ptr(x), batch, float(t),
+                                               _ptr(y), _stream(wt)),
+           "sparse_gemv_threshold_noalloc")
+    return y
 
 
 def sparse_gemv_corrected(wt: torch.Tensor, idx: torch.Tensor, val: torch.Tensor,

@@ -211,6 +211,38 @@ int sparse_gemv_scored(const uint16_t* wt, int64_t d_out, int64_t d_in, const ui
   return run_gemv(c, "sparse_gemv_scored", stream);
 }
 
+static_assert(SA_NOALLOC_SCRATCH_BYTES == sa::kNoAllocScratchBytes, "header and library agree");
+
+int sparse_gemv_threshold_noalloc(const uint16_t* wt, int64_t d_out, int64_t d_in,
+                                  const uint16_t* x, int64_t batch, float t, uint16_t* y,
+                                  void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_out, d_in, batch < 1 ? 1 : batch);
+  // sizes are checked before the scratch is looked up: an oversized call
+  // returns at once
+  int st = sa::check_gemv_common(wt, d_out, d_in, batch, y, nullptr, 0, 0);
+  if (st == SA_OK) st = sa::check_activation(x, "sparse_gemv_threshold_noalloc: x");
+  if (st == SA_OK) st = sa::check_threshold_value(t);
+  if (st == SA_OK) st = sa::check_noalloc_size(need, sa::kNoAllocScratchBytes);
+  if (st != SA_OK) return st;
+  if (batch == 0) return SA_OK;
+  void* ws = nullptr;
+  const hipError_t e = sa::gemv_noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "sparse_gemv_threshold_noalloc");
+  sa::GemvCall c;
+  c.mode = sa::kModeThreshold;
+  c.wt = wt;
+  c.d_out = d_out;
+  c.d_in = d_in;
+  c.batch = (int)batch;
+  c.x = x;
+  c.t = t;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = sa::kNoAllocScratchBytes;
+  return run_gemv(c, "sparse_gemv_threshold_noalloc", stream);
+}
+
 int sparse_gemv_corrected(const uint16_t* wt, int64_t d_out, int64_t d_in, const int32_t* idx,
                           const uint16_t* val, const int32_t* nnz, int64_t batch, int64_t cap,
                           const float* alpha, const uint16_t* bias, uint16_t* y, void* ws,

@@ -1645,6 +1645,39 @@ size_t gemv_workspace_zero_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
   return kTicketBytes;  // the hand-off counters; the rest is written before it is read
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (sparse_gemv_threshold_noalloc):
+// a fixed array in device memory, one copy per GPU the library runs on, held
+// until the process ends.  It is used exactly as a caller's workspace: its
+// first kTicketBytes are the hand-off counters, zero from load time (static
+// storage) and left zero by every call; the partial sums follow.  Host code
+// reaches it only through the address hipGetSymbolAddress gives for the
+// current device (the array's name is not a device address on the host).
+// ---------------------------------------------------------------------------
+namespace {
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static_assert(kNoAllocScratchBytes > kTicketBytes, "room for partials after the counters");
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+}  // namespace
+
+hipError_t gemv_noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 // The kernel and decomposition of one call shape.  cus / resident: the

@@ -82,6 +82,11 @@ size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch);
 // Leading bytes of that workspace that must be zero before a call (and are
 // zero after it): the hand-off counters, the status word and the slots.
 size_t gemv_workspace_zero_bytes(int64_t d_out, int64_t d_in, int64_t batch);
+// The allocation-free entry point's scratch: a static device array of
+// kNoAllocScratchBytes per GPU; *ptr gets the current device's copy (looked
+// up once per device).  Allocates nothing.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t gemv_noalloc_scratch(void** ptr);
 // Returns hipErrorInvalidValue if the workspace is too small for the launch
 // (checked by abi.cpp beforehand, so this is a second line of defence).
 hipError_t launch_gemv(const GemvCall& c, hipStream_t s);

@@ -193,6 +193,14 @@ int check_sparse_gemv(const void* idx, const void* val, const void* nnz, int64_t
   return SA_OK;
 }
 
+int check_noalloc_size(size_t need, size_t have) {
+  REQUIRE(need <= have, SA_ERR_UNSUPPORTED,
+          "sparse_gemv_threshold_noalloc: this shape needs %zu bytes of scratch, more than "
+          "the fixed %zu; use sparse_gemv_threshold with a workspace",
+          need, have);
+  return SA_OK;
+}
+
 int check_activation(const void* x, const char* name) {
   REQUIRE(x != nullptr, SA_ERR_INVALID_ARG, "%s must not be NULL", name);
   REQUIRE(aligned(x, 2), SA_ERR_INVALID_ARG, "%s must be 2-byte aligned", name);

@@ -35,6 +35,7 @@ int check_gemv_common(const void* wt, int64_t d_out, int64_t d_in, int64_t batch
 int check_sparse_gemv(const void* idx, const void* val, const void* nnz, int64_t batch,
                       int64_t cap);
 int check_activation(const void* x, const char* name);
+int check_noalloc_size(size_t need, size_t have);
 int check_threshold_value(float t);
 int check_swiglu(const void* g, const void* u, const void* colnorm, int64_t d_ff, double t,
                  int mode);
