@@ -109,6 +109,19 @@ int act_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k,
                       int32_t* nnz, int64_t cap, void* stream);
 
 /*
+ * act_topk_cutoff -- the per-token Top-K selection of act_sparsify_topk as
+ * a cutoff instead of lists: per row the pair (tau, i*) such that entry i
+ * survives iff its magnitude key (fp16 bits & 0x7fff) is > tau, or == tau
+ * and i <= i*.  tau is the k-th largest key and i* the index of the last
+ * surviving entry with that key (ties go to the lower index); k = 0 gives
+ * tau = 32768, i* = -1 (nothing survives).
+ *   cut [rows][2] int32 (device), 8-byte aligned
+ * Requires 0 <= k <= d, 1 <= d <= 65536.
+ */
+int act_topk_cutoff(const uint16_t* x, int64_t rows, int64_t d, int64_t k, int32_t* cut,
+                    void* stream);
+
+/*
  * act_sparsify_nm -- N:M activation sparsity.
  * [QS] answer on batched inference (Block Q-Sparse): N:M over M consecutive
  * entries; [NM] section 2 (methodology): N nonzeros kept per block of M,
@@ -238,6 +251,21 @@ int sparse_gemv(const uint16_t* wt, int64_t d_out, int64_t d_in,
 int sparse_gemv_threshold(const uint16_t* wt, int64_t d_out, int64_t d_in,
                           const uint16_t* x, int64_t batch, float t,
                           uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_gemv_topk -- per-token Top-K and the sparse GEMV, without lists:
+ * y[b] = W (keep_b .* x[b]) with keep_b the k largest |x[b]| (ties to the
+ * lower index), as act_sparsify_topk keeps them ([QS] answer comparing with
+ * MoE: per token, the smaller entries are pruned; answer A1: TopK =
+ * 60/50/40%).  Two launches on `stream`: act_topk_cutoff writes each row's
+ * (tau, i*) into the workspace, then the GEMV decides every entry from x
+ * and that pair in its own slice (no index list is written or read).
+ *   x [batch][d_in] fp16 (2-byte aligned); 0 <= k <= d_in <= 65536; other
+ *   arguments as sparse_gemv_threshold.
+ */
+int sparse_gemv_topk(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint16_t* x,
+                     int64_t batch, int64_t k, uint16_t* y, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /*
  * sparse_gemv_threshold_noalloc -- sparse_gemv_threshold without a
@@ -448,6 +476,13 @@ int dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
  *   sink device, SA_READ_STREAM_SINK_WORDS uint32 (contents meaningless)
  */
 int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
+/*
+ * sa_read_stream_grid -- the same read with a grid of `blocks` x 256 threads
+ * (1 <= blocks <= 16384), for a curve of read time against bytes and grid
+ * size.  sink holds blocks * 4 uint32 words.  Bench-only.
+ */
+int sa_read_stream_grid(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                        void* stream);
 
 /* ---- tuning hook -------------------------------------------------------- */
 
@@ -511,7 +546,8 @@ enum {
   SA_GEMV_LIST = 3,      /* sparse_gemv, sparse_gemv_corrected */
   SA_GEMV_SWIGLU = 4,    /* masked_swiglu_down */
   SA_GEMV_SCORED = 6,    /* sparse_gemv_scored */
-  SA_GEMV_SQUARE = 7     /* the second GEMV of rana_adapter_gemv */
+  SA_GEMV_SQUARE = 7,    /* the second GEMV of rana_adapter_gemv */
+  SA_GEMV_TOPK = 8       /* the GEMV of sparse_gemv_topk */
 };
 /*
  * The decomposition a GEMV entry point would use for a call shape, under the

@@ -24,7 +24,8 @@ import torch
 
 __all__ = [
     "SparseActError", "lib", "workspace",
-    "act_sparsify_threshold", "act_sparsify_topk", "act_sparsify_nm", "act_sparsify_nm_shared",
+    "act_sparsify_threshold", "act_sparsify_topk", "act_topk_cutoff", "sparse_gemv_topk",
+    "act_sparsify_nm", "act_sparsify_nm_shared",
     "act_sparsify_scored", "sparse_gemv_corrected", "sparse_gemv_scored",
     "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold",
     "sparse_gemv_threshold_noalloc", "rana_adapter_gemv",
@@ -47,6 +48,8 @@ _SIGNATURES = {
     "sa_version": (_i32, []),
     "act_sparsify_threshold": (_i32, [_vp, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _i64, _vp]),
     "act_sparsify_topk": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "act_topk_cutoff": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "sparse_gemv_topk": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "act_sparsify_nm": (_i32, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp]),
     "act_sparsify_nm_shared": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "act_calibrate_threshold": (_i32, [_vp, _i64, _f64, _vp, _vp]),
@@ -75,6 +78,7 @@ _SIGNATURES = {
                               _vp]),
     "sa_nm_shared_spmm_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32]),
     "sa_read_stream": (_i32, [_vp, _sz, _vp, _vp]),
+    "sa_read_stream_grid": (_i32, [_vp, _sz, _vp, _i32, _vp]),
     "dense_gemm": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "sa_set_gemv_tuning": (_i32, [_i32, _i32, _i32]),
     "sa_set_gemm_tuning": (_i32, [_i32, _i32, _i32]),
@@ -256,6 +260,16 @@ def act_sparsify_topk(x: torch.Tensor, k: int, with_mask: bool = True, cap: int 
     return mask, idx, val, nnz
 
 
+def act_topk_cutoff(x: torch.Tensor, k: int) -> torch.Tensor:
+    """Per row the Top-K cutoff ``(tau, i*)`` as an int32 ``[rows][2]`` tensor."""
+    _dev(x, "x", torch.float16)
+    rows, d = _rows(x)
+    cut = torch.empty((rows, 2), dtype=torch.int32, device=x.device)
+    _check(lib().act_topk_cutoff(_ptr(x), rows, d, int(k), _ptr(cut), _stream(x)),
+           "act_topk_cutoff")
+    return cut
+
+
 def act_sparsify_nm(x: torch.Tensor, n: int, m: int):
     """Returns ``(mask, val)``: bitmask words and the compressed kept values."""
     _dev(x, "x", torch.float16)
@@ -338,6 +352,20 @@ def sparse_gemv_threshold(wt: torch.Tensor, x: torch.Tensor, t: float,
     ws = workspace(wt.device, workspace_bytes(d_out, d_in, batch))
     _check(lib().sparse_gemv_threshold(_ptr(wt), d_out, d_in, _ptr(x), batch, float(t), _ptr(y),
                                        _ptr(ws), ws.numel(), _stream(wt)), "sparse_gemv_threshold")
+    return _ret(y, squeeze)
+
+
+def sparse_gemv_topk(wt: torch.Tensor, x: torch.Tensor, k: int, y: torch.Tensor | None = None):
+    """Per-token Top-K of ``x`` (``k`` kept per row) and the sparse GEMV, no lists."""
+    _dev(wt, "wt", torch.float16)
+    _dev(x, "x", torch.float16)
+    squeeze = x.dim() == 1
+    batch, d_in = _rows(x)
+    d_out = wt.shape[1]
+    y = _gemv_out(wt, batch, squeeze, y)
+    ws = workspace(wt.device, workspace_bytes(d_out, d_in, batch))
+    _check(lib().sparse_gemv_topk(_ptr(wt), d_out, d_in, _ptr(x), batch, int(k), _ptr(y),
+                                  _ptr(ws), ws.numel(), _stream(wt)), "sparse_gemv_topk")
     return _ret(y, squeeze)
 
 
@@ -504,13 +532,21 @@ WS_TICKET_BYTES = 1 << 20  # SA_WS_TICKET_BYTES
 READ_STREAM_SINK_WORDS = 8192  # SA_READ_STREAM_SINK_WORDS
 
 
-def read_stream(src: torch.Tensor, nbytes: int | None = None) -> torch.Tensor:
-    """Bench-only: read ``nbytes`` of ``src`` once (roofline calibration);
-    returns the sink, whose xor equals the xor of the bytes read."""
+def read_stream(src: torch.Tensor, nbytes: int | None = None, blocks: int | None = None,
+                sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Bench-only: read ``nbytes`` of ``src`` once (roofline calibration) with
+    the default grid, or ``blocks`` x 256 threads; returns the sink, whose xor
+    equals the xor of the bytes read."""
     _dev(src, "src", None)
     n = src.numel() * src.element_size() if nbytes is None else nbytes
-    sink = torch.empty(READ_STREAM_SINK_WORDS, dtype=torch.int32, device=src.device)
-    _check(lib().sa_read_stream(_ptr(src), n, _ptr(sink), _stream(src)), "sa_read_stream")
+    words = READ_STREAM_SINK_WORDS if blocks is None else 4 * blocks
+    if sink is None or sink.numel() < words:
+        sink = torch.empty(words, dtype=torch.int32, device=src.device)
+    if blocks is None:
+        _check(lib().sa_read_stream(_ptr(src), n, _ptr(sink), _stream(src)), "sa_read_stream")
+    else:
+        _check(lib().sa_read_stream_grid(_ptr(src), n, _ptr(sink), int(blocks), _stream(src)),
+               "sa_read_stream_grid")
     return sink
 
 
@@ -586,7 +622,7 @@ def set_gemm_tuning(tile_rows: int = 0, engine: int = 0, stages: int = 0) -> Non
 
 
 GEMV_OPS = {"threshold": 0, "dense": 1, "masked": 2, "list": 3, "swiglu": 4, "scored": 6,
-            "square": 7}
+            "square": 7, "topk": 8}
 
 
 def gemv_plan(op: str, d_out: int, d_in: int, batch: int = 1, cus: int = 0, resident: int = 0):

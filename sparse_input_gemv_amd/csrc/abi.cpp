@@ -67,9 +67,20 @@ int act_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k, uin
   int st = sa::check_topk(x, rows, d, k, mask, idx, val, nnz, cap);
   if (st != SA_OK) return st;
   if (rows == 0) return SA_OK;
-  return hip_status(
-      sa::launch_sparsify_topk(x, rows, d, k, mask, idx, val, nnz, cap, as_stream(stream)),
-      "act_sparsify_topk");
+  return hip_status(sa::launch_sparsify_topk(x, rows, d, k, mask, idx, val, nnz, cap, nullptr,
+                                             as_stream(stream)),
+                    "act_sparsify_topk");
+}
+
+int act_topk_cutoff(const uint16_t* x, int64_t rows, int64_t d, int64_t k, int32_t* cut,
+                    void* stream) {
+  sa::clear_error();
+  int st = sa::check_topk_cutoff(x, rows, d, k, cut, "act_topk_cutoff");
+  if (st != SA_OK) return st;
+  if (rows == 0) return SA_OK;
+  return hip_status(sa::launch_sparsify_topk(x, rows, d, k, nullptr, nullptr, nullptr, nullptr,
+                                             0, cut, as_stream(stream)),
+                    "act_topk_cutoff");
 }
 
 int act_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m, uint32_t* mask,
@@ -212,6 +223,37 @@ int sparse_gemv_scored(const uint16_t* wt, int64_t d_out, int64_t d_in, const ui
 }
 
 static_assert(SA_NOALLOC_SCRATCH_BYTES == sa::kNoAllocScratchBytes, "header and library agree");
+
+int sparse_gemv_topk(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint16_t* x,
+                     int64_t batch, int64_t k, uint16_t* y, void* ws, size_t ws_bytes,
+                     void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_out, d_in, batch < 1 ? 1 : batch);
+  int st = sa::check_gemv_common(wt, d_out, d_in, batch, y, ws, ws_bytes, need);
+  if (st == SA_OK && batch == 0) return SA_OK;
+  int32_t* cut = st == SA_OK ? reinterpret_cast<int32_t*>(
+                                   static_cast<unsigned char*>(ws) +
+                                   sa::gemv_workspace_cut_offset(d_out, d_in, batch))
+                             : nullptr;
+  if (st == SA_OK) st = sa::check_topk_cutoff(x, batch, d_in, k, cut, "sparse_gemv_topk");
+  if (st != SA_OK) return st;
+  st = hip_status(sa::launch_sparsify_topk(x, batch, d_in, k, nullptr, nullptr, nullptr, nullptr,
+                                           0, cut, as_stream(stream)),
+                  "sparse_gemv_topk");
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeTopK;
+  c.wt = wt;
+  c.d_out = d_out;
+  c.d_in = d_in;
+  c.batch = (int)batch;
+  c.x = x;
+  c.cut = cut;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return run_gemv(c, "sparse_gemv_topk", stream);
+}
 
 int sparse_gemv_threshold_noalloc(const uint16_t* wt, int64_t d_out, int64_t d_in,
                                   const uint16_t* x, int64_t batch, float t, uint16_t* y,
@@ -402,7 +444,8 @@ int weight_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* ou
 static_assert(SA_READ_STREAM_SINK_WORDS == sa::kReadStreamBlocks * sa::kReadStreamThreads / 64,
               "one sink word per wave of the read-stream grid");
 
-int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+int sa_read_stream_grid(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                        void* stream) {
   sa::clear_error();
   if (src == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0 ||
       (reinterpret_cast<uintptr_t>(src) & 15u) != 0 ||
@@ -411,8 +454,16 @@ int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream) 
                   "multiple of 16");
     return SA_ERR_INVALID_ARG;
   }
-  return hip_status(sa::launch_read_stream(src, bytes, sink, as_stream(stream)),
+  if (blocks < 1 || blocks > sa::kReadStreamMaxBlocks) {
+    sa::set_error("sa_read_stream_grid: blocks must be in [1, %d]", sa::kReadStreamMaxBlocks);
+    return SA_ERR_INVALID_ARG;
+  }
+  return hip_status(sa::launch_read_stream(src, bytes, sink, blocks, as_stream(stream)),
                     "sa_read_stream");
+}
+
+int sa_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  return sa_read_stream_grid(src, bytes, sink, sa::kReadStreamBlocks, stream);
 }
 
 size_t sa_nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m) {
@@ -526,7 +577,7 @@ int sa_gemv_plan(int op, int64_t d_out, int64_t d_in, int64_t batch, int cus, in
   sa::clear_error();
   const bool known = op == SA_GEMV_THRESHOLD || op == SA_GEMV_DENSE || op == SA_GEMV_MASKED ||
                      op == SA_GEMV_LIST || op == SA_GEMV_SWIGLU || op == SA_GEMV_SCORED ||
-                     op == SA_GEMV_SQUARE;
+                     op == SA_GEMV_SQUARE || op == SA_GEMV_TOPK;
   if (!known || d_out < 1 || d_in < 1 || batch < 1 || batch > SA_MAX_BATCH || cus < 0 ||
       resident < 0 || kernel == nullptr || tile_o == nullptr || grid_o == nullptr ||
       slices == nullptr || handoff == nullptr) {

@@ -150,6 +150,7 @@ struct KParams {
   const uint16_t* mu;
   double* vsum;
   int var;  // scored mode: apply the variance correction
+  const int32_t* cut;  // Top-K mode: [batch][2] (tau, i*) of the select
 };
 
 constexpr int kModeListBatched = 5;  // kModeList with batch > 1
@@ -169,6 +170,13 @@ __device__ __forceinline__ bool keep_entry(uint16_t xb, float t) {
   const float v = h2f(xb);
   if constexpr (MODE == kModeSquare) return v * v >= t;
   return mag_key(xb) != 0 && fabsf(v) >= t;
+}
+
+// Top-K mode: entry i of a row survives the select iff its magnitude key is
+// above the row's cutoff tau, or equal to it and i <= i* (the select's pair).
+__device__ __forceinline__ bool topk_keep(uint16_t xb, int64_t i, int tau, int istar) {
+  const int key = mag_key(xb);
+  return key > tau || (key == tau && i <= (int64_t)istar);
 }
 
 // Modes whose output takes the correction alpha * sum + bias (the list GEMV
@@ -410,6 +418,15 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   const int oblk = (int)(blockIdx.x % (unsigned)p.go);
   const int kblk = (int)(blockIdx.x / (unsigned)p.go);
   const int SL = p.slice;
+  int tk_tau[B], tk_ist[B];  // Top-K mode: each row's cutoff, read with the other arguments
+  if constexpr (MODE == kModeTopK) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int bb = b < p.batch ? b : 0;
+      tk_tau[b] = p.cut[2 * bb];
+      tk_ist[b] = p.cut[2 * bb + 1];
+    }
+  }
   int* lk = reinterpret_cast<int*>(smem);
   float* lv = reinterpret_cast<float*>(smem + (size_t)SL * 4);
   // Batch > 1: the values are the activations' fp16 bits, [B][SLH] with SLH
@@ -558,6 +575,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
           } else if (b < p.batch && k < k1) {
             if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
               kb = keep_entry<MODE>(xb, p.t);
+            } else if constexpr (MODE == kModeTopK) {
+              kb = topk_keep(xb, k, tk_tau[b], tk_ist[b]);
             } else if constexpr (MODE == kModeMasked) {
               kb = ((mw[c][b] >> (k & 31)) & 1u) != 0;
             } else {
@@ -663,6 +682,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
               bool kb;
               if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
                 kb = keep_entry<MODE>(xb, p.t);
+              } else if constexpr (MODE == kModeTopK) {
+                kb = topk_keep(xb, k, tk_tau[b], tk_ist[b]);
               } else if constexpr (MODE == kModeMasked) {
                 kb = ((mw[b] >> (k & 31)) & 1u) != 0;
               } else {
@@ -1109,6 +1130,15 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
   const bool o_ok = o < p.d_out;
   const uint16_t* __restrict__ wcol = p.wt + (o_ok ? o : 0);
   const int64_t ld = p.d_out;
+  int tk_tau[B], tk_ist[B];  // Top-K mode: each row's cutoff
+  if constexpr (MODE == kModeTopK) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int bb = b < p.batch ? b : 0;
+      tk_tau[b] = p.cut[2 * bb];
+      tk_ist[b] = p.cut[2 * bb + 1];
+    }
+  }
   const int64_t words = (p.d_in + 31) >> 5;
 
   int64_t n = p.d_in;
@@ -1199,6 +1229,8 @@ __global__ __launch_bounds__(NT) void k_gemv_fk(KParams p) {
             bool kb;
             if constexpr (MODE == kModeThreshold || MODE == kModeSquare) {
               kb = keep_entry<MODE>(xb, p.t);
+            } else if constexpr (MODE == kModeTopK) {
+              kb = topk_keep(xb, j, tk_tau[b], tk_ist[b]);
             } else if constexpr (MODE == kModeMasked) {
               kb = ((mw[q][b] >> (j & 31)) & 1u) != 0;
             } else {
@@ -1348,7 +1380,7 @@ int batch_pad(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ?
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t ticket_off, slicecnt_off, part_off, vsum_off, total;
+  size_t ticket_off, slicecnt_off, part_off, vsum_off, cut_off, total;
 };
 
 // Workspace: the hand-off counters (a fixed region, zero between calls: the
@@ -1364,7 +1396,8 @@ Layout ws_layout(int64_t d_out, int64_t d_in, int64_t batch) {
   L.vsum_off = L.part_off + align256((size_t)gk_max * (size_t)batch_pad((int)batch) *
                                      (size_t)d_out * 4);
   const size_t go_max = (size_t)((d_out + kMinSplitTileO - 1) / kMinSplitTileO);
-  L.total = L.vsum_off + (size_t)gk_max * go_max * 2 * sizeof(double);
+  L.cut_off = L.vsum_off + align256((size_t)gk_max * go_max * 2 * sizeof(double));
+  L.total = L.cut_off + 256;  // SA_MAX_BATCH (tau, i*) pairs of sparse_gemv_topk
   return L;
 }
 
@@ -1407,7 +1440,8 @@ using KFn = void (*)(KParams);
 
 template <int MODE, int B, bool LOCAL>
 KFn kernel_tiling_scope(int tiling) {
-  if constexpr (B == 1 && (MODE == kModeThreshold || MODE == kModeDense || MODE == kModeList)) {
+  if constexpr (B == 1 && (MODE == kModeThreshold || MODE == kModeDense || MODE == kModeList ||
+                           MODE == kModeTopK)) {
     switch (tiling) {
       case 1: return k_gemv<MODE, 256, 256, 8, B, LOCAL>;
       case 2: return k_gemv<MODE, 256, 512, 8, B, LOCAL>;
@@ -1450,6 +1484,7 @@ KFn select_kernel(int mode, int tiling, int B, bool local = false) {
     case kModeSwiglu: return kernel_tiling<kModeSwiglu, 1>(tiling, local);
     case kModeScored: return kernel_tiling<kModeScored, 1>(tiling, local);
     case kModeSquare: return kernel_batch<kModeSquare>(tiling, B, local);
+    case kModeTopK: return kernel_batch<kModeTopK>(tiling, B, local);
     default: return nullptr;
   }
 }
@@ -1638,6 +1673,10 @@ size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
   return ws_layout(d_out, d_in, batch).total;
 }
 
+size_t gemv_workspace_cut_offset(int64_t d_out, int64_t d_in, int64_t batch) {
+  return ws_layout(d_out, d_in, batch).cut_off;
+}
+
 size_t gemv_workspace_zero_bytes(int64_t d_out, int64_t d_in, int64_t batch) {
   (void)d_out;
   (void)d_in;
@@ -1702,7 +1741,8 @@ Decision decide_gemv(int mode, int64_t d_out, int64_t d_in, int64_t batch, int64
   // weights whose grid fills the chip or whose walk is short.
   const bool fk_ok = B <= 2 && mode != kModeListBatched;
   int tiling = g_tiling;
-  const bool hot = B == 1 && (mode == kModeThreshold || mode == kModeDense || mode == kModeList);
+  const bool hot = B == 1 && (mode == kModeThreshold || mode == kModeDense ||
+                              mode == kModeList || mode == kModeTopK);
   if (tiling < 0) {
     const int64_t wbytes = d_in * d_out * 2;
     const bool fk_fills = (d_out + kTilings[kDefaultFullK].tile_o - 1) /
@@ -1771,6 +1811,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   kp.alpha = c.alpha;
   kp.bias = c.bias;
   kp.mu = c.mu;
+  kp.cut = c.cut;
   kp.var = (mode == kModeScored && c.var) ? 1 : 0;
 
   if (dc.full_k) {
@@ -1792,6 +1833,9 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
       case kModeSquare:
         return B == 1 ? dispatch_fk<kModeSquare, 1>(kp, tiling, grid, s)
                       : dispatch_fk<kModeSquare, 2>(kp, tiling, grid, s);
+      case kModeTopK:
+        return B == 1 ? dispatch_fk<kModeTopK, 1>(kp, tiling, grid, s)
+                      : dispatch_fk<kModeTopK, 2>(kp, tiling, grid, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -16,9 +16,11 @@ hipError_t launch_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d,
                                   const uint16_t* mu, const double* colnorm, int n, int m,
                                   double t, uint32_t* mask, int32_t* idx, uint16_t* val,
                                   int32_t* nnz, float* alpha, int64_t cap, hipStream_t s);
+// cut (may be NULL): per row the pair (tau, i*) of the selection; mask, idx
+// and val may all be NULL (then only cut and nnz are written).
 hipError_t launch_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k,
                                 uint32_t* mask, int32_t* idx, uint16_t* val, int32_t* nnz,
-                                int64_t cap, hipStream_t s);
+                                int64_t cap, int32_t* cut, hipStream_t s);
 hipError_t launch_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
                               uint32_t* mask, uint16_t* val, hipStream_t s);
 hipError_t launch_sparsify_nm_shared(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
@@ -37,6 +39,8 @@ enum GemvMode : int {
   kModeSwiglu = 4,     // CATS / RaNA masked SwiGLU down
   kModeScored = 6,     // x + shift + weight norms: weight-aware threshold (batch 1)
   kModeSquare = 7,     // x + t: keep x_k iff x_k^2 >= t (the rank adapter's masker)
+  kModeTopK = 8,       // x + per-row (tau, i*) from the Top-K select: keep iff
+                       // key > tau, or key == tau and k <= i*
 };
 
 struct GemvCall {
@@ -49,6 +53,7 @@ struct GemvCall {
   const uint32_t* xmask = nullptr;
   float t = 0.f;
   const uint16_t* mu = nullptr;  // scored mode: static shift [d_in] (or none)
+  const int32_t* cut = nullptr;  // Top-K mode: [batch][2] (tau, i*)
   int var = 0;                   // scored mode: apply the variance correction
   // lists
   const int32_t* idx = nullptr;
@@ -79,6 +84,8 @@ constexpr int kMinSplitTileO = 64;
 constexpr size_t kGemvTicketBytes = (size_t)(524288 / kMinSplitTileO) * kTicketStride * 4;
 
 size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch);
+// Offset in that workspace of SA_MAX_BATCH (tau, i*) pairs for sparse_gemv_topk.
+size_t gemv_workspace_cut_offset(int64_t d_out, int64_t d_in, int64_t batch);
 // Leading bytes of that workspace that must be zero before a call (and are
 // zero after it): the hand-off counters, the status word and the slots.
 size_t gemv_workspace_zero_bytes(int64_t d_out, int64_t d_in, int64_t batch);
@@ -102,7 +109,9 @@ int gemv_tiling_info(int i, int* tile_o, int* threads, int* unroll);
 // ---- read-stream calibration (stream.hip) -----------------------------------
 constexpr int kReadStreamBlocks = 2048;  // measured best grid for a 45 MB read
 constexpr int kReadStreamThreads = 256;
-hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+constexpr int kReadStreamMaxBlocks = 16384;
+hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                              hipStream_t s);
 
 // ---- MFMA matmuls (gemm.hip) ------------------------------------------------
 // Compute units of the current device (cached per device).

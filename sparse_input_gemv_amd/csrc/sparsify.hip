@@ -206,130 +206,155 @@ __global__ __launch_bounds__(NT) void k_sparsify_scored(
   if (threadIdx.x == 0) nnz[row] = base;
 }
 
-// Wave 0 helper for the radix select: given per-lane counts of consecutive
-// bins (lane l holds bins P*l .. P*l+P-1, ascending), find the largest bin b
-// whose suffix count S(b) = sum_{b' >= b} + extra reaches k; also return
-// S(b+1) (count strictly above).  Bins with S >= k form a prefix because S
-// is non-increasing.
-template <int P>
-__device__ __forceinline__ void suffix_select(const int (&c)[P], int extra, int64_t k, int& bin,
-                                              int& above) {
-  const int lane = lane_id();
-  int s = 0;
-#pragma unroll
-  for (int j = 0; j < P; ++j) s += c[j];
-  int suf = s;  // inclusive suffix over lanes >= this one
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_down(suf, o, kWave);
-    if (lane + o < kWave) suf += t;
-  }
-  int S[P];
-  S[0] = suf + extra;
-#pragma unroll
-  for (int j = 1; j < P; ++j) S[j] = S[j - 1] - c[j - 1];
-  int nq = 0;
-#pragma unroll
-  for (int j = 0; j < P; ++j) nq += (S[j] >= k) ? 1 : 0;
-#pragma unroll
-  for (int o = kWave / 2; o >= 1; o >>= 1) nq += __shfl_xor(nq, o, kWave);
-  bin = nq - 1;
-  const int nb = bin + 1;  // S(bin+1) lives in lane nb/P, slot nb%P
-  int mine = S[0];
-#pragma unroll
-  for (int j = 1; j < P; ++j)
-    if ((nb % P) == j) mine = S[j];
-  int got = __shfl(mine, (nb / P) & (kWave - 1), kWave);
-  above = (nb >= P * kWave) ? extra : got;
-}
-
 // Exactly k survivors per row: the k largest magnitudes, ties to the lower
-// index.  15-bit magnitude keys; two-level radix select (256 then 128 bins in
-// LDS) gives the k-th largest key tau and the count above it; the first
-// r = k - above entries equal to tau (in index order, by a workgroup scan)
-// complete the set.  One workgroup per row; each thread keeps E keys.
+// index (fp16 magnitudes compared exactly as 15-bit keys; -0 == +0).  One LDS
+// bin per key value (2^15 bins, 128 KB): a single pass of LDS atomics counts
+// every key; each thread then owns 32 consecutive bins, and a workgroup scan
+// of the threads' sums, read from the top, finds the thread and then the bin
+// where the count of larger keys reaches k.  That bin is tau, the k-th
+// largest key, with r = k - #(keys > tau) of its entries still to keep; a
+// scan of the threads' counts of keys equal to tau, in index order, finds
+// the r-th of them, at index i*.  Entry i survives iff key_i > tau, or
+// key_i == tau and i <= i* (k = 0: tau = 2^15, i* = -1, nothing survives).
+// Outputs: the pair (tau, i*) per row in `cut` (may be NULL), the bitmask,
+// and the compacted list (staged in LDS for d <= NT * 16, so it leaves in
+// coalesced stores).  One workgroup per row; each thread keeps E keys.
+constexpr int kTopkBins = 1 << 15;
+
 template <int NT, int E>
-__global__ __launch_bounds__(NT) void k_sparsify_topk(
-    const uint16_t* __restrict__ x, int64_t d, int64_t k, uint32_t* __restrict__ mask,
-    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int32_t* __restrict__ nnz,
-    int64_t cap, int vec) {
-  __shared__ int hist[256];
+__global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int64_t d, int64_t k,
+                                             int32_t* __restrict__ cut,
+                                             uint32_t* __restrict__ mask,
+                                             int32_t* __restrict__ idx,
+                                             uint16_t* __restrict__ val,
+                                             int32_t* __restrict__ nnz, int64_t cap, int vec) {
+  __shared__ __align__(16) int hist[kTopkBins];  // the counts; then the output staging
   __shared__ int scan[NT / kWave];
   __shared__ int sel[2];
+  constexpr int BPT = kTopkBins / NT;  // bins per thread
+  static_assert(BPT % 4 == 0 && kTopkBins % NT == 0, "bins split into int4 runs");
+  const int tid = (int)threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * d;
-  const int64_t k0 = (int64_t)threadIdx.x * E;
+  const int64_t k0 = (int64_t)tid * E;
   uint16_t v[E];
   load_run<E>(xr, k0, d, vec != 0, v);
   int key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = (k0 + e < d) ? mag_key(v[e]) : -1;
 
-  int tau = 0x8000, r = 0;  // k == 0: nothing survives
+  int tau = kTopkBins, istar = -1;  // k == 0: no key reaches tau
   if (k > 0) {
-    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
+    int4* h4 = reinterpret_cast<int4*>(hist);
+    for (int i = tid; i < kTopkBins / 4; i += NT) h4[i] = int4{0, 0, 0, 0};
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (key[e] >= 0) atomicAdd(&hist[key[e] >> 7], 1);
+      if (key[e] >= 0) atomicAdd(&hist[key[e]], 1);
     __syncthreads();
-    if (threadIdx.x < kWave) {
-      int c[4];
+    int c[BPT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = hist[threadIdx.x * 4 + j];
-      int b1, above;
-      suffix_select<4>(c, 0, k, b1, above);
-      if (threadIdx.x == 0) {
-        sel[0] = b1;
-        sel[1] = above;
-      }
+    for (int q = 0; q < BPT / 4; ++q) {
+      const int4 t4 = h4[tid * (BPT / 4) + q];
+      c[4 * q] = t4.x;
+      c[4 * q + 1] = t4.y;
+      c[4 * q + 2] = t4.z;
+      c[4 * q + 3] = t4.w;
     }
-    __syncthreads();
-    const int b1 = sel[0];
-    const int above1 = sel[1];
-    for (int i = threadIdx.x; i < 128; i += NT) hist[i] = 0;
-    __syncthreads();
+    int mine = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (key[e] >= 0 && (key[e] >> 7) == b1) atomicAdd(&hist[key[e] & 127], 1);
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-      int c[2];
+    for (int j = 0; j < BPT; ++j) mine += c[j];
+    int total;
+    const int below = block_exclusive_scan<NT>(mine, scan, total);
+    const int64_t above = (int64_t)(total - below - mine);  // keys in higher threads' bins
+    if (above < k && k <= above + mine) {  // exactly one thread
+      int64_t acc = above;
+      int b = 0, gt = 0;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) c[j] = hist[threadIdx.x * 2 + j];
-      int b2, gt;
-      suffix_select<2>(c, above1, k, b2, gt);
-      if (threadIdx.x == 0) {
-        sel[0] = (b1 << 7) | b2;
-        sel[1] = (int)(k - gt);
+      for (int j = BPT - 1; j >= 0; --j) {
+        if (b == 0 && acc + c[j] >= k) {
+          b = tid * BPT + j + 1;  // + 1: 0 means not found yet
+          gt = (int)acc;
+        }
+        acc += c[j];
       }
+      sel[0] = b - 1;
+      sel[1] = (int)(k - gt);
     }
     __syncthreads();
     tau = sel[0];
-    r = sel[1];
+    const int r = sel[1];  // >= 1
+    int ties = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ties += (key[e] == tau) ? 1 : 0;
+    int tie_total;
+    const int tr = block_exclusive_scan<NT>(ties, scan, tie_total);
+    if (tr < r && r <= tr + ties) {  // exactly one thread holds the r-th tie
+      int n = tr, at = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (key[e] == tau) {
+          ++n;
+          if (n == r) at = (int)(k0 + e);
+        }
+      }
+      sel[0] = at;
+    }
+    __syncthreads();
+    istar = sel[0];
+  }
+  if (cut != nullptr && tid == 0) {
+    cut[2 * row] = tau;
+    cut[2 * row + 1] = istar;
+  }
+  if (idx == nullptr && mask == nullptr) {
+    if (nnz != nullptr && tid == 0) nnz[row] = (int32_t)k;
+    return;
   }
 
-  int ties = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) ties += (key[e] == tau) ? 1 : 0;
-  int tie_total;
-  int tr = block_exclusive_scan<NT>(ties, scan, tie_total);
   uint64_t bits = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    bool keep = key[e] > tau;
-    if (key[e] == tau) {
-      keep = tr < r;
-      ++tr;
-    }
+    const bool keep = key[e] > tau || (key[e] == tau && k0 + e <= (int64_t)istar);
     bits |= (uint64_t)keep << e;
   }
   int32_t* ir = idx + row * cap;
   uint16_t* vr = val + row * cap;
   uint32_t* mr = mask ? mask + row * ((d + 31) >> 5) : nullptr;
-  int base = 0;
-  compact_run<NT, E>(bits, v, k0, d, base, scan, ir, vr, mr);
-  if (threadIdx.x == 0) nnz[row] = base;
+  if constexpr ((int64_t)NT * E * 6 <= (int64_t)kTopkBins * 4) {
+    // stage the list in LDS (the counts are no longer read), then copy it out
+    if (mr != nullptr) {
+      if constexpr (E == 16) {
+        const uint32_t other = (uint32_t)__shfl_xor((int)bits, 1, kWave);
+        if ((tid & 1) == 0 && k0 < d) mr[k0 >> 5] = (uint32_t)bits | (other << 16);
+      } else {
+#pragma unroll
+        for (int q = 0; q < E / 32; ++q)
+          if (k0 + 32 * q < d) mr[(k0 >> 5) + q] = (uint32_t)(bits >> (32 * q));
+      }
+    }
+    int kept;
+    int pos = block_exclusive_scan<NT>(__popcll(bits), scan, kept);
+    int32_t* sidx = hist;
+    uint16_t* sval = reinterpret_cast<uint16_t*>(hist + NT * E);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if ((bits >> e) & 1ull) {
+        sidx[pos] = (int32_t)(k0 + e);
+        sval[pos] = v[e];
+        ++pos;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < kept; i += NT) {
+      ir[i] = sidx[i];
+      vr[i] = sval[i];
+    }
+  } else {
+    int base = 0;
+    compact_run<NT, E>(bits, v, k0, d, base, scan, ir, vr, mr);
+  }
+  if (tid == 0) nnz[row] = (int32_t)k;
 }
 
 // N:M: each thread owns 8 consecutive entries (one 16-byte load).  An entry
@@ -588,14 +613,14 @@ hipError_t launch_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d,
 
 hipError_t launch_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int64_t k,
                                 uint32_t* mask, int32_t* idx, uint16_t* val, int32_t* nnz,
-                                int64_t cap, hipStream_t s) {
+                                int64_t cap, int32_t* cut, hipStream_t s) {
   const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && (d % 8) == 0) ? 1 : 0;
   if (d <= (int64_t)kSparsifyThreads * 16) {
-    hipLaunchKernelGGL((k_sparsify_topk<kSparsifyThreads, 16>), dim3((unsigned)rows),
-                       dim3(kSparsifyThreads), 0, s, x, d, k, mask, idx, val, nnz, cap, vec);
+    hipLaunchKernelGGL((k_topk<kSparsifyThreads, 16>), dim3((unsigned)rows),
+                       dim3(kSparsifyThreads), 0, s, x, d, k, cut, mask, idx, val, nnz, cap, vec);
   } else {
-    hipLaunchKernelGGL((k_sparsify_topk<kSparsifyThreads, 64>), dim3((unsigned)rows),
-                       dim3(kSparsifyThreads), 0, s, x, d, k, mask, idx, val, nnz, cap, vec);
+    hipLaunchKernelGGL((k_topk<kSparsifyThreads, 64>), dim3((unsigned)rows),
+                       dim3(kSparsifyThreads), 0, s, x, d, k, cut, mask, idx, val, nnz, cap, vec);
   }
   return hipGetLastError();
 }

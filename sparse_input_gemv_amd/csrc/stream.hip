@@ -28,8 +28,9 @@ __global__ __launch_bounds__(kReadStreamThreads) void k_read_stream(const u32x4*
 
 }  // namespace
 
-hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
-  hipLaunchKernelGGL(k_read_stream, dim3(kReadStreamBlocks), dim3(kReadStreamThreads), 0, s,
+hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_read_stream, dim3(blocks), dim3(kReadStreamThreads), 0, s,
                      static_cast<const u32x4*>(src), (int64_t)(bytes / 16), sink);
   return hipGetLastError();
 }

@@ -114,6 +114,19 @@ int check_topk(const void* x, int64_t rows, int64_t d, int64_t k, const void* ma
   return SA_OK;
 }
 
+int check_topk_cutoff(const void* x, int64_t rows, int64_t d, int64_t k, const void* cut,
+                      const char* fn) {
+  int st = check_rows_d(rows, d, fn);
+  if (st) return st;
+  REQUIRE(x != nullptr && (cut != nullptr || rows == 0), SA_ERR_INVALID_ARG,
+          "%s: x and the cutoff output must not be NULL", fn);
+  REQUIRE(aligned(x, 2) && aligned(cut, 8), SA_ERR_INVALID_ARG,
+          "%s: x must be 2-byte and cut 8-byte aligned", fn);
+  REQUIRE(k >= 0 && k <= d, SA_ERR_INVALID_ARG, "%s: k = %lld not in [0, d = %lld]", fn,
+          (long long)k, (long long)d);
+  return SA_OK;
+}
+
 int check_nm(const void* x, int64_t rows, int64_t d, int n, int m, const void* mask,
              const void* val) {
   const char* fn = "act_sparsify_nm";

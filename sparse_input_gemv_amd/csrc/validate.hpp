@@ -21,6 +21,8 @@ int check_threshold(const void* x, int64_t rows, int64_t d, float t, const void*
 int check_scored(const void* x, int64_t rows, int64_t d, const void* mu, const void* colnorm,
                  int n, int m, double t, const void* mask, const void* idx, const void* val,
                  const void* nnz, int64_t cap, const void* alpha);
+int check_topk_cutoff(const void* x, int64_t rows, int64_t d, int64_t k, const void* cut,
+                      const char* fn);
 int check_topk(const void* x, int64_t rows, int64_t d, int64_t k, const void* mask,
                const void* idx, const void* val, const void* nnz, int64_t cap);
 int check_nm(const void* x, int64_t rows, int64_t d, int n, int m, const void* mask,

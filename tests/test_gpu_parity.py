@@ -296,6 +296,68 @@ def test_topk_edges_and_ties(d):
         check_lists(*sa.act_sparsify_topk(dev(X), k), X, keep)
 
 
+def oracle_cutoff(x, keep):
+    """The (tau, i*) pair an oracle Top-K mask implies: tau the smallest kept
+    magnitude key (fp16 bits without the sign), i* the last kept index with
+    that key; (32768, -1) when nothing is kept."""
+    key = np.atleast_2d(x).view(np.uint16).astype(np.int64) & 0x7FFF
+    out = []
+    for r in range(key.shape[0]):
+        kept = np.flatnonzero(np.atleast_2d(keep)[r])
+        if kept.size == 0:
+            out.append((32768, -1))
+            continue
+        tau = int(key[r, kept].min())
+        out.append((tau, int(kept[key[r, kept] == tau].max())))
+    return np.array(out, dtype=np.int32)
+
+
+@pytest.mark.parametrize("d", [1, 5, 64, 100, 4097, 11008, 16384, 16385, 30000, 65536])
+def test_topk_cutoff_bit_exact(d):
+    rng = np.random.default_rng(d + 7)
+    pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, 0.25], dtype=np.float16)
+    X = np.stack([pool[rng.integers(0, len(pool), size=d)], syn.laplace_f16((d,), 1.0, d),
+                  np.zeros(d, np.float16)])
+    for k in sorted({0, 1, d // 3, d // 2, d - 1, d} - {-1}):
+        keep = sparsify.topk_sparsify(X, k)[0]
+        cut = host(sa.act_topk_cutoff(dev(X), k))
+        assert np.array_equal(cut, oracle_cutoff(X, keep)), (d, k)
+        # the pair reproduces the mask it came from
+        key = X.view(np.uint16).astype(np.int64) & 0x7FFF
+        i = np.arange(d)[None, :]
+        rule = (key > cut[:, :1]) | ((key == cut[:, :1]) & (i <= cut[:, 1:]))
+        assert np.array_equal(rule, keep)
+
+
+@pytest.mark.parametrize("d", [4096, 11008])
+@pytest.mark.parametrize("pct", [60, 50, 40])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_sparse_gemv_topk(d, pct, batch):
+    k = syn.topk_k(pct, d)
+    X = syn.laplace_f16((batch, d), 1.0, 300 + batch)
+    keep = sparsify.topk_sparsify(X, k)[0]
+    d_out = 11008 if d == 4096 else 4096
+    wt = syn.weight_t(d_out, d, 40 + d)
+    y = sa.sparse_gemv_topk(dev(wt), dev(X), k)
+    assert_close(y, gemv.batched_masked_gemv(wt, X, keep))
+
+
+@pytest.mark.parametrize("d_out,d_in,batch", [(8, 1, 1), (104, 300, 3), (1024, 1024, 1),
+                                              (4096, 1000, 2), (336, 5000, 8)])
+def test_sparse_gemv_topk_edges(d_out, d_in, batch):
+    rng = np.random.default_rng(d_in)
+    pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0], dtype=np.float16)
+    X = pool[rng.integers(0, len(pool), size=(batch, d_in))]  # heavy ties
+    wt = syn.weight_t(d_out, d_in, 5)
+    wt_g, X_g = dev(wt), dev(X)
+    for k in sorted({0, 1, d_in // 2, d_in}):
+        keep = sparsify.topk_sparsify(X, k)[0]
+        y = sa.sparse_gemv_topk(wt_g, X_g, k)
+        assert_close(y, gemv.batched_masked_gemv(wt, X, keep))
+        if k == 0:
+            assert not np.any(host(y).view(np.uint16) & 0x7FFF)
+
+
 # ---------------------------------------------------------------------------
 # calibration
 # ---------------------------------------------------------------------------
