@@ -209,9 +209,13 @@ __global__ __launch_bounds__(NT) void k_sparsify_scored(
 // Exactly k survivors per row: the k largest magnitudes, ties to the lower
 // index (fp16 magnitudes compared exactly as 15-bit keys; -0 == +0).  One LDS
 // bin per key value (2^15 bins, 128 KB): a single pass of LDS atomics counts
-// every key; each thread then owns 32 consecutive bins, and a workgroup scan
-// of the threads' sums, read from the top, finds the thread and then the bin
-// where the count of larger keys reaches k.  That bin is tau, the k-th
+// every key; each thread then owns 32 consecutive keys' bins, and a workgroup
+// scan of the threads' sums, read from the top, finds the thread and then the
+// bin where the count of larger keys reaches k.  The bins of one thread are
+// stored as 8 int4 a workgroup-width apart (bin address below), so that the
+// threads of a wave read 64 consecutive int4 at a time, free of LDS bank
+// conflicts; stored contiguously, the 128-byte stride between threads put
+// every lane of a wave on the same four banks.  That bin is tau, the k-th
 // largest key, with r = k - #(keys > tau) of its entries still to keep; a
 // scan of the threads' counts of keys equal to tau, in index order, finds
 // the r-th of them, at index i*.  Entry i survives iff key_i > tau, or
@@ -221,6 +225,13 @@ __global__ __launch_bounds__(NT) void k_sparsify_scored(
 // coalesced stores).  One workgroup per row; each thread keeps E keys.
 constexpr int kTopkBins = 1 << 15;
 
+// LDS word of key `key`'s bin: thread t = key / BPT owns the int4 runs
+// q * NT + t, q < BPT / 4, holding its keys in order.
+template <int NT, int BPT>
+__device__ __forceinline__ int topk_bin(int key) {
+  return ((((key % BPT) >> 2) * NT + key / BPT) << 2) | (key & 3);
+}
+
 template <int NT, int E>
 __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int64_t d, int64_t k,
                                              int32_t* __restrict__ cut,
@@ -229,33 +240,36 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
                                              uint16_t* __restrict__ val,
                                              int32_t* __restrict__ nnz, int64_t cap, int vec) {
   __shared__ __align__(16) int hist[kTopkBins];  // the counts; then the output staging
-  __shared__ int scan[NT / kWave];
-  __shared__ int sel[2];
+  __shared__ int scan[3][NT / kWave];             // one per block scan
+  __shared__ int sel[3];                          // tau, ties to keep, i*
   constexpr int BPT = kTopkBins / NT;  // bins per thread
-  static_assert(BPT % 4 == 0 && kTopkBins % NT == 0, "bins split into int4 runs");
+  static_assert(BPT % 4 == 0 && kTopkBins % NT == 0 && BPT <= 32, "bins split into int4 runs");
   const int tid = (int)threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * d;
   const int64_t k0 = (int64_t)tid * E;
+  int4* h4 = reinterpret_cast<int4*>(hist);
   uint16_t v[E];
   load_run<E>(xr, k0, d, vec != 0, v);
+  // clear the bins while the row's loads are in flight
+  if (k > 0)
+    for (int i = tid; i < kTopkBins / 4; i += NT) h4[i] = int4{0, 0, 0, 0};
+  __builtin_amdgcn_sched_barrier(0);
   int key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = (k0 + e < d) ? mag_key(v[e]) : -1;
 
   int tau = kTopkBins, istar = -1;  // k == 0: no key reaches tau
   if (k > 0) {
-    int4* h4 = reinterpret_cast<int4*>(hist);
-    for (int i = tid; i < kTopkBins / 4; i += NT) h4[i] = int4{0, 0, 0, 0};
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (key[e] >= 0) atomicAdd(&hist[key[e]], 1);
+      if (key[e] >= 0) atomicAdd(&hist[topk_bin<NT, BPT>(key[e])], 1);
     __syncthreads();
     int c[BPT];
 #pragma unroll
     for (int q = 0; q < BPT / 4; ++q) {
-      const int4 t4 = h4[tid * (BPT / 4) + q];
+      const int4 t4 = h4[q * NT + tid];
       c[4 * q] = t4.x;
       c[4 * q + 1] = t4.y;
       c[4 * q + 2] = t4.z;
@@ -264,22 +278,32 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
     int mine = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) mine += c[j];
-    int total;
-    const int below = block_exclusive_scan<NT>(mine, scan, total);
-    const int64_t above = (int64_t)(total - below - mine);  // keys in higher threads' bins
-    if (above < k && k <= above + mine) {  // exactly one thread
-      int64_t acc = above;
-      int b = 0, gt = 0;
-#pragma unroll
-      for (int j = BPT - 1; j >= 0; --j) {
-        if (b == 0 && acc + c[j] >= k) {
-          b = tid * BPT + j + 1;  // + 1: 0 means not found yet
-          gt = (int)acc;
-        }
-        acc += c[j];
+    int total;  // == the number of entries, so k and every count fit an int
+    const int below = block_scan_once<NT>(mine, scan[0], total);
+    const int above = total - below - mine;  // keys in higher threads' bins
+    const int kk = (int)k;
+    // Exactly one thread t* has above < k <= above + mine.  Its wave finds
+    // the bin: lane l < BPT reads bin BPT*t* + (BPT-1-l) (top first) from
+    // LDS, an inclusive scan over those lanes gives the count of keys at or
+    // above each bin, and the first lane where above + count reaches k
+    // names tau; the keys above tau number gt, and r = k - gt of tau's own
+    // entries survive.
+    const uint64_t cross = __ballot(above < kk && kk <= above + mine);
+    if (cross != 0) {  // uniform: the wave holding t*
+      const int src = __builtin_ctzll(cross);
+      const int ts = __builtin_amdgcn_readfirstlane((int)threadIdx.x - lane_id() + src);
+      const int ab = __builtin_amdgcn_readlane(above, src);
+      const int lane = lane_id();
+      const int jb = BPT - 1 - (lane & (BPT - 1));
+      const int cb = lane < BPT ? hist[topk_bin<NT, BPT>(ts * BPT + jb)] : 0;
+      int sc = row16_inclusive_scan(cb);
+      if constexpr (BPT > 16) sc += (lane >> 4) == 1 ? __builtin_amdgcn_readlane(sc, 15) : 0;
+      const uint64_t hit = __ballot(lane < BPT && ab + sc >= kk);
+      const int l = __builtin_ctzll(hit);
+      if (lane == l) {
+        sel[0] = ts * BPT + jb;
+        sel[1] = kk - (ab + sc - cb);
       }
-      sel[0] = b - 1;
-      sel[1] = (int)(k - gt);
     }
     __syncthreads();
     tau = sel[0];
@@ -288,7 +312,7 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
 #pragma unroll
     for (int e = 0; e < E; ++e) ties += (key[e] == tau) ? 1 : 0;
     int tie_total;
-    const int tr = block_exclusive_scan<NT>(ties, scan, tie_total);
+    const int tr = block_scan_once<NT>(ties, scan[1], tie_total);
     if (tr < r && r <= tr + ties) {  // exactly one thread holds the r-th tie
       int n = tr, at = 0;
 #pragma unroll
@@ -298,10 +322,10 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
           if (n == r) at = (int)(k0 + e);
         }
       }
-      sel[0] = at;
+      sel[2] = at;
     }
     __syncthreads();
-    istar = sel[0];
+    istar = sel[2];
   }
   if (cut != nullptr && tid == 0) {
     cut[2 * row] = tau;
@@ -334,7 +358,7 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
       }
     }
     int kept;
-    int pos = block_exclusive_scan<NT>(__popcll(bits), scan, kept);
+    int pos = block_scan_once<NT>(__popcll(bits), scan[2], kept);
     int32_t* sidx = hist;
     uint16_t* sval = reinterpret_cast<uint16_t*>(hist + NT * E);
 #pragma unroll
@@ -352,7 +376,7 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
     }
   } else {
     int base = 0;
-    compact_run<NT, E>(bits, v, k0, d, base, scan, ir, vr, mr);
+    compact_run<NT, E>(bits, v, k0, d, base, scan[2], ir, vr, mr);
   }
   if (tid == 0) nnz[row] = (int32_t)k;
 }
