@@ -207,22 +207,24 @@ __global__ __launch_bounds__(NT) void k_sparsify_scored(
 }
 
 // Exactly k survivors per row: the k largest magnitudes, ties to the lower
-// index (fp16 magnitudes compared exactly as 15-bit keys; -0 == +0).  One LDS
-// bin per key value (2^15 bins, 128 KB): a single pass of LDS atomics counts
-// every key; each thread then owns 32 consecutive keys' bins, and a workgroup
-// scan of the threads' sums, read from the top, finds the thread and then the
-// bin where the count of larger keys reaches k.  The bins of one thread are
-// stored as 8 int4 a workgroup-width apart (bin address below), so that the
-// threads of a wave read 64 consecutive int4 at a time, free of LDS bank
-// conflicts; stored contiguously, the 128-byte stride between threads put
-// every lane of a wave on the same four banks.  That bin is tau, the k-th
-// largest key, with r = k - #(keys > tau) of its entries still to keep; a
-// scan of the threads' counts of keys equal to tau, in index order, finds
-// the r-th of them, at index i*.  Entry i survives iff key_i > tau, or
-// key_i == tau and i <= i* (k = 0: tau = 2^15, i* = -1, nothing survives).
-// Outputs: the pair (tau, i*) per row in `cut` (may be NULL), the bitmask,
-// and the compacted list (staged in LDS for d <= NT * 16, so it leaves in
-// coalesced stores).  One workgroup per row; each thread keeps E keys.
+// index (fp16 magnitudes compared exactly as 15-bit keys; -0 == +0).
+//  1. One LDS bin per key value (2^15 bins, 128 KB); a single pass of LDS
+//     atomics counts every key.
+//  2. Each thread owns 32 consecutive keys' bins.  A workgroup scan of the
+//     threads' sums, read from the top, finds the thread, and its wave the
+//     bin, where the count of larger keys reaches k: that bin is tau, the
+//     k-th largest key, and r = k - #(keys > tau) of its entries survive.
+//     A thread's bins are stored as int4 runs a workgroup-width apart (bin
+//     address below), so a wave reads 64 consecutive int4 at a time, free
+//     of LDS bank conflicts (contiguous runs would put the 128-byte stride
+//     between threads, and so a whole wave, on the same four banks).
+//  3. i* is the index of the r-th entry equal to tau in index order, found
+//     by a scan of the threads' counts of such entries.
+// Entry i survives iff key_i > tau, or key_i == tau and i <= i* (k = 0:
+// tau = 2^15, i* = -1, nothing survives).  Outputs: the pair (tau, i*) per
+// row in `cut` (may be NULL), the bitmask, and the compacted list (staged in
+// LDS for d <= NT * 16, so it leaves in coalesced stores).  One workgroup
+// per row; each thread keeps E keys.
 constexpr int kTopkBins = 1 << 15;
 
 // LDS word of key `key`'s bin: thread t = key / BPT owns the int4 runs
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
   __shared__ int scan[3][NT / kWave];             // one per block scan
   __shared__ int sel[3];                          // tau, ties to keep, i*
   constexpr int BPT = kTopkBins / NT;  // bins per thread
-  static_assert(BPT % 4 == 0 && kTopkBins % NT == 0 && BPT <= 32, "bins split into int4 runs");
+  static_assert(BPT % 4 == 0 && kTopkBins % NT == 0 && BPT <= kWave, "bins split into int4 runs");
   const int tid = (int)threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * d;
@@ -296,8 +298,7 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
       const int lane = lane_id();
       const int jb = BPT - 1 - (lane & (BPT - 1));
       const int cb = lane < BPT ? hist[topk_bin<NT, BPT>(ts * BPT + jb)] : 0;
-      int sc = row16_inclusive_scan(cb);
-      if constexpr (BPT > 16) sc += (lane >> 4) == 1 ? __builtin_amdgcn_readlane(sc, 15) : 0;
+      const int sc = BPT <= 16 ? row16_inclusive_scan(cb) : wave_inclusive_scan(cb);
       const uint64_t hit = __ballot(lane < BPT && ab + sc >= kk);
       const int l = __builtin_ctzll(hit);
       if (lane == l) {
@@ -306,8 +307,8 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
       }
     }
     __syncthreads();
-    tau = sel[0];
-    const int r = sel[1];  // >= 1
+    tau = __builtin_amdgcn_readfirstlane(sel[0]);
+    const int r = __builtin_amdgcn_readfirstlane(sel[1]);  // >= 1
     int ties = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) ties += (key[e] == tau) ? 1 : 0;
@@ -381,14 +382,10 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
   if (tid == 0) nnz[row] = (int32_t)k;
 }
 
-// N:M: each thread owns 8 consecutive entries (one 16-byte load).  An entry
-// is kept iff fewer than n entries of its group rank before it, where j
-// ranks before i iff |x_j| > |x_i|, or they are equal and j < i.  For
-// M <= 8 the groups are local and ranked pairwise.  For M = 16 / 32 the M/8
-// threads of a group find the n-th largest 15-bit magnitude key tau by a
-// bitwise binary search (15 steps, each a count of keys >= a candidate,
-// summed over the group with cross-lane shuffles), keep every key > tau and
-// the first n - #(> tau) keys equal to tau in index order.  The flattened
+// N:M, M <= 8: each thread owns 8 consecutive entries (one 16-byte load),
+// so its groups are its own.  An entry is kept iff fewer than n entries of
+// its group rank before it, where j ranks before i iff |x_j| > |x_i|, or
+// they are equal and j < i; the ranks are counted pairwise.  The flattened
 // array is a sequence of groups because d % M == 0 and d % 32 == 0.
 // Every group yields exactly n values, so a workgroup's 2048 entries give a
 // fixed, contiguous run of 2048*n/M outputs: the kept values are placed in
@@ -405,50 +402,6 @@ __device__ __forceinline__ int quad_perm(int v) {
 }
 constexpr int kQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
 constexpr int kQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
-constexpr int kQuadXor3 = 3 | (2 << 2) | (1 << 4) | (0 << 6);
-
-// Selection helpers on a lane's 8 keys (descending order = index order).
-// Batcher's odd-even merge sort network for 8 (19 comparators).
-__device__ __forceinline__ void nm_cx(int (&k)[8], int i, int j) {
-  const int a = k[i], b = k[j];
-  k[i] = a > b ? a : b;
-  k[j] = a > b ? b : a;
-}
-__device__ __forceinline__ void nm_sort8(int (&k)[8]) {
-  nm_cx(k, 0, 1); nm_cx(k, 2, 3); nm_cx(k, 4, 5); nm_cx(k, 6, 7);
-  nm_cx(k, 0, 2); nm_cx(k, 1, 3); nm_cx(k, 4, 6); nm_cx(k, 5, 7);
-  nm_cx(k, 1, 2); nm_cx(k, 5, 6);
-  nm_cx(k, 0, 4); nm_cx(k, 1, 5); nm_cx(k, 2, 6); nm_cx(k, 3, 7);
-  nm_cx(k, 2, 4); nm_cx(k, 3, 5);
-  nm_cx(k, 1, 2); nm_cx(k, 3, 4); nm_cx(k, 5, 6);
-}
-// A bitonic sequence of 8 into descending order (distances 4, 2, 1).
-__device__ __forceinline__ void nm_half_clean(int (&k)[8]) {
-  nm_cx(k, 0, 4); nm_cx(k, 1, 5); nm_cx(k, 2, 6); nm_cx(k, 3, 7);
-  nm_cx(k, 0, 2); nm_cx(k, 1, 3); nm_cx(k, 4, 6); nm_cx(k, 5, 7);
-  nm_cx(k, 0, 1); nm_cx(k, 2, 3); nm_cx(k, 4, 5); nm_cx(k, 6, 7);
-}
-// Compare slot i with slot 7 - i (REV) or slot i of the lane CTRL names;
-// the lane holding the earlier part of the sequence keeps the larger key.
-template <int CTRL, bool REV>
-__device__ __forceinline__ void nm_exchange(int (&k)[8], bool keep_max) {
-  int p[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = quad_perm<CTRL>(k[REV ? 7 - i : i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int hi = k[i] > p[i] ? k[i] : p[i];
-    const int lo = k[i] > p[i] ? p[i] : k[i];
-    k[i] = keep_max ? hi : lo;
-  }
-}
-
-// lane q of each aligned group of G (G = 2 or 4) lanes, to every lane of it
-template <int G, int Q>
-constexpr int quad_bcast() {
-  return G == 4 ? Q * 0x55 : (Q | (Q << 2) | ((2 + Q) << 4) | ((2 + Q) << 6));
-}
-
 template <int M>
 __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __restrict__ x,
                                                             int64_t n8, int n,
@@ -472,111 +425,28 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
 #pragma unroll
   for (int i = 0; i < 8; ++i) key[i] = mag_key(v[i]);
 
+  static_assert(M <= 8, "groups within a thread");
   uint32_t keep = 0;
-  if constexpr (M <= 8) {
-    constexpr int GPT = 8 / M;
+  constexpr int GPT = 8 / M;
 #pragma unroll
-    for (int gi = 0; gi < GPT; ++gi) {
+  for (int gi = 0; gi < GPT; ++gi) {
 #pragma unroll
-      for (int i = 0; i < M; ++i) {
-        const int p = gi * M + i;
-        int rank = 0;
+    for (int i = 0; i < M; ++i) {
+      const int p = gi * M + i;
+      int rank = 0;
 #pragma unroll
-        for (int j = 0; j < M; ++j) {
-          const int q = gi * M + j;
-          rank += (key[q] > key[p] || (key[q] == key[p] && j < i)) ? 1 : 0;
-        }
-        if (rank < n) keep |= 1u << p;
+      for (int j = 0; j < M; ++j) {
+        const int q = gi * M + j;
+        rank += (key[q] > key[p] || (key[q] == key[p] && j < i)) ? 1 : 0;
       }
-      // local group index gi of thread tid -> slots (tid*GPT + gi)*n ...
-      if (active) {
-        int slot = (tid * GPT + gi) * n;
-#pragma unroll
-        for (int i = 0; i < M; ++i)
-          if ((keep >> (gi * M + i)) & 1u) outs[slot++] = v[gi * M + i];
-      }
+      if (rank < n) keep |= 1u << p;
     }
-  } else {
-    constexpr int G = M / 8;  // threads per group, aligned lane runs
-    const int gl = lane & (G - 1);
-    static_assert(G == 2 || G == 4, "groups within a lane quad");
-    auto group_sum = [&](int c) {
-      c += quad_perm<kQuadXor1>(c);
-      if constexpr (G == 4) c += quad_perm<kQuadXor2>(c);
-      return c;
-    };
-    // exclusive prefix over the group's lanes of a per-lane count
-    auto group_prefix = [&](int x) {
-      int e = 0;
-      const int x0 = quad_perm<quad_bcast<G, 0>()>(x);
-      e += gl > 0 ? x0 : 0;
-      if constexpr (G == 4) {
-        const int x1 = quad_perm<quad_bcast<G, 1>()>(x);
-        const int x2 = quad_perm<quad_bcast<G, 2>()>(x);
-        e += gl > 1 ? x1 : 0;
-        e += gl > 2 ? x2 : 0;
-      }
-      return e;
-    };
-    // tau = the group's n-th largest key.  Each lane sorts its 8 keys, the
-    // group's lanes merge them with bitonic steps across lanes (DPP), so the
-    // group's M keys lie in descending order along (lane, slot); tau is
-    // entry n - 1: slot (n-1) % 8 of lane (n-1) / 8 (n is uniform).  A
-    // bisection over the 15 key bits gives the same tau with a dependency
-    // chain ~5x longer (measured at 2048 x 4096: 13.1 against 9.1 us at
-    // 8:16, 14.0 against 11.5 us at 16:32).
-    int sk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sk[i] = key[i];
-    nm_sort8(sk);
-    nm_exchange<kQuadXor1, true>(sk, (gl & 1) == 0);
-    nm_half_clean(sk);
-    if constexpr (G == 4) {
-      nm_exchange<kQuadXor3, true>(sk, gl < 2);
-      nm_exchange<kQuadXor1, false>(sk, (gl & 1) == 0);
-      nm_half_clean(sk);
-    }
-    const int r = n - 1;  // 0 <= r < M (checked on the host)
-    int pick = sk[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) pick = (r & 7) == i ? sk[i] : pick;
-    int tau;
-    if constexpr (G == 2) {
-      const int b0 = quad_perm<quad_bcast<2, 0>()>(pick);
-      const int b1 = quad_perm<quad_bcast<2, 1>()>(pick);
-      tau = (r >> 3) == 0 ? b0 : b1;
-    } else {
-      const int b0 = quad_perm<quad_bcast<4, 0>()>(pick);
-      const int b1 = quad_perm<quad_bcast<4, 1>()>(pick);
-      const int b2 = quad_perm<quad_bcast<4, 2>()>(pick);
-      const int b3 = quad_perm<quad_bcast<4, 3>()>(pick);
-      const int q = r >> 3;
-      tau = q == 0 ? b0 : (q == 1 ? b1 : (q == 2 ? b2 : b3));
-    }
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      gt += key[i] > tau ? 1 : 0;
-      eq += key[i] == tau ? 1 : 0;
-    }
-    const int need = n - group_sum(gt);  // ties at tau still to keep
-    int e = group_prefix(eq);             // ties at tau in lower lanes of the group
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (key[i] > tau) {
-        keep |= 1u << i;
-      } else if (key[i] == tau) {
-        if (e < need) keep |= 1u << i;
-        ++e;
-      }
-    }
-    // kept entries in lower lanes of the group come first
-    const int pre = group_prefix(__popc(keep));
+    // local group index gi of thread tid -> slots (tid*GPT + gi)*n ...
     if (active) {
-      int slot = (tid / G) * n + pre;
+      int slot = (tid * GPT + gi) * n;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if ((keep >> i) & 1u) outs[slot++] = v[i];
+      for (int i = 0; i < M; ++i)
+        if ((keep >> (gi * M + i)) & 1u) outs[slot++] = v[gi * M + i];
     }
   }
   // four neighbouring threads (a lane quad) make one 32-bit mask word
@@ -596,6 +466,203 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
       *reinterpret_cast<u32x4*>(dst + 8 * i) = *reinterpret_cast<const u32x4*>(outs + 8 * i);
   } else {
     for (int i = tid; i < count; i += kNmThreads) dst[i] = outs[i];
+  }
+}
+
+// N:M, M = 16 / 32: each thread takes two consecutive groups A and B whole
+// (2M entries, M/4 16-byte loads) and works on both at once: entry i of A
+// and entry i of B share one 32-bit register, A in the low half, so each
+// compare-exchange of a sorting network over the M registers is one packed
+// 16-bit max and one packed min for the two groups.  Batcher's odd-even
+// merge sort puts each group's 15-bit magnitude keys in descending order;
+// tau, the n-th largest, is entry n - 1.  The keys >= tau (one packed
+// subtraction and its sign bits per register) are exactly the survivors
+// unless ties at tau make more than n of them; then the surplus ties with
+// the highest positions are dropped (ties go to the lower position).  The
+// kept values are placed in LDS at their slots (group g's n outputs start
+// at g * n) and leave in 16-byte stores, as above.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+constexpr int kNmPkThreads = 256;
+constexpr int kNmPkBlocksPerCu = 4;  // workgroups of the grid per compute unit
+
+__device__ __forceinline__ uint32_t pk_bits(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ u16x2 pk_vec(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+
+// Descending sort of N packed pairs, both halves at once (Batcher's
+// odd-even merge sort: N = 16 takes 63 compare-exchanges, N = 32 takes 191).
+template <int N>
+__device__ __forceinline__ void pk_sort_desc(u16x2 (&s)[N]) {
+#pragma unroll
+  for (int p = 1; p < N; p <<= 1) {
+#pragma unroll
+    for (int k = p; k >= 1; k >>= 1) {
+#pragma unroll
+      for (int j = k % p; j + k < N; j += 2 * k) {
+#pragma unroll
+        for (int i = 0; i < k; ++i) {
+          const int a = i + j, b = i + j + k;
+          if (b < N && a / (2 * p) == b / (2 * p)) {
+            const u16x2 x = s[a], y = s[b];
+            s[a] = __builtin_elementwise_max(x, y);
+            s[b] = __builtin_elementwise_min(x, y);
+          }
+        }
+      }
+    }
+  }
+}
+
+// The survivors of one group (half h of the packed keys) when more than n
+// keys reach tau: every key above tau, then the ties in position order.
+// Packed keys of entries 2j (sel 0x05040100) or 2j + 1 (sel 0x07060302)
+// of A (low half) and B (high half), from the raw fp16 words.
+__device__ __forceinline__ uint32_t nm_pk_key(uint32_t wa, uint32_t wb, uint32_t sel) {
+  return __builtin_amdgcn_perm(wb, wa, sel) & 0x7fff7fffu;
+}
+
+template <int M>
+__device__ __forceinline__ uint32_t nm_pk_ties(const uint32_t (&w)[M / 2], uint32_t tau,
+                                               uint32_t ge, int n) {
+  uint32_t gt = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) gt |= (((w[i / 2] >> (16 * (i & 1))) & 0x7fffu) > tau ? 1u : 0u) << i;
+  uint32_t ties = ge & ~gt;
+  for (int drop = __popc(ge) - n; drop > 0; --drop) ties &= ~(1u << (31 - __clz(ties)));
+  return gt | ties;
+}
+
+// One block of 2 * kNmPkThreads groups: thread tid takes groups 2 tid and
+// 2 tid + 1 of it, whose raw fp16 words are wa and wb.
+template <int M>
+__device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const uint32_t (&wb)[M / 2],
+                                            int64_t blk, int64_t ngroups, int n,
+                                            uint32_t* __restrict__ mask,
+                                            uint16_t* __restrict__ val, int vec_out,
+                                            uint16_t* outs) {
+  constexpr int W = M / 2;
+  constexpr int64_t kGroups = kNmPkThreads * 2;
+  const int tid = (int)threadIdx.x;
+  const int64_t ga = blk * kGroups + 2 * tid;
+  const bool has_a = ga < ngroups, has_b = ga + 1 < ngroups;
+  // packed keys: entry i of A (low half) and of B (high half)
+  u16x2 sk[M];
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    sk[2 * j] = pk_vec(nm_pk_key(wa[j], wb[j], 0x05040100u));
+    sk[2 * j + 1] = pk_vec(nm_pk_key(wa[j], wb[j], 0x07060302u));
+  }
+  pk_sort_desc<M>(sk);
+  const int r = n - 1;  // 0 <= r < M (checked on the host); uniform
+  u16x2 tv = sk[0];
+#pragma unroll
+  for (int i = 1; i < M; ++i) tv = r == i ? sk[i] : tv;
+  // Key i of A / B below its group's tau: sign bit 15 / 31 of the packed
+  // difference.  Shifting it right by 15 - (i % 16) puts A's bit at
+  // i % 16 and B's at 16 + i % 16; entries 16..31 gather in a second word.
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const uint32_t kp = nm_pk_key(wa[i / 2], wb[i / 2], (i & 1) ? 0x07060302u : 0x05040100u);
+    const uint32_t dd = pk_bits(pk_vec(kp) - tv);  // keys rebuilt: fewer live registers
+    const int j = i & 15;
+    if (i < 16)
+      lo |= (dd >> (15 - j)) & (0x10001u << j);
+    else
+      hi |= (dd >> (15 - j)) & (0x10001u << j);
+  }
+  const uint32_t lt_a = M == 16 ? lo & 0xffffu : (lo & 0xffffu) | (hi << 16);
+  const uint32_t lt_b = M == 16 ? lo >> 16 : (lo >> 16) | (hi & 0xffff0000u);
+  constexpr uint32_t kAll = M == 32 ? 0xffffffffu : 0xffffu;
+  uint32_t keep_a = ~lt_a & kAll, keep_b = ~lt_b & kAll;
+  const uint32_t tb = pk_bits(tv);
+  if (__popc(keep_a) > n) keep_a = nm_pk_ties<M>(wa, tb & 0xffffu, keep_a, n);
+  if (__popc(keep_b) > n) keep_b = nm_pk_ties<M>(wb, tb >> 16, keep_b, n);
+
+  if (has_a) {
+    // every entry is stored: a kept one at its slot, a dropped one at this
+    // thread's spare slot past the outputs (no branch per entry)
+    // (slot - spare masked by 0 or -1, the entry's bit sign-extended)
+    const int spare = (int)kGroups * M + tid;
+    int sa = tid * 2 * n - spare, sb = sa + n;  // next slot of A / B, from spare
+    const uint32_t kb = has_b ? keep_b : 0u;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int m = (int)(keep_a << (31 - i)) >> 31;
+      outs[spare + (sa & m)] = (uint16_t)(wa[i / 2] >> (16 * (i & 1)));
+      sa -= m;
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int m = (int)(kb << (31 - i)) >> 31;
+      outs[spare + (sb & m)] = (uint16_t)(wb[i / 2] >> (16 * (i & 1)));
+      sb -= m;
+    }
+    if constexpr (M == 16) {
+      mask[ga >> 1] = keep_a | (keep_b << 16);  // the pair's 32 entries
+    } else {
+      mask[ga] = keep_a;
+      if (has_b) mask[ga + 1] = keep_b;
+    }
+  }
+  __syncthreads();
+  const int64_t first = blk * kGroups;  // the block's first group
+  const int64_t ng = (ngroups - first) < kGroups ? (ngroups - first) : kGroups;
+  const int count = (int)ng * n;
+  uint16_t* dst = val + first * n;
+  if (vec_out && (count % 8) == 0) {
+    for (int i = tid; i < count / 8; i += kNmPkThreads)
+      *reinterpret_cast<u32x4*>(dst + 8 * i) = *reinterpret_cast<const u32x4*>(outs + 8 * i);
+  } else {
+    for (int i = tid; i < count; i += kNmPkThreads) dst[i] = outs[i];
+  }
+  __syncthreads();  // outs is rewritten by the next block
+}
+
+template <int M>
+__global__ __launch_bounds__(kNmPkThreads) void k_sparsify_nm_pk(const uint16_t* __restrict__ x,
+                                                               int64_t ngroups, int n,
+                                                               uint32_t* __restrict__ mask,
+                                                               uint16_t* __restrict__ val,
+                                                               int vec_out) {
+  static_assert(M == 16 || M == 32, "two whole groups per thread");
+  constexpr int W = M / 2;                       // 32-bit words of one group
+  constexpr int64_t kGroups = kNmPkThreads * 2;  // groups of one block
+  __shared__ __align__(16) uint16_t outs[kGroups * M + kNmPkThreads];  // + a spare slot each
+  const int tid = (int)threadIdx.x;
+  const int64_t nblk = (ngroups + kGroups - 1) / kGroups;
+  // A workgroup walks blocks blockIdx.x, + gridDim.x, ...; the next block's
+  // loads are issued before the current one is worked on, so HBM stays busy
+  // while the sorts run.  Two register sets take turns (no copies).
+  // Groups past the end read the last group instead (their results are
+  // not stored): every load is unconditional.
+  auto load = [&](int64_t blk, uint32_t (&ra_)[W], uint32_t (&rb_)[W]) {
+    const int64_t ga = blk * kGroups + 2 * tid;
+    const u32x4* sa = reinterpret_cast<const u32x4*>(x + (ga < ngroups ? ga : ngroups - 1) * M);
+    const u32x4* sb =
+        reinterpret_cast<const u32x4*>(x + (ga + 1 < ngroups ? ga + 1 : ngroups - 1) * M);
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const u32x4 ra = sa[q];
+      const u32x4 rb = sb[q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        ra_[4 * q + c] = ra[c];
+        rb_[4 * q + c] = rb[c];
+      }
+    }
+  };
+  const int64_t step = gridDim.x;
+  uint32_t a0[W], b0[W], a1[W], b1[W];
+  int64_t blk = blockIdx.x;
+  if (blk < nblk) load(blk, a0, b0);
+  while (blk < nblk) {
+    if (blk + step < nblk) load(blk + step, a1, b1);
+    nm_pk_block<M>(a0, b0, blk, ngroups, n, mask, val, vec_out, outs);
+    blk += step;
+    if (blk >= nblk) break;
+    if (blk + step < nblk) load(blk + step, a0, b0);
+    nm_pk_block<M>(a1, b1, blk, ngroups, n, mask, val, vec_out, outs);
+    blk += step;
   }
 }
 
@@ -762,25 +829,30 @@ hipError_t launch_sparsify_nm_shared(const uint16_t* x, int64_t rows, int64_t d,
 
 hipError_t launch_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n, int m,
                               uint32_t* mask, uint16_t* val, hipStream_t s) {
+  // whole runs are 16-byte aligned when the output base is (each
+  // workgroup's run is a multiple of 8 values at every supported n / m)
+  const int vec = (reinterpret_cast<uintptr_t>(val) & 15u) == 0 ? 1 : 0;
+  if (m == 16 || m == 32) {
+    const int64_t ng = rows * d / m;
+    const int64_t nblk = (ng + 2 * kNmPkThreads - 1) / (2 * kNmPkThreads);
+    const int64_t cap = (int64_t)device_cus() * kNmPkBlocksPerCu;
+    const dim3 grid((unsigned)(nblk < cap ? nblk : cap));
+    if (m == 16)
+      hipLaunchKernelGGL(k_sparsify_nm_pk<16>, grid, dim3(kNmPkThreads), 0, s, x, ng, n, mask,
+                         val, vec);
+    else
+      hipLaunchKernelGGL(k_sparsify_nm_pk<32>, grid, dim3(kNmPkThreads), 0, s, x, ng, n, mask,
+                         val, vec);
+    return hipGetLastError();
+  }
   const int64_t n8 = rows * d / 8;
   const dim3 grid((unsigned)((n8 + kNmThreads - 1) / kNmThreads));
-  // whole runs are 16-byte aligned when the output base is (2048*n/M halves
-  // per workgroup is a multiple of 64)
-  const int vec = (reinterpret_cast<uintptr_t>(val) & 15u) == 0 ? 1 : 0;
   switch (m) {
     case 4:
       hipLaunchKernelGGL(k_sparsify_nm<4>, grid, dim3(kNmThreads), 0, s, x, n8, n, mask, val, vec);
       break;
     case 8:
       hipLaunchKernelGGL(k_sparsify_nm<8>, grid, dim3(kNmThreads), 0, s, x, n8, n, mask, val, vec);
-      break;
-    case 16:
-      hipLaunchKernelGGL(k_sparsify_nm<16>, grid, dim3(kNmThreads), 0, s, x, n8, n, mask, val,
-                         vec);
-      break;
-    case 32:
-      hipLaunchKernelGGL(k_sparsify_nm<32>, grid, dim3(kNmThreads), 0, s, x, n8, n, mask, val,
-                         vec);
       break;
     default:
       return hipErrorInvalidValue;
