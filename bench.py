@@ -668,12 +668,13 @@ def suite_rank_adapter(sa, syn, dev, ev_time, emit):
 
     d_out, d_in, r = 11008, 4096, 2048
     bt0, at0 = (torch.from_numpy(w).to(dev) for w in syn.rank_adapter_weights(d_out, d_in, r, 3000))
-    pair = (bt0.numel() + at0.numel()) * 2
+    b0 = bt0.t().contiguous()  # B [r][d_in], row-major
+    pair = (b0.numel() + at0.numel()) * 2
     n = max(2, -(-ROTATION_BYTES // pair))
-    # copy i permutes the rank index (B's rows and A's columns alike): other
-    # bytes in memory, the same adapter, mask size and y
-    rot = [(bt0, at0)] + [(torch.roll(bt0, 97 * i, 1).contiguous(),
-                           torch.roll(at0, 97 * i, 0).contiguous()) for i in range(1, n)]
+    # copy i permutes the rank index (B's rows and A's rows of A^T alike):
+    # other bytes in memory, the same adapter, mask size and y
+    rot = [(b0, at0)] + [(torch.roll(b0, 97 * i, 0).contiguous(),
+                          torch.roll(at0, 97 * i, 0).contiguous()) for i in range(1, n)]
     wt_gate = torch.from_numpy(syn.weight_t(d_out, d_in, syn.weight_seed("gate"))).to(dev)
     ng = max(2, -(-ROTATION_BYTES // (wt_gate.numel() * 2)))
     rot_g = [wt_gate] + [torch.roll(wt_gate, 997 * i, 0).contiguous() for i in range(1, ng)]
@@ -681,7 +682,7 @@ def suite_rank_adapter(sa, syn, dev, ev_time, emit):
     v = torch.empty((r,), dtype=torch.float16, device=dev)
     y = torch.empty((d_out,), dtype=torch.float16, device=dev)
     nr = len(rot)
-    sq = torch.sort(sa.rana_adapter_gemv(bt0, at0, x, 0.0)[0].double() ** 2).values
+    sq = torch.sort(sa.rana_adapter_gemv(b0, at0, x, 0.0)[0].double() ** 2).values
     for rate in (0.5, 0.7):
         k = int(rate * r)
         t = float(0.5 * (sq[k - 1] + sq[k]))

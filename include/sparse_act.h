@@ -325,21 +325,24 @@ int sparse_gemv_scored(const uint16_t* wt, int64_t d_out, int64_t d_in,
  * and the columns of A at the mask's zeros are skipped; Q4 (eqn. 9): the
  * masker squares B x element-wise and compares it with a threshold; Q2: one
  * plain GEMV for v = B x, one masked GEMV for A (m .* v).  Two launches on
- * `stream`: dense_gemv on B, then the masked GEMV on A with the mask decided
- * per workgroup from v as stored (fp16; its square is exact in fp32).
+ * `stream`: a dense GEMV on B in its own row-major layout (one wave per
+ * entry of v: each is one contiguous dot product, no workspace), then the
+ * masked GEMV on A^T with the mask decided per workgroup from v as stored
+ * (fp16; its square is exact in fp32).
  *
- *   bt [d_in][r] fp16: B^T (B is r x d_in), r % 8 == 0, 16-byte aligned
+ *   b  [r][d_in] fp16: B itself, row-major, 2-byte aligned (16-byte aligned
+ *      with d_in % 8 == 0 and x 16-byte aligned for 16-byte loads)
  *   at [r][d_out] fp16: A^T (A is d_out x r), d_out % 8 == 0, 16-byte aligned
  *   x  [batch][d_in] fp16, 2-byte aligned
  *   t  >= 0, finite: keep entry i iff v_i^2 >= t (t = 0 keeps every entry)
- *   v  [batch][r] fp16 out, 16-byte aligned: B x (the first GEMV's output)
+ *   v  [batch][r] fp16 out, 2-byte aligned: B x (the first GEMV's output)
  *   y  [batch][d_out] fp16 out, 16-byte aligned
- *   ws workspace of at least max(sa_workspace_bytes(r, d_in, batch),
- *      sa_workspace_bytes(d_out, r, batch)) bytes (both launches share it)
+ *   ws workspace of at least sa_workspace_bytes(d_out, r, batch) bytes (the
+ *      second GEMV's)
  * v must not overlap x or y.  With batch > 1 the rows of A in the union of
  * the rows' masks are read once for all rows.  Errors as sparse_gemv.
  */
-int rana_adapter_gemv(const uint16_t* bt, int64_t r, int64_t d_in,
+int rana_adapter_gemv(const uint16_t* b, int64_t r, int64_t d_in,
                       const uint16_t* at, int64_t d_out, const uint16_t* x,
                       int64_t batch, float t, uint16_t* v, uint16_t* y,
                       void* ws, size_t ws_bytes, void* stream);

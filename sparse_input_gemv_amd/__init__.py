@@ -319,7 +319,7 @@ def _gemv_out(wt, batch, squeeze, y):
 
 
 def _ret(y, squeeze):
-    return y[0] if squeeze else y
+    return y[0] if squeeze and y.dim() == 2 else y
 
 
 def sparse_gemv(wt: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, nnz: torch.Tensor,
@@ -438,25 +438,29 @@ def sparse_gemv_scored(wt: torch.Tensor, x: torch.Tensor, t: float,
     return _ret(y, True)
 
 
-def rana_adapter_gemv(bt: torch.Tensor, at: torch.Tensor, x: torch.Tensor, t: float,
+def rana_adapter_gemv(b: torch.Tensor, at: torch.Tensor, x: torch.Tensor, t: float,
                       v: torch.Tensor | None = None, y: torch.Tensor | None = None):
     """RaNA linear-layer rank adapter: ``v = B x``, ``y = A (m ⊙ v)`` with
-    ``m_i = v_i**2 >= t``; ``bt`` is ``B^T [d_in][r]``, ``at`` is
+    ``m_i = v_i**2 >= t``; ``b`` is ``B [r][d_in]`` (row-major), ``at`` is
     ``A^T [r][d_out]``.  Returns ``(v, y)``."""
-    _dev(bt, "bt", torch.float16)
+    _dev(b, "b", torch.float16)
     _dev(at, "at", torch.float16)
     _dev(x, "x", torch.float16)
     squeeze = x.dim() == 1
     batch, d_in = _rows(x)
-    r, d_out = bt.shape[1], at.shape[1]
-    if bt.shape[0] != d_in or at.shape[0] != r:
-        raise ValueError(f"shapes: bt {tuple(bt.shape)}, at {tuple(at.shape)}, x rows of {d_in}")
-    v = _gemv_out(bt, batch, squeeze, v)
+    r, d_out = b.shape[0], at.shape[1]
+    if b.shape[1] != d_in or at.shape[0] != r:
+        raise ValueError(f"shapes: b {tuple(b.shape)}, at {tuple(at.shape)}, x rows of {d_in}")
+    if v is None:
+        v = torch.empty((batch, r), dtype=torch.float16, device=b.device)
+    else:
+        _dev(v, "v", torch.float16)
+        if v.numel() < batch * r:
+            raise ValueError(f"v holds {v.numel()} values, {batch * r} needed")
     y = _gemv_out(at, batch, squeeze, y)
-    need = max(workspace_bytes(r, d_in, batch), workspace_bytes(d_out, r, batch))
-    ws = workspace(bt.device, need)
-    _check(lib().rana_adapter_gemv(_ptr(bt), r, d_in, _ptr(at), d_out, _ptr(x), batch, float(t),
-                                   _ptr(v), _ptr(y), _ptr(ws), ws.numel(), _stream(bt)),
+    ws = workspace(b.device, workspace_bytes(d_out, r, batch))
+    _check(lib().rana_adapter_gemv(_ptr(b), r, d_in, _ptr(at), d_out, _ptr(x), batch, float(t),
+                                   _ptr(v), _ptr(y), _ptr(ws), ws.numel(), _stream(b)),
            "rana_adapter_gemv")
     return _ret(v, squeeze), _ret(y, squeeze)
 

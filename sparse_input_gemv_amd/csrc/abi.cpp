@@ -317,38 +317,31 @@ int sparse_gemv_corrected(const uint16_t* wt, int64_t d_out, int64_t d_in, const
   return run_gemv(c, "sparse_gemv_corrected", stream);
 }
 
-int rana_adapter_gemv(const uint16_t* bt, int64_t r, int64_t d_in, const uint16_t* at,
+int rana_adapter_gemv(const uint16_t* b, int64_t r, int64_t d_in, const uint16_t* at,
                       int64_t d_out, const uint16_t* x, int64_t batch, float t, uint16_t* v,
                       uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
   sa::clear_error();
-  const int64_t b1 = batch < 1 ? 1 : batch;
-  const size_t n1 = sa::gemv_workspace_bytes(r, d_in, b1);
-  const size_t n2 = sa::gemv_workspace_bytes(d_out, r, b1);
-  const size_t need = n1 > n2 ? n1 : n2;
-  int st = sa::check_gemv_common(bt, r, d_in, batch, v, ws, ws_bytes, need);
+  const size_t need = sa::gemv_workspace_bytes(d_out, r, batch < 1 ? 1 : batch);
+  int st = sa::check_rows_gemv(b, r, d_in, batch, v, "rana_adapter_gemv");
   if (st == SA_OK) st = sa::check_gemv_common(at, d_out, r, batch, y, ws, ws_bytes, need);
   if (st == SA_OK) st = sa::check_activation(x, "rana_adapter_gemv: x");
   if (st == SA_OK) st = sa::check_threshold_value(t);
   if (st != SA_OK) return st;
-  sa::GemvCall c;
-  c.mode = sa::kModeDense;
-  c.wt = bt;
-  c.d_out = r;
-  c.d_in = d_in;
-  c.batch = (int)batch;
-  c.x = x;
-  c.y = v;
-  c.ws = ws;
-  c.ws_bytes = ws_bytes;
-  st = run_gemv(c, "rana_adapter_gemv", stream);
+  if (batch == 0) return SA_OK;
+  st = hip_status(sa::launch_gemv_rows(b, r, d_in, x, (int)batch, v, as_stream(stream)),
+                  "rana_adapter_gemv");
   if (st != SA_OK) return st;
+  sa::GemvCall c;
   c.mode = sa::kModeSquare;
   c.wt = at;
   c.d_out = d_out;
   c.d_in = r;
+  c.batch = (int)batch;
   c.x = v;
   c.t = t;
   c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
   return run_gemv(c, "rana_adapter_gemv", stream);
 }
 

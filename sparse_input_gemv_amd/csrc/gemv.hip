@@ -417,6 +417,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   const int tid = (int)threadIdx.x;
   const int oblk = (int)(blockIdx.x % (unsigned)p.go);
   const int kblk = (int)(blockIdx.x / (unsigned)p.go);
+  if ((int64_t)oblk * TILE_O >= p.d_out) return;  // a padding tile (whole workgroup)
   const int SL = p.slice;
   int tk_tau[B], tk_ist[B];  // Top-K mode: each row's cutoff, read with the other arguments
   if constexpr (MODE == kModeTopK) {
@@ -1372,6 +1373,93 @@ __global__ __launch_bounds__(256) void k_col_norms(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// dense GEMV on a row-major weight (the rank adapter's v = B x)
+// ---------------------------------------------------------------------------
+// One wave per output row: y[b][i] = sum_k W[i][k] x[b][k], W [d_out][d_in]
+// row-major.  Lane l takes the 8-column chunks l, l + 64, ..., U at a time
+// (16-byte loads of W and of each x row when VEC: d_in % 8 == 0 and 16-byte
+// aligned bases; 2-byte loads with bounds otherwise), multiplies with packed
+// fp16 dot products into fp32, and the wave's sum is taken with DPP row
+// shifts.  Every output is one wave's own dot product: no partial sums, no
+// hand-off, and each row's bytes are read once as contiguous 1 KB runs.
+template <int B, bool VEC>
+__global__ __launch_bounds__(256) void k_gemv_rows(const uint16_t* __restrict__ w, int64_t d_out,
+                                                   int64_t d_in, const uint16_t* __restrict__ x,
+                                                   int batch, uint16_t* __restrict__ y) {
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  constexpr int U = B <= 2 ? 8 : (B <= 4 ? 4 : 2);  // chunks in flight per lane
+  const int lane = lane_id();
+  const int64_t row = (int64_t)blockIdx.x * 4 + (int64_t)(threadIdx.x / kWave);
+  if (row >= d_out) return;  // the whole wave
+  const uint16_t* wr = w + row * d_in;
+  const int64_t nch = (d_in + 7) / 8;  // 8-column chunks of a row
+  float acc[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) acc[b] = 0.f;
+  for (int64_t c0 = 0; c0 < nch; c0 += (int64_t)kWave * U) {
+    u32x4 wv[U], xv[U][B];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + (int64_t)u * kWave + lane;
+      if constexpr (VEC) {
+        const int64_t cc = c < nch ? c : nch - 1;  // in range; its x is zeroed below
+        wv[u] = *reinterpret_cast<const u32x4*>(wr + cc * 8);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const int64_t bb = b < batch ? b : 0;
+          const u32x4 t = *reinterpret_cast<const u32x4*>(x + bb * d_in + cc * 8);
+          xv[u][b] = c < nch ? t : u32x4{0u, 0u, 0u, 0u};
+        }
+      } else {
+        uint32_t wq[4], xq[B][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t k0 = c * 8 + 2 * e, k1 = k0 + 1;
+          const uint32_t lo = k0 < d_in ? wr[k0] : 0u, hi = k1 < d_in ? wr[k1] : 0u;
+          wq[e] = lo | (hi << 16);
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const int64_t bb = b < batch ? b : 0;
+            const uint32_t xl = k0 < d_in ? x[bb * d_in + k0] : 0u;
+            const uint32_t xh = k1 < d_in ? x[bb * d_in + k1] : 0u;
+            xq[b][e] = xl | (xh << 16);
+          }
+        }
+        wv[u] = u32x4{wq[0], wq[1], wq[2], wq[3]};
+#pragma unroll
+        for (int b = 0; b < B; ++b) xv[u][b] = u32x4{xq[b][0], xq[b][1], xq[b][2], xq[b][3]};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // the elements go through scalars: a bit cast of a vector element
+          // taken in place would reinterpret element 0
+          const uint32_t we = wv[u][e], xe = xv[u][b][e];
+          acc[b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, we), __builtin_bit_cast(h2v, xe),
+                                          acc[b], false);
+        }
+  }
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    // wave sum: rows of 16 by DPP row shifts, then the four row totals
+    float s = acc[b];
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x111, 0xf, 0xf, true));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x112, 0xf, 0xf, true));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x114, 0xf, 0xf, true));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x118, 0xf, 0xf, true));
+    const float tot = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 15)) +
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 31))) +
+                      (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 47)) +
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63)));
+    if (lane == 0 && b < batch) y[(int64_t)b * d_out + row] = f2h(tot);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
@@ -1413,6 +1501,7 @@ size_t list_lds_bytes(int mode, int slice, int B) {
 struct Plan {
   int go, gk, slice;
   size_t smem;
+  int go_grid;  // output tiles of the grid: go, or go padded to a multiple of 8
 };
 
 }  // namespace
@@ -1545,6 +1634,7 @@ Plan plan_for(int mode, int tiling, int64_t d_out, int64_t d_in, int B, int64_t 
   if (red4 > red) red = red4;
   const size_t lst = list_lds_bytes(mode, pl.slice, B);
   pl.smem = lst > red ? lst : red;
+  pl.go_grid = pl.go;
   return pl;
 }
 
@@ -1624,7 +1714,7 @@ Plan make_plan(int mode, int tiling, int64_t d_out, int64_t d_in, int B) {
 hipError_t launch_split(KFn fn, int nt, const KParams& kp, const Plan& pl, hipStream_t s) {
   KParams arg = kp;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)(pl.go * pl.gk)),
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)(pl.go_grid * pl.gk)),
                          dim3(nt), args, pl.smem, s);
 }
 
@@ -1775,8 +1865,26 @@ Decision decide_gemv(int mode, int64_t d_out, int64_t d_in, int64_t batch, int64
   const bool l2_ok = d.pl.go % 8 == 0 && d.pl.gk <= kLocalMaxGk;
   const bool auto_one = B == 1 || (B == 2 && l2_ok && d.pl.gk <= kBatch2OneLaunchMaxGk);
   d.one_launch = d.pl.gk > 1 && (g_handoff == 0 ? auto_one : g_handoff >= 2);
+  // At batch 1 a tile count that is not a multiple of 8 is padded to one:
+  // the padding tiles' workgroups exit at once, and every slice of a real
+  // tile then shares one XCD too.  Only with at least 8 tiles (the padded
+  // count stays within the workspace's per-tile sums) and while the grid
+  // still fits one resident wave.
+  bool padded = false;
+  if (B == 1 && !l2_ok && d.pl.go >= 8 && d.pl.gk <= kLocalMaxGk && d.one_launch &&
+      g_handoff != 2) {
+    const int go8 = (d.pl.go + 7) / 8 * 8;
+    const int nt = kTilings[tiling].threads;
+    const int per = resident > 0 ? resident
+                                 : resident_per_cu(select_kernel(mode, tiling, B, true), nt,
+                                                   d.pl.smem);
+    if ((int64_t)go8 * d.pl.gk <= (int64_t)per * cus) {
+      d.pl.go_grid = go8;
+      padded = true;
+    }
+  }
   // partials kept in L2 when every slice of a tile runs on one XCD
-  d.local = d.one_launch && g_handoff != 2 && l2_ok;
+  d.local = d.one_launch && g_handoff != 2 && (l2_ok || padded);
   return d;
 }
 
@@ -1852,7 +1960,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   const bool local = dc.local;
   kp.tickets = one_launch ? reinterpret_cast<uint32_t*>(ws + L.ticket_off) : nullptr;
   kp.xcd_skew = g_test_hooks & 1;
-  kp.go = pl.go;
+  kp.go = pl.go_grid;
   kp.gk = pl.gk;
   kp.slice = pl.slice;
 
@@ -1861,6 +1969,32 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   const hipError_t e = launch_split(fn, kTilings[tiling].threads, kp, pl, s);
   if (e != hipSuccess || pl.gk == 1 || one_launch) return e;
   return launch_reduce(kp, pl, B, mode == kModeSwiglu && c.out_nnz != nullptr, s);
+}
+
+namespace {
+template <int B>
+void launch_rows_b(bool vec, dim3 grid, const uint16_t* w, int64_t d_out, int64_t d_in,
+                   const uint16_t* x, int batch, uint16_t* y, hipStream_t s) {
+  if (vec)
+    hipLaunchKernelGGL((k_gemv_rows<B, true>), grid, dim3(256), 0, s, w, d_out, d_in, x, batch, y);
+  else
+    hipLaunchKernelGGL((k_gemv_rows<B, false>), grid, dim3(256), 0, s, w, d_out, d_in, x, batch,
+                       y);
+}
+}  // namespace
+
+hipError_t launch_gemv_rows(const uint16_t* w, int64_t d_out, int64_t d_in, const uint16_t* x,
+                            int batch, uint16_t* y, hipStream_t s) {
+  const bool vec = (d_in % 8) == 0 && (reinterpret_cast<uintptr_t>(w) & 15u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+  const dim3 grid((unsigned)((d_out + 3) / 4));
+  switch (batch_pad(batch)) {
+    case 1: launch_rows_b<1>(vec, grid, w, d_out, d_in, x, batch, y, s); break;
+    case 2: launch_rows_b<2>(vec, grid, w, d_out, d_in, x, batch, y, s); break;
+    case 4: launch_rows_b<4>(vec, grid, w, d_out, d_in, x, batch, y, s); break;
+    default: launch_rows_b<8>(vec, grid, w, d_out, d_in, x, batch, y, s); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* out,

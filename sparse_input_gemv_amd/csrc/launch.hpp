@@ -86,6 +86,10 @@ constexpr size_t kGemvTicketBytes = (size_t)(524288 / kMinSplitTileO) * kTicketS
 size_t gemv_workspace_bytes(int64_t d_out, int64_t d_in, int64_t batch);
 // Offset in that workspace of SA_MAX_BATCH (tau, i*) pairs for sparse_gemv_topk.
 size_t gemv_workspace_cut_offset(int64_t d_out, int64_t d_in, int64_t batch);
+// Dense y[b] = W x[b] for a row-major W [d_out][d_in] (one wave per output;
+// no workspace).  batch in 1..8.
+hipError_t launch_gemv_rows(const uint16_t* w, int64_t d_out, int64_t d_in, const uint16_t* x,
+                            int batch, uint16_t* y, hipStream_t s);
 // Leading bytes of that workspace that must be zero before a call (and are
 // zero after it): the hand-off counters, the status word and the slots.
 size_t gemv_workspace_zero_bytes(int64_t d_out, int64_t d_in, int64_t batch);

@@ -195,6 +195,21 @@ int check_gemv_common(const void* wt, int64_t d_out, int64_t d_in, int64_t batch
   return SA_OK;
 }
 
+int check_rows_gemv(const void* w, int64_t d_out, int64_t d_in, int64_t batch, const void* y,
+                    const char* fn) {
+  REQUIRE(w != nullptr && y != nullptr, SA_ERR_INVALID_ARG, "%s: the weight and its output must not be NULL", fn);
+  REQUIRE(d_out >= 1 && d_out <= kMaxDOut, SA_ERR_INVALID_ARG,
+          "%s: the row-major weight's row count %lld is not in [1, %lld]", fn, (long long)d_out,
+          (long long)kMaxDOut);
+  REQUIRE(d_in >= 1 && d_in <= kMaxDIn, SA_ERR_INVALID_ARG, "%s: d_in = %lld out of range", fn,
+          (long long)d_in);
+  REQUIRE(batch >= 0 && batch <= SA_MAX_BATCH, SA_ERR_INVALID_ARG,
+          "%s: batch = %lld not in [0, %d]", fn, (long long)batch, SA_MAX_BATCH);
+  REQUIRE(aligned(w, 2) && aligned(y, 2), SA_ERR_INVALID_ARG,
+          "%s: the row-major weight and its output must be 2-byte aligned", fn);
+  return SA_OK;
+}
+
 int check_sparse_gemv(const void* idx, const void* val, const void* nnz, int64_t batch,
                       int64_t cap) {
   (void)batch;

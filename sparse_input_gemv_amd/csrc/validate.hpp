@@ -34,6 +34,9 @@ int check_calibrate(const void* samples, int64_t n, double s, const void* t_out)
 // GEMV family.  `need_ws` is the workspace the call requires.
 int check_gemv_common(const void* wt, int64_t d_out, int64_t d_in, int64_t batch,
                       const void* y, const void* ws, size_t ws_bytes, size_t need_ws);
+// A dense GEMV on a row-major weight [d_out][d_in] (no workspace).
+int check_rows_gemv(const void* w, int64_t d_out, int64_t d_in, int64_t batch, const void* y,
+                    const char* fn);
 int check_sparse_gemv(const void* idx, const void* val, const void* nnz, int64_t batch,
                       int64_t cap);
 int check_activation(const void* x, const char* name);

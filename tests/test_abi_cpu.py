@@ -240,11 +240,18 @@ def test_scored_gemv_checks(sa):
 
 
 def test_rana_adapter_checks(sa):
-    need = max(sa.sa_workspace_bytes(2048, 4096, 1), sa.sa_workspace_bytes(11008, 2048, 1))
+    # B is row-major and needs no workspace: only the second GEMV's counts
+    need = sa.sa_workspace_bytes(11008, 2048, 1)
     f = sa.rana_adapter_gemv
     ok = [P, 2048, 4096, P, 11008, P, 1, 0.5, P, P, P, need, None]
     args = list(ok)
-    args[1] = 2044  # r % 8
+    args[1] = 0  # r
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[0] = None  # b
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[0] = P + 1  # b misaligned
     assert f(*args) == SA_ERR_INVALID_ARG
     args = list(ok)
     args[4] = 11004  # d_out % 8
@@ -259,7 +266,7 @@ def test_rana_adapter_checks(sa):
     args[5] = None  # x
     assert f(*args) == SA_ERR_INVALID_ARG
     args = list(ok)
-    args[8] = P + 2  # v misaligned
+    args[8] = P + 1  # v misaligned
     assert f(*args) == SA_ERR_INVALID_ARG
     args = list(ok)
     args[6] = 0  # empty batch: nothing to do
@@ -324,9 +331,15 @@ def test_plan_headline_and_llama_shapes():
     assert _plan("threshold", 4096, 11008) == {"kernel": "split-K", "tile_o": 128, "grid_o": 32,
                                                "slices": 24, "handoff": 3}
     assert _plan("dense", 4096, 11008)["slices"] == 32
-    # 86 tiles are not a multiple of 8: the hand-off is written through
+    # 86 tiles are not a multiple of 8: at batch 1 the grid pads them to 88
+    # (the padding workgroups exit at once), so the partials stay in L2
     p = _plan("threshold", 11008, 4096)
-    assert (p["grid_o"], p["slices"], p["handoff"]) == (86, 8, 2)
+    assert (p["grid_o"], p["slices"], p["handoff"]) == (86, 8, 3)
+    assert _plan("threshold", 11008, 2048)["handoff"] == 3  # the rank adapter's A
+    assert _plan("threshold", 22016, 4096)["handoff"] == 3  # 172 tiles
+    # fewer than 8 tiles are not padded: written through
+    p = _plan("threshold", 640, 16384)
+    assert (p["kernel"], p["grid_o"], p["handoff"]) == ("split-K", 5, 2)
     # balance: 4 slices (688 workgroups, <= 3 per CU) rather than 5 (860, <= 4)
     assert _plan("threshold", 22016, 4096)["slices"] == 4
     assert _plan("dense", 22016, 4096)["slices"] == 4
@@ -339,7 +352,7 @@ def test_plan_headline_and_llama_shapes():
     assert _plan("threshold", 4096, 11008, 2)["handoff"] == 3
     assert _plan("threshold", 11008, 4096, 2)["handoff"] == 1  # 86 tiles
     assert _plan("dense", 1024, 4096, 2)["handoff"] == 1  # 32 slices
-    assert _plan("threshold", 11008, 4096, 1)["handoff"] == 2
+    assert _plan("threshold", 11008, 4096, 1)["handoff"] == 3
 
 
 def test_plan_small_weights():

@@ -709,7 +709,7 @@ def gpu_adapter_mask(bt, X, t):
     a kept entry has v^2 >= t > 0)."""
     r = bt.shape[1]
     eye = np.eye(r, dtype=np.float16)
-    v_g, y_g = sa.rana_adapter_gemv(dev(bt), dev(eye), dev(X), t)
+    v_g, y_g = sa.rana_adapter_gemv(dev(bt.T), dev(eye), dev(X), t)
     v, y = host(v_g).reshape(len(X), r), host(y_g).reshape(len(X), r)
     keep = y != 0
     assert np.array_equal(y[keep].view(np.uint16), v[keep].view(np.uint16))
@@ -753,7 +753,7 @@ def test_rana_adapter_small(r, d_in, d_out, batch):
     v16 = oracle_v16(bt, X)
     for rate in (0.0, 0.3, 0.5, 0.8, 1.0):
         t = gap_threshold(v16, rate)
-        v_g, y_g = sa.rana_adapter_gemv(dev(bt), dev(at), dev(X), t)
+        v_g, y_g = sa.rana_adapter_gemv(dev(bt.T), dev(at), dev(X), t)
         check_adapter(bt, at, X, t, v_g, y_g)
 
 
@@ -777,7 +777,7 @@ def test_rana_adapter_llama_gate(rate):
     bt, at = syn.rank_adapter_weights(11008, 4096, 2048, 3000)
     x = syn.activation((4096,), "gaussian", 7)[None]
     t = gap_threshold(oracle_v16(bt, x), rate)
-    v_g, y_g = sa.rana_adapter_gemv(dev(bt), dev(at), dev(x), t)
+    v_g, y_g = sa.rana_adapter_gemv(dev(bt.T), dev(at), dev(x), t)
     keep = check_adapter(bt, at, x, t, v_g, y_g)
     assert abs(int(keep.sum()) - round((1 - rate) * 2048)) <= 64
 
