@@ -10,8 +10,10 @@ rotates through distinct copies totalling >= 1 GiB so every step streams its
 kept columns from HBM rather than from the 256 MB Infinity Cache.
 
 Prints one JSON line (rank 0).  ``value`` is microseconds per step (lower is
-better); the roofline object gives the effective HBM bandwidth on the bytes
-the method must touch, against the 8 TB/s MI355X peak.
+better): the median of ten windows of --steps back-to-back steps each, every
+window between two HIP events on the launch stream (``windows`` gives the
+minimum and maximum).  The roofline object gives the effective HBM bandwidth
+on the bytes the method must touch, against the 8 TB/s MI355X peak.
 """
 
 from __future__ import annotations
@@ -37,6 +39,7 @@ ROTATION_BYTES = 1 << 30
 COPY_BYTES = 256 << 20
 GEMV_SOURCE = os.path.join(ROOT, "sparse_input_gemv_amd", "csrc", "gemv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_gemv_threshold_down_4096x11008.json")
+NUM_WINDOWS = 10  # timed windows of --steps steps each; the headline is their median
 
 
 def parse():
@@ -174,8 +177,8 @@ def main():
                     raise RuntimeError(L.sa_last_error().decode())
 
     def timed(calls_per_step, steps, warmup):
-        """ms per step in each of min(steps, 10) consecutive windows of the
-        timed steps (HIP events on the launch stream between the windows)."""
+        """ms per step in each of NUM_WINDOWS windows of `steps` steps (one
+        window of replays with --graph)."""
         run(calls_per_step, warmup)
         torch.cuda.synchronize()
         if args.graph:
@@ -198,22 +201,24 @@ def main():
             e1.record()
             torch.cuda.synchronize()
             return [e0.elapsed_time(e1) / (reps * per)]
-        nwin = max(1, min(steps, 10))
-        sizes = [steps // nwin + (1 if i < steps % nwin else 0) for i in range(nwin)]
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nwin + 1)]
-        torch.cuda.synchronize()
-        # The stream first runs a GPU-side wait, untimed, long enough for the
-        # host to enqueue every timed step behind it: the steps then run back
-        # to back, and the windows time the GPU, not the host's launch rate.
-        hold(2.0 + 0.03 * steps)
-        evs[0].record(stream)
-        done = 0
-        for i, n in enumerate(sizes):
-            run(calls_per_step, n, done)
-            done += n
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        return [evs[i].elapsed_time(evs[i + 1]) / sizes[i] for i in range(nwin)]
+        # Ten windows, each exactly `steps` steps between two HIP events on the
+        # launch stream.  Each window first runs a GPU-side wait, untimed,
+        # long enough for the host to enqueue every step of the window behind
+        # it: the steps then run back to back, and the window times the GPU,
+        # not the host's launch rate.  (Events between the steps of one window
+        # would add their own serialisation: ~1 us per event here.)
+        out, done = [], 0
+        for _ in range(NUM_WINDOWS):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            hold(2.0 + 0.03 * steps)
+            e0.record(stream)
+            run(calls_per_step, steps, done)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            done += steps
+            out.append(e0.elapsed_time(e1) / steps)
+        return out
 
     paths = {
         "fused": [[c] for c in fused],
@@ -267,7 +272,7 @@ def main():
             "algorithmic_bytes_per_launch": alg_bytes,
         },
         "windows": {
-            "n": len(wins[head]), "steps_each": args.steps // max(1, len(wins[head])),
+            "n": len(wins[head]), "steps_each": args.steps,
             "median_us": round(us, 3), "min_us": round(min(wins[head]) * 1000.0, 3),
             "max_us": round(max(wins[head]) * 1000.0, 3),
         },
