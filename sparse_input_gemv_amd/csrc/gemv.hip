@@ -275,8 +275,8 @@ __device__ __forceinline__ void store_coherent(T* p, T v) {
 // reset may stay in L2 as well.  The ticket checks the premise: with x its
 // XCD, every workgroup adds one arrival, x and x^2 in separate fields, and
 // the last one sees one XCD exactly when sum x = gk x_last and
-// sum x^2 = gk x_last^2 (zero variance); otherwise it writes NaN to its tile
-// rather than a sum of partials it cannot see.
+// sum x^2 = gk x_last^2 (zero variance); otherwise it cannot see the other
+// XCDs' partials and computes every slice of its tile itself (k_gemv).
 template <typename T>
 __device__ __forceinline__ void store_handoff(T* p, T v, int local) {
   if (local)

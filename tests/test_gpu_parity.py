@@ -161,6 +161,31 @@ def test_dense_gemv_matches_oracle():
         assert_close(y, np.stack([gemv.dense_gemv(wt, x[b]) for b in range(2)]))
 
 
+@pytest.mark.parametrize("d_out,d_in", [(11008, 4096), (22016, 4096), (11008, 2048),
+                                         (1032, 3000)])
+def test_padded_tile_plans(d_out, d_in):
+    """Batch 1 with a tile count that is not a multiple of 8: the grid pads
+    it (padding workgroups exit at once) and keeps the partials in L2.  The
+    result matches the oracle and the written-through form bit for bit."""
+    plan = sa.gemv_plan("threshold", d_out, d_in, 1)
+    assert plan["handoff"] == 3 and plan["grid_o"] % 8 != 0
+    wt = syn.weight_t(d_out, d_in, d_out + d_in)
+    x = syn.laplace_f16((d_in,), 1.0, 3)
+    t = 0.7
+    keep = sparsify.threshold_sparsify(x, t)[0]
+    wt_g, x_g = dev(wt), dev(x)
+    y_t = sa.sparse_gemv_threshold(wt_g, x_g, t)
+    y_d = sa.dense_gemv(wt_g, x_g)
+    assert_close(y_t, gemv.masked_gemv(wt, x, keep))
+    assert_close(y_d, gemv.dense_gemv(wt, x))
+    try:
+        sa.set_gemv_tuning(-1, 0, 2)
+        assert torch.equal(sa.sparse_gemv_threshold(wt_g, x_g, t), y_t)
+        assert torch.equal(sa.dense_gemv(wt_g, x_g), y_d)
+    finally:
+        sa.set_gemv_tuning(-1, 0, 0)
+
+
 def test_threshold_zero_reproduces_dense():
     wt = syn.weight_t(4096, 4096, 7)
     x = syn.gaussian_f16((4096,), 1.0, 8)
@@ -394,6 +419,34 @@ def test_nm_small(n, m):
     mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
     assert np.array_equal(words(mask_g), sparsify.pack_mask(keep))
     assert np.array_equal(host(val_g).view(np.uint16), vals.view(np.uint16))
+
+
+@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (1, 32), (31, 32), (5, 16)])
+@pytest.mark.parametrize("T,d", [(1, 32), (3, 96), (5, 160), (7, 2080), (33, 544)])
+def test_nm_ragged_group_counts(n, m, T, d):
+    """Group counts that leave a workgroup's last pair of groups half empty
+    (an odd number of 32-groups) or a short last block."""
+    X = syn.gaussian_f16((T, d), 1.0, T * d + m)
+    keep, vals = sparsify.nm_sparsify(X, n, m)
+    mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
+    assert np.array_equal(np.atleast_2d(words(mask_g)), sparsify.pack_mask(keep))
+    assert np.array_equal(np.atleast_2d(host(val_g)).view(np.uint16), vals.view(np.uint16))
+
+
+@pytest.mark.parametrize("n,m", [(8, 16), (5, 16), (16, 32), (3, 32)])
+def test_nm_multi_block(n, m):
+    """8192 x 4096: more blocks of groups than the grid has workgroups, so
+    each workgroup walks several blocks with its two register sets taking
+    turns.  Rows sampled across the whole array are checked against the
+    oracle (every row's groups are independent)."""
+    T, d = 8192, 4096
+    X = syn.gaussian_f16((T, d), 1.0, 77 + m)
+    X[5000, :] = np.float16(1.0)  # a row of ties
+    mask_g, val_g = sa.act_sparsify_nm(dev(X), n, m)
+    rows = np.unique(np.concatenate([np.arange(0, T, 97), [T - 1, 5000]]))
+    keep, vals = sparsify.nm_sparsify(X[rows], n, m)
+    assert np.array_equal(words(mask_g)[rows], sparsify.pack_mask(keep))
+    assert np.array_equal(host(val_g)[rows].view(np.uint16), vals.view(np.uint16))
 
 
 @pytest.mark.parametrize("n,m", [(1, 16), (3, 16), (8, 16), (15, 16), (1, 32), (7, 32),
@@ -745,7 +798,7 @@ def check_adapter(bt, at, X, t, v_g, y_g):
     return keep_ref
 
 
-@pytest.mark.parametrize("batch", [1, 2, 3])
+@pytest.mark.parametrize("batch", [1, 2, 3, 8])
 @pytest.mark.parametrize("r,d_in,d_out", [(136, 130, 72), (1024, 512, 264), (8, 33, 2056)])
 def test_rana_adapter_small(r, d_in, d_out, batch):
     bt, at = syn.rank_adapter_weights(d_out, d_in, r, r + d_in, std=0.1)
