@@ -567,7 +567,9 @@ enum {
  *   slices: input slices per output tile (1 for full-K);
  *   handoff: 0 none (one slice or full-K), 1 a second launch sums the
  *     partials, 2 the last workgroup of a tile sums them in the same launch,
- *     3 the same with the partials kept in L2.
+ *     3 the same with the partials kept in L2 (every slice of a tile on one
+ *     XCD: grid_o a multiple of 8, or at batch 1 a grid padded up to the
+ *     next multiple of 8 whose padding workgroups exit at once).
  * Returns SA_ERR_INVALID_ARG for an unknown op, a size out of range, a
  * negative count or a NULL output.
  */
