@@ -230,13 +230,13 @@ int sparse_gemv_topk(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint
   sa::clear_error();
   const size_t need = sa::gemv_workspace_bytes(d_out, d_in, batch < 1 ? 1 : batch);
   int st = sa::check_gemv_common(wt, d_out, d_in, batch, y, ws, ws_bytes, need);
-  if (st == SA_OK && batch == 0) return SA_OK;
-  int32_t* cut = st == SA_OK ? reinterpret_cast<int32_t*>(
-                                   static_cast<unsigned char*>(ws) +
-                                   sa::gemv_workspace_cut_offset(d_out, d_in, batch))
-                             : nullptr;
+  // the cutoff pairs live in the workspace (checked above when batch > 0)
+  int32_t* cut = (st == SA_OK && batch > 0)
+                     ? reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) +
+                                                  sa::gemv_workspace_cut_offset(d_out, d_in, batch))
+                     : nullptr;
   if (st == SA_OK) st = sa::check_topk_cutoff(x, batch, d_in, k, cut, "sparse_gemv_topk");
-  if (st != SA_OK) return st;
+  if (st != SA_OK || batch == 0) return st;
   st = hip_status(sa::launch_sparsify_topk(x, batch, d_in, k, nullptr, nullptr, nullptr, nullptr,
                                            0, cut, as_stream(stream)),
                   "sparse_gemv_topk");

@@ -76,6 +76,47 @@ def test_topk_checks(sa):
     assert f(P, 0, 16, 8, None, P, P, P, 8, None) == SA_OK
 
 
+def test_topk_cutoff_checks(sa):
+    f = sa.act_topk_cutoff  # (x, rows, d, k, cut, stream)
+    assert f(P, 1, 16, 17, P, None) == SA_ERR_INVALID_ARG  # k > d
+    assert f(P, 1, 16, -1, P, None) == SA_ERR_INVALID_ARG
+    assert f(P, 1, 16, 8, None, None) == SA_ERR_INVALID_ARG  # no output
+    assert f(P, 1, 16, 8, P + 4, None) == SA_ERR_INVALID_ARG  # cut not 8-byte aligned
+    assert f(P + 1, 1, 16, 8, P, None) == SA_ERR_INVALID_ARG  # x misaligned
+    assert f(P, 1, 70000, 8, P, None) == SA_ERR_UNSUPPORTED  # d > 65536
+    assert f(P, 0, 16, 8, None, None) == SA_OK  # empty call
+
+
+def test_sparse_gemv_topk_checks(sa):
+    # (wt, d_out, d_in, x, batch, k, y, ws, ws_bytes, stream)
+    f = sa.sparse_gemv_topk
+    need = sa.sparse_gemv_workspace_bytes(4096, 11008, 1)
+    ok = [P, 4096, 11008, P, 1, 5504, P, P, need, None]
+    args = list(ok)
+    args[5] = 11009  # k > d_in
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[5] = -1
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[3] = None  # x
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[8] = need - 1
+    assert f(*args) == SA_ERR_WORKSPACE
+    args = list(ok)
+    args[2] = 70000  # the select takes rows of at most 65536
+    args[8] = sa.sparse_gemv_workspace_bytes(4096, 70000, 1)
+    args[5] = 100
+    assert f(*args) == SA_ERR_UNSUPPORTED
+    args = list(ok)
+    args[4] = 0  # empty batch, arguments still checked
+    args[5] = 11009
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args[5] = 10
+    assert f(*args) == SA_OK
+
+
 def test_nm_checks(sa):
     f = sa.act_sparsify_nm
     assert f(P, 1, 64, 2, 6, P, P, None) == SA_ERR_INVALID_ARG  # m not supported
