@@ -523,15 +523,21 @@ int sa_set_gemv_test_hooks(int flags);
 /*
  * Process-wide matmul choices of dense_gemm / nm_act_spmm, for tuning sweeps
  * and cross-checks.
- *   tile_rows: 0 = automatic (dense: 256-row tiles when they give at least
- *     one workgroup per CU, else 128; 2:4: 128), or 128 / 256.
+ *   tile_rows: 0 = automatic (dense: 256 x 256 tiles where their rounds
+ *     over the CUs beat 256 x 128 tiles, else 256-row tiles when they give
+ *     at least one workgroup per CU, else 128; 2:4: 128), or 128 / 256
+ *     (128-column tiles of that height).
  *   engine: 0 = automatic, 1 = the staged-register engine, 2 = the
- *     pipelined engine (which applies when d_in is a multiple of its K
- *     step, 32 for dense and the expanded N:M patterns, 64 for 2:4, with
- *     16-byte aligned rows; other calls take the staged-register engine).
- *   stages: the pipelined engine's LDS stage count, 0 = automatic, or 3..6
- *     (loads run stages - 1 K steps ahead); a count whose stages exceed the
- *     160 KB of LDS for the tile is lowered to the most that fit.
+ *     pipelined engine with 128-column tiles, 3 = the pipelined engine with
+ *     256 x 256 tiles (dense and the expanded N:M patterns; 2:4 keeps
+ *     engine 2; tile_rows 0 or 256).  The pipelined engines apply when d_in
+ *     is a multiple of their K step, 32 for dense and the expanded N:M
+ *     patterns, 64 for 2:4, with 16-byte aligned rows; other calls take the
+ *     staged-register engine.
+ *   stages: the pipelined engine's LDS stage count, 0 = automatic (3 for
+ *     128-column tiles, 5 for 256 x 256), or 3..6 (loads run stages - 1 K
+ *     steps ahead); a count whose stages exceed the 160 KB of LDS for the
+ *     tile is lowered to the most that fit.
  * Every choice issues the same MFMA sequence per output element: identical
  * results.  Returns SA_ERR_INVALID_ARG for other values.  Not thread-safe.
  */

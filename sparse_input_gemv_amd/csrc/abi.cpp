@@ -558,8 +558,9 @@ int sa_set_gemv_test_hooks(int flags) {
 int sa_set_gemm_tuning(int tile_rows, int engine, int stages) {
   sa::clear_error();
   if (sa::gemm_set_tuning(tile_rows, engine, stages) != 0) {
-    sa::set_error("sa_set_gemm_tuning: tile_rows must be 0, 128 or 256 (got %d), engine 0, 1 "
-                  "or 2 (got %d) and stages 0 or 3..6 (got %d)", tile_rows, engine, stages);
+    sa::set_error("sa_set_gemm_tuning: tile_rows must be 0, 128 or 256 (got %d; 0 or 256 for "
+                  "engine 3), engine 0..3 (got %d) and stages 0 or 3..6 (got %d)", tile_rows,
+                  engine, stages);
     return SA_ERR_INVALID_ARG;
   }
   return SA_OK;

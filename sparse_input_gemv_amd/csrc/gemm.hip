@@ -819,6 +819,154 @@ __global__ __launch_bounds__(NTH, (pipe_wgs_per_cu<AK, BM, NS>())) void k_gemm_p
 }
 
 // ---------------------------------------------------------------------------
+// Wide dense engine (k_gemm_wide): 256 x 256 output tiles, eight waves of the
+// pipelined engine's 128 x 64 wave tile, K steps of 32 through NS stages of
+// 32 KB (A [256][32] and B [32][256], swizzled as in k_gemm_pipe; one
+// workgroup per CU).  A K step moves 32 KB into LDS for 4.2 MFLOP where the
+// 256 x 128 tile moves 24 KB for 2.1 MFLOP, so the load path -- what bounds
+// the pipelined engine -- carries a third less per FLOP, and the eight waves
+// on a CU share one set of barriers.  Every output block gets the same MFMA
+// sequence as in the other engines: identical results.
+// ---------------------------------------------------------------------------
+constexpr int WBM = 256, WBN = 256, WNT = 512;
+constexpr int kWideAHalves = WBM * BK;
+constexpr int kWideStageHalves = kWideAHalves + BK * WBN;
+constexpr int kWideLoadsPerWave = 4;  // two A and two B instructions of 1 KB
+constexpr int kWideMaxStages = 160 * 1024 / (2 * kWideStageHalves);
+static_assert(kWideMaxStages >= 3, "three wide stages must fit the LDS");
+
+// This wave's share of one K step's loads: A as 16 rows of 64 bytes and B as
+// 2 k rows of 512 bytes per instruction.  Rows past T and columns past d_out
+// read clamped (valid) addresses; their results are never stored.
+__device__ __forceinline__ void wide_issue(const GParams& p, int64_t m0, int64_t n0, int64_t k0,
+                                           uint16_t* S) {
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  uint16_t* As = S;
+  uint16_t* Bs = S + kWideAHalves;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rb = (w * 2 + i) * 16;
+    const int r = rb + lane / 4;
+    const int gc = (lane % 4) ^ swz_a(r);
+    int64_t row = m0 + r;
+    if (row >= p.T) row = p.T - 1;
+    load_to_lds16(p.x + row * p.d_in + k0 + 8 * gc, As + rb * BK);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int kb = (w * 2 + i) * 2;
+    const int k = kb + lane / 32;
+    const int gc = (lane % 32) ^ swz_b(k);
+    int64_t n = n0 + 8 * gc;
+    if (n >= p.d_out) n = p.d_out - 8;
+    load_to_lds16(p.wt + (k0 + k) * p.d_out + n, Bs + kb * WBN);
+  }
+}
+
+// b_quad on 256-column B rows.
+__device__ __forceinline__ s4v wide_b_quad(const uint16_t* Bs, int kq, int c0) {
+  const int lane = lane_id();
+  const int g = lane / 16, i = lane % 16;
+  const int k = kq + 8 * (g >> 1) + (i >> 2);
+  const int n = c0 + 16 * (g & 1) + 4 * (i & 3);
+  const uint16_t* ptr = Bs + k * WBN + 8 * ((n / 8) ^ swz_b(k)) + 4 * ((n / 4) & 1);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(SA_LDS4(ptr));
+}
+
+// One K step of a wave's 128 x 64 tile (pipe_compute's dense branch).
+__device__ __forceinline__ void wide_compute(const uint16_t* S, f16v (&acc)[4][2], int wm,
+                                             int wn) {
+  const int lane = lane_id();
+  const uint16_t* As = S;
+  const uint16_t* Bs = S + kWideAHalves;
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    h8 aop[4], bop[2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int m = wm * 128 + 32 * a + lane % 32;
+      const int q = 2 * kk + lane / 32;
+      aop[a] = *reinterpret_cast<const h8*>(As + m * BK + 8 * (q ^ swz_a(m)));
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int c0 = wn * 64 + 32 * b;
+      const s4v q0 = wide_b_quad(Bs, kk * 16, c0), q1 = wide_b_quad(Bs, kk * 16 + 4, c0);
+      typedef short s8v __attribute__((ext_vector_type(8)));
+      const s8v both = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+      bop[b] = __builtin_bit_cast(h8, both);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[a], bop[b], acc[a][b], 0, 0, 0);
+  }
+}
+
+template <int NS>
+__global__ __launch_bounds__(WNT, 1) void k_gemm_wide(GParams p) {
+  static_assert(NS >= 3 && NS <= kWideMaxStages, "wide stage count");
+  __shared__ __align__(16) uint16_t S[NS * kWideStageHalves];
+  const int lane = lane_id();
+  const int wave = (int)threadIdx.x / kWave;
+  const int wm = wave / 4, wn = wave % 4;
+  const int64_t mt = (p.T + WBM - 1) / WBM;
+  const int64_t ntl = (p.d_out + WBN - 1) / WBN;
+  int64_t mi, ni;
+  pipe_tile(blockIdx.x, mt, ntl, mi, ni);
+  const int64_t m0 = mi * WBM, n0 = ni * WBN;
+  f16v acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // the pipelined engine's K loop: loads D = NS - 1 steps ahead, a stage
+  // refilled only after the barrier that follows every wave's reads of it
+  constexpr int D = NS - 1;
+  const int64_t nk = p.d_in / BK;
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nk) wide_issue(p, m0, n0, j * BK, S + j * kWideStageHalves);
+  int64_t kt = 0;
+  for (; kt + NS + D - 1 < nk; kt += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      stage_barrier<(D - 1) * kWideLoadsPerWave>();
+      wide_issue(p, m0, n0, (kt + j + D) * BK, S + ((j + D) % NS) * kWideStageHalves);
+      wide_compute(S + j * kWideStageHalves, acc, wm, wn);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NS + D - 1; ++j) {
+    const int64_t t = kt + j;
+    if (t < nk) {
+      const int64_t later = nk - 1 - t;
+      stage_barrier_upto<kWideLoadsPerWave, D - 1>(later < D - 1 ? (int)later : D - 1);
+      if (t + D < nk)
+        wide_issue(p, m0, n0, (t + D) * BK, S + ((j + D) % NS) * kWideStageHalves);
+      wide_compute(S + (j % NS) * kWideStageHalves, acc, wm, wn);
+    }
+  }
+
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = n0 + wn * 64 + b * 32 + lane % 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 128 + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        if (row < p.T && col < p.d_out) p.y[row * p.d_out + col] = f2h(acc[a][b][r]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Tile-shared N:M engine.  Every 32-row block of tokens lies in one tile of
 // tt rows (tt a multiple of 32), so its rows share one N:M pattern; over one
 // K step the block's product is a dense MFMA product of the compressed values
@@ -1112,7 +1260,8 @@ hipError_t launch_nm_expand(const uint16_t* xval, const uint32_t* mask, int64_t 
 }
 
 int g_gemm_bm = 0;      // tuning override of the tile height: 0 = automatic, else 128 or 256
-int g_gemm_engine = 0;  // tuning override: 0 = automatic, 1 = staged-register engine, 2 = pipelined
+int g_gemm_engine = 0;  // tuning override: 0 = automatic, 1 = staged-register engine,
+                        // 2 = pipelined 256 x 128 / 128 x 128 tiles, 3 = wide (dense only)
 int g_gemm_stages = 0;  // tuning override of the pipelined stage count: 0 = automatic, else 3..6
 constexpr int kMaxStages = 6;
 
@@ -1131,12 +1280,50 @@ hipError_t launch_pipe_stages(const GParams& p, int64_t tiles, int ns, hipStream
   return hipGetLastError();
 }
 
+template <int NS = 3>
+hipError_t launch_wide_stages(const GParams& p, int64_t tiles, int ns, hipStream_t s) {
+  if constexpr (NS < kWideMaxStages) {
+    if (ns > NS) return launch_wide_stages<NS + 1>(p, tiles, ns, s);
+  }
+  hipLaunchKernelGGL((k_gemm_wide<NS>), dim3((unsigned)tiles), dim3(WNT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_wide(const GParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.T + WBM - 1) / WBM) * ((p.d_out + WBN - 1) / WBN);
+  if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
+  return launch_wide_stages(p, tiles, g_gemm_stages ? g_gemm_stages : kWideMaxStages, s);
+}
+
+// Wide or 256 x 128 tiles, from rates measured at K = 4096 (2048..8192 rows,
+// 4096..22016 outputs): a CU finishes one wide tile in ~115 us, and two
+// 256 x 128 tiles sharing it in ~150 us, i.e. the wide engine does ~1.29x
+// the work per CU.  But the wide engine runs in whole rounds of one tile per
+// CU, while the narrow engine's time grows about linearly with its tile
+// count (a CU's second slot refills as tiles finish).  So the wide engine
+// pays when its rounds take less than the narrow tiles at 1.29x the rate:
+// rounds <= 1.29 * narrow tiles / (2 * CUs).  It picked the faster engine at
+// each of the 17 shapes measured (losses of 2-7% avoided at 1.1-1.3 rounds
+// and just past 2; gains of 6-15% elsewhere).
+bool wide_pays(const GParams& p) {
+  const int64_t cus = device_cus();
+  const int64_t wide = ((p.T + WBM - 1) / WBM) * ((p.d_out + WBN - 1) / WBN);
+  const int64_t narrow = ((p.T + 255) / 256) * ((p.d_out + PBN - 1) / PBN);
+  const int64_t rounds = (wide + cus - 1) / cus;
+  return 200 * rounds * cus <= 129 * narrow;
+}
+
 // Pipelined engine tile height (measured): dense 256 rows, or 128 when
 // 256-row tiles would give fewer workgroups than the device has CUs; 2:4
 // always 128, where two workgroups share a CU (faster at both configured
-// shapes).
+// shapes).  Dense takes the wide engine where it pays (automatic choice) or
+// when asked for (engine 3).
 template <int AK>
 hipError_t launch_pipe(const GParams& p, hipStream_t s) {
+  if constexpr (AK == kADense) {
+    if (g_gemm_engine == 3 || (g_gemm_engine == 0 && g_gemm_bm == 0 && wide_pays(p)))
+      return launch_wide(p, s);
+  }
   const int64_t ntl = (p.d_out + PBN - 1) / PBN;
   const int64_t tiles256 = ((p.T + 255) / 256) * ntl;
   const int bm =
@@ -1249,8 +1436,8 @@ hipError_t launch_nm_shared_spmm(const uint16_t* xval, const uint32_t* mask, int
 }
 
 int gemm_set_tuning(int bm, int engine, int stages) {
-  if ((bm != 0 && bm != 128 && bm != 256) || engine < 0 || engine > 2 ||
-      (stages != 0 && (stages < 3 || stages > kMaxStages)))
+  if ((bm != 0 && bm != 128 && bm != 256) || engine < 0 || engine > 3 ||
+      (stages != 0 && (stages < 3 || stages > kMaxStages)) || (engine == 3 && bm == 128))
     return 1;
   g_gemm_bm = bm;
   g_gemm_engine = engine;

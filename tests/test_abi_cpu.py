@@ -216,11 +216,13 @@ def test_gemv_checks(sa):
     for handoff in (1, 2, 3, 0):
         assert sa.sa_set_gemv_tuning(-1, 0, handoff) == SA_OK
     assert sa.sa_set_gemm_tuning(64, 0, 0) == SA_ERR_INVALID_ARG
-    assert sa.sa_set_gemm_tuning(0, 3, 0) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemm_tuning(0, 4, 0) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemm_tuning(128, 3, 0) == SA_ERR_INVALID_ARG
     assert sa.sa_set_gemm_tuning(0, -1, 0) == SA_ERR_INVALID_ARG
     for stages in (1, 2, 7, -1):
         assert sa.sa_set_gemm_tuning(0, 0, stages) == SA_ERR_INVALID_ARG
-    for rows, engine, stages in ((128, 1, 0), (256, 2, 4), (128, 2, 6), (0, 0, 0)):
+    for rows, engine, stages in ((128, 1, 0), (256, 2, 4), (128, 2, 6), (0, 3, 0), (256, 3, 6),
+                                 (0, 0, 0)):
         assert sa.sa_set_gemm_tuning(rows, engine, stages) == SA_OK
 
 

@@ -843,9 +843,10 @@ from oracle import spmm  # noqa: E402
 
 
 # (tile rows, engine, pipelined stages): automatic, then each engine at each
-# tile height, then deeper pipelines
+# tile height, then deeper pipelines, then the 256 x 256 engine at each of
+# its stage counts
 GEMM_CHOICES = [(0, 0, 0), (128, 1, 0), (256, 1, 0), (128, 2, 0), (256, 2, 0), (128, 2, 4),
-                (256, 2, 5), (128, 2, 6)]
+                (256, 2, 5), (128, 2, 6), (0, 3, 0), (256, 3, 3), (0, 3, 4), (0, 3, 6)]
 STAGES = [3, 4, 5, 6]
 
 
@@ -883,6 +884,56 @@ def test_dense_gemm_k_pipeline_lengths(T, d_in, d_out, tile_rows, stages):
     finally:
         sa.set_gemm_tuning(0, 0, 0)
     assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
+
+
+@pytest.mark.parametrize("stages", [3, 4, 5])
+@pytest.mark.parametrize("T,d_in,d_out", [(64, 32, 128), (256, 64, 256), (40, 96, 136),
+                                          (300, 128, 520), (17, 192, 8), (129, 224, 72),
+                                          (513, 256, 264), (257, 320, 768), (70, 448, 1000),
+                                          (33, 352, 64), (96, 416, 264), (31, 480, 200),
+                                          (260, 1088, 392)])
+def test_dense_gemm_wide_k_pipeline_lengths(T, d_in, d_out, stages):
+    """The 256 x 256 engine (engine 3): 1 to 15 and 34 K steps at each of its
+    stage counts, ragged rows and columns (partial row and column tiles,
+    columns past the last 256 clamped), against the oracle and bit-equal to
+    the 256 x 128 engine."""
+    X = syn.gaussian_f16((T, d_in), 1.0, 2 * T + d_in)
+    wt = syn.weight_t(d_out, d_in, d_out + 5)
+    X_g, wt_g = dev(X), dev(wt)
+    try:
+        sa.set_gemm_tuning(0, 3, stages)
+        Y = sa.dense_gemm(X_g, wt_g).clone()
+        sa.set_gemm_tuning(256, 2, 0)
+        Yn = sa.dense_gemm(X_g, wt_g)
+    finally:
+        sa.set_gemm_tuning(0, 0, 0)
+    assert_close(Y, X.astype(np.float64) @ wt.astype(np.float64))
+    assert torch.equal(Y, Yn)
+
+
+@pytest.mark.parametrize("T,d_in,d_out", [(2048, 4096, 13312), (4096, 1024, 4096)])
+def test_dense_gemm_wide_full_shapes(T, d_in, d_out):
+    """Shapes where the automatic choice takes the 256 x 256 engine (2048 x
+    13312: 416 tiles on 256 CUs; 4096 x 4096: one tile per CU): every output
+    row against the oracle, bits equal to the 256 x 128 engine, and the
+    8:16 two-pass product (expanded copy on the same engine) likewise."""
+    X = syn.gaussian_f16((T, d_in), 1.0, 9)
+    wt = syn.weight_t(d_out, d_in, 43)
+    X_g, wt_g = dev(X), dev(wt)
+    Y = sa.dense_gemm(X_g, wt_g).clone()
+    mask_g, val_g = sa.act_sparsify_nm(X_g, 8, 16)
+    Ys = sa.nm_act_spmm(val_g, mask_g, 8, 16, wt_g).clone()
+    try:
+        sa.set_gemm_tuning(256, 2, 0)
+        Yn = sa.dense_gemm(X_g, wt_g)
+        Ysn = sa.nm_act_spmm(val_g, mask_g, 8, 16, wt_g)
+    finally:
+        sa.set_gemm_tuning(0, 0, 0)
+    assert torch.equal(Y, Yn)
+    assert torch.equal(Ys, Ysn)
+    assert_close(Y, spmm.masked_matmul(X, np.ones(X.shape, dtype=bool), wt))
+    keep, _ = sparsify.nm_sparsify(X, 8, 16)
+    assert_close(Ys, spmm.masked_matmul(X, keep, wt))
 
 
 @pytest.mark.parametrize("stages", STAGES)
