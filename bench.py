@@ -613,10 +613,16 @@ def suite_topk(sa, syn, dev, ev_time, emit, rotation):
                 emit("a2", f"act_topk_cutoff d={d} K={pct}% batch={batch}", us_c,
                      bytes_=batch * (2 * d + 8))
                 us_f = ev_time(lambda i: sa.sparse_gemv_topk(rot[i % nr], X, k, y=y), 500)
+                try:  # its two-launch form: the select kernel, then the GEMV
+                    sa.set_gemv_test_hooks(2)
+                    us_2 = ev_time(lambda i: sa.sparse_gemv_topk(rot[i % nr], X, k, y=y), 500)
+                finally:
+                    sa.set_gemv_test_hooks(0)
                 emit("a5" if batch > 1 else "a4", f"sparse_gemv_topk {d_out}x{d} K={pct}% "
-                     f"batch={batch} (cutoff + GEMV, no lists)", us_f,
+                     f"batch={batch} (select + GEMV, no lists)", us_f,
                      bytes_=2 * d_out * union + 2 * batch * d + 8 * batch + 2 * batch * d_out,
-                     flops=2 * d_out * k * batch, union_frac=round(union / d, 4))
+                     flops=2 * d_out * k * batch, union_frac=round(union / d, 4),
+                     two_launch_us=round(us_2, 3))
         del rot
         torch.cuda.empty_cache()
 
@@ -757,7 +763,11 @@ def suite_matmul(sa, syn, dev, ev_time, emit):
     algorithmic FLOPs against the dense fp16 peak, also for 2:4."""
     import torch
 
-    for (T, d_in, d_out) in [(4096, 1024, 1024), (2048, 4096, 11008)]:
+    # the two configured shapes (every pattern, with the sparsifier), then
+    # two where the dense engine takes 256 x 256 tiles (one and 2.7 tiles
+    # per CU)
+    for (T, d_in, d_out, full) in [(4096, 1024, 1024, True), (2048, 4096, 11008, True),
+                                   (4096, 4096, 4096, False), (4096, 4096, 11008, False)]:
         X = torch.from_numpy(syn.gaussian_f16((T, d_in), 1.0, 5)).to(dev)
         wt = torch.from_numpy(syn.weight_t(d_out, d_in, 41)).to(dev)
         y = torch.empty((T, d_out), dtype=torch.float16, device=dev)
@@ -766,11 +776,12 @@ def suite_matmul(sa, syn, dev, ev_time, emit):
         us_g = ev_time(lambda i: sa.dense_gemm(X, wt, y=y), steps, warmup=3)
         emit("a8", f"dense_gemm {T}x{d_in}x{d_out}", us_g, flops=dense_flop,
              frac_mfma=round(dense_flop / (us_g * 1e-6) / 2.5e15, 4))
-        for (n, m) in [(2, 4), (8, 16), (16, 32)]:
+        for (n, m) in ([(2, 4), (8, 16), (16, 32)] if full else [(2, 4), (8, 16)]):
             mask, val = sa.act_sparsify_nm(X, n, m)
-            us_s = ev_time(lambda i: sa.act_sparsify_nm(X, n, m), 200)
-            emit("a3", f"act_sparsify_nm {n}:{m} {T}x{d_in}", us_s,
-                 bytes_=2 * T * d_in + 2 * T * d_in * n // m + T * d_in // 8)
+            if full:
+                us_s = ev_time(lambda i: sa.act_sparsify_nm(X, n, m), 200)
+                emit("a3", f"act_sparsify_nm {n}:{m} {T}x{d_in}", us_s,
+                     bytes_=2 * T * d_in + 2 * T * d_in * n // m + T * d_in // 8)
             us = ev_time(lambda i: sa.nm_act_spmm(val, mask, n, m, wt, y=y), steps, warmup=3)
             alg = dense_flop * n // m
             emit("a7", f"nm_act_spmm {n}:{m} {T}x{d_in}x{d_out}", us, flops=alg,

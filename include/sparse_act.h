@@ -257,9 +257,16 @@ int sparse_gemv_threshold(const uint16_t* wt, int64_t d_out, int64_t d_in,
  * y[b] = W (keep_b .* x[b]) with keep_b the k largest |x[b]| (ties to the
  * lower index), as act_sparsify_topk keeps them ([QS] answer comparing with
  * MoE: per token, the smaller entries are pruned; answer A1: TopK =
- * 60/50/40%).  Two launches on `stream`: act_topk_cutoff writes each row's
- * (tau, i*) into the workspace, then the GEMV decides every entry from x
- * and that pair in its own slice (no index list is written or read).
+ * 60/50/40%).  Each row's cut is the pair (tau, i*) of act_topk_cutoff;
+ * the GEMV decides every entry of its own slice from x and that pair (no
+ * index list is written or read).  At batch 1, where a GEMV workgroup
+ * holds the row (d_in <= 16 x its threads, so at least 4096), one launch:
+ * every workgroup finds the pair itself from x, in two radix passes, and
+ * the GEMV runs split-K.  Otherwise two launches on `stream`:
+ * act_topk_cutoff writes the pairs into the workspace, then the GEMV reads
+ * them.  The two forms give the same bits wherever they run the same GEMV
+ * plan (the two-launch form takes the full-K kernel for some small
+ * weights).
  *   x [batch][d_in] fp16 (2-byte aligned); 0 <= k <= d_in <= 65536; other
  *   arguments as sparse_gemv_threshold.
  */
@@ -512,12 +519,16 @@ int sa_read_stream_grid(const void* src, size_t bytes, uint32_t* sink, int block
  */
 int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff);
 /*
- * Process-wide fault injection for tests of the L2-local hand-off (form 3).
+ * Process-wide switches for tests of paths the automatic choices hide.
  * flags bit 0: the first input slice of every output tile reports a
- * different XCD to the hand-off's placement check, as if it had run on
- * another XCD.  The last workgroup of every tile then takes the recompute
- * path; results are unchanged, bit for bit.  0 (the default) turns it off.
- * Returns SA_ERR_INVALID_ARG for other flags.  Not thread-safe.
+ * different XCD to the L2-local hand-off's (form 3) placement check, as if
+ * it had run on another XCD.  The last workgroup of every tile then takes
+ * the recompute path; results are unchanged, bit for bit.
+ * flags bit 1: sparse_gemv_topk always takes its two-launch form (the
+ * select kernel writes the cutoff pairs, then the GEMV reads them), also
+ * where its workgroups would select the cutoff themselves.
+ * 0 (the default) turns both off.  Returns SA_ERR_INVALID_ARG for other
+ * flags.  Not thread-safe.
  */
 int sa_set_gemv_test_hooks(int flags);
 /*

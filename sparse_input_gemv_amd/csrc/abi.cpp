@@ -237,10 +237,6 @@ int sparse_gemv_topk(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint
                      : nullptr;
   if (st == SA_OK) st = sa::check_topk_cutoff(x, batch, d_in, k, cut, "sparse_gemv_topk");
   if (st != SA_OK || batch == 0) return st;
-  st = hip_status(sa::launch_sparsify_topk(x, batch, d_in, k, nullptr, nullptr, nullptr, nullptr,
-                                           0, cut, as_stream(stream)),
-                  "sparse_gemv_topk");
-  if (st != SA_OK) return st;
   sa::GemvCall c;
   c.mode = sa::kModeTopK;
   c.wt = wt;
@@ -249,10 +245,11 @@ int sparse_gemv_topk(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint
   c.batch = (int)batch;
   c.x = x;
   c.cut = cut;
+  c.topk_k = k;
   c.y = y;
   c.ws = ws;
   c.ws_bytes = ws_bytes;
-  return run_gemv(c, "sparse_gemv_topk", stream);
+  return hip_status(sa::launch_gemv_topk(c, as_stream(stream)), "sparse_gemv_topk");
 }
 
 int sparse_gemv_threshold_noalloc(const uint16_t* wt, int64_t d_out, int64_t d_in,

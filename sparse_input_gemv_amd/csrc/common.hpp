@@ -31,6 +31,29 @@ __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
 // (for non-NaN values), and -0 and +0 share key 0.
 __device__ __forceinline__ int mag_key(uint16_t b) { return (int)(b & 0x7fffu); }
 
+// Loads E consecutive fp16 bit patterns starting at element k0 of a row
+// (entries past d read as 0).  The vector path needs a 16-byte aligned row
+// and k0 a multiple of 8.
+template <int E>
+__device__ __forceinline__ void load_run(const uint16_t* __restrict__ xr, int64_t k0, int64_t d,
+                                         bool vec, uint16_t (&v)[E]) {
+  if (vec && k0 + E <= d) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(xr + k0);
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) {
+      u32x4 r = p[q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[q * 8 + 2 * i] = (uint16_t)(r[i] & 0xffffu);
+        v[q * 8 + 2 * i + 1] = (uint16_t)(r[i] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = (k0 + e < d) ? xr[k0 + e] : (uint16_t)0;
+  }
+}
+
 // Inclusive prefix sum within each row of 16 lanes: DPP row shifts (a VALU
 // operand modifier: lane i reads lane i - n of its row, 0 where that lane is
 // outside the row).  No LDS traffic.

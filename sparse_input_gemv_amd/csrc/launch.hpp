@@ -41,6 +41,7 @@ enum GemvMode : int {
   kModeSquare = 7,     // x + t: keep x_k iff x_k^2 >= t (the rank adapter's masker)
   kModeTopK = 8,       // x + per-row (tau, i*) from the Top-K select: keep iff
                        // key > tau, or key == tau and k <= i*
+  kModeTopKSel = 9,    // kModeTopK with each workgroup selecting (tau, i*) itself
 };
 
 struct GemvCall {
@@ -54,6 +55,7 @@ struct GemvCall {
   float t = 0.f;
   const uint16_t* mu = nullptr;  // scored mode: static shift [d_in] (or none)
   const int32_t* cut = nullptr;  // Top-K mode: [batch][2] (tau, i*)
+  int64_t topk_k = 0;            // kModeTopKSel: entries kept per row
   int var = 0;                   // scored mode: apply the variance correction
   // lists
   const int32_t* idx = nullptr;
@@ -101,6 +103,13 @@ hipError_t gemv_noalloc_scratch(void** ptr);
 // Returns hipErrorInvalidValue if the workspace is too small for the launch
 // (checked by abi.cpp beforehand, so this is a second line of defence).
 hipError_t launch_gemv(const GemvCall& c, hipStream_t s);
+// Top-K GEMV (c.mode kModeTopK, c.cut the [batch][2] cutoff pairs in the
+// workspace, c.topk_k): one launch in which every workgroup selects the
+// row's cutoff itself where the in-workgroup select applies (split-K, batch
+// 1, d_in <= the workgroup's threads x kTopkSelPerThread), else the select
+// kernel writes c.cut and the GEMV reads it.
+constexpr int kTopkSelPerThread = 16;
+hipError_t launch_gemv_topk(const GemvCall& c, hipStream_t s);
 hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* out,
                             hipStream_t s);
 int gemv_set_tuning(int tiling, int target_wgs, int handoff);

@@ -16,28 +16,6 @@ namespace {
 
 constexpr int kSparsifyThreads = 1024;
 
-// Loads E consecutive fp16 bit patterns starting at element k0 of a row.
-// The vector path needs a 16-byte aligned row and k0 a multiple of 8.
-template <int E>
-__device__ __forceinline__ void load_run(const uint16_t* __restrict__ xr, int64_t k0, int64_t d,
-                                         bool vec, uint16_t (&v)[E]) {
-  if (vec && k0 + E <= d) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(xr + k0);
-#pragma unroll
-    for (int q = 0; q < E / 8; ++q) {
-      u32x4 r = p[q];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[q * 8 + 2 * i] = (uint16_t)(r[i] & 0xffffu);
-        v[q * 8 + 2 * i + 1] = (uint16_t)(r[i] >> 16);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = (k0 + e < d) ? xr[k0 + e] : (uint16_t)0;
-  }
-}
-
 // Writes the kept entries of one run per thread (bit e of `bits` <-> element
 // k0+e) at their ascending positions, and the bitmask words of the run.
 // Threads cover consecutive runs, so thread order is index order.

@@ -419,6 +419,26 @@ def test_plan_small_weights():
     assert (p["tile_o"], p["grid_o"] * p["slices"]) == (64, 256)
 
 
+def test_plan_topk_forms(sa):
+    import sparse_input_gemv_amd as m
+    # batch 1, one launch, every workgroup selecting the cutoff: the split-K
+    # plan of the threshold GEMV, also where the two-launch form would run
+    # full-K
+    assert _plan("topk", 11008, 4096) == _plan("threshold", 11008, 4096)
+    assert _plan("topk", 4096, 1024)["kernel"] == "split-K"
+    assert _plan("topk", 1024, 1024)["kernel"] == "split-K"
+    try:
+        m.set_gemv_test_hooks(2)  # the two-launch form
+        assert _plan("topk", 4096, 1024)["kernel"] == "full-K"
+        assert _plan("topk", 11008, 4096) == _plan("threshold", 11008, 4096)
+    finally:
+        m.set_gemv_test_hooks(0)
+    # batch 2 and more: two launches, the threshold GEMV's plans
+    assert _plan("topk", 4096, 4096, 2) == _plan("threshold", 4096, 4096, 2)
+    assert _plan("topk", 1024, 1024, 2)["kernel"] == "full-K"
+    assert _plan("topk", 4096, 1024, 4)["kernel"] == "split-K"
+
+
 def test_plan_follows_tuning(sa):
     import sparse_input_gemv_amd as m
     try:
@@ -448,7 +468,9 @@ def test_plan_checks(sa):
 
 
 def test_test_hook_checks(sa):
-    assert sa.sa_set_gemv_test_hooks(2) == SA_ERR_INVALID_ARG
+    assert sa.sa_set_gemv_test_hooks(4) == SA_ERR_INVALID_ARG
     assert sa.sa_set_gemv_test_hooks(-1) == SA_ERR_INVALID_ARG
     assert sa.sa_set_gemv_test_hooks(1) == SA_OK
+    assert sa.sa_set_gemv_test_hooks(3) == SA_OK
+    assert sa.sa_set_gemv_test_hooks(2) == SA_OK
     assert sa.sa_set_gemv_test_hooks(0) == SA_OK

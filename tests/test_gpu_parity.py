@@ -383,6 +383,39 @@ def test_sparse_gemv_topk_edges(d_out, d_in, batch):
             assert not np.any(host(y).view(np.uint16) & 0x7FFF)
 
 
+@pytest.mark.parametrize("d_out,d_in,batch", [(11008, 4096, 1), (4096, 4096, 1), (4096, 1024, 1),
+                                              (1024, 1024, 1), (8, 1, 1), (520, 4095, 1),
+                                              (264, 2055, 1), (4096, 4097, 1), (1024, 1000, 2)])
+def test_sparse_gemv_topk_one_launch_matches_two(d_out, d_in, batch):
+    """Where every GEMV workgroup selects the cutoff itself (batch 1, the
+    row fits a workgroup), the output equals the two-launch form's (the
+    select kernel, then the GEMV) bit for bit wherever both run the same
+    GEMV plan, on Laplace rows and on rows of heavy ties, for k from 0 to
+    d_in; both equal the oracle everywhere."""
+    rng = np.random.default_rng(d_in + batch)
+    pool = np.array([0.0, -0.0, 0.25, -0.25, 0.5, -0.5, 1.0, -1.0], dtype=np.float16)
+    wt = syn.weight_t(d_out, d_in, 6)
+    wt_g = dev(wt)
+    for X in (syn.laplace_f16((batch, d_in), 1.0, 500 + d_in),
+              pool[rng.integers(0, len(pool), size=(batch, d_in))]):
+        X_g = dev(X)
+        for k in sorted({min(k, d_in) for k in (0, 1, 2, d_in // 3, d_in // 2, d_in - 1, d_in)}):
+            y1 = sa.sparse_gemv_topk(wt_g, X_g, k).clone()
+            p1 = sa.gemv_plan("topk", d_out, d_in, batch)
+            try:
+                sa.set_gemv_test_hooks(2)
+                y2 = sa.sparse_gemv_topk(wt_g, X_g, k)
+                p2 = sa.gemv_plan("topk", d_out, d_in, batch)
+            finally:
+                sa.set_gemv_test_hooks(0)
+            if p1 == p2:
+                assert torch.equal(y1, y2), (k,)
+            keep = sparsify.topk_sparsify(X, k)[0]
+            ref = gemv.batched_masked_gemv(wt, X, keep)
+            assert_close(y1, ref)
+            assert_close(y2, ref)
+
+
 # ---------------------------------------------------------------------------
 # calibration
 # ---------------------------------------------------------------------------
