@@ -108,4 +108,113 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& to
   return r;
 }
 
+// The Top-K cutoff of one row, found by one workgroup: the pair (tau, i*)
+// with tau the k-th largest 15-bit magnitude key and i* the index of the
+// last surviving entry equal to it (ties to the lower index), for a row of
+// at most NT x E entries (thread t holds the run of E entries from k0 = t E
+// in v, loaded by the caller with load_run).
+// Two radix passes over 4 KB of LDS, small enough to sit beside a GEMV's
+// own LDS (the one-launch Top-K GEMV runs it in every workgroup):
+//  1. key >> 5 into 1024 LDS bins; a workgroup scan of the threads' bin
+//     sums (thread t owns 1024 / NT consecutive bins) finds the bin b1 that
+//     holds the k-th largest key, and r1 = k - #(keys in higher bins);
+//  2. the low 5 bits of the keys in bin b1 into 32 bins; one wave scans them
+//     from the top: tau = 32 b1 + that bin, and r = r1 - #(keys of b1 above
+//     tau) entries equal to tau survive;
+//  3. i* = the index of the r-th entry equal to tau, found by a scan of the
+//     threads' counts (thread order is index order).
+// k = 0 gives tau = 2^15, i* = -1 (nothing survives).  Requires k <= d.
+// Every thread of the workgroup must call it.
+constexpr int kSelBins = 1024, kSelSub = 32;
+struct SelLds {
+  int h1[kSelBins];
+  int h2[kSelSub];
+  int scan[2][16];
+  int sel[3];
+};
+
+template <int NT, int E>
+__device__ void wg_topk_cutoff(const uint16_t (&v)[E], int64_t d, int64_t k, SelLds& s,
+                               int& tau_out, int& istar_out) {
+  constexpr int BPT = kSelBins / NT;
+  static_assert(kSelBins % NT == 0 && BPT >= 1, "bins split over the threads");
+  const int tid = (int)threadIdx.x;
+  if (k <= 0) {
+    tau_out = 1 << 15;
+    istar_out = -1;
+    return;
+  }
+  const int64_t k0 = (int64_t)tid * E;
+  for (int i = tid; i < kSelBins; i += NT) s.h1[i] = 0;
+  if (tid < kSelSub) s.h2[tid] = 0;
+  int key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (k0 + e < d) ? mag_key(v[e]) : -1;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (key[e] >= 0) atomicAdd(&s.h1[key[e] >> 5], 1);
+  __syncthreads();
+  const int kk = (int)k;
+  int c[BPT], mine = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    c[j] = s.h1[tid * BPT + j];
+    mine += c[j];
+  }
+  int total;
+  const int below = block_scan_once<NT>(mine, s.scan[0], total);
+  const int above = total - below - mine;  // keys in higher threads' bins
+  if (above < kk && kk <= above + mine) {  // exactly one thread
+    int acc = above;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (acc < kk && kk <= acc + c[j]) {
+        s.sel[0] = tid * BPT + j;
+        s.sel[1] = kk - acc;
+      }
+      acc += c[j];
+    }
+  }
+  __syncthreads();
+  const int b1 = s.sel[0], r1 = s.sel[1];
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (key[e] >= 0 && (key[e] >> 5) == b1) atomicAdd(&s.h2[key[e] & 31], 1);
+  __syncthreads();
+  if (tid < kWave) {
+    const int lane = tid;
+    const int cb = lane < kSelSub ? s.h2[kSelSub - 1 - lane] : 0;
+    const int sc = wave_inclusive_scan(cb);  // keys of b1 at or above bin 31 - lane
+    const uint64_t hit = __ballot(lane < kSelSub && sc >= r1);
+    const int l = __builtin_ctzll(hit);
+    if (lane == l) {
+      s.sel[0] = b1 * kSelSub + (kSelSub - 1 - l);
+      s.sel[1] = r1 - (sc - cb);
+    }
+  }
+  __syncthreads();
+  const int tau = s.sel[0], r = s.sel[1];  // r >= 1
+  int ties = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) ties += key[e] == tau ? 1 : 0;
+  int tie_total;
+  const int tr = block_scan_once<NT>(ties, s.scan[1], tie_total);
+  if (tr < r && r <= tr + ties) {  // exactly one thread holds the r-th tie
+    int n = tr, at = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (key[e] == tau) {
+        ++n;
+        if (n == r) at = (int)(k0 + e);
+      }
+    }
+    s.sel[2] = at;
+  }
+  __syncthreads();
+  tau_out = tau;
+  istar_out = s.sel[2];
+  __syncthreads();  // the next row's select may overwrite sel
+}
+
 }  // namespace sa

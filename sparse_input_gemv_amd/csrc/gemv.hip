@@ -183,119 +183,6 @@ __device__ __forceinline__ bool topk_keep(uint16_t xb, int64_t i, int tau, int i
 template <int MODE>
 constexpr bool kTopKMode = MODE == kModeTopK || MODE == kModeTopKSel;
 
-// The Top-K cutoff of one row inside a GEMV workgroup (kModeTopKSel): the
-// pair (tau, i*) of act_topk_cutoff -- tau the k-th largest 15-bit magnitude
-// key, i* the index of the last surviving entry equal to it (ties to the
-// lower index) -- so the kept set, and every output bit, is that of the
-// select kernel followed by kModeTopK.  Every workgroup of the launch finds
-// it for itself from x (a row of at most NT x kTopkSelPerThread entries,
-// each thread holding a run of consecutive ones), in two radix passes
-// instead of the select kernel's 2^15 bins, which would not fit beside the
-// GEMV's own LDS:
-//  1. key >> 5 into 1024 LDS bins; a workgroup scan of the threads' bin
-//     sums (thread t owns 1024 / NT consecutive bins) finds the bin b1 that
-//     holds the k-th largest key, and r1 = k - #(keys in higher bins);
-//  2. the low 5 bits of the keys in bin b1 into 32 bins; one wave scans them
-//     from the top: tau = 32 b1 + that bin, and r = r1 - #(keys of b1 above
-//     tau) entries equal to tau survive;
-//  3. i* = the index of the r-th entry equal to tau, found by a scan of the
-//     threads' counts (thread order is index order).
-// k = 0 gives tau = 2^15, i* = -1 (nothing survives).  Requires k <= d.
-// Every thread of the workgroup must call it.
-constexpr int kSelBins = 1024, kSelSub = 32;
-struct SelLds {
-  int h1[kSelBins];
-  int h2[kSelSub];
-  int scan[2][16];
-  int sel[3];
-};
-
-template <int NT>
-__device__ void wg_topk_cutoff(const uint16_t* __restrict__ xr, int64_t d, int64_t k, SelLds& s,
-                               int& tau_out, int& istar_out) {
-  constexpr int E = kTopkSelPerThread;
-  constexpr int BPT = kSelBins / NT;
-  static_assert(kSelBins % NT == 0 && BPT >= 1, "bins split over the threads");
-  const int tid = (int)threadIdx.x;
-  if (k <= 0) {
-    tau_out = 1 << 15;
-    istar_out = -1;
-    return;
-  }
-  const int64_t k0 = (int64_t)tid * E;
-  uint16_t v[E];
-  load_run<E>(xr, k0, d, (reinterpret_cast<uintptr_t>(xr) & 15u) == 0, v);
-  for (int i = tid; i < kSelBins; i += NT) s.h1[i] = 0;
-  if (tid < kSelSub) s.h2[tid] = 0;
-  int key[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (k0 + e < d) ? mag_key(v[e]) : -1;
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (key[e] >= 0) atomicAdd(&s.h1[key[e] >> 5], 1);
-  __syncthreads();
-  const int kk = (int)k;
-  int c[BPT], mine = 0;
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    c[j] = s.h1[tid * BPT + j];
-    mine += c[j];
-  }
-  int total;
-  const int below = block_scan_once<NT>(mine, s.scan[0], total);
-  const int above = total - below - mine;  // keys in higher threads' bins
-  if (above < kk && kk <= above + mine) {  // exactly one thread
-    int acc = above;
-#pragma unroll
-    for (int j = BPT - 1; j >= 0; --j) {
-      if (acc < kk && kk <= acc + c[j]) {
-        s.sel[0] = tid * BPT + j;
-        s.sel[1] = kk - acc;
-      }
-      acc += c[j];
-    }
-  }
-  __syncthreads();
-  const int b1 = s.sel[0], r1 = s.sel[1];
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (key[e] >= 0 && (key[e] >> 5) == b1) atomicAdd(&s.h2[key[e] & 31], 1);
-  __syncthreads();
-  if (tid < kWave) {
-    const int lane = tid;
-    const int cb = lane < kSelSub ? s.h2[kSelSub - 1 - lane] : 0;
-    const int sc = wave_inclusive_scan(cb);  // keys of b1 at or above bin 31 - lane
-    const uint64_t hit = __ballot(lane < kSelSub && sc >= r1);
-    const int l = __builtin_ctzll(hit);
-    if (lane == l) {
-      s.sel[0] = b1 * kSelSub + (kSelSub - 1 - l);
-      s.sel[1] = r1 - (sc - cb);
-    }
-  }
-  __syncthreads();
-  const int tau = s.sel[0], r = s.sel[1];  // r >= 1
-  int ties = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) ties += key[e] == tau ? 1 : 0;
-  int tie_total;
-  const int tr = block_scan_once<NT>(ties, s.scan[1], tie_total);
-  if (tr < r && r <= tr + ties) {  // exactly one thread holds the r-th tie
-    int n = tr, at = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (key[e] == tau) {
-        ++n;
-        if (n == r) at = (int)(k0 + e);
-      }
-    }
-    s.sel[2] = at;
-  }
-  __syncthreads();
-  tau_out = tau;
-  istar_out = s.sel[2];
-  __syncthreads();  // the next row's select may overwrite sel
-}
 
 // Modes whose output takes the correction alpha * sum + bias (the list GEMV
 // and the scored mode); every other mode stores the plain rounding.
@@ -547,11 +434,14 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     }
   } else if constexpr (MODE == kModeTopKSel) {
     __shared__ SelLds sel_lds;
+    constexpr int E = kTopkSelPerThread;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       if (b < p.batch) {
-        wg_topk_cutoff<NT>(p.x + (int64_t)b * p.d_in, p.d_in, p.topk_k, sel_lds, tk_tau[b],
-                           tk_ist[b]);
+        const uint16_t* xb = p.x + (int64_t)b * p.d_in;
+        uint16_t v[E];
+        load_run<E>(xb, (int64_t)tid * E, p.d_in, (reinterpret_cast<uintptr_t>(xb) & 15u) == 0, v);
+        wg_topk_cutoff<NT, E>(v, p.d_in, p.topk_k, sel_lds, tk_tau[b], tk_ist[b]);
       } else {
         tk_tau[b] = tk_tau[0];
         tk_ist[b] = tk_ist[0];
@@ -1962,10 +1852,11 @@ Decision decide_gemv(int mode, int64_t d_out, int64_t d_in, int64_t batch, int64
   // Full-K serves batch <= 2 of every mode except batched lists and the
   // in-workgroup Top-K select, for small weights whose grid fills the chip
   // or whose walk is short.
-  const bool fk_ok = B <= 2 && mode != kModeListBatched && mode != kModeTopKSel;
+  const bool sel = mode == kModeTopKSel;
+  const bool fk_ok = B <= 2 && mode != kModeListBatched && !sel;
   int tiling = g_tiling;
   const bool hot = B == 1 && (mode == kModeThreshold || mode == kModeDense ||
-                              mode == kModeList || mode == kModeTopK || mode == kModeTopKSel);
+                              mode == kModeList || mode == kModeTopK || sel);
   if (tiling < 0) {
     const int64_t wbytes = d_in * d_out * 2;
     const bool fk_fills = (d_out + kTilings[kDefaultFullK].tile_o - 1) /
@@ -2106,23 +1997,29 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
 }
 
 namespace {
-// The fused Top-K decision: the in-workgroup select applies to a split-K
-// plan at batch 1 whose workgroups can hold the row (d_in <= threads x
-// kTopkSelPerThread).  At batch 2 each workgroup would select two rows one
-// after the other, and the two-launch form measured as fast (11008 x 4096:
-// 22.18 against 22.32 us at 50%).
-bool topk_fused(const Decision& d, int64_t d_in) {
-  return !d.full_k && d.B == 1 &&
-         d_in <= (int64_t)kTilings[d.tiling].threads * kTopkSelPerThread;
+// The fused Top-K mode of a call: the in-workgroup select applies to a
+// split-K plan at batch 1 whose workgroups can hold the row (d_in <= threads
+// x kTopkSelPerThread); 0 where it does not.  Measured at 50%: 11008 x 4096
+// 15.45 us in one launch against 17.16 us in two.  At batch 2 each workgroup
+// would select two rows one after the other, and the two-launch form
+// measured as fast (22.18 against 22.32 us).  Longer rows (48 entries per
+// thread) made every workgroup's select slower than the separate launch:
+// 4096 x 11008, 19.67 against 17.06 us.
+int topk_fused_mode(int64_t d_out, int64_t d_in, int64_t batch, int64_t cus, int resident,
+                    bool cached, Decision* out) {
+  if (batch != 1 || (g_test_hooks & 2) != 0) return 0;
+  const Decision d = decide_gemv(kModeTopKSel, d_out, d_in, batch, cus, resident, cached);
+  if (d.full_k || d_in > (int64_t)kTilings[d.tiling].threads * kTopkSelPerThread) return 0;
+  if (out) *out = d;
+  return kModeTopKSel;
 }
 }  // namespace
 
 hipError_t launch_gemv_topk(const GemvCall& c, hipStream_t s) {
   GemvCall g = c;
-  if (c.batch == 1 && (g_test_hooks & 2) == 0 &&
-      topk_fused(decide_gemv(kModeTopKSel, c.d_out, c.d_in, c.batch, device_cus(), 0, true),
-                 c.d_in)) {
-    g.mode = kModeTopKSel;
+  const int fused = topk_fused_mode(c.d_out, c.d_in, c.batch, device_cus(), 0, true, nullptr);
+  if (fused != 0) {
+    g.mode = fused;
     return launch_gemv(g, s);
   }
   const hipError_t e = launch_sparsify_topk(c.x, c.batch, c.d_in, c.topk_k, nullptr, nullptr,
@@ -2169,9 +2066,9 @@ int gemv_plan(int mode, int64_t d_out, int64_t d_in, int64_t batch, int cus, int
               int* kernel, int* tile_o, int* go, int* gk, int* handoff) {
   const int64_t n = cus > 0 ? cus : device_cus();
   Decision d = decide_gemv(mode, d_out, d_in, batch, n, resident, false);
-  if (mode == kModeTopK && batch == 1 && (g_test_hooks & 2) == 0) {  // what launch_gemv_topk runs
-    const Decision f = decide_gemv(kModeTopKSel, d_out, d_in, batch, n, resident, false);
-    if (topk_fused(f, d_in)) d = f;
+  if (mode == kModeTopK) {  // what launch_gemv_topk runs
+    Decision f{};
+    if (topk_fused_mode(d_out, d_in, batch, n, resident, false, &f) != 0) d = f;
   }
   const Tiling& T = kTilings[d.tiling];
   *kernel = d.full_k ? 1 : 0;

@@ -60,10 +60,14 @@ __device__ __forceinline__ int compact_row_lds(uint64_t bits, const uint16_t (&v
                                                uint32_t* __restrict__ mr) {
   const int tid = (int)threadIdx.x;
   if (mr != nullptr) {
-    if constexpr (E == 16) {
-      // two neighbouring threads hold the two halves of one 32-bit word
-      const uint32_t other = (uint32_t)__shfl_xor((int)bits, 1, kWave);
-      if ((tid & 1) == 0 && k0 < d) mr[k0 >> 5] = (uint32_t)bits | (other << 16);
+    if constexpr (E < 32) {
+      // 32 / E neighbouring threads hold the parts of one 32-bit word
+      static_assert(32 % E == 0, "runs tile the mask words");
+      constexpr int G = 32 / E;
+      uint32_t w = (uint32_t)bits;
+#pragma unroll
+      for (int j = 1; j < G; ++j) w |= (uint32_t)__shfl_down((int)bits, j, kWave) << (E * j);
+      if (tid % G == 0 && k0 < d) mr[k0 >> 5] = w;
     } else {
 #pragma unroll
       for (int q = 0; q < E / 32; ++q)
@@ -250,7 +254,8 @@ __global__ __launch_bounds__(NT) void k_sparsify_scored(
 }
 
 // Exactly k survivors per row: the k largest magnitudes, ties to the lower
-// index (fp16 magnitudes compared exactly as 15-bit keys; -0 == +0).
+// index (fp16 magnitudes compared exactly as 15-bit keys; -0 == +0); rows
+// longer than 4096 entries (shorter ones take the radix select below).
 //  1. One LDS bin per key value (2^15 bins, 128 KB); a single pass of LDS
 //     atomics counts every key.
 //  2. Each thread owns 32 consecutive keys' bins.  A workgroup scan of the
@@ -423,6 +428,72 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
     compact_run<NT, E>(bits, v, k0, d, base, scan[2], ir, vr, mr);
   }
   if (tid == 0) nnz[row] = (int32_t)k;
+}
+
+// Rows of up to 4096 entries: the two-pass radix select of wg_topk_cutoff,
+// one workgroup of 512 threads per row -- k_topk_cut for the cutoff pairs
+// alone (act_topk_cutoff and the two-launch Top-K GEMV), k_topk_radix for
+// the lists.  Measured (d = 4096, batch 1): 3.0 us for the pairs and 4.7 us
+// with the lists, against 4.5 and 6.6 us for k_topk, whose 128 KB of bins
+// take longer to clear and scan.  Longer rows stay on k_topk: at d = 11008
+// the radix passes' hot bins made them slower (5.0 us with 1024 threads,
+// against 4.6).
+constexpr int kCutThreads = 512, kCutE = 8;
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void k_topk_cut(const uint16_t* __restrict__ x, int64_t d,
+                                                 int64_t k, int32_t* __restrict__ cut,
+                                                 int32_t* __restrict__ nnz) {
+  __shared__ SelLds lds;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * d;
+  uint16_t v[E];
+  load_run<E>(xr, (int64_t)threadIdx.x * E, d, (reinterpret_cast<uintptr_t>(xr) & 15u) == 0, v);
+  int tau, istar;
+  wg_topk_cutoff<NT, E>(v, d, k, lds, tau, istar);
+  if (threadIdx.x == 0) {
+    cut[2 * row] = tau;
+    cut[2 * row + 1] = istar;
+    if (nnz != nullptr) nnz[row] = (int32_t)k;
+  }
+}
+
+// The lists of act_sparsify_topk (and its cutoff pairs where asked) for rows
+// of up to 4096 entries: the same select, then the kept entries -- key >
+// tau, or key == tau and index <= i* -- compacted through LDS.
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void k_topk_radix(const uint16_t* __restrict__ x, int64_t d,
+                                                   int64_t k, int32_t* __restrict__ cut,
+                                                   uint32_t* __restrict__ mask,
+                                                   int32_t* __restrict__ idx,
+                                                   uint16_t* __restrict__ val,
+                                                   int32_t* __restrict__ nnz, int64_t cap) {
+  __shared__ SelLds lds;
+  __shared__ int scan[NT / kWave];
+  __shared__ __align__(16) int32_t sidx[NT * E];
+  __shared__ __align__(16) uint16_t sval[NT * E];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * d;
+  const int64_t k0 = (int64_t)threadIdx.x * E;
+  uint16_t v[E];
+  load_run<E>(xr, k0, d, (reinterpret_cast<uintptr_t>(xr) & 15u) == 0, v);
+  int tau, istar;
+  wg_topk_cutoff<NT, E>(v, d, k, lds, tau, istar);
+  uint64_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int key = mag_key(v[e]);
+    const bool keep = k0 + e < d && (key > tau || (key == tau && k0 + e <= (int64_t)istar));
+    bits |= (uint64_t)keep << e;
+  }
+  compact_row_lds<NT, E>(bits, v, k0, d, scan, sidx, sval, idx + row * cap, val + row * cap,
+                         mask ? mask + row * ((d + 31) >> 5) : nullptr);
+  if (threadIdx.x == 0) {
+    if (cut != nullptr) {
+      cut[2 * row] = tau;
+      cut[2 * row + 1] = istar;
+    }
+    nnz[row] = (int32_t)k;
+  }
 }
 
 // N:M, M <= 8: each thread owns 8 consecutive entries (one 16-byte load),
@@ -749,6 +820,15 @@ hipError_t launch_sparsify_topk(const uint16_t* x, int64_t rows, int64_t d, int6
                                 uint32_t* mask, int32_t* idx, uint16_t* val, int32_t* nnz,
                                 int64_t cap, int32_t* cut, hipStream_t s) {
   const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && (d % 8) == 0) ? 1 : 0;
+  if (d <= (int64_t)kCutThreads * kCutE) {
+    if (mask == nullptr && idx == nullptr)
+      hipLaunchKernelGGL((k_topk_cut<kCutThreads, kCutE>), dim3((unsigned)rows),
+                         dim3(kCutThreads), 0, s, x, d, k, cut, nnz);
+    else
+      hipLaunchKernelGGL((k_topk_radix<kCutThreads, kCutE>), dim3((unsigned)rows), dim3(kCutThreads), 0, s, x, d, k, cut,
+                         mask, idx, val, nnz, cap);
+    return hipGetLastError();
+  }
   if (d <= (int64_t)kSparsifyThreads * 16) {
     hipLaunchKernelGGL((k_topk<kSparsifyThreads, 16>), dim3((unsigned)rows),
                        dim3(kSparsifyThreads), 0, s, x, d, k, cut, mask, idx, val, nnz, cap, vec);

@@ -309,7 +309,9 @@ def test_topk_and_union_gemv(d, pct, batch):
     assert_close(sa.masked_gemv(wt_g, X_g, m_g), ref)
 
 
-@pytest.mark.parametrize("d", [1, 5, 64, 100, 4097, 16384, 16385, 30000])
+# rows up to 4096 take the two-pass radix select (512 threads of 8
+# entries), longer ones the 2^15-bin select
+@pytest.mark.parametrize("d", [1, 5, 33, 64, 100, 1000, 4095, 4096, 4097, 16384, 16385, 30000])
 def test_topk_edges_and_ties(d):
     rng = np.random.default_rng(d)
     pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, 0.25], dtype=np.float16)
@@ -337,7 +339,8 @@ def oracle_cutoff(x, keep):
     return np.array(out, dtype=np.int32)
 
 
-@pytest.mark.parametrize("d", [1, 5, 64, 100, 4097, 11008, 16384, 16385, 30000, 65536])
+@pytest.mark.parametrize("d", [1, 5, 33, 64, 100, 1000, 4095, 4096, 4097, 11008, 16384, 16385,
+                               30000, 65536])
 def test_topk_cutoff_bit_exact(d):
     rng = np.random.default_rng(d + 7)
     pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, 0.25], dtype=np.float16)
@@ -385,7 +388,8 @@ def test_sparse_gemv_topk_edges(d_out, d_in, batch):
 
 @pytest.mark.parametrize("d_out,d_in,batch", [(11008, 4096, 1), (4096, 4096, 1), (4096, 1024, 1),
                                               (1024, 1024, 1), (8, 1, 1), (520, 4095, 1),
-                                              (264, 2055, 1), (4096, 4097, 1), (1024, 1000, 2)])
+                                              (264, 2055, 1), (4096, 4097, 1), (4096, 11008, 1),
+                                              (1032, 12288, 1), (264, 12289, 1), (1024, 1000, 2)])
 def test_sparse_gemv_topk_one_launch_matches_two(d_out, d_in, batch):
     """Where every GEMV workgroup selects the cutoff itself (batch 1, the
     row fits a workgroup), the output equals the two-launch form's (the
