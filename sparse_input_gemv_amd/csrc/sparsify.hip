@@ -626,6 +626,30 @@ __device__ __forceinline__ void pk_sort_desc(u16x2 (&s)[N]) {
   }
 }
 
+// tau for n = M / 2 without the full sort: each half sorted (descending),
+// then the half-cleaner -- max(a_i, b_(M/2-1-i)) over the two sorted halves
+// are the M/2 largest keys as a set (a sorted half followed by the other
+// reversed is bitonic) -- and tau is their minimum.  For 16 keys: 2 x 19
+// compare-exchanges + 8 max + 7 min (91 packed operations) against 63
+// compare-exchanges (126); for 32: 2 x 63 + 16 + 15 (283) against 191 (382).
+template <int M>
+__device__ __forceinline__ u16x2 pk_half_tau(const u16x2 (&s)[M]) {
+  constexpr int H = M / 2;
+  u16x2 a[H], b[H];
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    a[i] = s[i];
+    b[i] = s[H + i];
+  }
+  pk_sort_desc<H>(a);
+  pk_sort_desc<H>(b);
+  u16x2 t = __builtin_elementwise_max(a[0], b[H - 1]);
+#pragma unroll
+  for (int i = 1; i < H; ++i)
+    t = __builtin_elementwise_min(t, __builtin_elementwise_max(a[i], b[H - 1 - i]));
+  return t;
+}
+
 // The survivors of one group (half h of the packed keys) when more than n
 // keys reach tau: every key above tau, then the ties in position order.
 // Packed keys of entries 2j (sel 0x05040100) or 2j + 1 (sel 0x07060302)
@@ -646,8 +670,8 @@ __device__ __forceinline__ uint32_t nm_pk_ties(const uint32_t (&w)[M / 2], uint3
 }
 
 // One block of 2 * kNmPkThreads groups: thread tid takes groups 2 tid and
-// 2 tid + 1 of it, whose raw fp16 words are wa and wb.
-template <int M>
+// 2 tid + 1 of it, whose raw fp16 words are wa and wb.  HALF: n == M / 2.
+template <int M, bool HALF>
 __device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const uint32_t (&wb)[M / 2],
                                             int64_t blk, int64_t ngroups, int n,
                                             uint32_t* __restrict__ mask,
@@ -665,11 +689,16 @@ __device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const u
     sk[2 * j] = pk_vec(nm_pk_key(wa[j], wb[j], 0x05040100u));
     sk[2 * j + 1] = pk_vec(nm_pk_key(wa[j], wb[j], 0x07060302u));
   }
-  pk_sort_desc<M>(sk);
-  const int r = n - 1;  // 0 <= r < M (checked on the host); uniform
-  u16x2 tv = sk[0];
+  u16x2 tv;
+  if constexpr (HALF) {
+    tv = pk_half_tau<M>(sk);
+  } else {
+    pk_sort_desc<M>(sk);
+    const int r = n - 1;  // 0 <= r < M (checked on the host); uniform
+    tv = sk[0];
 #pragma unroll
-  for (int i = 1; i < M; ++i) tv = r == i ? sk[i] : tv;
+    for (int i = 1; i < M; ++i) tv = r == i ? sk[i] : tv;
+  }
   // Key i of A / B below its group's tau: sign bit 15 / 31 of the packed
   // difference.  Shifting it right by 15 - (i % 16) puts A's bit at
   // i % 16 and B's at 16 + i % 16; entries 16..31 gather in a second word.
@@ -732,7 +761,7 @@ __device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const u
   __syncthreads();  // outs is rewritten by the next block
 }
 
-template <int M>
+template <int M, bool HALF>
 __global__ __launch_bounds__(kNmPkThreads) void k_sparsify_nm_pk(const uint16_t* __restrict__ x,
                                                                int64_t ngroups, int n,
                                                                uint32_t* __restrict__ mask,
@@ -771,11 +800,11 @@ __global__ __launch_bounds__(kNmPkThreads) void k_sparsify_nm_pk(const uint16_t*
   if (blk < nblk) load(blk, a0, b0);
   while (blk < nblk) {
     if (blk + step < nblk) load(blk + step, a1, b1);
-    nm_pk_block<M>(a0, b0, blk, ngroups, n, mask, val, vec_out, outs);
+    nm_pk_block<M, HALF>(a0, b0, blk, ngroups, n, mask, val, vec_out, outs);
     blk += step;
     if (blk >= nblk) break;
     if (blk + step < nblk) load(blk + step, a0, b0);
-    nm_pk_block<M>(a1, b1, blk, ngroups, n, mask, val, vec_out, outs);
+    nm_pk_block<M, HALF>(a1, b1, blk, ngroups, n, mask, val, vec_out, outs);
     blk += step;
   }
 }
@@ -960,12 +989,15 @@ hipError_t launch_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n,
     const int64_t nblk = (ng + 2 * kNmPkThreads - 1) / (2 * kNmPkThreads);
     const int64_t cap = (int64_t)device_cus() * kNmPkBlocksPerCu;
     const dim3 grid((unsigned)(nblk < cap ? nblk : cap));
-    if (m == 16)
-      hipLaunchKernelGGL(k_sparsify_nm_pk<16>, grid, dim3(kNmPkThreads), 0, s, x, ng, n, mask,
-                         val, vec);
-    else
-      hipLaunchKernelGGL(k_sparsify_nm_pk<32>, grid, dim3(kNmPkThreads), 0, s, x, ng, n, mask,
-                         val, vec);
+    const bool half = 2 * n == m;
+#define SA_NM_PK(M, H) \
+  hipLaunchKernelGGL((k_sparsify_nm_pk<M, H>), grid, dim3(kNmPkThreads), 0, s, x, ng, n, mask, val, vec)
+    if (m == 16) {
+      if (half) SA_NM_PK(16, true); else SA_NM_PK(16, false);
+    } else {
+      if (half) SA_NM_PK(32, true); else SA_NM_PK(32, false);
+    }
+#undef SA_NM_PK
     return hipGetLastError();
   }
   const int64_t n8 = rows * d / 8;
