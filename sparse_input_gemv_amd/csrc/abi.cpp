@@ -244,12 +244,11 @@ int sparse_gemv_topk(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint
   c.d_in = d_in;
   c.batch = (int)batch;
   c.x = x;
-  c.cut = cut;
   c.topk_k = k;
   c.y = y;
   c.ws = ws;
   c.ws_bytes = ws_bytes;
-  return hip_status(sa::launch_gemv_topk(c, as_stream(stream)), "sparse_gemv_topk");
+  return hip_status(sa::launch_gemv_topk(c, cut, as_stream(stream)), "sparse_gemv_topk");
 }
 
 int sparse_gemv_threshold_noalloc(const uint16_t* wt, int64_t d_out, int64_t d_in,

@@ -2015,7 +2015,7 @@ int topk_fused_mode(int64_t d_out, int64_t d_in, int64_t batch, int64_t cus, int
 }
 }  // namespace
 
-hipError_t launch_gemv_topk(const GemvCall& c, hipStream_t s) {
+hipError_t launch_gemv_topk(const GemvCall& c, int32_t* cut, hipStream_t s) {
   GemvCall g = c;
   const int fused = topk_fused_mode(c.d_out, c.d_in, c.batch, device_cus(), 0, true, nullptr);
   if (fused != 0) {
@@ -2023,9 +2023,10 @@ hipError_t launch_gemv_topk(const GemvCall& c, hipStream_t s) {
     return launch_gemv(g, s);
   }
   const hipError_t e = launch_sparsify_topk(c.x, c.batch, c.d_in, c.topk_k, nullptr, nullptr,
-                                            nullptr, nullptr, 0, const_cast<int32_t*>(c.cut), s);
+                                            nullptr, nullptr, 0, cut, s);
   if (e != hipSuccess) return e;
   g.mode = kModeTopK;
+  g.cut = cut;
   return launch_gemv(g, s);
 }
 

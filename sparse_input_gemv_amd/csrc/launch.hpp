@@ -103,13 +103,13 @@ hipError_t gemv_noalloc_scratch(void** ptr);
 // Returns hipErrorInvalidValue if the workspace is too small for the launch
 // (checked by abi.cpp beforehand, so this is a second line of defence).
 hipError_t launch_gemv(const GemvCall& c, hipStream_t s);
-// Top-K GEMV (c.mode kModeTopK, c.cut the [batch][2] cutoff pairs in the
-// workspace, c.topk_k): one launch in which every workgroup selects the
+// Top-K GEMV (c.mode kModeTopK, c.topk_k; cut the [batch][2] cutoff pairs'
+// place in the workspace): one launch in which every workgroup selects the
 // row's cutoff itself where the in-workgroup select applies (split-K, batch
 // 1, d_in <= the workgroup's threads x kTopkSelPerThread), else the select
-// kernel writes c.cut and the GEMV reads it.
+// kernel writes cut and the GEMV reads it.
 constexpr int kTopkSelPerThread = 16;
-hipError_t launch_gemv_topk(const GemvCall& c, hipStream_t s);
+hipError_t launch_gemv_topk(const GemvCall& c, int32_t* cut, hipStream_t s);
 hipError_t launch_col_norms(const uint16_t* wt, int64_t d_in, int64_t d_out, double* out,
                             hipStream_t s);
 int gemv_set_tuning(int tiling, int target_wgs, int handoff);
