@@ -33,11 +33,11 @@ __device__ __forceinline__ int mag_key(uint16_t b) { return (int)(b & 0x7fffu); 
 
 // Loads E consecutive fp16 bit patterns starting at element k0 of a row
 // (entries past d read as 0).  The vector path needs a 16-byte aligned row
-// and k0 a multiple of 8.
+// and k0 a multiple of 8; runs of other lengths always load entry by entry.
 template <int E>
 __device__ __forceinline__ void load_run(const uint16_t* __restrict__ xr, int64_t k0, int64_t d,
                                          bool vec, uint16_t (&v)[E]) {
-  if (vec && k0 + E <= d) {
+  if (E % 8 == 0 && vec && k0 + E <= d) {
     const u32x4* p = reinterpret_cast<const u32x4*>(xr + k0);
 #pragma unroll
     for (int q = 0; q < E / 8; ++q) {
