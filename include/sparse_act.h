@@ -592,6 +592,22 @@ enum {
  */
 int sa_gemv_plan(int op, int64_t d_out, int64_t d_in, int64_t batch, int cus, int resident,
                  int* kernel, int* tile_o, int* grid_o, int* slices, int* handoff);
+/*
+ * The engine and output tile a matmul call would take, under the current
+ * sa_set_gemm_tuning choices, for inspection and performance work.  It
+ * computes nothing on the GPU and assumes 16-byte aligned operands.
+ *   op: 0 dense_gemm; 1 nm_act_spmm with pattern n:m (valid for d_in as
+ *     act_sparsify_nm requires), patterns other than 2:4 given a workspace.
+ *   T, d_in, d_out >= 1; cus: compute units to plan for (0: the current
+ *     device's).
+ * Outputs (HOST pointers, none NULL): engine 1 staged-register, 2
+ * pipelined (128-column tiles), 3 pipelined 256 x 256; tile_rows x
+ * tile_cols outputs per workgroup; tiles in the grid.
+ * Returns SA_ERR_INVALID_ARG for an unknown op or pattern, a size out of
+ * range or a NULL output.
+ */
+int sa_gemm_plan(int op, int64_t T, int64_t d_in, int64_t d_out, int n, int m, int cus,
+                 int* engine, int* tile_rows, int* tile_cols, int64_t* tiles);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ __all__ = [
     "masked_gemv",
     "dense_gemv", "masked_swiglu_down", "weight_col_norms", "nm_act_spmm", "nm_shared_spmm",
     "dense_gemm",
-    "set_gemv_tuning", "set_gemm_tuning", "gemv_tiling_info", "workspace_bytes",
+    "set_gemv_tuning", "set_gemm_tuning", "gemm_plan", "gemv_tiling_info", "workspace_bytes",
     "workspace_zero_bytes", "scratch", "MAX_BATCH",
 ]
 
@@ -84,6 +84,7 @@ _SIGNATURES = {
     "sa_set_gemm_tuning": (_i32, [_i32, _i32, _i32]),
     "sa_gemv_tiling_info": (_i32, [_i32, _vp, _vp, _vp]),
     "sa_gemv_plan": (_i32, [_i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "sa_gemm_plan": (_i32, [_i32, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "sa_set_gemv_test_hooks": (_i32, [_i32]),
 }
 
@@ -640,6 +641,19 @@ def gemv_plan(op: str, d_out: int, d_in: int, batch: int = 1, cus: int = 0, resi
     k, t, g, sl, h = (o.value for o in out)
     return {"kernel": "full-K" if k else "split-K", "tile_o": t, "grid_o": g, "slices": sl,
             "handoff": h}
+
+
+def gemm_plan(op: str, T: int, d_in: int, d_out: int, n: int = 0, m: int = 0, cus: int = 0):
+    """The engine and output tile a matmul call would take: a dict with
+    ``engine`` ("staged", "pipelined" or "wide"), ``tile_rows``, ``tile_cols``
+    and ``tiles``.  ``op`` is "dense" (dense_gemm) or "nm" (nm_act_spmm with
+    pattern n:m); ``cus`` 0 asks the current device."""
+    e, r, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    t = ctypes.c_int64()
+    _check(lib().sa_gemm_plan({"dense": 0, "nm": 1}[op], T, d_in, d_out, n, m, cus,
+                              *[ctypes.addressof(o) for o in (e, r, c, t)]), "sa_gemm_plan")
+    return {"engine": {1: "staged", 2: "pipelined", 3: "wide"}[e.value], "tile_rows": r.value,
+            "tile_cols": c.value, "tiles": t.value}
 
 
 def gemv_tiling_info(i: int):

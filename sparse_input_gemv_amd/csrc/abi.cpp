@@ -562,6 +562,23 @@ int sa_set_gemm_tuning(int tile_rows, int engine, int stages) {
   return SA_OK;
 }
 
+int sa_gemm_plan(int op, int64_t T, int64_t d_in, int64_t d_out, int n, int m, int cus,
+                 int* engine, int* tile_rows, int* tile_cols, int64_t* tiles) {
+  sa::clear_error();
+  const bool pattern_ok = op == 0 || (m >= 1 && n >= 1 && n <= m && (m == 4 || m == 8 ||
+                                                                     m == 16 || m == 32) &&
+                                      d_in % m == 0 && d_in % 32 == 0);
+  if ((op != 0 && op != 1) || !pattern_ok || T < 1 || d_in < 1 || d_out < 1 || cus < 0 ||
+      engine == nullptr || tile_rows == nullptr || tile_cols == nullptr || tiles == nullptr) {
+    sa::set_error("sa_gemm_plan: op must be 0 (dense_gemm) or 1 (nm_act_spmm, with a valid "
+                  "n:m for d_in), sizes >= 1, cus >= 0 and every output non-NULL");
+    return SA_ERR_INVALID_ARG;
+  }
+  sa::gemm_plan(op, T, d_in, d_out, n, m, cus > 0 ? cus : sa::device_cus(), engine, tile_rows,
+                tile_cols, tiles);
+  return SA_OK;
+}
+
 int sa_gemv_plan(int op, int64_t d_out, int64_t d_in, int64_t batch, int cus, int resident,
                  int* kernel, int* tile_o, int* grid_o, int* slices, int* handoff) {
   sa::clear_error();

@@ -1305,29 +1305,35 @@ hipError_t launch_wide(const GParams& p, hipStream_t s) {
 // rounds <= 1.29 * narrow tiles / (2 * CUs).  It picked the faster engine at
 // each of the 17 shapes measured (losses of 2-7% avoided at 1.1-1.3 rounds
 // and just past 2; gains of 6-15% elsewhere).
-bool wide_pays(const GParams& p) {
-  const int64_t cus = device_cus();
-  const int64_t wide = ((p.T + WBM - 1) / WBM) * ((p.d_out + WBN - 1) / WBN);
-  const int64_t narrow = ((p.T + 255) / 256) * ((p.d_out + PBN - 1) / PBN);
+bool wide_pays(int64_t T, int64_t d_out, int64_t cus) {
+  const int64_t wide = ((T + WBM - 1) / WBM) * ((d_out + WBN - 1) / WBN);
+  const int64_t narrow = ((T + 255) / 256) * ((d_out + PBN - 1) / PBN);
   const int64_t rounds = (wide + cus - 1) / cus;
   return 200 * rounds * cus <= 129 * narrow;
+}
+
+// Dense on the pipelined engines: the wide one where it pays (automatic
+// choice) or when asked for (engine 3).
+bool pipe_wide(int ak, int64_t T, int64_t d_out, int64_t cus) {
+  return ak == kADense &&
+         (g_gemm_engine == 3 || (g_gemm_engine == 0 && g_gemm_bm == 0 && wide_pays(T, d_out, cus)));
 }
 
 // Pipelined engine tile height (measured): dense 256 rows, or 128 when
 // 256-row tiles would give fewer workgroups than the device has CUs; 2:4
 // always 128, where two workgroups share a CU (faster at both configured
-// shapes).  Dense takes the wide engine where it pays (automatic choice) or
-// when asked for (engine 3).
+// shapes).
+int pipe_bm(int ak, int64_t T, int64_t d_out, int64_t cus) {
+  const int64_t tiles256 = ((T + 255) / 256) * ((d_out + PBN - 1) / PBN);
+  return g_gemm_bm ? g_gemm_bm : ((ak == kA24 || tiles256 < cus) ? 128 : 256);
+}
+
 template <int AK>
 hipError_t launch_pipe(const GParams& p, hipStream_t s) {
-  if constexpr (AK == kADense) {
-    if (g_gemm_engine == 3 || (g_gemm_engine == 0 && g_gemm_bm == 0 && wide_pays(p)))
-      return launch_wide(p, s);
-  }
+  const int64_t cus = device_cus();
+  if (pipe_wide(AK, p.T, p.d_out, cus)) return launch_wide(p, s);
   const int64_t ntl = (p.d_out + PBN - 1) / PBN;
-  const int64_t tiles256 = ((p.T + 255) / 256) * ntl;
-  const int bm =
-      g_gemm_bm ? g_gemm_bm : ((AK == kA24 || tiles256 < device_cus()) ? 128 : 256);
+  const int bm = pipe_bm(AK, p.T, p.d_out, cus);
   const int64_t tiles = ((p.T + bm - 1) / bm) * ntl;
   if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
   const int ns = g_gemm_stages ? g_gemm_stages : 3;
@@ -1347,12 +1353,15 @@ hipError_t launch_tile(const GParams& p, hipStream_t s) {
 // 256-row tiles when there are enough of them to fill the chip, 128 otherwise.
 // The zero-filled N:M staging (any pattern but 2:4) needs more registers per
 // row and measured slower at 256 rows, so it stays at 128 unless overridden.
+int kind_bm(int ak, int64_t T, int64_t d_out) {
+  const int64_t tiles256 = ((T + 255) / 256) * ((d_out + BN - 1) / BN);
+  const bool tall_ok = (ak == kADense || ak == kA24) && tiles256 >= 256;
+  return g_gemm_bm ? g_gemm_bm : (tall_ok ? 256 : 128);
+}
+
 template <int AK>
 hipError_t launch_kind(const GParams& p, hipStream_t s) {
-  const int64_t tiles256 = ((p.T + 255) / 256) * ((p.d_out + BN - 1) / BN);
-  const bool tall_ok = (AK == kADense || AK == kA24) && tiles256 >= 256;
-  const int bm = g_gemm_bm ? g_gemm_bm : (tall_ok ? 256 : 128);
-  if (bm == 256) return launch_tile<AK, 256>(p, s);
+  if (kind_bm(AK, p.T, p.d_out) == 256) return launch_tile<AK, 256>(p, s);
   return launch_tile<AK, 128>(p, s);
 }
 
@@ -1433,6 +1442,38 @@ hipError_t launch_nm_shared_spmm(const uint16_t* xval, const uint32_t* mask, int
   if (e != hipSuccess) return e;
   if (g_gemm_engine != 1 && pipe_ok<kADense>(pd)) return launch_pipe<kADense>(pd, s);
   return launch_kind<kADense>(pd, s);
+}
+
+int gemm_plan(int op, int64_t T, int64_t d_in, int64_t d_out, int n, int m, int64_t cus,
+              int* engine, int* tile_rows, int* tile_cols, int64_t* tiles) {
+  // the shape conditions of pipe_ok (16-byte aligned operands assumed)
+  auto pipe_shape = [&](int bk) { return d_in % bk == 0 && d_out % 8 == 0 && d_out >= 8; };
+  int ak = kADense;
+  bool pipe = false;
+  if (op == 0) {
+    pipe = g_gemm_engine != 1 && pipe_shape(Pipe<kADense, 256>::kBK);
+  } else if (n == 2 && m == 4) {
+    ak = kA24;
+    pipe = g_gemm_engine != 1 && pipe_shape(Pipe<kA24, 256>::kBK);
+  } else {  // the expanded copy on the dense engine, with a workspace
+    pipe = g_gemm_engine != 1 && pipe_shape(Pipe<kADense, 256>::kBK);
+    if (!pipe) ak = (4 * n) % m == 0 ? kANMVec : kANM;
+  }
+  if (pipe && pipe_wide(ak, T, d_out, cus)) {
+    *engine = 3;
+    *tile_rows = WBM;
+    *tile_cols = WBN;
+  } else if (pipe) {
+    *engine = 2;
+    *tile_rows = pipe_bm(ak, T, d_out, cus);
+    *tile_cols = PBN;
+  } else {
+    *engine = 1;
+    *tile_rows = kind_bm(ak, T, d_out);
+    *tile_cols = BN;
+  }
+  *tiles = ((T + *tile_rows - 1) / *tile_rows) * ((d_out + *tile_cols - 1) / *tile_cols);
+  return 0;
 }
 
 int gemm_set_tuning(int bm, int engine, int stages) {

@@ -132,6 +132,10 @@ int device_cus();
 
 hipError_t launch_dense_gemm(const uint16_t* x, int64_t T, int64_t d_in, const uint16_t* wt,
                              int64_t d_out, uint16_t* y, hipStream_t s);
+// The engine and tile a matmul call takes (op 0 dense_gemm, 1 nm_act_spmm
+// with a workspace), on `cus` compute units, under the current tuning.
+int gemm_plan(int op, int64_t T, int64_t d_in, int64_t d_out, int n, int m, int64_t cus,
+              int* engine, int* tile_rows, int* tile_cols, int64_t* tiles);
 size_t nm_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m);
 hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T, int64_t d_in,
                           int n, int m, const uint16_t* wt, int64_t d_out, uint16_t* y,

@@ -439,6 +439,63 @@ def test_plan_topk_forms(sa):
     assert _plan("topk", 4096, 1024, 4)["kernel"] == "split-K"
 
 
+def _gplan(op, T, d_in, d_out, n=0, m=0):
+    import sparse_input_gemv_amd as m_
+    return m_.gemm_plan(op, T, d_in, d_out, n, m, cus=256)
+
+
+def test_gemm_plan_engines(sa):
+    import sparse_input_gemv_amd as m
+    # 256 x 256 tiles only where their rounds over the CUs pay: 688 tiles of
+    # 256 x 128 at 2048 x 4096 x 11008 (344 wide tiles would take 1.34 rounds)
+    assert _gplan("dense", 2048, 4096, 11008) == {"engine": "pipelined", "tile_rows": 256,
+                                                  "tile_cols": 128, "tiles": 688}
+    assert _gplan("dense", 4096, 4096, 4096) == {"engine": "wide", "tile_rows": 256,
+                                                 "tile_cols": 256, "tiles": 256}
+    assert _gplan("dense", 2048, 4096, 13312)["tiles"] == 416  # wide, 1.6 rounds
+    assert _gplan("dense", 2048, 4096, 13312)["engine"] == "wide"
+    assert _gplan("dense", 4096, 4096, 11008)["engine"] == "wide"  # 688 wide tiles
+    assert _gplan("dense", 3072, 4096, 11008)["engine"] == "pipelined"  # 516: just past 2 rounds
+    # fewer 256-row tiles than CUs: 128-row tiles
+    assert _gplan("dense", 4096, 1024, 1024) == {"engine": "pipelined", "tile_rows": 128,
+                                                 "tile_cols": 128, "tiles": 256}
+    # K not a multiple of 32: the staged-register engine
+    assert _gplan("dense", 1000, 3000, 1032)["engine"] == "staged"
+    # 2:4 on 128-row pipelined tiles; other patterns on the dense engine's
+    # choice for the expanded copy
+    assert _gplan("nm", 2048, 4096, 11008, 2, 4) == {"engine": "pipelined", "tile_rows": 128,
+                                                     "tile_cols": 128, "tiles": 1376}
+    assert _gplan("nm", 4096, 4096, 4096, 8, 16)["engine"] == "wide"
+    assert _gplan("nm", 4096, 4096, 4096, 2, 4)["engine"] == "pipelined"
+    assert _gplan("nm", 2048, 4096, 11008, 16, 32)["engine"] == "pipelined"
+    try:
+        m.set_gemm_tuning(0, 3, 0)
+        assert _gplan("dense", 2048, 4096, 11008)["engine"] == "wide"
+        assert _gplan("nm", 2048, 4096, 11008, 2, 4)["engine"] == "pipelined"  # 2:4 stays
+        m.set_gemm_tuning(0, 2, 0)
+        assert _gplan("dense", 4096, 4096, 4096)["engine"] == "pipelined"
+        m.set_gemm_tuning(128, 0, 0)
+        assert _gplan("dense", 4096, 4096, 4096)["tile_rows"] == 128
+        m.set_gemm_tuning(0, 1, 0)
+        assert _gplan("dense", 4096, 4096, 4096)["engine"] == "staged"
+    finally:
+        m.set_gemm_tuning(0, 0, 0)
+
+
+def test_gemm_plan_checks(sa):
+    o = [ctypes.c_int() for _ in range(3)] + [ctypes.c_int64()]
+    a = [ctypes.addressof(x) for x in o]
+    assert sa.sa_gemm_plan(0, 2048, 4096, 11008, 0, 0, 256, *a) == SA_OK
+    assert sa.sa_gemm_plan(1, 2048, 4096, 11008, 2, 4, 256, *a) == SA_OK
+    assert sa.sa_gemm_plan(2, 2048, 4096, 11008, 0, 0, 256, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemm_plan(1, 2048, 4096, 11008, 3, 5, 256, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemm_plan(1, 2048, 4096, 11008, 5, 4, 256, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemm_plan(1, 2048, 4100, 11008, 2, 4, 256, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemm_plan(0, 0, 4096, 11008, 0, 0, 256, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemm_plan(0, 2048, 4096, 11008, 0, 0, -1, *a) == SA_ERR_INVALID_ARG
+    assert sa.sa_gemm_plan(0, 2048, 4096, 11008, 0, 0, 256, None, *a[1:]) == SA_ERR_INVALID_ARG
+
+
 def test_plan_follows_tuning(sa):
     import sparse_input_gemv_amd as m
     try:
