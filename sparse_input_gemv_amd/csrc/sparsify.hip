@@ -436,10 +436,11 @@ __global__ __launch_bounds__(NT) void k_topk(const uint16_t* __restrict__ x, int
 // the lists.  Measured (d = 4096, batch 1): 3.0 us for the pairs and 4.7 us
 // with the lists, against 4.5 and 6.6 us for k_topk, whose 128 KB of bins
 // take longer to clear and scan.  Longer rows stay on k_topk: at d = 11008
-// the radix select took 5.0 us with 1024 threads of 16 entries (4.96-5.24 us
-// for first-pass bins of 5, 4 or 3 low bits, so not atomic contention), 5.7
-// with 512 of 32, 8.0 with 256 of 48, and 6.3 with 1024 threads each holding
-// every 1024th entry, against 4.6 for k_topk.
+// the radix select took 5.0 us with 1024 threads of 16 entries (5.0-5.2 us
+// whether the first pass bins the keys' top 10, 11 or 12 bits, so LDS atomic
+// contention is not the cause), 5.7 with 512 of 32, 8.0 with 256 of 48, and
+// 6.3 with 1024 threads each holding every 1024th entry, against 4.6 for
+// k_topk.
 constexpr int kCutThreads = 512, kCutE = 8;
 template <int NT, int E>
 __global__ __launch_bounds__(NT) void k_topk_cut(const uint16_t* __restrict__ x, int64_t d,
