@@ -82,7 +82,9 @@ def test_single_layer_1024(seed):
     assert float(host(sa.act_calibrate_threshold(x_g, 0.5))[0]) == t
 
 
-@pytest.mark.parametrize("d", [1, 31, 32, 33, 100, 1000, 4097, 11008, 14336, 16385, 40000])
+# rows up to 4096 run 512 threads of 8 entries, longer ones 1024 threads of 16
+@pytest.mark.parametrize("d", [1, 31, 32, 33, 100, 1000, 4095, 4096, 4097, 11008, 14336, 16385,
+                               40000])
 def test_threshold_ragged_and_edges(d):
     rng = np.random.default_rng(d)
     X = syn.laplace_f16((3, d), 1.0, d)
