@@ -3,9 +3,11 @@
 // to a threshold).
 //
 // The histogram has one bin per fp16 magnitude (15-bit key), so the two
-// order statistics around the quantile position are found exactly: each is a
+// order statistics around the quantile position are found exactly: a
 // two-level radix select (256 bins of the high 8 key bits, then 128 bins of
-// the low 7) over the samples, in one workgroup.  The linear interpolation
+// the low 7) over the samples, in one workgroup, gives rank lo and, from the
+// same second pass, rank lo + 1 unless that one lies in a later high bin
+// (then a second select).  The linear interpolation
 // is done in fp64, operation by operation, and rounded once to fp32.
 #include <math.h>
 
@@ -17,13 +19,37 @@ namespace {
 
 constexpr int kCalThreads = 1024;
 
-// Key of the r-th smallest magnitude (0-based).  All threads call it.
-__device__ int select_rank(const uint16_t* __restrict__ smp, int64_t n, int64_t r, int* hist,
-                           int* sel) {
+// Samples held in registers: up to kCalThreads x kCalRun of them, thread t
+// holding the run from t kCalRun (loaded once for all four passes); larger
+// sample sets are read from memory in every pass.
+constexpr int kCalRun = 16;
+struct RegKeys {
+  int key[kCalRun];  // -1 past the end
+  template <typename F>
+  __device__ __forceinline__ void each(F f) const {
+#pragma unroll
+    for (int e = 0; e < kCalRun; ++e)
+      if (key[e] >= 0) f(key[e]);
+  }
+};
+struct MemKeys {
+  const uint16_t* smp;
+  int64_t n;
+  template <typename F>
+  __device__ __forceinline__ void each(F f) const {
+    for (int64_t i = threadIdx.x; i < n; i += kCalThreads) f(mag_key(smp[i]));
+  }
+};
+
+// Key of the r-th smallest magnitude (0-based), and in *next the key of
+// rank r + 1 when the second pass already holds it (rank r + 1 in the same
+// 128-key bin), else -1.  All threads call it.
+template <typename Keys>
+__device__ int select_rank(const Keys& keys, int64_t r, int* hist, int* sel, int* next) {
   const int tid = (int)threadIdx.x;
   for (int i = tid; i < 256; i += kCalThreads) hist[i] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < n; i += kCalThreads) atomicAdd(&hist[mag_key(smp[i]) >> 7], 1);
+  keys.each([&](int key) { atomicAdd(&hist[key >> 7], 1); });
   __syncthreads();
   if (tid < kWave) {
     // lane l holds bins 4l..4l+3; C(b) = count in bins <= b.  The bins with
@@ -66,10 +92,9 @@ __device__ int select_rank(const uint16_t* __restrict__ smp, int64_t n, int64_t 
   __syncthreads();
   for (int i = tid; i < 128; i += kCalThreads) hist[i] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < n; i += kCalThreads) {
-    const int key = mag_key(smp[i]);
+  keys.each([&](int key) {
     if ((key >> 7) == b1) atomicAdd(&hist[key & 127], 1);
-  }
+  });
   __syncthreads();
   if (tid < kWave) {
     const int c0 = hist[tid * 2], c1 = hist[tid * 2 + 1];
@@ -82,12 +107,20 @@ __device__ int select_rank(const uint16_t* __restrict__ smp, int64_t n, int64_t 
     const int C0 = below + pre - c1;  // count <= bin 2l
     const int C1 = below + pre;       // count <= bin 2l+1
     int nb = (C0 <= r ? 1 : 0) + (C1 <= r ? 1 : 0);
+    int nb1 = (C0 <= r + 1 ? 1 : 0) + (C1 <= r + 1 ? 1 : 0);
 #pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) nb += __shfl_xor(nb, o, kWave);
-    if (tid == 0) sel[2] = (b1 << 7) | nb;
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      nb += __shfl_xor(nb, o, kWave);
+      nb1 += __shfl_xor(nb1, o, kWave);
+    }
+    if (tid == 0) {
+      sel[2] = (b1 << 7) | nb;
+      sel[3] = nb1 < 128 ? ((b1 << 7) | nb1) : -1;
+    }
   }
   __syncthreads();
   const int key = sel[2];
+  *next = sel[3];
   __syncthreads();
   return key;
 }
@@ -116,8 +149,21 @@ __global__ __launch_bounds__(kCalThreads) void k_calibrate(const uint16_t* __res
   if (lo < 0) lo = 0;
   if (lo > n - 1) lo = n - 1;
   const int64_t hi = (lo + 1 < n) ? lo + 1 : n - 1;
-  const int key_lo = select_rank(smp, n, lo, hist, sel);
-  const int key_hi = (hi == lo) ? key_lo : select_rank(smp, n, hi, hist, sel);
+  int key_lo, key_hi, next;
+  if (n <= (int64_t)kCalThreads * kCalRun) {
+    RegKeys keys;
+    const int64_t k0 = (int64_t)threadIdx.x * kCalRun;
+    uint16_t v[kCalRun];
+    load_run<kCalRun>(smp, k0, n, (reinterpret_cast<uintptr_t>(smp) & 15u) == 0, v);
+#pragma unroll
+    for (int e = 0; e < kCalRun; ++e) keys.key[e] = k0 + e < n ? mag_key(v[e]) : -1;
+    key_lo = select_rank(keys, lo, hist, sel, &next);
+    key_hi = (hi == lo) ? key_lo : next >= 0 ? next : select_rank(keys, hi, hist, sel, &next);
+  } else {
+    const MemKeys keys{smp, n};
+    key_lo = select_rank(keys, lo, hist, sel, &next);
+    key_hi = (hi == lo) ? key_lo : next >= 0 ? next : select_rank(keys, hi, hist, sel, &next);
+  }
   if (threadIdx.x == 0) t_out[0] = interpolate(n, s, key_lo, key_hi);
 }
 

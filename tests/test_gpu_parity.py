@@ -437,7 +437,8 @@ def test_calibration_bit_exact(inp):
 
 
 def test_calibration_small_n():
-    for n in (1, 2, 3, 7, 1025):
+    # up to 16384 samples are held in registers; more are read in every pass
+    for n in (1, 2, 3, 7, 1025, 16383, 16384, 16385, 40000):
         smp = syn.laplace_f16((n,), 1.0, n)
         for s in (0.0, 0.3, 0.5, 1.0):
             t_ref = calibrate.magnitude_threshold(smp, s)
