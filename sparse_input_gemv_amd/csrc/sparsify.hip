@@ -601,6 +601,13 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kNmPkThreads = 256;
 constexpr int kNmPkBlocksPerCu = 4;  // workgroups of the grid per compute unit
+// LDS region of one thread's outputs (its two groups' survivors, at most
+// 2 M - 2 values) plus its spare slot, in fp16 units.  M + 1 dwords is odd,
+// so the 64 lanes' regions start on 64 different banks: with regions of
+// 2 n values (M / 2 or M dwords, a multiple of 8) the lanes' stores met on
+// 4 to 8 banks.
+template <int M>
+constexpr int kNmPkRegion = 2 * M + 2;
 
 __device__ __forceinline__ uint32_t pk_bits(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ u16x2 pk_vec(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
@@ -726,10 +733,10 @@ __device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const u
 
   if (has_a) {
     // every entry is stored: a kept one at its slot, a dropped one at this
-    // thread's spare slot past the outputs (no branch per entry)
+    // thread's spare slot, the last of its region (no branch per entry)
     // (slot - spare masked by 0 or -1, the entry's bit sign-extended)
-    const int spare = (int)kGroups * M + tid;
-    int sa = tid * 2 * n - spare, sb = sa + n;  // next slot of A / B, from spare
+    const int spare = tid * kNmPkRegion<M> + kNmPkRegion<M> - 1;
+    int sa = tid * kNmPkRegion<M> - spare, sb = sa + n;  // next slot of A / B, from spare
     const uint32_t kb = has_b ? keep_b : 0u;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
@@ -754,12 +761,23 @@ __device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const u
   const int64_t first = blk * kGroups;  // the block's first group
   const int64_t ng = (ngroups - first) < kGroups ? (ngroups - first) : kGroups;
   const int count = (int)ng * n;
+  const int per = 2 * n;  // outputs of one thread's region
   uint16_t* dst = val + first * n;
-  if (vec_out && (count % 8) == 0) {
-    for (int i = tid; i < count / 8; i += kNmPkThreads)
-      *reinterpret_cast<u32x4*>(dst + 8 * i) = *reinterpret_cast<const u32x4*>(outs + 8 * i);
+  if (vec_out && (count % 8) == 0 && (per % 8) == 0) {
+    // 8 outputs never straddle two regions; a region starts on a dword
+    for (int i = tid; i < count / 8; i += kNmPkThreads) {
+      const int e = 8 * i;
+      const int r = (HALF ? e / M : e / per);
+      const uint32_t* src =
+          reinterpret_cast<const uint32_t*>(outs + r * kNmPkRegion<M> + (e - r * per));
+      const u32x4 v = {src[0], src[1], src[2], src[3]};
+      *reinterpret_cast<u32x4*>(dst + e) = v;
+    }
   } else {
-    for (int i = tid; i < count; i += kNmPkThreads) dst[i] = outs[i];
+    for (int i = tid; i < count; i += kNmPkThreads) {
+      const int r = i / per;
+      dst[i] = outs[r * kNmPkRegion<M> + (i - r * per)];
+    }
   }
   __syncthreads();  // outs is rewritten by the next block
 }
@@ -773,7 +791,7 @@ __global__ __launch_bounds__(kNmPkThreads) void k_sparsify_nm_pk(const uint16_t*
   static_assert(M == 16 || M == 32, "two whole groups per thread");
   constexpr int W = M / 2;                       // 32-bit words of one group
   constexpr int64_t kGroups = kNmPkThreads * 2;  // groups of one block
-  __shared__ __align__(16) uint16_t outs[kGroups * M + kNmPkThreads];  // + a spare slot each
+  __shared__ __align__(16) uint16_t outs[kNmPkThreads * kNmPkRegion<M>];
   const int tid = (int)threadIdx.x;
   const int64_t nblk = (ngroups + kGroups - 1) / kGroups;
   // A workgroup walks blocks blockIdx.x, + gridDim.x, ...; the next block's
