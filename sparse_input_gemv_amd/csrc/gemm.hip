@@ -967,6 +967,160 @@ __global__ __launch_bounds__(WNT, 1) void k_gemm_wide(GParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Wide 2:4 engine (k_gemm_wide24): the wide engine's 256 x 256 tiles and
+// eight 128 x 64 wave tiles on the sparse MFMA.  A K step covers 64 dense k:
+// A holds 32 compressed values per row ([256][32], 64-byte rows swizzled as
+// the dense A) and the row's two mask words ([256][2]); B holds 64 k rows of
+// 256 columns ([64][256], as the wide B).  A stage is 50 KB, three fit the
+// LDS (one workgroup per CU).  Per 64 dense k a 128 x 128 2:4 tile stages
+// 25 KB for 1.05 MFLOP of sparse MFMA work and a wide tile 50 KB for 4.2, so
+// the load path carries half as much per FLOP.  The MFMA sequence per output
+// block is the pipelined 2:4 engine's: identical results.
+// ---------------------------------------------------------------------------
+constexpr int kW24BK = 64;
+constexpr int kW24AHalves = WBM * kW24BK / 2;   // [256][32] compressed
+constexpr int kW24MaskWords = WBM * 2;          // [256][2]
+constexpr int kW24StageHalves = kW24AHalves + kW24BK * WBN + 2 * kW24MaskWords;
+constexpr int kW24LoadsPerWave = 7;  // two A, four B, one mask instruction
+constexpr int kW24Stages = 3;
+static_assert(kW24Stages * kW24StageHalves * 2 + 256 <= 160 * 1024, "wide 2:4 stages fit the LDS");
+
+__device__ __forceinline__ void wide24_issue(const GParams& p, int64_t m0, int64_t n0, int64_t k0,
+                                             uint16_t* S) {
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  uint16_t* As = S;
+  uint16_t* Bs = S + kW24AHalves;
+  uint32_t* Ms = reinterpret_cast<uint32_t*>(Bs + kW24BK * WBN);
+  const int64_t kc = p.d_in / 2;  // compressed row length
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rb = (w * 2 + i) * 16;  // 16 rows of 64 bytes per instruction
+    const int r = rb + lane / 4;
+    const int gc = (lane % 4) ^ swz_a(r);
+    int64_t row = m0 + r;
+    if (row >= p.T) row = p.T - 1;
+    load_to_lds16(p.x + row * kc + k0 / 2 + 8 * gc, As + rb * (kW24BK / 2));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kb = (w * 4 + i) * 2;  // 2 k rows of 512 bytes per instruction
+    const int k = kb + lane / 32;
+    const int gc = (lane % 32) ^ swz_b(k);
+    int64_t n = n0 + 8 * gc;
+    if (n >= p.d_out) n = p.d_out - 8;
+    load_to_lds16(p.wt + (k0 + k) * p.d_out + n, Bs + kb * WBN);
+  }
+  {
+    const int rb = w * 32;  // 32 rows of 2 words per instruction
+    const int r = rb + lane / 2;
+    int64_t row = m0 + r;
+    if (row >= p.T) row = p.T - 1;
+    load_to_lds4(p.mask + row * (p.d_in / 32) + k0 / 32 + (lane % 2), Ms + rb * 2);
+  }
+}
+
+// One K step of a wave's 128 x 64 tile (pipe_compute's 2:4 branch).
+__device__ __forceinline__ void wide24_compute(const uint16_t* S, const uint8_t* code_lut,
+                                               f16v (&acc)[4][2], int wm, int wn) {
+  const int lane = lane_id();
+  const uint16_t* As = S;
+  const uint16_t* Bs = S + kW24AHalves;
+  const uint32_t* Ms = reinterpret_cast<const uint32_t*>(Bs + kW24BK * WBN);
+#pragma unroll
+  for (int kk = 0; kk < kW24BK / 32; ++kk) {
+    h8 aop[4];
+    int code[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int m = wm * 128 + 32 * a + lane % 32;
+      const int q = 2 * kk + lane / 32;
+      aop[a] = *reinterpret_cast<const h8*>(As + m * (kW24BK / 2) + 8 * (q ^ swz_a(m)));
+      const uint32_t bits = Ms[m * 2 + kk] >> (16 * (lane / 32));
+      code[a] = (int)code_lut[bits & 0xffu] | ((int)code_lut[(bits >> 8) & 0xffu] << 8);
+    }
+    // one column block at a time: a single 16-value B operand is live
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int c0 = wn * 64 + 32 * b;
+      const s4v q0 = wide_b_quad(Bs, kk * 32, c0), q1 = wide_b_quad(Bs, kk * 32 + 4, c0);
+      const s4v q2 = wide_b_quad(Bs, kk * 32 + 16, c0), q3 = wide_b_quad(Bs, kk * 32 + 20, c0);
+      typedef short s16v __attribute__((ext_vector_type(16)));
+      const s16v all = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3],
+                        q2[0], q2[1], q2[2], q2[3], q3[0], q3[1], q3[2], q3[3]};
+      const h16 bop = __builtin_bit_cast(h16, all);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        acc[a][b] =
+            __builtin_amdgcn_smfmac_f32_32x32x32_f16(aop[a], bop, acc[a][b], code[a], 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(WNT, 1) void k_gemm_wide24(GParams p) {
+  constexpr int NS = kW24Stages;
+  __shared__ __align__(16) uint16_t S[NS * kW24StageHalves];
+  __shared__ uint8_t code_lut[256];
+  const int lane = lane_id();
+  const int wave = (int)threadIdx.x / kWave;
+  const int wm = wave / 4, wn = wave % 4;
+  const int64_t mt = (p.T + WBM - 1) / WBM;
+  const int64_t ntl = (p.d_out + WBN - 1) / WBN;
+  int64_t mi, ni;
+  pipe_tile(blockIdx.x, mt, ntl, mi, ni);
+  const int64_t m0 = mi * WBM, n0 = ni * WBN;
+  f16v acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  // position code of every mask byte; the first stage barrier orders these
+  // writes before any read
+  if (threadIdx.x < 256) code_lut[threadIdx.x] = (uint8_t)code_of(threadIdx.x);
+
+  constexpr int D = NS - 1;
+  const int64_t nk = p.d_in / kW24BK;
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nk) wide24_issue(p, m0, n0, j * kW24BK, S + j * kW24StageHalves);
+  int64_t kt = 0;
+  for (; kt + NS + D - 1 < nk; kt += NS) {
+    // stages rolled, not unrolled: one set of LDS addresses stays live
+#pragma unroll 1
+    for (int j = 0; j < NS; ++j) {
+      stage_barrier<(D - 1) * kW24LoadsPerWave>();
+      wide24_issue(p, m0, n0, (kt + j + D) * kW24BK, S + ((j + D) % NS) * kW24StageHalves);
+      wide24_compute(S + j * kW24StageHalves, code_lut, acc, wm, wn);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NS + D - 1; ++j) {
+    const int64_t t = kt + j;
+    if (t < nk) {
+      const int64_t later = nk - 1 - t;
+      stage_barrier_upto<kW24LoadsPerWave, D - 1>(later < D - 1 ? (int)later : D - 1);
+      if (t + D < nk)
+        wide24_issue(p, m0, n0, (t + D) * kW24BK, S + ((j + D) % NS) * kW24StageHalves);
+      wide24_compute(S + (j % NS) * kW24StageHalves, code_lut, acc, wm, wn);
+    }
+  }
+
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = n0 + wn * 64 + b * 32 + lane % 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 128 + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        if (row < p.T && col < p.d_out) p.y[row * p.d_out + col] = f2h(acc[a][b][r]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Tile-shared N:M engine.  Every 32-row block of tokens lies in one tile of
 // tt rows (tt a multiple of 32), so its rows share one N:M pattern; over one
 // K step the block's product is a dense MFMA product of the compressed values
@@ -1305,11 +1459,38 @@ hipError_t launch_wide(const GParams& p, hipStream_t s) {
 // rounds <= 1.29 * narrow tiles / (2 * CUs).  It picked the faster engine at
 // each of the 17 shapes measured (losses of 2-7% avoided at 1.1-1.3 rounds
 // and just past 2; gains of 6-15% elsewhere).
+// 2:4 on wide tiles or on 128 x 128 tiles (two per CU).  Measured at
+// K = 4096: a round of wide tiles takes ~108 us and a round of 128 x 128
+// tiles ~71 us, so per unit of work the wide engine is ~1.3x faster, but it
+// runs in whole rounds of one tile per CU.  The wide engine is taken when
+// its rounds stay within 1.5x its tile count per CU: 344 tiles (2 rounds;
+// 190 against 206 us), 256, 688, 896 and 1376 tiles take it; 64 and 128
+// tiles (a round mostly idle: 28 against 16 us, 99 against 75 us) do not.
+bool wide24_pays(int64_t T, int64_t d_out, int64_t cus) {
+  const int64_t wide = ((T + WBM - 1) / WBM) * ((d_out + WBN - 1) / WBN);
+  const int64_t rounds = (wide + cus - 1) / cus;
+  return 100 * rounds * cus <= 150 * wide;
+}
+
 bool wide_pays(int64_t T, int64_t d_out, int64_t cus) {
   const int64_t wide = ((T + WBM - 1) / WBM) * ((d_out + WBN - 1) / WBN);
   const int64_t narrow = ((T + 255) / 256) * ((d_out + PBN - 1) / PBN);
   const int64_t rounds = (wide + cus - 1) / cus;
   return 200 * rounds * cus <= 129 * narrow;
+}
+
+hipError_t launch_wide24(const GParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.T + WBM - 1) / WBM) * ((p.d_out + WBN - 1) / WBN);
+  if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
+  hipLaunchKernelGGL(k_gemm_wide24, dim3((unsigned)tiles), dim3(WNT), 0, s, p);
+  return hipGetLastError();
+}
+
+// 2:4 on the wide engine: when asked for (engine 3), or automatically where
+// it pays (wide24_pays).
+bool wide24_pays(int64_t T, int64_t d_out, int64_t cus);
+bool wide24_chosen(int64_t T, int64_t d_out, int64_t cus) {
+  return g_gemm_engine == 3 || (g_gemm_engine == 0 && g_gemm_bm == 0 && wide24_pays(T, d_out, cus));
 }
 
 // Dense on the pipelined engines: the wide one where it pays (automatic
@@ -1459,7 +1640,7 @@ int gemm_plan(int op, int64_t T, int64_t d_in, int64_t d_out, int n, int m, int6
     pipe = g_gemm_engine != 1 && pipe_shape(Pipe<kADense, 256>::kBK);
     if (!pipe) ak = (4 * n) % m == 0 ? kANMVec : kANM;
   }
-  if (pipe && pipe_wide(ak, T, d_out, cus)) {
+  if (pipe && (pipe_wide(ak, T, d_out, cus) || (ak == kA24 && wide24_chosen(T, d_out, cus)))) {
     *engine = 3;
     *tile_rows = WBM;
     *tile_cols = WBN;
@@ -1520,7 +1701,10 @@ hipError_t launch_nm_spmm(const uint16_t* xval, const uint32_t* mask, int64_t T,
   // 2:4 on the sparse MFMA; every other pattern through zero-filled dense
   // tiles (vector loads when m divides 4n)
   if (n == 2 && m == 4) {
-    if (g_gemm_engine != 1 && pipe_ok<kA24>(p)) return launch_pipe<kA24>(p, s);
+    if (g_gemm_engine != 1 && pipe_ok<kA24>(p)) {
+      if (wide24_chosen(T, d_out, device_cus())) return launch_wide24(p, s);
+      return launch_pipe<kA24>(p, s);
+    }
     return launch_kind<kA24>(p, s);
   }
   // two passes through the dense pipelined engine when a workspace is given

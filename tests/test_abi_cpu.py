@@ -461,17 +461,24 @@ def test_gemm_plan_engines(sa):
                                                  "tile_cols": 128, "tiles": 256}
     # K not a multiple of 32: the staged-register engine
     assert _gplan("dense", 1000, 3000, 1032)["engine"] == "staged"
-    # 2:4 on 128-row pipelined tiles; other patterns on the dense engine's
+    # 2:4 on wide tiles once their rounds stay within 1.5x the tiles per CU,
+    # else on 128-row pipelined tiles; other patterns on the dense engine's
     # choice for the expanded copy
-    assert _gplan("nm", 2048, 4096, 11008, 2, 4) == {"engine": "pipelined", "tile_rows": 128,
-                                                     "tile_cols": 128, "tiles": 1376}
+    assert _gplan("nm", 2048, 4096, 11008, 2, 4) == {"engine": "wide", "tile_rows": 256,
+                                                     "tile_cols": 256, "tiles": 344}
+    assert _gplan("nm", 4096, 4096, 4096, 2, 4)["engine"] == "wide"
+    assert _gplan("nm", 1024, 4096, 16384, 2, 4)["engine"] == "wide"  # 256: one whole round
+    assert _gplan("nm", 2048, 4096, 4096, 2, 4) == {"engine": "pipelined", "tile_rows": 128,
+                                                   "tile_cols": 128, "tiles": 512}
+    assert _gplan("nm", 4096, 1024, 1024, 2, 4)["engine"] == "pipelined"
+    assert _gplan("nm", 1024, 4096, 16640, 2, 4)["engine"] == "pipelined"  # 260: 2 rounds
     assert _gplan("nm", 4096, 4096, 4096, 8, 16)["engine"] == "wide"
-    assert _gplan("nm", 4096, 4096, 4096, 2, 4)["engine"] == "pipelined"
     assert _gplan("nm", 2048, 4096, 11008, 16, 32)["engine"] == "pipelined"
     try:
         m.set_gemm_tuning(0, 3, 0)
         assert _gplan("dense", 2048, 4096, 11008)["engine"] == "wide"
-        assert _gplan("nm", 2048, 4096, 11008, 2, 4)["engine"] == "pipelined"  # 2:4 stays
+        assert _gplan("nm", 2048, 4096, 11008, 2, 4) == {"engine": "wide", "tile_rows": 256,
+                                                         "tile_cols": 256, "tiles": 344}
         m.set_gemm_tuning(0, 2, 0)
         assert _gplan("dense", 4096, 4096, 4096)["engine"] == "pipelined"
         m.set_gemm_tuning(128, 0, 0)

@@ -998,6 +998,33 @@ def test_nm24_k_pipeline_lengths(T, d_in, d_out, tile_rows, stages):
     assert_close(Y, ref)
 
 
+@pytest.mark.parametrize("T,d_in,d_out", [(1, 64, 8), (300, 128, 264), (257, 192, 520),
+                                          (40, 256, 136), (513, 320, 256), (64, 384, 1000),
+                                          (100, 448, 72), (256, 512, 512), (33, 704, 264),
+                                          (70, 2176, 256)])
+def test_nm24_wide_engine(T, d_in, d_out):
+    """2:4 on the 256 x 256-tile engine (engine 3): K steps of 64 from 1 to
+    34 (the tail alone, one rolled round and more), ragged rows and columns.
+    Against the oracle, and bit for bit against the 128 x 128-tile engine
+    (same sparse MFMA sequence per output block)."""
+    X = syn.gaussian_f16((T, d_in), 1.0, 11 * T + d_in)
+    X[0, :] = np.float16(0.5)  # ties
+    wt = syn.weight_t(d_out, d_in, d_out + 7)
+    keep, _ = sparsify.nm_sparsify(X, 2, 4)
+    mask_g, val_g = sa.act_sparsify_nm(dev(X), 2, 4)
+    wt_g = dev(wt)
+    try:
+        sa.set_gemm_tuning(0, 3, 0)
+        assert sa.gemm_plan("nm", T, d_in, d_out, 2, 4)["engine"] == "wide"
+        Yw = sa.nm_act_spmm(val_g, mask_g, 2, 4, wt_g).clone()
+        sa.set_gemm_tuning(128, 2, 0)
+        Yn = sa.nm_act_spmm(val_g, mask_g, 2, 4, wt_g).clone()
+    finally:
+        sa.set_gemm_tuning(0, 0, 0)
+    assert torch.equal(Yw, Yn)
+    assert_close(Yw, spmm.nm_spmm(X, keep, wt))
+
+
 @pytest.mark.parametrize("choice", GEMM_CHOICES)
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 4), (3, 4), (5, 16),
                                  (32, 32)])
