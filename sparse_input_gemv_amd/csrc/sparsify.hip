@@ -586,7 +586,8 @@ __global__ __launch_bounds__(kNmThreads) void k_sparsify_nm(const uint16_t* __re
   }
 }
 
-// N:M, M = 16 / 32: each thread takes two consecutive groups A and B whole
+// N:M, M = 16 / 32 with n != M / 2 (n = M / 2 takes k_sparsify_nm_half
+// below): each thread takes two consecutive groups A and B whole
 // (2M entries, M/4 16-byte loads) and works on both at once: entry i of A
 // and entry i of B share one 32-bit register, A in the low half, so each
 // compare-exchange of a sorting network over the M registers is one packed
@@ -636,30 +637,6 @@ __device__ __forceinline__ void pk_sort_desc(u16x2 (&s)[N]) {
   }
 }
 
-// tau for n = M / 2 without the full sort: each half sorted (descending),
-// then the half-cleaner -- max(a_i, b_(M/2-1-i)) over the two sorted halves
-// are the M/2 largest keys as a set (a sorted half followed by the other
-// reversed is bitonic) -- and tau is their minimum.  For 16 keys: 2 x 19
-// compare-exchanges + 8 max + 7 min (91 packed operations) against 63
-// compare-exchanges (126); for 32: 2 x 63 + 16 + 15 (283) against 191 (382).
-template <int M>
-__device__ __forceinline__ u16x2 pk_half_tau(const u16x2 (&s)[M]) {
-  constexpr int H = M / 2;
-  u16x2 a[H], b[H];
-#pragma unroll
-  for (int i = 0; i < H; ++i) {
-    a[i] = s[i];
-    b[i] = s[H + i];
-  }
-  pk_sort_desc<H>(a);
-  pk_sort_desc<H>(b);
-  u16x2 t = __builtin_elementwise_max(a[0], b[H - 1]);
-#pragma unroll
-  for (int i = 1; i < H; ++i)
-    t = __builtin_elementwise_min(t, __builtin_elementwise_max(a[i], b[H - 1 - i]));
-  return t;
-}
-
 // The survivors of one group (half h of the packed keys) when more than n
 // keys reach tau: every key above tau, then the ties in position order.
 // Packed keys of entries 2j (sel 0x05040100) or 2j + 1 (sel 0x07060302)
@@ -680,8 +657,8 @@ __device__ __forceinline__ uint32_t nm_pk_ties(const uint32_t (&w)[M / 2], uint3
 }
 
 // One block of 2 * kNmPkThreads groups: thread tid takes groups 2 tid and
-// 2 tid + 1 of it, whose raw fp16 words are wa and wb.  HALF: n == M / 2.
-template <int M, bool HALF>
+// 2 tid + 1 of it, whose raw fp16 words are wa and wb.
+template <int M>
 __device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const uint32_t (&wb)[M / 2],
                                             int64_t blk, int64_t ngroups, int n,
                                             uint32_t* __restrict__ mask,
@@ -699,16 +676,11 @@ __device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const u
     sk[2 * j] = pk_vec(nm_pk_key(wa[j], wb[j], 0x05040100u));
     sk[2 * j + 1] = pk_vec(nm_pk_key(wa[j], wb[j], 0x07060302u));
   }
-  u16x2 tv;
-  if constexpr (HALF) {
-    tv = pk_half_tau<M>(sk);
-  } else {
-    pk_sort_desc<M>(sk);
-    const int r = n - 1;  // 0 <= r < M (checked on the host); uniform
-    tv = sk[0];
+  pk_sort_desc<M>(sk);
+  const int r = n - 1;  // 0 <= r < M (checked on the host); uniform
+  u16x2 tv = sk[0];
 #pragma unroll
-    for (int i = 1; i < M; ++i) tv = r == i ? sk[i] : tv;
-  }
+  for (int i = 1; i < M; ++i) tv = r == i ? sk[i] : tv;
   // Key i of A / B below its group's tau: sign bit 15 / 31 of the packed
   // difference.  Shifting it right by 15 - (i % 16) puts A's bit at
   // i % 16 and B's at 16 + i % 16; entries 16..31 gather in a second word.
@@ -767,7 +739,7 @@ __device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const u
     // 8 outputs never straddle two regions; a region starts on a dword
     for (int i = tid; i < count / 8; i += kNmPkThreads) {
       const int e = 8 * i;
-      const int r = (HALF ? e / M : e / per);
+      const int r = e / per;
       const uint32_t* src =
           reinterpret_cast<const uint32_t*>(outs + r * kNmPkRegion<M> + (e - r * per));
       const u32x4 v = {src[0], src[1], src[2], src[3]};
@@ -782,7 +754,7 @@ __device__ __forceinline__ void nm_pk_block(const uint32_t (&wa)[M / 2], const u
   __syncthreads();  // outs is rewritten by the next block
 }
 
-template <int M, bool HALF>
+template <int M>
 __global__ __launch_bounds__(kNmPkThreads) void k_sparsify_nm_pk(const uint16_t* __restrict__ x,
                                                                int64_t ngroups, int n,
                                                                uint32_t* __restrict__ mask,
@@ -821,12 +793,154 @@ __global__ __launch_bounds__(kNmPkThreads) void k_sparsify_nm_pk(const uint16_t*
   if (blk < nblk) load(blk, a0, b0);
   while (blk < nblk) {
     if (blk + step < nblk) load(blk + step, a1, b1);
-    nm_pk_block<M, HALF>(a0, b0, blk, ngroups, n, mask, val, vec_out, outs);
+    nm_pk_block<M>(a0, b0, blk, ngroups, n, mask, val, vec_out, outs);
     blk += step;
     if (blk >= nblk) break;
     if (blk + step < nblk) load(blk + step, a0, b0);
-    nm_pk_block<M, HALF>(a1, b1, blk, ngroups, n, mask, val, vec_out, outs);
+    nm_pk_block<M>(a1, b1, blk, ngroups, n, mask, val, vec_out, outs);
     blk += step;
+  }
+}
+
+// n = m / 2 for m = 16, 32 with one group per thread: entry i of the group
+// (low half) and entry m/2 + i (high half) share packed key register i, so
+// one packed sort of m/2 registers sorts both halves of the group at once,
+// and the half-cleaner pairs half a's i-th largest with half b's
+// (m/2 - 1 - i)-th: tau, the (m/2)-th largest key, is min over i of
+// max(a_i, b_(m/2-1-i)).  A thread holds one group's m raw values and m/2
+// keys instead of k_sparsify_nm_pk's two groups, so more waves share a SIMD
+// and cover each other's loads (16:32 at 2048 x 4096: 8.03 -> 6.86 us).
+constexpr int kNmHalfThreads = 256;
+constexpr int kNmHalfBlocksPerCu = 8;  // workgroups of the grid per compute unit
+// LDS region of one thread's m/2 survivors plus its spare slot, fp16 units:
+// m/4 + 1 dwords, odd, so the lanes' regions start on distinct banks
+template <int M>
+constexpr int kNmHalfRegion = M / 2 + 2;
+
+template <int M>
+__global__ __launch_bounds__(kNmHalfThreads) void k_sparsify_nm_half(
+    const uint16_t* __restrict__ x, int64_t ngroups, uint32_t* __restrict__ mask,
+    uint16_t* __restrict__ val, int vec_out) {
+  static_assert(M == 16 || M == 32, "packed halves of one group");
+  constexpr int N = M / 2;   // survivors per group; also packed key registers
+  constexpr int W = M / 2;   // 32-bit words of raw values
+  constexpr int RG = kNmHalfRegion<M>;
+  __shared__ __align__(16) uint16_t outs[kNmHalfThreads * RG];
+  const int tid = (int)threadIdx.x;
+  const int64_t nblk = (ngroups + kNmHalfThreads - 1) / kNmHalfThreads;
+  // Groups past the end read the last group instead (their results are not
+  // stored): every load is unconditional.
+  auto load = [&](int64_t blk, uint32_t (&w)[W]) {
+    int64_t g = blk * kNmHalfThreads + tid;
+    if (g >= ngroups) g = ngroups - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + g * M);
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const u32x4 r = src[q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[4 * q + c] = r[c];
+    }
+  };
+  // packed key of entries i (low) and N + i (high)
+  auto key2 = [&](const uint32_t (&w)[W], int i) {
+    return nm_pk_key(w[i / 2], w[N / 2 + i / 2], (i & 1) ? 0x07060302u : 0x05040100u);
+  };
+  auto block = [&](const uint32_t (&w)[W], int64_t blk) {
+    const int64_t g = blk * kNmHalfThreads + tid;
+    u16x2 sk[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) sk[i] = pk_vec(key2(w, i));
+    pk_sort_desc<N>(sk);
+    // r_i = max(a_i, b_(N-1-i)) in the low half, max(b_i, a_(N-1-i)) -- the
+    // low half of r_(N-1-i) -- in the high half: r_0 .. r_(N/2-1) hold all N
+    auto swapped = [](u16x2 v) {
+      return pk_vec(__builtin_amdgcn_alignbit(pk_bits(v), pk_bits(v), 16));
+    };
+    u16x2 t = __builtin_elementwise_max(sk[0], swapped(sk[N - 1]));
+#pragma unroll
+    for (int i = 1; i < N / 2; ++i)
+      t = __builtin_elementwise_min(t, __builtin_elementwise_max(sk[i], swapped(sk[N - 1 - i])));
+    const uint32_t tb = pk_bits(t);
+    const uint32_t tau = (tb & 0xffffu) < (tb >> 16) ? (tb & 0xffffu) : (tb >> 16);
+    const u16x2 tv = pk_vec(tau | (tau << 16));
+    // entry i below tau: sign bit 15 of the packed difference, entry N + i:
+    // bit 31; shifted right by 15 - i they land on bits i and 16 + i
+    uint32_t lt = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t dd = pk_bits(pk_vec(key2(w, i)) - tv);
+      lt |= (dd >> (15 - i)) & (0x10001u << i);
+    }
+    if constexpr (M == 16) lt = (lt & 0xffu) | ((lt >> 8) & 0xff00u);
+    constexpr uint32_t kAll = M == 32 ? 0xffffffffu : 0xffffu;
+    uint32_t keep = ~lt & kAll;
+    if (__popc(keep) > N) {
+      // ties at tau: every key above it, then the first ties in position order
+      uint32_t gt = 0;
+#pragma unroll
+      for (int i = 0; i < M; ++i)
+        gt |= (((w[i / 2] >> (16 * (i & 1))) & 0x7fffu) > tau ? 1u : 0u) << i;
+      uint32_t ties = keep & ~gt;
+      for (int drop = __popc(keep) - N; drop > 0; --drop) ties &= ~(1u << (31 - __clz(ties)));
+      keep = gt | ties;
+    }
+    if (g < ngroups) {
+      // every entry is stored: a kept one at its slot, a dropped one at the
+      // spare slot ending the region (slot - spare masked by 0 or -1)
+      const int spare = tid * RG + RG - 1;
+      int sl = tid * RG - spare;
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int m = (int)(keep << (31 - i)) >> 31;
+        outs[spare + (sl & m)] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+        sl -= m;
+      }
+      if constexpr (M == 32)
+        mask[g] = keep;
+      else  // two groups per mask word, group g in half g % 2
+        reinterpret_cast<uint16_t*>(mask)[g] = (uint16_t)keep;
+    }
+    __syncthreads();
+    const int64_t first = blk * kNmHalfThreads;
+    const int64_t ng = (ngroups - first) < kNmHalfThreads ? (ngroups - first) : kNmHalfThreads;
+    const int count = (int)ng * N;
+    uint16_t* dst = val + first * N;
+    if (vec_out) {
+      // 8 values of one region per item; a region starts on a dword
+      for (int i = tid; i < count / 8; i += kNmHalfThreads) {
+        const int r = i / (N / 8);
+        const uint32_t* src =
+            reinterpret_cast<const uint32_t*>(outs + r * RG + 8 * (i % (N / 8)));
+        const u32x4 v = {src[0], src[1], src[2], src[3]};
+        *reinterpret_cast<u32x4*>(dst + 8 * i) = v;
+      }
+    } else {
+      for (int i = tid; i < count; i += kNmHalfThreads) dst[i] = outs[(i / N) * RG + (i % N)];
+    }
+    __syncthreads();  // outs is rewritten by the next block
+  };
+  const int64_t step = gridDim.x;
+  if constexpr (M == 32) {
+    // one register set: the grid holds every block at once where registers
+    // allow (four waves per SIMD), and a second set would cost occupancy
+    uint32_t w0[W];
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += step) {
+      load(blk, w0);
+      block(w0, blk);
+    }
+  } else {
+    uint32_t w0[W], w1[W];
+    int64_t blk = blockIdx.x;
+    if (blk < nblk) load(blk, w0);
+    while (blk < nblk) {
+      if (blk + step < nblk) load(blk + step, w1);
+      block(w0, blk);
+      blk += step;
+      if (blk >= nblk) break;
+      if (blk + step < nblk) load(blk + step, w0);
+      block(w1, blk);
+      blk += step;
+    }
   }
 }
 
@@ -1015,18 +1129,28 @@ hipError_t launch_sparsify_nm(const uint16_t* x, int64_t rows, int64_t d, int n,
   const int vec = (reinterpret_cast<uintptr_t>(val) & 15u) == 0 ? 1 : 0;
   if (m == 16 || m == 32) {
     const int64_t ng = rows * d / m;
+    if (2 * n == m) {  // one group per thread, both halves in packed registers
+      const int64_t nb = (ng + kNmHalfThreads - 1) / kNmHalfThreads;
+      const int64_t cap2 = (int64_t)device_cus() * kNmHalfBlocksPerCu;
+      const dim3 g2((unsigned)(nb < cap2 ? nb : cap2));
+      if (m == 32)
+        hipLaunchKernelGGL(k_sparsify_nm_half<32>, g2, dim3(kNmHalfThreads), 0, s, x, ng, mask,
+                           val, vec);
+      else
+        hipLaunchKernelGGL(k_sparsify_nm_half<16>, g2, dim3(kNmHalfThreads), 0, s, x, ng, mask,
+                           val, vec);
+      return hipGetLastError();
+    }
+    // other n: two groups per thread and the full sort
     const int64_t nblk = (ng + 2 * kNmPkThreads - 1) / (2 * kNmPkThreads);
     const int64_t cap = (int64_t)device_cus() * kNmPkBlocksPerCu;
     const dim3 grid((unsigned)(nblk < cap ? nblk : cap));
-    const bool half = 2 * n == m;
-#define SA_NM_PK(M, H) \
-  hipLaunchKernelGGL((k_sparsify_nm_pk<M, H>), grid, dim3(kNmPkThreads), 0, s, x, ng, n, mask, val, vec)
-    if (m == 16) {
-      if (half) SA_NM_PK(16, true); else SA_NM_PK(16, false);
-    } else {
-      if (half) SA_NM_PK(32, true); else SA_NM_PK(32, false);
-    }
-#undef SA_NM_PK
+    if (m == 16)
+      hipLaunchKernelGGL(k_sparsify_nm_pk<16>, grid, dim3(kNmPkThreads), 0, s, x, ng, n, mask,
+                         val, vec);
+    else
+      hipLaunchKernelGGL(k_sparsify_nm_pk<32>, grid, dim3(kNmPkThreads), 0, s, x, ng, n, mask,
+                         val, vec);
     return hipGetLastError();
   }
   const int64_t n8 = rows * d / 8;
