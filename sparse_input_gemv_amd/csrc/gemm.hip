@@ -1121,6 +1121,176 @@ __global__ __launch_bounds__(WNT, 1) void k_gemm_wide24(GParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Tile-shared N:M on 32-row tiles (k_gemm_g32): the whole-tile gather for
+// tiles of tt rows with tt a multiple of 32 (VW32 is tt = 32).  A 256-thread
+// workgroup computes a 32 x 128 output tile, one 32-row block of one pattern:
+// each wave one 32 x 32 block (wave w: columns 32 w .. 32 w + 31).  The K
+// loop runs over the d_in n / m compressed entries in steps of 32 through NS
+// stages of 10 KB: A [32][32] (the compressed values, rows swizzled as the
+// dense A) and B [32][128], the kept WT rows of the pattern only (as in the
+// whole-tile gather), so B bytes fall to n / m of dense.  Small stages let
+// five workgroups share a CU, whose loads cover each other's latency.
+//   Loads per step: A is 2 KB, one instruction each for waves 0 and 1; B is
+//   two instructions per wave.  A wave's stage wait counts its own loads.
+// The MFMA sequence per output block is the whole-tile gather's (compressed
+// k in order, 16 per MFMA): identical results.
+// ---------------------------------------------------------------------------
+constexpr int kG32BK = 32;
+constexpr int kG32AHalves = 32 * kG32BK;         // [32][32]
+constexpr int kG32StageHalves = kG32AHalves + kG32BK * PBN;
+constexpr int kG32GroupM = 16;  // row tiles grouped across the column tiles (L2 reuse of B)
+
+__device__ __forceinline__ void g32_issue(const GParams& p, int64_t m0, int64_t n0, int64_t k0,
+                                          uint16_t* S, const uint32_t* mrow, bool table) {
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  uint16_t* As = S;
+  uint16_t* Bs = S + kG32AHalves;
+  // this lane's two B rows of the step (entries k0 + 8 w + lane / 16 and
+  // + 4), read from the byte table before the A load so its latency
+  // overlaps it
+  uint32_t pair = 0;
+  if (table)
+    pair = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(mrow) + k0 + 8 * w +
+                                               2 * (lane / 16));
+  const int64_t lda = p.d_in / p.m * p.n;
+  if (w < 2) {
+    const int rb = w * 16;  // 16 rows of 64 bytes
+    const int r = rb + lane / 4;
+    const int gc = (lane % 4) ^ swz_a(r);
+    int64_t row = m0 + r;
+    if (row >= p.T) row = p.T - 1;
+    load_to_lds16(p.x + row * lda + k0 + 8 * gc, As + rb * kG32BK);
+  }
+  const int lper = __builtin_ctz((unsigned)(32 / p.m * p.n));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int kb = (w * 2 + i) * 4;  // 4 k rows of 256 bytes per instruction
+    const int k = kb + lane / 16;
+    const int gc = (lane % 16) ^ swz_b(k);
+    int64_t n = n0 + 8 * gc;
+    if (n >= p.d_out) n = p.d_out - 8;
+    const int64_t j = k0 + k;  // compressed entry
+    const int64_t wd = j >> lper;
+    const int pos = table ? (int)((pair >> (8 * i)) & 0xffu)
+                          : select_bit(mrow[wd], (int)(j & ((1 << lper) - 1)));
+    int64_t row = 32 * wd + pos;
+    if (row > p.d_in - 1) row = p.d_in - 1;
+    load_to_lds16(p.wt + row * p.d_out + n, Bs + kb * PBN);
+  }
+}
+
+__device__ __forceinline__ void g32_compute(const uint16_t* S, f16v& acc, int w) {
+  const int lane = lane_id();
+  const uint16_t* As = S;
+  const uint16_t* Bs = S + kG32AHalves;
+#pragma unroll
+  for (int kk = 0; kk < kG32BK / 16; ++kk) {
+    const int m = lane % 32;
+    const int q = 2 * kk + lane / 32;
+    const h8 aop = *reinterpret_cast<const h8*>(As + m * kG32BK + 8 * (q ^ swz_a(m)));
+    const int c0 = w * 32;
+    const s4v q0 = b_quad(Bs, kk * 16, c0), q1 = b_quad(Bs, kk * 16 + 4, c0);
+    typedef short s8v __attribute__((ext_vector_type(8)));
+    const s8v both = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, __builtin_bit_cast(h8, both), acc, 0, 0, 0);
+  }
+}
+
+// Stage wait of wave w: waves 0 and 1 have three loads per step, 2 and 3 two.
+template <int LATER>
+__device__ __forceinline__ void g32_barrier(int w) {
+  if (w < 2)
+    stage_barrier<LATER * 3>();
+  else
+    stage_barrier<LATER * 2>();
+}
+__device__ __forceinline__ void g32_barrier_upto(int w, int later) {
+  if (later >= 2)
+    g32_barrier<2>(w);
+  else if (later == 1)
+    g32_barrier<1>(w);
+  else
+    g32_barrier<0>(w);
+}
+
+// TB: bytes of the pattern table, sized to the call (512, 2048 or 4096
+// kept entries) so that more workgroups fit a CU; at 4096 the table also
+// holds the mask row for longer patterns.
+template <int NS, int TB>
+__global__ __launch_bounds__(NTH) void k_gemm_g32(GParams p) {
+  static_assert(NS == 3 || NS == 4, "the waits cover a prefetch distance of 2 or 3 steps");
+  static_assert(TB % 4 == 0 && TB <= kGatherTableBytes, "table size");
+  constexpr int D = NS - 1;
+  __shared__ __align__(16) uint16_t S[NS * kG32StageHalves];
+  __shared__ uint32_t mrow[TB / 4];
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int64_t mt = (p.T + 31) / 32;
+  const int64_t ntl = (p.d_out + PBN - 1) / PBN;
+  // grouped order, kG32GroupM row tiles across all column tiles, row tile
+  // fastest; each XCD takes a contiguous run of it (as pipe_tile)
+  int64_t mi, ni;
+  {
+    const int64_t b = blockIdx.x;
+    const int64_t G = mt * ntl;
+    const int64_t x = b % 8, l = b / 8;
+    const int64_t per = G / 8, rem = G % 8;
+    const int64_t t = x * per + (x < rem ? x : rem) + l;
+    const int64_t gsz = kG32GroupM * ntl;
+    const int64_t first = (t / gsz) * kG32GroupM;
+    const int64_t gm = (mt - first < kG32GroupM) ? mt - first : kG32GroupM;
+    mi = first + (t % gsz) % gm;
+    ni = (t % gsz) / gm;
+  }
+  const int64_t m0 = mi * 32, n0 = ni * PBN;
+  // the tile's pattern: the byte table of kept positions (as k_gemm_pipe's
+  // gather) or the mask row itself
+  const int64_t wpr = p.d_in / 32;
+  const uint32_t* src = p.mask + (m0 / p.tt) * wpr;
+  const bool table = p.d_in / p.m * p.n <= TB;  // else TB = 4096: the mask row (<= 1024 words)
+  if (table) {
+    const int per = 32 / p.m * p.n;
+    uint8_t* tab = reinterpret_cast<uint8_t*>(mrow);
+    for (int64_t i = threadIdx.x; i < wpr; i += NTH) {
+      uint32_t bits = src[i];
+      for (int e = 0; e < per; ++e) {
+        const int64_t j = i * per + e;
+        tab[(j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1)] = (uint8_t)(bits ? __builtin_ctz(bits) : 31);
+        bits &= bits - 1u;
+      }
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < wpr; i += NTH) mrow[i] = src[i];
+  }
+  __syncthreads();
+
+  f16v acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int nk = (int)(p.d_in / p.m * p.n / kG32BK);
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nk) g32_issue(p, m0, n0, j * kG32BK, S + j * kG32StageHalves, mrow, table);
+  for (int t = 0; t < nk; ++t) {
+    // wait for step t's loads, leaving the later steps' in flight (at most
+    // D - 1 of them), then refill the stage step t - 1 used
+    const int later = nk - 1 - t;
+    g32_barrier_upto(w, later < D - 1 ? later : D - 1);
+    if (t + D < nk)
+      g32_issue(p, m0, n0, (int64_t)(t + D) * kG32BK, S + ((t + D) % NS) * kG32StageHalves, mrow,
+                table);
+    g32_compute(S + (t % NS) * kG32StageHalves, acc, w);
+  }
+  const int64_t col = n0 + w * 32 + lane % 32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t row = m0 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+    if (row < p.T && col < p.d_out) p.y[row * p.d_out + col] = f2h(acc[r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tile-shared N:M engine.  Every 32-row block of tokens lies in one tile of
 // tt rows (tt a multiple of 32), so its rows share one N:M pattern; over one
 // K step the block's product is a dense MFMA product of the compressed values
@@ -1574,6 +1744,28 @@ bool gather_shape_ok(int64_t d_in, int n, int m, int tt) {
          d_in <= 32 * kGatherMaskWords && (d_in / m * n) % 32 == 0;
 }
 
+// 32-row tiles of one pattern (tt a multiple of 32), only the kept WT rows.
+bool g32_shape_ok(int64_t d_in, int n, int m, int tt) {
+  return tt % 32 == 0 && n >= 1 && 32 % n == 0 && n <= m && d_in % m == 0 &&
+         d_in <= 32 * kGatherMaskWords && (d_in / m * n) % kG32BK == 0;
+}
+
+hipError_t launch_g32(const GParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.T + 31) / 32) * ((p.d_out + PBN - 1) / PBN);
+  if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
+  const int64_t kept = p.d_in / p.m * p.n;
+  const dim3 grid((unsigned)tiles);
+  if (g_gemm_stages >= 4)
+    hipLaunchKernelGGL((k_gemm_g32<4, kGatherTableBytes>), grid, dim3(NTH), 0, s, p);
+  else if (kept <= 512)
+    hipLaunchKernelGGL((k_gemm_g32<3, 512>), grid, dim3(NTH), 0, s, p);
+  else if (kept <= 2048)
+    hipLaunchKernelGGL((k_gemm_g32<3, 2048>), grid, dim3(NTH), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemm_g32<3, kGatherTableBytes>), grid, dim3(NTH), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const GParams& p, hipStream_t s) {
   const int64_t ntl = (p.d_out + PBN - 1) / PBN;
   const int64_t tiles256 = ((p.T + 255) / 256) * ntl;
@@ -1589,7 +1781,9 @@ hipError_t launch_gather(const GParams& p, hipStream_t s) {
 }  // namespace
 
 size_t nm_shared_spmm_workspace_bytes(int64_t T, int64_t d_in, int n, int m, int tt) {
-  if (gather_shape_ok(d_in, n, m, tt) || shared_engine_ok(d_in, n, m, tt)) return 0;
+  if (gather_shape_ok(d_in, n, m, tt) || g32_shape_ok(d_in, n, m, tt) ||
+      shared_engine_ok(d_in, n, m, tt))
+    return 0;
   return (size_t)T * (size_t)d_in * 2;
 }
 
@@ -1609,6 +1803,10 @@ hipError_t launch_nm_shared_spmm(const uint16_t* xval, const uint32_t* mask, int
   p.m = m;
   p.tt = tt;
   if (gather_shape_ok(d_in, n, m, tt)) return launch_gather(p, s);
+  // 32-row tiles, unless a tile height is asked for and the per-block
+  // gather can take the shape
+  if (g32_shape_ok(d_in, n, m, tt) && (g_gemm_bm == 0 || !shared_engine_ok(d_in, n, m, tt)))
+    return launch_g32(p, s);
   if (shared_engine_ok(d_in, n, m, tt)) {
     if (32 * m / n == 64) return launch_shared_kb<64>(p, s);
     return launch_shared_kb<128>(p, s);

@@ -162,8 +162,10 @@ def test_nm_shared_checks(sa):
     assert ws(100, 1024, 8, 16, 16) == 100 * 1024 * 2
     assert ws(100, 1056, 8, 16, 32) == 100 * 1056 * 2  # d_in not a multiple of the K step
     assert ws(100, 1024, 3, 4, 32) == 100 * 1024 * 2
-    assert ws(100, 1024, 1, 8, 32) == 100 * 1024 * 2   # m / n = 8
-    assert ws(100, 1024, 32, 32, 32) == 100 * 1024 * 2  # m / n = 1
+    assert ws(100, 1024, 1, 8, 32) == 0                # m / n = 8: 32-row-tile gather
+    assert ws(100, 1024, 32, 32, 32) == 0               # m / n = 1: 32-row-tile gather
+    assert ws(100, 1024, 1, 8, 48) == 100 * 1024 * 2    # tiles not a multiple of 32 rows
+    assert ws(100, 40000, 8, 16, 32) == 0  # past the 32-row gather's mask copy: per-block gather
     assert ws(100, 1024, 1, 8, 128) == 0               # whole-tile gather
     assert ws(100, 1024, 3, 4, 128) == 100 * 1024 * 2   # n does not divide 32
     assert ws(10, 65536, 1, 8, 128) == 10 * 65536 * 2   # mask row beyond the LDS copy

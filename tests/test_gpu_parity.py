@@ -1183,14 +1183,68 @@ def test_nm_shared_spmm_gathering_kernel(T, d_in, d_out, tt, n, m, tile_rows):
     assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
 
 
+def shared_g32(d_in, n, m, tt):
+    """Conditions of the 32-row-tile gather."""
+    return (tt % 32 == 0 and 32 % n == 0 and d_in % m == 0 and d_in <= 32768
+            and (d_in // m * n) % 32 == 0)
+
+
+@pytest.mark.parametrize("stages", [3, 4])
+@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (2, 4), (1, 4), (4, 16), (1, 8), (32, 32)])
+@pytest.mark.parametrize("T,d_in,d_out,tt", [(64, 1024, 512, 32), (100, 128, 136, 32),
+                                             (33, 256, 8, 32), (1, 512, 1000, 64),
+                                             (257, 640, 128, 96), (300, 384, 264, 160),
+                                             (70, 2048, 256, 32)])
+def test_nm_shared_spmm_g32(T, d_in, d_out, tt, n, m, stages):
+    """32-row tiles of one pattern, only the pattern's kept WT rows loaded:
+    1 to 64 K steps of 32 compressed entries, ragged rows and columns,
+    tiles of 32 to 160 rows, both stage counts.  Against the oracle, and
+    bit for bit against the per-32-row-block gather where that kernel takes
+    the shape (the same MFMA sequence per output block)."""
+    if not shared_g32(d_in, n, m, tt) or shared_whole_tile(d_in, n, m, tt):
+        pytest.skip("not a 32-row-tile shape")
+    X = syn.gaussian_f16((T, d_in), 1.0, 3 * T + d_in + n)
+    X[0, :] = np.float16(0.5)  # a tile of ties
+    wt = syn.weight_t(d_out, d_in, d_out + 2 * m)
+    _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+    mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), n, m, tt)
+    wt_g = dev(wt)
+    try:
+        sa.set_gemm_tuning(0, 0, stages)
+        Y = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, wt_g).clone()
+        if shared_per_block(d_in, n, m, tt):
+            sa.set_gemm_tuning(128, 0, 0)
+            Yb = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, wt_g)
+            assert torch.equal(Y, Yb)
+    finally:
+        sa.set_gemm_tuning(0, 0, 0)
+    assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
+
+
+@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (1, 4)])
+def test_nm_shared_g32_long_k(n, m):
+    """32-row tiles past 4096 kept entries per row: the kept positions come
+    from the mask words instead of the byte table."""
+    T, d_in, d_out, tt = 96, 16384, 264, 32
+    if d_in // m * n <= 4096:
+        pytest.skip("within the byte table")
+    X = syn.gaussian_f16((T, d_in), 1.0, d_in + 3 * n)
+    wt = syn.weight_t(d_out, d_in, 19 + m)
+    _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
+    mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), n, m, tt)
+    Y = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, dev(wt))
+    assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
+
+
 @pytest.mark.parametrize("n,m,tt", [(3, 4, 32), (5, 16, 32), (7, 8, 64), (8, 16, 1), (8, 16, 16),
-                                    (2, 4, 7), (16, 32, 48), (1, 8, 32), (4, 32, 32), (32, 32, 32),
-                                    (4, 4, 64), (3, 4, 128), (5, 8, 256)])
+                                    (2, 4, 7), (16, 32, 48), (1, 8, 48), (4, 32, 40), (32, 32, 16),
+                                    (4, 4, 48), (3, 4, 128), (5, 8, 256)])
 def test_nm_shared_spmm_expanded(n, m, tt):
     """Tiles and patterns outside the gathering kernels: expansion into the
     workspace, then the dense matmul."""
     T, d_in, d_out = 130, 256, 264
     assert not shared_per_block(d_in, n, m, tt) and not shared_whole_tile(d_in, n, m, tt)
+    assert not shared_g32(d_in, n, m, tt)
     assert sa.lib().sa_nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt) == T * d_in * 2
     X = syn.gaussian_f16((T, d_in), 1.0, n * 7 + m + tt)
     wt = syn.weight_t(d_out, d_in, 3 * m)
