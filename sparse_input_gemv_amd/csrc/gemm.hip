@@ -1136,23 +1136,51 @@ __global__ __launch_bounds__(WNT, 1) void k_gemm_wide24(GParams p) {
 // k in order, 16 per MFMA): identical results.
 // ---------------------------------------------------------------------------
 constexpr int kG32BK = 32;
-constexpr int kG32AHalves = 32 * kG32BK;         // [32][32]
-constexpr int kG32StageHalves = kG32AHalves + kG32BK * PBN;
+constexpr int kG32AHalves = 32 * kG32BK;  // [32][32]
 constexpr int kG32GroupM = 16;  // row tiles grouped across the column tiles (L2 reuse of B)
+// Per tile width BN (128 or 256 columns): stage size and B loads per wave
+// and step (1 KB instructions of 4 rows of 256 bytes, or 2 rows of 512).
+template <int BN>
+struct G32 {
+  static_assert(BN == 128 || BN == 256, "tile width");
+  static constexpr int kStageHalves = kG32AHalves + kG32BK * BN;
+  static constexpr int kBLoads = kG32BK * BN * 2 / 1024 / 4;
+  static constexpr int kBlocks = BN / 128;  // 32 x 32 blocks per wave
+};
 
+// Pattern table entry of compressed entry j.  At 128 columns a lane loads
+// entries j and j + 4 of a step, stored side by side; at 256 columns the
+// table is in entry order.
+template <int BN>
+__device__ __forceinline__ int g32_slot(int64_t j) {
+  if constexpr (BN == 128)
+    return (int)((j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1));
+  else
+    return (int)j;
+}
+
+template <int BN>
 __device__ __forceinline__ void g32_issue(const GParams& p, int64_t m0, int64_t n0, int64_t k0,
                                           uint16_t* S, const uint32_t* mrow, bool table) {
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   uint16_t* As = S;
   uint16_t* Bs = S + kG32AHalves;
-  // this lane's two B rows of the step (entries k0 + 8 w + lane / 16 and
-  // + 4), read from the byte table before the A load so its latency
-  // overlaps it
-  uint32_t pair = 0;
-  if (table)
-    pair = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(mrow) + k0 + 8 * w +
-                                               2 * (lane / 16));
+  const uint8_t* tab = reinterpret_cast<const uint8_t*>(mrow);
+  // this lane's B rows of the step, read from the table before the A load
+  // so that their latency overlaps it
+  constexpr int BL = G32<BN>::kBLoads;
+  int pos[BL];
+  if constexpr (BN == 128) {
+    // entries k0 + 8 w + lane / 16 and + 4: one 16-bit read
+    const uint32_t pair =
+        table ? *reinterpret_cast<const uint16_t*>(tab + k0 + 8 * w + 2 * (lane / 16)) : 0u;
+    pos[0] = (int)(pair & 0xffu);
+    pos[1] = (int)(pair >> 8);
+  } else {
+#pragma unroll
+    for (int i = 0; i < BL; ++i) pos[i] = table ? (int)tab[k0 + (w * BL + i) * 2 + lane / 32] : 0;
+  }
   const int64_t lda = p.d_in / p.m * p.n;
   if (w < 2) {
     const int rb = w * 16;  // 16 rows of 64 bytes
@@ -1164,23 +1192,26 @@ __device__ __forceinline__ void g32_issue(const GParams& p, int64_t m0, int64_t 
   }
   const int lper = __builtin_ctz((unsigned)(32 / p.m * p.n));
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int kb = (w * 2 + i) * 4;  // 4 k rows of 256 bytes per instruction
-    const int k = kb + lane / 16;
-    const int gc = (lane % 16) ^ swz_b(k);
+  for (int i = 0; i < BL; ++i) {
+    constexpr int RPI = 1024 / (2 * BN);  // k rows per instruction
+    constexpr int CPR = BN / 8;           // 16-byte chunks per row
+    const int kb = (w * BL + i) * RPI;
+    const int k = kb + lane / CPR;
+    const int gc = (lane % CPR) ^ swz_b(k);
     int64_t n = n0 + 8 * gc;
     if (n >= p.d_out) n = p.d_out - 8;
     const int64_t j = k0 + k;  // compressed entry
     const int64_t wd = j >> lper;
-    const int pos = table ? (int)((pair >> (8 * i)) & 0xffu)
-                          : select_bit(mrow[wd], (int)(j & ((1 << lper) - 1)));
-    int64_t row = 32 * wd + pos;
+    const int ps = table ? pos[i] : select_bit(mrow[wd], (int)(j & ((1 << lper) - 1)));
+    int64_t row = 32 * wd + ps;
     if (row > p.d_in - 1) row = p.d_in - 1;
-    load_to_lds16(p.wt + row * p.d_out + n, Bs + kb * PBN);
+    load_to_lds16(p.wt + row * p.d_out + n, Bs + kb * BN);
   }
 }
 
-__device__ __forceinline__ void g32_compute(const uint16_t* S, f16v& acc, int w) {
+template <int BN>
+__device__ __forceinline__ void g32_compute(const uint16_t* S, f16v (&acc)[G32<BN>::kBlocks],
+                                            int w) {
   const int lane = lane_id();
   const uint16_t* As = S;
   const uint16_t* Bs = S + kG32AHalves;
@@ -1189,45 +1220,59 @@ __device__ __forceinline__ void g32_compute(const uint16_t* S, f16v& acc, int w)
     const int m = lane % 32;
     const int q = 2 * kk + lane / 32;
     const h8 aop = *reinterpret_cast<const h8*>(As + m * kG32BK + 8 * (q ^ swz_a(m)));
-    const int c0 = w * 32;
-    const s4v q0 = b_quad(Bs, kk * 16, c0), q1 = b_quad(Bs, kk * 16 + 4, c0);
-    typedef short s8v __attribute__((ext_vector_type(8)));
-    const s8v both = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, __builtin_bit_cast(h8, both), acc, 0, 0, 0);
+#pragma unroll
+    for (int b = 0; b < G32<BN>::kBlocks; ++b) {
+      const int c0 = w * (BN / 4) + 32 * b;
+      s4v q0, q1;
+      if constexpr (BN == 128) {
+        q0 = b_quad(Bs, kk * 16, c0);
+        q1 = b_quad(Bs, kk * 16 + 4, c0);
+      } else {
+        q0 = wide_b_quad(Bs, kk * 16, c0);
+        q1 = wide_b_quad(Bs, kk * 16 + 4, c0);
+      }
+      typedef short s8v __attribute__((ext_vector_type(8)));
+      const s8v both = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+      acc[b] =
+          __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, __builtin_bit_cast(h8, both), acc[b], 0, 0, 0);
+    }
   }
 }
 
-// Stage wait of wave w: waves 0 and 1 have three loads per step, 2 and 3 two.
-template <int LATER>
+// Stage wait of wave w: waves 0 and 1 also load A, one more load per step.
+template <int BL, int LATER>
 __device__ __forceinline__ void g32_barrier(int w) {
   if (w < 2)
-    stage_barrier<LATER * 3>();
+    stage_barrier<LATER * (BL + 1)>();
   else
-    stage_barrier<LATER * 2>();
+    stage_barrier<LATER * BL>();
 }
+template <int BL>
 __device__ __forceinline__ void g32_barrier_upto(int w, int later) {
   if (later >= 2)
-    g32_barrier<2>(w);
+    g32_barrier<BL, 2>(w);
   else if (later == 1)
-    g32_barrier<1>(w);
+    g32_barrier<BL, 1>(w);
   else
-    g32_barrier<0>(w);
+    g32_barrier<BL, 0>(w);
 }
 
 // TB: bytes of the pattern table, sized to the call (512, 2048 or 4096
 // kept entries) so that more workgroups fit a CU; at 4096 the table also
 // holds the mask row for longer patterns.
-template <int NS, int TB>
+template <int NS, int TB, int BN>
 __global__ __launch_bounds__(NTH) void k_gemm_g32(GParams p) {
   static_assert(NS == 3 || NS == 4, "the waits cover a prefetch distance of 2 or 3 steps");
   static_assert(TB % 4 == 0 && TB <= kGatherTableBytes, "table size");
   constexpr int D = NS - 1;
-  __shared__ __align__(16) uint16_t S[NS * kG32StageHalves];
+  constexpr int SH = G32<BN>::kStageHalves;
+  constexpr int NB = G32<BN>::kBlocks;
+  __shared__ __align__(16) uint16_t S[NS * SH];
   __shared__ uint32_t mrow[TB / 4];
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int64_t mt = (p.T + 31) / 32;
-  const int64_t ntl = (p.d_out + PBN - 1) / PBN;
+  const int64_t ntl = (p.d_out + BN - 1) / BN;
   // grouped order, kG32GroupM row tiles across all column tiles, row tile
   // fastest; each XCD takes a contiguous run of it (as pipe_tile)
   int64_t mi, ni;
@@ -1243,7 +1288,7 @@ __global__ __launch_bounds__(NTH) void k_gemm_g32(GParams p) {
     mi = first + (t % gsz) % gm;
     ni = (t % gsz) / gm;
   }
-  const int64_t m0 = mi * 32, n0 = ni * PBN;
+  const int64_t m0 = mi * 32, n0 = ni * BN;
   // the tile's pattern: the byte table of kept positions (as k_gemm_pipe's
   // gather) or the mask row itself
   const int64_t wpr = p.d_in / 32;
@@ -1255,8 +1300,7 @@ __global__ __launch_bounds__(NTH) void k_gemm_g32(GParams p) {
     for (int64_t i = threadIdx.x; i < wpr; i += NTH) {
       uint32_t bits = src[i];
       for (int e = 0; e < per; ++e) {
-        const int64_t j = i * per + e;
-        tab[(j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1)] = (uint8_t)(bits ? __builtin_ctz(bits) : 31);
+        tab[g32_slot<BN>(i * per + e)] = (uint8_t)(bits ? __builtin_ctz(bits) : 31);
         bits &= bits - 1u;
       }
     }
@@ -1265,28 +1309,32 @@ __global__ __launch_bounds__(NTH) void k_gemm_g32(GParams p) {
   }
   __syncthreads();
 
-  f16v acc;
+  f16v acc[NB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
   const int nk = (int)(p.d_in / p.m * p.n / kG32BK);
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (j < nk) g32_issue(p, m0, n0, j * kG32BK, S + j * kG32StageHalves, mrow, table);
+    if (j < nk) g32_issue<BN>(p, m0, n0, j * kG32BK, S + j * SH, mrow, table);
   for (int t = 0; t < nk; ++t) {
     // wait for step t's loads, leaving the later steps' in flight (at most
     // D - 1 of them), then refill the stage step t - 1 used
     const int later = nk - 1 - t;
-    g32_barrier_upto(w, later < D - 1 ? later : D - 1);
+    g32_barrier_upto<G32<BN>::kBLoads>(w, later < D - 1 ? later : D - 1);
     if (t + D < nk)
-      g32_issue(p, m0, n0, (int64_t)(t + D) * kG32BK, S + ((t + D) % NS) * kG32StageHalves, mrow,
-                table);
-    g32_compute(S + (t % NS) * kG32StageHalves, acc, w);
+      g32_issue<BN>(p, m0, n0, (int64_t)(t + D) * kG32BK, S + ((t + D) % NS) * SH, mrow, table);
+    g32_compute<BN>(S + (t % NS) * SH, acc, w);
   }
-  const int64_t col = n0 + w * 32 + lane % 32;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t row = m0 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-    if (row < p.T && col < p.d_out) p.y[row * p.d_out + col] = f2h(acc[r]);
+  for (int b = 0; b < NB; ++b) {
+    const int64_t col = n0 + w * (BN / 4) + 32 * b + lane % 32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = m0 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+      if (row < p.T && col < p.d_out) p.y[row * p.d_out + col] = f2h(acc[b][r]);
+    }
   }
 }
 
@@ -1750,20 +1798,26 @@ bool g32_shape_ok(int64_t d_in, int n, int m, int tt) {
          d_in <= 32 * kGatherMaskWords && (d_in / m * n) % kG32BK == 0;
 }
 
-hipError_t launch_g32(const GParams& p, hipStream_t s) {
-  const int64_t tiles = ((p.T + 31) / 32) * ((p.d_out + PBN - 1) / PBN);
+template <int BN>
+hipError_t launch_g32_bn(const GParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.T + 31) / 32) * ((p.d_out + BN - 1) / BN);
   if (tiles > 0x7fffffffLL) return hipErrorNotSupported;
   const int64_t kept = p.d_in / p.m * p.n;
   const dim3 grid((unsigned)tiles);
   if (g_gemm_stages >= 4)
-    hipLaunchKernelGGL((k_gemm_g32<4, kGatherTableBytes>), grid, dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_g32<4, kGatherTableBytes, BN>), grid, dim3(NTH), 0, s, p);
   else if (kept <= 512)
-    hipLaunchKernelGGL((k_gemm_g32<3, 512>), grid, dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_g32<3, 512, BN>), grid, dim3(NTH), 0, s, p);
   else if (kept <= 2048)
-    hipLaunchKernelGGL((k_gemm_g32<3, 2048>), grid, dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_g32<3, 2048, BN>), grid, dim3(NTH), 0, s, p);
   else
-    hipLaunchKernelGGL((k_gemm_g32<3, kGatherTableBytes>), grid, dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_g32<3, kGatherTableBytes, BN>), grid, dim3(NTH), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_g32(const GParams& p, hipStream_t s) {
+  if (g_gemm_engine == 3) return launch_g32_bn<256>(p, s);
+  return launch_g32_bn<128>(p, s);
 }
 
 hipError_t launch_gather(const GParams& p, hipStream_t s) {

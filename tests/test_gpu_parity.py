@@ -1189,16 +1189,18 @@ def shared_g32(d_in, n, m, tt):
             and (d_in // m * n) % 32 == 0)
 
 
+@pytest.mark.parametrize("engine", [0, 3])
 @pytest.mark.parametrize("stages", [3, 4])
 @pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (2, 4), (1, 4), (4, 16), (1, 8), (32, 32)])
 @pytest.mark.parametrize("T,d_in,d_out,tt", [(64, 1024, 512, 32), (100, 128, 136, 32),
                                              (33, 256, 8, 32), (1, 512, 1000, 64),
                                              (257, 640, 128, 96), (300, 384, 264, 160),
                                              (70, 2048, 256, 32)])
-def test_nm_shared_spmm_g32(T, d_in, d_out, tt, n, m, stages):
+def test_nm_shared_spmm_g32(T, d_in, d_out, tt, n, m, stages, engine):
     """32-row tiles of one pattern, only the pattern's kept WT rows loaded:
     1 to 64 K steps of 32 compressed entries, ragged rows and columns,
-    tiles of 32 to 160 rows, both stage counts.  Against the oracle, and
+    tiles of 32 to 160 rows, both stage counts, 128- and 256-column tiles
+    (engine 3).  Against the oracle, and
     bit for bit against the per-32-row-block gather where that kernel takes
     the shape (the same MFMA sequence per output block)."""
     if not shared_g32(d_in, n, m, tt) or shared_whole_tile(d_in, n, m, tt):
@@ -1210,7 +1212,7 @@ def test_nm_shared_spmm_g32(T, d_in, d_out, tt, n, m, stages):
     mask_g, val_g = sa.act_sparsify_nm_shared(dev(X), n, m, tt)
     wt_g = dev(wt)
     try:
-        sa.set_gemm_tuning(0, 0, stages)
+        sa.set_gemm_tuning(0, engine, stages)
         Y = sa.nm_shared_spmm(val_g, mask_g, n, m, tt, wt_g).clone()
         if shared_per_block(d_in, n, m, tt):
             sa.set_gemm_tuning(128, 0, 0)
