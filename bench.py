@@ -296,6 +296,7 @@ def main():
             "headline_frac_of_read_peak": round(achieved / rgbs, 4) if head == "fused" else None,
         }
 
+    out["device"] = device_info(torch, dev)
     if not args.no_cpu_baseline and not args.only:
         out["cpu_baseline"] = cpu_baseline(x_np, t, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -847,6 +848,26 @@ def _cpu_worker(args):
     return calls
 
 
+def device_info(torch, dev):
+    """The GPU, its runtime and the host the line was measured on."""
+    pr = torch.cuda.get_device_properties(dev)
+    return {
+        "name": pr.name, "arch": getattr(pr, "gcnArchName", None),
+        "compute_units": pr.multi_processor_count,
+        "hbm_gib": round(pr.total_memory / 2**30, 1),
+        "hip_runtime": getattr(torch.version, "hip", None), "torch": torch.__version__,
+        "host_cpu": _cpu_model(), "host_nproc": _nproc(),
+    }
+
+
+def _nproc():
+    """Cores this process may run on (its affinity set), as nproc counts them."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -881,10 +902,7 @@ def cpu_baseline(x, t, seconds):
                 break
     single_us = el / calls * 1e6
     del wt
-    try:
-        ncpu = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncpu = os.cpu_count() or 1
+    ncpu = _nproc()
     procs = max(1, min(ncpu, 16))
     window = seconds / 2
     ctx = mp.get_context("spawn")
