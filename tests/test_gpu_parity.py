@@ -1189,13 +1189,18 @@ def shared_g32(d_in, n, m, tt):
             and (d_in // m * n) % 32 == 0)
 
 
+G32_CASES = [(T, d_in, d_out, tt, n, m)
+             for (T, d_in, d_out, tt) in [(64, 1024, 512, 32), (100, 128, 136, 32),
+                                          (33, 256, 8, 32), (1, 512, 1000, 64),
+                                          (257, 640, 128, 96), (300, 384, 264, 160),
+                                          (70, 2048, 256, 32)]
+             for (n, m) in [(8, 16), (16, 32), (2, 4), (1, 4), (4, 16), (1, 8), (32, 32)]
+             if shared_g32(d_in, n, m, tt) and not shared_whole_tile(d_in, n, m, tt)]
+
+
 @pytest.mark.parametrize("engine", [0, 3])
 @pytest.mark.parametrize("stages", [3, 4])
-@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (2, 4), (1, 4), (4, 16), (1, 8), (32, 32)])
-@pytest.mark.parametrize("T,d_in,d_out,tt", [(64, 1024, 512, 32), (100, 128, 136, 32),
-                                             (33, 256, 8, 32), (1, 512, 1000, 64),
-                                             (257, 640, 128, 96), (300, 384, 264, 160),
-                                             (70, 2048, 256, 32)])
+@pytest.mark.parametrize("T,d_in,d_out,tt,n,m", G32_CASES)
 def test_nm_shared_spmm_g32(T, d_in, d_out, tt, n, m, stages, engine):
     """32-row tiles of one pattern, only the pattern's kept WT rows loaded:
     1 to 64 K steps of 32 compressed entries, ragged rows and columns,
@@ -1203,8 +1208,6 @@ def test_nm_shared_spmm_g32(T, d_in, d_out, tt, n, m, stages, engine):
     (engine 3).  Against the oracle, and
     bit for bit against the per-32-row-block gather where that kernel takes
     the shape (the same MFMA sequence per output block)."""
-    if not shared_g32(d_in, n, m, tt) or shared_whole_tile(d_in, n, m, tt):
-        pytest.skip("not a 32-row-tile shape")
     X = syn.gaussian_f16((T, d_in), 1.0, 3 * T + d_in + n)
     X[0, :] = np.float16(0.5)  # a tile of ties
     wt = syn.weight_t(d_out, d_in, d_out + 2 * m)
@@ -1223,13 +1226,12 @@ def test_nm_shared_spmm_g32(T, d_in, d_out, tt, n, m, stages, engine):
     assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
 
 
-@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (1, 4)])
+@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (2, 4)])
 def test_nm_shared_g32_long_k(n, m):
     """32-row tiles past 4096 kept entries per row: the kept positions come
     from the mask words instead of the byte table."""
     T, d_in, d_out, tt = 96, 16384, 264, 32
-    if d_in // m * n <= 4096:
-        pytest.skip("within the byte table")
+    assert d_in // m * n > 4096
     X = syn.gaussian_f16((T, d_in), 1.0, d_in + 3 * n)
     wt = syn.weight_t(d_out, d_in, 19 + m)
     _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
@@ -1256,19 +1258,22 @@ def test_nm_shared_spmm_expanded(n, m, tt):
     assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
 
 
+WHOLE_TILE_CASES = [(T, d_in, d_out, tt, n, m)
+                    for (T, d_in, d_out, tt) in [(256, 1024, 512, 128), (300, 512, 136, 128),
+                                                 (129, 2048, 264, 256), (1, 4096, 8, 128),
+                                                 (513, 768, 1000, 256), (640, 256, 128, 128)]
+                    for (n, m) in [(2, 4), (1, 4), (8, 16), (4, 16), (16, 32), (8, 32), (1, 8),
+                                   (2, 32), (32, 32), (4, 8)]
+                    if shared_whole_tile(d_in, n, m, tt)]
+
+
 @pytest.mark.parametrize("tile_rows", [0, 128, 256])
-@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (8, 16), (4, 16), (16, 32), (8, 32), (1, 8),
-                                 (2, 32), (32, 32), (4, 8)])
-@pytest.mark.parametrize("T,d_in,d_out,tt", [(256, 1024, 512, 128), (300, 512, 136, 128),
-                                             (129, 2048, 264, 256), (1, 4096, 8, 128),
-                                             (513, 768, 1000, 256), (640, 256, 128, 128)])
+@pytest.mark.parametrize("T,d_in,d_out,tt,n,m", WHOLE_TILE_CASES)
 def test_nm_shared_spmm_whole_tile(T, d_in, d_out, tt, n, m, tile_rows):
     """One pattern per row tile: only the kept WT rows are loaded and the
     dense engine runs over d_in n / m compressed entries (1 to 64 K steps
     of 32), ragged rows and columns, both tile heights where the tile
     allows them."""
-    if not shared_whole_tile(d_in, n, m, tt):
-        pytest.skip("d_in n / m not a multiple of 32")
     assert sa.lib().sa_nm_shared_spmm_workspace_bytes(T, d_in, n, m, tt) == 0
     X = syn.gaussian_f16((T, d_in), 1.0, 2 * T + d_in + n)
     wt = syn.weight_t(d_out, d_in, d_out + m + 1)
@@ -1283,14 +1288,13 @@ def test_nm_shared_spmm_whole_tile(T, d_in, d_out, tt, n, m, tile_rows):
     assert_close(Y, spmm.nm_shared_spmm(vals, tile_keep, tt, wt))
 
 
-@pytest.mark.parametrize("n,m", [(8, 16), (1, 4), (16, 32), (2, 4), (4, 8)])
-@pytest.mark.parametrize("d_in", [8256, 16384])
+@pytest.mark.parametrize("d_in,n,m", [(d, n, m) for d in [8256, 16384]
+                                      for (n, m) in [(8, 16), (1, 4), (16, 32), (2, 4), (4, 8)]
+                                      if shared_whole_tile(d, n, m, 128)])
 def test_nm_shared_whole_tile_long_k(d_in, n, m):
     """The kept positions come from a byte table up to 4096 kept entries per
     row and from the mask words beyond: both sides of that limit."""
     T, d_out, tt = 130, 264, 128
-    if not shared_whole_tile(d_in, n, m, tt):
-        pytest.skip("d_in n / m not a multiple of 32")
     X = syn.gaussian_f16((T, d_in), 1.0, d_in + n)
     wt = syn.weight_t(d_out, d_in, 9 + m)
     _, tile_keep, vals = sparsify.nm_shared_sparsify(X, n, m, tt)
