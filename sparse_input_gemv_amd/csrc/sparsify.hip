@@ -148,19 +148,18 @@ __global__ __launch_bounds__(NT) void k_sparsify_threshold(
 //   x' = fp16(fp32(x) - fp32(mu))   (mu null: x' = x)
 //   score = |x'| * c in fp64         (c null: |x'|; the fp64 product is
 //                                     correctly rounded, one operation)
-//   M == 0: keep iff score >= t and x' != 0
-//   M  > 0: keep the n largest scores of every M consecutive entries, ties to
-//           the lower index (n rounds of taking each group's largest score
-//           not yet taken; groups lie inside one thread's run, E % M == 0)
-// The kept x' are compacted as the threshold sparsifier does.  alpha[row] =
+//   threshold kind: keep iff score >= t and x' != 0
+//   N:M kinds (k_sparsify_scored_nm below): keep the n largest scores of
+//           every M consecutive entries, ties to the lower index
+// This kernel takes the threshold kind, one workgroup per row: the kept x'
+// are compacted as the threshold sparsifier does.  alpha[row] =
 // sqrt(sum x'^2 / sum_kept x'^2) (1 when nothing is kept), in fp64.
-template <int NT, int E, int M>
+template <int NT, int E>
 __global__ __launch_bounds__(NT) void k_sparsify_scored(
     const uint16_t* __restrict__ x, int64_t d, const uint16_t* __restrict__ mu,
-    const double* __restrict__ cn, double t, int n, uint32_t* __restrict__ mask,
+    const double* __restrict__ cn, double t, uint32_t* __restrict__ mask,
     int32_t* __restrict__ idx, uint16_t* __restrict__ val, int32_t* __restrict__ nnz,
     float* __restrict__ alpha, int64_t cap, int vec, int vec_mu) {
-  static_assert(M == 0 || E % M == 0, "groups inside one run");
   __shared__ int scan[NT / kWave];
   __shared__ double sums[2][NT / kWave];
   __shared__ __align__(16) int32_t sidx[NT * E];
@@ -190,33 +189,10 @@ __global__ __launch_bounds__(NT) void k_sparsify_scored(
       sc[e] = (k0 + e < d) ? (cn != nullptr ? a * cn[k0 + e] : a) : 0.0;
     }
     uint64_t bits = 0;
-    if constexpr (M == 0) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bool keep = (k0 + e < d) && sc[e] >= t && h2f(v[e]) != 0.f;
-        bits |= (uint64_t)keep << e;
-      }
-    } else {
-      // n rounds; each takes, in every group, the largest score not yet
-      // taken (strict >, scanning upwards: ties go to the lower index)
-      for (int it = 0; it < n; ++it) {
-#pragma unroll
-        for (int g = 0; g < E / M; ++g) {
-          int best = g * M;
-          double bs = -1.0;  // scores are >= 0
-#pragma unroll
-          for (int j = 0; j < M; ++j) {
-            const int e = g * M + j;
-            const bool take = ((bits >> e) & 1ull) == 0 && sc[e] > bs;
-            bs = take ? sc[e] : bs;
-            best = take ? e : best;
-          }
-          bits |= 1ull << best;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (k0 + e >= d) bits &= ~(1ull << e);  // groups past the row end
+    for (int e = 0; e < E; ++e) {
+      const bool keep = (k0 + e < d) && sc[e] >= t && h2f(v[e]) != 0.f;
+      bits |= (uint64_t)keep << e;
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -251,6 +227,151 @@ __global__ __launch_bounds__(NT) void k_sparsify_scored(
     }
   }
   if (threadIdx.x == 0) nnz[row] = base;
+}
+
+// The N:M kinds of k_sparsify_scored spread over many workgroups: every
+// group keeps exactly n entries, so group g's survivors go to slots
+// [g n, g n + n) of the row's list whatever the other groups keep, and no
+// compaction across groups is needed.  One thread per group of M, one wave
+// per workgroup (64 groups).  The selection is k_sparsify_scored's (n rounds
+// of taking the group's largest score not yet taken, the first of equal
+// scores), so the masks and lists are the same bit for bit.  The variance
+// correction needs the whole row: k_scored_alpha, launched after, sums x'^2
+// over the row and over its kept values.
+constexpr int kScoredNmGroups = 64;
+
+template <int M>
+__global__ __launch_bounds__(kScoredNmGroups) void k_sparsify_scored_nm(
+    const uint16_t* __restrict__ x, int64_t d, const uint16_t* __restrict__ mu,
+    const double* __restrict__ cn, int n, uint32_t* __restrict__ mask,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int32_t* __restrict__ nnz,
+    int64_t cap, int vec, int vec_mu) {
+  static_assert(M == 4 || M == 8 || M == 16 || M == 32, "group sizes");
+  const int64_t row = blockIdx.y;
+  const int lane = (int)threadIdx.x;
+  const int64_t ng = d / M;
+  const int64_t g = (int64_t)blockIdx.x * kScoredNmGroups + lane;
+  const bool ok = g < ng;
+  const int64_t k0 = (ok ? g : 0) * M;
+  const uint16_t* xr = x + row * d;
+  uint16_t v[M];
+  load_run<M>(xr, k0, d, vec != 0, v);
+  if (mu != nullptr) {
+    uint16_t m[M];
+    load_run<M>(mu, k0, d, vec_mu != 0, m);
+#pragma unroll
+    for (int e = 0; e < M; ++e) v[e] = f2h(h2f(v[e]) - h2f(m[e]));
+  }
+  double sc[M];
+#pragma unroll
+  for (int e = 0; e < M; ++e) {
+    const double a = fabs((double)h2f(v[e]));
+    sc[e] = cn != nullptr ? a * cn[k0 + e] : a;
+  }
+  uint32_t bits = 0;
+  for (int it = 0; it < n; ++it) {
+    int best = 0;
+    double bs = -1.0;  // scores are >= 0
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      const bool take = ((bits >> j) & 1u) == 0 && sc[j] > bs;
+      bs = take ? sc[j] : bs;
+      best = take ? j : best;
+    }
+    bits |= 1u << best;
+  }
+  if (!ok) bits = 0;
+  if (ok) {
+    int32_t* ir = idx + row * cap + g * n;
+    uint16_t* vr = val + row * cap + g * n;
+    int j = 0;
+#pragma unroll
+    for (int e = 0; e < M; ++e) {
+      if ((bits >> e) & 1u) {
+        ir[j] = (int32_t)(k0 + e);
+        vr[j] = v[e];
+        ++j;
+      }
+    }
+  }
+  if (mask != nullptr) {
+    // a mask word holds 32 / M consecutive groups, i.e. lanes: OR their bits
+    constexpr int GPW = 32 / M;
+    uint32_t w = bits << (M * (lane % GPW));
+#pragma unroll
+    for (int o = 1; o < GPW; o <<= 1) w |= (uint32_t)__shfl_xor((int)w, o, kWave);
+    const int64_t words = (d + 31) >> 5;
+    const int64_t wi = (g * M) >> 5;
+    if (lane % GPW == 0 && wi < words) mask[row * words + wi] = w;
+  }
+  if (blockIdx.x == 0 && lane == 0) nnz[row] = (int32_t)(ng * n);
+}
+
+// alpha[row] = sqrt(sum x'^2 / sum_kept x'^2), 1 when the kept sum is 0: both
+// sums in fp64 over the row (x' recomputed from x and mu) and over its
+// nk kept values, in a fixed order (thread-strided, then a wave and a
+// workgroup tree).
+__global__ __launch_bounds__(1024) void k_scored_alpha(const uint16_t* __restrict__ x, int64_t d,
+                                                        const uint16_t* __restrict__ mu,
+                                                        const uint16_t* __restrict__ val,
+                                                        int64_t cap, int64_t nk,
+                                                        float* __restrict__ alpha, int vec,
+                                                        int vec_mu, int vec_val) {
+  __shared__ double sums[2][1024 / kWave];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * d;
+  const uint16_t* vr = val + row * cap;
+  // Runs of 8 per thread (16-byte loads where aligned), two runs in flight
+  // per pass, so a pass costs one memory round trip.
+  double a = 0.0, k = 0.0;
+  const bool vx = vec != 0, vv = vec_val != 0;
+  for (int64_t i0 = (int64_t)threadIdx.x * 8; i0 < d; i0 += 2 * 1024 * 8) {
+    uint16_t xa[8], xb[8], ma[8], mb[8];
+    const int64_t i1 = i0 + 1024 * 8;
+    load_run<8>(xr, i0, d, vx, xa);
+    load_run<8>(xr, i1, d, vx, xb);
+    if (mu != nullptr) {
+      load_run<8>(mu, i0, d, vec_mu != 0, ma);
+      load_run<8>(mu, i1, d, vec_mu != 0, mb);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t p = mu != nullptr ? f2h(h2f(xa[e]) - h2f(ma[e])) : xa[e];
+      const uint16_t q = mu != nullptr ? f2h(h2f(xb[e]) - h2f(mb[e])) : xb[e];
+      const double dp = (i0 + e < d) ? (double)h2f(p) : 0.0;
+      const double dq = (i1 + e < d) ? (double)h2f(q) : 0.0;
+      a += dp * dp;
+      a += dq * dq;
+    }
+  }
+  for (int64_t i0 = (int64_t)threadIdx.x * 8; i0 < nk; i0 += 1024 * 8) {
+    uint16_t va[8];
+    load_run<8>(vr, i0, nk, vv, va);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double q = (double)h2f(va[e]);  // entries past nk read as 0
+      k += q * q;
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    a += __shfl_xor(a, o, kWave);
+    k += __shfl_xor(k, o, kWave);
+  }
+  const int w = (int)threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    sums[0][w] = a;
+    sums[1][w] = k;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double ta = 0.0, tk = 0.0;
+    for (int i = 0; i < 1024 / kWave; ++i) {
+      ta += sums[0][i];
+      tk += sums[1][i];
+    }
+    alpha[row] = tk > 0.0 ? (float)sqrt(ta / tk) : 1.f;
+  }
 }
 
 // Exactly k survivors per row: the k largest magnitudes, ties to the lower
@@ -970,21 +1091,32 @@ hipError_t launch_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d,
   const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && (d % 8) == 0) ? 1 : 0;
   const int vec_mu = ((reinterpret_cast<uintptr_t>(mu) & 15u) == 0) ? 1 : 0;
   const dim3 grid((unsigned)rows);
-  // Groups of 32 need runs of 32 fp64 scores per thread: 256-thread
-  // workgroups (one wave per SIMD, up to 512 registers) hold them without
-  // spilling; the other kinds fit the 128 registers of 1024 threads.
-#define SA_SCORED(NT, E, M)                                                                  \
-  hipLaunchKernelGGL((k_sparsify_scored<NT, E, M>), grid, dim3(NT), 0, s, x, d, mu, colnorm, t, \
-                     n, mask, idx, val, nnz, alpha, cap, vec, vec_mu)
+  if (m == 0) {  // threshold: one workgroup per row
+    hipLaunchKernelGGL((k_sparsify_scored<kSparsifyThreads, 16>), grid, dim3(kSparsifyThreads), 0,
+                       s, x, d, mu, colnorm, t, mask, idx, val, nnz, alpha, cap, vec, vec_mu);
+    return hipGetLastError();
+  }
+  // N:M: one thread per group over many workgroups, then the row sums of
+  // the variance correction
+  const int64_t ng = d / m;
+  const int64_t gx = (ng + kScoredNmGroups - 1) / kScoredNmGroups;
+  if (gx > 0x7fffffffLL || rows > 65535) return hipErrorNotSupported;
+  const dim3 g2((unsigned)gx, (unsigned)rows);
+#define SA_SCORED_NM(M)                                                                       \
+  hipLaunchKernelGGL((k_sparsify_scored_nm<M>), g2, dim3(kScoredNmGroups), 0, s, x, d, mu,   \
+                     colnorm, n, mask, idx, val, nnz, cap, vec, vec_mu)
   switch (m) {
-    case 0: SA_SCORED(kSparsifyThreads, 16, 0); break;
-    case 4: SA_SCORED(kSparsifyThreads, 16, 4); break;
-    case 8: SA_SCORED(kSparsifyThreads, 16, 8); break;
-    case 16: SA_SCORED(kSparsifyThreads, 16, 16); break;
-    case 32: SA_SCORED(256, 32, 32); break;
+    case 4: SA_SCORED_NM(4); break;
+    case 8: SA_SCORED_NM(8); break;
+    case 16: SA_SCORED_NM(16); break;
+    case 32: SA_SCORED_NM(32); break;
     default: return hipErrorInvalidValue;
   }
-#undef SA_SCORED
+#undef SA_SCORED_NM
+  if (alpha != nullptr)
+    hipLaunchKernelGGL(k_scored_alpha, grid, dim3(1024), 0, s, x, d, mu, val, cap, ng * n, alpha,
+                       vec, vec_mu,
+                       ((reinterpret_cast<uintptr_t>(val) & 15u) == 0 && cap % 8 == 0) ? 1 : 0);
   return hipGetLastError();
 }
 

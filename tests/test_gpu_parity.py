@@ -683,6 +683,34 @@ def test_scored_sparsify(d, rows, nm, shifted, weighted):
         assert alpha[r] == pytest.approx(correct.var_alpha(XS[r], keep[r]), rel=2e-6)
 
 
+@pytest.mark.parametrize("d,nm", [(48, (8, 16)), (1000, (2, 4)), (1000, (4, 8)), (4112, (8, 16)),
+                                  (72, (1, 4)), (40, (3, 8)), (8256, (31, 32)), (96, (16, 32))])
+def test_scored_sparsify_ragged_rows(d, nm):
+    """N:M by score over workgroups of 64 groups: rows whose last mask word
+    is partly past the row (d not a multiple of 32), rows ending inside a
+    workgroup, every n; lists, masks and alpha against the oracle."""
+    n, m = nm
+    rows = 3
+    X = syn.laplace_f16((rows, d), 1.0, 7 * d + m)
+    X[1, ::3] = np.float16(-0.0)
+    mu = syn.gaussian_f16((d,), 0.25, d + 1)
+    cn = correct.column_norms(syn.weight_t(16, d, 5))
+    mask_g, idx_g, val_g, nnz_g, alpha_g = sa.act_sparsify_scored(
+        dev(X), t=0.0, n=n, m=m, mu=dev(mu), colnorm=torch.from_numpy(cn).to(DEV))
+    XS = np.stack([correct.shift(X[r], mu) for r in range(rows)])
+    keep = np.stack([correct.nm_keep(XS[r], cn, n, m) for r in range(rows)])
+    check_lists(mask_g, idx_g, val_g, nnz_g, XS, keep)
+    alpha = host(alpha_g)
+    for r in range(rows):
+        assert alpha[r] == pytest.approx(correct.var_alpha(XS[r], keep[r]), rel=2e-6)
+    # without the mask output: the same lists and alpha
+    g2 = sa.act_sparsify_scored(dev(X), t=0.0, n=n, m=m, mu=dev(mu),
+                                colnorm=torch.from_numpy(cn).to(DEV), with_mask=False)
+    assert g2[0] is None
+    for a, b in zip(g2[1:], (idx_g, val_g, nnz_g, alpha_g)):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("kind", ["threshold", "8:16"])
 @pytest.mark.parametrize("d_out,d_in", [(4096, 11008), (264, 1024), (11008, 4096)])
 def test_corrected_gemv(d_out, d_in, kind):
