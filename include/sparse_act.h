@@ -532,23 +532,28 @@ int sa_set_gemv_tuning(int tiling, int target_wgs, int handoff);
  */
 int sa_set_gemv_test_hooks(int flags);
 /*
- * Process-wide matmul choices of dense_gemm / nm_act_spmm, for tuning sweeps
- * and cross-checks.
+ * Process-wide matmul choices of dense_gemm / nm_act_spmm / nm_shared_spmm,
+ * for tuning sweeps and cross-checks.
  *   tile_rows: 0 = automatic (dense: 256 x 256 tiles where their rounds
  *     over the CUs beat 256 x 128 tiles, else 256-row tiles when they give
- *     at least one workgroup per CU, else 128; 2:4: 128), or 128 / 256
- *     (128-column tiles of that height).
+ *     at least one workgroup per CU, else 128; 2:4: 256 x 256 tiles where
+ *     their rounds stay within 1.5x their tiles per CU, else 128 x 128), or
+ *     128 / 256 (128-column tiles of that height; for nm_shared_spmm with
+ *     tt a multiple of 32 but not of 128, the per-32-row-block gather at that
+ *     height instead of 32-row tiles).
  *   engine: 0 = automatic, 1 = the staged-register engine, 2 = the
  *     pipelined engine with 128-column tiles, 3 = the pipelined engine with
- *     256 x 256 tiles (dense and the expanded N:M patterns; 2:4 keeps
- *     engine 2; tile_rows 0 or 256).  The pipelined engines apply when d_in
- *     is a multiple of their K step, 32 for dense and the expanded N:M
- *     patterns, 64 for 2:4, with 16-byte aligned rows; other calls take the
- *     staged-register engine.
+ *     256 x 256 tiles (dense, 2:4 and the expanded N:M patterns; tile_rows
+ *     0 or 256; for nm_shared_spmm on 32-row tiles: 256 columns).  The
+ *     pipelined engines apply when d_in is a multiple of their K step, 32
+ *     for dense and the expanded N:M patterns, 64 for 2:4, with 16-byte
+ *     aligned rows; other calls take the staged-register engine.
  *   stages: the pipelined engine's LDS stage count, 0 = automatic (3 for
- *     128-column tiles, 5 for 256 x 256), or 3..6 (loads run stages - 1 K
- *     steps ahead); a count whose stages exceed the 160 KB of LDS for the
- *     tile is lowered to the most that fit.
+ *     128-column tiles, 5 for dense 256 x 256, 3 for 2:4 256 x 256 and for
+ *     32-row tiles), or 3..6 (loads run stages - 1 K steps ahead); a count
+ *     whose stages exceed the 160 KB of LDS for the tile is lowered to the
+ *     most that fit (2:4 256 x 256: always 3; 32-row tiles: 3, or 4 for any
+ *     count above 3).
  * Every choice issues the same MFMA sequence per output element: identical
  * results.  Returns SA_ERR_INVALID_ARG for other values.  Not thread-safe.
  */
