@@ -669,6 +669,14 @@ def suite_corrected(sa, syn, dev, ev_time, emit, rotation):
              bytes_=2 * d_out * kept + 6 * kept + 2 * d_in * 2 + 8 * d_in + 2 * d_out * 2,
              flops=2 * d_out * kept, kept=kept, sparsify_us=round(us_s, 3), gemv_us=round(us_g, 3),
              plain_fused_us=round(us_p, 3))
+    for (n, m) in ((8, 16), (16, 32)):
+        kept = d_in // m * n
+        us_n = ev_time(lambda i: sa.sparse_gemv_scored_nm(rot[i % nr], x, n, m, mu=mu, colnorm=cn,
+                                                          var=True, bias=bias, y=y), 1000)
+        emit("next3", f"sparse_gemv_scored_nm down {d_out}x{d_in} weight-aware {n}:{m}, shift + "
+             "VAR, one launch", us_n,
+             bytes_=2 * d_out * kept + 2 * d_in * 2 + 8 * d_in + 2 * d_out * 2,
+             flops=2 * d_out * kept, kept=kept, plain_fused_us=round(us_p, 3))
     del rot
     torch.cuda.empty_cache()
 

@@ -326,6 +326,27 @@ int sparse_gemv_scored(const uint16_t* wt, int64_t d_out, int64_t d_in,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sparse_gemv_scored_nm -- act_sparsify_scored (N:M kind) and
+ * sparse_gemv_corrected in one launch, for one row (Motivating Next-Gen
+ * Accelerators with Flexible (N:M) Activation Sparsity ..., section 2:
+ * weight-aware scores choose the n entries of every m consecutive ones):
+ *   x' = fp16(fp32(x) - fp32(mu)), score |x'| * colnorm (fp64), keep the n
+ *   largest scores of every group of m (ties to the lower index; x' = 0 may
+ *   be kept), y = fp16(alpha * W (keep .* x') + bias), alpha as
+ *   sparse_gemv_scored.  The kept set is act_sparsify_scored's, bit for bit.
+ * Each workgroup decides the groups of its own slice (slices start on
+ * multiples of 32 entries, so no group spans two).
+ *   m in {4, 8, 16, 32}, 1 <= n <= m, d_in % m == 0; other arguments as
+ *   sparse_gemv_scored.
+ * Errors: SA_ERR_INVALID_ARG for a bad n, m or d_in % m != 0, and as
+ * sparse_gemv_scored otherwise.
+ */
+int sparse_gemv_scored_nm(const uint16_t* wt, int64_t d_out, int64_t d_in,
+                          const uint16_t* x, const uint16_t* mu, const double* colnorm,
+                          int n, int m, int var, const uint16_t* bias, uint16_t* y,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * rana_adapter_gemv -- the RaNA linear-layer rank adapter
  * y[b] = A (m_b .* v[b]) with v[b] = B x[b] and m_b,i = (v[b][i]^2 >= t).
  * [RaNA] Q5.1 (Eq. 11): Up, Gate and QKV projections become A (m(x) .* B x),

@@ -26,7 +26,7 @@ __all__ = [
     "SparseActError", "lib", "workspace",
     "act_sparsify_threshold", "act_sparsify_topk", "act_topk_cutoff", "sparse_gemv_topk",
     "act_sparsify_nm", "act_sparsify_nm_shared",
-    "act_sparsify_scored", "sparse_gemv_corrected", "sparse_gemv_scored",
+    "act_sparsify_scored", "sparse_gemv_corrected", "sparse_gemv_scored", "sparse_gemv_scored_nm",
     "act_calibrate_threshold", "sparse_gemv", "sparse_gemv_threshold",
     "sparse_gemv_threshold_noalloc", "rana_adapter_gemv",
     "masked_gemv",
@@ -63,6 +63,8 @@ _SIGNATURES = {
                                    _vp, _i64, _vp, _vp]),
     "sparse_gemv_scored": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _f64, _i32, _vp, _vp, _vp, _sz,
                                   _vp]),
+    "sparse_gemv_scored_nm": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
+                                     _vp, _sz, _vp]),
     "sparse_gemv_corrected": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
                                      _vp, _sz, _vp]),
     "rana_adapter_gemv": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _f32, _vp, _vp, _vp,
@@ -436,6 +438,32 @@ def sparse_gemv_scored(wt: torch.Tensor, x: torch.Tensor, t: float,
     _check(lib().sparse_gemv_scored(_ptr(wt), d_out, d_in, _ptr(x), _ptr(mu), _ptr(colnorm),
                                     float(t), int(bool(var)), _ptr(bias), _ptr(y), _ptr(ws),
                                     ws.numel(), _stream(wt)), "sparse_gemv_scored")
+    return _ret(y, True)
+
+
+def sparse_gemv_scored_nm(wt: torch.Tensor, x: torch.Tensor, n: int, m: int,
+                          mu: torch.Tensor | None = None, colnorm: torch.Tensor | None = None,
+                          var: bool = True, bias: torch.Tensor | None = None,
+                          y: torch.Tensor | None = None):
+    """One launch: shift, n of every m entries kept by weight-aware score,
+    sparse GEMV, variance correction and bias, for one row ``x``."""
+    _dev(wt, "wt", torch.float16)
+    _dev(x, "x", torch.float16)
+    d_in, d_out = wt.shape
+    if x.numel() != d_in:
+        raise ValueError(f"x holds {x.numel()} values, {d_in} needed")
+    for name, tt, dt, cnt in (("mu", mu, torch.float16, d_in),
+                              ("colnorm", colnorm, torch.float64, d_in),
+                              ("bias", bias, torch.float16, d_out)):
+        if tt is not None:
+            _dev(tt, name, dt)
+            if tt.numel() != cnt:
+                raise ValueError(f"{name} holds {tt.numel()} values, {cnt} needed")
+    y = _gemv_out(wt, 1, True, y)
+    ws = workspace(wt.device, workspace_bytes(d_out, d_in, 1))
+    _check(lib().sparse_gemv_scored_nm(_ptr(wt), d_out, d_in, _ptr(x), _ptr(mu), _ptr(colnorm),
+                                       int(n), int(m), int(bool(var)), _ptr(bias), _ptr(y),
+                                       _ptr(ws), ws.numel(), _stream(wt)), "sparse_gemv_scored_nm")
     return _ret(y, True)
 
 

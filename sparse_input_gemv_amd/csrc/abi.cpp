@@ -222,6 +222,45 @@ int sparse_gemv_scored(const uint16_t* wt, int64_t d_out, int64_t d_in, const ui
   return run_gemv(c, "sparse_gemv_scored", stream);
 }
 
+int sparse_gemv_scored_nm(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint16_t* x,
+                          const uint16_t* mu, const double* colnorm, int n, int m, int var,
+                          const uint16_t* bias, uint16_t* y, void* ws, size_t ws_bytes,
+                          void* stream) {
+  sa::clear_error();
+  const size_t need = sa::gemv_workspace_bytes(d_out, d_in, 1);
+  int st = sa::check_gemv_common(wt, d_out, d_in, 1, y, ws, ws_bytes, need);
+  if (st == SA_OK) st = sa::check_activation(x, "sparse_gemv_scored_nm: x");
+  if (st == SA_OK && (!(m == 4 || m == 8 || m == 16 || m == 32) || n < 1 || n > m ||
+                      d_in % m != 0)) {
+    sa::set_error("sparse_gemv_scored_nm: need m in {4, 8, 16, 32}, 1 <= n <= m, d_in % m == 0");
+    st = SA_ERR_INVALID_ARG;
+  }
+  if (st == SA_OK && ((reinterpret_cast<uintptr_t>(mu) & 1u) != 0 ||
+                      (reinterpret_cast<uintptr_t>(colnorm) & 7u) != 0 ||
+                      (reinterpret_cast<uintptr_t>(bias) & 1u) != 0)) {
+    sa::set_error("sparse_gemv_scored_nm: mu, colnorm, bias must be aligned");
+    st = SA_ERR_INVALID_ARG;
+  }
+  if (st != SA_OK) return st;
+  sa::GemvCall c;
+  c.mode = sa::kModeScoredNM;
+  c.wt = wt;
+  c.d_out = d_out;
+  c.d_in = d_in;
+  c.batch = 1;
+  c.x = x;
+  c.mu = mu;
+  c.colnorm = colnorm;
+  c.sn = n;
+  c.sm = m;
+  c.var = var != 0;
+  c.bias = bias;
+  c.y = y;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  return run_gemv(c, "sparse_gemv_scored_nm", stream);
+}
+
 static_assert(SA_NOALLOC_SCRATCH_BYTES == sa::kNoAllocScratchBytes, "header and library agree");
 
 int sparse_gemv_topk(const uint16_t* wt, int64_t d_out, int64_t d_in, const uint16_t* x,

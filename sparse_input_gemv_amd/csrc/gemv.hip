@@ -84,6 +84,9 @@ constexpr int kDefaultFullK = 8;
 // SwiGLU slices start on 64-entry boundaries (each wave writes whole mask
 // words); the other modes take any slice length.
 constexpr int kSwigluSliceAlign = 64;
+// Scored N:M slices start on multiples of 32, so no group of m <= 32 entries
+// spans two slices, and a group's entries sit in consecutive lanes.
+constexpr int kScoredNMSliceAlign = 32;
 constexpr int kMaxGk = 256;     // input slices per output tile
 // default split-K grid: about one workgroup per 64 KB a CU streams, 2 to 4
 // workgroups per CU (measured)
@@ -152,6 +155,7 @@ struct KParams {
   const uint16_t* mu;
   double* vsum;
   int var;  // scored mode: apply the variance correction
+  int sn, sm;  // scored N:M mode: n kept of every m (m a power of two <= 32)
   const int32_t* cut;  // Top-K mode: [batch][2] (tau, i*) of the select
 };
 
@@ -187,7 +191,9 @@ constexpr bool kTopKMode = MODE == kModeTopK || MODE == kModeTopKSel;
 // Modes whose output takes the correction alpha * sum + bias (the list GEMV
 // and the scored mode); every other mode stores the plain rounding.
 template <int MODE>
-constexpr bool kCorrected = MODE == kModeList || MODE == kModeListBatched || MODE == kModeScored;
+constexpr bool kScoredMode = MODE == kModeScored || MODE == kModeScoredNM;
+template <int MODE>
+constexpr bool kCorrected = MODE == kModeList || MODE == kModeListBatched || kScoredMode<MODE>;
 
 // Scored mode, one entry: the shifted value x' = fp16(fp32(x) - fp32(mu))
 // (returned in xb), kept iff |x'| * colnorm >= t in fp64 and x' != 0; its
@@ -199,6 +205,51 @@ __device__ __forceinline__ bool scored_keep(const KParams& p, uint16_t& xb, uint
   const float v = h2f(xb);
   const double a = fabs((double)v);
   const bool kb = in && (p.colnorm != nullptr ? a * c : a) >= p.t64 && v != 0.f;
+  const double q = (double)v * (double)v;
+  s_all += in ? q : 0.0;
+  s_kept += kb ? q : 0.0;
+  return kb;
+}
+
+// Scored N:M mode, one entry: x' and its score as scored_keep; kept iff
+// fewer than n entries of its group of m rank before it (a larger score, or
+// an equal score at a lower position), i.e. the n largest scores of the
+// group, ties to the lower index -- the rule of the scored sparsifier.  The
+// group's m entries sit in m consecutive lanes (slices start on multiples of
+// 32 and chunks span whole waves), so the ranks come from m - 1 cross-lane
+// reads.  Every lane of the wave calls it; `in` clears lanes past the slice
+// (whole groups, as d_in % m == 0).
+// Rank of this lane's score in its group of M lanes (unrolled: the M - 1
+// cross-lane reads are in flight together).
+template <int M>
+__device__ __forceinline__ int group_rank(double sc) {
+  const int lane = lane_id();
+  const int pos = lane & (M - 1), base = lane - pos;
+  int rank = 0;
+#pragma unroll
+  for (int r = 1; r < M; ++r) {
+    const int pp = (pos + r) & (M - 1);
+    const double so = __shfl(sc, base + pp, kWave);
+    rank += (so > sc || (so == sc && pp < pos)) ? 1 : 0;
+  }
+  return rank;
+}
+
+__device__ __forceinline__ bool scored_keep_nm(const KParams& p, uint16_t& xb, uint16_t m,
+                                               double c, bool in, double& s_all,
+                                               double& s_kept) {
+  if (p.mu != nullptr) xb = f2h(h2f(xb) - h2f(m));
+  const float v = h2f(xb);
+  const double a = fabs((double)v);
+  const double sc = p.colnorm != nullptr ? a * c : a;
+  int rank;
+  switch (p.sm) {  // uniform
+    case 4: rank = group_rank<4>(sc); break;
+    case 8: rank = group_rank<8>(sc); break;
+    case 16: rank = group_rank<16>(sc); break;
+    default: rank = group_rank<32>(sc); break;
+  }
+  const bool kb = in && rank < p.sn;
   const double q = (double)v * (double)v;
   s_all += in ? q : 0.0;
   s_kept += kb ? q : 0.0;
@@ -460,7 +511,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   const int64_t o0 = (int64_t)oblk * TILE_O;
   // scored mode with the variance correction: alpha of the row (set below)
   __shared__ float s_alpha;
-  const float* alpha_out = (MODE == kModeScored && p.var) ? &s_alpha : alpha_arg;
+  const float* alpha_out = (kScoredMode<MODE> && p.var) ? &s_alpha : alpha_arg;
   __shared__ int s_last;
 
   // One pass per slice this workgroup computes: its own slice kblk, and only
@@ -571,7 +622,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
             if constexpr (MODE == kModeMasked) mw[c][b] = p.xmask[bb * words + (kc >> 5)];
           }
         }
-        if constexpr (MODE == kModeScored) {
+        if constexpr (kScoredMode<MODE>) {
           ms[c] = p.mu != nullptr ? p.mu[kc] : (uint16_t)0;
           cs[c] = p.colnorm != nullptr ? p.colnorm[kc] : 1.0;
         }
@@ -590,6 +641,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
           bool kb = false;
           if constexpr (MODE == kModeScored) {
             kb = scored_keep(p, xr[c][b], ms[c], cs[c], b < p.batch && k < k1, s_all, s_kept);
+          } else if constexpr (MODE == kModeScoredNM) {
+            kb = scored_keep_nm(p, xr[c][b], ms[c], cs[c], b < p.batch && k < k1, s_all, s_kept);
           } else if constexpr (MODE == kModeSwiglu) {
             hv[c] = 0.f;
             kb = k < k1 && swiglu_keep(xb, ms[c], cs[c], p.swiglu_mode, p.t64, hv[c]);
@@ -684,7 +737,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
             xr[b] = p.x[bb * p.d_in + kc];
             if constexpr (MODE == kModeMasked) mw[b] = p.xmask[bb * words + (kc >> 5)];
           }
-          if constexpr (MODE == kModeScored) {
+          if constexpr (kScoredMode<MODE>) {
             if (p.mu != nullptr) ms = p.mu[kc];
             if (p.colnorm != nullptr) cs = p.colnorm[kc];
           }
@@ -692,8 +745,12 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
           for (int b = 0; b < B; ++b) {
             vb[b] = 0.f;
             hb[b] = 0;
-            if constexpr (MODE == kModeScored) {
-              if (scored_keep(p, xr[b], ms, cs, in && b < p.batch, s_all, s_kept)) {
+            if constexpr (kScoredMode<MODE>) {
+              const bool kp = MODE == kModeScored
+                                  ? scored_keep(p, xr[b], ms, cs, in && b < p.batch, s_all, s_kept)
+                                  : scored_keep_nm(p, xr[b], ms, cs, in && b < p.batch, s_all,
+                                                   s_kept);
+              if (kp) {
                 vb[b] = h2f(xr[b]);
                 hb[b] = xr[b];
                 any = true;
@@ -764,7 +821,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     // kept x'^2.  One slice is the whole input: alpha now.  Otherwise the sums
     // go beside this workgroup's partial (written before its ticket, so the
     // tile's last workgroup reads every slice's sums with the partials).
-    if constexpr (MODE == kModeScored) {
+    if constexpr (kScoredMode<MODE>) {
       if (p.var) {
         __shared__ double vred[2][NT / kWave];
 #pragma unroll
@@ -976,7 +1033,7 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     wait_stores();
     __syncthreads();
   }
-  if constexpr (MODE == kModeScored) {
+  if constexpr (kScoredMode<MODE>) {
     if (p.var) {
       // every slice's sums for this tile (written before their tickets)
       double a = 0.0, k = 0.0;
@@ -1592,6 +1649,7 @@ KFn select_kernel(int mode, int tiling, int B, bool local = false) {
     case kModeListBatched: return kernel_batch<kModeListBatched>(tiling, B, local);
     case kModeSwiglu: return kernel_tiling<kModeSwiglu, 1>(tiling, local);
     case kModeScored: return kernel_tiling<kModeScored, 1>(tiling, local);
+    case kModeScoredNM: return kernel_tiling<kModeScoredNM, 1>(tiling, local);
     case kModeSquare: return kernel_batch<kModeSquare>(tiling, B, local);
     case kModeTopK: return kernel_batch<kModeTopK>(tiling, B, local);
     case kModeTopKSel:  // batch 1 only (launch_gemv_topk)
@@ -1642,7 +1700,8 @@ Plan plan_for(int mode, int tiling, int64_t d_out, int64_t d_in, int B, int64_t 
   pl.go = (int)((d_out + T.tile_o - 1) / T.tile_o);
   if (gk_req < 1) gk_req = 1;
   if (gk_req > kMaxGk) gk_req = kMaxGk;
-  const int64_t align = mode == kModeSwiglu ? kSwigluSliceAlign : 1;
+  const int64_t align =
+      mode == kModeSwiglu ? kSwigluSliceAlign : (mode == kModeScoredNM ? kScoredNMSliceAlign : 1);
   int64_t slice = (d_in + gk_req - 1) / gk_req;
   slice = (slice + align - 1) / align * align;
   // the kept list of a slice must fit the LDS budget
@@ -1853,7 +1912,7 @@ Decision decide_gemv(int mode, int64_t d_out, int64_t d_in, int64_t batch, int64
   // in-workgroup Top-K select, for small weights whose grid fills the chip
   // or whose walk is short.
   const bool sel = mode == kModeTopKSel;
-  const bool fk_ok = B <= 2 && mode != kModeListBatched && !sel;
+  const bool fk_ok = B <= 2 && mode != kModeListBatched && !sel && mode != kModeScoredNM;
   int tiling = g_tiling;
   const bool hot = B == 1 && (mode == kModeThreshold || mode == kModeDense ||
                               mode == kModeList || mode == kModeTopK || sel);
@@ -1945,7 +2004,9 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t s) {
   kp.mu = c.mu;
   kp.cut = c.cut;
   kp.topk_k = c.topk_k;
-  kp.var = (mode == kModeScored && c.var) ? 1 : 0;
+  kp.var = ((mode == kModeScored || mode == kModeScoredNM) && c.var) ? 1 : 0;
+  kp.sn = c.sn;
+  kp.sm = c.sm;
 
   if (dc.full_k) {
     const unsigned grid = (unsigned)((c.d_out + kTilings[tiling].tile_o - 1) /

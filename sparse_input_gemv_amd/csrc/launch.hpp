@@ -42,6 +42,7 @@ enum GemvMode : int {
   kModeTopK = 8,       // x + per-row (tau, i*) from the Top-K select: keep iff
                        // key > tau, or key == tau and k <= i*
   kModeTopKSel = 9,    // kModeTopK with each workgroup selecting (tau, i*) itself
+  kModeScoredNM = 10,  // kModeScored with n of every m entries kept by score (batch 1)
 };
 
 struct GemvCall {
@@ -57,6 +58,7 @@ struct GemvCall {
   const int32_t* cut = nullptr;  // Top-K mode: [batch][2] (tau, i*)
   int64_t topk_k = 0;            // kModeTopKSel: entries kept per row
   int var = 0;                   // scored mode: apply the variance correction
+  int sn = 0, sm = 0;            // scored N:M mode: n kept of every m
   // lists
   const int32_t* idx = nullptr;
   const uint16_t* val = nullptr;

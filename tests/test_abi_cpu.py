@@ -284,6 +284,28 @@ def test_scored_gemv_checks(sa):
     assert f(*args) == SA_ERR_INVALID_ARG
 
 
+def test_scored_nm_gemv_checks(sa):
+    need = sa.sa_workspace_bytes(4096, 11008, 1)
+    f = sa.sparse_gemv_scored_nm
+    ok = [P, 4096, 11008, P, None, None, 8, 16, 1, None, P, P, need, None]  # never called as is
+    for n, m in [(0, 16), (17, 16), (2, 6), (2, 64), (1, 2), (-1, 4)]:
+        args = list(ok)
+        args[6], args[7] = n, m
+        assert f(*args) == SA_ERR_INVALID_ARG, (n, m)
+    args = list(ok)
+    args[2] = 11000  # not a multiple of m = 16
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[5] = P + 4  # colnorm not 8-byte aligned
+    assert f(*args) == SA_ERR_INVALID_ARG
+    args = list(ok)
+    args[12] = need - 1
+    assert f(*args) == SA_ERR_WORKSPACE
+    args = list(ok)
+    args[3] = None
+    assert f(*args) == SA_ERR_INVALID_ARG
+
+
 def test_rana_adapter_checks(sa):
     # B is row-major and needs no workspace: only the second GEMV's counts
     need = sa.sa_workspace_bytes(11008, 2048, 1)

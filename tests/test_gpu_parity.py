@@ -783,6 +783,52 @@ def test_scored_fused(d_out, d_in, shifted, weighted, var, biased):
     assert_close(out[2], y_ref)
 
 
+@pytest.mark.parametrize("d_out,d_in,n,m", [(4096, 11008, 8, 16), (4096, 11008, 16, 32),
+                                           (264, 1024, 2, 4), (11008, 4096, 4, 8),
+                                           (72, 40000, 8, 16), (136, 1000, 4, 8),
+                                           (200, 96, 1, 32), (64, 4104, 3, 8)])
+@pytest.mark.parametrize("shifted,weighted,var,biased", [(True, True, True, True),
+                                                        (False, True, False, False),
+                                                        (True, False, True, False)])
+def test_scored_nm_fused(d_out, d_in, n, m, shifted, weighted, var, biased):
+    """sparse_gemv_scored_nm (one launch) against the oracle's corrected GEMV
+    with n of every m kept by score; the one- and two-launch hand-offs give
+    identical bits; the list path (act_sparsify_scored, then
+    sparse_gemv_corrected) agrees within the tolerance."""
+    wt = syn.weight_t(d_out, d_in, d_out + 3 * d_in + m)
+    x = syn.laplace_f16((d_in,), 1.0, 31 + n)
+    x[::13] = np.float16(0.25)  # ties inside groups
+    mu = syn.gaussian_f16((d_in,), 0.25, 32) if shifted else None
+    wt_g = dev(wt)
+    cn_g = sa.weight_col_norms(wt_g) if weighted else None
+    cn = host(cn_g) if weighted else None
+    bias_g = sa.dense_gemv(wt_g, dev(mu if mu is not None else x)) if biased else None
+    _, keep, alpha, y_ref = correct.corrected_gemv(
+        wt, x, mu, cn, lambda v, c: correct.nm_keep(v, c, n, m), var=var)
+    if mu is not None:
+        y_ref = y_ref - gemv.dense_gemv(wt, mu)
+    if biased:
+        y_ref = y_ref + host(bias_g).astype(np.float64)
+    mu_g = dev(mu) if mu is not None else None
+    out = {}
+    try:
+        for handoff in (2, 1, 3):
+            sa.set_gemv_tuning(-1, 0, handoff)
+            out[handoff] = sa.sparse_gemv_scored_nm(wt_g, dev(x), n, m, mu=mu_g, colnorm=cn_g,
+                                                    var=var, bias=bias_g).clone()
+    finally:
+        sa.set_gemv_tuning(-1, 0, 0)
+    assert torch.equal(out[1], out[2]) and torch.equal(out[1], out[3])
+    assert_close(out[2], y_ref)
+    # the two-step list path: same kept set (bit-exact lists), same output within tolerance
+    mask_g, idx_g, val_g, nnz_g, alpha_g = sa.act_sparsify_scored(
+        dev(x).reshape(1, -1), t=0.0, n=n, m=m, mu=mu_g, colnorm=cn_g)
+    assert np.array_equal(host(idx_g)[0, :int(host(nnz_g)[0])], np.flatnonzero(keep))
+    y2 = sa.sparse_gemv_corrected(wt_g, idx_g, val_g, nnz_g, alpha=alpha_g if var else None,
+                                  bias=bias_g)
+    assert_close(out[2], host(y2).reshape(-1).astype(np.float64))
+
+
 # ---------------------------------------------------------------------------
 # RaNA linear-layer rank adapter A (m ⊙ B x), m_i = v_i^2 >= t
 # ---------------------------------------------------------------------------
