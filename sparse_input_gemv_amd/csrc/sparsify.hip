@@ -247,10 +247,10 @@ __global__ __launch_bounds__(kScoredNmGroups) void k_sparsify_scored_nm(
     int32_t* __restrict__ idx, uint16_t* __restrict__ val, int32_t* __restrict__ nnz,
     int64_t cap, int vec, int vec_mu) {
   static_assert(M == 4 || M == 8 || M == 16 || M == 32, "group sizes");
-  const int64_t row = blockIdx.y;
+  const int64_t row = blockIdx.x;  // rows in x (up to 2^31 - 1), a row's chunks in y
   const int lane = (int)threadIdx.x;
   const int64_t ng = d / M;
-  const int64_t g = (int64_t)blockIdx.x * kScoredNmGroups + lane;
+  const int64_t g = (int64_t)blockIdx.y * kScoredNmGroups + lane;
   const bool ok = g < ng;
   const int64_t k0 = (ok ? g : 0) * M;
   const uint16_t* xr = x + row * d;
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kScoredNmGroups) void k_sparsify_scored_nm(
     const int64_t wi = (g * M) >> 5;
     if (lane % GPW == 0 && wi < words) mask[row * words + wi] = w;
   }
-  if (blockIdx.x == 0 && lane == 0) nnz[row] = (int32_t)(ng * n);
+  if (blockIdx.y == 0 && lane == 0) nnz[row] = (int32_t)(ng * n);
 }
 
 // alpha[row] = sqrt(sum x'^2 / sum_kept x'^2), 1 when the kept sum is 0: both
@@ -1099,9 +1099,9 @@ hipError_t launch_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d,
   // N:M: one thread per group over many workgroups, then the row sums of
   // the variance correction
   const int64_t ng = d / m;
-  const int64_t gx = (ng + kScoredNmGroups - 1) / kScoredNmGroups;
-  if (gx > 0x7fffffffLL || rows > 65535) return hipErrorNotSupported;
-  const dim3 g2((unsigned)gx, (unsigned)rows);
+  const int64_t gy = (ng + kScoredNmGroups - 1) / kScoredNmGroups;
+  if (gy > 65535 || rows > 0x7fffffffLL) return hipErrorNotSupported;  // d <= 4194240 m
+  const dim3 g2((unsigned)rows, (unsigned)gy);
 #define SA_SCORED_NM(M)                                                                       \
   hipLaunchKernelGGL((k_sparsify_scored_nm<M>), g2, dim3(kScoredNmGroups), 0, s, x, d, mu,   \
                      colnorm, n, mask, idx, val, nnz, cap, vec, vec_mu)

@@ -711,6 +711,21 @@ def test_scored_sparsify_ragged_rows(d, nm):
         assert torch.equal(a, b)
 
 
+def test_scored_sparsify_many_rows():
+    """More rows than a grid's y dimension holds (70000 > 65535): rows run
+    along x.  Sampled rows against the oracle."""
+    rows, d, n, m = 70000, 64, 2, 4
+    X = syn.laplace_f16((rows, d), 1.0, 91)
+    mask_g, idx_g, val_g, nnz_g, alpha_g = sa.act_sparsify_scored(dev(X), t=0.0, n=n, m=m)
+    sample = np.unique(np.concatenate([np.arange(0, rows, 997), [65535, 65536, rows - 1]]))
+    XS = X[sample]
+    keep = np.stack([correct.nm_keep(XS[i], None, n, m) for i in range(len(sample))])
+    check_lists(mask_g[sample], idx_g[sample], val_g[sample], nnz_g[sample], XS, keep)
+    alpha = host(alpha_g)[sample]
+    for i in range(len(sample)):
+        assert alpha[i] == pytest.approx(correct.var_alpha(XS[i], keep[i]), rel=2e-6)
+
+
 @pytest.mark.parametrize("kind", ["threshold", "8:16"])
 @pytest.mark.parametrize("d_out,d_in", [(4096, 11008), (264, 1024), (11008, 4096)])
 def test_corrected_gemv(d_out, d_in, kind):
