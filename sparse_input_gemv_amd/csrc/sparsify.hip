@@ -141,6 +141,82 @@ __global__ __launch_bounds__(NT) void k_sparsify_threshold(
   if (threadIdx.x == 0) nnz[row] = base;
 }
 
+// Two-pass form of the threshold kind for long rows (kScoredThrMinD <= d
+// <= kScoredThrMaxD): the scores need x, mu and the fp64 weight norms (12
+// bytes per entry), which one workgroup per row reads through one CU.  The
+// first pass (k_scored_thr_bits) spreads the decisions over chunks of
+// kScoredThrChunk entries, one workgroup each: it writes the mask and
+// stages the keep bits (as half-words at the head of the row's val buffer)
+// and the chunk's fp64 sums of x'^2 and kept x'^2 (as int32 pairs at the
+// head of the row's idx buffer; the row holds cap >= d entries of each).
+// The second pass, k_sparsify_scored<.., true>, reads them back and writes
+// the list from x and mu alone.
+constexpr int kScoredThrChunk = 1024;
+constexpr int64_t kScoredThrMinD = 4096;
+constexpr int64_t kScoredThrMaxD = 65536;
+
+__global__ __launch_bounds__(256) void k_scored_thr_bits(
+    const uint16_t* __restrict__ x, int64_t d, const uint16_t* __restrict__ mu,
+    const double* __restrict__ cn, double t, uint32_t* __restrict__ mask,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ val, int64_t cap) {
+  constexpr int E = kScoredThrChunk / 256;  // 4 entries per thread
+  __shared__ double ws[2][256 / kWave];
+  const int64_t row = blockIdx.x, c = blockIdx.y;
+  const int tid = (int)threadIdx.x;
+  const int64_t k0 = c * kScoredThrChunk + (int64_t)tid * E;
+  const uint16_t* xr = x + row * d;
+  uint32_t bits = 0;
+  double s_all = 0.0, s_kept = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int64_t k = k0 + e;
+    if (k < d) {
+      uint16_t v = xr[k];
+      if (mu != nullptr) v = f2h(h2f(v) - h2f(mu[k]));
+      const double a = fabs((double)h2f(v));
+      const bool keep = (cn != nullptr ? a * cn[k] : a) >= t && h2f(v) != 0.f;
+      const double q = (double)h2f(v) * (double)h2f(v);
+      s_all += q;
+      s_kept += keep ? q : 0.0;
+      bits |= (uint32_t)keep << e;
+    }
+  }
+  // 8 neighbouring threads hold one 32-bit word
+  uint32_t w = bits << (E * (tid % 8));
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) w |= (uint32_t)__shfl_xor((int)w, o, kWave);
+  const int64_t wi = (c * kScoredThrChunk + (int64_t)tid * E) >> 5;
+  if (tid % 8 == 0 && wi * 32 < d) {
+    if (mask != nullptr) mask[row * ((d + 31) >> 5) + wi] = w;
+    uint16_t* vr = val + row * cap;
+    vr[2 * wi] = (uint16_t)(w & 0xffffu);
+    if (wi * 32 + 16 < d) vr[2 * wi + 1] = (uint16_t)(w >> 16);
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    s_all += __shfl_xor(s_all, o, kWave);
+    s_kept += __shfl_xor(s_kept, o, kWave);
+  }
+  if (lane_id() == 0) {
+    ws[0][tid / kWave] = s_all;
+    ws[1][tid / kWave] = s_kept;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double a = 0.0, k = 0.0;
+    for (int i = 0; i < 256 / kWave; ++i) {
+      a += ws[0][i];
+      k += ws[1][i];
+    }
+    int32_t* ir = idx + row * cap + 4 * c;
+    const uint64_t ab = __builtin_bit_cast(uint64_t, a), kb = __builtin_bit_cast(uint64_t, k);
+    ir[0] = (int32_t)(uint32_t)ab;
+    ir[1] = (int32_t)(uint32_t)(ab >> 32);
+    ir[2] = (int32_t)(uint32_t)kb;
+    ir[3] = (int32_t)(uint32_t)(kb >> 32);
+  }
+}
+
 // Weight-aware selection with a static shift (the flexible N:M
 // activation-sparsity summary, section 2: WT and Amber-Pruner score entries
 // by the weight they multiply; S-PTS shifts activations towards zero; VAR
@@ -154,7 +230,12 @@ __global__ __launch_bounds__(NT) void k_sparsify_threshold(
 // This kernel takes the threshold kind, one workgroup per row: the kept x'
 // are compacted as the threshold sparsifier does.  alpha[row] =
 // sqrt(sum x'^2 / sum_kept x'^2) (1 when nothing is kept), in fp64.
-template <int NT, int E>
+//
+// PRE (the second pass of the two-pass form below): the keep bits and the
+// per-chunk sums come from k_scored_thr_bits, staged in this row's own val
+// and idx buffers; they are read into LDS first, then the list overwrites
+// them.  The mask was written by the first pass.
+template <int NT, int E, bool PRE = false>
 __global__ __launch_bounds__(NT) void k_sparsify_scored(
     const uint16_t* __restrict__ x, int64_t d, const uint16_t* __restrict__ mu,
     const double* __restrict__ cn, double t, uint32_t* __restrict__ mask,
@@ -164,14 +245,33 @@ __global__ __launch_bounds__(NT) void k_sparsify_scored(
   __shared__ double sums[2][NT / kWave];
   __shared__ __align__(16) int32_t sidx[NT * E];
   __shared__ __align__(16) uint16_t sval[NT * E];
+  __shared__ uint16_t pbits[PRE ? kScoredThrMaxD / 16 : 1];
   const bool one_pass = d <= (int64_t)NT * E;
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * d;
   int32_t* ir = idx + row * cap;
   uint16_t* vr = val + row * cap;
-  uint32_t* mr = mask ? mask + row * ((d + 31) >> 5) : nullptr;
+  uint32_t* mr = (mask && !PRE) ? mask + row * ((d + 31) >> 5) : nullptr;
   int base = 0;
   double s_all = 0.0, s_kept = 0.0;
+  if constexpr (PRE) {
+    // every staged value is read before the first list write
+    const int64_t nh = (d + 15) / 16;
+    for (int64_t i = threadIdx.x; i < nh; i += NT) pbits[i] = vr[i];
+    if (threadIdx.x == 0 && alpha != nullptr) {
+      const int64_t nc = (d + kScoredThrChunk - 1) / kScoredThrChunk;
+      double a = 0.0, k = 0.0;
+      for (int64_t c = 0; c < nc; ++c) {  // chunk order: a fixed sum
+        a += __builtin_bit_cast(double, (uint64_t)(uint32_t)ir[4 * c] |
+                                            ((uint64_t)(uint32_t)ir[4 * c + 1] << 32));
+        k += __builtin_bit_cast(double, (uint64_t)(uint32_t)ir[4 * c + 2] |
+                                            ((uint64_t)(uint32_t)ir[4 * c + 3] << 32));
+      }
+      sums[0][0] = a;
+      sums[1][0] = k;
+    }
+    __syncthreads();
+  }
   for (int64_t c0 = 0; c0 < d; c0 += (int64_t)NT * E) {
     const int64_t k0 = c0 + (int64_t)threadIdx.x * E;
     uint16_t v[E];
@@ -182,30 +282,37 @@ __global__ __launch_bounds__(NT) void k_sparsify_scored(
 #pragma unroll
       for (int e = 0; e < E; ++e) v[e] = (k0 + e < d) ? f2h(h2f(v[e]) - h2f(m[e])) : (uint16_t)0;
     }
-    double sc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const double a = fabs((double)h2f(v[e]));
-      sc[e] = (k0 + e < d) ? (cn != nullptr ? a * cn[k0 + e] : a) : 0.0;
-    }
     uint64_t bits = 0;
+    if constexpr (PRE) {
+      static_assert(E == 16, "a thread's run is one staged half-word of bits");
+      bits = k0 < d ? (uint64_t)pbits[k0 / 16] : 0ull;
+    } else {
+      double sc[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool keep = (k0 + e < d) && sc[e] >= t && h2f(v[e]) != 0.f;
-      bits |= (uint64_t)keep << e;
-    }
+      for (int e = 0; e < E; ++e) {
+        const double a = fabs((double)h2f(v[e]));
+        sc[e] = (k0 + e < d) ? (cn != nullptr ? a * cn[k0 + e] : a) : 0.0;
+      }
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const double q = (double)h2f(v[e]) * (double)h2f(v[e]);
-      s_all += (k0 + e < d) ? q : 0.0;
-      s_kept += ((bits >> e) & 1ull) ? q : 0.0;
+      for (int e = 0; e < E; ++e) {
+        const bool keep = (k0 + e < d) && sc[e] >= t && h2f(v[e]) != 0.f;
+        bits |= (uint64_t)keep << e;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const double q = (double)h2f(v[e]) * (double)h2f(v[e]);
+        s_all += (k0 + e < d) ? q : 0.0;
+        s_kept += ((bits >> e) & 1ull) ? q : 0.0;
+      }
     }
     if (one_pass)
       base = compact_row_lds<NT, E>(bits, v, k0, d, scan, sidx, sval, ir, vr, mr);
     else
       compact_run<NT, E>(bits, v, k0, d, base, scan, ir, vr, mr);
   }
-  if (alpha != nullptr) {
+  if (PRE && alpha != nullptr && threadIdx.x == 0)
+    alpha[row] = sums[1][0] > 0.0 ? (float)sqrt(sums[0][0] / sums[1][0]) : 1.f;
+  if (!PRE && alpha != nullptr) {
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) {
       s_all += __shfl_xor(s_all, o, kWave);
@@ -1091,7 +1198,18 @@ hipError_t launch_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d,
   const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && (d % 8) == 0) ? 1 : 0;
   const int vec_mu = ((reinterpret_cast<uintptr_t>(mu) & 15u) == 0) ? 1 : 0;
   const dim3 grid((unsigned)rows);
-  if (m == 0) {  // threshold: one workgroup per row
+  if (m == 0) {
+    if (d >= kScoredThrMinD && d <= kScoredThrMaxD && rows <= 0x7fffffffLL) {
+      // two passes: decisions over chunks, then the list
+      const int64_t nc = (d + kScoredThrChunk - 1) / kScoredThrChunk;
+      hipLaunchKernelGGL(k_scored_thr_bits, dim3((unsigned)rows, (unsigned)nc), dim3(256), 0, s,
+                         x, d, mu, colnorm, t, mask, idx, val, cap);
+      hipLaunchKernelGGL((k_sparsify_scored<kSparsifyThreads, 16, true>), grid,
+                         dim3(kSparsifyThreads), 0, s, x, d, mu, colnorm, t, mask, idx, val, nnz,
+                         alpha, cap, vec, vec_mu);
+      return hipGetLastError();
+    }
+    // short rows: one workgroup per row
     hipLaunchKernelGGL((k_sparsify_scored<kSparsifyThreads, 16>), grid, dim3(kSparsifyThreads), 0,
                        s, x, d, mu, colnorm, t, mask, idx, val, nnz, alpha, cap, vec, vec_mu);
     return hipGetLastError();

@@ -711,6 +711,38 @@ def test_scored_sparsify_ragged_rows(d, nm):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d", [4096, 4112, 5000, 4127, 16400, 65536])
+def test_scored_threshold_two_pass(d):
+    """Rows long enough for the two-pass threshold kind (decisions over
+    1024-entry chunks, then the list): last mask words cut at 8, 16 and 31
+    entries, a list longer than one pass, the longest row; with and without
+    the mask output."""
+    rows = 3
+    X = syn.laplace_f16((rows, d), 1.0, 5 * d + 1)
+    X[2, ::5] = np.float16(0.0)
+    mu = syn.gaussian_f16((d,), 0.25, d + 2)
+    cn = correct.column_norms(syn.weight_t(16, d, 6))
+    XS = np.stack([correct.shift(X[r], mu) for r in range(rows)])
+    sc = np.sort(correct.scores(XS[0], cn))
+    t = float(0.5 * (sc[d // 2 - 1] + sc[d // 2]))
+    args = dict(t=t, n=0, m=0, mu=dev(mu), colnorm=torch.from_numpy(cn).to(DEV))
+    mask_g, idx_g, val_g, nnz_g, alpha_g = sa.act_sparsify_scored(dev(X), **args)
+    keep = np.stack([correct.threshold_keep(XS[r], cn, t) for r in range(rows)])
+    check_lists(mask_g, idx_g, val_g, nnz_g, XS, keep)
+    alpha = host(alpha_g)
+    for r in range(rows):
+        assert alpha[r] == pytest.approx(correct.var_alpha(XS[r], keep[r]), rel=2e-6)
+    g2 = sa.act_sparsify_scored(dev(X), with_mask=False, **args)
+    assert g2[0] is None
+    for a, b in zip(g2[1:], (idx_g, val_g, nnz_g, alpha_g)):
+        n_ = host(nnz_g)
+        if a.dim() == 2 and a.shape == b.shape and a.dtype != torch.float32:
+            for r in range(rows):
+                assert torch.equal(a[r, :int(n_[r])], b[r, :int(n_[r])])
+        else:
+            assert torch.equal(a, b)
+
+
 def test_scored_sparsify_many_rows():
     """More rows than a grid's y dimension holds (70000 > 65535): rows run
     along x.  Sampled rows against the oracle."""
