@@ -181,6 +181,9 @@ int act_sparsify_nm_shared(const uint16_t* x, int64_t rows, int64_t d, int n, in
  *   alpha   [rows] fp32 or NULL
  * Requires t finite >= 0 and cap >= d when m == 0; m in {4,8,16,32},
  * 1 <= n <= m, d % m == 0 and cap >= d*n/m otherwise.
+ * Entries of idx and val past nnz are undefined afterwards: for m == 0 and
+ * 4096 <= d <= 65536 the call stages intermediate results at the head of
+ * each row's idx and val before writing the lists there.
  */
 int act_sparsify_scored(const uint16_t* x, int64_t rows, int64_t d, const uint16_t* mu,
                         const double* colnorm, int n, int m, double t, uint32_t* mask,
