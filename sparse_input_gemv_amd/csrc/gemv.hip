@@ -235,6 +235,47 @@ __device__ __forceinline__ int group_rank(double sc) {
   return rank;
 }
 
+// The same rank from fp32 roundings of the scores, exchanged by DPP row
+// rotations (a VALU operand modifier, no LDS round trip).  Rounding to fp32
+// is monotone, so a strictly larger fp32 key means a strictly larger fp64
+// score; when no two keys of a group are equal the fp32 ranks are the fp64
+// ranks.  If any group of the wave has two equal keys (equal scores, zeros,
+// or scores closer than fp32 resolves) the whole wave takes group_rank.
+template <int R>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v) {  // DPP row_ror:R
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + R, 0xf, 0xf, false);
+}
+// Compares f with g rotated by R..15 lanes within the row of 16.  W < 16:
+// only lanes of this lane's aligned W-lane group count (the source lane's
+// position rotates with it, so the rotation's direction does not matter).
+template <int W, int R>
+__device__ __forceinline__ void rank_rot(float f, float g, int pos16, int& rank, bool& tie) {
+  if constexpr (R < 16) {
+    const float go = __builtin_bit_cast(float, row_ror<R>(__builtin_bit_cast(uint32_t, g)));
+    bool mine = true;
+    if constexpr (W < 16) mine = ((int)row_ror<R>((uint32_t)pos16) ^ pos16) < W;
+    rank += (mine && go > f) ? 1 : 0;
+    tie = tie || (mine && go == f);
+    rank_rot<W, R + 1>(f, g, pos16, rank, tie);
+  }
+}
+template <int M>
+__device__ __forceinline__ int group_rank_fast(double sc, bool in) {
+  const float f = (float)sc;
+  const int pos16 = lane_id() & 15;
+  int rank = 0;
+  bool tie = false;
+  rank_rot<(M < 16 ? M : 16), 1>(f, f, pos16, rank, tie);
+  if constexpr (M == 32) {  // the other row of 16 of the group
+    const float h = __shfl_xor(f, 16, kWave);
+    rank += h > f ? 1 : 0;
+    tie = tie || h == f;
+    rank_rot<16, 1>(f, h, pos16, rank, tie);
+  }
+  if (__ballot(in && tie) != 0) return group_rank<M>(sc);  // uniform
+  return rank;
+}
+
 __device__ __forceinline__ bool scored_keep_nm(const KParams& p, uint16_t& xb, uint16_t m,
                                                double c, bool in, double& s_all,
                                                double& s_kept) {
@@ -244,10 +285,10 @@ __device__ __forceinline__ bool scored_keep_nm(const KParams& p, uint16_t& xb, u
   const double sc = p.colnorm != nullptr ? a * c : a;
   int rank;
   switch (p.sm) {  // uniform
-    case 4: rank = group_rank<4>(sc); break;
-    case 8: rank = group_rank<8>(sc); break;
-    case 16: rank = group_rank<16>(sc); break;
-    default: rank = group_rank<32>(sc); break;
+    case 4: rank = group_rank_fast<4>(sc, in); break;
+    case 8: rank = group_rank_fast<8>(sc, in); break;
+    case 16: rank = group_rank_fast<16>(sc, in); break;
+    default: rank = group_rank_fast<32>(sc, in); break;
   }
   const bool kb = in && rank < p.sn;
   const double q = (double)v * (double)v;

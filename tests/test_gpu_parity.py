@@ -876,6 +876,47 @@ def test_scored_nm_fused(d_out, d_in, n, m, shifted, weighted, var, biased):
     assert_close(out[2], host(y2).reshape(-1).astype(np.float64))
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (3, 8), (8, 16), (5, 16), (16, 32), (11, 32)])
+def test_scored_nm_near_ties(n, m):
+    """The one-launch N:M GEMV ranks scores in fp32 when that decides them,
+    else in fp64.  Groups whose fp64 scores differ below fp32's resolution,
+    exact ties, and zeros sit in some 64-entry blocks, plain random groups in
+    the others.  With the identity as the weight, y is x on the kept entries
+    and 0 elsewhere, so the kept set is compared bit for bit with the oracle's
+    N:M rule."""
+    d = 4096
+    rng = np.random.default_rng(1000 + 37 * m + n)
+    x = syn.laplace_f16((d,), 1.0, 500 + n + m)
+    cn = rng.uniform(0.5, 2.0, d)
+    for blk in range(0, d, 64):
+        kind = (blk // 64) % 4
+        if kind == 0:
+            continue  # random scores: decided in fp32
+        for g in range(blk, blk + 64, m):
+            if kind == 1:  # equal x, fp64 norms 2^-40 apart: one fp32 key
+                x[g:g + m] = np.float16(0.5)
+                cn[g:g + m] = 1.0 + rng.permutation(m) * 2.0 ** -40
+            elif kind == 2:  # exact ties: the lower index wins
+                x[g:g + m] = np.float16(-0.75)
+                cn[g:g + m] = 1.25
+            else:  # some zeros among random entries
+                x[g:g + m:3] = np.float16(0)
+    wt = np.eye(d, dtype=np.float16)
+    keep = correct.nm_keep(x, cn, n, m)
+    y = sa.sparse_gemv_scored_nm(dev(wt), dev(x), n, m, colnorm=dev(cn), var=False)
+    expect = np.where(keep, x, np.float16(0))
+    assert np.array_equal(host(y).view(np.uint16), expect.view(np.uint16))
+    # near-tie groups are not decided by position alone
+    kind1 = np.zeros(d, dtype=bool)
+    for blk in range(64, d, 256):
+        kind1[blk:blk + 64] = True
+    first_n = np.zeros(d, dtype=bool)
+    for g in range(0, d, m):
+        first_n[g:g + n] = True
+    assert not np.array_equal(keep[kind1], first_n[kind1])
+
+
 # ---------------------------------------------------------------------------
 # RaNA linear-layer rank adapter A (m ⊙ B x), m_i = v_i^2 >= t
 # ---------------------------------------------------------------------------
