@@ -400,6 +400,24 @@ __device__ __forceinline__ void wait_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Variance-correction sums over a row's slices, in one fixed order that both
+// hand-offs use: lane l of one wave adds slices l, l + 64, l + 128, ... in
+// increasing order (a0/k0 hold slice l's sums, 0 past gk), then the wave's
+// lanes are added by an xor tree.  get(kk) returns slice kk's pair.
+template <typename Get>
+__device__ __forceinline__ void var_wave_sums(double& a, double& k, int gk, Get get) {
+  for (int kk = lane_id() + kWave; kk < gk; kk += kWave) {
+    const double2 v = get(kk);
+    a += v.x;
+    k += v.y;
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) {
+    a += __shfl_xor(a, off, kWave);
+    k += __shfl_xor(k, off, kWave);
+  }
+}
+
 // Final sum of one output tile over the gk partial tiles, by the workgroup
 // that arrived last.  Thread pairs (g, o) -- slice group g of 16, output o
 // -- add slices g, g+16, g+32, ... in increasing order; then the groups are
@@ -407,9 +425,14 @@ __device__ __forceinline__ void wait_stores() {
 // and order, so both hand-offs round identically.  A wave's 64 lanes take 64
 // consecutive outputs of one slice group, so each load is one wave-uniform
 // address plus the lane: whole lines per wave and few address registers.
-template <int TILE_O, int NT, int B, bool LOCAL>
+//
+// VAR (scored mode with the variance correction): wave 0 also loads every
+// slice's sums of this tile (stored before their tickets), with the partials
+// in flight, and sets *alpha_w before the barrier that precedes the outputs.
+template <int TILE_O, int NT, int B, bool LOCAL, bool VAR = false>
 __device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0, unsigned char* smem,
-                                               const float* alpha, const uint16_t* bias) {
+                                               const float* alpha, const uint16_t* bias,
+                                               int oblk = 0, float* alpha_w = nullptr) {
   constexpr int G = kReduceGroups;
   constexpr int PAIRS = G * TILE_O;
   constexpr int PP = (PAIRS + NT - 1) / NT;  // pairs per thread
@@ -420,6 +443,19 @@ __device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0, uns
   const int lane = lane_id();
   const int w0 = __builtin_amdgcn_readfirstlane(tid - lane);
   const int64_t stride = (int64_t)B * p.d_out;
+  double va = 0.0, vk = 0.0;
+  const bool var_wave = VAR && p.var && tid < kWave;
+  auto vsum_at = [&](int kk) {
+    const double* src = p.vsum + ((int64_t)kk * p.go + oblk) * 2;
+    return make_double2(load_handoff(src, (int)LOCAL), load_handoff(src + 1, (int)LOCAL));
+  };
+  if constexpr (VAR) {
+    if (var_wave && lane < p.gk) {
+      const double2 v = vsum_at(lane);
+      va = v.x;
+      vk = v.y;
+    }
+  }
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     if (b >= p.batch) break;
@@ -452,6 +488,12 @@ __device__ __forceinline__ void handoff_reduce(const KParams& p, int64_t o0, uns
     for (int pp = 0; pp < PP; ++pp) {
       const int e = tid + pp * NT;
       if (e < PAIRS) red[e] = s[pp];
+    }
+    if constexpr (VAR) {
+      if (var_wave) {
+        var_wave_sums(va, vk, p.gk, vsum_at);
+        if (tid == 0) *alpha_w = var_alpha(va, vk);
+      }
     }
     __syncthreads();
     for (int oo = tid; oo < TILE_O; oo += NT) {
@@ -552,6 +594,12 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
   const int64_t o0 = (int64_t)oblk * TILE_O;
   // scored mode with the variance correction: alpha of the row (set below)
   __shared__ float s_alpha;
+  // scored mode with VAR: per-wave sums of x'^2 ([0, NW)) and kept x'^2 ([NW, 2 NW))
+  double* vred = nullptr;
+  if constexpr (kScoredMode<MODE>) {
+    __shared__ double vred_lds[2 * (NT / kWave)];
+    vred = vred_lds;
+  }
   const float* alpha_out = (kScoredMode<MODE> && p.var) ? &s_alpha : alpha_arg;
   __shared__ int s_last;
 
@@ -858,46 +906,6 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
       __syncthreads();
     }
 
-    // Scored mode with the variance correction: this slice's sums of x'^2 and
-    // kept x'^2.  One slice is the whole input: alpha now.  Otherwise the sums
-    // go beside this workgroup's partial (written before its ticket, so the
-    // tile's last workgroup reads every slice's sums with the partials).
-    if constexpr (kScoredMode<MODE>) {
-      if (p.var) {
-        __shared__ double vred[2][NT / kWave];
-#pragma unroll
-        for (int off = kWave / 2; off >= 1; off >>= 1) {
-          s_all += __shfl_xor(s_all, off, kWave);
-          s_kept += __shfl_xor(s_kept, off, kWave);
-        }
-        if (lane_id() == 0) {
-          vred[0][tid / kWave] = s_all;
-          vred[1][tid / kWave] = s_kept;
-        }
-        __syncthreads();
-        if (tid == 0) {
-          double a = 0.0, k = 0.0;
-          for (int i = 0; i < NT / kWave; ++i) {
-            a += vred[0][i];
-            k += vred[1][i];
-          }
-          if (p.gk == 1) {
-            s_alpha = var_alpha(a, k);
-          } else {
-            double* dst = p.vsum + ((int64_t)kb * p.go + oblk) * 2;
-            if (p.tickets != nullptr) {
-              store_handoff(dst, a, LOCAL);
-              store_handoff(dst + 1, k, LOCAL);
-            } else {
-              dst[0] = a;
-              dst[1] = k;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
-
     // ---------------- phase 2: stream the kept rows --------------------------
     const int o_lane = tid % OL;
     const int r_lane = tid / OL;
@@ -942,15 +950,46 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
           }
         }
       };
-      if (r_lane < cnt) {
+      if constexpr (kScoredMode<MODE>) {
+        // Scored mode with the variance correction: this slice's sums of x'^2
+        // and kept x'^2, reduced per wave while the first rows are in flight
+        // (every lane takes part); the workgroup's sum follows in phase 3.
         half8 wa[H], wb[H];
-        issue(wa, r_lane);
-        issue(wb, r_lane + H * R);
-        for (int j0 = r_lane; j0 < cnt; j0 += U * R) {
-          consume(wa, j0);
-          issue(wa, j0 + U * R);
-          consume(wb, j0 + H * R);
-          issue(wb, j0 + U * R + H * R);
+        const bool rows = r_lane < cnt;
+        if (rows) {
+          issue(wa, r_lane);
+          issue(wb, r_lane + H * R);
+        }
+        if (p.var) {
+#pragma unroll
+          for (int off = kWave / 2; off >= 1; off >>= 1) {
+            s_all += __shfl_xor(s_all, off, kWave);
+            s_kept += __shfl_xor(s_kept, off, kWave);
+          }
+          if (lane_id() == 0) {
+            vred[tid / kWave] = s_all;
+            vred[NT / kWave + tid / kWave] = s_kept;
+          }
+        }
+        if (rows) {
+          for (int j0 = r_lane; j0 < cnt; j0 += U * R) {
+            consume(wa, j0);
+            issue(wa, j0 + U * R);
+            consume(wb, j0 + H * R);
+            issue(wb, j0 + U * R + H * R);
+          }
+        }
+      } else {
+        if (r_lane < cnt) {
+          half8 wa[H], wb[H];
+          issue(wa, r_lane);
+          issue(wb, r_lane + H * R);
+          for (int j0 = r_lane; j0 < cnt; j0 += U * R) {
+            consume(wa, j0);
+            issue(wa, j0 + U * R);
+            consume(wb, j0 + H * R);
+            issue(wb, j0 + U * R + H * R);
+          }
         }
       }
     } else {
@@ -1008,6 +1047,31 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     float* red = reinterpret_cast<float*>(smem);
     const bool single = p.gk == 1;
     const bool handoff = !single && p.tickets != nullptr;
+    // Scored mode with VAR: the slice's sums.  One slice is the whole input:
+    // alpha now (read after the barrier below).  Otherwise the sums go beside
+    // this workgroup's partial, stored before its ticket, so the tile's last
+    // workgroup reads every slice's sums with the partials.
+    if constexpr (kScoredMode<MODE>) {
+      if (p.var && tid == 0) {
+        double a = 0.0, k = 0.0;
+        for (int i = 0; i < NT / kWave; ++i) {
+          a += vred[i];
+          k += vred[NT / kWave + i];
+        }
+        if (single) {
+          s_alpha = var_alpha(a, k);
+        } else {
+          double* dst = p.vsum + ((int64_t)kb * p.go + oblk) * 2;
+          if (handoff) {
+            store_handoff(dst, a, LOCAL);
+            store_handoff(dst + 1, k, LOCAL);
+          } else {
+            dst[0] = a;
+            dst[1] = k;
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       if (b >= p.batch) break;
@@ -1074,38 +1138,8 @@ __global__ __launch_bounds__(NT) void k_gemv(KParams p) {
     wait_stores();
     __syncthreads();
   }
-  if constexpr (kScoredMode<MODE>) {
-    if (p.var) {
-      // every slice's sums for this tile (written before their tickets)
-      double a = 0.0, k = 0.0;
-      for (int kk = tid; kk < p.gk; kk += NT) {
-        const double* src = p.vsum + ((int64_t)kk * p.go + oblk) * 2;
-        a += load_handoff(src, LOCAL);
-        k += load_handoff(src + 1, LOCAL);
-      }
-      __shared__ double vr2[2][NT / kWave];
-#pragma unroll
-      for (int off = kWave / 2; off >= 1; off >>= 1) {
-        a += __shfl_xor(a, off, kWave);
-        k += __shfl_xor(k, off, kWave);
-      }
-      if (lane_id() == 0) {
-        vr2[0][tid / kWave] = a;
-        vr2[1][tid / kWave] = k;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        double ta = 0.0, tk = 0.0;
-        for (int i = 0; i < NT / kWave; ++i) {
-          ta += vr2[0][i];
-          tk += vr2[1][i];
-        }
-        s_alpha = var_alpha(ta, tk);
-      }
-      __syncthreads();
-    }
-  }
-  handoff_reduce<TILE_O, NT, B, LOCAL>(p, o0, smem, alpha_out, bias_arg);
+  handoff_reduce<TILE_O, NT, B, LOCAL, kScoredMode<MODE>>(p, o0, smem, alpha_out, bias_arg,
+                                                         oblk, &s_alpha);
   if constexpr (MODE == kModeSwiglu) {
     if (oblk == 0 && p.out_nnz != nullptr) {
       int c = 0;
@@ -1146,29 +1180,18 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, 
   if (vsum != nullptr) {
     // the variance correction of the (single) row from every slice's sums
     // (tile 0's copies; every tile's are the same)
-    __shared__ double vr[2][256 / kWave];
-    double a = 0.0, k = 0.0;
-    for (int kk = tid; kk < gk; kk += 256) {
-      a += vsum[(int64_t)kk * go * 2];
-      k += vsum[(int64_t)kk * go * 2 + 1];
-    }
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) {
-      a += __shfl_xor(a, off, kWave);
-      k += __shfl_xor(k, off, kWave);
-    }
-    if (lane_id() == 0) {
-      vr[0][tid / kWave] = a;
-      vr[1][tid / kWave] = k;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double ta = 0.0, tk = 0.0;
-      for (int i = 0; i < 256 / kWave; ++i) {
-        ta += vr[0][i];
-        tk += vr[1][i];
+    if (tid < kWave) {
+      auto at = [&](int kk) {
+        return make_double2(vsum[(int64_t)kk * go * 2], vsum[(int64_t)kk * go * 2 + 1]);
+      };
+      double a = 0.0, k = 0.0;
+      if (tid < gk) {
+        const double2 v = at(tid);
+        a = v.x;
+        k = v.y;
       }
-      s_alpha = var_alpha(ta, tk);
+      var_wave_sums(a, k, gk, at);
+      if (tid == 0) s_alpha = var_alpha(a, k);
     }
     __syncthreads();
     alpha = &s_alpha;
