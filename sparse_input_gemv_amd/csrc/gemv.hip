@@ -241,36 +241,54 @@ __device__ __forceinline__ int group_rank(double sc) {
 // score; when no two keys of a group are equal the fp32 ranks are the fp64
 // ranks.  If any group of the wave has two equal keys (equal scores, zeros,
 // or scores closer than fp32 resolves) the whole wave takes group_rank.
-template <int R>
-__device__ __forceinline__ uint32_t row_ror(uint32_t v) {  // DPP row_ror:R
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + R, 0xf, 0xf, false);
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {  // every lane reads a lane of its own row
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                             0xf, 0xf, false));
 }
-// Compares f with g rotated by R..15 lanes within the row of 16.  W < 16:
-// only lanes of this lane's aligned W-lane group count (the source lane's
-// position rotates with it, so the rotation's direction does not matter).
-template <int W, int R>
-__device__ __forceinline__ void rank_rot(float f, float g, int pos16, int& rank, bool& tie) {
+// quad_perm controls (lane i of a quad reads lane (ctrl >> 2i) & 3): the
+// quad rotated by 1, 2, 3; row_half_mirror: lane i of 8 reads lane 7 - i,
+// which sits in the other quad of its 8; row_ror:R rotates a row of 16.
+constexpr int kQuadRot1 = 0x39, kQuadRot2 = 0x4e, kQuadRot3 = 0x93, kHalfMirror = 0x141;
+constexpr int kRowRor = 0x120;
+// Compares f with g rotated by R..15 lanes within the row of 16.
+template <int R>
+__device__ __forceinline__ void rank_rot(float f, float g, int& rank, bool& tie) {
   if constexpr (R < 16) {
-    const float go = __builtin_bit_cast(float, row_ror<R>(__builtin_bit_cast(uint32_t, g)));
-    bool mine = true;
-    if constexpr (W < 16) mine = ((int)row_ror<R>((uint32_t)pos16) ^ pos16) < W;
-    rank += (mine && go > f) ? 1 : 0;
-    tie = tie || (mine && go == f);
-    rank_rot<W, R + 1>(f, g, pos16, rank, tie);
+    const float go = dpp_f<kRowRor + R>(g);
+    rank += go > f ? 1 : 0;
+    tie = tie || go == f;
+    rank_rot<R + 1>(f, g, rank, tie);
   }
 }
 template <int M>
 __device__ __forceinline__ int group_rank_fast(double sc, bool in) {
   const float f = (float)sc;
-  const int pos16 = lane_id() & 15;
   int rank = 0;
   bool tie = false;
-  rank_rot<(M < 16 ? M : 16), 1>(f, f, pos16, rank, tie);
-  if constexpr (M == 32) {  // the other row of 16 of the group
-    const float h = __shfl_xor(f, 16, kWave);
-    rank += h > f ? 1 : 0;
-    tie = tie || h == f;
-    rank_rot<16, 1>(f, h, pos16, rank, tie);
+  auto cmp = [&](float g) {
+    rank += g > f ? 1 : 0;
+    tie = tie || g == f;
+  };
+  auto quad = [&](float g) {  // the three other lanes of g's quad
+    cmp(dpp_f<kQuadRot1>(g));
+    cmp(dpp_f<kQuadRot2>(g));
+    cmp(dpp_f<kQuadRot3>(g));
+  };
+  if constexpr (M == 4) {
+    quad(f);
+  } else if constexpr (M == 8) {
+    quad(f);
+    const float h = dpp_f<kHalfMirror>(f);  // a lane of the other quad, then its quad
+    cmp(h);
+    quad(h);
+  } else {
+    rank_rot<1>(f, f, rank, tie);
+    if constexpr (M == 32) {  // the other row of 16 of the group
+      const float h = __shfl_xor(f, 16, kWave);
+      cmp(h);
+      rank_rot<1>(f, h, rank, tie);
+    }
   }
   if (__ballot(in && tie) != 0) return group_rank<M>(sc);  // uniform
   return rank;
